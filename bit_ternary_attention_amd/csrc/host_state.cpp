@@ -1,0 +1,290 @@
+// Host-side cache state (no HIP).  See host_state.h.
+#include "host_state.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <unordered_set>
+
+namespace vk {
+namespace {
+
+std::string fmt_str(const char* f, long long a, long long b = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, f, a, b);
+  return buf;
+}
+
+bool valid_format(int32_t f) { return f == VK_FMT_TERNARY2 || f == VK_FMT_FP8E4M3 || f == VK_FMT_F16; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// splitmix64 (Steele, Lea, Flood: "Fast splittable pseudorandom number generators").
+struct SplitMix64 {
+  uint64_t x;
+  uint64_t next() {
+    x += 0x9E3779B97F4A7C15ull;
+    uint64_t z = x;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+  }
+};
+
+}  // namespace
+
+std::string validate_config(const vk_cache_config& c) {
+  if (c.n_layers < 1) return "n_layers must be >= 1";
+  if (c.n_kv_heads < 1) return "n_kv_heads must be >= 1";
+  if (c.n_q_heads < 1 || c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a positive multiple of n_kv_heads";
+  int g = c.n_q_heads / c.n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return "n_q_heads / n_kv_heads must be 1, 2, 4 or 8";
+  if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
+  if (c.block_size < kUnit || c.block_size > 65536 || (c.block_size & (c.block_size - 1)))
+    return "block_size must be a power of two in [16, 65536]";
+  if (c.max_seqs < 1) return "max_seqs must be >= 1";
+  if (c.max_tokens_per_seq < 1) return "max_tokens_per_seq must be >= 1";
+  if (c.sink_tokens < 0) return "sink_tokens must be >= 0";
+  if (c.recent_tokens < 0) return "recent_tokens must be >= 0";
+  if (!valid_format(c.sink_format) || !valid_format(c.recent_format)) return "unknown page format";
+  if (c.reserved0 != 0) return "reserved0 must be 0";
+  if (c.pages_ternary < 0 || c.pages_fp8 < 0 || c.pages_f16 < 0) return "pool capacities must be >= 0";
+  if (c.pages_ternary >= (1ll << 30) || c.pages_fp8 >= (1ll << 30) || c.pages_f16 >= (1ll << 30))
+    return "pool capacities must be < 2^30 pages";
+  if (!(c.eps >= 0.0f) || !std::isfinite(c.eps)) return "eps must be finite and >= 0";
+  if (!(c.fp8_scale > 0.0f) || !std::isfinite(c.fp8_scale)) return "fp8_scale must be finite and > 0";
+  int64_t max_pages = cdiv(c.max_tokens_per_seq, c.block_size);
+  if (static_cast<int64_t>(c.max_seqs) * max_pages > (1ll << 31) - 1) return "block table too large";
+  return "";
+}
+
+int64_t tile_bytes(const vk_cache_config& c, int fmt) {
+  int64_t elems = static_cast<int64_t>(c.block_size) * c.head_dim;
+  switch (fmt) {
+    case VK_FMT_TERNARY2: return elems / 4;
+    case VK_FMT_FP8E4M3: return elems;
+    case VK_FMT_F16: return elems * 2;
+  }
+  return 0;
+}
+
+int64_t page_bytes(const vk_cache_config& c, int fmt) { return 2ll * c.n_kv_heads * tile_bytes(c, fmt); }
+
+UnitRanges attended_units(int32_t length, int32_t sink_tokens, int32_t window) {
+  UnitRanges r;
+  r.sinks = std::min(sink_tokens, length);
+  int32_t all = static_cast<int32_t>(cdiv(length, kUnit));
+  if (window < 0 || static_cast<int64_t>(length) - window <= r.sinks) {
+    r.a_end = r.b_begin = r.b_end = all;
+    r.w0 = 0;
+    return r;
+  }
+  r.w0 = length - window;
+  r.a_end = static_cast<int32_t>(cdiv(r.sinks, kUnit));
+  if (window == 0) {
+    r.b_begin = r.b_end = r.a_end;
+  } else {
+    r.b_begin = std::max(r.a_end, r.w0 / kUnit);
+    r.b_end = all;
+  }
+  return r;
+}
+
+int32_t choose_splits(int64_t n_items, int32_t max_units, int32_t target_groups, int32_t max_splits,
+                      int32_t min_units) {
+  if (n_items <= 0 || max_units <= 0) return 1;
+  int64_t want = cdiv(target_groups, n_items);
+  int64_t by_work = std::max<int64_t>(1, max_units / std::max(1, min_units));
+  int64_t s = std::min<int64_t>({want, by_work, static_cast<int64_t>(max_splits)});
+  return static_cast<int32_t>(std::max<int64_t>(1, s));
+}
+
+HostState::HostState(const vk_cache_config& cfg) : cfg_(cfg) {
+  max_pages_ = static_cast<int32_t>(cdiv(cfg.max_tokens_per_seq, cfg.block_size));
+  seqs_.resize(cfg.max_seqs);
+  const int64_t caps[kFormats] = {cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16};
+  SplitMix64 rng{cfg.page_shuffle_seed};
+  for (int f = 0; f < kFormats; ++f) {
+    std::vector<int32_t> ids(caps[f]);
+    for (int64_t i = 0; i < caps[f]; ++i) ids[i] = static_cast<int32_t>(i);
+    if (cfg.page_shuffle_seed != 0) {
+      for (int64_t i = caps[f] - 1; i > 0; --i) {
+        int64_t j = static_cast<int64_t>(rng.next() % static_cast<uint64_t>(i + 1));
+        std::swap(ids[i], ids[j]);
+      }
+    }
+    free_[f].assign(ids.begin(), ids.end());
+  }
+}
+
+int32_t HostState::new_page_format(int32_t page, int32_t new_len) const {
+  const int64_t bs = cfg_.block_size;
+  if (page < cdiv(cfg_.sink_tokens, bs)) return cfg_.sink_format;
+  const int64_t lo = page * bs, hi = lo + bs;
+  if (cfg_.recent_tokens > 0 && lo < new_len && hi > static_cast<int64_t>(new_len) - cfg_.recent_tokens)
+    return cfg_.recent_format;
+  return VK_FMT_TERNARY2;
+}
+
+vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, int32_t n_tokens, AppendPlan* plan,
+                                 std::string* err) const {
+  if (n_seqs < 1 || n_seqs > cfg_.max_seqs) {
+    *err = fmt_str("n_seqs %lld out of range [1, %lld]", n_seqs, cfg_.max_seqs);
+    return VK_ERR_ARG;
+  }
+  if (!seq_ids) { *err = "seq_ids is NULL"; return VK_ERR_ARG; }
+  if (n_tokens < 1) { *err = "n_tokens must be >= 1"; return VK_ERR_ARG; }
+  std::unordered_set<int32_t> seen;
+  const int32_t bs = cfg_.block_size;
+  plan->seqs.clear();
+  plan->entries.clear();
+  plan->new_fmt.clear();
+  plan->max_units = 0;
+  plan->max_tern_tokens = 0;
+  plan->n_tokens = n_tokens;
+  for (int f = 0; f < kFormats; ++f) plan->new_pages[f] = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t s = seq_ids[i];
+    if (s < 0 || s >= cfg_.max_seqs) { *err = fmt_str("seq id %lld out of range", s); return VK_ERR_ARG; }
+    if (!seen.insert(s).second) { *err = fmt_str("seq id %lld repeated", s); return VK_ERR_ARG; }
+    const SeqState& st = seqs_[s];
+    const int64_t t0 = st.length, t1 = t0 + n_tokens;
+    if (t1 > cfg_.max_tokens_per_seq) {
+      *err = fmt_str("seq %lld would exceed max_tokens_per_seq (%lld)", s, cfg_.max_tokens_per_seq);
+      return VK_ERR_ARG;
+    }
+    if (t0 % bs) {
+      const int32_t e = st.pages[t0 / bs];
+      if (entry_fmt(e) == VK_FMT_TERNARY2) {
+        *err = fmt_str("seq %lld ends inside a ternary page (length %lld); ternary pages are written by one append",
+                       s, t0);
+        return VK_ERR_ALIGN;
+      }
+    }
+    AppendSeqDesc d{};
+    d.slot = s;
+    d.t0 = static_cast<int32_t>(t0);
+    d.page_first = static_cast<int32_t>(t0 / bs);
+    d.page_off = static_cast<int32_t>(plan->entries.size());
+    const int32_t page_end = static_cast<int32_t>(cdiv(t1, bs));
+    d.n_pages = page_end - d.page_first;
+    d.unit_first = static_cast<int32_t>(t0 / kUnit);
+    const int32_t unit_end = static_cast<int32_t>(cdiv(t1, kUnit));
+    plan->max_units = std::max(plan->max_units, unit_end - d.unit_first);
+    int64_t tlo = t1, thi = t0;  // ternary token range (absolute)
+    for (int32_t p = d.page_first; p < page_end; ++p) {
+      if (p < static_cast<int32_t>(st.pages.size())) {
+        plan->entries.push_back(st.pages[p]);  // existing partly filled page (fp8 / f16)
+        continue;
+      }
+      const int32_t f = new_page_format(p, static_cast<int32_t>(t1));
+      plan->new_pages[f] += 1;
+      plan->new_fmt.push_back(f);
+      plan->entries.push_back(make_entry(f, 0));  // index filled at commit
+      if (f == VK_FMT_TERNARY2) {
+        tlo = std::min<int64_t>(tlo, std::max<int64_t>(static_cast<int64_t>(p) * bs, t0));
+        thi = std::max<int64_t>(thi, std::min<int64_t>(static_cast<int64_t>(p + 1) * bs, t1));
+      }
+    }
+    if (thi > tlo) {
+      d.tern_lo = static_cast<int32_t>(tlo - t0);
+      d.tern_hi = static_cast<int32_t>(thi - t0);
+    } else {
+      d.tern_lo = d.tern_hi = 0;
+    }
+    plan->max_tern_tokens = std::max(plan->max_tern_tokens, d.tern_hi - d.tern_lo);
+    plan->seqs.push_back(d);
+  }
+  for (int f = 0; f < kFormats; ++f) {
+    if (plan->new_pages[f] > static_cast<int64_t>(free_[f].size())) {
+      static const char* names[kFormats] = {"ternary", "fp8", "f16"};
+      char buf[160];
+      std::snprintf(buf, sizeof buf, "pool of %s pages exhausted: need %lld, %lld free", names[f],
+                    static_cast<long long>(plan->new_pages[f]), static_cast<long long>(free_[f].size()));
+      *err = buf;
+      return VK_ERR_CAPACITY;
+    }
+  }
+  return VK_OK;
+}
+
+void HostState::commit_append(AppendPlan* plan) {
+  const int32_t bs = cfg_.block_size;
+  for (AppendSeqDesc& d : plan->seqs) {
+    SeqState& st = seqs_[d.slot];
+    for (int32_t j = 0; j < d.n_pages; ++j) {
+      const int32_t p = d.page_first + j;
+      int32_t& e = plan->entries[d.page_off + j];
+      if (p < static_cast<int32_t>(st.pages.size())) continue;
+      const int f = entry_fmt(e);
+      const int32_t idx = free_[f].front();
+      free_[f].pop_front();
+      e = make_entry(f, idx);
+      st.pages.push_back(e);
+      if (st.runs.empty() || st.runs.back().second != f) st.runs.emplace_back(p, f);
+    }
+    st.length += plan->n_tokens;
+  }
+  (void)bs;
+}
+
+vk_status HostState::check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_t window, std::string* err) const {
+  if (n_seqs < 1) { *err = "n_seqs must be >= 1"; return VK_ERR_ARG; }
+  if (!seq_ids) { *err = "seq_ids is NULL"; return VK_ERR_ARG; }
+  if (window < -1) { *err = "window must be >= -1"; return VK_ERR_ARG; }
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t s = seq_ids[i];
+    if (s < 0 || s >= cfg_.max_seqs) { *err = fmt_str("seq id %lld out of range", s); return VK_ERR_ARG; }
+    if (seqs_[s].length < 1) { *err = fmt_str("seq %lld is empty", s); return VK_ERR_ARG; }
+  }
+  return VK_OK;
+}
+
+void HostState::count_units(int32_t slot, int32_t window, int64_t out[kFormats]) const {
+  const SeqState& st = seqs_[slot];
+  const UnitRanges r = attended_units(st.length, cfg_.sink_tokens, window);
+  const int64_t upp = cfg_.block_size / kUnit;
+  const int64_t n_pages = static_cast<int64_t>(st.pages.size());
+  for (size_t k = 0; k < st.runs.size(); ++k) {
+    const int64_t p0 = st.runs[k].first;
+    const int64_t p1 = k + 1 < st.runs.size() ? st.runs[k + 1].first : n_pages;
+    const int64_t u0 = p0 * upp, u1 = p1 * upp;
+    int64_t n = std::max<int64_t>(0, std::min<int64_t>(u1, r.a_end) - u0);
+    n += std::max<int64_t>(0, std::min<int64_t>(u1, r.b_end) - std::max<int64_t>(u0, r.b_begin));
+    out[st.runs[k].second] += n;
+  }
+}
+
+vk_status HostState::reset_seqs(int32_t n_seqs, const int32_t* seq_ids, std::string* err) {
+  if (n_seqs < 0 || (n_seqs > 0 && !seq_ids)) { *err = "bad seq list"; return VK_ERR_ARG; }
+  std::unordered_set<int32_t> seen;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (seq_ids[i] < 0 || seq_ids[i] >= cfg_.max_seqs) { *err = fmt_str("seq id %lld out of range", seq_ids[i]); return VK_ERR_ARG; }
+    if (!seen.insert(seq_ids[i]).second) { *err = fmt_str("seq id %lld repeated", seq_ids[i]); return VK_ERR_ARG; }
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    SeqState& st = seqs_[seq_ids[i]];
+    for (int32_t e : st.pages) free_[entry_fmt(e)].push_back(entry_idx(e));
+    st = SeqState();
+  }
+  return VK_OK;
+}
+
+int64_t HostState::pages_used(int fmt) const {
+  const int64_t caps[kFormats] = {cfg_.pages_ternary, cfg_.pages_fp8, cfg_.pages_f16};
+  return caps[fmt] - static_cast<int64_t>(free_[fmt].size());
+}
+
+int64_t HostState::tokens_stored(int fmt) const {
+  int64_t n = 0;
+  const int64_t bs = cfg_.block_size;
+  for (const SeqState& st : seqs_) {
+    for (size_t p = 0; p < st.pages.size(); ++p) {
+      if (entry_fmt(st.pages[p]) != fmt) continue;
+      n += std::min<int64_t>(bs, st.length - static_cast<int64_t>(p) * bs);
+    }
+  }
+  return n;
+}
+
+}  // namespace vk

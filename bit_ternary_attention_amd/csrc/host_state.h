@@ -1,0 +1,113 @@
+// Host-side cache state: configuration checks, page allocator, tier router,
+// append planner and decode planner.  Pure C++17, no HIP, so it can be built
+// and exercised on a machine without a GPU.
+//
+// Tiers follow "Minima-KV" (twodots.gr), section "Recent, Anchor and Stale":
+// recent pages in FP8, anchor pages (initial attention sinks) at higher
+// fidelity, older pages packed, every page addressable through the block table.
+#pragma once
+
+#include <cstdint>
+#include <deque>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "vk.h"
+
+namespace vk {
+
+constexpr int kFormats = 3;
+constexpr int kUnit = 16;          // tokens per unit: the decode and pack work granule
+constexpr int32_t kNoPage = -1;
+
+inline int32_t make_entry(int fmt, int32_t idx) {
+  return static_cast<int32_t>((static_cast<uint32_t>(fmt) << 30) | static_cast<uint32_t>(idx));
+}
+inline int entry_fmt(int32_t e) { return static_cast<int>(static_cast<uint32_t>(e) >> 30); }
+inline int32_t entry_idx(int32_t e) { return e & 0x3FFFFFFF; }
+
+// Returns "" when cfg is usable, else the reason.
+std::string validate_config(const vk_cache_config& cfg);
+// Bytes of one (K or V, one KV head) tile of a page of `fmt`.
+int64_t tile_bytes(const vk_cache_config& cfg, int fmt);
+// Bytes of a whole page (K and V, every KV head).
+int64_t page_bytes(const vk_cache_config& cfg, int fmt);
+
+// One sequence of an append call, as the device kernels read it.
+struct AppendSeqDesc {
+  int32_t slot;        // sequence id (block-table row)
+  int32_t t0;          // length before the call
+  int32_t tern_lo;     // ternary-routed tokens of the call: [tern_lo, tern_hi), call-relative
+  int32_t tern_hi;
+  int32_t page_first;  // first page the call touches
+  int32_t page_off;    // offset of that page's entry in the entry list
+  int32_t n_pages;     // pages touched
+  int32_t unit_first;  // first 16-token unit touched
+};
+static_assert(sizeof(AppendSeqDesc) == 32, "device layout");
+
+struct AppendPlan {
+  std::vector<AppendSeqDesc> seqs;
+  std::vector<int32_t> entries;     // block-table entries of every touched page, per seq
+  int32_t n_tokens = 0;             // tokens added to every sequence
+  int32_t max_units = 0;            // most 16-token units touched by one sequence
+  int32_t max_tern_tokens = 0;      // most ternary tokens in one sequence
+  int64_t new_pages[kFormats] = {0, 0, 0};
+  std::vector<int32_t> new_fmt;     // per new page, in order (seq, page)
+};
+
+struct SeqState {
+  int32_t length = 0;
+  std::vector<int32_t> pages;                       // entries of allocated pages
+  std::vector<std::pair<int32_t, int32_t>> runs;    // (first page, format) of same-format runs
+};
+
+// Attended 16-token units of a sequence: [0, a_end) and [b_begin, b_end).
+struct UnitRanges {
+  int32_t a_end = 0, b_begin = 0, b_end = 0;
+  int32_t sinks = 0;       // min(S, L)
+  int32_t w0 = 0;          // first window token
+  int32_t n_units() const { return a_end + (b_end - b_begin); }
+};
+UnitRanges attended_units(int32_t length, int32_t sink_tokens, int32_t window);
+
+// Split-K factor: enough work groups to fill the chip, at least `min_units` units per split.
+int32_t choose_splits(int64_t n_items, int32_t max_units, int32_t target_groups, int32_t max_splits,
+                      int32_t min_units);
+
+class HostState {
+ public:
+  explicit HostState(const vk_cache_config& cfg);
+
+  const vk_cache_config& cfg() const { return cfg_; }
+  int32_t max_pages() const { return max_pages_; }
+  const SeqState& seq(int32_t s) const { return seqs_[s]; }
+
+  // Format of page `page` when first written by an append ending at new_len.
+  int32_t new_page_format(int32_t page, int32_t new_len) const;
+
+  // Checks an append and computes what it needs.  Nothing changes.
+  vk_status plan_append(int32_t n_seqs, const int32_t* seq_ids, int32_t n_tokens, AppendPlan* plan,
+                        std::string* err) const;
+  // Takes the pages from the free lists, fills plan->entries, advances lengths.
+  void commit_append(AppendPlan* plan);
+
+  vk_status check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_t window, std::string* err) const;
+  // Attended units of `slot` by page format (route counters).
+  void count_units(int32_t slot, int32_t window, int64_t out[kFormats]) const;
+
+  vk_status reset_seqs(int32_t n_seqs, const int32_t* seq_ids, std::string* err);
+
+  int64_t pages_used(int fmt) const;
+  int64_t tokens_stored(int fmt) const;
+  int64_t free_pages(int fmt) const { return static_cast<int64_t>(free_[fmt].size()); }
+
+ private:
+  vk_cache_config cfg_;
+  int32_t max_pages_;
+  std::vector<SeqState> seqs_;
+  std::deque<int32_t> free_[kFormats];
+};
+
+}  // namespace vk

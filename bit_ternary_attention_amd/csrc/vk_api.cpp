@@ -1,0 +1,494 @@
+// C ABI of libvk.so (see include/vk.h).  Owns every device buffer; plans on
+// the host (host_state.cpp) and launches the HIP kernels (vk_write.hip,
+// vk_decode.hip) on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "host_state.h"
+#include "vk.h"
+#include "vk_params.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+vk_status fail(vk_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+constexpr int kRing = 4;                 // append plan staging slots
+constexpr int64_t kMaxPartials = 1 << 20;  // float64 absmean partials per append call
+constexpr int64_t kMaxSegs = 65535;        // (layer, seq, K|V) segments per append call (grid y)
+constexpr int kDecodeTargetGroups = 4096;  // work groups a decode launch aims for
+constexpr int kDecodeMaxSplits = 64;
+constexpr int kDecodeMinUnits = 8;         // 16-token units per split, at least
+constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
+
+}  // namespace
+
+struct vk_cache {
+  vk_cache_config cfg;
+  std::unique_ptr<vk::HostState> host;
+  int device = 0;
+  bool poisoned = false;
+  vk::PoolsView pools{};
+  double* partials = nullptr;
+  vk::SegInfo* seg = nullptr;
+  float* dec_partials = nullptr;
+  int64_t plan_bytes = 0;
+  uint8_t* plan_host[kRing] = {};
+  uint8_t* plan_dev[kRing] = {};
+  hipEvent_t plan_ev[kRing] = {};
+  bool plan_ev_used[kRing] = {};
+  int ring_next = 0;
+  int64_t device_bytes = 0;
+  std::vector<void*> allocations;
+  vk_stats stats{};
+};
+
+namespace {
+
+vk_status hip_fail(vk_cache* c, hipError_t e, const char* what) {
+  if (c) c->poisoned = true;
+  return fail(VK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t partial_count(const vk_cache_config& cfg) {
+  const int g = cfg.n_q_heads / cfg.n_kv_heads;
+  return kDecodeScratchItems * g * (cfg.head_dim + 2);
+}
+
+int64_t plan_bytes_for(const vk_cache_config& cfg) {
+  const int64_t max_pages = (cfg.max_tokens_per_seq + cfg.block_size - 1) / cfg.block_size;
+  const int64_t b = static_cast<int64_t>(cfg.max_seqs) * (sizeof(vk::AppendSeqDesc) + 4 * (max_pages + 1));
+  return (b + 255) & ~int64_t(255);
+}
+
+// Device bytes of every buffer vk_create_cache allocates, in allocation order.
+std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
+  std::vector<int64_t> s;
+  const int64_t caps[3] = {cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16};
+  for (int f = 0; f < 3; ++f) s.push_back(static_cast<int64_t>(cfg.n_layers) * caps[f] * vk::page_bytes(cfg, f));
+  s.push_back(static_cast<int64_t>(cfg.n_layers) * caps[0] * 2 * 4);  // gamma
+  const int64_t max_pages = (cfg.max_tokens_per_seq + cfg.block_size - 1) / cfg.block_size;
+  s.push_back(static_cast<int64_t>(cfg.max_seqs) * max_pages * 4);    // block table
+  s.push_back(kMaxPartials * 8);                                      // absmean partials
+  s.push_back(kMaxSegs * static_cast<int64_t>(sizeof(vk::SegInfo)));  // segment info
+  s.push_back(partial_count(cfg) * 4);                                // decode split partials
+  for (int r = 0; r < kRing; ++r) s.push_back(plan_bytes_for(cfg));   // staged plans
+  return s;
+}
+
+void free_all(vk_cache* c) {
+  for (void* p : c->allocations) (void)hipFree(p);
+  c->allocations.clear();
+  for (int r = 0; r < kRing; ++r) {
+    if (c->plan_host[r]) (void)hipHostFree(c->plan_host[r]);
+    if (c->plan_ev[r]) (void)hipEventDestroy(c->plan_ev[r]);
+    c->plan_host[r] = nullptr;
+    c->plan_ev[r] = nullptr;
+  }
+}
+
+vk_status check_handle(vk_cache* c) {
+  if (!c) return fail(VK_ERR_ARG, "cache handle is NULL");
+  if (c->poisoned) return fail(VK_ERR_STATE, "cache handle poisoned by an earlier HIP failure");
+  return VK_OK;
+}
+
+vk_status set_device(vk_cache* c) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(c, e, "hipGetDevice");
+  if (cur != c->device) {
+    e = hipSetDevice(c->device);
+    if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+  }
+  return VK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+VK_API void vk_config_defaults(vk_cache_config* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof *cfg);
+  cfg->sink_tokens = 4;
+  cfg->sink_format = VK_FMT_TERNARY2;
+  cfg->recent_tokens = 0;
+  cfg->recent_format = VK_FMT_FP8E4M3;
+  cfg->eps = 1e-5f;
+  cfg->fp8_scale = 1.0f;
+}
+
+VK_API vk_status vk_cache_device_bytes(const vk_cache_config* cfg, int64_t* bytes) {
+  if (!cfg || !bytes) return fail(VK_ERR_ARG, "NULL argument");
+  const std::string why = vk::validate_config(*cfg);
+  if (!why.empty()) return fail(VK_ERR_ARG, "%s", why.c_str());
+  int64_t total = 0;
+  for (int64_t s : buffer_sizes(*cfg)) total += s;
+  *bytes = total;
+  return VK_OK;
+}
+
+VK_API int64_t vk_page_bytes(const vk_cache_config* cfg, int32_t fmt) {
+  if (!cfg || fmt < 0 || fmt > 2 || !vk::validate_config(*cfg).empty()) return 0;
+  return vk::page_bytes(*cfg, fmt);
+}
+
+VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
+  if (!cfg || !out) return fail(VK_ERR_ARG, "NULL argument");
+  const std::string why = vk::validate_config(*cfg);
+  if (!why.empty()) return fail(VK_ERR_ARG, "%s", why.c_str());
+  std::unique_ptr<vk_cache> c(new vk_cache());
+  c->cfg = *cfg;
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) return fail(VK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  const std::vector<int64_t> sizes = buffer_sizes(*cfg);
+  std::vector<void*> ptrs(sizes.size(), nullptr);
+  for (size_t i = 0; i < sizes.size(); ++i) {
+    if (sizes[i] == 0) continue;
+    e = hipMalloc(&ptrs[i], static_cast<size_t>(sizes[i]));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      c->allocations = ptrs;
+      free_all(c.get());
+      return fail(VK_ERR_OOM, "hipMalloc of %lld bytes failed: %s", static_cast<long long>(sizes[i]),
+                  hipGetErrorString(e));
+    }
+    c->device_bytes += sizes[i];
+  }
+  c->allocations = ptrs;
+  // pools and gamma start zeroed (finite bytes everywhere); the block table starts empty
+  for (size_t i = 0; i < 4; ++i)
+    if (ptrs[i]) {
+      e = hipMemset(ptrs[i], 0, static_cast<size_t>(sizes[i]));
+      if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)); }
+    }
+  e = hipMemset(ptrs[4], 0xFF, static_cast<size_t>(sizes[4]));
+  if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)); }
+  vk::PoolsView& P = c->pools;
+  const int64_t caps[3] = {cfg->pages_ternary, cfg->pages_fp8, cfg->pages_f16};
+  for (int f = 0; f < 3; ++f) {
+    P.pool[f] = static_cast<uint8_t*>(ptrs[f]);
+    P.cap[f] = caps[f];
+    P.tile_bytes[f] = vk::tile_bytes(*cfg, f);
+    P.page_bytes[f] = vk::page_bytes(*cfg, f);
+  }
+  P.gamma = static_cast<float*>(ptrs[3]);
+  P.block_table = static_cast<int32_t*>(ptrs[4]);
+  P.max_pages = static_cast<int32_t>((cfg->max_tokens_per_seq + cfg->block_size - 1) / cfg->block_size);
+  P.n_layers = cfg->n_layers;
+  P.hkv = cfg->n_kv_heads;
+  P.dim = cfg->head_dim;
+  P.bs = cfg->block_size;
+  P.bs_shift = 0;
+  while ((1 << P.bs_shift) < cfg->block_size) ++P.bs_shift;
+  P.fp8_scale = cfg->fp8_scale;
+  c->partials = static_cast<double*>(ptrs[5]);
+  c->seg = static_cast<vk::SegInfo*>(ptrs[6]);
+  c->dec_partials = static_cast<float*>(ptrs[7]);
+  c->plan_bytes = plan_bytes_for(*cfg);
+  for (int r = 0; r < kRing; ++r) {
+    c->plan_dev[r] = static_cast<uint8_t*>(ptrs[8 + r]);
+    e = hipHostMalloc(reinterpret_cast<void**>(&c->plan_host[r]), static_cast<size_t>(c->plan_bytes), 0);
+    if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_OOM, "hipHostMalloc: %s", hipGetErrorString(e)); }
+    e = hipEventCreateWithFlags(&c->plan_ev[r], hipEventDisableTiming);
+    if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e)); }
+  }
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e)); }
+  c->host.reset(new vk::HostState(*cfg));
+  c->stats.device_bytes = c->device_bytes;
+  for (int f = 0; f < 3; ++f) c->stats.pool_pages[f] = caps[f];
+  *out = c.release();
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                           const int32_t* seq_ids, int32_t n_tokens, const void* k, const void* v,
+                           int32_t dtype, void* stream) {
+  vk_status st = check_handle(c);
+  if (st) return st;
+  const vk_cache_config& cfg = c->cfg;
+  if (n_layers < 1 || layer_begin < 0 || layer_begin + static_cast<int64_t>(n_layers) > cfg.n_layers)
+    return fail(VK_ERR_ARG, "layer span [%d, %d) outside [0, %d)", layer_begin, layer_begin + n_layers, cfg.n_layers);
+  if (dtype != VK_DTYPE_F16 && dtype != VK_DTYPE_BF16) return fail(VK_ERR_ARG, "dtype must be F16 or BF16");
+  if (!k || !v) return fail(VK_ERR_ARG, "k or v is NULL");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+    return fail(VK_ERR_ARG, "k and v must be 16-byte aligned");
+  vk::AppendPlan plan;
+  std::string err;
+  st = c->host->plan_append(n_seqs, seq_ids, n_tokens, &plan, &err);
+  if (st) return fail(st, "%s", err.c_str());
+  const int64_t n_seg = static_cast<int64_t>(n_layers) * n_seqs * 2;
+  const int64_t row = static_cast<int64_t>(cfg.n_kv_heads) * cfg.head_dim;
+  const int64_t n_blk = (static_cast<int64_t>(plan.max_tern_tokens) * row + vk::kAbsElemsPerBlock - 1) /
+                        vk::kAbsElemsPerBlock;
+  if (n_seg > kMaxSegs || n_seg * n_blk > kMaxPartials)
+    return fail(VK_ERR_ARG, "append too large for one call (%lld segments x %lld blocks); split it",
+                static_cast<long long>(n_seg), static_cast<long long>(n_blk));
+  if (n_blk > 65535) return fail(VK_ERR_ARG, "too many tokens in one call");
+  if (static_cast<int64_t>(n_layers) * n_seqs > 65535) return fail(VK_ERR_ARG, "n_layers * n_seqs must be <= 65535");
+  const int64_t need = static_cast<int64_t>(plan.seqs.size()) * sizeof(vk::AppendSeqDesc) +
+                       static_cast<int64_t>(plan.entries.size()) * 4;
+  if (need > c->plan_bytes) return fail(VK_ERR_ARG, "append plan too large");
+  st = set_device(c);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int slot = c->ring_next;
+  c->ring_next = (c->ring_next + 1) % kRing;
+  hipError_t e = hipSuccess;
+  if (c->plan_ev_used[slot]) {
+    e = hipEventSynchronize(c->plan_ev[slot]);
+    if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
+  }
+  // from here on the host state changes: any failure poisons the handle
+  c->host->commit_append(&plan);
+  uint8_t* hp = c->plan_host[slot];
+  const size_t desc_bytes = plan.seqs.size() * sizeof(vk::AppendSeqDesc);
+  std::memcpy(hp, plan.seqs.data(), desc_bytes);
+  std::memcpy(hp + desc_bytes, plan.entries.data(), plan.entries.size() * 4);
+  e = hipMemcpyAsync(c->plan_dev[slot], hp, static_cast<size_t>(need), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync");
+  vk::AppendArgs a{};
+  a.P = c->pools;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.descs = reinterpret_cast<const vk::AppendSeqDesc*>(c->plan_dev[slot]);
+  a.entries = reinterpret_cast<const int32_t*>(c->plan_dev[slot] + desc_bytes);
+  a.partials = c->partials;
+  a.seg = c->seg;
+  a.dtype = dtype;
+  a.layer_begin = layer_begin;
+  a.n_layers = n_layers;
+  a.n_seqs = n_seqs;
+  a.n_tokens = n_tokens;
+  a.n_blk = static_cast<int32_t>(n_blk);
+  a.max_units = plan.max_units;
+  a.eps = cfg.eps;
+  e = vk::launch_append(a, static_cast<int32_t>(n_seg), s);
+  if (e != hipSuccess) return hip_fail(c, e, "append kernels");
+  e = hipEventRecord(c->plan_ev[slot], s);
+  if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
+  c->plan_ev_used[slot] = true;
+  c->stats.append_calls += 1;
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q,
+                                int32_t q_dtype, int32_t window, float softmax_scale, float* out, void* stream) {
+  vk_status st = check_handle(c);
+  if (st) return st;
+  const vk_cache_config& cfg = c->cfg;
+  if (layer < 0 || layer >= cfg.n_layers) return fail(VK_ERR_ARG, "layer %d out of range", layer);
+  if (q_dtype != VK_DTYPE_F16 && q_dtype != VK_DTYPE_BF16) return fail(VK_ERR_ARG, "q_dtype must be F16 or BF16");
+  if (!q || !out) return fail(VK_ERR_ARG, "q or out is NULL");
+  if ((reinterpret_cast<uintptr_t>(q) & 3) || (reinterpret_cast<uintptr_t>(out) & 15))
+    return fail(VK_ERR_ARG, "q must be 4-byte and out 16-byte aligned");
+  if (!std::isfinite(softmax_scale)) return fail(VK_ERR_ARG, "softmax_scale must be finite");
+  if (cfg.sink_tokens == 0 && window == 0) return fail(VK_ERR_ARG, "no sinks and window 0 attend nothing");
+  std::string err;
+  st = c->host->check_decode(n_seqs, seq_ids, window, &err);
+  if (st) return fail(st, "%s", err.c_str());
+  st = set_device(c);
+  if (st) return st;
+  const int g = cfg.n_q_heads / cfg.n_kv_heads;
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t units[3] = {0, 0, 0};
+  int32_t splits_used = 1;
+  for (int32_t base = 0; base < n_seqs; base += vk::kDecodeMaxSeqs) {
+    const int32_t nb = std::min<int32_t>(vk::kDecodeMaxSeqs, n_seqs - base);
+    vk::DecodeArgs a{};
+    a.P = c->pools;
+    a.q = static_cast<const uint16_t*>(q) + static_cast<int64_t>(base) * cfg.n_q_heads * cfg.head_dim;
+    a.out = out + static_cast<int64_t>(base) * cfg.n_q_heads * cfg.head_dim;
+    a.partials = c->dec_partials;
+    a.q_dtype = q_dtype;
+    a.layer = layer;
+    a.n_seqs = nb;
+    a.hq = cfg.n_q_heads;
+    a.sink_tokens = cfg.sink_tokens;
+    a.window = window;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    int32_t max_units = 0;
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t sid = seq_ids[base + i];
+      a.slots[i] = sid;
+      a.lens[i] = c->host->seq(sid).length;
+      max_units = std::max(max_units, vk::attended_units(a.lens[i], cfg.sink_tokens, window).n_units());
+      c->host->count_units(sid, window, units);
+    }
+    const int64_t items = static_cast<int64_t>(nb) * cfg.n_kv_heads;
+    const int32_t max_splits =
+        static_cast<int32_t>(std::min<int64_t>(kDecodeMaxSplits, kDecodeScratchItems / items));
+    a.n_splits = vk::choose_splits(items, max_units, kDecodeTargetGroups, std::max(1, max_splits), kDecodeMinUnits);
+    splits_used = a.n_splits;
+    hipError_t e = vk::launch_decode(a, g, s);
+    if (e != hipSuccess) return hip_fail(c, e, "decode kernels");
+  }
+  c->stats.decode_calls += 1;
+  c->stats.last_decode_splits = splits_used;
+  for (int f = 0; f < 3; ++f) {
+    c->stats.last_decode_units[f] = units[f];
+    c->stats.total_decode_units[f] += units[f];
+  }
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API vk_status vk_reset_seqs(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, void* stream) {
+  vk_status st = check_handle(c);
+  if (st) return st;
+  std::string err;
+  // validate before waiting
+  if (n_seqs < 0 || (n_seqs > 0 && !seq_ids)) return fail(VK_ERR_ARG, "bad sequence list");
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (seq_ids[i] < 0 || seq_ids[i] >= c->cfg.max_seqs) return fail(VK_ERR_ARG, "seq id %d out of range", seq_ids[i]);
+  st = set_device(c);
+  if (st) return st;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  st = c->host->reset_seqs(n_seqs, seq_ids, &err);
+  if (st) return fail(st, "%s", err.c_str());
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API vk_status vk_seq_length(vk_cache* c, int32_t seq, int32_t* length) {
+  if (!c || !length) return fail(VK_ERR_ARG, "NULL argument");
+  if (seq < 0 || seq >= c->cfg.max_seqs) return fail(VK_ERR_ARG, "seq id %d out of range", seq);
+  *length = c->host->seq(seq).length;
+  return VK_OK;
+}
+
+VK_API vk_status vk_read_pages(vk_cache* c, int32_t layer, int32_t seq, int32_t page0, int32_t n_pages,
+                               uint8_t* host_bytes, int32_t* host_fmt, float* host_gamma) {
+  vk_status st = check_handle(c);
+  if (st) return st;
+  const vk_cache_config& cfg = c->cfg;
+  if (layer < 0 || layer >= cfg.n_layers) return fail(VK_ERR_ARG, "layer out of range");
+  if (seq < 0 || seq >= cfg.max_seqs) return fail(VK_ERR_ARG, "seq out of range");
+  const vk::SeqState& ss = c->host->seq(seq);
+  if (page0 < 0 || n_pages < 0 || page0 + static_cast<int64_t>(n_pages) > static_cast<int64_t>(ss.pages.size()))
+    return fail(VK_ERR_ARG, "pages [%d, %d) not allocated", page0, page0 + n_pages);
+  if (n_pages > 0 && (!host_bytes || !host_fmt || !host_gamma)) return fail(VK_ERR_ARG, "NULL output");
+  st = set_device(c);
+  if (st) return st;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(c, e, "hipDeviceSynchronize");
+  const int64_t stride = vk::page_bytes(cfg, VK_FMT_F16);
+  for (int32_t j = 0; j < n_pages; ++j) {
+    const int32_t ent = ss.pages[page0 + j];
+    const int f = vk::entry_fmt(ent);
+    const int64_t idx = vk::entry_idx(ent);
+    const uint8_t* src = c->pools.pool[f] + (static_cast<int64_t>(layer) * c->pools.cap[f] + idx) * c->pools.page_bytes[f];
+    e = hipMemcpy(host_bytes + j * stride, src, static_cast<size_t>(c->pools.page_bytes[f]), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(c, e, "hipMemcpy");
+    host_fmt[j] = f;
+    if (f == VK_FMT_TERNARY2) {
+      e = hipMemcpy(host_gamma + 2 * j, c->pools.gamma + (static_cast<int64_t>(layer) * c->pools.cap[0] + idx) * 2, 8,
+                    hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(c, e, "hipMemcpy");
+    } else {
+      host_gamma[2 * j] = host_gamma[2 * j + 1] = std::nanf("");
+    }
+  }
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out) {
+  if (!c || !out) return fail(VK_ERR_ARG, "NULL argument");
+  vk_stats s = c->stats;
+  for (int f = 0; f < 3; ++f) {
+    s.pages_used[f] = c->host->pages_used(f);
+    s.tokens_stored[f] = c->host->tokens_stored(f);
+  }
+  *out = s;
+  return VK_OK;
+}
+
+VK_API vk_status vk_release(vk_cache* c) {
+  if (!c) return VK_OK;
+  vk_status st = VK_OK;
+  int cur = -1;
+  if (hipGetDevice(&cur) == hipSuccess && cur != c->device) (void)hipSetDevice(c->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) st = fail(VK_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  free_all(c);
+  if (cur >= 0 && cur != c->device) (void)hipSetDevice(cur);
+  delete c;
+  return st;
+}
+
+VK_API int64_t vk_quantize_pack_workspace_bytes(int64_t n) {
+  if (n < 0) return 0;
+  const int64_t n_blk = (n + vk::kAbsElemsPerBlock - 1) / vk::kAbsElemsPerBlock;
+  return 256 + ((n_blk * 8 + 255) & ~int64_t(255));
+}
+
+VK_API vk_status vk_quantize_pack(const void* x, int64_t n, int32_t dtype, float eps, const float* gamma_in,
+                                  uint8_t* packed, float* gamma_out, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  if (!x || !packed || !gamma_out || !workspace) return fail(VK_ERR_ARG, "NULL argument");
+  if (n < 8 || n % 8) return fail(VK_ERR_ARG, "n must be a positive multiple of 8");
+  if (dtype != VK_DTYPE_F16 && dtype != VK_DTYPE_BF16) return fail(VK_ERR_ARG, "dtype must be F16 or BF16");
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(VK_ERR_ARG, "eps must be finite and >= 0");
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(packed) & 1) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return fail(VK_ERR_ARG, "x and workspace must be 16-byte aligned, packed 2-byte aligned");
+  if (workspace_bytes < vk_quantize_pack_workspace_bytes(n)) return fail(VK_ERR_ARG, "workspace too small");
+  const int64_t n_blk = (n + vk::kAbsElemsPerBlock - 1) / vk::kAbsElemsPerBlock;
+  if (n_blk > 0x7FFFFFFF) return fail(VK_ERR_ARG, "tensor too large");
+  vk::QuantArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.packed = packed;
+  a.gamma_in = gamma_in;
+  a.gamma_out = gamma_out;
+  a.seg = static_cast<vk::SegInfo*>(workspace);
+  a.partials = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + 256);
+  a.n = n;
+  a.dtype = dtype;
+  a.n_blk = static_cast<int32_t>(n_blk);
+  a.eps = eps;
+  hipError_t e = vk::launch_quantize(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VK_ERR_HIP, "quantize kernels: %s", hipGetErrorString(e));
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API const char* vk_last_error(void) { return g_error.c_str(); }
+
+VK_API const char* vk_status_string(vk_status s) {
+  switch (s) {
+    case VK_OK: return "VK_OK";
+    case VK_ERR_ARG: return "VK_ERR_ARG";
+    case VK_ERR_OOM: return "VK_ERR_OOM";
+    case VK_ERR_CAPACITY: return "VK_ERR_CAPACITY";
+    case VK_ERR_ALIGN: return "VK_ERR_ALIGN";
+    case VK_ERR_STATE: return "VK_ERR_STATE";
+    case VK_ERR_HIP: return "VK_ERR_HIP";
+  }
+  return "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Kernel argument blocks and launchers shared by the host API and the HIP
+// kernels.  Everything here is plain data passed by value.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace vk {
+
+struct AppendSeqDesc;  // host_state.h
+
+// Device view of the paged pools.  Page `idx` of format f in layer `layer`:
+//   pool[f] + (layer * cap[f] + idx) * page_bytes[f]
+// with the page laid out [K tile head 0..Hkv-1][V tile head 0..Hkv-1].
+struct PoolsView {
+  uint8_t* pool[3];
+  float* gamma;            // [n_layers][cap[0]][2]: K and V gamma of ternary pages
+  int32_t* block_table;    // [max_seqs][max_pages]: (format << 30) | pool index
+  int64_t cap[3];          // pages per layer
+  int64_t tile_bytes[3];   // one (K|V, head) tile
+  int64_t page_bytes[3];
+  int32_t max_pages;
+  int32_t n_layers;
+  int32_t hkv;
+  int32_t dim;
+  int32_t bs;              // tokens per page (power of two)
+  int32_t bs_shift;        // log2(bs)
+  float fp8_scale;
+  int32_t pad;
+};
+
+struct SegInfo {           // per (layer, seq, K|V) of one append call
+  float gamma;             // mean |x| of the ternary-routed tokens, float32
+  uint32_t thresh;         // smallest 16-bit magnitude whose code is nonzero
+};
+
+constexpr int kAbsThreads = 256;
+constexpr int kAbsElemsPerThreadIter = 8;       // one 16-byte load
+constexpr int kAbsIters = 8;
+constexpr int kAbsElemsPerBlock = kAbsThreads * kAbsElemsPerThreadIter * kAbsIters;
+
+struct AppendArgs {
+  PoolsView P;
+  const uint16_t* k;       // [n_layers][n_seqs][n_tokens][hkv][dim]
+  const uint16_t* v;
+  const AppendSeqDesc* descs;
+  const int32_t* entries;
+  double* partials;        // [n_seg][n_blk]
+  SegInfo* seg;            // [n_seg]
+  int32_t dtype;           // 0 f16, 1 bf16
+  int32_t layer_begin;
+  int32_t n_layers;
+  int32_t n_seqs;
+  int32_t n_tokens;
+  int32_t n_blk;           // absmean blocks per segment
+  int32_t max_units;       // most 16-token units touched by one sequence
+  float eps;
+};
+
+constexpr int kDecodeMaxSeqs = 64;    // sequences per decode launch (kernel-argument table)
+constexpr int kDecodeUnitsPerIter = 4;
+
+struct DecodeArgs {
+  PoolsView P;
+  const uint16_t* q;       // [n_seqs][hq][dim]
+  float* out;              // [n_seqs][hq][dim]
+  float* partials;         // [n_seqs][hq][n_splits][dim + 2]
+  int32_t q_dtype;
+  int32_t layer;
+  int32_t n_seqs;          // in this launch (<= kDecodeMaxSeqs)
+  int32_t hq;
+  int32_t sink_tokens;
+  int32_t window;
+  int32_t n_splits;
+  float scale_log2;        // softmax scale * log2(e)
+  int32_t slots[kDecodeMaxSeqs];
+  int32_t lens[kDecodeMaxSeqs];
+};
+
+struct QuantArgs {
+  const uint16_t* x;
+  uint8_t* packed;
+  const float* gamma_in;   // NULL: compute
+  float* gamma_out;
+  double* partials;        // [n_blk]
+  SegInfo* seg;            // [1]
+  int64_t n;
+  int32_t dtype;
+  int32_t n_blk;
+  float eps;
+};
+
+// Launchers (vk_write.hip, vk_decode.hip).  Return the first HIP error.
+hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+}  // namespace vk

@@ -1,0 +1,449 @@
+// Write side: per-tensor absmean scale, ternary quantisation, 2-bit packing
+// and page scatter, for gfx950.
+//
+// Follows "Show HN: Vantage-V-AI" (newshot.cc), section "core architecture":
+// gamma = mean(|X|) per tensor, states {-1, 0, +1}, four elements per uint8.
+// FP8 recent pages and FP16 anchor (sink) pages follow "Minima-KV"
+// (twodots.gr), section "Recent, Anchor and Stale".
+//
+// Three kernels per append call:
+//   k_absmean_partial  pass 1: fixed-partition float64 sums of |x|, one per
+//                      (segment, 32 KiB block), no atomics -> deterministic
+//   k_gamma_finalize   one wave per segment: fixed-order sum, gamma = fp32(S/N),
+//                      and the exact 16-bit magnitude threshold of a nonzero code
+//   k_pack             pass 2: one wave per (16-token unit, K|V, head) tile;
+//                      codes from an integer compare against the threshold,
+//                      keys stored token-major, values transposed through LDS
+//
+// Exactness of the threshold: with d = gamma + eps > 0 and RNE float32
+// division, round(x/d) is nonzero exactly when the float32 quotient exceeds
+// 1/2, i.e. when |x|/d > 1/2 + 2^-25 (the midpoint to the next float32 above
+// 1/2; a tie rounds to 1/2, whose significand is even).  d * (1/2 + 2^-25)
+// is exact in float64 (24 + 25 significand bits), so no division is needed
+// and the compare is exact.  The magnitude order of 16-bit patterns equals
+// their value order, so the compare runs on the raw bits.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "host_state.h"
+#include "vk_params.h"
+
+namespace vk {
+namespace {
+
+template <int DT>
+__device__ __forceinline__ float to_f32(uint32_t h) {  // low 16 bits
+  if (DT == 1) return __uint_as_float(h << 16);
+  return __half2float(__ushort_as_half(static_cast<unsigned short>(h)));
+}
+
+// Sum of |x| over the eight 16-bit values of a 16-byte load, in float64.
+template <int DT>
+__device__ __forceinline__ double abs_sum8(uint4 w) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    s += static_cast<double>(fabsf(to_f32<DT>(ws[k] & 0xFFFFu)));
+    s += static_cast<double>(fabsf(to_f32<DT>(ws[k] >> 16)));
+  }
+  return s;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Fixed-order block reduction (256 threads = 4 waves).
+__device__ __forceinline__ double block_sum256(double x) {
+  __shared__ double part[4];
+  x = wave_sum(x);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[wave] = x;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) t = ((part[0] + part[1]) + part[2]) + part[3];
+  return t;
+}
+
+// Exact value of a non-negative 16-bit magnitude pattern.
+template <int DT>
+__device__ double value16(uint32_t m) {
+  if (DT == 1) return static_cast<double>(__uint_as_float(m << 16));
+  const uint32_t e = m >> 10, f = m & 0x3FFu;
+  if (e == 0) return ldexp(static_cast<double>(f), -24);
+  if (e == 31) return __longlong_as_double(0x7FF0000000000000ll);
+  return ldexp(static_cast<double>(f + 1024u), static_cast<int>(e) - 25);
+}
+
+// Smallest magnitude pattern m with value(m) > d * (1/2 + 2^-25): codes are
+// nonzero exactly for |x| >= value(m).  Searches up to the infinity pattern.
+template <int DT>
+__device__ uint32_t threshold16(float d) {
+  const double tau = static_cast<double>(d) * (0.5 + 0x1p-25);
+  uint32_t lo = 0, hi = DT == 1 ? 0x7F80u : 0x7C00u;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (value16<DT>(mid) > tau) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+template <int DT>
+__device__ __forceinline__ SegInfo finalize(double s, int64_t n, float eps) {
+  SegInfo info;
+  if (n == 0) {
+    info.gamma = 0.0f;
+    info.thresh = 0x8000u;  // no magnitude reaches it: every code 0 (never read)
+    return info;
+  }
+  info.gamma = static_cast<float>(s / static_cast<double>(n));
+  const float d = info.gamma + eps;  // float32, as the encoding defines it
+  info.thresh = threshold16<DT>(d);
+  return info;
+}
+
+// 2-bit fields (code + 1) of eight 16-bit inputs, element e at bits 2e.
+// u = 1 + nz - 2*nz*neg per 16-bit half: nz = (|x| >= T), neg = sign bit.
+__device__ __forceinline__ uint32_t code_word8(uint4 w, uint32_t thresh) {
+  const uint32_t add = (0x8000u - thresh) * 0x00010001u;  // halves never carry: <= 0x7FFF + 0x7FFF
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t y = (ws[k] & 0x7FFF7FFFu) + add;
+    const uint32_t nz = (y >> 15) & 0x00010001u;
+    const uint32_t ng = (ws[k] >> 15) & 0x00010001u;
+    const uint32_t u = 0x00010001u + nz - ((nz & ng) << 1);
+    out |= ((u | (u >> 14)) & 0xFu) << (4 * k);
+  }
+  return out;
+}
+
+// OCP e4m3fn of a float32, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3fn_rne(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = static_cast<uint32_t>(rintf(a * 512.0f));  // subnormal steps of 2^-9 (8 -> min normal)
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t m3 = (b >> 20) & 7u, rest = b & 0xFFFFFu;
+    code = ((((b >> 23) - 120u) << 3) | m3);
+    if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) code += 1;  // carry into exponent is right
+  }
+  return sign | code;
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t to_f16_bits(uint32_t h) {
+  if (DT == 0) return h;
+  return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(to_f32<1>(h))));
+}
+
+// ------------------------------------------------------------- pass 1 ---
+
+template <int DT>
+__global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(AppendArgs a) {
+  const int seg = blockIdx.y, blk = blockIdx.x;
+  const int kv = seg & 1, li = seg >> 1;
+  const int i = li % a.n_seqs, l_rel = li / a.n_seqs;
+  const AppendSeqDesc d = a.descs[i];
+  const int64_t row = static_cast<int64_t>(a.P.hkv) * a.P.dim;
+  const int64_t n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * row;
+  const uint16_t* base =
+      (kv ? a.v : a.k) + ((static_cast<int64_t>(l_rel) * a.n_seqs + i) * a.n_tokens + d.tern_lo) * row;
+  const int64_t start = static_cast<int64_t>(blk) * kAbsElemsPerBlock;
+  uint4 w[kAbsIters];
+#pragma unroll
+  for (int it = 0; it < kAbsIters; ++it) {
+    const int64_t e = start + (static_cast<int64_t>(it) * kAbsThreads + threadIdx.x) * kAbsElemsPerThreadIter;
+    w[it] = e < n ? *reinterpret_cast<const uint4*>(base + e) : make_uint4(0, 0, 0, 0);
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int it = 0; it < kAbsIters; ++it) acc += abs_sum8<DT>(w[it]);
+  const double total = block_sum256(acc);
+  if (threadIdx.x == 0) a.partials[static_cast<int64_t>(seg) * a.n_blk + blk] = total;
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void k_gamma_finalize(AppendArgs a) {
+  const int seg = blockIdx.x;
+  const int i = (seg >> 1) % a.n_seqs;
+  const AppendSeqDesc d = a.descs[i];
+  const int64_t n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * a.P.hkv * a.P.dim;
+  double s = 0.0;
+  for (int j = threadIdx.x; j < a.n_blk; j += 64) s += a.partials[static_cast<int64_t>(seg) * a.n_blk + j];
+  s = wave_sum(s);
+  if (threadIdx.x == 0) a.seg[seg] = finalize<DT>(s, n, a.eps);
+}
+
+// ------------------------------------------------------------- pass 2 ---
+
+template <int DT, int D>
+__global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
+  constexpr int CPR = D / 8;     // 16-byte chunks per token row
+  constexpr int RPI = 64 / CPR;  // rows per wave-wide load
+  constexpr int NI = 16 / RPI;   // loads per lane per unit
+  constexpr int DPL = D / 64;    // head dims per lane in the transposed value store
+  __shared__ uint32_t lds[D * 16 * 2 / 4 + 4];
+  uint16_t* lds16 = reinterpret_cast<uint16_t*>(lds);
+  uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
+
+  const int lane = threadIdx.x;
+  const int li = blockIdx.y;
+  const int i = li % a.n_seqs, l_rel = li / a.n_seqs;
+  const int layer = a.layer_begin + l_rel;
+  const AppendSeqDesc d = a.descs[i];
+  const int hkv = a.P.hkv;
+  const int64_t row = static_cast<int64_t>(hkv) * D;
+  const int t1 = d.t0 + a.n_tokens;
+  const int n_tasks = a.max_units * 2 * hkv;
+  const int c = lane % CPR, rg = lane / CPR;
+
+  for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
+    const int h = task % hkv;
+    const int kv = (task / hkv) & 1;
+    const int uk = task / (2 * hkv);
+    const int unit = d.unit_first + uk;
+    if (unit * 16 >= t1) continue;  // uniform over the block
+    const int pos0 = unit * 16;
+    const int page = pos0 >> a.P.bs_shift;
+    const int upi = (pos0 & (a.P.bs - 1)) >> 4;
+    const int32_t entry = a.entries[d.page_off + page - d.page_first];
+    const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
+    const int64_t idx = entry & 0x3FFFFFFF;
+    uint8_t* tile = a.P.pool[fmt] + (static_cast<int64_t>(layer) * a.P.cap[fmt] + idx) * a.P.page_bytes[fmt] +
+                    static_cast<int64_t>(kv * hkv + h) * a.P.tile_bytes[fmt];
+    const uint16_t* src =
+        (kv ? a.v : a.k) + (static_cast<int64_t>(l_rel) * a.n_seqs + i) * a.n_tokens * row + h * D + c * 8;
+
+    if (l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
+      a.P.block_table[static_cast<int64_t>(d.slot) * a.P.max_pages + page] = entry;
+
+    uint4 w[NI];
+    bool ok[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int r = rg * NI + k;
+      const int j = pos0 + r - d.t0;  // call-relative token
+      ok[k] = j >= 0 && j < a.n_tokens;
+      w[k] = ok[k] ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * row) : make_uint4(0, 0, 0, 0);
+    }
+
+    if (fmt == VK_FMT_TERNARY2) {
+      const SegInfo si = a.seg[(l_rel * a.n_seqs + i) * 2 + kv];
+      if (upi == 0 && h == 0 && lane == 0)
+        a.P.gamma[(static_cast<int64_t>(layer) * a.P.cap[0] + idx) * 2 + kv] = si.gamma;
+      if (kv == 0) {
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+          const int r = rg * NI + k;
+          const uint32_t cw = code_word8(w[k], si.thresh);
+          *reinterpret_cast<uint16_t*>(tile + (upi * 16 + r) * (D / 4) + 2 * c) = static_cast<uint16_t>(cw);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+          const int r = rg * NI + k;
+          lds16[c * 16 + r] = static_cast<uint16_t>(code_word8(w[k], si.thresh));
+        }
+        __syncthreads();
+        // dims lane*DPL .. +DPL-1 share chunk cc; rows (2m, 2m+1) arrive as one dword
+        const int dd0 = lane * DPL;
+        const int cc = dd0 / 8, e0 = dd0 % 8;
+        const uint32_t* colw = reinterpret_cast<const uint32_t*>(lds16 + cc * 16);
+        uint32_t word[DPL];
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) word[j] = 0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t x = colw[m];
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) word[j] |= ((x >> (2 * (e0 + j))) & 0x00030003u) << (2 * m);
+        }
+        uint32_t* vout = reinterpret_cast<uint32_t*>(tile);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) vout[(dd0 + j) * (a.P.bs / 16) + upi] = word[j];
+        __syncthreads();
+      }
+    } else if (fmt == VK_FMT_FP8E4M3) {
+      const float s = a.P.fp8_scale;
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int r = rg * NI + k;
+        const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = to_f32<DT>((ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          b[e] = e4m3fn_rne(s == 1.0f ? x : x / s);
+        }
+        if (kv == 0) {
+          if (ok[k]) {
+            uint2 o;
+            o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+            o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+            *reinterpret_cast<uint2*>(tile + (upi * 16 + r) * D + 8 * c) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lds8[(8 * c + e) * 16 + r] = static_cast<uint8_t>(b[e]);
+        }
+      }
+      if (kv == 1) {
+        __syncthreads();
+        const bool full = pos0 >= d.t0 && pos0 + 16 <= t1;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) {
+          const int dd = lane * DPL + j;
+          uint8_t* dst = tile + static_cast<int64_t>(dd) * a.P.bs + upi * 16;
+          if (full) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(lds8 + dd * 16);
+          } else {
+            for (int t = 0; t < 16; ++t)
+              if (pos0 + t >= d.t0 && pos0 + t < t1) dst[t] = lds8[dd * 16 + t];
+          }
+        }
+        __syncthreads();
+      }
+    } else {  // VK_FMT_F16
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int r = rg * NI + k;
+        const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        uint32_t hb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hb[e] = to_f16_bits<DT>((ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        if (kv == 0) {
+          if (ok[k]) {
+            uint4 o;
+            o.x = hb[0] | (hb[1] << 16);
+            o.y = hb[2] | (hb[3] << 16);
+            o.z = hb[4] | (hb[5] << 16);
+            o.w = hb[6] | (hb[7] << 16);
+            *reinterpret_cast<uint4*>(tile + ((upi * 16 + r) * D + 8 * c) * 2) = o;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lds16[(8 * c + e) * 16 + r] = static_cast<uint16_t>(hb[e]);
+        }
+      }
+      if (kv == 1) {
+        __syncthreads();
+        const bool full = pos0 >= d.t0 && pos0 + 16 <= t1;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) {
+          const int dd = lane * DPL + j;
+          uint16_t* dst = reinterpret_cast<uint16_t*>(tile) + static_cast<int64_t>(dd) * a.P.bs + upi * 16;
+          if (full) {
+            const uint4* s4 = reinterpret_cast<const uint4*>(lds16 + dd * 16);
+            reinterpret_cast<uint4*>(dst)[0] = s4[0];
+            reinterpret_cast<uint4*>(dst)[1] = s4[1];
+          } else {
+            for (int t = 0; t < 16; ++t)
+              if (pos0 + t >= d.t0 && pos0 + t < t1) dst[t] = lds16[dd * 16 + t];
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- flat tensor ---
+
+template <int DT>
+__global__ __launch_bounds__(kAbsThreads) void k_flat_absmean(QuantArgs a) {
+  const int blk = blockIdx.x;
+  const int64_t start = static_cast<int64_t>(blk) * kAbsElemsPerBlock;
+  uint4 w[kAbsIters];
+#pragma unroll
+  for (int it = 0; it < kAbsIters; ++it) {
+    const int64_t e = start + (static_cast<int64_t>(it) * kAbsThreads + threadIdx.x) * kAbsElemsPerThreadIter;
+    w[it] = e < a.n ? *reinterpret_cast<const uint4*>(a.x + e) : make_uint4(0, 0, 0, 0);
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int it = 0; it < kAbsIters; ++it) acc += abs_sum8<DT>(w[it]);
+  const double total = block_sum256(acc);
+  if (threadIdx.x == 0) a.partials[blk] = total;
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void k_flat_finalize(QuantArgs a) {
+  if (a.gamma_in) {
+    if (threadIdx.x == 0) {
+      SegInfo info;
+      info.gamma = *a.gamma_in;
+      info.thresh = threshold16<DT>(info.gamma + a.eps);
+      a.seg[0] = info;
+      *a.gamma_out = info.gamma;
+    }
+    return;
+  }
+  double s = 0.0;
+  for (int j = threadIdx.x; j < a.n_blk; j += 64) s += a.partials[j];
+  s = wave_sum(s);
+  if (threadIdx.x == 0) {
+    const SegInfo info = finalize<DT>(s, a.n, a.eps);
+    a.seg[0] = info;
+    *a.gamma_out = info.gamma;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_flat_pack(QuantArgs a) {
+  const uint32_t thresh = a.seg[0].thresh;
+  const int64_t n8 = a.n / 8;
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < n8;
+       g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const uint4 w = reinterpret_cast<const uint4*>(a.x)[g];
+    reinterpret_cast<uint16_t*>(a.packed)[g] = static_cast<uint16_t>(code_word8(w, thresh));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s) {
+  const bool bf = a.dtype == VK_DTYPE_BF16;
+  if (a.n_blk > 0) {
+    const dim3 g1(a.n_blk, n_seg);
+    if (bf) k_absmean_partial<1><<<g1, kAbsThreads, 0, s>>>(a);
+    else k_absmean_partial<0><<<g1, kAbsThreads, 0, s>>>(a);
+    if (bf) k_gamma_finalize<1><<<n_seg, 64, 0, s>>>(a);
+    else k_gamma_finalize<0><<<n_seg, 64, 0, s>>>(a);
+  }
+  const int n_tasks = a.max_units * 2 * a.P.hkv;
+  const dim3 g2(n_tasks < 1024 ? n_tasks : 1024, a.n_layers * a.n_seqs);
+  if (a.P.dim == 128) {
+    if (bf) k_pack<1, 128><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 128><<<g2, 64, 0, s>>>(a);
+  } else {
+    if (bf) k_pack<1, 64><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 64><<<g2, 64, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  const bool bf = a.dtype == VK_DTYPE_BF16;
+  if (!a.gamma_in) {
+    if (bf) k_flat_absmean<1><<<a.n_blk, kAbsThreads, 0, s>>>(a);
+    else k_flat_absmean<0><<<a.n_blk, kAbsThreads, 0, s>>>(a);
+  }
+  if (bf) k_flat_finalize<1><<<1, 64, 0, s>>>(a);
+  else k_flat_finalize<0><<<1, 64, 0, s>>>(a);
+  int64_t blocks = (a.n / 8 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  if (bf) k_flat_pack<1><<<static_cast<unsigned>(blocks), 256, 0, s>>>(a);
+  else k_flat_pack<0><<<static_cast<unsigned>(blocks), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace vk

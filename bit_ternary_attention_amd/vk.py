@@ -1,0 +1,250 @@
+"""Python binding of libvk.so: argument marshalling only.
+
+Every step of the cache runs in the library's HIP kernels; torch is used for
+device memory and streams.  Loading fails loudly if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvk.so")
+
+OK, ERR_ARG, ERR_OOM, ERR_CAPACITY, ERR_ALIGN, ERR_STATE, ERR_HIP = range(7)
+DTYPE_F16, DTYPE_BF16 = 0, 1
+FMT_TERNARY2, FMT_FP8E4M3, FMT_F16 = 0, 1, 2
+
+_c_i32, _c_i64, _c_f32, _c_u64, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_void_p
+
+
+class CacheConfig(ctypes.Structure):
+    _fields_ = [("n_layers", _c_i32), ("n_kv_heads", _c_i32), ("n_q_heads", _c_i32), ("head_dim", _c_i32),
+                ("block_size", _c_i32), ("max_seqs", _c_i32), ("max_tokens_per_seq", _c_i32),
+                ("sink_tokens", _c_i32), ("sink_format", _c_i32), ("recent_tokens", _c_i32),
+                ("recent_format", _c_i32), ("reserved0", _c_i32),
+                ("pages_ternary", _c_i64), ("pages_fp8", _c_i64), ("pages_f16", _c_i64),
+                ("eps", _c_f32), ("fp8_scale", _c_f32), ("page_shuffle_seed", _c_u64)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("device_bytes", _c_i64), ("pool_pages", _c_i64 * 3), ("pages_used", _c_i64 * 3),
+                ("tokens_stored", _c_i64 * 3), ("append_calls", _c_i64), ("decode_calls", _c_i64),
+                ("last_decode_units", _c_i64 * 3), ("total_decode_units", _c_i64 * 3),
+                ("last_decode_splits", _c_i32), ("reserved", _c_i32)]
+
+    def as_dict(self):
+        out = {}
+        for name, _ in self._fields_:
+            v = getattr(self, name)
+            out[name] = list(v) if hasattr(v, "__len__") else int(v)
+        return out
+
+
+EXPORTS = {
+    "vk_config_defaults": (None, [ctypes.POINTER(CacheConfig)]),
+    "vk_cache_device_bytes": (_c_i32, [ctypes.POINTER(CacheConfig), ctypes.POINTER(_c_i64)]),
+    "vk_page_bytes": (_c_i64, [ctypes.POINTER(CacheConfig), _c_i32]),
+    "vk_create_cache": (_c_i32, [ctypes.POINTER(CacheConfig), ctypes.POINTER(_c_vp)]),
+    "vk_append": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_i32, _c_vp, _c_vp, _c_i32, _c_vp]),
+    "vk_decode_attn": (_c_i32, [_c_vp, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_vp, _c_i32, _c_i32, _c_f32,
+                                _c_vp, _c_vp]),
+    "vk_reset_seqs": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32), _c_vp]),
+    "vk_seq_length": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32)]),
+    "vk_read_pages": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, ctypes.POINTER(_c_i32),
+                               ctypes.POINTER(_c_f32)]),
+    "vk_get_stats": (_c_i32, [_c_vp, ctypes.POINTER(Stats)]),
+    "vk_release": (_c_i32, [_c_vp]),
+    "vk_quantize_pack_workspace_bytes": (_c_i64, [_c_i64]),
+    "vk_quantize_pack": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "vk_last_error": (ctypes.c_char_p, []),
+    "vk_status_string": (ctypes.c_char_p, [_c_i32]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run `python -m bit_ternary_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class VkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{lib().vk_status_string(status).decode()}: {message}")
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise VkError(status, lib().vk_last_error().decode())
+
+
+def _ids(seq_ids: Sequence[int]):
+    arr = (ctypes.c_int32 * len(seq_ids))(*[int(s) for s in seq_ids])
+    return arr, len(seq_ids)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return DTYPE_F16
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError("tensor must be float16 or bfloat16")
+
+
+def make_config(**kw) -> CacheConfig:
+    cfg = CacheConfig()
+    lib().vk_config_defaults(ctypes.byref(cfg))
+    for k, v in kw.items():
+        if not hasattr(cfg, k):
+            raise TypeError(f"unknown config field {k}")
+        setattr(cfg, k, v)
+    return cfg
+
+
+def device_bytes(cfg: CacheConfig) -> int:
+    out = ctypes.c_int64()
+    _check(lib().vk_cache_device_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def page_bytes(cfg: CacheConfig, fmt: int) -> int:
+    return int(lib().vk_page_bytes(ctypes.byref(cfg), fmt))
+
+
+class Cache:
+    """A packed, tiered KV cache on the current HIP device."""
+
+    def __init__(self, cfg: Optional[CacheConfig] = None, **kw):
+        self.cfg = cfg if cfg is not None else make_config(**kw)
+        h = ctypes.c_void_p()
+        _check(lib().vk_create_cache(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("cache released")
+        return self._h
+
+    def append(self, k, v, seq_ids: Sequence[int], layer_begin: int = 0, stream=None) -> None:
+        """k, v: [n_layers][n_seqs][n_tokens][Hkv][D] float16/bfloat16 device tensors."""
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 5:
+            raise ValueError("k and v must have the same 5-d shape and dtype")
+        if not (k.is_cuda and v.is_cuda and k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("k and v must be contiguous device tensors")
+        if k.shape[1] != len(seq_ids) or k.shape[3] != self.cfg.n_kv_heads or k.shape[4] != self.cfg.head_dim:
+            raise ValueError(f"k shape {tuple(k.shape)} does not match the cache / seq_ids")
+        ids, n = _ids(seq_ids)
+        _check(lib().vk_append(self.handle, layer_begin, k.shape[0], n, ids, k.shape[2],
+                               ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                               _dtype_code(k), _stream(stream)))
+
+    def decode(self, q, seq_ids: Sequence[int], layer: int, window: int = -1, softmax_scale: float = 0.0,
+               out=None, stream=None):
+        """q: [n_seqs][Hq][D] device tensor -> float32 [n_seqs][Hq][D]."""
+        import torch
+        if not (q.is_cuda and q.is_contiguous()) or q.dim() != 3:
+            raise ValueError("q must be a contiguous 3-d device tensor")
+        if q.shape != (len(seq_ids), self.cfg.n_q_heads, self.cfg.head_dim):
+            raise ValueError(f"q shape {tuple(q.shape)} does not match the cache / seq_ids")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor shaped like q")
+        ids, n = _ids(seq_ids)
+        _check(lib().vk_decode_attn(self.handle, layer, n, ids, ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
+                                    window, softmax_scale, ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+        return out
+
+    def reset(self, seq_ids: Sequence[int], stream=None) -> None:
+        ids, n = _ids(seq_ids)
+        _check(lib().vk_reset_seqs(self.handle, n, ids, _stream(stream)))
+
+    def seq_length(self, seq: int) -> int:
+        out = ctypes.c_int32()
+        _check(lib().vk_seq_length(self.handle, seq, ctypes.byref(out)))
+        return out.value
+
+    def read_pages(self, layer: int, seq: int, page0: int, n_pages: int):
+        """(bytes [n_pages, max page bytes] uint8, formats [n_pages], gamma [n_pages, 2])."""
+        stride = page_bytes(self.cfg, FMT_F16)
+        buf = np.zeros((n_pages, stride), dtype=np.uint8)
+        fmt = np.zeros(n_pages, dtype=np.int32)
+        gam = np.zeros((n_pages, 2), dtype=np.float32)
+        _check(lib().vk_read_pages(self.handle, layer, seq, page0, n_pages, buf.ctypes.data_as(ctypes.c_void_p),
+                                   fmt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   gam.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+        return buf, fmt, gam
+
+    def stats(self) -> dict:
+        s = Stats()
+        _check(lib().vk_get_stats(self.handle, ctypes.byref(s)))
+        return s.as_dict()
+
+    def close(self) -> None:
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check(lib().vk_release(h))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def quantize_pack_workspace_bytes(n: int) -> int:
+    return int(lib().vk_quantize_pack_workspace_bytes(n))
+
+
+def quantize_pack(x, eps: float = 1e-5, gamma=None, packed=None, gamma_out=None, workspace=None, stream=None):
+    """Flat per-tensor quantise+pack of a float16/bfloat16 device tensor.
+
+    Returns (packed uint8 [n/4], gamma float32 [1]) device tensors.  ``gamma``
+    (a float32 device tensor of one element) replaces the computed mean |x|.
+    """
+    import torch
+    if not (x.is_cuda and x.is_contiguous()):
+        raise ValueError("x must be a contiguous device tensor")
+    n = x.numel()
+    if packed is None:
+        packed = torch.empty(n // 4, dtype=torch.uint8, device=x.device)
+    if gamma_out is None:
+        gamma_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    wb = quantize_pack_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=x.device)
+    gptr = ctypes.c_void_p(gamma.data_ptr()) if gamma is not None else ctypes.c_void_p(0)
+    _check(lib().vk_quantize_pack(ctypes.c_void_p(x.data_ptr()), n, _dtype_code(x), eps, gptr,
+                                  ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(gamma_out.data_ptr()),
+                                  ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return packed, gamma_out

@@ -181,12 +181,14 @@ def to_bits(x: torch.Tensor) -> np.ndarray:
     return x.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def small_workload(n_layers=1, n_seqs=1, n_q_heads=8, n_kv_heads=2, head_dim=64,
+def small_workload(n_layers=1, n_seqs=None, n_q_heads=8, n_kv_heads=2, head_dim=64,
                    dtype=DTYPE_F16, block_size=16, sink_tokens=4, window=-1,
                    sink_format=FMT_TERNARY2, recent_tokens=0, recent_format=FMT_FP8E4M3,
                    page_shuffle_seed=0, lengths=(64,), chunk_tokens=0, number=9,
                    outlier_frac=0.0, batch_appends=True) -> Workload:
     """A custom small workload for edge-case tests (same generators)."""
+    if n_seqs is None:
+        n_seqs = len(lengths)
     return Workload(number, "custom", n_layers, n_seqs, n_q_heads, n_kv_heads, head_dim, dtype,
                     block_size, sink_tokens, window, sink_format, recent_tokens, recent_format,
                     page_shuffle_seed, tuple(lengths), chunk_tokens, outlier_frac=outlier_frac,

@@ -1,0 +1,217 @@
+/*
+ * vk.h - packed 2-bit ternary KV cache with direct decode attention (gfx950).
+ *
+ * C ABI of libvk.so.  Plain pointers and sizes only.
+ *
+ * What the library computes follows two pages:
+ *   - "Show HN: Vantage-V-AI" (newshot.cc), section "core architecture":
+ *     keys and values are quantised to ternary states {-1, 0, +1} with a
+ *     per-tensor dynamic scale gamma = mean(|X|), packed four elements per
+ *     uint8 (2.0 bits per element); attention-sink tokens (sink_tokens = 4)
+ *     are retained beside a bounded recent window (quick start:
+ *     max_active_tokens, sink_tokens, quant_mode).
+ *   - "Minima-KV" (twodots.gr), sections "Recent, Anchor and Stale" and on
+ *     mixed-format attention: recent pages stay FP8, anchor pages (the initial
+ *     sinks) keep higher fidelity, older pages are packed; every page stays
+ *     addressable through the block table and is read directly by
+ *     format-specific branches whose partial softmax states are merged in
+ *     logical page order; no dense copy of the cache exists.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers ("device") must be memory of the current HIP device, as
+ *     returned by hipMalloc or by torch; host pointers ("host") are read or
+ *     written before the call returns.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *     default stream) and reads/writes the caller's device buffers in stream
+ *     order: they must stay valid until the stream has passed the call.
+ *   - Every argument is checked on the host before anything is enqueued; on
+ *     any error the cache is left exactly as it was and a message is available
+ *     from vk_last_error() (thread-local).  A HIP failure after enqueueing has
+ *     begun poisons the handle: later calls return VK_ERR_STATE.
+ *   - No call allocates device memory except vk_create_cache, and none blocks
+ *     on the device except vk_read_pages, vk_reset_seqs and vk_release.
+ *   - A handle is not thread-safe; distinct handles are independent.
+ */
+#ifndef VK_H_
+#define VK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VK_API __attribute__((visibility("default")))
+
+typedef int32_t vk_status;
+enum {
+  VK_OK = 0,
+  VK_ERR_ARG = 1,       /* an argument is out of range or inconsistent        */
+  VK_ERR_OOM = 2,       /* device or pinned host allocation failed (create)   */
+  VK_ERR_CAPACITY = 3,  /* not enough free pages of some format               */
+  VK_ERR_ALIGN = 4,     /* append into a partly filled ternary page           */
+  VK_ERR_STATE = 5,     /* handle poisoned by an earlier HIP failure          */
+  VK_ERR_HIP = 6        /* a HIP runtime call failed                          */
+};
+
+/* 16-bit input element types */
+enum { VK_DTYPE_F16 = 0, VK_DTYPE_BF16 = 1 };
+
+/* page formats (the tiers of Minima-KV, "Recent, Anchor and Stale") */
+enum {
+  VK_FMT_TERNARY2 = 0,  /* 2-bit codes, 4 per byte, one float32 gamma per page for K and for V */
+  VK_FMT_FP8E4M3 = 1,   /* OCP e4m3fn bytes of x / fp8_scale, round to nearest even, saturating */
+  VK_FMT_F16 = 2        /* IEEE float16, round to nearest even from the input                    */
+};
+
+typedef struct vk_cache vk_cache; /* opaque; owned by the library */
+
+/*
+ * Cache geometry and tiering.
+ *
+ * Page p of a sequence holds tokens [p*block_size, (p+1)*block_size).  When an
+ * append brings a sequence to length L', each page it writes for the first
+ * time takes: sink_format if p < ceil(sink_tokens / block_size); else
+ * recent_format if recent_tokens > 0 and the page meets [L' - recent_tokens,
+ * L'); else VK_FMT_TERNARY2.  A page keeps its format.  Pool capacities are per
+ * layer; the block table is shared by all layers.
+ */
+typedef struct vk_cache_config {
+  int32_t n_layers;           /* >= 1                                                  */
+  int32_t n_kv_heads;         /* >= 1                                                  */
+  int32_t n_q_heads;          /* multiple of n_kv_heads; n_q_heads/n_kv_heads in {1,2,4,8} */
+  int32_t head_dim;           /* 64 or 128                                             */
+  int32_t block_size;         /* tokens per page: power of two in [16, 65536]          */
+  int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1                      */
+  int32_t max_tokens_per_seq; /* >= 1                                                  */
+  int32_t sink_tokens;        /* S >= 0 (the pages use 4)                              */
+  int32_t sink_format;        /* VK_FMT_*                                              */
+  int32_t recent_tokens;      /* R >= 0; 0 = no recent tier                            */
+  int32_t recent_format;      /* VK_FMT_*                                              */
+  int32_t reserved0;          /* must be 0                                             */
+  int64_t pages_ternary;      /* pool capacity per layer, pages (>= 0)                 */
+  int64_t pages_fp8;
+  int64_t pages_f16;
+  float eps;                  /* added to gamma before dividing (default 1e-5), >= 0   */
+  float fp8_scale;            /* static FP8 scale s > 0 (default 1.0)                  */
+  uint64_t page_shuffle_seed; /* 0: pages are handed out in index order; else a seeded
+                                 permutation of each free list (splitmix64 Fisher-Yates) */
+} vk_cache_config;
+
+/* Fills defaults: sink_tokens 4, sink/recent formats ternary/fp8, recent_tokens 0,
+   eps 1e-5, fp8_scale 1; every size field 0 (the caller sets them). */
+VK_API void vk_config_defaults(vk_cache_config* cfg);
+
+/* Host only: checks cfg and returns the device bytes vk_create_cache would allocate. */
+VK_API vk_status vk_cache_device_bytes(const vk_cache_config* cfg, int64_t* bytes);
+
+/* Bytes of one page of `fmt` (K and V, every KV head) under cfg; 0 if invalid. */
+VK_API int64_t vk_page_bytes(const vk_cache_config* cfg, int32_t fmt);
+
+/* Allocates every device buffer (pools, gamma, block table, scratch, staging) on
+   the current device.  *out is set only on success. */
+VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out);
+
+/*
+ * Quantise and pack new tokens into the cache (the write side).
+ *
+ * k, v: device, contiguous [n_layers][n_seqs][n_tokens][n_kv_heads][head_dim]
+ *       of `dtype`, 16-byte aligned; layers layer_begin .. layer_begin+n_layers-1.
+ * seq_ids: host, n_seqs distinct ids; each sequence grows by n_tokens.
+ *
+ * For every (layer, sequence, K|V) the ternary-routed tokens of this call form
+ * one tensor whose gamma = mean(|X|) is reduced in float64 and rounded to
+ * float32 (Show HN: Vantage-V-AI, core architecture); each element becomes
+ * RoundClip(x / (gamma + eps), -1, 1) (ties to even), stored as code+1 in 2
+ * bits.  Key tiles are token-major ([block][head_dim/4] bytes, element 4j+i at
+ * bits 2i of byte j); value tiles are dimension-major (per head dimension, one
+ * little-endian 32-bit word per 16 tokens, token t at bits 2*(t/2)+16*(t%2)).
+ * gamma never returns to the host.
+ *
+ * Errors: VK_ERR_ARG (ids, sizes, pointers, dtype), VK_ERR_CAPACITY (pool
+ * exhausted), VK_ERR_ALIGN (a sequence ends inside a ternary page).
+ */
+VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                           const int32_t* seq_ids, int32_t n_tokens, const void* k, const void* v,
+                           int32_t dtype, void* stream);
+
+/*
+ * One decode step of GQA attention for one layer (the read side).
+ *
+ * q: device [n_seqs][n_q_heads][head_dim] of q_dtype (|q| < 65504).
+ * out: device float32 [n_seqs][n_q_heads][head_dim].
+ * Attended tokens of a sequence of length L: [0, min(sink_tokens, L)) and
+ * [max(0, L - window), L); window = -1 attends the whole context (the
+ * retention-preserving case of Minima-KV).  softmax_scale <= 0 means
+ * 1/sqrt(head_dim).  Query head h reads KV head h / (n_q_heads/n_kv_heads).
+ * Pages are read in their stored format through the block table; no dense
+ * copy is made.  Every sequence must have L >= 1.
+ */
+VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
+                                const void* q, int32_t q_dtype, int32_t window, float softmax_scale,
+                                float* out, void* stream);
+
+/* Frees every page of the given sequences and sets their length to 0.  Waits
+   for work already enqueued on `stream` first (so pages in flight are not
+   reused early). */
+VK_API vk_status vk_reset_seqs(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, void* stream);
+
+/* Current length of a sequence (host-side state; no device access). */
+VK_API vk_status vk_seq_length(vk_cache* c, int32_t seq, int32_t* length);
+
+/*
+ * Introspection, synchronous (waits for the device): copies pages
+ * [page0, page0+n_pages) of (layer, seq) to host.  Page j lands at
+ * host_bytes + j * vk_page_bytes(cfg, VK_FMT_F16) (the largest page), laid out
+ * [K tile head 0..Hkv-1][V tile head 0..Hkv-1] in its own format.
+ * host_fmt[j] receives the format; host_gamma[2j], [2j+1] the K and V gamma
+ * of ternary pages (NaN otherwise).  Pages must be allocated.
+ */
+VK_API vk_status vk_read_pages(vk_cache* c, int32_t layer, int32_t seq, int32_t page0, int32_t n_pages,
+                               uint8_t* host_bytes, int32_t* host_fmt, float* host_gamma);
+
+typedef struct vk_stats {
+  int64_t device_bytes;             /* all device memory owned by the handle              */
+  int64_t pool_pages[3];            /* capacity per layer, by format                      */
+  int64_t pages_used[3];            /* allocated pages per layer, by format               */
+  int64_t tokens_stored[3];         /* tokens held, by format (per layer)                 */
+  int64_t append_calls, decode_calls;
+  int64_t last_decode_units[3];     /* 16-token units read by the last decode, by format  */
+  int64_t total_decode_units[3];    /* route counters over the handle's life              */
+  int32_t last_decode_splits;       /* split-K factor the last decode used                */
+  int32_t reserved;
+} vk_stats;
+
+VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out);
+
+/* Waits for the device, then frees everything.  NULL is a no-op. */
+VK_API vk_status vk_release(vk_cache* c);
+
+/*
+ * Flat per-tensor quantise+pack (the write side on a plain tensor).
+ *
+ * x: device, n elements of dtype (n % 8 == 0, 16-byte aligned).
+ * gamma_in: device float32 or NULL.  NULL: gamma = mean(|x|) (float64 sum,
+ *           rounded to float32) is computed and written to *gamma_out
+ *           (device).  Otherwise *gamma_in is used as gamma and copied to
+ *           *gamma_out.
+ * packed: device, n/4 bytes; element 4j+i at bits 2i of byte j, code+1.
+ * workspace: device scratch of at least vk_quantize_pack_workspace_bytes(n).
+ */
+VK_API int64_t vk_quantize_pack_workspace_bytes(int64_t n);
+VK_API vk_status vk_quantize_pack(const void* x, int64_t n, int32_t dtype, float eps, const float* gamma_in,
+                                  uint8_t* packed, float* gamma_out, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+
+/* Thread-local text of the last error ("" if none). */
+VK_API const char* vk_last_error(void);
+
+/* Name of a status code. */
+VK_API const char* vk_status_string(vk_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VK_H_ */

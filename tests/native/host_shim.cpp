@@ -1,0 +1,72 @@
+// Test-only C shim over the HIP-free host state (page allocator, tier
+// router, planners), so the host logic can be checked on a machine without
+// a GPU.  Built by the tests with g++; not part of libvk.so.
+#include <cstring>
+#include <string>
+
+#include "host_state.h"
+
+extern "C" {
+
+void* hs_create(const vk_cache_config* cfg, char* err, int errlen) {
+  const std::string why = vk::validate_config(*cfg);
+  if (!why.empty()) {
+    std::strncpy(err, why.c_str(), errlen - 1);
+    err[errlen - 1] = 0;
+    return nullptr;
+  }
+  return new vk::HostState(*cfg);
+}
+
+void hs_destroy(void* h) { delete static_cast<vk::HostState*>(h); }
+
+// Plans and, on success, commits an append.  Returns the status; fills the
+// per-seq ternary token ranges (2 ints per seq) and pages taken per format.
+int hs_append(void* h, int n_seqs, const int* ids, int n_tokens, int* tern_ranges, long long* new_pages,
+              char* err, int errlen) {
+  auto* s = static_cast<vk::HostState*>(h);
+  vk::AppendPlan plan;
+  std::string e;
+  const vk_status st = s->plan_append(n_seqs, ids, n_tokens, &plan, &e);
+  if (st) {
+    std::strncpy(err, e.c_str(), errlen - 1);
+    err[errlen - 1] = 0;
+    return st;
+  }
+  s->commit_append(&plan);
+  for (size_t i = 0; i < plan.seqs.size(); ++i) {
+    tern_ranges[2 * i] = plan.seqs[i].tern_lo;
+    tern_ranges[2 * i + 1] = plan.seqs[i].tern_hi;
+  }
+  for (int f = 0; f < 3; ++f) new_pages[f] = plan.new_pages[f];
+  return 0;
+}
+
+int hs_length(void* h, int seq) { return static_cast<vk::HostState*>(h)->seq(seq).length; }
+int hs_n_pages(void* h, int seq) { return static_cast<int>(static_cast<vk::HostState*>(h)->seq(seq).pages.size()); }
+int hs_page_entry(void* h, int seq, int page) { return static_cast<vk::HostState*>(h)->seq(seq).pages[page]; }
+long long hs_free_pages(void* h, int fmt) { return static_cast<vk::HostState*>(h)->free_pages(fmt); }
+long long hs_tokens_stored(void* h, int fmt) { return static_cast<vk::HostState*>(h)->tokens_stored(fmt); }
+
+void hs_count_units(void* h, int seq, int window, long long* out3) {
+  int64_t o[3] = {0, 0, 0};
+  static_cast<vk::HostState*>(h)->count_units(seq, window, o);
+  for (int f = 0; f < 3; ++f) out3[f] = o[f];
+}
+
+int hs_reset(void* h, int n, const int* ids) {
+  std::string e;
+  return static_cast<vk::HostState*>(h)->reset_seqs(n, ids, &e);
+}
+
+void hs_attended_units(int length, int sinks, int window, int* out3) {
+  const vk::UnitRanges r = vk::attended_units(length, sinks, window);
+  out3[0] = r.a_end;
+  out3[1] = r.b_begin;
+  out3[2] = r.b_end;
+}
+
+int hs_choose_splits(long long items, int max_units, int target, int max_splits, int min_units) {
+  return vk::choose_splits(items, max_units, target, max_splits, min_units);
+}
+}

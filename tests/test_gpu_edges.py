@@ -1,0 +1,247 @@
+"""GPU edge cases, exhaustive encoding sweeps and properties, against the oracle.
+
+* every finite 16-bit input through the flat ternary pack (forced gamma, with
+  exact ties), the fp8 page route and the fp16 page route, bit-exact;
+* ragged appends, partial pages, window/sink corner cases, GQA 1..8,
+  head_dim 64/128, block sizes 16..64, both input dtypes;
+* bit-identical outputs under a different page placement and on repeats;
+* error paths leave the cache usable and unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_ternary_attention_amd import vk
+from bit_ternary_attention_amd import workloads as wl
+from oracle import cache as oc
+from oracle import fp8 as of
+from oracle import ternary as ot
+
+from gpu_harness import (ATTN_ATOL, GAMMA_RTOL, check_decode, check_pages, fill, host_kv, make_cache,
+                         say, seq_calls, spec_of)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def all_finite_patterns(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = ot.values16(bits, dtype)
+    bits = bits.copy()
+    bits[~np.isfinite(vals)] = 0
+    return bits
+
+
+def to_dev(bits, dtype):
+    t = torch.from_numpy(bits.view(np.int16).copy()).cuda()
+    return t.view(torch.float16 if dtype == 0 else torch.bfloat16)
+
+
+# ------------------------------------------------------------- sweeps ---
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_flat_pack_exhaustive_forced_gamma(dtype):
+    bits = all_finite_patterns(dtype)
+    x = to_dev(bits, dtype)
+    vals = ot.values16(bits, dtype)
+    gammas = [1.0, 0.828125, 2.0 ** -20, 0.7978846, 3.0, 0.5, 1.0 / 3.0, 1e-3]
+    if dtype == 1:
+        gammas += [1e30, 7.5e-30]
+    for g in gammas:
+        for eps in (0.0, 1e-5):
+            gt = torch.tensor([g], dtype=torch.float32, device="cuda")
+            packed, gout = vk.quantize_pack(x, eps=eps, gamma=gt)
+            torch.cuda.synchronize()
+            want = ot.pack_flat(ot.ternary_codes(vals, np.float32(g), eps))
+            got = packed.cpu().numpy()
+            assert float(gout.item()) == float(np.float32(g))
+            if not np.array_equal(got, want):
+                bad = np.nonzero(got != want)[0]
+                raise AssertionError(f"dtype {dtype} gamma {g} eps {eps}: {bad.size} bytes differ, first {bad[0]}")
+
+
+@pytest.mark.parametrize("n,dtype", [(8, 0), (24, 1), (16384 + 8, 1), (3 * 1024 * 1024 + 40, 1), (1 << 20, 0)])
+def test_flat_pack_gamma_and_codes(n, dtype):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(n)
+    x = (torch.randn(n, generator=g, device="cuda") * 1.7).to(torch.float16 if dtype == 0 else torch.bfloat16)
+    packed, gout = vk.quantize_pack(x)
+    torch.cuda.synchronize()
+    bits = wl.to_bits(x)
+    vals = ot.values16(bits, dtype)
+    want_g = ot.absmean_gamma(vals)
+    got_g = np.float32(gout.item())
+    assert abs(float(got_g) - float(want_g)) <= GAMMA_RTOL * float(want_g)
+    want = ot.pack_flat(ot.ternary_codes(vals, got_g, 1e-5))
+    assert np.array_equal(packed.cpu().numpy(), want)
+
+
+def _route_workload(fmt, dtype, scale=1.0):
+    # 512 tokens x 1 head x 128 dims = every 16-bit pattern once
+    if fmt == oc.FP8E4M3:
+        return wl.small_workload(n_kv_heads=1, n_q_heads=1, head_dim=128, dtype=dtype, block_size=16,
+                                 sink_tokens=0, recent_tokens=1 << 20, recent_format=oc.FP8E4M3, lengths=(512,))
+    return wl.small_workload(n_kv_heads=1, n_q_heads=1, head_dim=128, dtype=dtype, block_size=16,
+                             sink_tokens=512, sink_format=oc.F16, lengths=(512,))
+
+
+@pytest.mark.parametrize("fmt,dtype,scale", [(oc.FP8E4M3, 1, 1.0), (oc.FP8E4M3, 0, 1.0), (oc.FP8E4M3, 1, 3.0),
+                                             (oc.FP8E4M3, 1, 0.0078125), (oc.F16, 1, 1.0), (oc.F16, 0, 1.0)])
+def test_page_routes_exhaustive(fmt, dtype, scale):
+    w = _route_workload(fmt, dtype)
+    bits = all_finite_patterns(dtype)
+    kb = bits.reshape(512, 1, 128)
+    vb = np.ascontiguousarray(bits[::-1]).reshape(512, 1, 128)
+    cache = make_cache(w, fp8_scale=scale)
+    k = to_dev(kb.ravel(), dtype).view(1, 1, 512, 1, 128)
+    v = to_dev(vb.ravel(), dtype).view(1, 1, 512, 1, 128)
+    cache.append(k, v, [0])
+    enc = check_pages(cache, w, 0, 0, kb, vb, pages=list(range(32)), fp8_scale=scale)
+    assert set(enc.page_format) == {fmt}
+    cache.close()
+
+
+# ---------------------------------------------------- ragged and edges ---
+
+EDGE_CASES = [
+    # (name, workload kwargs, windows)
+    ("single-token", dict(lengths=(1,)), [-1, 0, 5]),
+    ("short-partial-unit", dict(lengths=(5,), sink_tokens=4), [-1, 1, 2]),
+    ("one-unit", dict(lengths=(16,)), [-1, 3]),
+    ("unit-plus-one", dict(lengths=(17,)), [-1, 1, 13]),
+    ("no-sinks", dict(lengths=(300,), sink_tokens=0), [-1, 1, 17, 256]),
+    ("many-sinks", dict(lengths=(300,), sink_tokens=40), [-1, 0, 7, 256]),
+    ("mha-d64", dict(n_q_heads=3, n_kv_heads=3, head_dim=64, lengths=(200, 77)), [-1, 50]),
+    ("gqa2-bs32", dict(n_q_heads=4, n_kv_heads=2, block_size=32, lengths=(333, 64, 1)), [-1, 100]),
+    ("gqa8-d128-bf16", dict(n_q_heads=16, n_kv_heads=2, head_dim=128, dtype=1, lengths=(1000, 513)), [-1, 256]),
+    ("bs64-chunks", dict(block_size=64, lengths=(640,), chunk_tokens=128), [-1, 200]),
+    ("mixed-tiers-f16-fp8", dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
+                                 recent_tokens=48, recent_format=oc.FP8E4M3, lengths=(700, 31, 250),
+                                 page_shuffle_seed=99, batch_appends=False), [-1, 60, 0]),
+    ("recent-ternary-sink-fp8", dict(sink_tokens=20, sink_format=oc.FP8E4M3, recent_tokens=32,
+                                     recent_format=oc.F16, lengths=(400,)), [-1, 33]),
+]
+
+
+@pytest.mark.parametrize("name,kw,windows", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_edge_workloads(name, kw, windows):
+    w = wl.small_workload(**kw)
+    say(f"edge {name}: {w}")
+    cache = make_cache(w)
+    fill(cache, w)
+    encs = {}
+    for s in range(w.n_seqs):
+        kb, vb = host_kv(w, 0, s)
+        encs[s] = check_pages(cache, w, 0, s, kb, vb, pages=list(range(-(-w.lengths[s] // w.block_size))))
+    q = wl.queries(w, 0, device="cuda")
+    for W in windows:
+        if w.sink_tokens == 0 and W == 0:
+            continue
+        out = cache.decode(q, list(range(w.n_seqs)), 0, window=W)
+        torch.cuda.synchronize()
+        err = check_decode(out, q, w, encs, W)
+        say(f"edge {name} window {W}: max err {err:.2e}")
+    cache.close()
+
+
+def test_incremental_decode_appends_into_recent_tier():
+    """Prefill, then one-token appends (the recent fp8 tier grows page by page), decoding each step."""
+    w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
+                          recent_tokens=64, recent_format=oc.FP8E4M3, lengths=(300,))
+    steps = [(0, 250)] + [(250 + i, 1) for i in range(50)]
+    cache = make_cache(w, slack_pages=(0, 8, 0))
+    spec = spec_of(w)
+    kall = wl.kv_block(w, "k", 0, 0, 0, 300, device="cuda")
+    vall = wl.kv_block(w, "v", 0, 0, 0, 300, device="cuda")
+    kb, vb = wl.to_bits(kall), wl.to_bits(vall)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    for i, (t0, n) in enumerate(steps):
+        cache.append(kall[t0:t0 + n][None, None].contiguous(), vall[t0:t0 + n][None, None].contiguous(), [0])
+        if i % 7 == 0 or i == len(steps) - 1:
+            L = t0 + n
+            enc = oc.encode_sequence(spec, kb[:L], vb[:L], 1, steps[:i + 1])
+            q = torch.randn((1, 8, 128), generator=g, device="cuda").to(torch.bfloat16)
+            out = cache.decode(q, [0], 0, window=-1)
+            torch.cuda.synchronize()
+            check_decode(out, q, w, {0: enc}, -1)
+    assert cache.seq_length(0) == 300
+    cache.close()
+
+
+def test_page_placement_and_repeats_are_bit_identical():
+    w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
+                          recent_tokens=100, lengths=(900, 455, 1200), batch_appends=False)
+    outs = []
+    for shuffle in (0, 1004, 77):
+        cache = make_cache(w, shuffle=shuffle, slack_pages=(50, 50, 50))
+        fill(cache, w)
+        q = wl.queries(w, 0, device="cuda")
+        for W in (-1, 300):
+            outs.append((shuffle, W, cache.decode(q, [0, 1, 2], 0, window=W).cpu()))
+            again = cache.decode(q, [0, 1, 2], 0, window=W).cpu()
+            assert torch.equal(outs[-1][2], again)
+        cache.close()
+    for W in (-1, 300):
+        ref = [o for s, ww, o in outs if ww == W]
+        assert all(torch.equal(ref[0], r) for r in ref[1:])
+
+
+def test_many_sequences_subset_and_order():
+    """More sequences than one launch holds; decode a reordered subset."""
+    w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, n_seqs=70, lengths=tuple(range(20, 90)),
+                          batch_appends=False)
+    cache = make_cache(w)
+    fill(cache, w)
+    q = wl.queries(w, 0, device="cuda")
+    encs = {}
+    for s in (0, 33, 64, 69):
+        kb, vb = host_kv(w, 0, s)
+        encs[s] = oc.encode_sequence(spec_of(w), kb, vb, 0, seq_calls(w, s))
+    out = cache.decode(q, list(range(70)), 0, window=-1)
+    torch.cuda.synchronize()
+    check_decode(out, q, w, encs, -1)
+    ids = [69, 0, 33, 64]
+    sub = cache.decode(q[ids].contiguous(), ids, 0, window=-1)
+    torch.cuda.synchronize()
+    assert float((sub - out[ids]).abs().max()) <= 1e-5
+    cache.close()
+
+
+def test_errors_leave_cache_unchanged_and_usable():
+    w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(64, 64), n_seqs=2)
+    cache = make_cache(w)          # exactly the pages two 64-token sequences need (+2 slack)
+    fill(cache, w)
+    before = cache.stats()
+    k = torch.zeros((1, 1, 64, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(vk.VkError) as e:
+        cache.append(k, k, [0])                 # pool exhausted
+    assert e.value.status == vk.ERR_CAPACITY
+    with pytest.raises(vk.VkError) as e:
+        cache.append(k, k, [5])                 # id out of range
+    assert e.value.status == vk.ERR_ARG
+    with pytest.raises(vk.VkError) as e:
+        cache.append(k[:, :, :3].contiguous(), k[:, :, :3].contiguous(), [0], layer_begin=1)
+    assert e.value.status == vk.ERR_ARG
+    after = cache.stats()
+    assert after["pages_used"] == before["pages_used"] and cache.seq_length(0) == 64
+    q = wl.queries(w, 0, device="cuda")
+    ok = cache.decode(q, [0, 1], 0).cpu()
+    cache.reset([1])
+    assert cache.seq_length(1) == 0
+    with pytest.raises(vk.VkError) as e:
+        cache.decode(q, [0, 1], 0)              # seq 1 is empty now
+    assert e.value.status == vk.ERR_ARG
+    fill_one = wl.append_inputs(w, [1], 0, 64, device="cuda")
+    cache.append(fill_one[0], fill_one[1], [1])  # freed pages are reused
+    again = cache.decode(q, [0, 1], 0).cpu()
+    assert torch.equal(ok, again)
+    small = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(20,))
+    c2 = make_cache(small, slack_pages=(4, 0, 0))
+    fill(c2, small)                              # page 1 ternary, partly filled
+    kk = torch.zeros((1, 1, 4, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(vk.VkError) as e:
+        c2.append(kk, kk, [0])
+    assert e.value.status == vk.ERR_ALIGN
+    c2.close()
+    cache.close()

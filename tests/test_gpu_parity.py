@@ -1,0 +1,53 @@
+"""GPU parity of the five seeded workloads against the CPU oracle.
+
+Each test runs the workload at its full size through the C ABI, in the same
+launch configuration the benchmark times, and checks sampled sequences,
+layers and pages bit-exactly (codes, bytes), gamma within 2^-22 and decode
+outputs within max-abs 2e-3 of the float64 oracle.
+"""
+import pytest
+import torch
+
+from bit_ternary_attention_amd import workloads as wl
+
+from gpu_harness import run_workload, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def test_workload1_tiny():
+    w = wl.workload(1)
+    r = run_workload(w, sample_seqs=[0], page_layers=[0], decode_layers=[0])
+    assert r["stats"]["last_decode_units"] == [17, 0, 0]   # units holding tokens 0..3 and 256..511
+    say(f"workload 1: {r}")
+
+
+def test_workload2_qwen_shaped_36_layers():
+    w = wl.workload(2)
+    r = run_workload(w, sample_seqs=[0], page_layers=[0, 17, 35], decode_layers=list(range(36)))
+    assert r["stats"]["pages_used"] == [256, 0, 0]
+    say(f"workload 2: max err {r['max_err']:.3e}")
+
+
+def test_workload3_full_retention_outliers():
+    w = wl.workload(3)
+    r = run_workload(w, sample_seqs=[0, 13, 31], page_layers=[0], decode_layers=[0])
+    say(f"workload 3: max err {r['max_err']:.3e}")
+
+
+def test_workload4_mixed_format_paged():
+    w = wl.workload(4)
+    lengths = list(w.lengths)
+    sample = sorted({lengths.index(min(lengths)), lengths.index(max(lengths)), 5, 40})
+    r = run_workload(w, sample_seqs=sample, page_layers=[0], decode_layers=[0])
+    units = r["stats"]["last_decode_units"]
+    assert units[0] > 0 and units[1] > 0 and units[2] == 64   # every route ran
+    say(f"workload 4: max err {r['max_err']:.3e} units {units}")
+
+
+def test_workload5_prefill_128k_chunked():
+    w = wl.workload(5)
+    r = run_workload(w, sample_seqs=[2], page_layers=[0], decode_layers=[0])
+    assert r["stats"]["append_calls"] == 32
+    say(f"workload 5: max err {r['max_err']:.3e}")

@@ -1,0 +1,261 @@
+"""CPU checks of the library boundary and the HIP-free host logic.
+
+* libvk.so loads and exports every entry point include/vk.h declares;
+* configuration checks and size arithmetic (no device call);
+* the page allocator, tier router and planners (host_state.cpp, through a
+  g++-built test shim) against the oracle's format rule and attended set.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from bit_ternary_attention_amd import vk
+from oracle import attention as oa
+from oracle import cache as oc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vk.h")
+CSRC = os.path.join(ROOT, "bit_ternary_attention_amd", "csrc")
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"VK_API\s+[\w\s\*]+?\b(vk_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_entry_points()
+    assert len(names) >= 14
+    L = vk.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(vk.EXPORTS), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", vk.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    assert all(e.startswith("vk_") for e in exported), "only vk_* symbols are exported"
+
+
+def base_cfg(**kw):
+    d = dict(n_layers=2, n_kv_heads=2, n_q_heads=8, head_dim=128, block_size=16, max_seqs=4,
+             max_tokens_per_seq=1024, pages_ternary=100, pages_fp8=10, pages_f16=5)
+    d.update(kw)
+    return vk.make_config(**d)
+
+
+def test_config_defaults():
+    c = vk.make_config()
+    assert c.sink_tokens == 4 and c.sink_format == vk.FMT_TERNARY2 and c.recent_tokens == 0
+    assert c.recent_format == vk.FMT_FP8E4M3 and abs(c.eps - 1e-5) < 1e-12 and c.fp8_scale == 1.0
+
+
+@pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_q_heads=12), dict(n_q_heads=2, n_kv_heads=4),
+                                 dict(n_q_heads=48, n_kv_heads=2), dict(head_dim=96), dict(block_size=24),
+                                 dict(block_size=8), dict(max_seqs=0), dict(sink_tokens=-1),
+                                 dict(sink_format=3), dict(pages_fp8=-1), dict(eps=-1.0),
+                                 dict(fp8_scale=0.0), dict(reserved0=1), dict(eps=float("nan"))])
+def test_config_rejected(bad):
+    with pytest.raises(vk.VkError) as e:
+        vk.device_bytes(base_cfg(**bad))
+    assert e.value.status == vk.ERR_ARG
+
+
+def test_sizes():
+    c = base_cfg()
+    assert vk.page_bytes(c, vk.FMT_TERNARY2) == 2 * 2 * 16 * 128 // 4
+    assert vk.page_bytes(c, vk.FMT_FP8E4M3) == 2 * 2 * 16 * 128
+    assert vk.page_bytes(c, vk.FMT_F16) == 2 * 2 * 16 * 128 * 2
+    total = vk.device_bytes(c)
+    pools = 2 * (100 * 2048 + 10 * 8192 + 5 * 16384)
+    assert total >= pools + 2 * 100 * 8 + 4 * 64 * 4
+    # pools dominate a large cache: no hidden dense copy of the KV
+    big = base_cfg(pages_ternary=1 << 20, pages_fp8=0, pages_f16=0)
+    assert vk.device_bytes(big) - 2 * (1 << 20) * (2048 + 8) < 64 << 20
+    assert vk.quantize_pack_workspace_bytes(1 << 20) >= 8 * 64
+
+
+# ------------------------------------------------------------ host shim ---
+
+@pytest.fixture(scope="module")
+def hs():
+    d = tempfile.mkdtemp(prefix="vk_hs_")
+    so = os.path.join(d, "libhs.so")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-shared", "-fPIC", "-I" + os.path.join(ROOT, "include"),
+                    "-I" + CSRC, os.path.join(ROOT, "tests", "native", "host_shim.cpp"),
+                    os.path.join(CSRC, "host_state.cpp"), "-o", so], check=True)
+    L = ctypes.CDLL(so)
+    P = ctypes.POINTER
+    L.hs_create.restype = ctypes.c_void_p
+    L.hs_create.argtypes = [P(vk.CacheConfig), ctypes.c_char_p, ctypes.c_int]
+    L.hs_destroy.argtypes = [ctypes.c_void_p]
+    L.hs_append.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), ctypes.c_int, P(ctypes.c_int),
+                            P(ctypes.c_longlong), ctypes.c_char_p, ctypes.c_int]
+    for n in ("hs_length", "hs_n_pages"):
+        getattr(L, n).argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.hs_page_entry.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    L.hs_free_pages.restype = ctypes.c_longlong
+    L.hs_free_pages.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.hs_tokens_stored.restype = ctypes.c_longlong
+    L.hs_tokens_stored.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.hs_count_units.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(ctypes.c_longlong)]
+    L.hs_reset.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int)]
+    L.hs_attended_units.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(ctypes.c_int)]
+    L.hs_choose_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    return L
+
+
+class Host:
+    def __init__(self, L, cfg):
+        self.L, self.cfg = L, cfg
+        err = ctypes.create_string_buffer(256)
+        self.h = L.hs_create(ctypes.byref(cfg), err, 256)
+        assert self.h, err.value
+
+    def append(self, ids, n):
+        arr = (ctypes.c_int * len(ids))(*ids)
+        rng = (ctypes.c_int * (2 * len(ids)))()
+        newp = (ctypes.c_longlong * 3)()
+        err = ctypes.create_string_buffer(256)
+        st = self.L.hs_append(self.h, len(ids), arr, n, rng, newp, err, 256)
+        return st, [(rng[2 * i], rng[2 * i + 1]) for i in range(len(ids))], list(newp), err.value.decode()
+
+    def pages(self, s):
+        return [self.L.hs_page_entry(self.h, s, p) for p in range(self.L.hs_n_pages(self.h, s))]
+
+    def free(self):
+        return [self.L.hs_free_pages(self.h, f) for f in range(3)]
+
+    def __del__(self):
+        self.L.hs_destroy(self.h)
+
+
+def spec_of(cfg):
+    return oc.CacheSpec(n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, block_size=cfg.block_size,
+                        sink_tokens=cfg.sink_tokens, sink_format=cfg.sink_format,
+                        recent_tokens=cfg.recent_tokens, recent_format=cfg.recent_format)
+
+
+@pytest.mark.parametrize("bs,S,sinkf,R,recf", [(16, 4, 2, 256, 1), (16, 4, 0, 0, 1), (32, 40, 2, 33, 1),
+                                               (64, 0, 0, 100, 2), (16, 20, 1, 16, 0)])
+def test_tier_router_matches_oracle(hs, bs, S, sinkf, R, recf):
+    cfg = base_cfg(block_size=bs, sink_tokens=S, sink_format=sinkf, recent_tokens=R, recent_format=recf,
+                   max_tokens_per_seq=4096, pages_ternary=4000, pages_fp8=4000, pages_f16=4000, max_seqs=2)
+    h = Host(hs, cfg)
+    spec = spec_of(cfg)
+    rng = np.random.default_rng(bs + S + R)
+    calls, length = [], 0
+    while length < 3000:
+        n = int(rng.integers(1, 400))
+        if length % bs and oc.new_page_format(spec, length // bs, length) == oc.TERNARY2:
+            n = bs - length % bs + int(rng.integers(0, 3)) * bs   # never extend a ternary page
+        bits = np.zeros((length + n, 1, 4), dtype=np.uint16)
+        try:
+            enc = oc.encode_sequence(spec, bits, bits, 0, calls + [(length, n)])
+        except oc.AlignError:
+            st, _, _, _ = h.append([1], n)
+            assert st == vk.ERR_ALIGN
+            break
+        st, rngs, newp, err = h.append([1], n)
+        assert st == 0, err
+        fmts = [p >> 30 & 3 for p in h.pages(1)]
+        assert fmts == enc.page_format
+        tern = np.nonzero(enc.token_format[length:length + n] == oc.TERNARY2)[0]
+        if tern.size:
+            assert rngs[0] == (tern[0], tern[-1] + 1) and tern.size == tern[-1] + 1 - tern[0]
+        else:
+            assert rngs[0][0] == rngs[0][1]
+        calls.append((length, n))
+        length += n
+        assert hs.hs_length(h.h, 1) == length
+        for f in range(3):
+            assert hs.hs_tokens_stored(h.h, f) == int(np.sum(enc.token_format == f))
+
+
+def test_capacity_align_and_argument_errors_leave_state_unchanged(hs):
+    cfg = base_cfg(pages_ternary=10, pages_fp8=2, pages_f16=1, sink_format=2, recent_tokens=16)
+    h = Host(hs, cfg)
+    st, _, newp, _ = h.append([0, 1], 64)     # per seq: page 0 f16, pages 1-2 ternary, page 3 fp8
+    assert st == vk.ERR_CAPACITY               # two f16 pages needed, one in the pool
+    assert h.free() == [10, 2, 1] and hs.hs_length(h.h, 0) == 0
+    st, _, newp, err = h.append([0], 64)
+    assert st == 0 and newp == [2, 1, 1], err
+    assert h.free() == [8, 1, 0]
+    st, *_ = h.append([0, 0], 1)
+    assert st == vk.ERR_ARG                    # repeated id
+    st, *_ = h.append([7], 1)
+    assert st == vk.ERR_ARG                    # id out of range
+    st, *_ = h.append([0], 2000)
+    assert st == vk.ERR_ARG                    # beyond max_tokens_per_seq
+    cfg0 = base_cfg(recent_tokens=0)
+    h0 = Host(hs, cfg0)
+    assert h0.append([2], 20)[0] == 0          # page 1 ternary, 4 of 16 tokens filled
+    st, _, _, err = h0.append([2], 5)
+    assert st == vk.ERR_ALIGN and "ternary" in err
+    assert hs.hs_length(h0.h, 2) == 20
+
+
+def test_allocator_shuffle_and_reset(hs):
+    seq = Host(hs, base_cfg(page_shuffle_seed=0, recent_tokens=0, sink_tokens=0))
+    assert seq.append([0], 160)[0] == 0
+    assert [p & 0x3FFFFFFF for p in seq.pages(0)] == list(range(10))
+    a = Host(hs, base_cfg(page_shuffle_seed=1004, sink_tokens=0, max_tokens_per_seq=1600))
+    b = Host(hs, base_cfg(page_shuffle_seed=1004, sink_tokens=0, max_tokens_per_seq=1600))
+    c = Host(hs, base_cfg(page_shuffle_seed=7, sink_tokens=0, max_tokens_per_seq=1600))
+    for x in (a, b, c):
+        assert x.append([0], 1600)[0] == 0
+    pa, pb, pc = ([p & 0x3FFFFFFF for p in x.pages(0)] for x in (a, b, c))
+    assert pa == pb and pa != pc and pa != list(range(100))
+    assert sorted(pa) == list(range(100))      # a permutation of the whole pool
+    assert a.free()[0] == 0
+    arr = (ctypes.c_int * 1)(0)
+    assert hs.hs_reset(a.h, 1, arr) == 0
+    assert a.free()[0] == 100 and hs.hs_length(a.h, 0) == 0
+    assert a.append([0], 1600)[0] == 0         # freed pages are reusable
+
+
+def test_attended_units_match_oracle(hs):
+    out = (ctypes.c_int * 3)()
+    rng = np.random.default_rng(0)
+    cases = [(1, 4, 256), (4, 4, 0), (17, 4, 0), (260, 4, 256), (261, 4, 256), (4096, 4, 256), (40, 0, 1),
+             (100, 30, 10), (100, 4, -1), (33, 40, 5), (512, 4, 256)]
+    cases += [(int(rng.integers(1, 3000)), int(rng.integers(0, 40)), int(rng.integers(-1, 600))) for _ in range(400)]
+    for L, S, W in cases:
+        if S == 0 and W == 0:
+            continue
+        hs.hs_attended_units(L, S, W, out)
+        a_end, b0, b1 = out[0], out[1], out[2]
+        units = set(range(a_end)) | set(range(b0, b1))
+        assert a_end <= b0 <= b1 or (b0 == b1)
+        want = {int(t) // 16 for t in oa.attended_tokens(L, S, W)}
+        assert units == want, (L, S, W)
+
+
+def test_route_counters_match_page_formats(hs):
+    cfg = base_cfg(sink_format=2, recent_tokens=256, recent_format=1, max_tokens_per_seq=4096,
+                   pages_ternary=400, pages_fp8=100, pages_f16=10, max_seqs=2)
+    h = Host(hs, cfg)
+    assert h.append([1], 1000)[0] == 0
+    assert h.append([1], 37)[0] == 0
+    spec = spec_of(cfg)
+    bits = np.zeros((1037, 1, 4), dtype=np.uint16)
+    enc = oc.encode_sequence(spec, bits, bits, 0, [(0, 1000), (1000, 37)])
+    out = (ctypes.c_longlong * 3)()
+    for W in (-1, 256, 100, 0, 1):
+        hs.hs_count_units(h.h, 1, W, out)
+        units = sorted({int(t) // 16 for t in oa.attended_tokens(1037, 4, W)})
+        want = [0, 0, 0]
+        for u in units:
+            want[enc.page_format[u]] += 1
+        assert list(out) == want, W
+
+
+def test_split_choice(hs):
+    assert hs.hs_choose_splits(256, 2048, 4096, 64, 8) == 16
+    assert hs.hs_choose_splits(32, 8192, 4096, 64, 8) == 64
+    assert hs.hs_choose_splits(2, 17, 4096, 64, 8) == 2
+    assert hs.hs_choose_splits(4096, 100, 4096, 64, 8) == 1
