@@ -1,0 +1,247 @@
+"""Benchmark: quantize+pack into the packed ternary KV cache, then decode attention over it.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+every append call of the workload (absmean pass, gamma finalize, quantise +
+pack + page scatter) followed by one decode step of every layer.  The default
+workload is the Qwen2.5-3B-shaped cache (36 layers, 16 query / 2 KV heads,
+head_dim 128, 4096 bf16 tokens, sinks 4 + window 256).  Other workloads are
+selectable with --workload for reference numbers.
+
+Prints one JSON line.  `value` is whole-step algorithmic bytes / step time
+(GB/s): both passes of the write side over the input, every stored byte, and
+the attended page bytes the decode reads.  Inputs are resident in HBM before
+the timed region; several input sets rotate so that no step reads inputs still
+held in the 256 MB Infinity Cache from an earlier step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode-attn over packed KV: GB/s & % HBM peak; quantize+pack GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Qwen2.5-3B-shaped)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-layers", type=int, default=0, help="0 = workload's own sample rule")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from bit_ternary_attention_amd import vk
+    from bit_ternary_attention_amd import workloads as wl
+
+    torch.cuda.set_device(0)
+    w = wl.workload(args.workload)
+    calls = w.appends()
+    ids_all = list(range(w.n_seqs))
+
+    # pages per format needed by one step (format rule of the cache config)
+    cfg = vk.make_config(n_layers=w.n_layers, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
+                         head_dim=w.head_dim, block_size=w.block_size, max_seqs=w.n_seqs,
+                         max_tokens_per_seq=w.max_len, sink_tokens=w.sink_tokens, sink_format=w.sink_format,
+                         recent_tokens=w.recent_tokens, recent_format=w.recent_format,
+                         page_shuffle_seed=w.page_shuffle_seed)
+    need = [0, 0, 0]
+    bs = w.block_size
+    for s in range(w.n_seqs):
+        for ids, t0, n in calls:
+            if s not in ids:
+                continue
+            for p in range(-(-t0 // bs), -(-(t0 + n) // bs)):
+                lo = p * bs
+                if p < -(-w.sink_tokens // bs):
+                    f = w.sink_format
+                elif w.recent_tokens > 0 and lo < t0 + n and lo + bs > t0 + n - w.recent_tokens:
+                    f = w.recent_format
+                else:
+                    f = vk.FMT_TERNARY2
+                need[f] += 1
+    cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16 = need
+    cache = vk.Cache(cfg)
+
+    # inputs resident in HBM: rotate enough sets to exceed the 256 MB Infinity Cache
+    in_bytes = sum(2 * w.n_layers * len(ids) * n * w.n_kv_heads * w.head_dim * 2 for ids, _, n in calls)
+    n_sets = max(1, min(3, -(-768 * 2 ** 20 // in_bytes)))
+    sets = []
+    for r in range(n_sets):
+        per_call = []
+        for ci, (ids, t0, n) in enumerate(calls):
+            k, v = wl.append_inputs(w, ids, t0, n, device="cuda")
+            if r:  # other sets: same shapes, different draws
+                k = k[:, :, torch.randperm(n, device="cuda")].contiguous()
+                v = v[:, :, torch.randperm(n, device="cuda")].contiguous()
+            per_call.append((ids, k, v))
+        sets.append(per_call)
+    qs = [wl.queries(w, layer, device="cuda") for layer in range(w.n_layers)]
+    outs = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for q in qs]
+    torch.cuda.synchronize()
+
+    def step(i):
+        cache.reset(ids_all)
+        for ids, k, v in sets[i % n_sets]:
+            cache.append(k, v, ids)
+        for layer in range(w.n_layers):
+            cache.decode(qs[layer], ids_all, layer, window=w.window, out=outs[layer])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # same steps again with per-kernel HIP event timing (library hooks on the launch stream)
+    cache.kernel_timing(True)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    kt = cache.kernel_times()
+    cache.kernel_timing(False)
+    ms_step_timed = (t3 - t2) * 1e3 / args.steps
+    stats = cache.stats()
+
+    kernels = {}
+    for name, (launches, ms, by) in kt.items():
+        if launches == 0:
+            continue
+        avg_us = ms * 1e3 / launches
+        gbps = by / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        kernels[name] = {"launches_per_step": launches / args.steps, "avg_us": round(avg_us, 3),
+                         "bytes_per_launch": by / launches, "GBps": round(gbps, 1),
+                         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "ms_per_step": round(ms / args.steps, 4)}
+    step_bytes = sum(by for (_, _, by) in kt.values()) / args.steps
+    write_bytes = sum(kt[k][2] for k in ("absmean", "finalize", "pack")) / args.steps
+    write_ms = sum(kt[k][1] for k in ("absmean", "finalize", "pack")) / args.steps
+    read_bytes = sum(kt[k][2] for k in ("decode", "merge")) / args.steps
+    read_ms = sum(kt[k][1] for k in ("decode", "merge")) / args.steps
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dominant]
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    kv_tokens = sum(len(ids) * n for ids, _, n in calls)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "dtype_detail": ("bf16/f16 inputs; 2-bit codes, 4 per u8; f16 x f16 -> f32 dot products; "
+                         "f32 softmax and accumulation"),
+        "data": "synthetic (seeded torch.randn, see bit_ternary_attention_amd/workloads.py)",
+        "config": {"workload": w.name, "layers": w.n_layers, "seqs": w.n_seqs,
+                   "tokens_per_seq": list(sorted(set(w.lengths))) if len(set(w.lengths)) > 1 else w.lengths[0],
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "sink_tokens": w.sink_tokens, "window": w.window,
+                   "append_calls": len(calls), "input_sets": n_sets},
+        "quantize_pack": {"GBps": round(write_bytes / (write_ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(write_bytes / (write_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                          "bytes_per_step": write_bytes, "device_ms_per_step": round(write_ms, 4),
+                          "kv_tokens_per_s": round(kv_tokens * w.n_layers / (write_ms * 1e-3), 1)},
+        "decode_attn": {"GBps": round(read_bytes / (read_ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(read_bytes / (read_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "bytes_per_step": read_bytes, "device_ms_per_step": round(read_ms, 4),
+                        "us_per_layer": round(read_ms * 1e3 / w.n_layers, 3),
+                        "splits": stats["last_decode_splits"], "units_by_format": stats["last_decode_units"]},
+        "kernels": kernels,
+        "ms_per_step_with_kernel_timing": round(ms_step_timed, 4),
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": None,
+                     "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": dk["avg_us"]},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_sample_layers)
+    print(json.dumps(result), flush=True)
+    cache.close()
+
+
+def cpu_baseline(w, calls, sample_layers):
+    """The CPU oracle, as written, on a bounded sample of the same workload (one thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from bit_ternary_attention_amd import workloads as wl
+    from oracle import attention as oa
+    from oracle import cache as oc
+    from oracle import ternary as ot
+
+    spec = oc.CacheSpec(n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, block_size=w.block_size,
+                        sink_tokens=w.sink_tokens, sink_format=w.sink_format, recent_tokens=w.recent_tokens,
+                        recent_format=w.recent_format)
+    # sample: whole layers of whole sequences, about 10-30 s of oracle work
+    layers = sample_layers or min(w.n_layers, 36)
+    seqs = [0]
+    if w.max_len > 8192:
+        layers = 1
+    total_in = 0.0
+    total_bytes = 0.0
+    elapsed = 0.0
+    n_tok = 0
+    passes = 0
+    with threadpool_limits(limits=1):
+      while passes < 3 and (passes == 0 or elapsed < 10.0):
+        passes += 1
+        for layer in range(layers):
+            q = wl.queries(w, layer, device="cpu")
+            for s in seqs:
+                L = w.lengths[s]
+                # bounded: at most 16384 tokens of a long sequence
+                Ls = min(L, 16384)
+                kb = wl.to_bits(wl.kv_block(w, "k", layer, s, 0, L, device="cpu")[:Ls])
+                vb = wl.to_bits(wl.kv_block(w, "v", layer, s, 0, L, device="cpu")[:Ls])
+                scalls = [(t0, min(n, Ls - t0)) for ids, t0, n in calls if s in ids and t0 < Ls]
+                qv = ot.values16(wl.to_bits(q[s]), w.dtype)
+                t0 = time.perf_counter()
+                enc = oc.encode_sequence(spec, kb, vb, w.dtype, scalls)
+                pages = [oc.page_tiles(spec, enc, p) for p in range(len(enc.page_format))]
+                out = oa.decode_attention(qv, enc.k_hat, enc.v_hat, Ls, w.sink_tokens, w.window)
+                elapsed += time.perf_counter() - t0
+                stored = sum(p.size for p in pages)
+                n_att = len(oa.attended_tokens(Ls, w.sink_tokens, w.window))
+                att_bytes = n_att * w.n_kv_heads * 2 * (w.head_dim / 4)
+                total_bytes += 2 * kb.nbytes * 2 + stored + att_bytes
+                total_in += kb.nbytes * 2
+                n_tok += Ls
+                del enc, pages, out
+    return {"value": round(total_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(elapsed, 2),
+            "sample": f"{passes} pass(es) over {layers} layer(s) x seq {seqs} x {n_tok // max(1, layers * passes)} tokens: oracle quantize+pack "
+                      f"(every page) + float64 decode attention, algorithmic bytes counted as on the GPU"}
+
+
+if __name__ == "__main__":
+    main()

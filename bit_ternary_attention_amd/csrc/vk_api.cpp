@@ -38,6 +38,69 @@ constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMinUnits = 8;         // 16-token units per split, at least
 constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
 
+// Per-kind launch timing with HIP event pairs recorded on the launch stream.
+class EventTimer : public vk::LaunchTimer {
+ public:
+  bool on = false;
+  int64_t launches[VK_KERNEL_COUNT] = {};
+  double ms[VK_KERNEL_COUNT] = {};
+  double bytes[VK_KERNEL_COUNT] = {};
+
+  ~EventTimer() override {
+    for (Rec& r : pending_) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+    for (hipEvent_t e : pool_) (void)hipEventDestroy(e);
+  }
+  void reset() {
+    flush();
+    for (int k = 0; k < VK_KERNEL_COUNT; ++k) launches[k] = 0, ms[k] = 0.0, bytes[k] = 0.0;
+  }
+  void add_bytes(int kind, double b) {
+    if (on) bytes[kind] += b;
+  }
+  void begin(int kind, hipStream_t s) override {
+    if (!on) return;
+    open_ = Rec{kind, get(), get()};
+    (void)hipEventRecord(open_.a, s);
+  }
+  void end(int kind, hipStream_t s) override {
+    if (!on || open_.kind != kind) return;
+    (void)hipEventRecord(open_.b, s);
+    pending_.push_back(open_);
+    launches[kind] += 1;
+    open_.kind = -1;
+    if (pending_.size() >= 4096) flush();
+  }
+  // Waits for every recorded pair and folds it into the totals.
+  void flush() {
+    for (Rec& r : pending_) {
+      float t = 0.0f;
+      if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) ms[r.kind] += t;
+      pool_.push_back(r.a);
+      pool_.push_back(r.b);
+    }
+    pending_.clear();
+  }
+
+ private:
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  hipEvent_t get() {
+    if (!pool_.empty()) {
+      hipEvent_t e = pool_.back();
+      pool_.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    (void)hipEventCreate(&e);
+    return e;
+  }
+  std::vector<Rec> pending_;
+  std::vector<hipEvent_t> pool_;
+  Rec open_{-1, nullptr, nullptr};
+};
+
 }  // namespace
 
 struct vk_cache {
@@ -58,6 +121,7 @@ struct vk_cache {
   int64_t device_bytes = 0;
   std::vector<void*> allocations;
   vk_stats stats{};
+  EventTimer timer;
 };
 
 namespace {
@@ -283,7 +347,29 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
   a.n_blk = static_cast<int32_t>(n_blk);
   a.max_units = plan.max_units;
   a.eps = cfg.eps;
-  e = vk::launch_append(a, static_cast<int32_t>(n_seg), s);
+  if (c->timer.on) {
+    // algorithmic bytes: pass 1 reads the ternary-routed input once; pass 2 reads
+    // all input once and writes every stored byte once (+ one gamma per ternary page)
+    double tern_tokens = 0.0;
+    for (const vk::AppendSeqDesc& d : plan.seqs) tern_tokens += d.tern_hi - d.tern_lo;
+    const double layers = n_layers;
+    c->timer.add_bytes(VK_KERNEL_ABSMEAN, layers * 2.0 * tern_tokens * row * 2.0);
+    c->timer.add_bytes(VK_KERNEL_FINALIZE, static_cast<double>(n_seg) * n_blk * 8.0);
+    const double in_bytes = layers * n_seqs * 2.0 * n_tokens * row * 2.0;
+    const double per_elem[3] = {0.25, 1.0, 2.0};
+    double out_bytes = 0.0;
+    for (const vk::AppendSeqDesc& d : plan.seqs) {
+      for (int32_t j = 0; j < d.n_pages; ++j) {
+        const int32_t p = d.page_first + j;
+        const int f = vk::entry_fmt(plan.entries[d.page_off + j]);
+        const int64_t lo = std::max<int64_t>(static_cast<int64_t>(p) * cfg.block_size, d.t0);
+        const int64_t hi = std::min<int64_t>(static_cast<int64_t>(p + 1) * cfg.block_size, d.t0 + n_tokens);
+        out_bytes += 2.0 * (hi - lo) * row * per_elem[f] + (f == VK_FMT_TERNARY2 && lo % cfg.block_size == 0 ? 8.0 : 0.0);
+      }
+    }
+    c->timer.add_bytes(VK_KERNEL_PACK, in_bytes + layers * out_bytes);
+  }
+  e = vk::launch_append(a, static_cast<int32_t>(n_seg), s, c->timer.on ? &c->timer : nullptr);
   if (e != hipSuccess) return hip_fail(c, e, "append kernels");
   e = hipEventRecord(c->plan_ev[slot], s);
   if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
@@ -342,7 +428,18 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
         static_cast<int32_t>(std::min<int64_t>(kDecodeMaxSplits, kDecodeScratchItems / items));
     a.n_splits = vk::choose_splits(items, max_units, kDecodeTargetGroups, std::max(1, max_splits), kDecodeMinUnits);
     splits_used = a.n_splits;
-    hipError_t e = vk::launch_decode(a, g, s);
+    if (c->timer.on) {
+      int64_t cu[3] = {0, 0, 0};
+      for (int32_t i = 0; i < nb; ++i) c->host->count_units(seq_ids[base + i], window, cu);
+      const double row = cfg.head_dim;
+      const double unit_kv = 2.0 * 16.0 * cfg.n_kv_heads;  // K and V, 16 tokens, every KV head
+      const double kv_bytes = unit_kv * (cu[0] * row / 4.0 + cu[1] * row + cu[2] * row * 2.0);
+      const double qo = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * (2.0 + 4.0);
+      const double part = static_cast<double>(nb) * cfg.n_q_heads * a.n_splits * (cfg.head_dim + 2) * 4.0;
+      c->timer.add_bytes(VK_KERNEL_DECODE, kv_bytes + qo + (a.n_splits > 1 ? part - nb * cfg.n_q_heads * cfg.head_dim * 4.0 : 0.0));
+      if (a.n_splits > 1) c->timer.add_bytes(VK_KERNEL_MERGE, part + nb * cfg.n_q_heads * cfg.head_dim * 4.0);
+    }
+    hipError_t e = vk::launch_decode(a, g, s, c->timer.on ? &c->timer : nullptr);
     if (e != hipSuccess) return hip_fail(c, e, "decode kernels");
   }
   c->stats.decode_calls += 1;
@@ -363,10 +460,7 @@ VK_API vk_status vk_reset_seqs(vk_cache* c, int32_t n_seqs, const int32_t* seq_i
   if (n_seqs < 0 || (n_seqs > 0 && !seq_ids)) return fail(VK_ERR_ARG, "bad sequence list");
   for (int32_t i = 0; i < n_seqs; ++i)
     if (seq_ids[i] < 0 || seq_ids[i] >= c->cfg.max_seqs) return fail(VK_ERR_ARG, "seq id %d out of range", seq_ids[i]);
-  st = set_device(c);
-  if (st) return st;
-  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(c, e, "hipStreamSynchronize");
+  (void)stream;  // frees are ordered by later appends on the same stream
   st = c->host->reset_seqs(n_seqs, seq_ids, &err);
   if (st) return fail(st, "%s", err.c_str());
   g_error.clear();
@@ -424,6 +518,35 @@ VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out) {
     s.tokens_stored[f] = c->host->tokens_stored(f);
   }
   *out = s;
+  return VK_OK;
+}
+
+VK_API vk_status vk_set_kernel_timing(vk_cache* c, int32_t enable) {
+  vk_status st = check_handle(c);
+  if (st) return st;
+  st = set_device(c);
+  if (st) return st;
+  if (enable) {
+    c->timer.on = true;
+    c->timer.reset();
+  } else {
+    c->timer.flush();
+    c->timer.on = false;
+  }
+  return VK_OK;
+}
+
+VK_API vk_status vk_get_kernel_times(vk_cache* c, int64_t* launches, double* milliseconds, double* bytes) {
+  vk_status st = check_handle(c);
+  if (st) return st;
+  st = set_device(c);
+  if (st) return st;
+  c->timer.flush();
+  for (int k = 0; k < VK_KERNEL_COUNT; ++k) {
+    if (launches) launches[k] = c->timer.launches[k];
+    if (milliseconds) milliseconds[k] = c->timer.ms[k];
+    if (bytes) bytes[k] = c->timer.bytes[k];
+  }
   return VK_OK;
 }
 

@@ -352,30 +352,36 @@ __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
 }
 
 template <int D, int G>
-hipError_t launch_dg(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   const dim3 grid(a.n_splits, a.P.hkv, a.n_seqs);
+  if (t) t->begin(VK_KERNEL_DECODE, s);
   if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
   else k_decode<D, G, 0><<<grid, 64, 0, s>>>(a);
-  if (a.n_splits > 1) k_merge<D><<<dim3(a.hq, a.n_seqs), D, 0, s>>>(a);
+  if (t) t->end(VK_KERNEL_DECODE, s);
+  if (a.n_splits > 1) {
+    if (t) t->begin(VK_KERNEL_MERGE, s);
+    k_merge<D><<<dim3(a.hq, a.n_seqs), D, 0, s>>>(a);
+    if (t) t->end(VK_KERNEL_MERGE, s);
+  }
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const DecodeArgs& a, int32_t group, hipStream_t s) {
+hipError_t launch_d(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t) {
   switch (group) {
-    case 1: return launch_dg<D, 1>(a, s);
-    case 2: return launch_dg<D, 2>(a, s);
-    case 4: return launch_dg<D, 4>(a, s);
-    case 8: return launch_dg<D, 8>(a, s);
+    case 1: return launch_dg<D, 1>(a, s, t);
+    case 2: return launch_dg<D, 2>(a, s, t);
+    case 4: return launch_dg<D, 4>(a, s, t);
+    case 8: return launch_dg<D, 8>(a, s, t);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s) {
-  if (a.P.dim == 128) return launch_d<128>(a, group, s);
-  if (a.P.dim == 64) return launch_d<64>(a, group, s);
+hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t) {
+  if (a.P.dim == 128) return launch_d<128>(a, group, s, t);
+  if (a.P.dim == 64) return launch_d<64>(a, group, s, t);
   return hipErrorInvalidValue;
 }
 

@@ -90,9 +90,18 @@ struct QuantArgs {
   float eps;
 };
 
+// Optional per-launch timing: launchers bracket each kernel with begin/end
+// (kind = VK_KERNEL_* of vk.h).  nullptr = no timing.
+class LaunchTimer {
+ public:
+  virtual ~LaunchTimer() = default;
+  virtual void begin(int kind, hipStream_t s) = 0;
+  virtual void end(int kind, hipStream_t s) = 0;
+};
+
 // Launchers (vk_write.hip, vk_decode.hip).  Return the first HIP error.
-hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, LaunchTimer* t);
+hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 
 }  // namespace vk

@@ -409,17 +409,22 @@ __global__ __launch_bounds__(256) void k_flat_pack(QuantArgs a) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s) {
+hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, LaunchTimer* t) {
   const bool bf = a.dtype == VK_DTYPE_BF16;
   if (a.n_blk > 0) {
     const dim3 g1(a.n_blk, n_seg);
+    if (t) t->begin(VK_KERNEL_ABSMEAN, s);
     if (bf) k_absmean_partial<1><<<g1, kAbsThreads, 0, s>>>(a);
     else k_absmean_partial<0><<<g1, kAbsThreads, 0, s>>>(a);
+    if (t) t->end(VK_KERNEL_ABSMEAN, s);
+    if (t) t->begin(VK_KERNEL_FINALIZE, s);
     if (bf) k_gamma_finalize<1><<<n_seg, 64, 0, s>>>(a);
     else k_gamma_finalize<0><<<n_seg, 64, 0, s>>>(a);
+    if (t) t->end(VK_KERNEL_FINALIZE, s);
   }
   const int n_tasks = a.max_units * 2 * a.P.hkv;
   const dim3 g2(n_tasks < 1024 ? n_tasks : 1024, a.n_layers * a.n_seqs);
+  if (t) t->begin(VK_KERNEL_PACK, s);
   if (a.P.dim == 128) {
     if (bf) k_pack<1, 128><<<g2, 64, 0, s>>>(a);
     else k_pack<0, 128><<<g2, 64, 0, s>>>(a);
@@ -427,6 +432,7 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s) {
     if (bf) k_pack<1, 64><<<g2, 64, 0, s>>>(a);
     else k_pack<0, 64><<<g2, 64, 0, s>>>(a);
   }
+  if (t) t->end(VK_KERNEL_PACK, s);
   return hipGetLastError();
 }
 

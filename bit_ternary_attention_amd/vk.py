@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libvk.so")
 OK, ERR_ARG, ERR_OOM, ERR_CAPACITY, ERR_ALIGN, ERR_STATE, ERR_HIP = range(7)
 DTYPE_F16, DTYPE_BF16 = 0, 1
 FMT_TERNARY2, FMT_FP8E4M3, FMT_F16 = 0, 1, 2
+KERNELS = ("absmean", "finalize", "pack", "decode", "merge")
 
 _c_i32, _c_i64, _c_f32, _c_u64, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_void_p
 
@@ -57,6 +58,9 @@ EXPORTS = {
     "vk_read_pages": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, ctypes.POINTER(_c_i32),
                                ctypes.POINTER(_c_f32)]),
     "vk_get_stats": (_c_i32, [_c_vp, ctypes.POINTER(Stats)]),
+    "vk_set_kernel_timing": (_c_i32, [_c_vp, _c_i32]),
+    "vk_get_kernel_times": (_c_i32, [_c_vp, ctypes.POINTER(_c_i64), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double)]),
     "vk_release": (_c_i32, [_c_vp]),
     "vk_quantize_pack_workspace_bytes": (_c_i64, [_c_i64]),
     "vk_quantize_pack": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
@@ -203,6 +207,17 @@ class Cache:
         s = Stats()
         _check(lib().vk_get_stats(self.handle, ctypes.byref(s)))
         return s.as_dict()
+
+    def kernel_timing(self, enable: bool) -> None:
+        """Start (clearing totals) or stop per-kernel event timing."""
+        _check(lib().vk_set_kernel_timing(self.handle, 1 if enable else 0))
+
+    def kernel_times(self) -> dict:
+        """{kernel: (launches, milliseconds, algorithmic bytes)}; waits for the device."""
+        n = len(KERNELS)
+        la, ms, by = (ctypes.c_int64 * n)(), (ctypes.c_double * n)(), (ctypes.c_double * n)()
+        _check(lib().vk_get_kernel_times(self.handle, la, ms, by))
+        return {k: (int(la[i]), float(ms[i]), float(by[i])) for i, k in enumerate(KERNELS)}
 
     def close(self) -> None:
         if self._h is not None:

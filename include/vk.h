@@ -29,7 +29,8 @@
  *     from vk_last_error() (thread-local).  A HIP failure after enqueueing has
  *     begun poisons the handle: later calls return VK_ERR_STATE.
  *   - No call allocates device memory except vk_create_cache, and none blocks
- *     on the device except vk_read_pages, vk_reset_seqs and vk_release.
+ *     on the device except vk_read_pages, vk_get_kernel_times and vk_release
+ *     (and vk_append, when all its plan staging slots are still in flight).
  *   - A handle is not thread-safe; distinct handles are independent.
  */
 #ifndef VK_H_
@@ -152,9 +153,12 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
                                 const void* q, int32_t q_dtype, int32_t window, float softmax_scale,
                                 float* out, void* stream);
 
-/* Frees every page of the given sequences and sets their length to 0.  Waits
-   for work already enqueued on `stream` first (so pages in flight are not
-   reused early). */
+/* Frees every page of the given sequences and sets their length to 0 (host
+   state only; nothing is enqueued and nothing waits).  Freed pages are handed
+   out again by later vk_append calls; work already enqueued that reads them
+   stays correct as long as those later appends go to the same stream (stream
+   order), so callers that use several streams must order them.  `stream` names
+   that stream and is not otherwise used. */
 VK_API vk_status vk_reset_seqs(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, void* stream);
 
 /* Current length of a sequence (host-side state; no device access). */
@@ -184,6 +188,27 @@ typedef struct vk_stats {
 } vk_stats;
 
 VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out);
+
+/*
+ * Kernel timing (observability).  While enabled, every kernel the handle
+ * launches is bracketed by two HIP events on its stream, and the handle
+ * accumulates per kernel kind: launches, device milliseconds and algorithmic
+ * bytes (the bytes the operation must move: inputs read once per pass,
+ * outputs written once; ternary pages D/4 bytes per token and head).
+ */
+enum {
+  VK_KERNEL_ABSMEAN = 0,   /* write side pass 1: mean |x| partial sums        */
+  VK_KERNEL_FINALIZE = 1,  /* gamma and code threshold per segment            */
+  VK_KERNEL_PACK = 2,      /* write side pass 2: quantise, pack, scatter      */
+  VK_KERNEL_DECODE = 3,    /* paged decode attention (per split)              */
+  VK_KERNEL_MERGE = 4,     /* split-K online-softmax merge                    */
+  VK_KERNEL_COUNT = 5
+};
+/* enable != 0 starts timing and clears the totals; 0 stops it. */
+VK_API vk_status vk_set_kernel_timing(vk_cache* c, int32_t enable);
+/* Waits for the device and returns totals per kind (arrays of VK_KERNEL_COUNT);
+   any pointer may be NULL. */
+VK_API vk_status vk_get_kernel_times(vk_cache* c, int64_t* launches, double* milliseconds, double* bytes);
 
 /* Waits for the device, then frees everything.  NULL is a no-op. */
 VK_API vk_status vk_release(vk_cache* c);

@@ -52,11 +52,12 @@ def pages_needed(w: wl.Workload) -> List[int]:
     return [x + 2 for x in need]
 
 
-def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_pages=(0, 0, 0)) -> vk.Cache:
+def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_pages=(0, 0, 0),
+               max_tokens=None) -> vk.Cache:
     need = pages_needed(w)
     cfg = vk.make_config(n_layers=w.n_layers, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
                          head_dim=w.head_dim, block_size=w.block_size, max_seqs=w.n_seqs,
-                         max_tokens_per_seq=w.max_len, sink_tokens=w.sink_tokens, sink_format=w.sink_format,
+                         max_tokens_per_seq=max_tokens or w.max_len, sink_tokens=w.sink_tokens, sink_format=w.sink_format,
                          recent_tokens=w.recent_tokens, recent_format=w.recent_format,
                          pages_ternary=need[0] + slack_pages[0], pages_fp8=need[1] + slack_pages[1],
                          pages_f16=need[2] + slack_pages[2], eps=eps, fp8_scale=fp8_scale,

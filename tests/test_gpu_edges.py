@@ -210,7 +210,7 @@ def test_many_sequences_subset_and_order():
 
 def test_errors_leave_cache_unchanged_and_usable():
     w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(64, 64), n_seqs=2)
-    cache = make_cache(w)          # exactly the pages two 64-token sequences need (+2 slack)
+    cache = make_cache(w, max_tokens=256)  # exactly the pages two 64-token sequences need (+2 slack)
     fill(cache, w)
     before = cache.stats()
     k = torch.zeros((1, 1, 64, 2, 64), dtype=torch.float16, device="cuda")
