@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Qwen2.5-3B-shaped)")
+    ap.add_argument("--decode-kernel", type=int, default=0, help="0 default, 1 vector ALU, 2 matrix cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=0, help="0 = workload's own sample rule")
     return ap.parse_args()
@@ -61,7 +62,7 @@ def main():
                          head_dim=w.head_dim, block_size=w.block_size, max_seqs=w.n_seqs,
                          max_tokens_per_seq=w.max_len, sink_tokens=w.sink_tokens, sink_format=w.sink_format,
                          recent_tokens=w.recent_tokens, recent_format=w.recent_format,
-                         page_shuffle_seed=w.page_shuffle_seed)
+                         page_shuffle_seed=w.page_shuffle_seed, decode_kernel=args.decode_kernel)
     need = [0, 0, 0]
     bs = w.block_size
     for s in range(w.n_seqs):
@@ -175,7 +176,8 @@ def main():
                         "hbm_frac": round(read_bytes / (read_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                         "bytes_per_step": read_bytes, "device_ms_per_step": round(read_ms, 4),
                         "us_per_layer": round(read_ms * 1e3 / w.n_layers, 3),
-                        "splits": stats["last_decode_splits"], "units_by_format": stats["last_decode_units"]},
+                        "splits": stats["last_decode_splits"], "units_by_format": stats["last_decode_units"],
+                        "kernel": {0: "default (matrix cores)", 1: "vector ALU", 2: "matrix cores"}[args.decode_kernel]},
         "kernels": kernels,
         "ms_per_step_with_kernel_timing": round(ms_step_timed, 4),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS,

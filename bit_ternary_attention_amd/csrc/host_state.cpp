@@ -47,7 +47,7 @@ std::string validate_config(const vk_cache_config& c) {
   if (c.sink_tokens < 0) return "sink_tokens must be >= 0";
   if (c.recent_tokens < 0) return "recent_tokens must be >= 0";
   if (!valid_format(c.sink_format) || !valid_format(c.recent_format)) return "unknown page format";
-  if (c.reserved0 != 0) return "reserved0 must be 0";
+  if (c.decode_kernel < 0 || c.decode_kernel > 2) return "decode_kernel must be 0, 1 or 2";
   if (c.pages_ternary < 0 || c.pages_fp8 < 0 || c.pages_f16 < 0) return "pool capacities must be >= 0";
   if (c.pages_ternary >= (1ll << 30) || c.pages_fp8 >= (1ll << 30) || c.pages_f16 >= (1ll << 30))
     return "pool capacities must be < 2^30 pages";

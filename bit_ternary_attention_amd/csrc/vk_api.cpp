@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <string>
@@ -35,8 +36,13 @@ constexpr int64_t kMaxPartials = 1 << 20;  // float64 absmean partials per appen
 constexpr int64_t kMaxSegs = 65535;        // (layer, seq, K|V) segments per append call (grid y)
 constexpr int kDecodeTargetGroups = 4096;  // work groups a decode launch aims for
 constexpr int kDecodeMaxSplits = 64;
-constexpr int kDecodeMinUnits = 8;         // 16-token units per split, at least
+constexpr int kDecodeMinUnits = 4;         // 16-token units per split, at least (vector-ALU kernel)
+constexpr int kDecodeMinUnitsPerWave = 8;  // matrix-core kernel: units per wave, at least
 constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
+int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
+  const char* e = std::getenv("VK_DECODE_UPI");
+  return (e && e[0] == '4') ? 4 : 8;
+}
 
 // Per-kind launch timing with HIP event pairs recorded on the launch stream.
 class EventTimer : public vk::LaunchTimer {
@@ -154,6 +160,7 @@ std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
   s.push_back(kMaxSegs * static_cast<int64_t>(sizeof(vk::SegInfo)));  // segment info
   s.push_back(partial_count(cfg) * 4);                                // decode split partials
   for (int r = 0; r < kRing; ++r) s.push_back(plan_bytes_for(cfg));   // staged plans
+  s.push_back(vk::page_bytes(cfg, VK_FMT_TERNARY2));                          // dummy page
   return s;
 }
 
@@ -238,8 +245,9 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
     c->device_bytes += sizes[i];
   }
   c->allocations = ptrs;
-  // pools and gamma start zeroed (finite bytes everywhere); the block table starts empty
-  for (size_t i = 0; i < 4; ++i)
+  // pools and gamma start zeroed (finite bytes everywhere); the block table starts empty;
+  // the dummy page (target of speculative decode loads) is zero too
+  for (size_t i : {size_t(0), size_t(1), size_t(2), size_t(3), size_t(8 + kRing)})
     if (ptrs[i]) {
       e = hipMemset(ptrs[i], 0, static_cast<size_t>(sizes[i]));
       if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)); }
@@ -267,6 +275,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   c->partials = static_cast<double*>(ptrs[5]);
   c->seg = static_cast<vk::SegInfo*>(ptrs[6]);
   c->dec_partials = static_cast<float*>(ptrs[7]);
+  P.dummy_page = static_cast<const uint8_t*>(ptrs[8 + kRing]);
   c->plan_bytes = plan_bytes_for(*cfg);
   for (int r = 0; r < kRing; ++r) {
     c->plan_dev[r] = static_cast<uint8_t*>(ptrs[8 + r]);
@@ -414,6 +423,8 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     a.hq = cfg.n_q_heads;
     a.sink_tokens = cfg.sink_tokens;
     a.window = window;
+    a.kernel = cfg.decode_kernel == VK_DECODE_VALU ? VK_DECODE_VALU : VK_DECODE_MFMA;
+    a.units_per_iter = decode_units_per_iter();
     a.scale_log2 = scale * 1.4426950408889634f;
     int32_t max_units = 0;
     for (int32_t i = 0; i < nb; ++i) {
@@ -426,7 +437,11 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     const int64_t items = static_cast<int64_t>(nb) * cfg.n_kv_heads;
     const int32_t max_splits =
         static_cast<int32_t>(std::min<int64_t>(kDecodeMaxSplits, kDecodeScratchItems / items));
-    a.n_splits = vk::choose_splits(items, max_units, kDecodeTargetGroups, std::max(1, max_splits), kDecodeMinUnits);
+    const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
+    a.n_splits = mfma ? vk::choose_splits(items, max_units, kDecodeTargetGroups / 4, std::max(1, max_splits),
+                                          4 * kDecodeMinUnitsPerWave)
+                      : vk::choose_splits(items, max_units, kDecodeTargetGroups, std::max(1, max_splits),
+                                          kDecodeMinUnits);
     splits_used = a.n_splits;
     if (c->timer.on) {
       int64_t cu[3] = {0, 0, 0};
@@ -437,7 +452,10 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       const double qo = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * (2.0 + 4.0);
       const double part = static_cast<double>(nb) * cfg.n_q_heads * a.n_splits * (cfg.head_dim + 2) * 4.0;
       c->timer.add_bytes(VK_KERNEL_DECODE, kv_bytes + qo + (a.n_splits > 1 ? part - nb * cfg.n_q_heads * cfg.head_dim * 4.0 : 0.0));
-      if (a.n_splits > 1) c->timer.add_bytes(VK_KERNEL_MERGE, part + nb * cfg.n_q_heads * cfg.head_dim * 4.0);
+      if (a.n_splits > 1) {
+        const double merge_bytes = part + nb * cfg.n_q_heads * cfg.head_dim * 4.0;
+        c->timer.add_bytes(VK_KERNEL_MERGE, merge_bytes);
+      }
     }
     hipError_t e = vk::launch_decode(a, g, s, c->timer.on ? &c->timer : nullptr);
     if (e != hipSuccess) return hip_fail(c, e, "decode kernels");

@@ -18,10 +18,11 @@
 //   softmax the reference max is shared by the wave (cross-lane max), so
 //           probabilities of all four units are comparable; they go to LDS
 //           as f16 (scaled by 2^14 to stay clear of f16 subnormals);
-//   PV      lane = head dimension: the value tile is stored dimension-major,
-//           so one 32-bit word holds 16 tokens of one dimension; pairs of
-//           tokens are unpacked the same way and dotted with the matching
-//           probability pairs; gamma_V (or the fp8 scale) is applied per unit.
+//   PV      lane = head dimension: the value chunks of a unit hold two
+//           consecutive tokens of one dimension in the two 16-bit halves of a
+//           word, so pairs of tokens are unpacked the same way and dotted with
+//           the matching probability pairs; gamma_V (or the fp8 scale) is
+//           applied per unit.
 // Splits write (o, max, sum) partials that k_merge combines; with one split
 // the kernel writes the normalised output.
 #include <hip/hip_runtime.h>
@@ -259,15 +260,29 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
         for (int j = 0; j < DPL; ++j) tmp[hh][j] = 0.0f;
       float vscale;
       if (fmt == VK_FMT_TERNARY2) {
+        // value chunks of this unit: chunk 4*(d%16) + g holds tokens 4g..4g+3 of dimension d
+        const uint8_t* vu = vt + upi * 4 * D;
 #pragma unroll
         for (int j = 0; j < DPL; ++j) {
           const int dd = lane * DPL + j;
-          const uint32_t wv = reinterpret_cast<const uint32_t*>(vt)[dd * (P.bs >> 4) + upi];
+          const int cq = dd & 15, jj = dd >> 4;
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const h2_t c2 = tern2(wv, ii);
+          for (int g = 0; g < 4; ++g) {
+            h2_t c01, c23;  // tokens (4g, 4g+1) and (4g+2, 4g+3)
+            if (D == 128) {
+              const uint2 x = *reinterpret_cast<const uint2*>(vu + (cq * 4 + g) * (D / 16));
+              c01 = tern2(x.x, jj);
+              c23 = tern2(x.y, jj);
+            } else {
+              const uint32_t x = *reinterpret_cast<const uint32_t*>(vu + (cq * 4 + g) * (D / 16));
+              c01 = tern2(x, jj);
+              c23 = tern2(x, jj + 4);
+            }
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) tmp[hh][j] = dot2(pp[hh * 8 + ii], c2, tmp[hh][j]);
+            for (int hh = 0; hh < G; ++hh) {
+              tmp[hh][j] = dot2(pp[hh * 8 + 2 * g], c01, tmp[hh][j]);
+              tmp[hh][j] = dot2(pp[hh * 8 + 2 * g + 1], c23, tmp[hh][j]);
+            }
           }
         }
         vscale = P.gamma[(layer * P.cap[0] + idx) * 2 + 1];
@@ -331,32 +346,474 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
   }
 }
 
-// Combines split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-template <int D>
-__global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
-  const int64_t qh = static_cast<int64_t>(blockIdx.y) * a.hq + blockIdx.x;
-  const int dd = threadIdx.x;
-  const float* base = a.partials + qh * a.n_splits * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, base[s * (D + 2) + D]);
-  float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ls = base[s * (D + 2) + D + 1];
-    if (ls > 0.0f) {
-      const float w = exp2f(base[s * (D + 2) + D] - M);
-      num = fmaf(w, base[s * (D + 2) + dd], num);
-      den = fmaf(w, ls, den);
+// ------------------------------------------------------------------------
+// Matrix-core variant.  Per 16-token unit:
+//   S^T[16 tok x 16 heads] = K[16 x D] * Q^T[D x 16]   (D/32 x v_mfma_f32_16x16x32_f16)
+//   O^T[D x 16 heads]     += V^T[D x 16] * P[16 x 16]   (D/16 x v_mfma_f32_16x16x16_f16)
+// Lane l holds token/dimension row l%16 of the A operands and query head l%16
+// of the B operands; the score output (lane l: tokens 4(l/16)+r, head l%16) is
+// exactly the P operand layout of the second product, so probabilities never
+// leave registers.  Query heads beyond the group (g < 16) are zero columns.
+//
+// Codes enter the products as u = code + 1 in {0, 1, 2}: the f16 bit pattern
+// u << 10 is the value u * 2^-14 (0, the smallest normal, twice it), so each
+// pair of codes costs one shift and one AND.  The offsets are removed once per
+// head: sum_d q_d (u_d - 1) = 2^14 * acc - sum_d q_d for scores, and
+// sum_t p_t (u_t - 1) = 2^14 * acc - sum_t p_t for the output.
+//
+// Four waves share one (sequence, KV head, split): each walks a quarter of
+// its units (prefetching codes PF units ahead into registers, one block-table
+// entry and gamma pair per lane for 64 units at a time), and the four partial
+// states are merged through LDS.  Global splits, when there are several, are
+// merged by k_merge.
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaWaves = 4;
+
+__device__ __forceinline__ uint32_t h2u(h2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// 2-bit fields at bit s of each 16-bit half, as f16 u * 2^-14 (bit pattern u << 10).
+template <int S>
+__device__ __forceinline__ uint32_t ucode2(uint32_t w) {
+  if (S <= 10) return (w << (10 - S)) & 0x0C000C00u;
+  return (w >> (S - 10)) & 0x0C000C00u;
+}
+
+template <int NC, int NV>
+struct UnitRaw {
+  uint32_t k[NC];  // key codes of token l%16, dims of lane group l/16
+  uint32_t v[NV];  // value chunk 4(l%16) + l/16: tokens 4(l/16)..+3 of dims 16j + l%16
+};
+
+// A operands of the score product: pairs (d, d+8) of each 16-dimension code word.
+template <int NS, int NC>
+__device__ __forceinline__ void ka_ternary(const uint32_t (&k)[NC], h8_t (&ka)[NS]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{ucode2<0>(k[c]), ucode2<2>(k[c]), ucode2<4>(k[c]), ucode2<6>(k[c])});
+    ka[2 * c + 1] =
+        __builtin_bit_cast(h8_t, u4_t{ucode2<8>(k[c]), ucode2<10>(k[c]), ucode2<12>(k[c]), ucode2<14>(k[c])});
+  }
+}
+
+// A operand of block j of the value product: tokens (4g, 4g+1), (4g+2, 4g+3) of dim 16j + l%16.
+template <int NV, int J>
+__device__ __forceinline__ h4_t va_ternary(const uint32_t (&v)[NV]) {
+  if (NV == 2) return __builtin_bit_cast(h4_t, u2_t{ucode2<2 * J>(v[0]), ucode2<2 * J>(v[NV - 1])});
+  return __builtin_bit_cast(h4_t, u2_t{ucode2<2 * J>(v[0]), ucode2<2 * J + 8>(v[0])});
+}
+
+template <int NV, int NB, int J = 0>
+__device__ __forceinline__ void va_all(const uint32_t (&v)[NV], h4_t (&va)[NB]) {
+  if constexpr (J < NB) {
+    va[J] = va_ternary<NV, J>(v);
+    va_all<NV, NB, J + 1>(v, va);
+  }
+}
+
+template <int D, int G, int QDT, int PF>
+__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_decode_mfma(DecodeArgs a) {
+  constexpr int NC = D / 64;   // 32-bit key code words per lane per unit
+  constexpr int NV = D / 64;   // 32-bit value chunk words per lane per unit
+  constexpr int NS = D / 32;   // 16x16x32 steps per unit
+  constexpr int NB = D / 16;   // 16-dimension output blocks (P*V products per unit)
+  constexpr int CH = 64;       // units per metadata chunk (one per lane)
+  constexpr int UG = 2;        // units sharing one online-softmax update
+  static_assert(G <= 16, "one query head per lane column");
+  static_assert(CH % PF == 0 && PF % UG == 0, "chunks hold whole prefetch rounds and groups");
+  __shared__ float lds_o[kMfmaWaves][G][D];
+  __shared__ float lds_m[kMfmaWaves][G], lds_l[kMfmaWaves][G];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, c16 = lane & 15;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int slot = a.slots[b], L = a.lens[b];
+  const PoolsView& P = a.P;
+  const Units R = attended(L, a.sink_tokens, a.window);
+  const int n_a = R.a_end;
+  const int U = R.a_end + (R.b_end - R.b_begin);
+  const int s_begin = static_cast<int>((static_cast<int64_t>(split) * U) / a.n_splits);
+  const int s_end = static_cast<int>((static_cast<int64_t>(split + 1) * U) / a.n_splits);
+  const int u_begin = s_begin + ((s_end - s_begin) * wave) / kMfmaWaves;
+  const int u_end = s_begin + ((s_end - s_begin) * (wave + 1)) / kMfmaWaves;
+  const int dbase = grp * (D / 4);  // first head dimension of this lane group's key slice
+  const int64_t layer = a.layer;
+  const int32_t* bt = P.block_table + static_cast<int64_t>(slot) * P.max_pages;
+  const int tile0 = static_cast<int>(P.tile_bytes[0]);
+  const int64_t qh0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+
+  auto unit_of = [&](int lu) { return lu < n_a ? lu : R.b_begin + (lu - n_a); };
+  // every token of logical units [lu, lu + n) is attended
+  auto fully_attended = [&](int lu, int n) {
+    if (lu + n > u_end) return false;
+    const int u0 = unit_of(lu), u1 = unit_of(lu + n - 1);
+    if (u1 - u0 != n - 1) return false;
+    if (R.single) return (u1 * 16 + 16) <= L;
+    return (u1 * 16 + 16 <= R.sinks) || (u0 * 16 >= R.w0 && u1 * 16 + 16 <= L);
+  };
+  // Per-chunk unit metadata, one unit per lane: block-table entry and, for ternary pages,
+  // the K and V gamma (lanes past the end repeat the last unit).
+  struct Chunk {
+    int32_t ent;
+    float gk, gv;
+  };
+  auto load_chunk = [&](int c0) -> Chunk {
+    const int lu = min(c0 + lane, max(u_end - 1, 0));
+    Chunk c;
+    c.ent = bt[(unit_of(lu) * 16) >> P.bs_shift];
+    const bool tern = (static_cast<uint32_t>(c.ent) >> 30) == VK_FMT_TERNARY2;
+    const float* gp = tern ? P.gamma + (layer * P.cap[0] + (c.ent & 0x3FFFFFFF)) * 2
+                           : reinterpret_cast<const float*>(P.dummy_page);
+    const float2 gg = *reinterpret_cast<const float2*>(gp);
+    c.gk = gg.x;
+    c.gv = gg.y;
+    return c;
+  };
+
+  // query head c16 (zero beyond the group) as the B operand of the score product, and its sum
+  h8_t qb[NS];
+  float qsum = 0.0f;
+  {
+    const uint16_t* qrow = a.q + (qh0 + (c16 < G ? c16 : 0)) * D + dbase;
+    uint32_t w[NS][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 x0 = reinterpret_cast<const uint4*>(qrow + 16 * c)[0];  // dims 16c .. 16c+7
+      const uint4 x1 = reinterpret_cast<const uint4*>(qrow + 16 * c)[1];  // dims 16c+8 .. 16c+15
+      const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t e0 = (lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t e1 = (hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t pr =
+            c16 < G ? (q_f16<QDT>(static_cast<uint16_t>(e0)) | (q_f16<QDT>(static_cast<uint16_t>(e1)) << 16)) : 0u;
+        w[2 * c + (i >> 2)][i & 3] = pr;
+        const h2_t hp = as_h2(pr);
+        qsum += static_cast<float>(hp[0]) + static_cast<float>(hp[1]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qb[s] = __builtin_bit_cast(h8_t, u4_t{w[s][0], w[s][1], w[s][2], w[s][3]});
+    qsum += __shfl_xor(qsum, 16, 64);
+    qsum += __shfl_xor(qsum, 32, 64);
+  }
+
+  f4_t oacc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) oacc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+  // oacc = sum p' u 2^-14 and sacc = sum p' (p' = f16(p 2^14)), both in units of vcur
+  float m = -INFINITY, lsum = 0.0f, sacc = 0.0f, vcur = 0.0f;
+
+  // Packed codes of logical unit lu into r.  Always issued (a fixed number of loads per
+  // unit, so the compiler can wait precisely): other formats and units past the end
+  // read the zeroed dummy page instead.
+  auto load_raw = [&](int lu, const Chunk& cc, const Chunk& cn, int c0, UnitRaw<NC, NV>& r) {
+    const int k = min(lu, max(u_end - 1, 0)) - c0;
+    const int32_t entry = k < CH ? __builtin_amdgcn_readlane(cc.ent, k) : __builtin_amdgcn_readlane(cn.ent, k - CH);
+    const bool tern = lu < u_end && (static_cast<uint32_t>(entry) >> 30) == VK_FMT_TERNARY2;
+    const int upi = tern ? ((unit_of(lu) * 16) & (P.bs - 1)) >> 4 : 0;
+    const uint8_t* pg =
+        tern ? P.pool[0] + (layer * P.cap[0] + (entry & 0x3FFFFFFF)) * P.page_bytes[0] : P.dummy_page;
+    const uint8_t* krow = pg + kvh * tile0 + (upi * 16 + c16) * (D / 4) + grp * (D / 16);
+    const uint8_t* vch = pg + (P.hkv + kvh) * tile0 + upi * 4 * D + (4 * c16 + grp) * (D / 16);
+    if (NC == 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(krow);
+      const uint2 y = *reinterpret_cast<const uint2*>(vch);
+      r.k[0] = x.x;
+      r.k[NC - 1] = x.y;
+      r.v[0] = y.x;
+      r.v[NV - 1] = y.y;
+    } else {
+      r.k[0] = *reinterpret_cast<const uint32_t*>(krow);
+      r.v[0] = *reinterpret_cast<const uint32_t*>(vch);
+    }
+  };
+
+  // A operands and scales of a non-ternary unit, loaded here (f16 values, not u * 2^-14)
+  auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float& scale) {
+    const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
+    const int64_t idx = entry & 0x3FFFFFFF;
+    const int upi = ((unit_of(lu) * 16) & (P.bs - 1)) >> 4;
+    if (fmt == VK_FMT_FP8E4M3) {
+      const uint8_t* pg = P.pool[1] + (layer * P.cap[1] + idx) * P.page_bytes[1];
+      const uint4* kp = reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[1] + (upi * 16 + c16) * D + dbase);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 x = kp[c];
+        const uint32_t lo[2] = {x.x, x.y}, hi[2] = {x.z, x.w};
+        uint32_t t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t bl = (lo[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          const uint32_t bh = (hi[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          t[i] = h2u(fp8x2(bl | (bh << 16)));
+        }
+        ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{t[0], t[1], t[2], t[3]});
+        ka[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{t[4], t[5], t[6], t[7]});
+      }
+      const uint8_t* vt = pg + (P.hkv + kvh) * P.tile_bytes[1];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t x =
+            *reinterpret_cast<const uint32_t*>(vt + static_cast<int64_t>(16 * j + c16) * P.bs + upi * 16 + 4 * grp);
+        va[j] = __builtin_bit_cast(h4_t, u2_t{h2u(fp8x2((x & 0xFFu) | ((x & 0xFF00u) << 8))),
+                                              h2u(fp8x2(((x >> 16) & 0xFFu) | ((x >> 8) & 0x00FF0000u)))});
+      }
+      scale = P.fp8_scale;
+    } else {
+      const uint8_t* pg = P.pool[2] + (layer * P.cap[2] + idx) * P.page_bytes[2];
+      const uint4* kp =
+          reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[2] + ((upi * 16 + c16) * D + dbase) * 2);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 x0 = kp[2 * c], x1 = kp[2 * c + 1];
+        const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+        uint32_t t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          t[i] = ((lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) | (((hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+        ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{t[0], t[1], t[2], t[3]});
+        ka[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{t[4], t[5], t[6], t[7]});
+      }
+      const uint8_t* vt = pg + (P.hkv + kvh) * P.tile_bytes[2];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint2 x =
+            *reinterpret_cast<const uint2*>(vt + (static_cast<int64_t>(16 * j + c16) * P.bs + upi * 16 + 4 * grp) * 2);
+        va[j] = __builtin_bit_cast(h4_t, u2_t{x.x, x.y});
+      }
+      scale = 1.0f;
+    }
+  };
+
+  // UG consecutive units: scores, one online-softmax update, then P*V.
+  auto process_group = [&](int lu0, const Chunk& cc, int c0, const UnitRaw<NC, NV>* raw) {
+    float sc[UG][4];
+    h4_t va[UG][NB];
+    float vsc[UG];
+    bool tern[UG];
+    const bool full = fully_attended(lu0, UG);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < UG; ++g) {
+      const int lu = lu0 + g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[g][r] = -INFINITY;
+      vsc[g] = 0.0f;
+      tern[g] = true;
+      if (lu >= u_end) continue;
+      const int k = lu - c0;
+      const int32_t entry = __builtin_amdgcn_readlane(cc.ent, k);
+      h8_t ka[NS];
+      float a0, a1;  // logit = a0 * acc + a1
+      if ((static_cast<uint32_t>(entry) >> 30) == VK_FMT_TERNARY2) {
+        ka_ternary<NS, NC>(raw[g].k, ka);
+        const float gk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cc.gk), k));
+        vsc[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cc.gv), k));
+        const float ks = gk * a.scale_log2;
+        a0 = ks * 16384.0f;
+        a1 = -qsum * ks;
+      } else {
+        tern[g] = false;
+        float scale;
+        operands_other(lu, entry, ka, va[g], scale);
+        vsc[g] = scale;
+        a0 = scale * a.scale_log2;
+        a1 = 0.0f;
+      }
+      f4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
+      } else {
+        const int u = unit_of(lu);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = u * 16 + 4 * grp + r;
+          const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
+          sc[g][r] = att ? fmaf(s4[r], a0, a1) : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[g][r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (__ballot(mx > m) != 0) {  // uniform; per-lane factors (lane = head)
+      const float mn = fmaxf(m, mx);
+      const float corr = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) oacc[j] *= corr;
+      lsum *= corr;
+      sacc *= corr;
+      m = mn;
+    }
+#pragma unroll
+    for (int g = 0; g < UG; ++g) {
+      if (lu0 + g >= u_end) break;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = sc[g][r] == -INFINITY ? 0.0f : exp2f(sc[g][r] - m);
+        lsum += p[r];
+      }
+      const float vscale = vsc[g];
+      if (vscale == 0.0f) continue;  // every value of the page is 0: no contribution
+      if (vscale != vcur) {          // uniform: keep the sums in units of the current value scale
+        const float ratio = vcur / vscale;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) oacc[j] *= ratio;
+        sacc *= ratio;
+        vcur = vscale;
+      }
+      const h2_t p01 = h2_t{static_cast<_Float16>(p[0] * 16384.0f), static_cast<_Float16>(p[1] * 16384.0f)};
+      const h2_t p23 = h2_t{static_cast<_Float16>(p[2] * 16384.0f), static_cast<_Float16>(p[3] * 16384.0f)};
+      const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(p01), h2u(p23)});
+      if (tern[g]) {
+        sacc += (static_cast<float>(p01[0]) + static_cast<float>(p01[1])) +
+                (static_cast<float>(p23[0]) + static_cast<float>(p23[1]));
+        h4_t vt[NB];
+        va_all<NV, NB>(raw[g].v, vt);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt[j], pb, oacc[j], 0, 0, 0);
+      } else {
+        // f16 / fp8 values enter as themselves: add 2^-14 v so that 2^14 oacc - sacc keeps counting v
+        constexpr float kInv = 1.0f / 16384.0f;
+        f4_t tmp[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          tmp[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[g][j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          oacc[j] += tmp[j] * kInv;
+        }
+      }
+    }
+  };
+
+  if (u_begin < u_end) {
+    Chunk ch_cur = load_chunk(u_begin);
+    Chunk ch_nxt = load_chunk(u_begin + CH);
+    UnitRaw<NC, NV> ring[PF];
+#pragma unroll
+    for (int t = 0; t < PF; ++t) load_raw(u_begin + t, ch_cur, ch_nxt, u_begin, ring[t]);
+    for (int c0 = u_begin; c0 < u_end; c0 += CH) {
+      const int c_end = min(c0 + CH, u_end);
+#pragma unroll 1
+      for (int k = c0; k < c_end; k += UG) {
+        process_group(k, ch_cur, c0, ring);
+        // shift the ring by one group and fetch the group PF units ahead into its tail
+#pragma unroll
+        for (int t = 0; t + UG < PF; ++t) ring[t] = ring[t + UG];
+#pragma unroll
+        for (int g = 0; g < UG; ++g) load_raw(k + PF + g, ch_cur, ch_nxt, c0, ring[PF - UG + g]);
+      }
+      ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
+      ch_nxt = load_chunk(c0 + 2 * CH);
     }
   }
-  a.out[qh * D + dd] = num / den;
+
+  // ---------------- this wave's partial state -> LDS ----------------
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  sacc += __shfl_xor(sacc, 16, 64);
+  sacc += __shfl_xor(sacc, 32, 64);
+  if (c16 < G) {
+    const float sub = sacc * (1.0f / 16384.0f);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lds_o[wave][c16][16 * j + 4 * grp + r] = (oacc[j][r] - sub) * vcur;
+    if (grp == 0) {
+      lds_m[wave][c16] = m;
+      lds_l[wave][c16] = lsum;
+    }
+  }
+  __syncthreads();
+
+  // ---------------- merge the four waves ----------------
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kMfmaWaves) {
+    const int hh = idx / D, dd = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; ++w) M = fmaxf(M, lds_m[w][hh]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; ++w) {
+      const float lw = lds_l[w][hh];
+      if (lw > 0.0f) {
+        const float wt = exp2f(lds_m[w][hh] - M);
+        num = fmaf(wt, lds_o[w][hh][dd], num);
+        den = fmaf(wt, lw, den);
+      }
+    }
+    const int64_t qh = qh0 + hh;
+    if (a.n_splits == 1) {
+      a.out[qh * D + dd] = num / den;
+    } else {
+      float* part = a.partials + (qh * a.n_splits + split) * (D + 2);
+      part[dd] = num;
+      if (dd == 0) {
+        part[D] = M;
+        part[D + 1] = den;
+      }
+    }
+  }
+}
+
+// Combines split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// One block per (sequence, query head); weights computed once into LDS, then
+// every dimension sums its column with eight independent loads in flight.
+template <int D>
+__global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
+  __shared__ float wts[64];
+  __shared__ float den_s;
+  const int64_t qh = static_cast<int64_t>(blockIdx.y) * a.hq + blockIdx.x;
+  const int dd = threadIdx.x;
+  const int ns = a.n_splits;  // <= 64
+  const float* base = a.partials + qh * ns * (D + 2);
+  if (dd < 64) {
+    const float ms = dd < ns ? base[dd * (D + 2) + D] : -INFINITY;
+    const float ls = dd < ns ? base[dd * (D + 2) + D + 1] : 0.0f;
+    float M = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float wgt = ls > 0.0f ? exp2f(ms - M) : 0.0f;
+    float den = wgt * ls;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    wts[dd] = wgt;
+    if (dd == 0) den_s = den;
+  }
+  __syncthreads();
+  float num = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float o8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o8[k] = s0 + k < ns ? base[(s0 + k) * (D + 2) + dd] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) num = s0 + k < ns ? fmaf(wts[s0 + k], o8[k], num) : num;
+  }
+  a.out[qh * D + dd] = num / den_s;
 }
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   const dim3 grid(a.n_splits, a.P.hkv, a.n_seqs);
   if (t) t->begin(VK_KERNEL_DECODE, s);
-  if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
-  else k_decode<D, G, 0><<<grid, 64, 0, s>>>(a);
+  if (a.kernel == VK_DECODE_VALU) {
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
+    else k_decode<D, G, 0><<<grid, 64, 0, s>>>(a);
+  } else if (a.units_per_iter == 8) {
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 8><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+  } else {
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 4><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 4><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+  }
   if (t) t->end(VK_KERNEL_DECODE, s);
   if (a.n_splits > 1) {
     if (t) t->begin(VK_KERNEL_MERGE, s);

@@ -27,6 +27,7 @@ struct PoolsView {
   int32_t bs_shift;        // log2(bs)
   float fp8_scale;
   int32_t pad;
+  const uint8_t* dummy_page;  // a zeroed ternary-page-sized buffer: target of speculative loads
 };
 
 struct SegInfo {           // per (layer, seq, K|V) of one append call
@@ -72,6 +73,8 @@ struct DecodeArgs {
   int32_t sink_tokens;
   int32_t window;
   int32_t n_splits;
+  int32_t kernel;          // VK_DECODE_VALU or VK_DECODE_MFMA
+  int32_t units_per_iter;  // matrix-core kernel: prefetch depth in 16-token units (4 or 8)
   float scale_log2;        // softmax scale * log2(e)
   int32_t slots[kDecodeMaxSeqs];
   int32_t lens[kDecodeMaxSeqs];

@@ -13,7 +13,8 @@
 //                      and the exact 16-bit magnitude threshold of a nonzero code
 //   k_pack             pass 2: one wave per (16-token unit, K|V, head) tile;
 //                      codes from an integer compare against the threshold,
-//                      keys stored token-major, values transposed through LDS
+//                      keys stored token-major, values rearranged through LDS
+//                      into per-unit chunks (one chunk per decode lane)
 //
 // Exactness of the threshold: with d = gamma + eps > 0 and RNE float32
 // division, round(x/d) is nonzero exactly when the float32 quotient exceeds
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   constexpr int CPR = D / 8;     // 16-byte chunks per token row
   constexpr int RPI = 64 / CPR;  // rows per wave-wide load
   constexpr int NI = 16 / RPI;   // loads per lane per unit
-  constexpr int DPL = D / 64;    // head dims per lane in the transposed value store
+  constexpr int DPL = D / 64;    // head dims per lane in the transposed fp8 / fp16 value stores
   __shared__ uint32_t lds[D * 16 * 2 / 4 + 4];
   uint16_t* lds16 = reinterpret_cast<uint16_t*>(lds);
   uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
@@ -253,22 +254,27 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
           lds16[c * 16 + r] = static_cast<uint16_t>(code_word8(w[k], si.thresh));
         }
         __syncthreads();
-        // dims lane*DPL .. +DPL-1 share chunk cc; rows (2m, 2m+1) arrive as one dword
-        const int dd0 = lane * DPL;
-        const int cc = dd0 / 8, e0 = dd0 % 8;
-        const uint32_t* colw = reinterpret_cast<const uint32_t*>(lds16 + cc * 16);
-        uint32_t word[DPL];
+        // value tile, chunked per 16-token unit: lane = chunk 4*cq + g = tokens 4g..4g+3 of
+        // dimensions 16j + cq; LDS rows (4g, 4g+1) and (4g+2, 4g+3) arrive as one dword each
+        const int cq = lane >> 2, g = lane & 3;
+        const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds16);
+        uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) word[j] = 0;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const uint32_t x = colw[m];
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) word[j] |= ((x >> (2 * (e0 + j))) & 0x00030003u) << (2 * m);
+        for (int j = 0; j < D / 16; ++j) {
+          const int dd = 16 * j + cq;
+          const int cc = dd >> 3, e = dd & 7;
+          const uint32_t f01 = (l32[cc * 8 + 2 * g] >> (2 * e)) & 0x00030003u;
+          const uint32_t f23 = (l32[cc * 8 + 2 * g + 1] >> (2 * e)) & 0x00030003u;
+          if (D == 128) {
+            w0 |= f01 << (2 * j);
+            w1 |= f23 << (2 * j);
+          } else {
+            w0 |= (f01 << (2 * j)) | (f23 << (8 + 2 * j));
+          }
         }
-        uint32_t* vout = reinterpret_cast<uint32_t*>(tile);
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) vout[(dd0 + j) * (a.P.bs / 16) + upi] = word[j];
+        uint8_t* vdst = tile + upi * 4 * D + lane * (D / 16);
+        if (D == 128) *reinterpret_cast<uint2*>(vdst) = make_uint2(w0, w1);
+        else *reinterpret_cast<uint32_t*>(vdst) = w0;
         __syncthreads();
       }
     } else if (fmt == VK_FMT_FP8E4M3) {

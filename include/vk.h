@@ -66,6 +66,14 @@ enum {
   VK_FMT_F16 = 2        /* IEEE float16, round to nearest even from the input                    */
 };
 
+/* decode kernels (same results within the decode tolerance; see vk_decode_attn) */
+enum {
+  VK_DECODE_DEFAULT = 0,  /* the library's choice (currently VK_DECODE_MFMA)                      */
+  VK_DECODE_VALU = 1,     /* vector ALU: v_dot2_f32_f16 over unpacked codes, query rows in LDS     */
+  VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores, 16x16x16 f16 P*V, codes unpacked
+                             to f16 in registers, query rows resident as the B operand             */
+};
+
 typedef struct vk_cache vk_cache; /* opaque; owned by the library */
 
 /*
@@ -90,7 +98,7 @@ typedef struct vk_cache_config {
   int32_t sink_format;        /* VK_FMT_*                                              */
   int32_t recent_tokens;      /* R >= 0; 0 = no recent tier                            */
   int32_t recent_format;      /* VK_FMT_*                                              */
-  int32_t reserved0;          /* must be 0                                             */
+  int32_t decode_kernel;      /* VK_DECODE_*: which decode kernel reads the pages        */
   int64_t pages_ternary;      /* pool capacity per layer, pages (>= 0)                 */
   int64_t pages_fp8;
   int64_t pages_f16;

@@ -15,9 +15,16 @@ Readings where that page is silent:
     0b11 is never written.
   * Flat tensors and key page rows pack along the last axis, element 4j+i in
     bits [2i, 2i+1] of byte j (least significant first).
-  * Value page tiles are stored dimension-major: for each head dimension d,
-    one little-endian 32-bit word per 16-token unit, token t of the unit at
-    bits 2*(t // 2) + 16*(t % 2).  Still four codes per byte.
+  * Value page tiles are stored per 16-token unit (4*D bytes each, units in
+    token order).  A unit is 64 chunks of D/16 bytes; chunk 4*c + g holds the
+    codes of tokens 4g..4g+3 of the unit for the dimensions 16*j + c
+    (j = 0..D/16-1), read as little-endian 32-bit words:
+      D = 128: word h (h = 0, 1) holds token 4g+2h in its low 16 bits and
+               token 4g+2h+1 in its high 16 bits, dimension 16j+c at bits 2j;
+      D = 64:  one word; its low 16 bits hold token 4g (bits 0-7) and 4g+2
+               (bits 8-15), its high 16 bits token 4g+1 and 4g+3; dimension
+               16j+c at bits 2j of each byte.
+    Still four codes per byte.
 
 All inputs are the raw 16-bit patterns of float16 or bfloat16 tensors.
 """
@@ -103,36 +110,49 @@ def k_tile(codes: np.ndarray) -> np.ndarray:
     return pack_flat(codes)
 
 
-def v_tile(codes: np.ndarray) -> np.ndarray:
-    """Value page tile of one head: codes [Bs, D] -> bytes [D, Bs/4] (dimension-major).
+def _v_bit(r: int, j: int, dim: int) -> int:
+    """Bit position, inside its chunk, of token 4g+r and dimension 16j+c."""
+    if dim == 128:
+        return 32 * (r // 2) + 16 * (r % 2) + 2 * j
+    if dim == 64:
+        return 16 * (r % 2) + 8 * (r // 2) + 2 * j
+    raise ValueError("head_dim must be 64 or 128")
 
-    For dimension d and 16-token unit k, the little-endian 32-bit word holds
-    token 16k+t at bits 2*(t//2) + 16*(t%2).
-    """
+
+def v_tile(codes: np.ndarray) -> np.ndarray:
+    """Value page tile of one head: codes [Bs, D] -> bytes [Bs*D/4] (chunked, see module doc)."""
     q = np.asarray(codes, dtype=np.int16)
     bs, dim = q.shape
     if bs % 16:
         raise ValueError("block size must be a multiple of 16")
-    u = (q + 1).astype(np.uint32)
-    words = np.zeros((dim, bs // 16), dtype=np.uint32)
+    u = (q + 1).astype(np.uint64)
+    nb = dim // 16                                  # dimensions per chunk; chunk = nb bytes
+    out = np.zeros((bs // 16, 64), dtype=np.uint64)  # one chunk per (c, g), as an integer
     for k in range(bs // 16):
-        for t in range(16):
-            shift = 2 * (t // 2) + 16 * (t % 2)
-            words[:, k] |= u[16 * k + t, :] << np.uint32(shift)
-    return words.astype("<u4").view(np.uint8).reshape(dim, bs // 4)
+        for c in range(16):
+            for g in range(4):
+                val = 0
+                for r in range(4):
+                    for j in range(nb):
+                        val |= int(u[16 * k + 4 * g + r, 16 * j + c]) << _v_bit(r, j, dim)
+                out[k, 4 * c + g] = val
+    chunk_bytes = out.astype("<u8").view(np.uint8).reshape(bs // 16, 64, 8)[:, :, :nb]
+    return np.ascontiguousarray(chunk_bytes).reshape(-1)
 
 
-def v_tile_codes(tile: np.ndarray, bs: int) -> np.ndarray:
-    """Inverse of v_tile: bytes [D, Bs/4] -> codes [Bs, D]."""
-    b = np.ascontiguousarray(np.asarray(tile, dtype=np.uint8))
-    dim = b.shape[0]
-    words = b.reshape(dim, bs // 4).view("<u4").astype(np.uint32)
+def v_tile_codes(tile: np.ndarray, bs: int, dim: int) -> np.ndarray:
+    """Inverse of v_tile: bytes [Bs*D/4] -> codes [Bs, D]."""
+    b = np.asarray(tile, dtype=np.uint8).reshape(bs // 16, 64, dim // 16)
+    nb = dim // 16
     out = np.zeros((bs, dim), dtype=np.int8)
     for k in range(bs // 16):
-        for t in range(16):
-            shift = 2 * (t // 2) + 16 * (t % 2)
-            u = (words[:, k] >> np.uint32(shift)) & 3
-            if np.any(u == 3):
-                raise ValueError("reserved 2-bit code 0b11")
-            out[16 * k + t, :] = u.astype(np.int8) - 1
+        for c in range(16):
+            for g in range(4):
+                val = int.from_bytes(bytes(b[k, 4 * c + g]), "little")
+                for r in range(4):
+                    for j in range(nb):
+                        u = (val >> _v_bit(r, j, dim)) & 3
+                        if u == 3:
+                            raise ValueError("reserved 2-bit code 0b11")
+                        out[16 * k + 4 * g + r, 16 * j + c] = u - 1
     return out

@@ -53,7 +53,7 @@ def pages_needed(w: wl.Workload) -> List[int]:
 
 
 def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_pages=(0, 0, 0),
-               max_tokens=None) -> vk.Cache:
+               max_tokens=None, decode_kernel=0) -> vk.Cache:
     need = pages_needed(w)
     cfg = vk.make_config(n_layers=w.n_layers, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
                          head_dim=w.head_dim, block_size=w.block_size, max_seqs=w.n_seqs,
@@ -61,7 +61,8 @@ def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_page
                          recent_tokens=w.recent_tokens, recent_format=w.recent_format,
                          pages_ternary=need[0] + slack_pages[0], pages_fp8=need[1] + slack_pages[1],
                          pages_f16=need[2] + slack_pages[2], eps=eps, fp8_scale=fp8_scale,
-                         page_shuffle_seed=w.page_shuffle_seed if shuffle is None else shuffle)
+                         page_shuffle_seed=w.page_shuffle_seed if shuffle is None else shuffle,
+                         decode_kernel=decode_kernel)
     return vk.Cache(cfg)
 
 
@@ -141,7 +142,7 @@ def check_partial_page(spec, enc, p, got, fmt, n_tok):
             tile = got[off + h * tb: off + (h + 1) * tb]
             if fmt == oc.TERNARY2:
                 codes = ot.unpack_flat(tile.reshape(bs, dim // 4)) if which == "k" else \
-                    ot.v_tile_codes(tile.reshape(dim, bs // 4), bs)
+                    ot.v_tile_codes(tile, bs, dim)
                 want = getattr(enc, which + "_code")[lo:lo + n_tok, h]
             elif fmt == oc.FP8E4M3:
                 codes = tile.reshape(bs, dim) if which == "k" else tile.reshape(dim, bs).T
@@ -177,9 +178,9 @@ def check_decode(out: torch.Tensor, q: torch.Tensor, w: wl.Workload, encs: Dict[
 
 
 def run_workload(w: wl.Workload, sample_seqs: Sequence[int], page_layers: Sequence[int],
-                 decode_layers: Sequence[int], shuffle=None) -> dict:
-    say(f"[{w.name}] create+fill")
-    cache = make_cache(w, shuffle=shuffle)
+                 decode_layers: Sequence[int], shuffle=None, decode_kernel=0) -> dict:
+    say(f"[{w.name}] create+fill (decode kernel {decode_kernel})")
+    cache = make_cache(w, shuffle=shuffle, decode_kernel=decode_kernel)
     fill(cache, w)
     report = {"gamma_checked": 0, "max_err": 0.0}
     encs_by_layer = {}
@@ -199,7 +200,7 @@ def run_workload(w: wl.Workload, sample_seqs: Sequence[int], page_layers: Sequen
             torch.cuda.synchronize()
             err = check_decode(out, q, w, encs, w.window)
             report["max_err"] = max(report["max_err"], err)
-            say(f"[{w.name}] decode layer {layer}: max abs err {err:.3e}")
+            say(f"[{w.name}] decode kernel {decode_kernel} layer {layer}: max abs err {err:.3e}")
         encs_by_layer.pop(layer, None)
     report["stats"] = cache.stats()
     cache.close()

@@ -123,11 +123,12 @@ EDGE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
 @pytest.mark.parametrize("name,kw,windows", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
-def test_edge_workloads(name, kw, windows):
+def test_edge_workloads(name, kw, windows, kernel):
     w = wl.small_workload(**kw)
-    say(f"edge {name}: {w}")
-    cache = make_cache(w)
+    say(f"edge {name} kernel {kernel}: {w}")
+    cache = make_cache(w, decode_kernel=kernel)
     fill(cache, w)
     encs = {}
     for s in range(w.n_seqs):
@@ -144,12 +145,13 @@ def test_edge_workloads(name, kw, windows):
     cache.close()
 
 
-def test_incremental_decode_appends_into_recent_tier():
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
+def test_incremental_decode_appends_into_recent_tier(kernel):
     """Prefill, then one-token appends (the recent fp8 tier grows page by page), decoding each step."""
     w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
                           recent_tokens=64, recent_format=oc.FP8E4M3, lengths=(300,))
     steps = [(0, 250)] + [(250 + i, 1) for i in range(50)]
-    cache = make_cache(w, slack_pages=(0, 8, 0))
+    cache = make_cache(w, slack_pages=(0, 8, 0), decode_kernel=kernel)
     spec = spec_of(w)
     kall = wl.kv_block(w, "k", 0, 0, 0, 300, device="cuda")
     vall = wl.kv_block(w, "v", 0, 0, 0, 300, device="cuda")
@@ -169,12 +171,13 @@ def test_incremental_decode_appends_into_recent_tier():
     cache.close()
 
 
-def test_page_placement_and_repeats_are_bit_identical():
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
+def test_page_placement_and_repeats_are_bit_identical(kernel):
     w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
                           recent_tokens=100, lengths=(900, 455, 1200), batch_appends=False)
     outs = []
     for shuffle in (0, 1004, 77):
-        cache = make_cache(w, shuffle=shuffle, slack_pages=(50, 50, 50))
+        cache = make_cache(w, shuffle=shuffle, slack_pages=(50, 50, 50), decode_kernel=kernel)
         fill(cache, w)
         q = wl.queries(w, 0, device="cuda")
         for W in (-1, 300):
@@ -187,11 +190,12 @@ def test_page_placement_and_repeats_are_bit_identical():
         assert all(torch.equal(ref[0], r) for r in ref[1:])
 
 
-def test_many_sequences_subset_and_order():
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
+def test_many_sequences_subset_and_order(kernel):
     """More sequences than one launch holds; decode a reordered subset."""
     w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, n_seqs=70, lengths=tuple(range(20, 90)),
                           batch_appends=False)
-    cache = make_cache(w)
+    cache = make_cache(w, decode_kernel=kernel)
     fill(cache, w)
     q = wl.queries(w, 0, device="cuda")
     encs = {}
@@ -237,7 +241,7 @@ def test_errors_leave_cache_unchanged_and_usable():
     again = cache.decode(q, [0, 1], 0).cpu()
     assert torch.equal(ok, again)
     small = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(20,))
-    c2 = make_cache(small, slack_pages=(4, 0, 0))
+    c2 = make_cache(small, slack_pages=(4, 0, 0), max_tokens=64)
     fill(c2, small)                              # page 1 ternary, partly filled
     kk = torch.zeros((1, 1, 4, 2, 64), dtype=torch.float16, device="cuda")
     with pytest.raises(vk.VkError) as e:

@@ -58,7 +58,7 @@ def test_config_defaults():
                                  dict(n_q_heads=48, n_kv_heads=2), dict(head_dim=96), dict(block_size=24),
                                  dict(block_size=8), dict(max_seqs=0), dict(sink_tokens=-1),
                                  dict(sink_format=3), dict(pages_fp8=-1), dict(eps=-1.0),
-                                 dict(fp8_scale=0.0), dict(reserved0=1), dict(eps=float("nan"))])
+                                 dict(fp8_scale=0.0), dict(decode_kernel=3), dict(eps=float("nan"))])
 def test_config_rejected(bad):
     with pytest.raises(vk.VkError) as e:
         vk.device_bytes(base_cfg(**bad))

@@ -141,18 +141,26 @@ def test_pack_invariants_and_round_trip():
 
 def test_v_tile_hand_example_and_inverse():
     g = golden("v_tile_example.json")
-    codes = np.array(g["codes_by_token"], dtype=np.int8).reshape(16, 1)
-    tile = ot.v_tile(codes)
-    assert tile.ravel().tolist() == g["bytes"]
-    assert int(tile.ravel().view("<u4")[0]) == g["word"]
+    for case in g["cases"]:
+        dim = case["dim"]
+        codes = np.zeros((16, dim), dtype=np.int8)
+        for t, d, c in case["codes"]:
+            codes[t, d] = c
+        tile = ot.v_tile(codes)
+        assert tile.size == case["tile_bytes"]
+        want = np.full(case["tile_bytes"], 0x55, dtype=np.uint8)
+        for k, v in case["bytes_not_0x55"].items():
+            want[int(k)] = v
+        assert tile.tolist() == want.tolist(), dim
     rng = np.random.default_rng(5)
-    q = rng.integers(-1, 2, size=(64, 128)).astype(np.int8)
-    assert np.array_equal(ot.v_tile_codes(ot.v_tile(q), 64), q)
-    # the V tile of dimension d only depends on column d
-    q2 = q.copy()
-    q2[:, 7] = 0
-    a, b = ot.v_tile(q), ot.v_tile(q2)
-    assert np.array_equal(np.delete(a, 7, axis=0), np.delete(b, 7, axis=0))
+    for dim in (64, 128):
+        q = rng.integers(-1, 2, size=(64, dim)).astype(np.int8)
+        assert np.array_equal(ot.v_tile_codes(ot.v_tile(q), 64, dim), q)
+        # each unit's chunk bytes depend only on that unit's tokens
+        q2 = q.copy()
+        q2[20] = 0
+        a, b = ot.v_tile(q).reshape(4, -1), ot.v_tile(q2).reshape(4, -1)
+        assert np.array_equal(np.delete(a, 1, axis=0), np.delete(b, 1, axis=0))
 
 
 # ------------------------------------------------------------ fp8 / fp16 ---
@@ -240,15 +248,15 @@ def test_gamma_is_per_append_over_ternary_tokens_only():
 
 
 def test_page_tiles_layout():
-    spec = oc.CacheSpec(n_kv_heads=2, head_dim=8, block_size=16)
+    spec = oc.CacheSpec(n_kv_heads=2, head_dim=64, block_size=16)
     rng = np.random.default_rng(2)
-    k = f16_bits(rng.standard_normal((16, 2, 8)))
+    k = f16_bits(rng.standard_normal((16, 2, 64)))
     enc = oc.encode_sequence(spec, k, k, ot.F16, [(0, 16)])
     b = oc.page_tiles(spec, enc, 0)
-    assert b.size == oc.page_bytes(spec, oc.TERNARY2) == 2 * 2 * 16 * 8 // 4
-    kt = 16 * 8 // 4
-    assert np.array_equal(b[kt:2 * kt].reshape(16, 2), ot.pack_flat(enc.k_code[:, 1]))
-    assert np.array_equal(ot.v_tile_codes(b[2 * kt:3 * kt].reshape(8, 4), 16), enc.v_code[:, 0])
+    assert b.size == oc.page_bytes(spec, oc.TERNARY2) == 2 * 2 * 16 * 64 // 4
+    kt = 16 * 64 // 4
+    assert np.array_equal(b[kt:2 * kt].reshape(16, 16), ot.pack_flat(enc.k_code[:, 1]))
+    assert np.array_equal(ot.v_tile_codes(b[2 * kt:3 * kt], 16, 64), enc.v_code[:, 0])
 
 
 def test_storage_ratio_matches_page():
