@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--decode-kernel", type=int, default=0, help="0 default, 1 vector ALU, 2 matrix cores")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=0, help="0 = workload's own sample rule")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
@@ -53,6 +55,13 @@ def main():
     from bit_ternary_attention_amd import workloads as wl
 
     torch.cuda.set_device(0)
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = wl.workload(args.workload)
     calls = w.appends()
     ids_all = list(range(w.n_seqs))

@@ -410,8 +410,12 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   int64_t units[3] = {0, 0, 0};
   int32_t splits_used = 1;
-  for (int32_t base = 0; base < n_seqs; base += vk::kDecodeMaxSeqs) {
-    const int32_t nb = std::min<int32_t>(vk::kDecodeMaxSeqs, n_seqs - base);
+  const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
+  // sequences per launch: every (sequence, KV head) needs room for two partial slots
+  const int32_t per_launch = static_cast<int32_t>(
+      std::max<int64_t>(1, std::min<int64_t>(vk::kDecodeMaxSeqs, kDecodeScratchItems / (2 * cfg.n_kv_heads))));
+  for (int32_t base = 0; base < n_seqs; base += per_launch) {
+    const int32_t nb = std::min<int32_t>(per_launch, n_seqs - base);
     vk::DecodeArgs a{};
     a.P = c->pools;
     a.q = static_cast<const uint16_t*>(q) + static_cast<int64_t>(base) * cfg.n_q_heads * cfg.head_dim;
@@ -423,39 +427,42 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     a.hq = cfg.n_q_heads;
     a.sink_tokens = cfg.sink_tokens;
     a.window = window;
-    a.kernel = cfg.decode_kernel == VK_DECODE_VALU ? VK_DECODE_VALU : VK_DECODE_MFMA;
+    a.kernel = mfma ? VK_DECODE_MFMA : VK_DECODE_VALU;
     a.units_per_iter = decode_units_per_iter();
     a.scale_log2 = scale * 1.4426950408889634f;
     int32_t max_units = 0;
+    int64_t cu[3] = {0, 0, 0};  // attended units per format in this launch
     for (int32_t i = 0; i < nb; ++i) {
       const int32_t sid = seq_ids[base + i];
       a.slots[i] = sid;
       a.lens[i] = c->host->seq(sid).length;
       max_units = std::max(max_units, vk::attended_units(a.lens[i], cfg.sink_tokens, window).n_units());
-      c->host->count_units(sid, window, units);
+      c->host->count_units(sid, window, cu);
     }
+    for (int f = 0; f < 3; ++f) units[f] += cu[f];
+    // matrix-core path: fp8 / fp16 pages go to their own kernel, as one more partial state
+    const bool mixed = mfma && (cu[1] + cu[2]) > 0;
     const int64_t items = static_cast<int64_t>(nb) * cfg.n_kv_heads;
-    const int32_t max_splits =
-        static_cast<int32_t>(std::min<int64_t>(kDecodeMaxSplits, kDecodeScratchItems / items));
-    const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
+    const int32_t max_splits = static_cast<int32_t>(
+        std::min<int64_t>(kDecodeMaxSplits - (mixed ? 1 : 0), kDecodeScratchItems / items - (mixed ? 1 : 0)));
     a.n_splits = mfma ? vk::choose_splits(items, max_units, kDecodeTargetGroups / 4, std::max(1, max_splits),
                                           4 * kDecodeMinUnitsPerWave)
                       : vk::choose_splits(items, max_units, kDecodeTargetGroups, std::max(1, max_splits),
                                           kDecodeMinUnits);
+    a.n_parts = a.n_splits + (mixed ? 1 : 0);
     splits_used = a.n_splits;
     if (c->timer.on) {
-      int64_t cu[3] = {0, 0, 0};
-      for (int32_t i = 0; i < nb; ++i) c->host->count_units(seq_ids[base + i], window, cu);
       const double row = cfg.head_dim;
       const double unit_kv = 2.0 * 16.0 * cfg.n_kv_heads;  // K and V, 16 tokens, every KV head
-      const double kv_bytes = unit_kv * (cu[0] * row / 4.0 + cu[1] * row + cu[2] * row * 2.0);
-      const double qo = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * (2.0 + 4.0);
-      const double part = static_cast<double>(nb) * cfg.n_q_heads * a.n_splits * (cfg.head_dim + 2) * 4.0;
-      c->timer.add_bytes(VK_KERNEL_DECODE, kv_bytes + qo + (a.n_splits > 1 ? part - nb * cfg.n_q_heads * cfg.head_dim * 4.0 : 0.0));
-      if (a.n_splits > 1) {
-        const double merge_bytes = part + nb * cfg.n_q_heads * cfg.head_dim * 4.0;
-        c->timer.add_bytes(VK_KERNEL_MERGE, merge_bytes);
-      }
+      const double tern_bytes = unit_kv * cu[0] * row / 4.0;
+      const double other_bytes = unit_kv * (cu[1] * row + cu[2] * row * 2.0);
+      const double q_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 2.0;
+      const double out_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 4.0;
+      const double part1 = static_cast<double>(nb) * cfg.n_q_heads * (cfg.head_dim + 2) * 4.0;  // one part
+      const double dec_out = a.n_parts > 1 ? part1 * a.n_splits : out_bytes;
+      c->timer.add_bytes(VK_KERNEL_DECODE, (mixed ? tern_bytes : tern_bytes + other_bytes) + q_bytes + dec_out);
+      if (mixed) c->timer.add_bytes(VK_KERNEL_DECODE_MIXED, other_bytes + q_bytes + part1);
+      if (a.n_parts > 1) c->timer.add_bytes(VK_KERNEL_MERGE, part1 * a.n_parts + out_bytes);
     }
     hipError_t e = vk::launch_decode(a, g, s, c->timer.on ? &c->timer : nullptr);
     if (e != hipSuccess) return hip_fail(c, e, "decode kernels");

@@ -68,6 +68,22 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// max over the four 16-lane rows of each lane column (lanes l, l^16, l^32, l^48), with the
+// gfx950 row-swap permutes (VALU only, no LDS round trip).  permlane16_swap(x, x) returns
+// rows (0, 0, 2, 2) and (1, 1, 3, 3); permlane32_swap(x, x) returns halves (lo, lo), (hi, hi).
+// (The swap results are copied to scalars before reinterpretation: a bit cast applied to a
+// vector element directly reads element 0 with this compiler.)
+__device__ __forceinline__ float max_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = r16[0], a1 = r16[1];
+  x = fmaxf(__uint_as_float(a0), __uint_as_float(a1));
+  const uint32_t v = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const uint32_t b0 = r32[0], b1 = r32[1];
+  return fmaxf(__uint_as_float(b0), __uint_as_float(b1));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -330,12 +346,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
   for (int hh = 0; hh < G; ++hh) {
     const float l = wave_sum(lsum[hh]);
     const int64_t qh = static_cast<int64_t>(b) * a.hq + kvh * G + hh;
-    if (a.n_splits == 1) {
+    if (a.n_parts == 1) {
       const float inv = 1.0f / l;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) a.out[qh * D + lane * DPL + j] = o[hh][j] * inv;
     } else {
-      float* part = a.partials + (qh * a.n_splits + split) * (D + 2);
+      float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
 #pragma unroll
       for (int j = 0; j < DPL; ++j) part[lane * DPL + j] = o[hh][j];
       if (lane == 0) {
@@ -373,6 +389,9 @@ typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWaves = 4;
+// Fourth word of a raw buffer descriptor on gfx9-family parts (32-bit data format; byte
+// offsets checked against the record count, reads past it return 0).
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ uint32_t h2u(h2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
@@ -389,29 +408,98 @@ struct UnitRaw {
   uint32_t v[NV];  // value chunk 4(l%16) + l/16: tokens 4(l/16)..+3 of dims 16j + l%16
 };
 
+// Offset form of a code pair, one AND-OR per pair for most positions: the 2-bit fields at
+// bits (P, P+16) of w become, in each 16-bit half, the f16 value 2^(-4-pe) + u * 2^-14,
+// i.e. the field sits in mantissa bits [pe, pe+1] under the exponent 11 - pe.  Fields at
+// P = 4, 6, 8 are used in place (pe = P); P = 10, 12, 14 come from w >> 6 and P = 0, 2 from
+// w << 4 (pe = 4, 6, 8 and 4, 6), so every value is a normal f16 and the constant part is
+// at most 64 times the code step.  The constant parts are removed once per head (keys) or
+// once per output block (values).
+template <int P>
+struct OPos {
+  static constexpr int pe = P < 4 ? P + 4 : (P <= 8 ? P : P - 6);
+  static constexpr float off = 1.0f / static_cast<float>(1u << (4 + pe));  // 2^(-4-pe)
+};
+__device__ __forceinline__ float ocode_off(int p) {  // same as OPos<p>::off, for loops
+  const int pe = p < 4 ? p + 4 : (p <= 8 ? p : p - 6);
+  return 1.0f / static_cast<float>(1u << (4 + pe));
+}
+// The masks (scalar registers) and exponent words (vector registers) of pe = 4, 6, 8, made
+// opaque so that each pair compiles to a single v_and_or_b32 (a VOP3 encoding takes no
+// literal constants and at most one scalar operand).
+struct OConst {
+  uint32_t m[3], e[3];
+};
+__device__ __forceinline__ OConst oconst() {
+  OConst c;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int pe = 4 + 2 * i;
+    c.m[i] = 0x00030003u << pe;
+    c.e[i] = ((11u - pe) << 10) * 0x00010001u;
+    asm volatile("" : "+s"(c.m[i]));
+    asm volatile("" : "+v"(c.e[i]));
+  }
+  return c;
+}
+template <int P>
+__device__ __forceinline__ uint32_t ocode2(uint32_t w, uint32_t wl4, uint32_t wr6, const OConst& c) {
+  constexpr int i = (OPos<P>::pe - 4) / 2;
+  const uint32_t src = P < 4 ? wl4 : (P <= 8 ? w : wr6);
+  return (src & c.m[i]) | c.e[i];
+}
+
 // A operands of the score product: pairs (d, d+8) of each 16-dimension code word.
 template <int NS, int NC>
-__device__ __forceinline__ void ka_ternary(const uint32_t (&k)[NC], h8_t (&ka)[NS]) {
+__device__ __forceinline__ void ka_ternary(const uint32_t (&k)[NC], h8_t (&ka)[NS], const OConst& o) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{ucode2<0>(k[c]), ucode2<2>(k[c]), ucode2<4>(k[c]), ucode2<6>(k[c])});
-    ka[2 * c + 1] =
-        __builtin_bit_cast(h8_t, u4_t{ucode2<8>(k[c]), ucode2<10>(k[c]), ucode2<12>(k[c]), ucode2<14>(k[c])});
+    const uint32_t w = k[c], l4 = w << 4, r6 = w >> 6;
+    ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{ocode2<0>(w, l4, r6, o), ocode2<2>(w, l4, r6, o),
+                                              ocode2<4>(w, l4, r6, o), ocode2<6>(w, l4, r6, o)});
+    ka[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{ocode2<8>(w, l4, r6, o), ocode2<10>(w, l4, r6, o),
+                                                  ocode2<12>(w, l4, r6, o), ocode2<14>(w, l4, r6, o)});
   }
 }
 
+// Value chunk words with their shifted copies (offset form, head_dim 128).
+template <int NV>
+struct VWords {
+  uint32_t w[NV], l4[NV], r6[NV];
+};
+template <int NV>
+__device__ __forceinline__ VWords<NV> vwords(const uint32_t (&v)[NV]) {
+  VWords<NV> r;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    r.w[i] = v[i];
+    r.l4[i] = v[i] << 4;
+    r.r6[i] = v[i] >> 6;
+  }
+  return r;
+}
+
 // A operand of block j of the value product: tokens (4g, 4g+1), (4g+2, 4g+3) of dim 16j + l%16.
+// Head dim 128 (two words, block j at bits 2j of each): offset form, constant OPos<2j>::off.
+// Head dim 64 (one word, bits 2j and 8 + 2j): plain form u * 2^-14 (bit pattern u << 10).
 template <int NV, int J>
-__device__ __forceinline__ h4_t va_ternary(const uint32_t (&v)[NV]) {
-  if (NV == 2) return __builtin_bit_cast(h4_t, u2_t{ucode2<2 * J>(v[0]), ucode2<2 * J>(v[NV - 1])});
-  return __builtin_bit_cast(h4_t, u2_t{ucode2<2 * J>(v[0]), ucode2<2 * J + 8>(v[0])});
+__device__ __forceinline__ h4_t va_ternary(const VWords<NV>& v, const OConst& o) {
+  if constexpr (NV == 2)
+    return __builtin_bit_cast(h4_t, u2_t{ocode2<2 * J>(v.w[0], v.l4[0], v.r6[0], o),
+                                         ocode2<2 * J>(v.w[NV - 1], v.l4[NV - 1], v.r6[NV - 1], o)});
+  else
+    return __builtin_bit_cast(h4_t, u2_t{ucode2<2 * J>(v.w[0]), ucode2<2 * J + 8>(v.w[0])});
+}
+template <int NV>
+__device__ __forceinline__ float va_off(int j) {
+  return NV == 2 ? ocode_off(2 * j) : 0.0f;
 }
 
 template <int NV, int NB, int J = 0>
-__device__ __forceinline__ void va_all(const uint32_t (&v)[NV], h4_t (&va)[NB]) {
+__device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], const OConst& o) {
   if constexpr (J < NB) {
-    va[J] = va_ternary<NV, J>(v);
-    va_all<NV, NB, J + 1>(v, va);
+    va[J] = va_ternary<NV, J>(v, o);
+    va_all<NV, NB, J + 1>(v, va, o);
   }
 }
 
@@ -419,16 +507,18 @@ template <int D, int G, int QDT, int PF>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_decode_mfma(DecodeArgs a) {
   constexpr int NC = D / 64;   // 32-bit key code words per lane per unit
   constexpr int NV = D / 64;   // 32-bit value chunk words per lane per unit
-  constexpr int NS = D / 32;   // 16x16x32 steps per unit
-  constexpr int NB = D / 16;   // 16-dimension output blocks (P*V products per unit)
+  constexpr int NS = D / 32;   // 16x16x32 steps per unit of the score product
+  constexpr int NB = D / 16;   // 16-dimension output blocks
   constexpr int CH = 64;       // units per metadata chunk (one per lane)
-  constexpr int UG = 2;        // units sharing one online-softmax update
+  constexpr int UG = 2;        // units sharing one online-softmax update and one P*V product
   static_assert(G <= 16, "one query head per lane column");
   static_assert(CH % PF == 0 && PF % UG == 0, "chunks hold whole prefetch rounds and groups");
   __shared__ float lds_o[kMfmaWaves][G][D];
   __shared__ float lds_m[kMfmaWaves][G], lds_l[kMfmaWaves][G];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, c16 = lane & 15;
+  // wave-uniform indices live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63, grp = lane >> 4, c16 = lane & 15;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int slot = a.slots[b], L = a.lens[b];
   const PoolsView& P = a.P;
@@ -439,11 +529,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   const int s_end = static_cast<int>((static_cast<int64_t>(split + 1) * U) / a.n_splits);
   const int u_begin = s_begin + ((s_end - s_begin) * wave) / kMfmaWaves;
   const int u_end = s_begin + ((s_end - s_begin) * (wave + 1)) / kMfmaWaves;
+  const int u_last = max(u_end - 1, 0);
   const int dbase = grp * (D / 4);  // first head dimension of this lane group's key slice
   const int64_t layer = a.layer;
   const int32_t* bt = P.block_table + static_cast<int64_t>(slot) * P.max_pages;
   const int tile0 = static_cast<int>(P.tile_bytes[0]);
+  const int page_bytes0 = static_cast<int>(P.page_bytes[0]);
   const int64_t qh0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+  // per-lane byte offsets of the key row slice and the value chunk within a unit
+  const uint32_t lane_k = c16 * (D / 4) + grp * (D / 16);
+  const uint32_t lane_v = (4 * c16 + grp) * (D / 16);
 
   auto unit_of = [&](int lu) { return lu < n_a ? lu : R.b_begin + (lu - n_a); };
   // every token of logical units [lu, lu + n) is attended
@@ -454,28 +549,37 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     if (R.single) return (u1 * 16 + 16) <= L;
     return (u1 * 16 + 16 <= R.sinks) || (u0 * 16 >= R.w0 && u1 * 16 + 16 <= L);
   };
-  // Per-chunk unit metadata, one unit per lane: block-table entry and, for ternary pages,
-  // the K and V gamma (lanes past the end repeat the last unit).
+  // Per-chunk unit metadata, one unit per lane (lanes past the end repeat the last unit):
+  // block-table entry, the K and V gamma of ternary pages, and the address of the page the
+  // codes are read from (the zeroed dummy page for other formats).  Page addresses are
+  // computed here, per lane, once per 64 units; a unit takes them with readlane.
   struct Chunk {
     int32_t ent;
     float gk, gv;
+    uint32_t plo, phi;
   };
   auto load_chunk = [&](int c0) -> Chunk {
-    const int lu = min(c0 + lane, max(u_end - 1, 0));
+    const int lu = min(c0 + lane, u_last);
     Chunk c;
     c.ent = bt[(unit_of(lu) * 16) >> P.bs_shift];
     const bool tern = (static_cast<uint32_t>(c.ent) >> 30) == VK_FMT_TERNARY2;
-    const float* gp = tern ? P.gamma + (layer * P.cap[0] + (c.ent & 0x3FFFFFFF)) * 2
-                           : reinterpret_cast<const float*>(P.dummy_page);
-    const float2 gg = *reinterpret_cast<const float2*>(gp);
+    const int64_t gi = layer * P.cap[0] + (tern ? (c.ent & 0x3FFFFFFF) : 0);
+    const float2 gg = *reinterpret_cast<const float2*>(P.gamma + gi * 2);
     c.gk = gg.x;
     c.gv = gg.y;
+    const uint64_t pg = tern ? reinterpret_cast<uint64_t>(P.pool[0] + gi * P.page_bytes[0])
+                             : reinterpret_cast<uint64_t>(P.dummy_page);
+    c.plo = static_cast<uint32_t>(pg);
+    c.phi = static_cast<uint32_t>(pg >> 32);
     return c;
+  };
+  auto lane_f = [](float x, int k) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), k));
   };
 
   // query head c16 (zero beyond the group) as the B operand of the score product, and its sum
   h8_t qb[NS];
-  float qsum = 0.0f;
+  float qsum = 0.0f, qoff = 0.0f;
   {
     const uint16_t* qrow = a.q + (qh0 + (c16 < G ? c16 : 0)) * D + dbase;
     uint32_t w[NS][4];
@@ -495,42 +599,309 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         qsum += static_cast<float>(hp[0]) + static_cast<float>(hp[1]);
       }
     }
+    // constant part of the key operands: koff = sum_d off(d) q_d, with off(d) that of the
+    // code pair (position p = 2 (4 (s & 1) + i)) the dimension pair sits in
+    float koff = 0.0f;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qb[s] = __builtin_bit_cast(h8_t, u4_t{w[s][0], w[s][1], w[s][2], w[s][3]});
+    for (int s = 0; s < NS; ++s) {
+      qb[s] = __builtin_bit_cast(h8_t, u4_t{w[s][0], w[s][1], w[s][2], w[s][3]});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h2_t hp = as_h2(w[s][i]);
+        koff += ocode_off(2 * (4 * (s & 1) + i)) * (static_cast<float>(hp[0]) + static_cast<float>(hp[1]));
+      }
+    }
     qsum += __shfl_xor(qsum, 16, 64);
     qsum += __shfl_xor(qsum, 32, 64);
+    koff += __shfl_xor(koff, 16, 64);
+    koff += __shfl_xor(koff, 32, 64);
+    // logit = ks (2^14 acc - qoff) with acc the score product
+    qoff = 16384.0f * koff + qsum;
   }
 
   f4_t oacc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) oacc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
-  // oacc = sum p' u 2^-14 and sacc = sum p' (p' = f16(p 2^14)), both in units of vcur
-  float m = -INFINITY, lsum = 0.0f, sacc = 0.0f, vcur = 0.0f;
+  // p' = f16(2^14 p).  oacc = sum p' u 2^-14 (ternary) or sum p' v 2^-14 (other formats) and
+  // tsum = sum p' over ternary tokens, both in units of vcur; lsum = sum p' over all tokens.
+  float m = -INFINITY, lsum = 0.0f, tsum = 0.0f, vcur = 0.0f;
+  const h2_t ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  const OConst oc = oconst();
 
   // Packed codes of logical unit lu into r.  Always issued (a fixed number of loads per
   // unit, so the compiler can wait precisely): other formats and units past the end
   // read the zeroed dummy page instead.
   auto load_raw = [&](int lu, const Chunk& cc, const Chunk& cn, int c0, UnitRaw<NC, NV>& r) {
-    const int k = min(lu, max(u_end - 1, 0)) - c0;
-    const int32_t entry = k < CH ? __builtin_amdgcn_readlane(cc.ent, k) : __builtin_amdgcn_readlane(cn.ent, k - CH);
-    const bool tern = lu < u_end && (static_cast<uint32_t>(entry) >> 30) == VK_FMT_TERNARY2;
-    const int upi = tern ? ((unit_of(lu) * 16) & (P.bs - 1)) >> 4 : 0;
-    const uint8_t* pg =
-        tern ? P.pool[0] + (layer * P.cap[0] + (entry & 0x3FFFFFFF)) * P.page_bytes[0] : P.dummy_page;
-    const uint8_t* krow = pg + kvh * tile0 + (upi * 16 + c16) * (D / 4) + grp * (D / 16);
-    const uint8_t* vch = pg + (P.hkv + kvh) * tile0 + upi * 4 * D + (4 * c16 + grp) * (D / 16);
+    // units past the end re-read the last unit: their scores are masked
+    const int lc = min(lu, u_last);
+    const int k = lc - c0;
+    const bool in_cur = k < CH;
+    const uint32_t lo = __builtin_amdgcn_readlane(in_cur ? cc.plo : cn.plo, in_cur ? k : k - CH);
+    const uint32_t hi = __builtin_amdgcn_readlane(in_cur ? cc.phi : cn.phi, in_cur ? k : k - CH);
+    const uint8_t* pg = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+    const int upi = ((unit_of(lc) * 16) & (P.bs - 1)) >> 4;  // the dummy page takes any unit offset
+    // buffer loads: page base in the descriptor, unit offset scalar, lane offset vector
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, page_bytes0, kBufferWord3);
+    const int sk = kvh * tile0 + upi * 16 * (D / 4);
+    const int sv = (P.hkv + kvh) * tile0 + upi * 4 * D;
     if (NC == 2) {
-      const uint2 x = *reinterpret_cast<const uint2*>(krow);
-      const uint2 y = *reinterpret_cast<const uint2*>(vch);
-      r.k[0] = x.x;
-      r.k[NC - 1] = x.y;
-      r.v[0] = y.x;
-      r.v[NV - 1] = y.y;
+      const u2_t x = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, lane_k, sk, 0));
+      const u2_t y = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, lane_v, sv, 0));
+      r.k[0] = x[0];
+      r.k[NC - 1] = x[1];
+      r.v[0] = y[0];
+      r.v[NV - 1] = y[1];
     } else {
-      r.k[0] = *reinterpret_cast<const uint32_t*>(krow);
-      r.v[0] = *reinterpret_cast<const uint32_t*>(vch);
+      r.k[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_k, sk, 0);
+      r.v[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_v, sv, 0);
     }
   };
+
+  // keep oacc and tsum in units of vs (uniform; rare: gamma_V changes between append calls)
+  auto set_value_scale = [&](float vs) {
+    if (vs != vcur) {
+      const float ratio = vcur / vs;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) oacc[j] *= ratio;
+      tsum *= ratio;
+      vcur = vs;
+    }
+  };
+
+  // Two consecutive units: scores, one online-softmax update, then P*V (one 16x16x32
+  // product per 16-dimension block when both units are ternary with one gamma_V).
+  auto process_group = [&](int lu0, const Chunk& cc, int c0, const UnitRaw<NC, NV>& r0,
+                           const UnitRaw<NC, NV>& r1) {
+    if (lu0 >= u_end) return;
+    const bool have1 = lu0 + 1 < u_end;
+    const int k0 = lu0 - c0;
+    const int32_t e0 = __builtin_amdgcn_readlane(cc.ent, k0);
+    const int32_t e1 = have1 ? __builtin_amdgcn_readlane(cc.ent, k0 + 1) : e0;
+    // fp8 / fp16 units are left to the mixed-format kernel: here they count as masked
+    bool tern[UG];
+    tern[0] = (static_cast<uint32_t>(e0) >> 30) == VK_FMT_TERNARY2;
+    tern[1] = have1 && (static_cast<uint32_t>(e1) >> 30) == VK_FMT_TERNARY2;
+    if (!tern[0] && !tern[1]) return;
+    const bool full = tern[0] && tern[1] && fully_attended(lu0, UG);
+    float sc[UG][4], vs[UG];
+#pragma unroll
+    for (int g = 0; g < UG; ++g) {
+      const int lu = lu0 + g;
+      vs[g] = 0.0f;
+      if (!tern[g]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[g][r] = -INFINITY;
+        continue;
+      }
+      const UnitRaw<NC, NV>& raw = g == 0 ? r0 : r1;
+      h8_t ka[NS];
+      ka_ternary<NS, NC>(raw.k, ka, oc);
+      const float ks = lane_f(cc.gk, k0 + g) * a.scale_log2;
+      vs[g] = lane_f(cc.gv, k0 + g);
+      const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
+      f4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
+      } else {
+        const int u = unit_of(lu);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = u * 16 + 4 * grp + r;
+          const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
+          sc[g][r] = att ? fmaf(s4[r], a0, a1) : -INFINITY;
+        }
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = max_rows(mx);
+    // the mask is the same for every head: a group with no attended token adds nothing
+    if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) return;
+    if (__ballot(mx > m) != 0) {  // uniform; per-lane factors (lane = head)
+      const float mn = fmaxf(m, mx);
+      const float corr = __builtin_amdgcn_exp2f(m - mn);  // m = -inf gives 0
+#pragma unroll
+      for (int j = 0; j < NB; ++j) oacc[j] *= corr;
+      lsum *= corr;
+      tsum *= corr;
+      m = mn;
+    }
+    const float ms = m - 14.0f;  // p' = 2^(s - m + 14), at most 2^14
+    uint32_t pk[UG][2];
+#pragma unroll
+    for (int g = 0; g < UG; ++g) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const h2_t p2 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h] - ms)),
+                         static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h + 1] - ms))};
+        pk[g][h] = h2u(p2);
+        lsum = __builtin_amdgcn_fdot2(p2, ones, lsum, false);
+      }
+    }
+    if (tern[0] && tern[1] && vs[0] == vs[1]) {
+      if (vs[0] == 0.0f) return;  // every value of these pages is 0
+      set_value_scale(vs[0]);
+#pragma unroll
+      for (int g = 0; g < UG; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][h]), ones, tsum, false);
+      const h8_t pb = __builtin_bit_cast(h8_t, u4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
+      h4_t v0[NB], v1[NB];
+      va_all<NV, NB>(vwords<NV>(r0.v), v0, oc);
+      va_all<NV, NB>(vwords<NV>(r1.v), v1, oc);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const u2_t x0 = __builtin_bit_cast(u2_t, v0[j]), x1 = __builtin_bit_cast(u2_t, v1[j]);
+        const h8_t av = __builtin_bit_cast(h8_t, u4_t{x0[0], x0[1], x1[0], x1[1]});
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, oacc[j], 0, 0, 0);
+      }
+      return;
+    }
+    // one ternary unit (the other masked or non-ternary), or two gamma values: one at a time
+#pragma unroll
+    for (int g = 0; g < UG; ++g) {
+      if (!tern[g] || vs[g] == 0.0f) continue;
+      set_value_scale(vs[g]);
+      const h4_t pb = __builtin_bit_cast(h4_t, u2_t{pk[g][0], pk[g][1]});
+      tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][0]), ones, tsum, false);
+      tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][1]), ones, tsum, false);
+      h4_t vt[NB];
+      va_all<NV, NB>(vwords<NV>(g == 0 ? r0.v : r1.v), vt, oc);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt[j], pb, oacc[j], 0, 0, 0);
+    }
+  };
+
+  if (u_begin < u_end) {
+    // Two register buffers of PH units each: while one is processed, the other's loads
+    // are in flight (every wait then targets loads issued a whole phase earlier).
+    constexpr int PH = PF / 2;
+    Chunk ch_cur = load_chunk(u_begin);
+    Chunk ch_nxt = load_chunk(u_begin + CH);
+    UnitRaw<NC, NV> buf_a[PH], buf_b[PH];
+#pragma unroll
+    for (int t = 0; t < PH; ++t) load_raw(u_begin + t, ch_cur, ch_nxt, u_begin, buf_a[t]);
+    for (int c0 = u_begin; c0 < u_end; c0 += CH) {
+      const int c_end = min(c0 + CH, u_end);
+#pragma unroll 1
+      for (int k = c0; k < c_end; k += 2 * PH) {
+#pragma unroll
+        for (int t = 0; t < PH; ++t) load_raw(k + PH + t, ch_cur, ch_nxt, c0, buf_b[t]);
+#pragma unroll
+        for (int gi = 0; gi < PH / UG; ++gi) process_group(k + gi * UG, ch_cur, c0, buf_a[gi * UG], buf_a[gi * UG + 1]);
+#pragma unroll
+        for (int t = 0; t < PH; ++t) load_raw(k + 2 * PH + t, ch_cur, ch_nxt, c0, buf_a[t]);
+#pragma unroll
+        for (int gi = 0; gi < PH / UG; ++gi)
+          process_group(k + PH + gi * UG, ch_cur, c0, buf_b[gi * UG], buf_b[gi * UG + 1]);
+      }
+      ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
+      ch_nxt = load_chunk(c0 + 2 * CH);
+    }
+  }
+
+  // ---------------- this wave's partial state -> LDS ----------------
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  tsum += __shfl_xor(tsum, 16, 64);
+  tsum += __shfl_xor(tsum, 32, 64);
+  if (c16 < G) {
+    constexpr float kInv = 1.0f / 16384.0f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      // ternary tokens added p' (off_j + u 2^-14); their values are gamma (u - 1)
+      const float sub = tsum * (va_off<NV>(j) + kInv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lds_o[wave][c16][16 * j + 4 * grp + r] = (oacc[j][r] - sub) * vcur;
+    }
+    if (grp == 0) {
+      lds_m[wave][c16] = m;
+      lds_l[wave][c16] = lsum * kInv;
+    }
+  }
+  __syncthreads();
+
+  // ---------------- merge the four waves ----------------
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kMfmaWaves) {
+    const int hh = idx / D, dd = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; ++w) M = fmaxf(M, lds_m[w][hh]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; ++w) {
+      const float lw = lds_l[w][hh];
+      if (lw > 0.0f) {
+        const float wt = exp2f(lds_m[w][hh] - M);
+        num = fmaf(wt, lds_o[w][hh][dd], num);
+        den = fmaf(wt, lw, den);
+      }
+    }
+    const int64_t qh = qh0 + hh;
+    if (a.n_parts == 1) {
+      a.out[qh * D + dd] = num / den;
+    } else {
+      float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
+      part[dd] = num;
+      if (dd == 0) {
+        part[D] = M;
+        part[D + 1] = den;
+      }
+    }
+  }
+}
+
+// fp8 / fp16 pages on the matrix-core path.  One wave per (sequence, KV head) walks the
+// attended units 64 at a time, picks the non-ternary ones from the block table (a ballot
+// over one entry per lane) and folds them into one online-softmax state, written as part
+// n_splits of the split partials (an empty state if the sequence has no such page).  The
+// values enter the second product as themselves (fp8 scaled by fp8_scale), so this part
+// needs no offset bookkeeping.
+template <int D, int G, int QDT>
+__global__ __launch_bounds__(64) void k_decode_mixed(DecodeArgs a) {
+  constexpr int NC = D / 64, NS = D / 32, NB = D / 16;
+  const int lane = threadIdx.x, grp = lane >> 4, c16 = lane & 15;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int slot = a.slots[b], L = a.lens[b];
+  const PoolsView& P = a.P;
+  const Units R = attended(L, a.sink_tokens, a.window);
+  const int n_a = R.a_end;
+  const int U = R.a_end + (R.b_end - R.b_begin);
+  const int dbase = grp * (D / 4);
+  const int64_t layer = a.layer;
+  const int32_t* bt = P.block_table + static_cast<int64_t>(slot) * P.max_pages;
+  const int64_t qh0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+  auto unit_of = [&](int lu) { return lu < n_a ? lu : R.b_begin + (lu - n_a); };
+
+  // query head c16 as the B operand of the score product (plain f16 values)
+  h8_t qb[NS];
+  {
+    const uint16_t* qrow = a.q + (qh0 + (c16 < G ? c16 : 0)) * D + dbase;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint4 x0 = reinterpret_cast<const uint4*>(qrow + 16 * c)[0];
+      const uint4 x1 = reinterpret_cast<const uint4*>(qrow + 16 * c)[1];
+      const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t e0 = (lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const uint32_t e1 = (hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        w[i] = c16 < G ? (q_f16<QDT>(static_cast<uint16_t>(e0)) | (q_f16<QDT>(static_cast<uint16_t>(e1)) << 16)) : 0u;
+      }
+      qb[2 * c] = __builtin_bit_cast(h8_t, u4_t{w[0], w[1], w[2], w[3]});
+      qb[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{w[4], w[5], w[6], w[7]});
+    }
+  }
+  const h2_t ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  f4_t oacc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) oacc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.0f;  // oacc and lsum count p' = 2^14 p
 
   // A operands and scales of a non-ternary unit, loaded here (f16 values, not u * 2^-14)
   auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float& scale) {
@@ -589,177 +960,70 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  // UG consecutive units: scores, one online-softmax update, then P*V.
-  auto process_group = [&](int lu0, const Chunk& cc, int c0, const UnitRaw<NC, NV>* raw) {
-    float sc[UG][4];
-    h4_t va[UG][NB];
-    float vsc[UG];
-    bool tern[UG];
-    const bool full = fully_attended(lu0, UG);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < UG; ++g) {
-      const int lu = lu0 + g;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[g][r] = -INFINITY;
-      vsc[g] = 0.0f;
-      tern[g] = true;
-      if (lu >= u_end) continue;
-      const int k = lu - c0;
-      const int32_t entry = __builtin_amdgcn_readlane(cc.ent, k);
+  for (int c0 = 0; c0 < U; c0 += 64) {
+    const int lu_l = c0 + lane;
+    const int32_t ent_l = lu_l < U ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
+    uint64_t todo = __ballot(lu_l < U && (static_cast<uint32_t>(ent_l) >> 30) != VK_FMT_TERNARY2);
+    while (todo) {
+      const int k = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int lu = c0 + k;
+      const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
       h8_t ka[NS];
-      float a0, a1;  // logit = a0 * acc + a1
-      if ((static_cast<uint32_t>(entry) >> 30) == VK_FMT_TERNARY2) {
-        ka_ternary<NS, NC>(raw[g].k, ka);
-        const float gk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cc.gk), k));
-        vsc[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cc.gv), k));
-        const float ks = gk * a.scale_log2;
-        a0 = ks * 16384.0f;
-        a1 = -qsum * ks;
-      } else {
-        tern[g] = false;
-        float scale;
-        operands_other(lu, entry, ka, va[g], scale);
-        vsc[g] = scale;
-        a0 = scale * a.scale_log2;
-        a1 = 0.0f;
-      }
+      h4_t va[NB];
+      float vscale;
+      operands_other(lu, entry, ka, va, vscale);
       f4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
-      if (full) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
-      } else {
-        const int u = unit_of(lu);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = u * 16 + 4 * grp + r;
-          const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
-          sc[g][r] = att ? fmaf(s4[r], a0, a1) : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[g][r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (__ballot(mx > m) != 0) {  // uniform; per-lane factors (lane = head)
-      const float mn = fmaxf(m, mx);
-      const float corr = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) oacc[j] *= corr;
-      lsum *= corr;
-      sacc *= corr;
-      m = mn;
-    }
-#pragma unroll
-    for (int g = 0; g < UG; ++g) {
-      if (lu0 + g >= u_end) break;
-      float p[4];
+      const float a0 = vscale * a.scale_log2;
+      const int u = unit_of(lu);
+      float sc[4];
+      float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = sc[g][r] == -INFINITY ? 0.0f : exp2f(sc[g][r] - m);
-        lsum += p[r];
+        const int t = u * 16 + 4 * grp + r;
+        const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
+        sc[r] = att ? s4[r] * a0 : -INFINITY;
+        mx = fmaxf(mx, sc[r]);
       }
-      const float vscale = vsc[g];
-      if (vscale == 0.0f) continue;  // every value of the page is 0: no contribution
-      if (vscale != vcur) {          // uniform: keep the sums in units of the current value scale
-        const float ratio = vcur / vscale;
+      mx = max_rows(mx);
+      if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) continue;
+      if (__ballot(mx > m) != 0) {
+        const float mn = fmaxf(m, mx);
+        const float corr = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) oacc[j] *= ratio;
-        sacc *= ratio;
-        vcur = vscale;
+        for (int j = 0; j < NB; ++j) oacc[j] *= corr;
+        lsum *= corr;
+        m = mn;
       }
-      const h2_t p01 = h2_t{static_cast<_Float16>(p[0] * 16384.0f), static_cast<_Float16>(p[1] * 16384.0f)};
-      const h2_t p23 = h2_t{static_cast<_Float16>(p[2] * 16384.0f), static_cast<_Float16>(p[3] * 16384.0f)};
+      const float ms = m - 14.0f;
+      const h2_t p01 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[0] - ms)),
+                        static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[1] - ms))};
+      const h2_t p23 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[2] - ms)),
+                        static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[3] - ms))};
+      lsum = __builtin_amdgcn_fdot2(p01, ones, lsum, false);
+      lsum = __builtin_amdgcn_fdot2(p23, ones, lsum, false);
       const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(p01), h2u(p23)});
-      if (tern[g]) {
-        sacc += (static_cast<float>(p01[0]) + static_cast<float>(p01[1])) +
-                (static_cast<float>(p23[0]) + static_cast<float>(p23[1]));
-        h4_t vt[NB];
-        va_all<NV, NB>(raw[g].v, vt);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt[j], pb, oacc[j], 0, 0, 0);
-      } else {
-        // f16 / fp8 values enter as themselves: add 2^-14 v so that 2^14 oacc - sacc keeps counting v
-        constexpr float kInv = 1.0f / 16384.0f;
-        f4_t tmp[NB];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          tmp[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[g][j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          oacc[j] += tmp[j] * kInv;
-        }
+      for (int j = 0; j < NB; ++j) {
+        const f4_t t4 = __builtin_amdgcn_mfma_f32_16x16x16f16(va[j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        oacc[j] += t4 * vscale;
       }
-    }
-  };
-
-  if (u_begin < u_end) {
-    Chunk ch_cur = load_chunk(u_begin);
-    Chunk ch_nxt = load_chunk(u_begin + CH);
-    UnitRaw<NC, NV> ring[PF];
-#pragma unroll
-    for (int t = 0; t < PF; ++t) load_raw(u_begin + t, ch_cur, ch_nxt, u_begin, ring[t]);
-    for (int c0 = u_begin; c0 < u_end; c0 += CH) {
-      const int c_end = min(c0 + CH, u_end);
-#pragma unroll 1
-      for (int k = c0; k < c_end; k += UG) {
-        process_group(k, ch_cur, c0, ring);
-        // shift the ring by one group and fetch the group PF units ahead into its tail
-#pragma unroll
-        for (int t = 0; t + UG < PF; ++t) ring[t] = ring[t + UG];
-#pragma unroll
-        for (int g = 0; g < UG; ++g) load_raw(k + PF + g, ch_cur, ch_nxt, c0, ring[PF - UG + g]);
-      }
-      ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
-      ch_nxt = load_chunk(c0 + 2 * CH);
     }
   }
-
-  // ---------------- this wave's partial state -> LDS ----------------
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
-  sacc += __shfl_xor(sacc, 16, 64);
-  sacc += __shfl_xor(sacc, 32, 64);
   if (c16 < G) {
-    const float sub = sacc * (1.0f / 16384.0f);
+    constexpr float kInv = 1.0f / 16384.0f;
+    float* part = a.partials + ((qh0 + c16) * a.n_parts + a.n_splits) * (D + 2);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lds_o[wave][c16][16 * j + 4 * grp + r] = (oacc[j][r] - sub) * vcur;
+      for (int r = 0; r < 4; ++r) part[16 * j + 4 * grp + r] = oacc[j][r] * kInv;
     if (grp == 0) {
-      lds_m[wave][c16] = m;
-      lds_l[wave][c16] = lsum;
-    }
-  }
-  __syncthreads();
-
-  // ---------------- merge the four waves ----------------
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kMfmaWaves) {
-    const int hh = idx / D, dd = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMfmaWaves; ++w) M = fmaxf(M, lds_m[w][hh]);
-    float num = 0.0f, den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kMfmaWaves; ++w) {
-      const float lw = lds_l[w][hh];
-      if (lw > 0.0f) {
-        const float wt = exp2f(lds_m[w][hh] - M);
-        num = fmaf(wt, lds_o[w][hh][dd], num);
-        den = fmaf(wt, lw, den);
-      }
-    }
-    const int64_t qh = qh0 + hh;
-    if (a.n_splits == 1) {
-      a.out[qh * D + dd] = num / den;
-    } else {
-      float* part = a.partials + (qh * a.n_splits + split) * (D + 2);
-      part[dd] = num;
-      if (dd == 0) {
-        part[D] = M;
-        part[D + 1] = den;
-      }
+      part[D] = m;
+      part[D + 1] = lsum * kInv;
     }
   }
 }
@@ -773,7 +1037,7 @@ __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
   __shared__ float den_s;
   const int64_t qh = static_cast<int64_t>(blockIdx.y) * a.hq + blockIdx.x;
   const int dd = threadIdx.x;
-  const int ns = a.n_splits;  // <= 64
+  const int ns = a.n_parts;  // <= 64
   const float* base = a.partials + qh * ns * (D + 2);
   if (dd < 64) {
     const float ms = dd < ns ? base[dd * (D + 2) + D] : -INFINITY;
@@ -815,7 +1079,13 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
     else k_decode_mfma<D, G, 0, 4><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   }
   if (t) t->end(VK_KERNEL_DECODE, s);
-  if (a.n_splits > 1) {
+  if (a.kernel != VK_DECODE_VALU && a.n_parts > a.n_splits) {
+    if (t) t->begin(VK_KERNEL_DECODE_MIXED, s);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mixed<D, G, 1><<<dim3(1, a.P.hkv, a.n_seqs), 64, 0, s>>>(a);
+    else k_decode_mixed<D, G, 0><<<dim3(1, a.P.hkv, a.n_seqs), 64, 0, s>>>(a);
+    if (t) t->end(VK_KERNEL_DECODE_MIXED, s);
+  }
+  if (a.n_parts > 1) {
     if (t) t->begin(VK_KERNEL_MERGE, s);
     k_merge<D><<<dim3(a.hq, a.n_seqs), D, 0, s>>>(a);
     if (t) t->end(VK_KERNEL_MERGE, s);

@@ -65,14 +65,16 @@ struct DecodeArgs {
   PoolsView P;
   const uint16_t* q;       // [n_seqs][hq][dim]
   float* out;              // [n_seqs][hq][dim]
-  float* partials;         // [n_seqs][hq][n_splits][dim + 2]
+  float* partials;         // [n_seqs][hq][n_parts][dim + 2]: (o, max, sum) per part
   int32_t q_dtype;
   int32_t layer;
   int32_t n_seqs;          // in this launch (<= kDecodeMaxSeqs)
   int32_t hq;
   int32_t sink_tokens;
   int32_t window;
-  int32_t n_splits;
+  int32_t n_splits;        // splits of the attended units (parts 0 .. n_splits-1)
+  int32_t n_parts;         // n_splits, or n_splits + 1 when part n_splits holds the fp8 / fp16
+                           // pages (matrix-core path); 1 = the decode kernel writes out directly
   int32_t kernel;          // VK_DECODE_VALU or VK_DECODE_MFMA
   int32_t units_per_iter;  // matrix-core kernel: prefetch depth in 16-token units (4 or 8)
   float scale_log2;        // softmax scale * log2(e)
