@@ -90,13 +90,12 @@ UnitRanges attended_units(int32_t length, int32_t sink_tokens, int32_t window) {
   return r;
 }
 
-int32_t choose_splits(int64_t n_items, int32_t max_units, int32_t target_groups, int32_t max_splits,
+SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blocks, int32_t max_splits,
                       int32_t min_units) {
-  if (n_items <= 0 || max_units <= 0) return 1;
-  int64_t want = cdiv(target_groups, n_items);
-  int64_t by_work = std::max<int64_t>(1, max_units / std::max(1, min_units));
-  int64_t s = std::min<int64_t>({want, by_work, static_cast<int64_t>(max_splits)});
-  return static_cast<int32_t>(std::max<int64_t>(1, s));
+  if (max_units <= 0) return {1, 1};
+  const int64_t want = std::max<int64_t>(std::max(1, min_units), cdiv(total_units, std::max(1, target_blocks)));
+  const int64_t n = std::min<int64_t>(std::max<int64_t>(1, cdiv(max_units, want)), std::max(1, max_splits));
+  return {static_cast<int32_t>(n), static_cast<int32_t>(cdiv(max_units, n))};
 }
 
 HostState::HostState(const vk_cache_config& cfg) : cfg_(cfg) {

@@ -72,8 +72,16 @@ struct UnitRanges {
 };
 UnitRanges attended_units(int32_t length, int32_t sink_tokens, int32_t window);
 
-// Split-K factor: enough work groups to fill the chip, at least `min_units` units per split.
-int32_t choose_splits(int64_t n_items, int32_t max_units, int32_t target_groups, int32_t max_splits,
+// Split-K plan of a decode launch: every split holds units_per_split logical units of its
+// sequence (the last one fewer), so long sequences get more splits than short ones.
+// total_units = attended units summed over the launch's (sequence, KV head) items; the
+// split size aims at target_blocks blocks in all, with at least min_units units, and
+// n_splits = ceil(max_units / units_per_split) <= max_splits.
+struct SplitPlan {
+  int32_t n_splits;
+  int32_t units_per_split;
+};
+SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blocks, int32_t max_splits,
                       int32_t min_units);
 
 class HostState {

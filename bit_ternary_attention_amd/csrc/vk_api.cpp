@@ -39,6 +39,7 @@ constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMinUnits = 4;         // 16-token units per split, at least (vector-ALU kernel)
 constexpr int kDecodeMinUnitsPerWave = 8;  // matrix-core kernel: units per wave, at least
 constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
+constexpr int64_t kDecodeTargetBlocks = 2048;   // matrix-core decode blocks per launch (2 per CU-slot round)
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
   const char* e = std::getenv("VK_DECODE_UPI");
   return (e && e[0] == '4') ? 4 : 8;
@@ -440,15 +441,21 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       c->host->count_units(sid, window, cu);
     }
     for (int f = 0; f < 3; ++f) units[f] += cu[f];
-    // matrix-core path: fp8 / fp16 pages go to their own kernel, as one more partial state
+    // matrix-core path: fp8 / fp16 pages go to one more block per (sequence, KV head), which
+    // writes one more partial state
     const bool mixed = mfma && (cu[1] + cu[2]) > 0;
     const int64_t items = static_cast<int64_t>(nb) * cfg.n_kv_heads;
     const int32_t max_splits = static_cast<int32_t>(
         std::min<int64_t>(kDecodeMaxSplits - (mixed ? 1 : 0), kDecodeScratchItems / items - (mixed ? 1 : 0)));
-    a.n_splits = mfma ? vk::choose_splits(items, max_units, kDecodeTargetGroups / 4, std::max(1, max_splits),
-                                          4 * kDecodeMinUnitsPerWave)
-                      : vk::choose_splits(items, max_units, kDecodeTargetGroups, std::max(1, max_splits),
-                                          kDecodeMinUnits);
+    // Splits hold a fixed number of units, so long sequences get more of them than short
+    // ones (a block past a sequence's units writes an empty part).
+    const int64_t all_units = (cu[0] + cu[1] + cu[2]) * cfg.n_kv_heads;
+    const vk::SplitPlan sp = mfma ? vk::plan_splits(all_units, max_units, kDecodeTargetBlocks,
+                                                    std::max(1, max_splits), 4 * kDecodeMinUnitsPerWave)
+                                  : vk::plan_splits(all_units, max_units, kDecodeTargetGroups,
+                                                    std::max(1, max_splits), kDecodeMinUnits);
+    a.n_splits = sp.n_splits;
+    a.units_per_split = sp.units_per_split;
     a.n_parts = a.n_splits + (mixed ? 1 : 0);
     splits_used = a.n_splits;
     if (c->timer.on) {
@@ -460,8 +467,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       const double out_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 4.0;
       const double part1 = static_cast<double>(nb) * cfg.n_q_heads * (cfg.head_dim + 2) * 4.0;  // one part
       const double dec_out = a.n_parts > 1 ? part1 * a.n_splits : out_bytes;
-      c->timer.add_bytes(VK_KERNEL_DECODE, (mixed ? tern_bytes : tern_bytes + other_bytes) + q_bytes + dec_out);
-      if (mixed) c->timer.add_bytes(VK_KERNEL_DECODE_MIXED, other_bytes + q_bytes + part1);
+      c->timer.add_bytes(VK_KERNEL_DECODE, tern_bytes + other_bytes + q_bytes + dec_out + (mixed ? part1 : 0.0));
       if (a.n_parts > 1) c->timer.add_bytes(VK_KERNEL_MERGE, part1 * a.n_parts + out_bytes);
     }
     hipError_t e = vk::launch_decode(a, g, s, c->timer.on ? &c->timer : nullptr);

@@ -134,8 +134,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
   const Units R = attended(L, a.sink_tokens, a.window);
   const int n_a = R.a_end;
   const int U = R.a_end + (R.b_end - R.b_begin);
-  const int u_begin = static_cast<int>((static_cast<int64_t>(split) * U) / a.n_splits);
-  const int u_end = static_cast<int>((static_cast<int64_t>(split + 1) * U) / a.n_splits);
+  const int u_begin = min(split * a.units_per_split, U);
+  const int u_end = min(u_begin + a.units_per_split, U);
 
   // query rows of this KV head's group, as f16 pairs (d, d+8) within each 16-dim block
   for (int j = lane; j < G * QP; j += 64) {
@@ -392,14 +392,17 @@ constexpr int kMfmaWaves = 4;
 // Fourth word of a raw buffer descriptor on gfx9-family parts (32-bit data format; byte
 // offsets checked against the record count, reads past it return 0).
 constexpr int kBufferWord3 = 0x00020000;
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0), the others at their maximum
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), the others at their maximum
 
 __device__ __forceinline__ uint32_t h2u(h2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
 // 2-bit fields at bit s of each 16-bit half, as f16 u * 2^-14 (bit pattern u << 10).
 template <int S>
 __device__ __forceinline__ uint32_t ucode2(uint32_t w) {
-  if (S <= 10) return (w << (10 - S)) & 0x0C000C00u;
-  return (w >> (S - 10)) & 0x0C000C00u;
+  if constexpr (S <= 10) return (w << (10 - S)) & 0x0C000C00u;
+  else return (w >> (S - 10)) & 0x0C000C00u;
 }
 
 template <int NC, int NV>
@@ -504,7 +507,7 @@ __device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], cons
 }
 
 template <int D, int G, int QDT, int PF>
-__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_decode_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_decode_mfma(DecodeArgs a) {
   constexpr int NC = D / 64;   // 32-bit key code words per lane per unit
   constexpr int NV = D / 64;   // 32-bit value chunk words per lane per unit
   constexpr int NS = D / 32;   // 16x16x32 steps per unit of the score product
@@ -513,8 +516,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int UG = 2;        // units sharing one online-softmax update and one P*V product
   static_assert(G <= 16, "one query head per lane column");
   static_assert(CH % PF == 0 && PF % UG == 0, "chunks hold whole prefetch rounds and groups");
-  __shared__ float lds_o[kMfmaWaves][G][D];
   __shared__ float lds_m[kMfmaWaves][G], lds_l[kMfmaWaves][G];
+  // LDS ring: NR slots per wave, each one unit's key tile then value tile (8 D bytes), filled
+  // by buffer-to-LDS loads.  One array per slot, so the compiler's wait counting can tell
+  // the slots apart and waits only for the load of the slot it reads.
+  constexpr int UB = 8 * D;     // bytes of one unit's tiles of one head
+  constexpr int RB = 64 * 16;   // ring row: one 16-byte piece per lane (head dim 64 fills half)
+  constexpr int NR = PF;
+  static_assert(NR == 8 || NR == 4, "ring of 4 or 8 slots");
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kMfmaWaves][RB], ring1[kMfmaWaves][RB],
+      ring2[kMfmaWaves][RB], ring3[kMfmaWaves][RB], ring4[NR == 8 ? kMfmaWaves : 1][RB],
+      ring5[NR == 8 ? kMfmaWaves : 1][RB], ring6[NR == 8 ? kMfmaWaves : 1][RB], ring7[NR == 8 ? kMfmaWaves : 1][RB];
 
   // wave-uniform indices live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -525,8 +537,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   const Units R = attended(L, a.sink_tokens, a.window);
   const int n_a = R.a_end;
   const int U = R.a_end + (R.b_end - R.b_begin);
-  const int s_begin = static_cast<int>((static_cast<int64_t>(split) * U) / a.n_splits);
-  const int s_end = static_cast<int>((static_cast<int64_t>(split + 1) * U) / a.n_splits);
+  const bool mixed_part = split >= a.n_splits;  // the extra block of the fp8 / fp16 pages
+  const int s_begin = min(split * a.units_per_split, U);  // empty past the sequence's units
+  const int s_end = min(s_begin + a.units_per_split, U);
   const int u_begin = s_begin + ((s_end - s_begin) * wave) / kMfmaWaves;
   const int u_end = s_begin + ((s_end - s_begin) * (wave + 1)) / kMfmaWaves;
   const int u_last = max(u_end - 1, 0);
@@ -536,9 +549,30 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   const int tile0 = static_cast<int>(P.tile_bytes[0]);
   const int page_bytes0 = static_cast<int>(P.page_bytes[0]);
   const int64_t qh0 = static_cast<int64_t>(b) * a.hq + kvh * G;
-  // per-lane byte offsets of the key row slice and the value chunk within a unit
-  const uint32_t lane_k = c16 * (D / 4) + grp * (D / 16);
-  const uint32_t lane_v = (4 * c16 + grp) * (D / 16);
+  // Lane (c16, grp) needs bytes [32 c16 + 8 grp, +8) of the unit's key tile (row c16, dims
+  // 32 grp ..) and the same bytes of its value tile (chunk 4 c16 + grp); head dim 64: 4 bytes
+  // at 16 c16 + 4 grp.  The copy moves 16-byte pieces, lane i to ring offset 16 i.  Head dim
+  // 128 places piece (row r, half h) at 16 (16 h + r): then the 8-byte reads of lanes
+  // 0..31 (and of 32..63) cover 256 contiguous bytes, free of bank conflicts.
+  // lane_k = this lane's read offset in the key half of a ring row (+ UB / 2: value half).
+  const uint32_t lane_k = D == 128 ? 256 * (grp >> 1) + 16 * c16 + 8 * (grp & 1) : c16 * (D / 4) + grp * (D / 16);
+  // piece fetched by this lane: lanes [0, D/4) the key tile, [D/4, D/2) the value tile; with
+  // head dim 64 lanes [32, 64) repeat lanes [0, 32) (every lane issues the copy: no branch)
+  const int hkv_tile = P.hkv * tile0;
+  const int dl = lane % (D / 2), dp = dl % (D / 4);
+  const uint32_t piece = D == 128 ? 32 * (dp % 16) + 16 * (dp / 16) : 16 * dp;
+  const uint32_t dma_off = dl < D / 4 ? piece : hkv_tile + piece;
+  auto ring_row = [&](auto I) -> uint8_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return ring0[wave];
+    else if constexpr (i == 1) return ring1[wave];
+    else if constexpr (i == 2) return ring2[wave];
+    else if constexpr (i == 3) return ring3[wave];
+    else if constexpr (i == 4) return ring4[wave];
+    else if constexpr (i == 5) return ring5[wave];
+    else if constexpr (i == 6) return ring6[wave];
+    else return ring7[wave];
+  };
 
   auto unit_of = [&](int lu) { return lu < n_a ? lu : R.b_begin + (lu - n_a); };
   // every token of logical units [lu, lu + n) is attended
@@ -577,12 +611,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), k));
   };
 
-  // query head c16 (zero beyond the group) as the B operand of the score product, and its sum
+  // Query head c16 (zero beyond the group) as the B operand of the score product: f16
+  // pairs (d, d+8) of each 16-dimension block.  For ternary codes in offset form the logit
+  // is ks (2^14 acc - qoff), qoff = 2^14 sum_d off(d) q_d + sum_d q_d.
   h8_t qb[NS];
   float qsum = 0.0f, qoff = 0.0f;
-  {
-    const uint16_t* qrow = a.q + (qh0 + (c16 < G ? c16 : 0)) * D + dbase;
+  const uint16_t* qhead = a.q + (qh0 + (c16 < G ? c16 : 0)) * D;
+  auto make_qb = [&]() {
+    const uint16_t* qrow = qhead + dbase;
     uint32_t w[NS][4];
+    float sum = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint4 x0 = reinterpret_cast<const uint4*>(qrow + 16 * c)[0];  // dims 16c .. 16c+7
@@ -596,28 +634,26 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             c16 < G ? (q_f16<QDT>(static_cast<uint16_t>(e0)) | (q_f16<QDT>(static_cast<uint16_t>(e1)) << 16)) : 0u;
         w[2 * c + (i >> 2)][i & 3] = pr;
         const h2_t hp = as_h2(pr);
-        qsum += static_cast<float>(hp[0]) + static_cast<float>(hp[1]);
+        sum += static_cast<float>(hp[0]) + static_cast<float>(hp[1]);
       }
     }
-    // constant part of the key operands: koff = sum_d off(d) q_d, with off(d) that of the
-    // code pair (position p = 2 (4 (s & 1) + i)) the dimension pair sits in
     float koff = 0.0f;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qb[s] = __builtin_bit_cast(h8_t, u4_t{w[s][0], w[s][1], w[s][2], w[s][3]});
+    for (int st = 0; st < NS; ++st) {
+      qb[st] = __builtin_bit_cast(h8_t, u4_t{w[st][0], w[st][1], w[st][2], w[st][3]});
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const h2_t hp = as_h2(w[s][i]);
-        koff += ocode_off(2 * (4 * (s & 1) + i)) * (static_cast<float>(hp[0]) + static_cast<float>(hp[1]));
+        const h2_t hp = as_h2(w[st][i]);
+        koff += ocode_off(2 * (4 * (st & 1) + i)) * (static_cast<float>(hp[0]) + static_cast<float>(hp[1]));
       }
     }
-    qsum += __shfl_xor(qsum, 16, 64);
-    qsum += __shfl_xor(qsum, 32, 64);
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
     koff += __shfl_xor(koff, 16, 64);
     koff += __shfl_xor(koff, 32, 64);
-    // logit = ks (2^14 acc - qoff) with acc the score product
-    qoff = 16384.0f * koff + qsum;
-  }
+    qsum = sum;
+    qoff = 16384.0f * koff + sum;  // logit = ks (2^14 acc - qoff) for offset-form codes
+  };
 
   f4_t oacc[NB];
 #pragma unroll
@@ -628,11 +664,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   const h2_t ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
   const OConst oc = oconst();
 
-  // Packed codes of logical unit lu into r.  Always issued (a fixed number of loads per
-  // unit, so the compiler can wait precisely): other formats and units past the end
-  // read the zeroed dummy page instead.
-  auto load_raw = [&](int lu, const Chunk& cc, const Chunk& cn, int c0, UnitRaw<NC, NV>& r) {
-    // units past the end re-read the last unit: their scores are masked
+  // Starts the copy of logical unit lu's key and value tiles of this head into a ring row.
+  // Always issued (a fixed number of loads per unit keeps the waits exact): other formats
+  // read the zeroed dummy page, units past the end re-read the last unit (masked).
+  auto dma_unit = [&](int lu, const Chunk& cc, const Chunk& cn, int c0, uint8_t* row) {
     const int lc = min(lu, u_last);
     const int k = lc - c0;
     const bool in_cur = k < CH;
@@ -640,21 +675,22 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const uint32_t hi = __builtin_amdgcn_readlane(in_cur ? cc.phi : cn.phi, in_cur ? k : k - CH);
     const uint8_t* pg = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
     const int upi = ((unit_of(lc) * 16) & (P.bs - 1)) >> 4;  // the dummy page takes any unit offset
-    // buffer loads: page base in the descriptor, unit offset scalar, lane offset vector
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, page_bytes0, kBufferWord3);
-    const int sk = kvh * tile0 + upi * 16 * (D / 4);
-    const int sv = (P.hkv + kvh) * tile0 + upi * 4 * D;
+    const int soff = kvh * tile0 + upi * 4 * D;  // unit offset within the key (and value) tile
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)row, 16, dma_off, soff, 0, 0);
+  };
+  auto read_unit = [&](const uint8_t* row, UnitRaw<NC, NV>& r) {
     if (NC == 2) {
-      const u2_t x = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, lane_k, sk, 0));
-      const u2_t y = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, lane_v, sv, 0));
-      r.k[0] = x[0];
-      r.k[NC - 1] = x[1];
-      r.v[0] = y[0];
-      r.v[NV - 1] = y[1];
+      const uint2 x = *reinterpret_cast<const uint2*>(row + lane_k);
+      const uint2 y = *reinterpret_cast<const uint2*>(row + UB / 2 + lane_k);
+      r.k[0] = x.x;
+      r.k[NC - 1] = x.y;
+      r.v[0] = y.x;
+      r.v[NV - 1] = y.y;
     } else {
-      r.k[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_k, sk, 0);
-      r.v[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane_v, sv, 0);
+      r.k[0] = *reinterpret_cast<const uint32_t*>(row + lane_k);
+      r.v[0] = *reinterpret_cast<const uint32_t*>(row + UB / 2 + lane_k);
     }
   };
 
@@ -695,14 +731,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         continue;
       }
       const UnitRaw<NC, NV>& raw = g == 0 ? r0 : r1;
-      h8_t ka[NS];
-      ka_ternary<NS, NC>(raw.k, ka, oc);
       const float ks = lane_f(cc.gk, k0 + g) * a.scale_log2;
       vs[g] = lane_f(cc.gv, k0 + g);
-      const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
+      h8_t ka[NS];
+      ka_ternary<NS, NC>(raw.k, ka, oc);
       f4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
+      for (int st = 0; st < NS; ++st) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[st], qb[st], s4, 0, 0, 0);
+      const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
       if (full) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
@@ -776,133 +812,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  if (u_begin < u_end) {
-    // Two register buffers of PH units each: while one is processed, the other's loads
-    // are in flight (every wait then targets loads issued a whole phase earlier).
-    constexpr int PH = PF / 2;
-    Chunk ch_cur = load_chunk(u_begin);
-    Chunk ch_nxt = load_chunk(u_begin + CH);
-    UnitRaw<NC, NV> buf_a[PH], buf_b[PH];
-#pragma unroll
-    for (int t = 0; t < PH; ++t) load_raw(u_begin + t, ch_cur, ch_nxt, u_begin, buf_a[t]);
-    for (int c0 = u_begin; c0 < u_end; c0 += CH) {
-      const int c_end = min(c0 + CH, u_end);
-#pragma unroll 1
-      for (int k = c0; k < c_end; k += 2 * PH) {
-#pragma unroll
-        for (int t = 0; t < PH; ++t) load_raw(k + PH + t, ch_cur, ch_nxt, c0, buf_b[t]);
-#pragma unroll
-        for (int gi = 0; gi < PH / UG; ++gi) process_group(k + gi * UG, ch_cur, c0, buf_a[gi * UG], buf_a[gi * UG + 1]);
-#pragma unroll
-        for (int t = 0; t < PH; ++t) load_raw(k + 2 * PH + t, ch_cur, ch_nxt, c0, buf_a[t]);
-#pragma unroll
-        for (int gi = 0; gi < PH / UG; ++gi)
-          process_group(k + PH + gi * UG, ch_cur, c0, buf_b[gi * UG], buf_b[gi * UG + 1]);
-      }
-      ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
-      ch_nxt = load_chunk(c0 + 2 * CH);
-    }
-  }
-
-  // ---------------- this wave's partial state -> LDS ----------------
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  tsum += __shfl_xor(tsum, 16, 64);
-  tsum += __shfl_xor(tsum, 32, 64);
-  if (c16 < G) {
-    constexpr float kInv = 1.0f / 16384.0f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      // ternary tokens added p' (off_j + u 2^-14); their values are gamma (u - 1)
-      const float sub = tsum * (va_off<NV>(j) + kInv);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lds_o[wave][c16][16 * j + 4 * grp + r] = (oacc[j][r] - sub) * vcur;
-    }
-    if (grp == 0) {
-      lds_m[wave][c16] = m;
-      lds_l[wave][c16] = lsum * kInv;
-    }
-  }
-  __syncthreads();
-
-  // ---------------- merge the four waves ----------------
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kMfmaWaves) {
-    const int hh = idx / D, dd = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMfmaWaves; ++w) M = fmaxf(M, lds_m[w][hh]);
-    float num = 0.0f, den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kMfmaWaves; ++w) {
-      const float lw = lds_l[w][hh];
-      if (lw > 0.0f) {
-        const float wt = exp2f(lds_m[w][hh] - M);
-        num = fmaf(wt, lds_o[w][hh][dd], num);
-        den = fmaf(wt, lw, den);
-      }
-    }
-    const int64_t qh = qh0 + hh;
-    if (a.n_parts == 1) {
-      a.out[qh * D + dd] = num / den;
-    } else {
-      float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
-      part[dd] = num;
-      if (dd == 0) {
-        part[D] = M;
-        part[D + 1] = den;
-      }
-    }
-  }
-}
-
-// fp8 / fp16 pages on the matrix-core path.  One wave per (sequence, KV head) walks the
-// attended units 64 at a time, picks the non-ternary ones from the block table (a ballot
-// over one entry per lane) and folds them into one online-softmax state, written as part
-// n_splits of the split partials (an empty state if the sequence has no such page).  The
-// values enter the second product as themselves (fp8 scaled by fp8_scale), so this part
-// needs no offset bookkeeping.
-template <int D, int G, int QDT>
-__global__ __launch_bounds__(64) void k_decode_mixed(DecodeArgs a) {
-  constexpr int NC = D / 64, NS = D / 32, NB = D / 16;
-  const int lane = threadIdx.x, grp = lane >> 4, c16 = lane & 15;
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int slot = a.slots[b], L = a.lens[b];
-  const PoolsView& P = a.P;
-  const Units R = attended(L, a.sink_tokens, a.window);
-  const int n_a = R.a_end;
-  const int U = R.a_end + (R.b_end - R.b_begin);
-  const int dbase = grp * (D / 4);
-  const int64_t layer = a.layer;
-  const int32_t* bt = P.block_table + static_cast<int64_t>(slot) * P.max_pages;
-  const int64_t qh0 = static_cast<int64_t>(b) * a.hq + kvh * G;
-  auto unit_of = [&](int lu) { return lu < n_a ? lu : R.b_begin + (lu - n_a); };
-
-  // query head c16 as the B operand of the score product (plain f16 values)
-  h8_t qb[NS];
-  {
-    const uint16_t* qrow = a.q + (qh0 + (c16 < G ? c16 : 0)) * D + dbase;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint4 x0 = reinterpret_cast<const uint4*>(qrow + 16 * c)[0];
-      const uint4 x1 = reinterpret_cast<const uint4*>(qrow + 16 * c)[1];
-      const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
-      uint32_t w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t e0 = (lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t e1 = (hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        w[i] = c16 < G ? (q_f16<QDT>(static_cast<uint16_t>(e0)) | (q_f16<QDT>(static_cast<uint16_t>(e1)) << 16)) : 0u;
-      }
-      qb[2 * c] = __builtin_bit_cast(h8_t, u4_t{w[0], w[1], w[2], w[3]});
-      qb[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{w[4], w[5], w[6], w[7]});
-    }
-  }
-  const h2_t ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
-  f4_t oacc[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) oacc[j] = f4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.0f;  // oacc and lsum count p' = 2^14 p
-
   // A operands and scales of a non-ternary unit, loaded here (f16 values, not u * 2^-14)
   auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float& scale) {
     const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
@@ -960,70 +869,171 @@ __global__ __launch_bounds__(64) void k_decode_mixed(DecodeArgs a) {
     }
   };
 
-  for (int c0 = 0; c0 < U; c0 += 64) {
-    const int lu_l = c0 + lane;
-    const int32_t ent_l = lu_l < U ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
-    uint64_t todo = __ballot(lu_l < U && (static_cast<uint32_t>(ent_l) >> 30) != VK_FMT_TERNARY2);
-    while (todo) {
-      const int k = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      const int lu = c0 + k;
-      const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
-      h8_t ka[NS];
-      h4_t va[NB];
-      float vscale;
-      operands_other(lu, entry, ka, va, vscale);
-      f4_t s4 = {0.f, 0.f, 0.f, 0.f};
+  // Block x = n_splits: the fp8 / fp16 units of every attended range.  Every wave scans the
+  // range 64 units at a time (a ballot over one block-table entry per lane) and takes every
+  // fourth such unit.  Their values enter the product as themselves (fp8 scaled by
+  // fp8_scale): no offsets, no gamma bookkeeping (vcur stays 1, tsum 0).
+  if (mixed_part) {
+    make_qb();
+    vcur = 1.0f;
+    int rank = 0;  // non-ternary units seen so far (uniform)
+    for (int c0 = 0; c0 < U; c0 += 64) {
+      const int lu_l = c0 + lane;
+      const int32_t ent_l = lu_l < U ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
+      uint64_t todo = __ballot(lu_l < U && (static_cast<uint32_t>(ent_l) >> 30) != VK_FMT_TERNARY2);
+      while (todo) {
+        const int k = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        if (rank++ % kMfmaWaves != wave) continue;
+        const int lu = c0 + k;
+        const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
+        h8_t ka[NS];
+        h4_t va[NB];
+        float vscale;
+        operands_other(lu, entry, ka, va, vscale);
+        f4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
-      const float a0 = vscale * a.scale_log2;
-      const int u = unit_of(lu);
-      float sc[4];
-      float mx = -INFINITY;
+        for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
+        const float a0 = vscale * a.scale_log2;
+        const int u = unit_of(lu);
+        float sc[4];
+        float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = u * 16 + 4 * grp + r;
-        const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
-        sc[r] = att ? s4[r] * a0 : -INFINITY;
-        mx = fmaxf(mx, sc[r]);
-      }
-      mx = max_rows(mx);
-      if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) continue;
-      if (__ballot(mx > m) != 0) {
-        const float mn = fmaxf(m, mx);
-        const float corr = __builtin_amdgcn_exp2f(m - mn);
+        for (int r = 0; r < 4; ++r) {
+          const int t = u * 16 + 4 * grp + r;
+          const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
+          sc[r] = att ? s4[r] * a0 : -INFINITY;
+          mx = fmaxf(mx, sc[r]);
+        }
+        mx = max_rows(mx);
+        if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) continue;
+        if (__ballot(mx > m) != 0) {
+          const float mn = fmaxf(m, mx);
+          const float corr = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) oacc[j] *= corr;
-        lsum *= corr;
-        m = mn;
-      }
-      const float ms = m - 14.0f;
-      const h2_t p01 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[0] - ms)),
-                        static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[1] - ms))};
-      const h2_t p23 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[2] - ms)),
-                        static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[3] - ms))};
-      lsum = __builtin_amdgcn_fdot2(p01, ones, lsum, false);
-      lsum = __builtin_amdgcn_fdot2(p23, ones, lsum, false);
-      const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(p01), h2u(p23)});
+          for (int j = 0; j < NB; ++j) oacc[j] *= corr;
+          lsum *= corr;
+          m = mn;
+        }
+        const float ms = m - 14.0f;
+        const h2_t p01 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[0] - ms)),
+                          static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[1] - ms))};
+        const h2_t p23 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[2] - ms)),
+                          static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[3] - ms))};
+        lsum = __builtin_amdgcn_fdot2(p01, ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2(p23, ones, lsum, false);
+        const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(p01), h2u(p23)});
+        const float vs14 = vscale * (1.0f / 16384.0f);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const f4_t t4 = __builtin_amdgcn_mfma_f32_16x16x16f16(va[j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        oacc[j] += t4 * vscale;
+        for (int j = 0; j < NB; ++j) {
+          const f4_t t4 = __builtin_amdgcn_mfma_f32_16x16x16f16(va[j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          oacc[j] += t4 * vs14;
+        }
       }
     }
   }
+
+  if (!mixed_part && u_begin < u_end) {
+    // ring slot s holds unit k + s while the group of slots (2i, 2i + 1) is processed; a
+    // processed slot is refilled with the unit NR ahead.  The query set-up overlaps the
+    // first copies.
+    using std::integral_constant;
+    Chunk ch_cur = load_chunk(u_begin);
+    Chunk ch_nxt = load_chunk(u_begin + CH);
+    auto prologue = [&](auto I) { dma_unit(u_begin + decltype(I)::value, ch_cur, ch_nxt, u_begin, ring_row(I)); };
+    prologue(integral_constant<int, 0>{});
+    prologue(integral_constant<int, 1>{});
+    prologue(integral_constant<int, 2>{});
+    prologue(integral_constant<int, 3>{});
+    if constexpr (NR == 8) {
+      prologue(integral_constant<int, 4>{});
+      prologue(integral_constant<int, 5>{});
+      prologue(integral_constant<int, 6>{});
+      prologue(integral_constant<int, 7>{});
+    }
+    make_qb();
+    for (int c0 = u_begin; c0 < u_end; c0 += CH) {
+      const int c_end = min(c0 + CH, u_end);
+#pragma unroll 1
+      for (int k = c0; k < c_end; k += NR) {
+        auto step = [&](auto GI) {
+          constexpr int gi = decltype(GI)::value;
+          UnitRaw<NC, NV> r0, r1;
+          read_unit(ring_row(integral_constant<int, 2 * gi>{}), r0);
+          read_unit(ring_row(integral_constant<int, 2 * gi + 1>{}), r1);
+          process_group(k + 2 * gi, ch_cur, c0, r0, r1);
+          // the slot reads have returned before their rows are overwritten
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          dma_unit(k + NR + 2 * gi, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi>{}));
+          dma_unit(k + NR + 2 * gi + 1, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi + 1>{}));
+        };
+        step(integral_constant<int, 0>{});
+        step(integral_constant<int, 1>{});
+        if constexpr (NR == 8) {
+          step(integral_constant<int, 2>{});
+          step(integral_constant<int, 3>{});
+        }
+      }
+      ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
+      ch_nxt = load_chunk(c0 + 2 * CH);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy into the ring is left in flight
+  }
+
+  // ---------------- this wave's partial state -> LDS ----------------
+  // (the G x D outputs of wave w go to ring array w, free once every wave has left its loop)
+  static_assert(G * D * 4 <= kMfmaWaves * RB, "a wave's outputs fit one ring array");
+  auto out_row = [&](int w) -> float* {
+    uint8_t* r = w == 0 ? &ring0[0][0] : w == 1 ? &ring1[0][0] : w == 2 ? &ring2[0][0] : &ring3[0][0];
+    return reinterpret_cast<float*>(r);
+  };
+  __syncthreads();
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  tsum += __shfl_xor(tsum, 16, 64);
+  tsum += __shfl_xor(tsum, 32, 64);
   if (c16 < G) {
     constexpr float kInv = 1.0f / 16384.0f;
-    float* part = a.partials + ((qh0 + c16) * a.n_parts + a.n_splits) * (D + 2);
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NB; ++j) {
+      // ternary tokens added p' (off_j + u 2^-14); their values are gamma (u - 1)
+      const float sub = tsum * (va_off<NV>(j) + kInv);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part[16 * j + 4 * grp + r] = oacc[j][r] * kInv;
+      for (int r = 0; r < 4; ++r) out_row(wave)[c16 * D + 16 * j + 4 * grp + r] = (oacc[j][r] - sub) * vcur;
+    }
     if (grp == 0) {
-      part[D] = m;
-      part[D + 1] = lsum * kInv;
+      lds_m[wave][c16] = m;
+      lds_l[wave][c16] = lsum * kInv;
+    }
+  }
+  __syncthreads();
+
+  // ---------------- merge the four waves ----------------
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kMfmaWaves) {
+    const int hh = idx / D, dd = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; ++w) M = fmaxf(M, lds_m[w][hh]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMfmaWaves; ++w) {
+      const float lw = lds_l[w][hh];
+      if (lw > 0.0f) {
+        const float wt = exp2f(lds_m[w][hh] - M);
+        num = fmaf(wt, out_row(w)[hh * D + dd], num);
+        den = fmaf(wt, lw, den);
+      }
+    }
+    const int64_t qh = qh0 + hh;
+    if (a.n_parts == 1) {
+      a.out[qh * D + dd] = num / den;
+    } else {
+      float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
+      part[dd] = num;
+      if (dd == 0) {
+        part[D] = M;
+        part[D + 1] = den;
+      }
     }
   }
 }
@@ -1066,7 +1076,8 @@ __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
-  const dim3 grid(a.n_splits, a.P.hkv, a.n_seqs);
+  // matrix-core path: block x = n_splits (when present) takes the fp8 / fp16 pages
+  const dim3 grid(a.kernel == VK_DECODE_VALU ? a.n_splits : a.n_parts, a.P.hkv, a.n_seqs);
   if (t) t->begin(VK_KERNEL_DECODE, s);
   if (a.kernel == VK_DECODE_VALU) {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
@@ -1079,12 +1090,6 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
     else k_decode_mfma<D, G, 0, 4><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   }
   if (t) t->end(VK_KERNEL_DECODE, s);
-  if (a.kernel != VK_DECODE_VALU && a.n_parts > a.n_splits) {
-    if (t) t->begin(VK_KERNEL_DECODE_MIXED, s);
-    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mixed<D, G, 1><<<dim3(1, a.P.hkv, a.n_seqs), 64, 0, s>>>(a);
-    else k_decode_mixed<D, G, 0><<<dim3(1, a.P.hkv, a.n_seqs), 64, 0, s>>>(a);
-    if (t) t->end(VK_KERNEL_DECODE_MIXED, s);
-  }
   if (a.n_parts > 1) {
     if (t) t->begin(VK_KERNEL_MERGE, s);
     k_merge<D><<<dim3(a.hq, a.n_seqs), D, 0, s>>>(a);

@@ -73,6 +73,8 @@ struct DecodeArgs {
   int32_t sink_tokens;
   int32_t window;
   int32_t n_splits;        // splits of the attended units (parts 0 .. n_splits-1)
+  int32_t units_per_split; // split x takes logical units [x u, (x + 1) u) of its sequence
+                           // (none past the sequence's end: an empty part)
   int32_t n_parts;         // n_splits, or n_splits + 1 when part n_splits holds the fp8 / fp16
                            // pages (matrix-core path); 1 = the decode kernel writes out directly
   int32_t kernel;          // VK_DECODE_VALU or VK_DECODE_MFMA

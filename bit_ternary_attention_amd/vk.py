@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libvk.so")
 OK, ERR_ARG, ERR_OOM, ERR_CAPACITY, ERR_ALIGN, ERR_STATE, ERR_HIP = range(7)
 DTYPE_F16, DTYPE_BF16 = 0, 1
 FMT_TERNARY2, FMT_FP8E4M3, FMT_F16 = 0, 1, 2
-KERNELS = ("absmean", "finalize", "pack", "decode", "merge", "decode_mixed")
+KERNELS = ("absmean", "finalize", "pack", "decode", "merge")
 DECODE_DEFAULT, DECODE_VALU, DECODE_MFMA = 0, 1, 2
 
 _c_i32, _c_i64, _c_f32, _c_u64, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_void_p

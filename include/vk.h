@@ -210,9 +210,7 @@ enum {
   VK_KERNEL_PACK = 2,      /* write side pass 2: quantise, pack, scatter      */
   VK_KERNEL_DECODE = 3,    /* paged decode attention (per split)              */
   VK_KERNEL_MERGE = 4,     /* split-K online-softmax merge                    */
-  VK_KERNEL_DECODE_MIXED = 5, /* fp8 / fp16 pages of the matrix-core path,
-                                 one partial state per sequence and head      */
-  VK_KERNEL_COUNT = 6
+  VK_KERNEL_COUNT = 5
 };
 /* enable != 0 starts timing and clears the totals; 0 stops it. */
 VK_API vk_status vk_set_kernel_timing(vk_cache* c, int32_t enable);

@@ -105,7 +105,8 @@ def hs():
     L.hs_count_units.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(ctypes.c_longlong)]
     L.hs_reset.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int)]
     L.hs_attended_units.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(ctypes.c_int)]
-    L.hs_choose_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.hs_plan_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.POINTER(ctypes.c_int)]
     return L
 
 
@@ -254,8 +255,22 @@ def test_route_counters_match_page_formats(hs):
         assert list(out) == want, W
 
 
-def test_split_choice(hs):
-    assert hs.hs_choose_splits(256, 2048, 4096, 64, 8) == 16
-    assert hs.hs_choose_splits(32, 8192, 4096, 64, 8) == 64
-    assert hs.hs_choose_splits(2, 17, 4096, 64, 8) == 2
-    assert hs.hs_choose_splits(4096, 100, 4096, 64, 8) == 1
+def _plan(hs, total, max_units, target, max_splits, min_units):
+    ups = ctypes.c_int(0)
+    n = hs.hs_plan_splits(total, max_units, target, max_splits, min_units, ctypes.byref(ups))
+    return n, ups.value
+
+
+def test_split_plan(hs):
+    # 32 sequences x 8 heads x 2048 units, 2048 blocks wanted: 256-unit splits
+    assert _plan(hs, 32 * 8 * 2048, 2048, 2048, 64, 32) == (8, 256)
+    # few items: the minimum split size rules
+    assert _plan(hs, 2 * 17, 17, 2048, 64, 32) == (1, 17)
+    # the split cap rules: splits grow to cover the longest sequence
+    assert _plan(hs, 4 * 8 * 8192, 8192, 2048, 32, 32) == (32, 256)
+    # mixed lengths: the split size follows the total, the count the longest sequence
+    n, ups = _plan(hs, 8 * (1024 + 64), 1024, 64, 64, 8)
+    assert (n, ups) == (8, 128)  # 136 wanted; 8 splits then cover 1024 units with 128 each
+    for total, mx, tgt, cap, mn in [(1, 1, 2048, 64, 32), (10**7, 12345, 2048, 64, 32), (500, 7, 4096, 3, 4)]:
+        n, ups = _plan(hs, total, mx, tgt, cap, mn)
+        assert 1 <= n <= cap and n * ups >= mx and (n - 1) * ups < mx
