@@ -39,7 +39,7 @@ constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMinUnits = 4;         // 16-token units per split, at least (vector-ALU kernel)
 constexpr int kDecodeMinUnitsPerWave = 8;  // matrix-core kernel: units per wave, at least
 constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
-constexpr int64_t kDecodeTargetBlocks = 2048;   // matrix-core decode blocks per launch (2 per CU-slot round)
+constexpr int64_t kDecodeTargetBlocks = 1024;   // matrix-core decode blocks per launch (one round of 4 per CU)
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
   const char* e = std::getenv("VK_DECODE_UPI");
   return (e && e[0] == '4') ? 4 : 8;
@@ -433,11 +433,20 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     a.scale_log2 = scale * 1.4426950408889634f;
     int32_t max_units = 0;
     int64_t cu[3] = {0, 0, 0};  // attended units per format in this launch
+    // longest attended ranges first: their blocks are dispatched first, shorter ones fill in
+    int32_t order[vk::kDecodeMaxSeqs], units_of[vk::kDecodeMaxSeqs];
     for (int32_t i = 0; i < nb; ++i) {
       const int32_t sid = seq_ids[base + i];
+      units_of[i] = vk::attended_units(c->host->seq(sid).length, cfg.sink_tokens, window).n_units();
+      order[i] = i;
+    }
+    std::stable_sort(order, order + nb, [&](int32_t x, int32_t y) { return units_of[x] > units_of[y]; });
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t sid = seq_ids[base + order[i]];
       a.slots[i] = sid;
       a.lens[i] = c->host->seq(sid).length;
-      max_units = std::max(max_units, vk::attended_units(a.lens[i], cfg.sink_tokens, window).n_units());
+      a.rows[i] = order[i];
+      max_units = std::max(max_units, units_of[order[i]]);
       c->host->count_units(sid, window, cu);
     }
     for (int f = 0; f < 3; ++f) units[f] += cu[f];

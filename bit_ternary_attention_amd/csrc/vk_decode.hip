@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
   // query rows of this KV head's group, as f16 pairs (d, d+8) within each 16-dim block
   for (int j = lane; j < G * QP; j += 64) {
     const int hh = j / QP, jj = j % QP, w = jj >> 3, ii = jj & 7;
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(b) * a.hq + kvh * G + hh) * D;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(a.rows[b]) * a.hq + kvh * G + hh) * D;
     q2[j] = q_f16<QDT>(qrow[16 * w + ii]) | (q_f16<QDT>(qrow[16 * w + 8 + ii]) << 16);
   }
   __syncthreads();
@@ -345,11 +345,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const float l = wave_sum(lsum[hh]);
-    const int64_t qh = static_cast<int64_t>(b) * a.hq + kvh * G + hh;
+    const int64_t qh = static_cast<int64_t>(b) * a.hq + kvh * G + hh;  // partial slot
     if (a.n_parts == 1) {
       const float inv = 1.0f / l;
+      const int64_t qo = static_cast<int64_t>(a.rows[b]) * a.hq + kvh * G + hh;
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) a.out[qh * D + lane * DPL + j] = o[hh][j] * inv;
+      for (int j = 0; j < DPL; ++j) a.out[qo * D + lane * DPL + j] = o[hh][j] * inv;
     } else {
       float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
 #pragma unroll
@@ -548,7 +549,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   const int32_t* bt = P.block_table + static_cast<int64_t>(slot) * P.max_pages;
   const int tile0 = static_cast<int>(P.tile_bytes[0]);
   const int page_bytes0 = static_cast<int>(P.page_bytes[0]);
-  const int64_t qh0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+  const int64_t qh0 = static_cast<int64_t>(b) * a.hq + kvh * G;          // partial slots
+  const int64_t qo0 = static_cast<int64_t>(a.rows[b]) * a.hq + kvh * G;  // query / output rows
   // Lane (c16, grp) needs bytes [32 c16 + 8 grp, +8) of the unit's key tile (row c16, dims
   // 32 grp ..) and the same bytes of its value tile (chunk 4 c16 + grp); head dim 64: 4 bytes
   // at 16 c16 + 4 grp.  The copy moves 16-byte pieces, lane i to ring offset 16 i.  Head dim
@@ -616,7 +618,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // is ks (2^14 acc - qoff), qoff = 2^14 sum_d off(d) q_d + sum_d q_d.
   h8_t qb[NS];
   float qsum = 0.0f, qoff = 0.0f;
-  const uint16_t* qhead = a.q + (qh0 + (c16 < G ? c16 : 0)) * D;
+  const uint16_t* qhead = a.q + (qo0 + (c16 < G ? c16 : 0)) * D;
   auto make_qb = [&]() {
     const uint16_t* qrow = qhead + dbase;
     uint32_t w[NS][4];
@@ -1026,7 +1028,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
     const int64_t qh = qh0 + hh;
     if (a.n_parts == 1) {
-      a.out[qh * D + dd] = num / den;
+      a.out[(qo0 + hh) * D + dd] = num / den;
     } else {
       float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
       part[dd] = num;
@@ -1071,7 +1073,7 @@ __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) num = s0 + k < ns ? fmaf(wts[s0 + k], o8[k], num) : num;
   }
-  a.out[qh * D + dd] = num / den_s;
+  a.out[(static_cast<int64_t>(a.rows[blockIdx.y]) * a.hq + blockIdx.x) * D + dd] = num / den_s;
 }
 
 template <int D, int G>

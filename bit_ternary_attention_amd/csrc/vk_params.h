@@ -80,8 +80,9 @@ struct DecodeArgs {
   int32_t kernel;          // VK_DECODE_VALU or VK_DECODE_MFMA
   int32_t units_per_iter;  // matrix-core kernel: prefetch depth in 16-token units (4 or 8)
   float scale_log2;        // softmax scale * log2(e)
-  int32_t slots[kDecodeMaxSeqs];
+  int32_t slots[kDecodeMaxSeqs];   // launch order: longest attended range first
   int32_t lens[kDecodeMaxSeqs];
+  int32_t rows[kDecodeMaxSeqs];    // query / output row (within the launch) of each
 };
 
 struct QuantArgs {
