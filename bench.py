@@ -56,10 +56,13 @@ def main():
 
     torch.cuda.set_device(0)
     if args.calibration_copy_mib:
+        # a plain copy of known size (read n bytes, write n bytes) under a kernel name of its
+        # own, to scale the FETCH_SIZE / WRITE_SIZE counters
         n = args.calibration_copy_mib * 2 ** 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     w = wl.workload(args.workload)
@@ -190,7 +193,7 @@ def main():
         "kernels": kernels,
         "ms_per_step_with_kernel_timing": round(ms_step_timed, 4),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": None,
+                     "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": measured_traffic(dominant, w.name),
                      "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": dk["avg_us"]},
     }
 
@@ -198,6 +201,24 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_sample_layers)
     print(json.dumps(result), flush=True)
     cache.close()
+
+
+def measured_traffic(kind, workload_name):
+    """HBM bytes per launch of this kernel on this workload, from the FETCH_SIZE / WRITE_SIZE
+    counter record kept with the profiles (calibrated by a plain copy), or None when there
+    is no record or the kernel's sources have changed since it was taken."""
+    from bit_ternary_attention_amd import profsum
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kind}|{workload_name}")
+    if rec is None:
+        return None
+    srcs = [os.path.join(ROOT, p) for p in rec["sources"]]
+    if not all(os.path.exists(p) for p in srcs) or profsum.sources_sha256(srcs) != rec["source_sha256"]:
+        return None
+    return round(rec["hbm_bytes_per_dispatch"])
 
 
 def cpu_baseline(w, calls, sample_layers):

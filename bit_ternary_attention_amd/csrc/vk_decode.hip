@@ -4,27 +4,20 @@
 // Follows "Minima-KV" (twodots.gr), section on mixed-format attention: each
 // page is read in its own format as it is loaded (no dense copy), every
 // branch produces a partial state (max score, sum of exponentials, output),
-// and partial states are merged with one online-softmax normalisation in
-// logical page order.  The attended set (first sink_tokens plus the recent
-// window, or the whole context) follows "Show HN: Vantage-V-AI", quick start
-// and core architecture.
+// and partial states are merged with one online-softmax normalisation.  The
+// attended set (first sink_tokens plus the recent window, or the whole
+// context) follows "Show HN: Vantage-V-AI", quick start and core architecture.
 //
-// One wave per (sequence, KV head, split).  A split walks its attended
-// 16-token units four at a time:
-//   scores  lane = token: the key row's 2-bit codes are unpacked to f16
-//           {-1, 0, +1} in registers (OR into the mantissa of 1024.0, then
-//           subtract 1025) and dotted with the g query rows kept in LDS,
-//           two dimensions per v_dot2_f32_f16, accumulated in float32;
-//   softmax the reference max is shared by the wave (cross-lane max), so
-//           probabilities of all four units are comparable; they go to LDS
-//           as f16 (scaled by 2^14 to stay clear of f16 subnormals);
-//   PV      lane = head dimension: the value chunks of a unit hold two
-//           consecutive tokens of one dimension in the two 16-bit halves of a
-//           word, so pairs of tokens are unpacked the same way and dotted with
-//           the matching probability pairs; gamma_V (or the fp8 scale) is
-//           applied per unit.
-// Splits write (o, max, sum) partials that k_merge combines; with one split
-// the kernel writes the normalised output.
+// Two kernels compute the same thing:
+//   k_decode_mfma (default): scores and P*V on the matrix cores (the g query
+//     heads of a KV head share every unpacked code), pages staged in LDS by
+//     buffer-to-LDS copies; see the section comment further down;
+//   k_decode (vector ALU): one wave per (sequence, KV head, split), codes
+//     unpacked to f16 {-1, 0, +1} pairs and dotted with v_dot2_f32_f16 against
+//     the query rows in LDS (scores, lane = token) and the probabilities
+//     (P*V, lane = head dimension).
+// Splits write (o, max, sum) partials that k_merge combines; with a single
+// part the kernel writes the normalised output.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -366,23 +359,25 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 // ------------------------------------------------------------------------
 // Matrix-core variant.  Per 16-token unit:
 //   S^T[16 tok x 16 heads] = K[16 x D] * Q^T[D x 16]   (D/32 x v_mfma_f32_16x16x32_f16)
-//   O^T[D x 16 heads]     += V^T[D x 16] * P[16 x 16]   (D/16 x v_mfma_f32_16x16x16_f16)
+//   O^T[D x 16 heads]     += V^T[D x 32] * P[32 x 16]   (per two units, D/16 x 16x16x32)
 // Lane l holds token/dimension row l%16 of the A operands and query head l%16
 // of the B operands; the score output (lane l: tokens 4(l/16)+r, head l%16) is
 // exactly the P operand layout of the second product, so probabilities never
 // leave registers.  Query heads beyond the group (g < 16) are zero columns.
 //
-// Codes enter the products as u = code + 1 in {0, 1, 2}: the f16 bit pattern
-// u << 10 is the value u * 2^-14 (0, the smallest normal, twice it), so each
-// pair of codes costs one shift and one AND.  The offsets are removed once per
-// head: sum_d q_d (u_d - 1) = 2^14 * acc - sum_d q_d for scores, and
-// sum_t p_t (u_t - 1) = 2^14 * acc - sum_t p_t for the output.
+// Codes enter the products as u = code + 1 in {0, 1, 2}, as f16 values off + u 2^-14
+// (offset form below: one v_and_or_b32 per pair of codes); the constant parts are
+// removed once per head: sum_d q_d (u_d - 1) follows from the score product and
+// sum_d (off_d + 2^-14) q_d, and sum_t p_t (u_t - 1) from the P*V product and
+// sum_t p_t (off_j + 2^-14) per 16-dimension block j.
 //
-// Four waves share one (sequence, KV head, split): each walks a quarter of
-// its units (prefetching codes PF units ahead into registers, one block-table
-// entry and gamma pair per lane for 64 units at a time), and the four partial
-// states are merged through LDS.  Global splits, when there are several, are
-// merged by k_merge.
+// Four waves share one (sequence, KV head, split): each walks a quarter of the
+// split's units.  A unit's key and value tiles of the head (8 D bytes) are copied
+// into the wave's LDS ring by one buffer-to-LDS load, NR units ahead; the page
+// addresses come from the block table, one entry per lane for 64 units at a time.
+// The four partial states are merged through LDS; global splits by k_merge.
+// Block x = n_splits (when the attended set has fp8 / fp16 pages) handles those
+// pages and writes one more partial state.
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));

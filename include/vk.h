@@ -70,8 +70,10 @@ enum {
 enum {
   VK_DECODE_DEFAULT = 0,  /* the library's choice (currently VK_DECODE_MFMA)                      */
   VK_DECODE_VALU = 1,     /* vector ALU: v_dot2_f32_f16 over unpacked codes, query rows in LDS     */
-  VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores, 16x16x16 f16 P*V, codes unpacked
-                             to f16 in registers, query rows resident as the B operand             */
+  VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores and P*V, pages staged in LDS by
+                             buffer-to-LDS copies, codes unpacked to f16 in registers, query rows
+                             resident as the B operand; fp8 / fp16 pages in one extra block per
+                             (sequence, KV head) that writes its own partial state             */
 };
 
 typedef struct vk_cache vk_cache; /* opaque; owned by the library */
