@@ -14,14 +14,30 @@ Readings where the pages are silent:
     append's gamma); appending into a partly filled ternary page is an error.
   * "Per tensor" gamma = one gamma per (layer, sequence, K or V, append call),
     over that call's ternary-routed tokens (all heads and dimensions).
-  * Page bytes: [K tile of head 0..Hkv-1][V tile of head 0..Hkv-1]; key tiles
-    token-major, value tiles dimension-major (see ternary.v_tile); fp8 and
-    fp16 value tiles are [D][Bs] arrays, key tiles [Bs][D].
+  * Page bytes: [K tile of head 0..Hkv-1][V tile of head 0..Hkv-1]; ternary
+    key tiles token-major, ternary value tiles chunked per 16-token unit (see
+    ternary.v_tile); fp8 and fp16 value tiles are [D][Bs] arrays, key tiles
+    [Bs][D].
+
+Retiering ("Minima-KV", tiers in "Recent, Anchor and Stale"; the evaluated
+profile runs with dynamic retiering, "quality" section): recent pages leave
+the FP8 tier for the packed tier once they are out of the recent window.
+Readings where the page is silent:
+  * At length L a page p is retiered when it is in FP8, is not a sink page
+    (p >= ceil(S / Bs)) and lies wholly before the window: (p + 1) * Bs <= L - R.
+    Such a page is full.  Sink pages and pages already packed are untouched.
+  * Its source is what the page holds: x = s * v, the dequantised FP8 values
+    (the original 16-bit input is gone; no dense copy is kept).
+  * gamma is per (page, K or V): mean(|x|) over the page's Bs * Hkv * D
+    elements, as float64 rounded to float32 (the per-tensor absmean with the
+    page as the tensor).  Codes are RoundClip(x / (gamma + eps), -1, 1) with x
+    taken in float32 (exact when s is a power of two) and the float32 quotient.
+  * The page's FP8 bytes are replaced, not kept beside the packed copy.
 """
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Sequence, Tuple
+from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
 
@@ -77,6 +93,8 @@ class EncodedSequence:
     v_f16: np.ndarray
     k_hat: np.ndarray                     # [T, Hkv, D] float64 dequantised
     v_hat: np.ndarray
+    # pages converted from FP8 by retier(): page -> (gamma_K, gamma_V) of that page
+    page_gamma: Dict[int, Tuple[np.float32, np.float32]] = dataclasses.field(default_factory=dict)
 
 
 def encode_sequence(spec: CacheSpec, k_bits: np.ndarray, v_bits: np.ndarray, dtype: int,
@@ -141,6 +159,53 @@ def encode_sequence(spec: CacheSpec, k_bits: np.ndarray, v_bits: np.ndarray, dty
                 out[hat][f16] = _fp8.f16_value(c)
         length = new_len
     return EncodedSequence(length, page_format, tok_fmt, tok_call, gammas, **out)
+
+
+def retier_pages(spec: CacheSpec, enc: EncodedSequence, length: int = None) -> List[int]:
+    """Pages that retiering at ``length`` (default: the sequence's length) converts."""
+    L = enc.length if length is None else length
+    if L > enc.length:
+        raise ValueError("length beyond the sequence")
+    bs = spec.block_size
+    first = -(-spec.sink_tokens // bs)
+    if spec.recent_tokens <= 0:
+        return []
+    return [p for p, f in enumerate(enc.page_format)
+            if f == FP8E4M3 and p >= first and (p + 1) * bs <= L - spec.recent_tokens]
+
+
+def retier(spec: CacheSpec, enc: EncodedSequence, length: int = None,
+           gamma_override: Dict[int, Tuple[float, float]] = None) -> EncodedSequence:
+    """A copy of ``enc`` with every page of retier_pages(spec, enc, length) re-encoded
+    as a ternary page from its FP8 values.
+
+    gamma_override: page -> (gamma_K, gamma_V) to quantise with instead of the
+    computed one (to check codes bit-exactly against a gamma read from the device).
+    """
+    out = dataclasses.replace(
+        enc, page_format=list(enc.page_format), token_format=enc.token_format.copy(),
+        k_code=enc.k_code.copy(), v_code=enc.v_code.copy(), k_fp8=enc.k_fp8.copy(),
+        v_fp8=enc.v_fp8.copy(), k_hat=enc.k_hat.copy(), v_hat=enc.v_hat.copy(),
+        page_gamma=dict(enc.page_gamma))
+    bs = spec.block_size
+    for p in retier_pages(spec, enc, length):
+        t = slice(p * bs, (p + 1) * bs)
+        gammas = []
+        for which in ("k", "v"):
+            x = _fp8.fp8_dequantize(getattr(out, which + "_fp8")[t], spec.fp8_scale)
+            if gamma_override is not None:
+                g = np.float32(gamma_override[p][which == "v"])
+            else:
+                g = _t.absmean_gamma(x)
+            c = _t.ternary_codes(x, g, spec.eps)
+            getattr(out, which + "_code")[t] = c
+            getattr(out, which + "_hat")[t] = _t.dequantize(c, g)
+            getattr(out, which + "_fp8")[t] = 0
+            gammas.append(g)
+        out.page_format[p] = TERNARY2
+        out.token_format[t] = TERNARY2
+        out.page_gamma[p] = (gammas[0], gammas[1])
+    return out
 
 
 def page_tiles(spec: CacheSpec, enc: EncodedSequence, page: int) -> np.ndarray:
