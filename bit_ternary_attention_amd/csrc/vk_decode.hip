@@ -391,6 +391,7 @@ constexpr int kBufferWord3 = 0x00020000;
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0), the others at their maximum
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0), the others at their maximum
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }  // vmcnt(n) only
 
 __device__ __forceinline__ uint32_t h2u(h2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
@@ -955,6 +956,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       for (int k = c0; k < c_end; k += NR) {
         auto step = [&](auto GI) {
           constexpr int gi = decltype(GI)::value;
+          // The copies into slots 2 gi and 2 gi + 1 have landed: at most NR - 2 ring copies
+          // were issued after them (vector memory returns in issue order; any other load
+          // in between only makes this wait stricter).  The compiler's own wait counting does
+          // not follow buffer-to-LDS copies into every ring array, so the wait is explicit.
+          __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
           UnitRaw<NC, NV> r0, r1;
           read_unit(ring_row(integral_constant<int, 2 * gi>{}), r0);
           read_unit(ring_row(integral_constant<int, 2 * gi + 1>{}), r1);

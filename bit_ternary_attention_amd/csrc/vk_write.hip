@@ -428,8 +428,11 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, Laun
     else k_gamma_finalize<0><<<n_seg, 64, 0, s>>>(a);
     if (t) t->end(VK_KERNEL_FINALIZE, s);
   }
+  // enough one-wave blocks to keep every SIMD busy (about 16 per CU), at most one per task
   const int n_tasks = a.max_units * 2 * a.P.hkv;
-  const dim3 g2(n_tasks < 1024 ? n_tasks : 1024, a.n_layers * a.n_seqs);
+  const int gy = a.n_layers * a.n_seqs;
+  const int gx_max = gy < 16 ? 16384 / gy : 1024;
+  const dim3 g2(n_tasks < gx_max ? n_tasks : gx_max, gy);
   if (t) t->begin(VK_KERNEL_PACK, s);
   if (a.P.dim == 128) {
     if (bf) k_pack<1, 128><<<g2, 64, 0, s>>>(a);
