@@ -26,7 +26,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibili
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra",
              "-D__HIP_PLATFORM_AMD__", "-I" + INCLUDE, "-I" + CSRC, "-I" + os.path.join(ROCM, "include")]
 
-HIP_SOURCES = ["vk_write.hip", "vk_decode.hip"]
+HIP_SOURCES = ["vk_write.hip", "vk_decode.hip", "vk_retier.hip"]
 CXX_SOURCES = ["host_state.cpp", "vk_api.cpp"]
 
 

@@ -227,6 +227,61 @@ void HostState::commit_append(AppendPlan* plan) {
   (void)bs;
 }
 
+vk_status HostState::plan_retier(int32_t n_seqs, const int32_t* seq_ids, RetierPlan* plan,
+                                 std::string* err) const {
+  if (n_seqs < 1 || n_seqs > cfg_.max_seqs) {
+    *err = fmt_str("n_seqs %lld out of range [1, %lld]", n_seqs, cfg_.max_seqs);
+    return VK_ERR_ARG;
+  }
+  if (!seq_ids) { *err = "seq_ids is NULL"; return VK_ERR_ARG; }
+  std::unordered_set<int32_t> seen;
+  plan->tasks.clear();
+  plan->page_end.clear();
+  const int64_t bs = cfg_.block_size;
+  const int32_t first = static_cast<int32_t>(cdiv(cfg_.sink_tokens, bs));
+  const bool tiered = cfg_.recent_tokens > 0 && cfg_.recent_format == VK_FMT_FP8E4M3;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t s = seq_ids[i];
+    if (s < 0 || s >= cfg_.max_seqs) { *err = fmt_str("seq id %lld out of range", s); return VK_ERR_ARG; }
+    if (!seen.insert(s).second) { *err = fmt_str("seq id %lld repeated", s); return VK_ERR_ARG; }
+    const SeqState& st = seqs_[s];
+    // pages [0, end) end at or before length - R
+    const int64_t settled = static_cast<int64_t>(st.length) - cfg_.recent_tokens;
+    const int32_t end = tiered && settled > 0 ? static_cast<int32_t>(settled / bs) : st.retier_from;
+    for (int32_t p = std::max(st.retier_from, first); p < end; ++p)
+      if (entry_fmt(st.pages[p]) == VK_FMT_FP8E4M3) plan->tasks.push_back({s, p, entry_idx(st.pages[p]), 0});
+    plan->page_end.push_back(std::max(end, st.retier_from));
+  }
+  if (static_cast<int64_t>(plan->tasks.size()) > static_cast<int64_t>(free_[VK_FMT_TERNARY2].size())) {
+    *err = fmt_str("pool of ternary pages exhausted: need %lld, %lld free", static_cast<int64_t>(plan->tasks.size()),
+                   static_cast<int64_t>(free_[VK_FMT_TERNARY2].size()));
+    return VK_ERR_CAPACITY;
+  }
+  return VK_OK;
+}
+
+void HostState::commit_retier(int32_t n_seqs, const int32_t* seq_ids, RetierPlan* plan) {
+  for (RetierTask& t : plan->tasks) {
+    t.dst = free_[VK_FMT_TERNARY2].front();
+    free_[VK_FMT_TERNARY2].pop_front();
+    free_[VK_FMT_FP8E4M3].push_back(t.src);
+    seqs_[t.slot].pages[t.page] = make_entry(VK_FMT_TERNARY2, t.dst);
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    SeqState& st = seqs_[seq_ids[i]];
+    st.retier_from = plan->page_end[i];
+  }
+  if (plan->tasks.empty()) return;
+  for (int32_t i = 0; i < n_seqs; ++i) {  // rebuild the same-format runs of the changed sequences
+    SeqState& st = seqs_[seq_ids[i]];
+    st.runs.clear();
+    for (size_t p = 0; p < st.pages.size(); ++p) {
+      const int f = entry_fmt(st.pages[p]);
+      if (st.runs.empty() || st.runs.back().second != f) st.runs.emplace_back(static_cast<int32_t>(p), f);
+    }
+  }
+}
+
 vk_status HostState::check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_t window, std::string* err) const {
   if (n_seqs < 1) { *err = "n_seqs must be >= 1"; return VK_ERR_ARG; }
   if (!seq_ids) { *err = "seq_ids is NULL"; return VK_ERR_ARG; }

@@ -61,6 +61,21 @@ struct SeqState {
   int32_t length = 0;
   std::vector<int32_t> pages;                       // entries of allocated pages
   std::vector<std::pair<int32_t, int32_t>> runs;    // (first page, format) of same-format runs
+  int32_t retier_from = 0;                          // pages below were examined by a retier
+};
+
+// One page of one sequence moving from the FP8 tier to the ternary tier (all layers).
+struct RetierTask {
+  int32_t slot;   // sequence id (block-table row)
+  int32_t page;   // logical page
+  int32_t src;    // FP8 pool index (freed by the commit)
+  int32_t dst;    // ternary pool index (taken by the commit)
+};
+static_assert(sizeof(RetierTask) == 16, "device layout");
+
+struct RetierPlan {
+  std::vector<RetierTask> tasks;
+  std::vector<int32_t> page_end;   // per listed sequence: pages below are settled
 };
 
 // Attended 16-token units of a sequence: [0, a_end) and [b_begin, b_end).
@@ -100,6 +115,14 @@ class HostState {
                         std::string* err) const;
   // Takes the pages from the free lists, fills plan->entries, advances lengths.
   void commit_append(AppendPlan* plan);
+
+  // Retiering ("Minima-KV", Recent/Anchor/Stale tiers): every FP8 page of the listed
+  // sequences that is not a sink page and ends at or before length - recent_tokens.
+  // Checks ids and ternary capacity; nothing changes.
+  vk_status plan_retier(int32_t n_seqs, const int32_t* seq_ids, RetierPlan* plan, std::string* err) const;
+  // Takes ternary pages (fills tasks[].dst), returns the FP8 pages to their free list,
+  // flips the host block table.
+  void commit_retier(int32_t n_seqs, const int32_t* seq_ids, RetierPlan* plan);
 
   vk_status check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_t window, std::string* err) const;
   // Attended units of `slot` by page format (route counters).

@@ -1,6 +1,6 @@
 // C ABI of libvk.so (see include/vk.h).  Owns every device buffer; plans on
 // the host (host_state.cpp) and launches the HIP kernels (vk_write.hip,
-// vk_decode.hip) on the caller's stream.
+// vk_decode.hip, vk_retier.hip) on the caller's stream.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -385,6 +385,59 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
   if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
   c->plan_ev_used[slot] = true;
   c->stats.append_calls += 1;
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API vk_status vk_retier(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, int64_t* n_pages, void* stream) {
+  vk_status st = check_handle(c);
+  if (st) return st;
+  vk::RetierPlan plan;
+  std::string err;
+  st = c->host->plan_retier(n_seqs, seq_ids, &plan, &err);
+  if (st) return fail(st, "%s", err.c_str());
+  const int64_t n_tasks = static_cast<int64_t>(plan.tasks.size());
+  if (n_tasks > 0) {
+    st = set_device(c);
+    if (st) return st;
+  }
+  // from here on the host state changes: any failure poisons the handle
+  c->host->commit_retier(n_seqs, seq_ids, &plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t per_launch = c->plan_bytes / static_cast<int64_t>(sizeof(vk::RetierTask));
+  for (int64_t first = 0; first < n_tasks; first += per_launch) {
+    const int64_t cnt = std::min(per_launch, n_tasks - first);
+    const int slot = c->ring_next;
+    c->ring_next = (c->ring_next + 1) % kRing;
+    hipError_t e = hipSuccess;
+    if (c->plan_ev_used[slot]) {
+      e = hipEventSynchronize(c->plan_ev[slot]);
+      if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
+    }
+    const size_t bytes = static_cast<size_t>(cnt) * sizeof(vk::RetierTask);
+    std::memcpy(c->plan_host[slot], plan.tasks.data() + first, bytes);
+    e = hipMemcpyAsync(c->plan_dev[slot], c->plan_host[slot], bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync");
+    vk::RetierArgs a{};
+    a.P = c->pools;
+    a.tasks = reinterpret_cast<const vk::RetierTask*>(c->plan_dev[slot]);
+    a.n_tasks = static_cast<int32_t>(cnt);
+    a.eps = c->cfg.eps;
+    if (c->timer.on) {
+      // reads every FP8 page once, writes the ternary page and its two gammas
+      const double per_page = static_cast<double>(vk::page_bytes(c->cfg, VK_FMT_FP8E4M3)) +
+                              static_cast<double>(vk::page_bytes(c->cfg, VK_FMT_TERNARY2)) + 8.0;
+      c->timer.add_bytes(VK_KERNEL_RETIER, static_cast<double>(cnt) * c->cfg.n_layers * per_page);
+    }
+    e = vk::launch_retier(a, s, c->timer.on ? &c->timer : nullptr);
+    if (e != hipSuccess) return hip_fail(c, e, "retier kernel");
+    e = hipEventRecord(c->plan_ev[slot], s);
+    if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");
+    c->plan_ev_used[slot] = true;
+  }
+  c->stats.retier_calls += 1;
+  c->stats.pages_retiered += n_tasks;
+  if (n_pages) *n_pages = n_tasks;
   g_error.clear();
   return VK_OK;
 }

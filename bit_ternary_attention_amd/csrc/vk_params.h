@@ -8,6 +8,7 @@
 namespace vk {
 
 struct AppendSeqDesc;  // host_state.h
+struct RetierTask;     // host_state.h
 
 // Device view of the paged pools.  Page `idx` of format f in layer `layer`:
 //   pool[f] + (layer * cap[f] + idx) * page_bytes[f]
@@ -98,6 +99,13 @@ struct QuantArgs {
   float eps;
 };
 
+struct RetierArgs {
+  PoolsView P;
+  const RetierTask* tasks;  // [n_tasks]
+  int32_t n_tasks;
+  float eps;
+};
+
 // Optional per-launch timing: launchers bracket each kernel with begin/end
 // (kind = VK_KERNEL_* of vk.h).  nullptr = no timing.
 class LaunchTimer {
@@ -107,9 +115,10 @@ class LaunchTimer {
   virtual void end(int kind, hipStream_t s) = 0;
 };
 
-// Launchers (vk_write.hip, vk_decode.hip).  Return the first HIP error.
+// Launchers (vk_write.hip, vk_decode.hip, vk_retier.hip).  Return the first HIP error.
 hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, LaunchTimer* t);
 hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_retier(const RetierArgs& a, hipStream_t s, LaunchTimer* t);
 
 }  // namespace vk

@@ -21,7 +21,7 @@ import sys
 
 # kernel kinds as the library's timing hooks name them
 KINDS = {"k_absmean_partial": "absmean", "k_gamma_finalize": "finalize", "k_pack": "pack",
-         "k_decode_mfma": "decode", "k_decode<": "decode", "k_merge": "merge"}
+         "k_decode_mfma": "decode", "k_decode<": "decode", "k_merge": "merge", "k_retier": "retier"}
 
 
 def trace(db_path: str, name_filter: str = "vk::"):

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libvk.so")
 OK, ERR_ARG, ERR_OOM, ERR_CAPACITY, ERR_ALIGN, ERR_STATE, ERR_HIP = range(7)
 DTYPE_F16, DTYPE_BF16 = 0, 1
 FMT_TERNARY2, FMT_FP8E4M3, FMT_F16 = 0, 1, 2
-KERNELS = ("absmean", "finalize", "pack", "decode", "merge")
+KERNELS = ("absmean", "finalize", "pack", "decode", "merge", "retier")
 DECODE_DEFAULT, DECODE_VALU, DECODE_MFMA = 0, 1, 2
 
 _c_i32, _c_i64, _c_f32, _c_u64, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64, ctypes.c_void_p
@@ -36,7 +36,8 @@ class Stats(ctypes.Structure):
     _fields_ = [("device_bytes", _c_i64), ("pool_pages", _c_i64 * 3), ("pages_used", _c_i64 * 3),
                 ("tokens_stored", _c_i64 * 3), ("append_calls", _c_i64), ("decode_calls", _c_i64),
                 ("last_decode_units", _c_i64 * 3), ("total_decode_units", _c_i64 * 3),
-                ("last_decode_splits", _c_i32), ("reserved", _c_i32)]
+                ("last_decode_splits", _c_i32), ("reserved", _c_i32), ("retier_calls", _c_i64),
+                ("pages_retiered", _c_i64)]
 
     def as_dict(self):
         out = {}
@@ -54,6 +55,7 @@ EXPORTS = {
     "vk_append": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_i32, _c_vp, _c_vp, _c_i32, _c_vp]),
     "vk_decode_attn": (_c_i32, [_c_vp, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_vp, _c_i32, _c_i32, _c_f32,
                                 _c_vp, _c_vp]),
+    "vk_retier": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64), _c_vp]),
     "vk_reset_seqs": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32), _c_vp]),
     "vk_seq_length": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32)]),
     "vk_read_pages": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, ctypes.POINTER(_c_i32),
@@ -183,6 +185,13 @@ class Cache:
         _check(lib().vk_decode_attn(self.handle, layer, n, ids, ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
                                     window, softmax_scale, ctypes.c_void_p(out.data_ptr()), _stream(stream)))
         return out
+
+    def retier(self, seq_ids: Sequence[int], stream=None) -> int:
+        """Moves the FP8 pages that left the recent window to the ternary tier; returns their count."""
+        ids, n = _ids(seq_ids)
+        out = ctypes.c_int64()
+        _check(lib().vk_retier(self.handle, n, ids, ctypes.byref(out), _stream(stream)))
+        return out.value
 
     def reset(self, seq_ids: Sequence[int], stream=None) -> None:
         ids, n = _ids(seq_ids)

@@ -136,8 +136,12 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out);
  * float32 (Show HN: Vantage-V-AI, core architecture); each element becomes
  * RoundClip(x / (gamma + eps), -1, 1) (ties to even), stored as code+1 in 2
  * bits.  Key tiles are token-major ([block][head_dim/4] bytes, element 4j+i at
- * bits 2i of byte j); value tiles are dimension-major (per head dimension, one
- * little-endian 32-bit word per 16 tokens, token t at bits 2*(t/2)+16*(t%2)).
+ * bits 2i of byte j); value tiles are stored per 16-token unit, 64 chunks of
+ * head_dim/16 bytes each, chunk 4c+g holding tokens 4g..4g+3 of the dimensions
+ * 16j+c (head_dim 128: two little-endian words, word h with token 4g+2h in its
+ * low and 4g+2h+1 in its high 16 bits, dimension 16j+c at bits 2j; head_dim 64:
+ * one word, tokens 4g, 4g+2, 4g+1, 4g+3 in bytes 0..3, dimension 16j+c at bits
+ * 2j of each byte).
  * gamma never returns to the host.
  *
  * Errors: VK_ERR_ARG (ids, sizes, pointers, dtype), VK_ERR_CAPACITY (pool
@@ -162,6 +166,32 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
 VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                 const void* q, int32_t q_dtype, int32_t window, float softmax_scale,
                                 float* out, void* stream);
+
+/*
+ * Retiering: moves pages that have left the recent window from the FP8 tier to
+ * the ternary tier ("Minima-KV", twodots.gr: section "Recent, Anchor and
+ * Stale" names the FP8 recent tier and the packed older pages; the quality
+ * section's evaluated profile retiers pages dynamically).
+ *
+ * For each listed sequence of length L, every page in VK_FMT_FP8E4M3 that is
+ * not a sink page (p >= ceil(sink_tokens / block_size)) and ends at or before
+ * L - recent_tokens is converted in every layer: x = fp8_scale * v (its
+ * dequantised values); gamma = mean(|x|) over the page's block_size *
+ * n_kv_heads * head_dim keys (and separately values), float32 of the exact
+ * mean; codes RoundClip(x / (gamma + eps), -1, 1) with x in float32, packed
+ * as vk_append packs them.  The page takes a ternary pool page, its FP8 page
+ * returns to the FP8 free list, and its block-table entry is flipped on the
+ * device.  Nothing happens when recent_tokens == 0 or recent_format is not
+ * FP8.  Pages already examined are not looked at again, so calling it after
+ * every append costs only the new pages.
+ *
+ * seq_ids: host, n_seqs distinct ids.  *n_pages (host, may be NULL) receives
+ * the number of pages converted.  Call on the stream the cache's appends and
+ * decodes use: the freed FP8 pages are handed out again by later appends.
+ * Errors: VK_ERR_ARG (ids), VK_ERR_CAPACITY (not enough free ternary pages;
+ * nothing changes).
+ */
+VK_API vk_status vk_retier(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, int64_t* n_pages, void* stream);
 
 /* Frees every page of the given sequences and sets their length to 0 (host
    state only; nothing is enqueued and nothing waits).  Freed pages are handed
@@ -195,6 +225,8 @@ typedef struct vk_stats {
   int64_t total_decode_units[3];    /* route counters over the handle's life              */
   int32_t last_decode_splits;       /* split-K factor the last decode used                */
   int32_t reserved;
+  int64_t retier_calls;             /* vk_retier calls                                    */
+  int64_t pages_retiered;           /* pages moved from FP8 to ternary (each in every layer) */
 } vk_stats;
 
 VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out);
@@ -212,7 +244,8 @@ enum {
   VK_KERNEL_PACK = 2,      /* write side pass 2: quantise, pack, scatter      */
   VK_KERNEL_DECODE = 3,    /* paged decode attention (per split)              */
   VK_KERNEL_MERGE = 4,     /* split-K online-softmax merge                    */
-  VK_KERNEL_COUNT = 5
+  VK_KERNEL_RETIER = 5,    /* FP8 -> ternary page conversion (vk_retier)      */
+  VK_KERNEL_COUNT = 6
 };
 /* enable != 0 starts timing and clears the totals; 0 stops it. */
 VK_API vk_status vk_set_kernel_timing(vk_cache* c, int32_t enable);

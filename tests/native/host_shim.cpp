@@ -42,6 +42,29 @@ int hs_append(void* h, int n_seqs, const int* ids, int n_tokens, int* tern_range
   return 0;
 }
 
+// Plans and, on success, commits a retier.  Returns the status; fills up to max_tasks
+// (slot, page, src, dst) quadruples and *n_tasks.
+int hs_retier(void* h, int n_seqs, const int* ids, int* tasks, int max_tasks, int* n_tasks, char* err, int errlen) {
+  auto* s = static_cast<vk::HostState*>(h);
+  vk::RetierPlan plan;
+  std::string e;
+  const vk_status st = s->plan_retier(n_seqs, ids, &plan, &e);
+  if (st) {
+    std::strncpy(err, e.c_str(), errlen - 1);
+    err[errlen - 1] = 0;
+    return st;
+  }
+  s->commit_retier(n_seqs, ids, &plan);
+  *n_tasks = static_cast<int>(plan.tasks.size());
+  for (int i = 0; i < *n_tasks && i < max_tasks; ++i) {
+    tasks[4 * i] = plan.tasks[i].slot;
+    tasks[4 * i + 1] = plan.tasks[i].page;
+    tasks[4 * i + 2] = plan.tasks[i].src;
+    tasks[4 * i + 3] = plan.tasks[i].dst;
+  }
+  return 0;
+}
+
 int hs_length(void* h, int seq) { return static_cast<vk::HostState*>(h)->seq(seq).length; }
 int hs_n_pages(void* h, int seq) { return static_cast<int>(static_cast<vk::HostState*>(h)->seq(seq).pages.size()); }
 int hs_page_entry(void* h, int seq, int page) { return static_cast<vk::HostState*>(h)->seq(seq).pages[page]; }

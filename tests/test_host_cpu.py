@@ -105,6 +105,8 @@ def hs():
     L.hs_count_units.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(ctypes.c_longlong)]
     L.hs_reset.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int)]
     L.hs_attended_units.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(ctypes.c_int)]
+    L.hs_retier.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), P(ctypes.c_int), ctypes.c_int,
+                            P(ctypes.c_int), ctypes.c_char_p, ctypes.c_int]
     L.hs_plan_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_int)]
     return L
@@ -124,6 +126,16 @@ class Host:
         err = ctypes.create_string_buffer(256)
         st = self.L.hs_append(self.h, len(ids), arr, n, rng, newp, err, 256)
         return st, [(rng[2 * i], rng[2 * i + 1]) for i in range(len(ids))], list(newp), err.value.decode()
+
+    def retier(self, ids):
+        arr = (ctypes.c_int * len(ids))(*ids)
+        buf = (ctypes.c_int * 4 * 4096)()
+        n = ctypes.c_int(0)
+        err = ctypes.create_string_buffer(256)
+        st = self.L.hs_retier(self.h, len(ids), arr, ctypes.cast(buf, ctypes.POINTER(ctypes.c_int)), 4096,
+                              ctypes.byref(n), err, 256)
+        flat = list(ctypes.cast(buf, ctypes.POINTER(ctypes.c_int))[:4 * n.value])
+        return st, [tuple(flat[4 * i:4 * i + 4]) for i in range(n.value)], err.value.decode()
 
     def pages(self, s):
         return [self.L.hs_page_entry(self.h, s, p) for p in range(self.L.hs_n_pages(self.h, s))]
@@ -274,3 +286,55 @@ def test_split_plan(hs):
     for total, mx, tgt, cap, mn in [(1, 1, 2048, 64, 32), (10**7, 12345, 2048, 64, 32), (500, 7, 4096, 3, 4)]:
         n, ups = _plan(hs, total, mx, tgt, cap, mn)
         assert 1 <= n <= cap and n * ups >= mx and (n - 1) * ups < mx
+
+
+@pytest.mark.parametrize("bs,S,sinkf,R", [(16, 4, 2, 256), (16, 4, 1, 16), (32, 40, 2, 33), (64, 0, 0, 100)])
+def test_retier_plan_matches_oracle(hs, bs, S, sinkf, R):
+    """Pages the host converts (and the free lists afterwards) against the oracle's rule,
+    with retiering after random appends; pages already examined are not planned again."""
+    cfg = base_cfg(block_size=bs, sink_tokens=S, sink_format=sinkf, recent_tokens=R, recent_format=1,
+                   max_tokens_per_seq=4096, pages_ternary=4000, pages_fp8=4000, pages_f16=4000, max_seqs=2)
+    h = Host(hs, cfg)
+    spec = spec_of(cfg)
+    rng = np.random.default_rng(bs + S + R)
+    calls, length = [], 0
+    bits = np.zeros((4096, 1, 4), dtype=np.uint16)
+    converted = set()
+    while length < 3500:
+        n = int(rng.integers(1, 300))
+        if length % bs and oc.new_page_format(spec, length // bs, length) == oc.TERNARY2:
+            n = bs - length % bs
+        assert h.append([1], n)[0] == 0
+        calls.append((length, n))
+        length += n
+        free_before = h.free()
+        enc = oc.encode_sequence(spec, bits[:length], bits[:length], 0, calls)
+        want = [p for p in oc.retier_pages(spec, enc) if p not in converted]
+        st, tasks, err = h.retier([1])
+        assert st == 0, err
+        assert [t[1] for t in tasks] == want and all(t[0] == 1 for t in tasks)
+        converted |= set(want)
+        pages = h.pages(1)
+        for slot, page, src, dst in tasks:
+            assert pages[page] == dst                    # format 0, pool index dst
+        assert h.free() == [free_before[0] - len(tasks), free_before[1] + len(tasks), free_before[2]]
+        fmts = [e >> 30 & 3 for e in pages]
+        want_fmts = [oc.TERNARY2 if p in converted else f for p, f in enumerate(enc.page_format)]
+        assert fmts == want_fmts
+        assert h.retier([1])[1] == []                    # nothing left to do
+    assert converted
+
+
+def test_retier_capacity_and_argument_errors(hs):
+    cfg = base_cfg(pages_ternary=3, pages_fp8=40, pages_f16=5, sink_format=2, recent_tokens=16,
+                   max_tokens_per_seq=1024)
+    h = Host(hs, cfg)
+    for _ in range(40):                                   # 16 tokens at a time: all fp8 but page 0
+        assert h.append([0], 16)[0] == 0
+    before = (h.pages(0), h.free())
+    st, tasks, err = h.retier([0])
+    assert st == vk.ERR_CAPACITY and "ternary" in err     # 38 pages to convert, 3 free
+    assert (h.pages(0), h.free()) == before
+    assert h.retier([0, 0])[0] == vk.ERR_ARG
+    assert h.retier([9])[0] == vk.ERR_ARG
+    assert h.retier([1]) == (0, [], "")                   # empty sequence: nothing to do
