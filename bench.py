@@ -197,10 +197,73 @@ def main():
                      "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": dk["avg_us"]},
     }
 
+    if w.recent_tokens > 0 and w.recent_format == vk.FMT_FP8E4M3:
+        cache.close()
+        result["retier"] = retier_leg(w, args.steps, args.warmup)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_sample_layers)
     print(json.dumps(result), flush=True)
     cache.close()
+
+
+def retier_leg(w, steps, warmup):
+    """FP8 -> ternary retiering on the workload's shape: every sequence gets R tokens (all
+    in FP8 pages but the sink page), then R more, so the first R tokens' pages leave the
+    recent window; one vk_retier call over all sequences converts them.  Only that call
+    is timed (HIP events around its kernel)."""
+    import torch
+
+    from bit_ternary_attention_amd import vk
+
+    R, bs = w.recent_tokens, w.block_size
+    ids = list(range(w.n_seqs))
+    n_sink = -(-w.sink_tokens // bs)
+    cfg = vk.make_config(n_layers=w.n_layers, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
+                         head_dim=w.head_dim, block_size=bs, max_seqs=w.n_seqs, max_tokens_per_seq=2 * R,
+                         sink_tokens=w.sink_tokens, sink_format=w.sink_format, recent_tokens=R,
+                         recent_format=vk.FMT_FP8E4M3)
+    per_seq = -(-2 * R // bs)
+    cfg.pages_ternary = per_seq * w.n_seqs
+    cfg.pages_fp8 = per_seq * w.n_seqs
+    cfg.pages_f16 = n_sink * w.n_seqs
+    cache = vk.Cache(cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5000 + w.number)
+    shape = (w.n_layers, w.n_seqs, R, w.n_kv_heads, w.head_dim)
+    kv = [torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4)]
+    converted = []
+
+    def one(timed):
+        cache.reset(ids)
+        cache.append(kv[0], kv[1], ids)
+        cache.append(kv[2], kv[3], ids)
+        if timed:
+            cache.kernel_timing(True)
+        converted.append(cache.retier(ids))
+        if timed:
+            launches, ms, by = cache.kernel_times()["retier"]
+            cache.kernel_timing(False)
+            return launches, ms, by
+        return None
+
+    for _ in range(warmup):
+        one(False)
+    tot = [0, 0.0, 0.0]
+    for _ in range(steps):
+        la, ms, by = one(True)
+        tot[0] += la
+        tot[1] += ms
+        tot[2] += by
+    torch.cuda.synchronize()
+    cache.close()
+    gbps = tot[2] / (tot[1] * 1e-3) / 1e9
+    return {"kernel": "retier", "pages_per_call": converted[-1], "layers": w.n_layers,
+            "launches": tot[0], "avg_us": round(tot[1] * 1e3 / tot[0], 3),
+            "bytes_per_launch": tot[2] / tot[0], "GBps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "config": f"{w.n_seqs} seqs x {w.n_kv_heads} KV heads x head_dim {w.head_dim}, block {bs}: "
+                      f"{R} + {R} tokens appended, pages {n_sink}..{R // bs - 1} of every sequence retiered"}
 
 
 def measured_traffic(kind, workload_name):

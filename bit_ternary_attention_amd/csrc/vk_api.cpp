@@ -32,6 +32,7 @@ vk_status fail(vk_status s, const char* fmt, ...) {
 }
 
 constexpr int kRing = 4;                 // append plan staging slots
+constexpr int64_t kRetierTasksPerLaunch = 65536;  // pages one retier launch converts, at most
 constexpr int64_t kMaxPartials = 1 << 20;  // float64 absmean partials per append call
 constexpr int64_t kMaxSegs = 65535;        // (layer, seq, K|V) segments per append call (grid y)
 constexpr int kDecodeTargetGroups = 4096;  // work groups a decode launch aims for
@@ -145,7 +146,11 @@ int64_t partial_count(const vk_cache_config& cfg) {
 
 int64_t plan_bytes_for(const vk_cache_config& cfg) {
   const int64_t max_pages = (cfg.max_tokens_per_seq + cfg.block_size - 1) / cfg.block_size;
-  const int64_t b = static_cast<int64_t>(cfg.max_seqs) * (sizeof(vk::AppendSeqDesc) + 4 * (max_pages + 1));
+  const int64_t append = static_cast<int64_t>(cfg.max_seqs) * (sizeof(vk::AppendSeqDesc) + 4 * (max_pages + 1));
+  // a retier of every page of every sequence in one launch, up to kRetierTasksPerLaunch
+  const int64_t retier = std::min<int64_t>(static_cast<int64_t>(cfg.max_seqs) * max_pages, kRetierTasksPerLaunch) *
+                         static_cast<int64_t>(sizeof(vk::RetierTask));
+  const int64_t b = std::max(append, retier);
   return (b + 255) & ~int64_t(255);
 }
 

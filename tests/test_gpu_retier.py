@@ -213,3 +213,40 @@ def test_retier_capacity_error_leaves_cache_unchanged():
     assert fmt.tolist() == enc.page_format        # nothing flipped
     err = check_decode(cache, st, {0: enc}, 0, -1, S)
     say(f"capacity error: decode still matches, max abs err {err:.3e}")
+
+
+def test_retier_every_fp8_code_exact_gamma():
+    """Pages holding every finite e4m3fn value (through the FP8 route, exactly) in three mixes;
+    with fp8_scale 1 the page sum is exact on both sides, so gamma must match bit for bit."""
+    from oracle import fp8 as of
+    hkv, dim, bs = 2, 128, 16
+    vals = of.E4M3_POS[:127]                                   # 0 .. 448, every magnitude
+    rng = np.random.default_rng(3)
+    mixes = [np.concatenate([vals, -vals]),                    # everything, both signs
+             np.concatenate([vals[:40], -vals[:40]]),          # subnormals and small normals
+             np.concatenate([vals[100:], -vals[100:], np.zeros(10)])]  # large values and zeros
+    st = Stream(1, len(mixes), hkv, 8, dim, wl.DTYPE_BF16, seed=1)
+    cache = make(st, bs, 0, wl.FMT_TERNARY2, bs, (8, 8, 2))
+    spec = spec_for(st, bs, 0, wl.FMT_TERNARY2, bs)
+    for s, mix in enumerate(mixes):
+        k = rng.choice(mix, size=(bs, hkv, dim))
+        v = rng.choice(mix, size=(bs, hkv, dim))[:, :, ::-1] * 0.5
+        for part in ((k, v), (np.ones((bs, hkv, dim)), np.ones((bs, hkv, dim)))):
+            kt = torch.tensor(np.ascontiguousarray(part[0]), dtype=torch.float32).to(torch.bfloat16)
+            vt = torch.tensor(np.ascontiguousarray(part[1]), dtype=torch.float32).to(torch.bfloat16)
+            assert np.array_equal(kt.float().numpy(), part[0]) and np.array_equal(vt.float().numpy(), part[1])
+            kb, vb = wl.to_bits(kt), wl.to_bits(vt)
+            for arr, store in ((kb, st.k[0][s]), (vb, st.v[0][s])):
+                store.append(arr)
+            st.calls[s].append((st.length[s], bs))
+            st.length[s] += bs
+            cache.append(kt[None, None].cuda().contiguous(), vt[None, None].cuda().contiguous(), [s])
+    assert cache.retier(list(range(len(mixes)))) == len(mixes)
+    torch.cuda.synchronize()
+    for s in range(len(mixes)):
+        kb, vb = st.bits(0, s)
+        ref = oc.retier(spec, oc.encode_sequence(spec, kb, vb, st.dtype, st.calls[s]))
+        buf, fmt, gam = cache.read_pages(0, s, 0, 1)
+        assert int(fmt[0]) == oc.TERNARY2
+        assert (float(gam[0, 0]), float(gam[0, 1])) == tuple(float(x) for x in ref.page_gamma[0]), s
+        assert np.array_equal(buf[0][:oc.page_bytes(spec, oc.TERNARY2)], oc.page_tiles(spec, ref, 0)), s
