@@ -208,6 +208,25 @@ def retier(spec: CacheSpec, enc: EncodedSequence, length: int = None,
     return out
 
 
+def evict_pages(spec: CacheSpec, length: int, window: int) -> List[int]:
+    """Pages bounded-memory eviction frees at length L for window W (sorted).
+
+    "Show HN: Vantage-V-AI", quick start (max_active_tokens bounds the active
+    window, sink_tokens are kept) and core architecture (bounded-memory
+    streaming cache with attention-sink retention).  Reading: a page is freed
+    when it is not a sink page (p >= ceil(S / Bs)) and holds no token of the
+    window, i.e. it ends at or before L - W: (p + 1) * Bs <= L - W.  Its tokens
+    are gone for good; a later decode may only attend windows W' <= W (measured
+    from a length >= L).  W = -1 (the whole context) frees nothing.
+    """
+    if window < 0:
+        return []
+    bs = spec.block_size
+    first = -(-spec.sink_tokens // bs)
+    last = (length - window) // bs if length > window else 0   # pages [first, last) end by L - W
+    return list(range(first, max(first, last)))
+
+
 def page_tiles(spec: CacheSpec, enc: EncodedSequence, page: int) -> np.ndarray:
     """Expected bytes of one page ([K tiles][V tiles]) for a page filled to the end.
 
