@@ -249,7 +249,8 @@ vk_status HostState::plan_retier(int32_t n_seqs, const int32_t* seq_ids, RetierP
     const int64_t settled = static_cast<int64_t>(st.length) - cfg_.recent_tokens;
     const int32_t end = tiered && settled > 0 ? static_cast<int32_t>(settled / bs) : st.retier_from;
     for (int32_t p = std::max(st.retier_from, first); p < end; ++p)
-      if (entry_fmt(st.pages[p]) == VK_FMT_FP8E4M3) plan->tasks.push_back({s, p, entry_idx(st.pages[p]), 0});
+      if (st.pages[p] != kNoPage && entry_fmt(st.pages[p]) == VK_FMT_FP8E4M3)
+        plan->tasks.push_back({s, p, entry_idx(st.pages[p]), 0});
     plan->page_end.push_back(std::max(end, st.retier_from));
   }
   if (static_cast<int64_t>(plan->tasks.size()) > static_cast<int64_t>(free_[VK_FMT_TERNARY2].size())) {
@@ -276,10 +277,52 @@ void HostState::commit_retier(int32_t n_seqs, const int32_t* seq_ids, RetierPlan
     SeqState& st = seqs_[seq_ids[i]];
     st.runs.clear();
     for (size_t p = 0; p < st.pages.size(); ++p) {
-      const int f = entry_fmt(st.pages[p]);
+      const int f = st.pages[p] == kNoPage ? kFormats : entry_fmt(st.pages[p]);
       if (st.runs.empty() || st.runs.back().second != f) st.runs.emplace_back(static_cast<int32_t>(p), f);
     }
   }
+}
+
+vk_status HostState::evict(int32_t n_seqs, const int32_t* seq_ids, int32_t window, int64_t* n_pages,
+                           std::string* err) {
+  if (n_seqs < 1 || n_seqs > cfg_.max_seqs) {
+    *err = fmt_str("n_seqs %lld out of range [1, %lld]", n_seqs, cfg_.max_seqs);
+    return VK_ERR_ARG;
+  }
+  if (!seq_ids) { *err = "seq_ids is NULL"; return VK_ERR_ARG; }
+  if (window < -1) { *err = "window must be >= -1"; return VK_ERR_ARG; }
+  std::unordered_set<int32_t> seen;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t s = seq_ids[i];
+    if (s < 0 || s >= cfg_.max_seqs) { *err = fmt_str("seq id %lld out of range", s); return VK_ERR_ARG; }
+    if (!seen.insert(s).second) { *err = fmt_str("seq id %lld repeated", s); return VK_ERR_ARG; }
+  }
+  int64_t freed = 0;
+  if (window >= 0) {
+    const int64_t bs = cfg_.block_size;
+    const int32_t first = static_cast<int32_t>(cdiv(cfg_.sink_tokens, bs));
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      SeqState& st = seqs_[seq_ids[i]];
+      const int64_t edge = static_cast<int64_t>(st.length) - window;  // pages ending by here go
+      const int32_t last = edge > 0 ? static_cast<int32_t>(edge / bs) : 0;
+      const int32_t from = std::max(st.evict_end, first);
+      if (last <= from) continue;
+      for (int32_t p = from; p < last; ++p) {
+        const int32_t e = st.pages[p];
+        free_[entry_fmt(e)].push_back(entry_idx(e));
+        st.pages[p] = kNoPage;
+        ++freed;
+      }
+      st.evict_end = last;
+      st.runs.clear();
+      for (size_t p = 0; p < st.pages.size(); ++p) {
+        const int f = st.pages[p] == kNoPage ? kFormats : entry_fmt(st.pages[p]);
+        if (st.runs.empty() || st.runs.back().second != f) st.runs.emplace_back(static_cast<int32_t>(p), f);
+      }
+    }
+  }
+  if (n_pages) *n_pages = freed;
+  return VK_OK;
 }
 
 vk_status HostState::check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_t window, std::string* err) const {
@@ -289,7 +332,14 @@ vk_status HostState::check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t s = seq_ids[i];
     if (s < 0 || s >= cfg_.max_seqs) { *err = fmt_str("seq id %lld out of range", s); return VK_ERR_ARG; }
-    if (seqs_[s].length < 1) { *err = fmt_str("seq %lld is empty", s); return VK_ERR_ARG; }
+    const SeqState& st = seqs_[s];
+    if (st.length < 1) { *err = fmt_str("seq %lld is empty", s); return VK_ERR_ARG; }
+    // tokens [sink pages * Bs, evict_end * Bs) are gone: the window must start at or after them
+    const int64_t gone_end = static_cast<int64_t>(st.evict_end) * cfg_.block_size;
+    if (gone_end > 0 && (window < 0 || static_cast<int64_t>(st.length) - window < gone_end)) {
+      *err = fmt_str("seq %lld: the window reaches tokens freed by eviction (below %lld)", s, gone_end);
+      return VK_ERR_ARG;
+    }
   }
   return VK_OK;
 }
@@ -305,7 +355,7 @@ void HostState::count_units(int32_t slot, int32_t window, int64_t out[kFormats])
     const int64_t u0 = p0 * upp, u1 = p1 * upp;
     int64_t n = std::max<int64_t>(0, std::min<int64_t>(u1, r.a_end) - u0);
     n += std::max<int64_t>(0, std::min<int64_t>(u1, r.b_end) - std::max<int64_t>(u0, r.b_begin));
-    out[st.runs[k].second] += n;
+    if (st.runs[k].second < kFormats) out[st.runs[k].second] += n;  // freed pages are never attended
   }
 }
 
@@ -318,7 +368,8 @@ vk_status HostState::reset_seqs(int32_t n_seqs, const int32_t* seq_ids, std::str
   }
   for (int32_t i = 0; i < n_seqs; ++i) {
     SeqState& st = seqs_[seq_ids[i]];
-    for (int32_t e : st.pages) free_[entry_fmt(e)].push_back(entry_idx(e));
+    for (int32_t e : st.pages)
+      if (e != kNoPage) free_[entry_fmt(e)].push_back(entry_idx(e));
     st = SeqState();
   }
   return VK_OK;
@@ -334,7 +385,7 @@ int64_t HostState::tokens_stored(int fmt) const {
   const int64_t bs = cfg_.block_size;
   for (const SeqState& st : seqs_) {
     for (size_t p = 0; p < st.pages.size(); ++p) {
-      if (entry_fmt(st.pages[p]) != fmt) continue;
+      if (st.pages[p] == kNoPage || entry_fmt(st.pages[p]) != fmt) continue;
       n += std::min<int64_t>(bs, st.length - static_cast<int64_t>(p) * bs);
     }
   }

@@ -62,6 +62,7 @@ struct SeqState {
   std::vector<int32_t> pages;                       // entries of allocated pages
   std::vector<std::pair<int32_t, int32_t>> runs;    // (first page, format) of same-format runs
   int32_t retier_from = 0;                          // pages below were examined by a retier
+  int32_t evict_end = 0;                            // pages [sink pages, evict_end) are freed
 };
 
 // One page of one sequence moving from the FP8 tier to the ternary tier (all layers).
@@ -123,6 +124,11 @@ class HostState {
   // Takes ternary pages (fills tasks[].dst), returns the FP8 pages to their free list,
   // flips the host block table.
   void commit_retier(int32_t n_seqs, const int32_t* seq_ids, RetierPlan* plan);
+
+  // Bounded-memory eviction ("Show HN: Vantage-V-AI": max_active_tokens with sink
+  // tokens kept): frees every page of the listed sequences past the sink pages that ends
+  // at or before length - window; their entries become kNoPage.  Returns the page count.
+  vk_status evict(int32_t n_seqs, const int32_t* seq_ids, int32_t window, int64_t* n_pages, std::string* err);
 
   vk_status check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_t window, std::string* err) const;
   // Attended units of `slot` by page format (route counters).

@@ -447,6 +447,21 @@ VK_API vk_status vk_retier(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, 
   return VK_OK;
 }
 
+VK_API vk_status vk_evict(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, int32_t window, int64_t* n_pages,
+                          void* stream) {
+  (void)stream;  // host state only: the freed pages are reused by later appends in stream order
+  vk_status st = check_handle(c);
+  if (st) return st;
+  std::string err;
+  int64_t freed = 0;
+  st = c->host->evict(n_seqs, seq_ids, window, &freed, &err);
+  if (st) return fail(st, "%s", err.c_str());
+  c->stats.pages_evicted += freed;
+  if (n_pages) *n_pages = freed;
+  g_error.clear();
+  return VK_OK;
+}
+
 VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids, const void* q,
                                 int32_t q_dtype, int32_t window, float softmax_scale, float* out, void* stream) {
   vk_status st = check_handle(c);
@@ -590,6 +605,12 @@ VK_API vk_status vk_read_pages(vk_cache* c, int32_t layer, int32_t seq, int32_t 
   const int64_t stride = vk::page_bytes(cfg, VK_FMT_F16);
   for (int32_t j = 0; j < n_pages; ++j) {
     const int32_t ent = ss.pages[page0 + j];
+    if (ent == vk::kNoPage) {  // freed by eviction
+      std::memset(host_bytes + j * stride, 0, static_cast<size_t>(stride));
+      host_fmt[j] = -1;
+      host_gamma[2 * j] = host_gamma[2 * j + 1] = std::nanf("");
+      continue;
+    }
     const int f = vk::entry_fmt(ent);
     const int64_t idx = vk::entry_idx(ent);
     const uint8_t* src = c->pools.pool[f] + (static_cast<int64_t>(layer) * c->pools.cap[f] + idx) * c->pools.page_bytes[f];

@@ -37,7 +37,7 @@ class Stats(ctypes.Structure):
                 ("tokens_stored", _c_i64 * 3), ("append_calls", _c_i64), ("decode_calls", _c_i64),
                 ("last_decode_units", _c_i64 * 3), ("total_decode_units", _c_i64 * 3),
                 ("last_decode_splits", _c_i32), ("reserved", _c_i32), ("retier_calls", _c_i64),
-                ("pages_retiered", _c_i64)]
+                ("pages_retiered", _c_i64), ("pages_evicted", _c_i64)]
 
     def as_dict(self):
         out = {}
@@ -56,6 +56,7 @@ EXPORTS = {
     "vk_decode_attn": (_c_i32, [_c_vp, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_vp, _c_i32, _c_i32, _c_f32,
                                 _c_vp, _c_vp]),
     "vk_retier": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64), _c_vp]),
+    "vk_evict": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32), _c_i32, ctypes.POINTER(_c_i64), _c_vp]),
     "vk_reset_seqs": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32), _c_vp]),
     "vk_seq_length": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32)]),
     "vk_read_pages": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp, ctypes.POINTER(_c_i32),
@@ -191,6 +192,13 @@ class Cache:
         ids, n = _ids(seq_ids)
         out = ctypes.c_int64()
         _check(lib().vk_retier(self.handle, n, ids, ctypes.byref(out), _stream(stream)))
+        return out.value
+
+    def evict(self, seq_ids: Sequence[int], window: int, stream=None) -> int:
+        """Frees the pages between the sinks and the last ``window`` tokens; returns their count."""
+        ids, n = _ids(seq_ids)
+        out = ctypes.c_int64()
+        _check(lib().vk_evict(self.handle, n, ids, window, ctypes.byref(out), _stream(stream)))
         return out.value
 
     def reset(self, seq_ids: Sequence[int], stream=None) -> None:

@@ -193,6 +193,29 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
  */
 VK_API vk_status vk_retier(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, int64_t* n_pages, void* stream);
 
+/*
+ * Bounded-memory eviction ("Show HN: Vantage-V-AI", quick start: max_active_tokens
+ * bounds the active attention window while sink_tokens are kept; core
+ * architecture: a bounded-memory streaming cache with attention-sink retention).
+ *
+ * For each listed sequence of length L, frees every page past the sink pages
+ * (p >= ceil(sink_tokens / block_size)) that ends at or before L - window, in
+ * every layer: the tokens between the sinks and the window.  The pages return
+ * to their free lists and are handed out again by later appends; calling it
+ * after every append keeps a sequence within ceil(sink_tokens / block_size) +
+ * ceil(window / block_size) + 1 pages.  Freed tokens are gone: a later
+ * vk_decode_attn of the sequence fails with VK_ERR_ARG unless its window starts
+ * at or after them (window >= 0 and L' - window' >= the end of the freed pages),
+ * and vk_read_pages reports such pages with format -1.  window = -1 frees
+ * nothing.  Host state only: nothing is enqueued and nothing waits; `stream`
+ * names the stream of the cache's appends (see vk_reset_seqs for the ordering).
+ *
+ * seq_ids: host, n_seqs distinct ids.  *n_pages (host, may be NULL) receives
+ * the number of pages freed per layer.  Errors: VK_ERR_ARG (ids, window < -1).
+ */
+VK_API vk_status vk_evict(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, int32_t window, int64_t* n_pages,
+                          void* stream);
+
 /* Frees every page of the given sequences and sets their length to 0 (host
    state only; nothing is enqueued and nothing waits).  Freed pages are handed
    out again by later vk_append calls; work already enqueued that reads them
@@ -206,7 +229,8 @@ VK_API vk_status vk_seq_length(vk_cache* c, int32_t seq, int32_t* length);
 
 /*
  * Introspection, synchronous (waits for the device): copies pages
- * [page0, page0+n_pages) of (layer, seq) to host.  Page j lands at
+ * [page0, page0+n_pages) of (layer, seq) to host (a page freed by vk_evict
+ * reads as zeros with format -1).  Page j lands at
  * host_bytes + j * vk_page_bytes(cfg, VK_FMT_F16) (the largest page), laid out
  * [K tile head 0..Hkv-1][V tile head 0..Hkv-1] in its own format.
  * host_fmt[j] receives the format; host_gamma[2j], [2j+1] the K and V gamma
@@ -227,6 +251,7 @@ typedef struct vk_stats {
   int32_t reserved;
   int64_t retier_calls;             /* vk_retier calls                                    */
   int64_t pages_retiered;           /* pages moved from FP8 to ternary (each in every layer) */
+  int64_t pages_evicted;            /* pages freed by vk_evict                            */
 } vk_stats;
 
 VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out);

@@ -65,6 +65,19 @@ int hs_retier(void* h, int n_seqs, const int* ids, int* tasks, int max_tasks, in
   return 0;
 }
 
+int hs_evict(void* h, int n_seqs, const int* ids, int window, long long* n_pages) {
+  std::string e;
+  int64_t n = 0;
+  const int st = static_cast<vk::HostState*>(h)->evict(n_seqs, ids, window, &n, &e);
+  *n_pages = n;
+  return st;
+}
+
+int hs_check_decode(void* h, int n_seqs, const int* ids, int window) {
+  std::string e;
+  return static_cast<vk::HostState*>(h)->check_decode(n_seqs, ids, window, &e);
+}
+
 int hs_length(void* h, int seq) { return static_cast<vk::HostState*>(h)->seq(seq).length; }
 int hs_n_pages(void* h, int seq) { return static_cast<int>(static_cast<vk::HostState*>(h)->seq(seq).pages.size()); }
 int hs_page_entry(void* h, int seq, int page) { return static_cast<vk::HostState*>(h)->seq(seq).pages[page]; }

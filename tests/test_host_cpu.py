@@ -107,6 +107,8 @@ def hs():
     L.hs_attended_units.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(ctypes.c_int)]
     L.hs_retier.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), P(ctypes.c_int), ctypes.c_int,
                             P(ctypes.c_int), ctypes.c_char_p, ctypes.c_int]
+    L.hs_evict.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), ctypes.c_int, P(ctypes.c_longlong)]
+    L.hs_check_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), ctypes.c_int]
     L.hs_plan_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_int)]
     return L
@@ -136,6 +138,16 @@ class Host:
                               ctypes.byref(n), err, 256)
         flat = list(ctypes.cast(buf, ctypes.POINTER(ctypes.c_int))[:4 * n.value])
         return st, [tuple(flat[4 * i:4 * i + 4]) for i in range(n.value)], err.value.decode()
+
+    def evict(self, ids, window):
+        arr = (ctypes.c_int * len(ids))(*ids)
+        n = ctypes.c_longlong(0)
+        st = self.L.hs_evict(self.h, len(ids), arr, window, ctypes.byref(n))
+        return st, n.value
+
+    def check_decode(self, ids, window):
+        arr = (ctypes.c_int * len(ids))(*ids)
+        return self.L.hs_check_decode(self.h, len(ids), arr, window)
 
     def pages(self, s):
         return [self.L.hs_page_entry(self.h, s, p) for p in range(self.L.hs_n_pages(self.h, s))]
@@ -338,3 +350,64 @@ def test_retier_capacity_and_argument_errors(hs):
     assert h.retier([0, 0])[0] == vk.ERR_ARG
     assert h.retier([9])[0] == vk.ERR_ARG
     assert h.retier([1]) == (0, [], "")                   # empty sequence: nothing to do
+
+
+@pytest.mark.parametrize("bs,S,sinkf,R,W", [(16, 4, 2, 64, 256), (16, 4, 0, 0, 100), (32, 40, 2, 33, 50),
+                                            (64, 0, 0, 100, 0), (16, 20, 1, 16, 16)])
+def test_eviction_matches_oracle_and_bounds_memory(hs, bs, S, sinkf, R, W):
+    """Streaming appends with eviction (and retiering) after each: freed pages match the oracle's
+    rule, memory stays bounded, pools recycle, decode windows are checked against freed tokens."""
+    cfg = base_cfg(block_size=bs, sink_tokens=S, sink_format=sinkf, recent_tokens=R, recent_format=1,
+                   max_tokens_per_seq=60000, pages_ternary=400, pages_fp8=400, pages_f16=40, max_seqs=2)
+    h = Host(hs, cfg)
+    spec = spec_of(cfg)
+    rng = np.random.default_rng(bs + S + R + W)
+    length, freed_total = 0, 0
+    bound = -(-S // bs) + -(-W // bs) + 1
+    while length < 20000:                         # far more tokens than the pools could hold
+        n = int(rng.integers(1, 2 * bs + 40))
+        if R == 0:
+            n = bs * (1 + n % 3)                   # ternary pages are written whole
+        elif length < -(-S // bs) * bs and sinkf == oc.TERNARY2:
+            n = max(n, -(-S // bs) * bs - length)  # fill the ternary sink pages in one call
+        st, _, _, err = h.append([1], n)
+        assert st == 0, err
+        length += n
+        if R:
+            assert h.retier([1])[0] == 0
+        st, freed = h.evict([1], W)
+        assert st == 0
+        freed_total += freed
+        pages = h.pages(1)
+        gone = [p for p, e in enumerate(pages) if e == -1]
+        assert gone == oc.evict_pages(spec, length, W)
+        assert len(pages) - len(gone) <= bound
+        # decode: windows inside the kept tokens pass, wider ones are refused
+        if S or W:
+            assert h.check_decode([1], W) == 0
+        if gone:
+            gone_end = (gone[-1] + 1) * bs
+            assert h.check_decode([1], -1) == vk.ERR_ARG
+            for w2 in (W + 1, W + bs, W + 3 * bs):
+                want = vk.ERR_ARG if length - w2 < gone_end else 0
+                assert h.check_decode([1], w2) == want, (length, w2, gone_end)
+    assert freed_total > 0 and length > 4000
+    used = [cfg.pages_ternary - h.free()[0], cfg.pages_fp8 - h.free()[1], cfg.pages_f16 - h.free()[2]]
+    assert sum(used) == len([e for e in h.pages(1) if e != -1])
+    arr = (ctypes.c_int * 1)(1)
+    assert hs.hs_reset(h.h, 1, arr) == 0
+    assert h.free() == [cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16]
+
+
+def test_eviction_arguments(hs):
+    h = Host(hs, base_cfg(recent_tokens=0))
+    assert h.append([0], 300)[0] == 0
+    assert h.evict([0], -2)[0] == vk.ERR_ARG
+    assert h.evict([0, 0], 10)[0] == vk.ERR_ARG
+    assert h.evict([5], 10)[0] == vk.ERR_ARG
+    assert h.evict([0], -1) == (0, 0)            # the whole context: nothing to free
+    assert h.evict([0], 400) == (0, 0)           # the window covers the sequence
+    assert h.evict([0], 100) == (0, 11)          # pages 1..11 end by 200 (freed tokens 16..191)
+    assert h.evict([0], 100) == (0, 0)           # already freed
+    assert h.check_decode([0], 108) == 0         # the window starts at 192
+    assert h.check_decode([0], 109) == vk.ERR_ARG and h.check_decode([0], -1) == vk.ERR_ARG
