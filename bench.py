@@ -200,6 +200,7 @@ def main():
     if w.recent_tokens > 0 and w.recent_format == vk.FMT_FP8E4M3:
         cache.close()
         result["retier"] = retier_leg(w, args.steps, args.warmup)
+        result["stream"] = stream_leg(w, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_sample_layers)
@@ -264,6 +265,79 @@ def retier_leg(w, steps, warmup):
             "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
             "config": f"{w.n_seqs} seqs x {w.n_kv_heads} KV heads x head_dim {w.head_dim}, block {bs}: "
                       f"{R} + {R} tokens appended, pages {n_sink}..{R // bs - 1} of every sequence retiered"}
+
+
+def stream_leg(w, steps, warmup, prefill=1024, window=512):
+    """A bounded-memory serving loop on the workload's shape (its sequences, heads, head dim,
+    block size, sinks and FP8 recent tier): after a prefill, every step appends one token
+    to every sequence, evicts the pages between the sinks and the last `window` tokens
+    (max_active_tokens), retiers the FP8 pages that left the recent tier (evicting first
+    spares converting pages that are about to go), and decodes one layer with that window.  Reports steps per second, the library's device time per
+    kernel, the host time of the two page-table calls, and the pages in use (constant)."""
+    import torch
+
+    from bit_ternary_attention_amd import vk
+
+    bs = w.block_size
+    ids = list(range(w.n_seqs))
+    n_steps = warmup + steps
+    n_sink = -(-w.sink_tokens // bs)
+    per_seq = n_sink + -(-window // bs) + 2
+    cfg = vk.make_config(n_layers=1, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads, head_dim=w.head_dim,
+                         block_size=bs, max_seqs=w.n_seqs, max_tokens_per_seq=prefill + n_steps,
+                         sink_tokens=w.sink_tokens, sink_format=w.sink_format, recent_tokens=w.recent_tokens,
+                         recent_format=vk.FMT_FP8E4M3)
+    chunk = 64  # prefill chunk: retier and evict after each, as the loop does per token
+    cfg.pages_ternary = (per_seq + chunk // bs) * w.n_seqs
+    cfg.pages_fp8 = ((w.recent_tokens + chunk) // bs + 3) * w.n_seqs
+    cfg.pages_f16 = n_sink * w.n_seqs
+    cache = vk.Cache(cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6000 + w.number)
+    shape = (prefill // chunk, 2, 1, w.n_seqs, chunk, w.n_kv_heads, w.head_dim)
+    pre = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+    tok = torch.randn((n_steps, 2, 1, w.n_seqs, 1, w.n_kv_heads, w.head_dim), generator=g,
+                      device="cuda").to(torch.bfloat16)
+    q = torch.randn((n_steps, w.n_seqs, w.n_q_heads, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((w.n_seqs, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    for c in range(prefill // chunk):
+        cache.append(pre[c, 0], pre[c, 1], ids)
+        cache.evict(ids, window)
+        cache.retier(ids)
+    del pre
+    host_s = [0.0, 0.0]
+
+    def one(i):
+        cache.append(tok[i, 0], tok[i, 1], ids)
+        t = time.perf_counter()
+        cache.evict(ids, window)
+        host_s[1] += time.perf_counter() - t
+        t = time.perf_counter()
+        cache.retier(ids)
+        host_s[0] += time.perf_counter() - t
+        cache.decode(q[i], ids, 0, window=window, out=out)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    host_s[0] = host_s[1] = 0.0
+    cache.kernel_timing(True)
+    t0 = time.perf_counter()
+    for i in range(warmup, n_steps):
+        one(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = cache.kernel_times()
+    cache.kernel_timing(False)
+    st = cache.stats()
+    cache.close()
+    ms = (t1 - t0) * 1e3 / steps
+    return {"steps": steps, "seqs": w.n_seqs, "window": window, "prefill": prefill,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.n_seqs / (ms * 1e-3), 1),
+            "device_us_per_step": {k: round(v[1] * 1e3 / steps, 3) for k, v in kt.items() if v[0]},
+            "host_us_per_call": {"retier": round(host_s[0] * 1e6 / steps, 2), "evict": round(host_s[1] * 1e6 / steps, 2)},
+            "pages_in_use": st["pages_used"], "page_bound": (per_seq - 1) * w.n_seqs,
+            "pages_retiered": st["pages_retiered"], "pages_evicted": st["pages_evicted"]}
 
 
 def measured_traffic(kind, workload_name):
