@@ -17,7 +17,8 @@ Readings where the pages are silent:
   * Page bytes: [K tile of head 0..Hkv-1][V tile of head 0..Hkv-1]; ternary
     key tiles token-major, ternary value tiles chunked per 16-token unit (see
     ternary.v_tile); fp8 and fp16 value tiles are [D][Bs] arrays, key tiles
-    [Bs][D].
+    [Bs][D].  With dynamic FP8 each FP8 tile is followed by its Bs float32
+    scales in token order.
 
 Retiering ("Minima-KV", tiers in "Recent, Anchor and Stale"; the evaluated
 profile runs with dynamic retiering, "quality" section): recent pages leave
@@ -27,7 +28,8 @@ Readings where the page is silent:
     (p >= ceil(S / Bs)) and lies wholly before the window: (p + 1) * Bs <= L - R.
     Such a page is full.  Sink pages and pages already packed are untouched.
   * Its source is what the page holds: x = s * v, the dequantised FP8 values
-    (the original 16-bit input is gone; no dense copy is kept).
+    (s the cache's static scale, or the token's dynamic scale; the original
+    16-bit input is gone; no dense copy is kept).
   * gamma is per (page, K or V): mean(|x|) over the page's Bs * Hkv * D
     elements, as float64 rounded to float32 (the per-tensor absmean with the
     page as the tensor).  Codes are RoundClip(x / (gamma + eps), -1, 1) with x
@@ -64,6 +66,7 @@ class CacheSpec:
     recent_format: int = FP8E4M3
     eps: float = 1e-5
     fp8_scale: float = 1.0
+    fp8_dynamic: bool = False      # FP8 pages carry a scale per (token, KV head) (fp8.fp8_dynamic_encode)
 
 
 def new_page_format(spec: CacheSpec, page: int, new_len: int) -> int:
@@ -93,6 +96,8 @@ class EncodedSequence:
     v_f16: np.ndarray
     k_hat: np.ndarray                     # [T, Hkv, D] float64 dequantised
     v_hat: np.ndarray
+    k_fp8_scale: np.ndarray = None        # [T, Hkv] float32 dynamic FP8 scales (0 where not fp8)
+    v_fp8_scale: np.ndarray = None
     # pages converted from FP8 by retier(): page -> (gamma_K, gamma_V) of that page
     page_gamma: Dict[int, Tuple[np.float32, np.float32]] = dataclasses.field(default_factory=dict)
 
@@ -121,6 +126,8 @@ def encode_sequence(spec: CacheSpec, k_bits: np.ndarray, v_bits: np.ndarray, dty
     out = {name: np.zeros(shape, dt) for name, dt in
            (("k_code", np.int8), ("v_code", np.int8), ("k_fp8", np.uint8), ("v_fp8", np.uint8),
             ("k_f16", np.uint16), ("v_f16", np.uint16), ("k_hat", np.float64), ("v_hat", np.float64))}
+    out["k_fp8_scale"] = np.zeros(shape[:2], np.float32)
+    out["v_fp8_scale"] = np.zeros(shape[:2], np.float32)
     for ci, (t0, n) in enumerate(calls):
         if t0 != length:
             raise ValueError("appends must be contiguous")
@@ -148,9 +155,15 @@ def encode_sequence(spec: CacheSpec, k_bits: np.ndarray, v_bits: np.ndarray, dty
         f8 = np.nonzero(tok_fmt[t0:new_len] == FP8E4M3)[0] + t0
         if f8.size:
             for src, code, hat in ((kx, "k_fp8", "k_hat"), (vx, "v_fp8", "v_hat")):
-                c = _fp8.fp8_encode_input(src[f8], spec.fp8_scale)
-                out[code][f8] = c
-                out[hat][f8] = _fp8.fp8_dequantize(c, spec.fp8_scale)
+                if spec.fp8_dynamic:
+                    c, sc = _fp8.fp8_dynamic_encode(src[f8])
+                    out[code][f8] = c
+                    out[code + "_scale"][f8] = sc
+                    out[hat][f8] = _fp8.fp8_dynamic_dequantize(c, sc)
+                else:
+                    c = _fp8.fp8_encode_input(src[f8], spec.fp8_scale)
+                    out[code][f8] = c
+                    out[hat][f8] = _fp8.fp8_dequantize(c, spec.fp8_scale)
         f16 = np.nonzero(tok_fmt[t0:new_len] == F16)[0] + t0
         if f16.size:
             for bits, code, hat in ((k_bits, "k_f16", "k_hat"), (v_bits, "v_f16", "v_hat")):
@@ -186,13 +199,17 @@ def retier(spec: CacheSpec, enc: EncodedSequence, length: int = None,
         enc, page_format=list(enc.page_format), token_format=enc.token_format.copy(),
         k_code=enc.k_code.copy(), v_code=enc.v_code.copy(), k_fp8=enc.k_fp8.copy(),
         v_fp8=enc.v_fp8.copy(), k_hat=enc.k_hat.copy(), v_hat=enc.v_hat.copy(),
+        k_fp8_scale=enc.k_fp8_scale.copy(), v_fp8_scale=enc.v_fp8_scale.copy(),
         page_gamma=dict(enc.page_gamma))
     bs = spec.block_size
     for p in retier_pages(spec, enc, length):
         t = slice(p * bs, (p + 1) * bs)
         gammas = []
         for which in ("k", "v"):
-            x = _fp8.fp8_dequantize(getattr(out, which + "_fp8")[t], spec.fp8_scale)
+            if spec.fp8_dynamic:
+                x = _fp8.fp8_dynamic_dequantize(getattr(out, which + "_fp8")[t], getattr(out, which + "_fp8_scale")[t])
+            else:
+                x = _fp8.fp8_dequantize(getattr(out, which + "_fp8")[t], spec.fp8_scale)
             if gamma_override is not None:
                 g = np.float32(gamma_override[p][which == "v"])
             else:
@@ -201,6 +218,7 @@ def retier(spec: CacheSpec, enc: EncodedSequence, length: int = None,
             getattr(out, which + "_code")[t] = c
             getattr(out, which + "_hat")[t] = _t.dequantize(c, g)
             getattr(out, which + "_fp8")[t] = 0
+            getattr(out, which + "_fp8_scale")[t] = 0
             gammas.append(g)
         out.page_format[p] = TERNARY2
         out.token_format[t] = TERNARY2
@@ -247,6 +265,10 @@ def page_tiles(spec: CacheSpec, enc: EncodedSequence, page: int) -> np.ndarray:
                 c = np.zeros((bs, dim), dtype=np.uint8)
                 c[: hi - lo] = getattr(enc, which + "_fp8")[lo:hi, h]
                 parts.append((c if which == "k" else c.T.copy()).ravel())
+                if spec.fp8_dynamic:   # then the tile's Bs float32 scales, token order
+                    sc = np.zeros(bs, dtype="<f4")
+                    sc[: hi - lo] = getattr(enc, which + "_fp8_scale")[lo:hi, h]
+                    parts.append(sc.view(np.uint8))
             else:
                 c = np.zeros((bs, dim), dtype=np.uint16)
                 c[: hi - lo] = getattr(enc, which + "_f16")[lo:hi, h]
@@ -257,7 +279,8 @@ def page_tiles(spec: CacheSpec, enc: EncodedSequence, page: int) -> np.ndarray:
 def page_bytes(spec: CacheSpec, fmt: int) -> int:
     """Bytes of one page of a format (K and V, every head)."""
     per_elem = {TERNARY2: 0.25, FP8E4M3: 1, F16: 2}[fmt]
-    return int(2 * spec.n_kv_heads * spec.block_size * spec.head_dim * per_elem)
+    extra = 4 * spec.block_size if fmt == FP8E4M3 and spec.fp8_dynamic else 0   # scales per tile
+    return int(2 * spec.n_kv_heads * (spec.block_size * spec.head_dim * per_elem + extra))
 
 
 def stored_bytes(spec: CacheSpec, page_formats: Sequence[int]) -> int:

@@ -12,6 +12,12 @@ Readings where the pages are silent:
     s a static per-cache scale (1.0 by default).  Dequantised value = s * v.
   * Anchor (sink) pages are IEEE float16, rounded to nearest even from the
     input (float16 input is stored verbatim).
+  * Dynamic FP8 (the "dynamic FP8 streaming mode" of Show HN: Vantage-V-AI,
+    core architecture and benchmark table): the scale is not fixed per cache
+    but taken from the data, one per (token, KV head) for keys and one for
+    values: s = float32(amax / 448) with amax = max |x| over the head's D
+    elements (float32 division); codes e4m3fn(float32(x / s)) as above; an
+    all-zero vector has s = 0 and codes 0.  Dequantised value = s * v.
 
 The e4m3fn table is built by enumerating the format's definition, not by
 calling a conversion routine.
@@ -67,6 +73,22 @@ def fp8_encode_input(x: np.ndarray, scale: float) -> np.ndarray:
 
 def fp8_dequantize(codes: np.ndarray, scale: float) -> np.ndarray:
     return np.float64(np.float32(scale)) * e4m3fn_decode(codes)
+
+
+def fp8_dynamic_encode(x: np.ndarray):
+    """Dynamic FP8 of vectors along the last axis: (codes uint8 [..., D], scales float32 [...])."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    s = (amax / np.float32(448.0)).astype(np.float32)            # float32 division
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        codes = e4m3fn_encode(x32 / safe[..., None])
+    codes = np.where((s > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, s
+
+
+def fp8_dynamic_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    return np.asarray(scales, dtype=np.float32).astype(np.float64)[..., None] * e4m3fn_decode(codes)
 
 
 def f16_encode_input(bits: np.ndarray, dtype: int) -> np.ndarray:
