@@ -48,6 +48,8 @@ std::string validate_config(const vk_cache_config& c) {
   if (c.recent_tokens < 0) return "recent_tokens must be >= 0";
   if (!valid_format(c.sink_format) || !valid_format(c.recent_format)) return "unknown page format";
   if (c.decode_kernel < 0 || c.decode_kernel > 2) return "decode_kernel must be 0, 1 or 2";
+  if (c.fp8_dynamic != 0 && c.fp8_dynamic != 1) return "fp8_dynamic must be 0 or 1";
+  if (c.reserved0 != 0) return "reserved0 must be 0";
   if (c.pages_ternary < 0 || c.pages_fp8 < 0 || c.pages_f16 < 0) return "pool capacities must be >= 0";
   if (c.pages_ternary >= (1ll << 30) || c.pages_fp8 >= (1ll << 30) || c.pages_f16 >= (1ll << 30))
     return "pool capacities must be < 2^30 pages";
@@ -62,7 +64,7 @@ int64_t tile_bytes(const vk_cache_config& c, int fmt) {
   int64_t elems = static_cast<int64_t>(c.block_size) * c.head_dim;
   switch (fmt) {
     case VK_FMT_TERNARY2: return elems / 4;
-    case VK_FMT_FP8E4M3: return elems;
+    case VK_FMT_FP8E4M3: return elems + (c.fp8_dynamic ? 4ll * c.block_size : 0);  // + token scales
     case VK_FMT_F16: return elems * 2;
   }
   return 0;

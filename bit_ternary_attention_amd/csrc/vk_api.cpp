@@ -278,6 +278,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   P.bs_shift = 0;
   while ((1 << P.bs_shift) < cfg->block_size) ++P.bs_shift;
   P.fp8_scale = cfg->fp8_scale;
+  P.fp8_dynamic = cfg->fp8_dynamic;
   c->partials = static_cast<double*>(ptrs[5]);
   c->seg = static_cast<vk::SegInfo*>(ptrs[6]);
   c->dec_partials = static_cast<float*>(ptrs[7]);
@@ -371,7 +372,7 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
     c->timer.add_bytes(VK_KERNEL_ABSMEAN, layers * 2.0 * tern_tokens * row * 2.0);
     c->timer.add_bytes(VK_KERNEL_FINALIZE, static_cast<double>(n_seg) * n_blk * 8.0);
     const double in_bytes = layers * n_seqs * 2.0 * n_tokens * row * 2.0;
-    const double per_elem[3] = {0.25, 1.0, 2.0};
+    const double per_elem[3] = {0.25, 1.0 + (cfg.fp8_dynamic ? 4.0 / cfg.head_dim : 0.0), 2.0};  // + token scales
     double out_bytes = 0.0;
     for (const vk::AppendSeqDesc& d : plan.seqs) {
       for (int32_t j = 0; j < d.n_pages; ++j) {
@@ -544,7 +545,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       const double row = cfg.head_dim;
       const double unit_kv = 2.0 * 16.0 * cfg.n_kv_heads;  // K and V, 16 tokens, every KV head
       const double tern_bytes = unit_kv * cu[0] * row / 4.0;
-      const double other_bytes = unit_kv * (cu[1] * row + cu[2] * row * 2.0);
+      const double other_bytes = unit_kv * (cu[1] * (row + (cfg.fp8_dynamic ? 4.0 : 0.0)) + cu[2] * row * 2.0);
       const double q_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 2.0;
       const double out_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 4.0;
       const double part1 = static_cast<double>(nb) * cfg.n_q_heads * (cfg.head_dim + 2) * 4.0;  // one part

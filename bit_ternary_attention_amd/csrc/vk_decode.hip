@@ -119,6 +119,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
   constexpr int UPI = kDecodeUnitsPerIter;
   __shared__ uint32_t q2[G * QP];
   __shared__ uint32_t pbuf[UPI * G * 8];
+  __shared__ float vmax_s[UPI];  // dynamic FP8: largest value scale of each unit's 16 tokens
 
   const int lane = threadIdx.x;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
     float logit[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) logit[hh] = -INFINITY;
+    float vsc = 1.0f;  // dynamic FP8: this token's value scale (1 elsewhere)
     if (uv) {
       const int page = (u * 16) >> P.bs_shift;
       const int upi = ((u * 16) & (P.bs - 1)) >> 4;
@@ -207,6 +209,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
           }
         }
         kscale = P.fp8_scale;
+        if (P.fp8_dynamic) {  // the tiles' token scales follow their codes
+          const int64_t so = static_cast<int64_t>(P.bs) * D + 4 * (upi * 16 + r);
+          kscale = *reinterpret_cast<const float*>(pg + kvh * P.tile_bytes[1] + so);
+          // a token slot past the sequence may hold a stale scale of a recycled page
+          vsc = att ? *reinterpret_cast<const float*>(pg + (P.hkv + kvh) * P.tile_bytes[1] + so) : 0.0f;
+        }
       } else {
         const uint4* krow = reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[2] + (upi * 16 + r) * D * 2);
 #pragma unroll
@@ -231,6 +239,14 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
       }
     }
 
+    // dynamic FP8 values enter P*V as v * (s_t / s_max) with s_max the unit's largest scale
+    // (no overflow in f16), and the unit's sum is multiplied by s_max
+    float vmax = vsc;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    const float vratio = vmax > 0.0f ? vsc / vmax : 0.0f;
+    if (r == 0) vmax_s[us] = vmax;
+
     // ---------------- online softmax, wave-wide reference ----------------
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -243,8 +259,12 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
         m[hh] = mx;
       }
       const float p = (logit[hh] == -INFINITY) ? 0.0f : exp2f(logit[hh] - m[hh]);
-      lsum[hh] += p;
-      pb16[(us * G + hh) * 16 + r] = __half_as_ushort(__float2half_rn(p * 16384.0f));
+      // the sum takes each weight as P*V will see it: the f16 product, divided back by the
+      // value ratio (numerator and denominator then round alike)
+      const __half ph = __float2half_rn(p * vratio * 16384.0f);
+      const float pr = __half2float(ph);  // below the f16 normal range the ratio is not kept
+      lsum[hh] += pr >= 0x1p-14f ? pr * (1.0f / 16384.0f) / vratio : p;
+      pb16[(us * G + hh) * 16 + r] = __half_as_ushort(ph);
     }
     __syncthreads();
 
@@ -309,7 +329,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
             for (int hh = 0; hh < G; ++hh) tmp[hh][j] = dot2(pp[hh * 8 + ii], c2, tmp[hh][j]);
           }
         }
-        vscale = P.fp8_scale;
+        vscale = P.fp8_dynamic ? vmax_s[us2] : P.fp8_scale;
       } else {
 #pragma unroll
         for (int j = 0; j < DPL; ++j) {
@@ -381,6 +401,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
@@ -503,7 +524,7 @@ __device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], cons
   }
 }
 
-template <int D, int G, int QDT, int PF>
+template <int D, int G, int QDT, int PF, bool DYN>
 __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_decode_mfma(DecodeArgs a) {
   constexpr int NC = D / 64;   // 32-bit key code words per lane per unit
   constexpr int NV = D / 64;   // 32-bit value chunk words per lane per unit
@@ -810,11 +831,21 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  // A operands and scales of a non-ternary unit, loaded here (f16 values, not u * 2^-14)
-  auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float& scale) {
+  // A operands and scales of a non-ternary unit, loaded here (f16 values, not u * 2^-14).
+  // ks[r]: factor of the score of token 4 grp + r (applied to the float32 product); rt[r]:
+  // factor of that token's probability in P*V; vscale: factor of the unit's P*V sum.  Dynamic
+  // FP8 gives every token its own scales: ks = s_t, rt = s_t / s_max (at most 1: no f16
+  // overflow) and vscale = s_max for the values.  Only attended tokens count towards s_max:
+  // a slot past the sequence may hold a stale scale of a recycled page.
+  auto attended_tok = [&](int t) { return R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L)); };
+  auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float (&ks)[4], float (&rt)[4],
+                            float& vscale) {
     const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
     const int64_t idx = entry & 0x3FFFFFFF;
     const int upi = ((unit_of(lu) * 16) & (P.bs - 1)) >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ks[r] = 1.0f, rt[r] = 1.0f;
+    vscale = 1.0f;
     if (fmt == VK_FMT_FP8E4M3) {
       const uint8_t* pg = P.pool[1] + (layer * P.cap[1] + idx) * P.page_bytes[1];
       const uint4* kp = reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[1] + (upi * 16 + c16) * D + dbase);
@@ -840,7 +871,27 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         va[j] = __builtin_bit_cast(h4_t, u2_t{h2u(fp8x2((x & 0xFFu) | ((x & 0xFF00u) << 8))),
                                               h2u(fp8x2(((x >> 16) & 0xFFu) | ((x >> 8) & 0x00FF0000u)))});
       }
-      scale = P.fp8_scale;
+      if constexpr (!DYN) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ks[r] = P.fp8_scale;
+        vscale = P.fp8_scale;
+      } else {
+        // token scales after each tile's codes; this lane's score and value rows are tokens
+        // 4 grp .. 4 grp + 3
+        const int t0 = unit_of(lu) * 16;
+        const int64_t so = static_cast<int64_t>(P.bs) * D + 4 * (upi * 16 + 4 * grp);
+        const float4 k4 = *reinterpret_cast<const float4*>(pg + kvh * P.tile_bytes[1] + so);
+        ks[0] = k4.x; ks[1] = k4.y; ks[2] = k4.z; ks[3] = k4.w;
+        const float4 v4 = *reinterpret_cast<const float4*>(vt + so);
+        float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vv[r] = attended_tok(t0 + 4 * grp + r) ? vv[r] : 0.0f;
+        const float vmax = max_rows(fmaxf(fmaxf(vv[0], vv[1]), fmaxf(vv[2], vv[3])));
+        const float inv = vmax > 0.0f ? 1.0f / vmax : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rt[r] = vv[r] * inv;
+        vscale = vmax;
+      }
     } else {
       const uint8_t* pg = P.pool[2] + (layer * P.cap[2] + idx) * P.page_bytes[2];
       const uint4* kp =
@@ -863,9 +914,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
             *reinterpret_cast<const uint2*>(vt + (static_cast<int64_t>(16 * j + c16) * P.bs + upi * 16 + 4 * grp) * 2);
         va[j] = __builtin_bit_cast(h4_t, u2_t{x.x, x.y});
       }
-      scale = 1.0f;
     }
   };
+
 
   // Block x = n_splits: the fp8 / fp16 units of every attended range.  Every wave scans the
   // range 64 units at a time (a ballot over one block-table entry per lane) and takes every
@@ -887,12 +938,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
         h8_t ka[NS];
         h4_t va[NB];
-        float vscale;
-        operands_other(lu, entry, ka, va, vscale);
+        float ksc[4], prt[4], vscale;
+        operands_other(lu, entry, ka, va, ksc, prt, vscale);
         f4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
-        const float a0 = vscale * a.scale_log2;
         const int u = unit_of(lu);
         float sc[4];
         float mx = -INFINITY;
@@ -900,7 +950,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
         for (int r = 0; r < 4; ++r) {
           const int t = u * 16 + 4 * grp + r;
           const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
-          sc[r] = att ? s4[r] * a0 : -INFINITY;
+          sc[r] = att ? s4[r] * (ksc[r] * a.scale_log2) : -INFINITY;
           mx = fmaxf(mx, sc[r]);
         }
         mx = max_rows(mx);
@@ -918,9 +968,26 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                           static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[1] - ms))};
         const h2_t p23 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[2] - ms)),
                           static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[3] - ms))};
-        lsum = __builtin_amdgcn_fdot2(p01, ones, lsum, false);
-        lsum = __builtin_amdgcn_fdot2(p23, ones, lsum, false);
-        const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(p01), h2u(p23)});
+        h2_t q01 = p01, q23 = p23;
+        if constexpr (!DYN) {
+          lsum = __builtin_amdgcn_fdot2(p01, ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2(p23, ones, lsum, false);
+        } else {
+          // each token's value scale relative to the unit's largest; the sum takes each weight
+          // as P*V sees it (the f16 product divided back by the ratio) so both round alike
+          const float pf[4] = {__builtin_amdgcn_exp2f(sc[0] - ms), __builtin_amdgcn_exp2f(sc[1] - ms),
+                               __builtin_amdgcn_exp2f(sc[2] - ms), __builtin_amdgcn_exp2f(sc[3] - ms)};
+          _Float16 qh[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            qh[r] = static_cast<_Float16>(pf[r] * prt[r]);
+            const float qr = static_cast<float>(qh[r]);  // below the f16 normal range: unrounded
+            lsum += qr >= 0x1p-14f ? qr / prt[r] : pf[r];
+          }
+          q01 = h2_t{qh[0], qh[1]};
+          q23 = h2_t{qh[2], qh[3]};
+        }
+        const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(q01), h2u(q23)});
         const float vs14 = vscale * (1.0f / 16384.0f);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -1085,12 +1152,15 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   if (a.kernel == VK_DECODE_VALU) {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
     else k_decode<D, G, 0><<<grid, 64, 0, s>>>(a);
+  } else if (a.P.fp8_dynamic) {  // dynamic FP8 pages: their scale handling in its own instance
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, true><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 8, true><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   } else if (a.units_per_iter == 8) {
-    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
-    else k_decode_mfma<D, G, 0, 8><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 8, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   } else {
-    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 4><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
-    else k_decode_mfma<D, G, 0, 4><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 4, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 4, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   }
   if (t) t->end(VK_KERNEL_DECODE, s);
   if (a.n_parts > 1) {

@@ -27,7 +27,7 @@ struct PoolsView {
   int32_t bs;              // tokens per page (power of two)
   int32_t bs_shift;        // log2(bs)
   float fp8_scale;
-  int32_t pad;
+  int32_t fp8_dynamic;     // FP8 tiles end with block_size float32 scales (one per token)
   const uint8_t* dummy_page;  // a zeroed ternary-page-sized buffer: target of speculative loads
 };
 

@@ -112,17 +112,20 @@ __device__ __forceinline__ uint32_t key_word(uint4 w, uint32_t add) {
   return key_byte(w.x, add) | (key_byte(w.y, add) << 8) | (key_byte(w.z, add) << 16) | (key_byte(w.w, add) << 24);
 }
 
-// One value chunk: x[j] = FP8 bytes of tokens 4g..4g+3 (little-endian) of dimension 16j + c.
-// Dimensions are taken two at a time: one byte permute puts bytes (b0, b1) of x[j] and
-// x[j+1] side by side, so their fields land two bits apart.
+// One value chunk: x[j] = FP8 bytes of tokens 4g..4g+3 (little-endian) of dimension 16j + c;
+// byte r of `add` belongs to token 4g + r.  Dimensions are taken two at a time: one byte
+// permute puts bytes (b0, b1) of x[j] and x[j+1] side by side, so their fields land two
+// bits apart (the add bytes are permuted the same way).
 template <int D>
 __device__ __forceinline__ void store_chunk(const uint32_t* x, uint32_t add, uint8_t* out) {
+  const uint32_t add01 = __builtin_amdgcn_perm(add, add, 0x01010000u);  // tokens 0, 0, 1, 1
+  const uint32_t add23 = __builtin_amdgcn_perm(add, add, 0x03030202u);  // tokens 2, 2, 3, 3
   uint32_t w0 = 0, w1 = 0;
 #pragma unroll
   for (int j = 0; j < D / 16; j += 2) {
     // [x_j.b0, x_j+1.b0, x_j.b1, x_j+1.b1] and the same of bytes 2, 3
-    const uint32_t f01 = fields4(__builtin_amdgcn_perm(x[j + 1], x[j], 0x05010400u), add);
-    const uint32_t f23 = fields4(__builtin_amdgcn_perm(x[j + 1], x[j], 0x07030602u), add);
+    const uint32_t f01 = fields4(__builtin_amdgcn_perm(x[j + 1], x[j], 0x05010400u), add01);
+    const uint32_t f23 = fields4(__builtin_amdgcn_perm(x[j + 1], x[j], 0x07030602u), add23);
     const uint32_t t01 = (f01 & 0x00030003u) | ((f01 >> 6) & 0x000C000Cu);  // bits 0-3, 16-19
     const uint32_t t23 = (f23 & 0x00030003u) | ((f23 >> 6) & 0x000C000Cu);
     if (D == 128) {
@@ -234,14 +237,123 @@ __global__ __launch_bounds__(kRetierThreads) void k_retier(RetierArgs a) {
   }
 }
 
+// Dynamic FP8 pages: every token has its own scale s_t (stored after each tile's codes),
+// so x = s_t v.  Sum in float64: per token the float32 sum of |v| is exact, times s_t.
+// A code is nonzero when float32(s_t v) > tau, i.e. when the byte's magnitude index reaches
+// the token's own threshold index (a 7-step search over the 127 magnitudes).  Two passes.
+__device__ __forceinline__ uint32_t thresh_index(float s, double tau) {
+  uint32_t lo = 0, hi = 127;  // count of indices m with float32(s * v(m)) <= tau (a prefix)
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    const uint32_t mid = (lo + hi) >> 1;
+    const bool le = static_cast<double>(s * (static_cast<float>(e4m3_x512(mid)) * 0x1p-9f)) <= tau;
+    lo = le ? mid + 1 : lo;
+    hi = le ? hi : mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ double block_sum_f64(double x, double* part) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+template <int D>
+__global__ __launch_bounds__(kRetierThreads) void k_retier_dyn(RetierArgs a) {
+  __shared__ double part[kRetierThreads / 64];
+  const RetierTask t = a.tasks[blockIdx.x];
+  const int layer = blockIdx.y, kv = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hkv = a.P.hkv, bs = a.P.bs, units = bs >> 4;
+  const int64_t tile = a.P.tile_bytes[VK_FMT_FP8E4M3];  // bs * D codes, then bs float32 scales
+  const int64_t n = static_cast<int64_t>(hkv) * bs * D;
+  const int64_t per_head = static_cast<int64_t>(bs) * D / 16;  // 16-byte key pieces per head
+  const uint8_t* src = a.P.pool[VK_FMT_FP8E4M3] +
+                       (static_cast<int64_t>(layer) * a.P.cap[VK_FMT_FP8E4M3] + t.src) * a.P.page_bytes[VK_FMT_FP8E4M3] +
+                       kv * hkv * tile;
+  uint8_t* dst = a.P.pool[VK_FMT_TERNARY2] +
+                 (static_cast<int64_t>(layer) * a.P.cap[VK_FMT_TERNARY2] + t.dst) * a.P.page_bytes[VK_FMT_TERNARY2] +
+                 kv * (n / 4);
+  auto scale_of = [&](int h, int tok) {
+    return *reinterpret_cast<const float*>(src + h * tile + static_cast<int64_t>(bs) * D + 4 * tok);
+  };
+  const int c = lane >> 2, g = lane & 3;
+
+  double acc = 0.0;
+  if (kv == 0) {
+    for (int64_t i = tid; i < hkv * per_head; i += kRetierThreads) {
+      const int h = static_cast<int>(i / per_head);
+      const int64_t rem = i - h * per_head;
+      const uint4 w = *reinterpret_cast<const uint4*>(src + h * tile + 16 * rem);
+      const float s16 = (abs_sum4f(w.x) + abs_sum4f(w.y)) + (abs_sum4f(w.z) + abs_sum4f(w.w));
+      acc += static_cast<double>(s16) * static_cast<double>(scale_of(h, static_cast<int>(16 * rem / D)));
+    }
+  } else {
+    for (int pair = wave; pair < hkv * units; pair += kRetierThreads / 64) {
+      const int h = pair / units, u = pair - h * units;
+      const uint8_t* vs = src + h * tile + 16 * u + 4 * g;
+      float tok[4] = {0.f, 0.f, 0.f, 0.f};  // per token: at most D / 16 values, exact
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(vs + static_cast<int64_t>(16 * j + c) * bs);
+        const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(x), false);
+        const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(x), true);
+        tok[0] += fabsf(lo.x); tok[1] += fabsf(lo.y); tok[2] += fabsf(hi.x); tok[3] += fabsf(hi.y);
+      }
+      const float4 s4 = *reinterpret_cast<const float4*>(src + h * tile + static_cast<int64_t>(bs) * D + 4 * (16 * u + 4 * g));
+      acc += static_cast<double>(tok[0]) * s4.x + static_cast<double>(tok[1]) * s4.y +
+             static_cast<double>(tok[2]) * s4.z + static_cast<double>(tok[3]) * s4.w;
+    }
+  }
+  const double total = block_sum_f64(acc, part);
+  const float gamma = static_cast<float>(total / static_cast<double>(n));
+  const float d = gamma + a.eps;
+  const double tau = static_cast<double>(d) * (0.5 + 0x1p-25);
+  auto add_of = [&](float sc) { return d > 0.0f ? 0x80u - thresh_index(sc, tau) : 0u; };  // per byte
+
+  if (kv == 0) {
+    for (int64_t i = tid; i < hkv * per_head; i += kRetierThreads) {
+      const int h = static_cast<int>(i / per_head);
+      const int64_t rem = i - h * per_head;
+      const uint4 w = *reinterpret_cast<const uint4*>(src + h * tile + 16 * rem);
+      const uint32_t add = add_of(scale_of(h, static_cast<int>(16 * rem / D))) * 0x01010101u;
+      *reinterpret_cast<uint32_t*>(dst + h * (per_head * 4) + 4 * rem) = key_word(w, add);
+    }
+  } else {
+    for (int pair = wave; pair < hkv * units; pair += kRetierThreads / 64) {
+      const int h = pair / units, u = pair - h * units;
+      const uint8_t* vs = src + h * tile + 16 * u + 4 * g;
+      const float4 s4 = *reinterpret_cast<const float4*>(src + h * tile + static_cast<int64_t>(bs) * D + 4 * (16 * u + 4 * g));
+      const uint32_t add = add_of(s4.x) | (add_of(s4.y) << 8) | (add_of(s4.z) << 16) | (add_of(s4.w) << 24);
+      uint32_t x[D / 16];
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) x[j] = *reinterpret_cast<const uint32_t*>(vs + static_cast<int64_t>(16 * j + c) * bs);
+      store_chunk<D>(x, add, dst + static_cast<int64_t>(h) * bs * (D / 4) + u * 4 * D + lane * (D / 16));
+    }
+  }
+  if (tid == 0) {
+    a.P.gamma[(static_cast<int64_t>(layer) * a.P.cap[VK_FMT_TERNARY2] + t.dst) * 2 + kv] = gamma;
+    if (layer == 0 && kv == 0)
+      a.P.block_table[static_cast<int64_t>(t.slot) * a.P.max_pages + t.page] = t.dst;  // format 0 = ternary
+  }
+}
+
 }  // namespace
 
 hipError_t launch_retier(const RetierArgs& a, hipStream_t s, LaunchTimer* t) {
   if (a.n_tasks <= 0) return hipSuccess;
   const dim3 grid(a.n_tasks, a.P.n_layers, 2);
   if (t) t->begin(VK_KERNEL_RETIER, s);
-  if (a.P.dim == 128) k_retier<128><<<grid, kRetierThreads, 0, s>>>(a);
-  else k_retier<64><<<grid, kRetierThreads, 0, s>>>(a);
+  if (a.P.fp8_dynamic) {
+    if (a.P.dim == 128) k_retier_dyn<128><<<grid, kRetierThreads, 0, s>>>(a);
+    else k_retier_dyn<64><<<grid, kRetierThreads, 0, s>>>(a);
+  } else {
+    if (a.P.dim == 128) k_retier<128><<<grid, kRetierThreads, 0, s>>>(a);
+    else k_retier<64><<<grid, kRetierThreads, 0, s>>>(a);
+  }
   if (t) t->end(VK_KERNEL_RETIER, s);
   return hipGetLastError();
 }

@@ -278,16 +278,28 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
         __syncthreads();
       }
     } else if (fmt == VK_FMT_FP8E4M3) {
-      const float s = a.P.fp8_scale;
+      const bool dyn = a.P.fp8_dynamic != 0;
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
         const int r = rg * NI + k;
         const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        float s = a.P.fp8_scale;
+        if (dyn) {
+          // dynamic FP8: s = float32(max |x| / 448) over the row (the CPR lanes of rg)
+          float amax = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(to_f32<DT>((ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu)));
+#pragma unroll
+          for (int off = 1; off < CPR; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+          s = amax / 448.0f;
+          if (c == 0 && ok[k])
+            *reinterpret_cast<float*>(tile + static_cast<int64_t>(a.P.bs) * D + 4 * (upi * 16 + r)) = s;
+        }
         uint32_t b[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = to_f32<DT>((ws[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          b[e] = e4m3fn_rne(s == 1.0f ? x : x / s);
+          b[e] = dyn ? (s > 0.0f ? e4m3fn_rne(x / s) : 0u) : e4m3fn_rne(s == 1.0f ? x : x / s);
         }
         if (kv == 0) {
           if (ok[k]) {

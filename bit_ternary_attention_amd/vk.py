@@ -27,7 +27,7 @@ class CacheConfig(ctypes.Structure):
     _fields_ = [("n_layers", _c_i32), ("n_kv_heads", _c_i32), ("n_q_heads", _c_i32), ("head_dim", _c_i32),
                 ("block_size", _c_i32), ("max_seqs", _c_i32), ("max_tokens_per_seq", _c_i32),
                 ("sink_tokens", _c_i32), ("sink_format", _c_i32), ("recent_tokens", _c_i32),
-                ("recent_format", _c_i32), ("decode_kernel", _c_i32),
+                ("recent_format", _c_i32), ("decode_kernel", _c_i32), ("fp8_dynamic", _c_i32), ("reserved0", _c_i32),
                 ("pages_ternary", _c_i64), ("pages_fp8", _c_i64), ("pages_f16", _c_i64),
                 ("eps", _c_f32), ("fp8_scale", _c_f32), ("page_shuffle_seed", _c_u64)]
 

@@ -62,7 +62,11 @@ enum { VK_DTYPE_F16 = 0, VK_DTYPE_BF16 = 1 };
 /* page formats (the tiers of Minima-KV, "Recent, Anchor and Stale") */
 enum {
   VK_FMT_TERNARY2 = 0,  /* 2-bit codes, 4 per byte, one float32 gamma per page for K and for V */
-  VK_FMT_FP8E4M3 = 1,   /* OCP e4m3fn bytes of x / fp8_scale, round to nearest even, saturating */
+  VK_FMT_FP8E4M3 = 1,   /* OCP e4m3fn bytes of x / s, round to nearest even, saturating; s =
+                           fp8_scale, or with fp8_dynamic s = float32(max|x| / 448) per (token,
+                           KV head) vector (0 and codes 0 for a zero vector), stored after each
+                           tile as block_size float32 values ("dynamic FP8 streaming mode" of
+                           Show HN: Vantage-V-AI)                                              */
   VK_FMT_F16 = 2        /* IEEE float16, round to nearest even from the input                    */
 };
 
@@ -101,6 +105,9 @@ typedef struct vk_cache_config {
   int32_t recent_tokens;      /* R >= 0; 0 = no recent tier                            */
   int32_t recent_format;      /* VK_FMT_*                                              */
   int32_t decode_kernel;      /* VK_DECODE_*: which decode kernel reads the pages        */
+  int32_t fp8_dynamic;        /* 0: FP8 pages use the static fp8_scale; 1: dynamic FP8, one
+                                 float32 scale per (token, KV head) for K and for V       */
+  int32_t reserved0;          /* 0                                                     */
   int64_t pages_ternary;      /* pool capacity per layer, pages (>= 0)                 */
   int64_t pages_fp8;
   int64_t pages_f16;

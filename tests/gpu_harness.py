@@ -29,10 +29,10 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def spec_of(w: wl.Workload, eps=1e-5, fp8_scale=1.0) -> oc.CacheSpec:
+def spec_of(w: wl.Workload, eps=1e-5, fp8_scale=1.0, fp8_dynamic=False) -> oc.CacheSpec:
     return oc.CacheSpec(n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, block_size=w.block_size,
                         sink_tokens=w.sink_tokens, sink_format=w.sink_format, recent_tokens=w.recent_tokens,
-                        recent_format=w.recent_format, eps=eps, fp8_scale=fp8_scale)
+                        recent_format=w.recent_format, eps=eps, fp8_scale=fp8_scale, fp8_dynamic=bool(fp8_dynamic))
 
 
 def seq_calls(w: wl.Workload, seq: int):
@@ -53,7 +53,7 @@ def pages_needed(w: wl.Workload) -> List[int]:
 
 
 def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_pages=(0, 0, 0),
-               max_tokens=None, decode_kernel=0) -> vk.Cache:
+               max_tokens=None, decode_kernel=0, fp8_dynamic=0) -> vk.Cache:
     need = pages_needed(w)
     cfg = vk.make_config(n_layers=w.n_layers, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
                          head_dim=w.head_dim, block_size=w.block_size, max_seqs=w.n_seqs,
@@ -62,7 +62,7 @@ def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_page
                          pages_ternary=need[0] + slack_pages[0], pages_fp8=need[1] + slack_pages[1],
                          pages_f16=need[2] + slack_pages[2], eps=eps, fp8_scale=fp8_scale,
                          page_shuffle_seed=w.page_shuffle_seed if shuffle is None else shuffle,
-                         decode_kernel=decode_kernel)
+                         decode_kernel=decode_kernel, fp8_dynamic=int(fp8_dynamic))
     return vk.Cache(cfg)
 
 
@@ -95,9 +95,9 @@ def read_page(cache: vk.Cache, layer: int, seq: int, p: int):
 
 
 def check_pages(cache: vk.Cache, w: wl.Workload, layer: int, seq: int, kbits, vbits, pages=None,
-                eps=1e-5, fp8_scale=1.0) -> oc.EncodedSequence:
+                eps=1e-5, fp8_scale=1.0, fp8_dynamic=False) -> oc.EncodedSequence:
     """Formats, gamma (2^-22 rel) and bytes (exact, re-encoded with the device gamma) of sampled pages."""
-    spec = spec_of(w, eps, fp8_scale)
+    spec = spec_of(w, eps, fp8_scale, fp8_dynamic)
     calls = seq_calls(w, seq)
     enc = oc.encode_sequence(spec, kbits, vbits, w.dtype, calls)
     bs = w.block_size
@@ -136,10 +136,14 @@ def check_partial_page(spec, enc, p, got, fmt, n_tok):
     """Per-token comparison for a page whose tail was never written."""
     bs, hkv, dim = spec.block_size, spec.n_kv_heads, spec.head_dim
     tb = {oc.TERNARY2: bs * dim // 4, oc.FP8E4M3: bs * dim, oc.F16: bs * dim * 2}[fmt]
+    stride = tb + (4 * bs if fmt == oc.FP8E4M3 and spec.fp8_dynamic else 0)   # + token scales
     lo = p * bs
-    for which, off in (("k", 0), ("v", hkv * tb)):
+    for which, off in (("k", 0), ("v", hkv * stride)):
         for h in range(hkv):
-            tile = got[off + h * tb: off + (h + 1) * tb]
+            tile = got[off + h * stride: off + h * stride + tb]
+            if stride != tb:
+                sc = got[off + h * stride + tb: off + (h + 1) * stride].view("<f4")
+                assert np.array_equal(sc[:n_tok], getattr(enc, which + "_fp8_scale")[lo:lo + n_tok, h]), (p, which, h)
             if fmt == oc.TERNARY2:
                 codes = ot.unpack_flat(tile.reshape(bs, dim // 4)) if which == "k" else \
                     ot.v_tile_codes(tile, bs, dim)
@@ -178,9 +182,9 @@ def check_decode(out: torch.Tensor, q: torch.Tensor, w: wl.Workload, encs: Dict[
 
 
 def run_workload(w: wl.Workload, sample_seqs: Sequence[int], page_layers: Sequence[int],
-                 decode_layers: Sequence[int], shuffle=None, decode_kernel=0) -> dict:
-    say(f"[{w.name}] create+fill (decode kernel {decode_kernel})")
-    cache = make_cache(w, shuffle=shuffle, decode_kernel=decode_kernel)
+                 decode_layers: Sequence[int], shuffle=None, decode_kernel=0, fp8_dynamic=0) -> dict:
+    say(f"[{w.name}] create+fill (decode kernel {decode_kernel}, dynamic fp8 {fp8_dynamic})")
+    cache = make_cache(w, shuffle=shuffle, decode_kernel=decode_kernel, fp8_dynamic=fp8_dynamic)
     fill(cache, w)
     report = {"gamma_checked": 0, "max_err": 0.0}
     encs_by_layer = {}
@@ -190,9 +194,9 @@ def run_workload(w: wl.Workload, sample_seqs: Sequence[int], page_layers: Sequen
             kb, vb = host_kv(w, layer, s)
             if layer in page_layers:
                 say(f"[{w.name}] pages layer {layer} seq {s}")
-                encs[s] = check_pages(cache, w, layer, s, kb, vb)
+                encs[s] = check_pages(cache, w, layer, s, kb, vb, fp8_dynamic=fp8_dynamic)
             else:
-                encs[s] = oc.encode_sequence(spec_of(w), kb, vb, w.dtype, seq_calls(w, s))
+                encs[s] = oc.encode_sequence(spec_of(w, fp8_dynamic=fp8_dynamic), kb, vb, w.dtype, seq_calls(w, s))
         encs_by_layer[layer] = encs
         if layer in decode_layers:
             q = wl.queries(w, layer, device="cuda")

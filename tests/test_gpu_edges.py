@@ -85,18 +85,23 @@ def _route_workload(fmt, dtype, scale=1.0):
                              sink_tokens=512, sink_format=oc.F16, lengths=(512,))
 
 
-@pytest.mark.parametrize("fmt,dtype,scale", [(oc.FP8E4M3, 1, 1.0), (oc.FP8E4M3, 0, 1.0), (oc.FP8E4M3, 1, 3.0),
-                                             (oc.FP8E4M3, 1, 0.0078125), (oc.F16, 1, 1.0), (oc.F16, 0, 1.0)])
-def test_page_routes_exhaustive(fmt, dtype, scale):
+@pytest.mark.parametrize("fmt,dtype,scale,dyn", [(oc.FP8E4M3, 1, 1.0, 0), (oc.FP8E4M3, 0, 1.0, 0),
+                                                 (oc.FP8E4M3, 1, 3.0, 0), (oc.FP8E4M3, 1, 0.0078125, 0),
+                                                 (oc.FP8E4M3, 1, 1.0, 1), (oc.FP8E4M3, 0, 1.0, 1),
+                                                 (oc.F16, 1, 1.0, 0), (oc.F16, 0, 1.0, 0)])
+def test_page_routes_exhaustive(fmt, dtype, scale, dyn):
     w = _route_workload(fmt, dtype)
     bits = all_finite_patterns(dtype)
     kb = bits.reshape(512, 1, 128)
     vb = np.ascontiguousarray(bits[::-1]).reshape(512, 1, 128)
-    cache = make_cache(w, fp8_scale=scale)
+    if dyn:  # a zero row (scale 0) among the rows of every pattern
+        kb = kb.copy()
+        kb[3] = 0
+    cache = make_cache(w, fp8_scale=scale, fp8_dynamic=dyn)
     k = to_dev(kb.ravel(), dtype).view(1, 1, 512, 1, 128)
     v = to_dev(vb.ravel(), dtype).view(1, 1, 512, 1, 128)
     cache.append(k, v, [0])
-    enc = check_pages(cache, w, 0, 0, kb, vb, pages=list(range(32)), fp8_scale=scale)
+    enc = check_pages(cache, w, 0, 0, kb, vb, pages=list(range(32)), fp8_scale=scale, fp8_dynamic=dyn)
     assert set(enc.page_format) == {fmt}
     cache.close()
 
@@ -145,14 +150,15 @@ def test_edge_workloads(name, kw, windows, kernel):
     cache.close()
 
 
+@pytest.mark.parametrize("dyn", [0, 1], ids=["static-fp8", "dynamic-fp8"])
 @pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
-def test_incremental_decode_appends_into_recent_tier(kernel):
+def test_incremental_decode_appends_into_recent_tier(kernel, dyn):
     """Prefill, then one-token appends (the recent fp8 tier grows page by page), decoding each step."""
     w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
                           recent_tokens=64, recent_format=oc.FP8E4M3, lengths=(300,))
     steps = [(0, 250)] + [(250 + i, 1) for i in range(50)]
-    cache = make_cache(w, slack_pages=(0, 8, 0), decode_kernel=kernel)
-    spec = spec_of(w)
+    cache = make_cache(w, slack_pages=(0, 8, 0), decode_kernel=kernel, fp8_dynamic=dyn)
+    spec = spec_of(w, fp8_dynamic=dyn)
     kall = wl.kv_block(w, "k", 0, 0, 0, 300, device="cuda")
     vall = wl.kv_block(w, "v", 0, 0, 0, 300, device="cuda")
     kb, vb = wl.to_bits(kall), wl.to_bits(vall)
@@ -248,4 +254,31 @@ def test_errors_leave_cache_unchanged_and_usable():
         c2.append(kk, kk, [0])
     assert e.value.status == vk.ERR_ALIGN
     c2.close()
+    cache.close()
+
+
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
+def test_dynamic_fp8_mixed_tiers_with_extreme_rows(kernel):
+    """Dynamic FP8 recent pages holding zero rows, tiny rows and rows near the bfloat16 range
+    next to ordinary ones; pages (codes and scales) exact, decode within tolerance."""
+    w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
+                          recent_tokens=80, recent_format=oc.FP8E4M3, lengths=(211, 37, 160),
+                          page_shuffle_seed=5, batch_appends=False)
+    cache = make_cache(w, decode_kernel=kernel, fp8_dynamic=1)
+    encs = {}
+    for ids, t0, n in w.appends():
+        k, v = wl.append_inputs(w, ids, t0, n, device="cuda")
+        k[0, 0, -3] = 0.0                         # a zero key row for both heads (scale 0)
+        v[0, 0, -5, 1] = 1e-30                    # a tiny value row
+        k[0, 0, -7, 0] *= 1e4                     # a large key row
+        cache.append(k.contiguous(), v.contiguous(), ids)
+        kb, vb = wl.to_bits(k[0, 0]), wl.to_bits(v[0, 0])
+        encs[ids[0]] = check_pages(cache, w, 0, ids[0], kb, vb, fp8_dynamic=1,
+                                   pages=list(range(-(-n // w.block_size))))
+    q = wl.queries(w, 0, device="cuda")
+    for W in (-1, 70, 0):
+        out = cache.decode(q, [0, 1, 2], 0, window=W)
+        torch.cuda.synchronize()
+        err = check_decode(out, q, w, encs, W)
+        say(f"dynamic fp8 window {W}: max err {err:.2e}")
     cache.close()

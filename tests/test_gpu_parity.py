@@ -54,6 +54,17 @@ def test_workload4_mixed_format_paged(kernel):
 
 
 @KERNELS
+def test_workload4_dynamic_fp8(kernel):
+    """Workload 4 with the recent tier in dynamic FP8 (one scale per token and KV head)."""
+    w = wl.workload(4)
+    lengths = list(w.lengths)
+    sample = sorted({lengths.index(max(lengths)), 7, 40})
+    r = run_workload(w, sample_seqs=sample, page_layers=[0], decode_layers=[0], decode_kernel=kernel, fp8_dynamic=1)
+    assert r["stats"]["last_decode_units"][1] > 0
+    say(f"workload 4 dynamic fp8: max err {r['max_err']:.3e}")
+
+
+@KERNELS
 def test_workload5_prefill_128k_chunked(kernel):
     w = wl.workload(5)
     r = run_workload(w, sample_seqs=[2], page_layers=[0], decode_layers=[0], decode_kernel=kernel)

@@ -56,18 +56,19 @@ class Stream:
         return torch.randn((self.n_seqs, self.hq, self.dim), generator=self.gen, device="cuda").to(self.tdtype)
 
 
-def make(stream, bs, S, sinkf, R, cap, fp8_scale=1.0, decode_kernel=0, max_tokens=4096):
+def make(stream, bs, S, sinkf, R, cap, fp8_scale=1.0, decode_kernel=0, max_tokens=4096, fp8_dynamic=0):
     cfg = vk.make_config(n_layers=stream.n_layers, n_kv_heads=stream.hkv, n_q_heads=stream.hq,
                          head_dim=stream.dim, block_size=bs, max_seqs=stream.n_seqs, max_tokens_per_seq=max_tokens,
                          sink_tokens=S, sink_format=sinkf, recent_tokens=R, recent_format=vk.FMT_FP8E4M3,
                          pages_ternary=cap[0], pages_fp8=cap[1], pages_f16=cap[2], fp8_scale=fp8_scale,
-                         page_shuffle_seed=77, decode_kernel=decode_kernel)
+                         page_shuffle_seed=77, decode_kernel=decode_kernel, fp8_dynamic=fp8_dynamic)
     return vk.Cache(cfg)
 
 
-def spec_for(stream, bs, S, sinkf, R, fp8_scale=1.0):
+def spec_for(stream, bs, S, sinkf, R, fp8_scale=1.0, fp8_dynamic=0):
     return oc.CacheSpec(n_kv_heads=stream.hkv, head_dim=stream.dim, block_size=bs, sink_tokens=S,
-                        sink_format=sinkf, recent_tokens=R, recent_format=oc.FP8E4M3, fp8_scale=fp8_scale)
+                        sink_format=sinkf, recent_tokens=R, recent_format=oc.FP8E4M3, fp8_scale=fp8_scale,
+                        fp8_dynamic=bool(fp8_dynamic))
 
 
 def check_retiered(cache, stream, spec, layer, s):
@@ -132,17 +133,20 @@ def check_decode(cache, stream, encs, layer, window, S):
     return worst
 
 
-@pytest.mark.parametrize("dim,bs,S,sinkf,R,scale", [(128, 16, 4, wl.FMT_F16, 48, 1.0),
-                                                     (64, 32, 4, wl.FMT_TERNARY2, 40, 1.0),
-                                                     (128, 64, 0, wl.FMT_TERNARY2, 100, 0.3),
-                                                     (64, 16, 20, wl.FMT_FP8E4M3, 16, 0.25)])
-def test_retier_ragged_appends(dim, bs, S, sinkf, R, scale):
+@pytest.mark.parametrize("dim,bs,S,sinkf,R,scale,dyn", [(128, 16, 4, wl.FMT_F16, 48, 1.0, 0),
+                                                         (64, 32, 4, wl.FMT_TERNARY2, 40, 1.0, 0),
+                                                         (128, 64, 0, wl.FMT_TERNARY2, 100, 0.3, 0),
+                                                         (64, 16, 20, wl.FMT_FP8E4M3, 16, 0.25, 0),
+                                                         (128, 16, 4, wl.FMT_F16, 48, 1.0, 1),
+                                                         (64, 32, 4, wl.FMT_TERNARY2, 40, 1.0, 1),
+                                                         (128, 64, 20, wl.FMT_FP8E4M3, 100, 1.0, 1)])
+def test_retier_ragged_appends(dim, bs, S, sinkf, R, scale, dyn):
     """Ragged appends per sequence, retiering after every call; every page checked."""
-    say(f"retier ragged: dim {dim} bs {bs} S {S} sink fmt {sinkf} R {R} scale {scale}")
+    say(f"retier ragged: dim {dim} bs {bs} S {S} sink fmt {sinkf} R {R} scale {scale} dynamic {dyn}")
     st = Stream(2, 3, 2, 8, dim, wl.DTYPE_BF16, seed=dim + bs + R)
     rng = np.random.default_rng(dim * bs + R)
-    cache = make(st, bs, S, sinkf, R, (600, 200, 40), fp8_scale=scale)
-    spec = spec_for(st, bs, S, sinkf, R, scale)
+    cache = make(st, bs, S, sinkf, R, (600, 200, 40), fp8_scale=scale, fp8_dynamic=dyn)
+    spec = spec_for(st, bs, S, sinkf, R, scale, dyn)
     done = 0
     for _ in range(14):
         s = int(rng.integers(0, 3))
