@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Qwen2.5-3B-shaped)")
     ap.add_argument("--decode-kernel", type=int, default=0, help="0 default, 1 vector ALU, 2 matrix cores")
+    ap.add_argument("--fp8-dynamic", action="store_true",
+                    help="FP8 pages with one scale per token and KV head instead of the static scale")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=0, help="0 = workload's own sample rule")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -74,7 +76,8 @@ def main():
                          head_dim=w.head_dim, block_size=w.block_size, max_seqs=w.n_seqs,
                          max_tokens_per_seq=w.max_len, sink_tokens=w.sink_tokens, sink_format=w.sink_format,
                          recent_tokens=w.recent_tokens, recent_format=w.recent_format,
-                         page_shuffle_seed=w.page_shuffle_seed, decode_kernel=args.decode_kernel)
+                         page_shuffle_seed=w.page_shuffle_seed, decode_kernel=args.decode_kernel,
+                         fp8_dynamic=int(args.fp8_dynamic))
     need = [0, 0, 0]
     bs = w.block_size
     for s in range(w.n_seqs):
@@ -179,7 +182,8 @@ def main():
                    "tokens_per_seq": list(sorted(set(w.lengths))) if len(set(w.lengths)) > 1 else w.lengths[0],
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "sink_tokens": w.sink_tokens, "window": w.window,
-                   "append_calls": len(calls), "input_sets": n_sets},
+                   "append_calls": len(calls), "input_sets": n_sets,
+                   "fp8": "dynamic per (token, head)" if args.fp8_dynamic else "static scale"},
         "quantize_pack": {"GBps": round(write_bytes / (write_ms * 1e-3) / 1e9, 1),
                           "hbm_frac": round(write_bytes / (write_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "bytes_per_step": write_bytes, "device_ms_per_step": round(write_ms, 4),
@@ -199,8 +203,8 @@ def main():
 
     if w.recent_tokens > 0 and w.recent_format == vk.FMT_FP8E4M3:
         cache.close()
-        result["retier"] = retier_leg(w, args.steps, args.warmup)
-        result["stream"] = stream_leg(w, args.steps, args.warmup)
+        result["retier"] = retier_leg(w, args.steps, args.warmup, args.fp8_dynamic)
+        result["stream"] = stream_leg(w, args.steps, args.warmup, fp8_dynamic=args.fp8_dynamic)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_sample_layers)
@@ -208,7 +212,7 @@ def main():
     cache.close()
 
 
-def retier_leg(w, steps, warmup):
+def retier_leg(w, steps, warmup, fp8_dynamic=False):
     """FP8 -> ternary retiering on the workload's shape: every sequence gets R tokens (all
     in FP8 pages but the sink page), then R more, so the first R tokens' pages leave the
     recent window; one vk_retier call over all sequences converts them.  Only that call
@@ -223,7 +227,7 @@ def retier_leg(w, steps, warmup):
     cfg = vk.make_config(n_layers=w.n_layers, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads,
                          head_dim=w.head_dim, block_size=bs, max_seqs=w.n_seqs, max_tokens_per_seq=2 * R,
                          sink_tokens=w.sink_tokens, sink_format=w.sink_format, recent_tokens=R,
-                         recent_format=vk.FMT_FP8E4M3)
+                         recent_format=vk.FMT_FP8E4M3, fp8_dynamic=int(fp8_dynamic))
     per_seq = -(-2 * R // bs)
     cfg.pages_ternary = per_seq * w.n_seqs
     cfg.pages_fp8 = per_seq * w.n_seqs
@@ -267,7 +271,7 @@ def retier_leg(w, steps, warmup):
                       f"{R} + {R} tokens appended, pages {n_sink}..{R // bs - 1} of every sequence retiered"}
 
 
-def stream_leg(w, steps, warmup, prefill=1024, window=512):
+def stream_leg(w, steps, warmup, prefill=1024, window=512, fp8_dynamic=False):
     """A bounded-memory serving loop on the workload's shape (its sequences, heads, head dim,
     block size, sinks and FP8 recent tier): after a prefill, every step appends one token
     to every sequence, evicts the pages between the sinks and the last `window` tokens
@@ -286,7 +290,7 @@ def stream_leg(w, steps, warmup, prefill=1024, window=512):
     cfg = vk.make_config(n_layers=1, n_kv_heads=w.n_kv_heads, n_q_heads=w.n_q_heads, head_dim=w.head_dim,
                          block_size=bs, max_seqs=w.n_seqs, max_tokens_per_seq=prefill + n_steps,
                          sink_tokens=w.sink_tokens, sink_format=w.sink_format, recent_tokens=w.recent_tokens,
-                         recent_format=vk.FMT_FP8E4M3)
+                         recent_format=vk.FMT_FP8E4M3, fp8_dynamic=int(fp8_dynamic))
     chunk = 64  # prefill chunk: retier and evict after each, as the loop does per token
     cfg.pages_ternary = (per_seq + chunk // bs) * w.n_seqs
     cfg.pages_fp8 = ((w.recent_tokens + chunk) // bs + 3) * w.n_seqs
