@@ -694,8 +694,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     const uint32_t hi = __builtin_amdgcn_readlane(in_cur ? cc.phi : cn.phi, in_cur ? k : k - CH);
     const uint8_t* pg = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
     const int upi = ((unit_of(lc) * 16) & (P.bs - 1)) >> 4;  // the dummy page takes any unit offset
+    // A copy for a unit past the wave's range is still issued (the ring's waits count on a
+    // fixed number of copies), with an empty record range: out of range, it reads no memory.
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, page_bytes0, kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, lu < u_end ? page_bytes0 : 0, kBufferWord3);
     const int soff = kvh * tile0 + upi * 4 * D;  // unit offset within the key (and value) tile
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)row, 16, dma_off, soff, 0, 0);
   };
