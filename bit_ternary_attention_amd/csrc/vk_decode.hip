@@ -775,10 +775,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = max_rows(mx);
-    // the mask is the same for every head: a group with no attended token adds nothing
-    if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) return;
-    if (__ballot(mx > m) != 0) {  // uniform; per-lane factors (lane = head)
+    // Lazy running max: m only has to stay within 1 (log2 units) of every score seen, so that
+    // p' = 2^(s - m + 14) <= 2^15 fits f16.  The max across the lane rows and the rescale run
+    // only when a score exceeds m + 1 (a uniform branch; m = -inf takes it for any score).
+    if (__ballot(mx > m + 1.0f) != 0) {
+      mx = max_rows(mx);
       const float mn = fmaxf(m, mx);
       const float corr = __builtin_amdgcn_exp2f(m - mn);  // m = -inf gives 0
 #pragma unroll
@@ -787,7 +788,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       tsum *= corr;
       m = mn;
     }
-    const float ms = m - 14.0f;  // p' = 2^(s - m + 14), at most 2^14
+    // nothing attended yet (this group included): it adds nothing, and m - 14 is not finite
+    if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, m)) == __builtin_bit_cast(int, -INFINITY)) return;
+    const float ms = m - 14.0f;  // p' = 2^(s - m + 14), at most 2^15
     uint32_t pk[UG][2];
 #pragma unroll
     for (int g = 0; g < UG; ++g) {
