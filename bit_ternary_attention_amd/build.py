@@ -27,6 +27,9 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wex
              "-D__HIP_PLATFORM_AMD__", "-I" + INCLUDE, "-I" + CSRC, "-I" + os.path.join(ROCM, "include")]
 
 HIP_SOURCES = ["vk_write.hip", "vk_decode.hip", "vk_retier.hip"]
+# per-source flags: the decode kernels never produce or consume NaN (masked scores are -inf),
+# so float max needs no NaN quieting (otherwise each fmaxf operand is canonicalised first)
+HIP_SOURCE_FLAGS = {"vk_decode.hip": ["-fno-honor-nans"]}
 CXX_SOURCES = ["host_state.cpp", "vk_api.cpp"]
 
 
@@ -47,7 +50,7 @@ def build_library(verbose: bool = False) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        jobs.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIP_FLAGS, *HIP_SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
@@ -66,7 +69,8 @@ def build_library(verbose: bool = False) -> str:
 def asm(source: str, out: str) -> None:
     """Writes the gfx950 assembly of one kernel source (for inspection)."""
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
-    _run([hipcc, *HIP_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, source), "-o", out], True)
+    _run([hipcc, *HIP_FLAGS, *HIP_SOURCE_FLAGS.get(source, []), "--cuda-device-only", "-S", os.path.join(CSRC, source),
+          "-o", out], True)
 
 
 if __name__ == "__main__":
