@@ -10,6 +10,10 @@
       <kernel-filter> <workload> <out.json> <source>...
       the traffic of one kernel as a JSON record, with the SHA-256 of the sources it was
       built from (a reader can tell whether the kernel has changed since)
+  python -m bit_ternary_attention_amd.profsum calls <results.db> <name-filter>
+      per-call durations of the matching kernels, in launch order
+  --largest (traffic, record): average only each kernel's dispatches that fetch at least
+      90% of its largest one (one launch size out of a run that mixes several)
 """
 import csv
 import hashlib
@@ -37,23 +41,26 @@ def trace(db_path: str, name_filter: str = "vk::"):
 
 
 def short(name: str) -> str:
-    for junk in ("vk::(anonymous namespace)::", "(vk::AppendArgs)", "(vk::DecodeArgs)", "(vk::QuantArgs)"):
+    for junk in ("vk::(anonymous namespace)::", "(vk::AppendArgs)", "(vk::DecodeArgs)", "(vk::QuantArgs)",
+                 "(vk::RetierArgs)"):
         name = name.replace(junk, "")
     return name
 
 
-def _counter(path: str, counter: str):
+def _counter(path: str, counter: str, largest: bool = False):
     per = {}
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
         per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    if largest:
+        per = {k: [x for x in v if x >= 0.9 * max(v)] for k, v in per.items()}
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
-def traffic(fetch_csv: str, write_csv: str, calib_name: str, calib_bytes: float):
-    fetch, n_f = _counter(fetch_csv, "FETCH_SIZE")
-    write, _ = _counter(write_csv, "WRITE_SIZE")
+def traffic(fetch_csv: str, write_csv: str, calib_name: str, calib_bytes: float, largest: bool = False):
+    fetch, n_f = _counter(fetch_csv, "FETCH_SIZE", largest)
+    write, _ = _counter(write_csv, "WRITE_SIZE", largest)
     cf = [v for k, v in fetch.items() if calib_name in k]
     cw = [v for k, v in write.items() if calib_name in k]
     if not cf or not cw:
@@ -80,6 +87,8 @@ def sources_sha256(paths):
 
 
 def main():
+    largest = "--largest" in sys.argv
+    sys.argv = [a for a in sys.argv if a != "--largest"]
     mode = sys.argv[1]
     if mode == "trace":
         filt = sys.argv[3] if len(sys.argv) > 3 else "vk::"
@@ -87,7 +96,7 @@ def main():
         for name, n, tot, avg, mn, mx in trace(sys.argv[2], filt):
             print(f"{short(name)[:70]:70s} {n:6d} {tot:10.1f} {avg:9.3f} {mn:9.3f} {mx:9.3f}")
     elif mode == "traffic":
-        f_scale, w_scale, rows = traffic(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5]))
+        f_scale, w_scale, rows = traffic(sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5]), largest)
         print(f"calibration: FETCH_SIZE reads {f_scale:.5f} and WRITE_SIZE {w_scale:.5f} of the copied bytes")
         print(f"{'kernel':70s} {'n':>4s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'HBM bytes/dispatch':>20s}")
         for k, n, fk, wk, hbm in rows:
@@ -96,7 +105,7 @@ def main():
     elif mode == "record":
         fetch_csv, write_csv, calib, cbytes, kfilt, workload, out = sys.argv[2:9]
         srcs = sys.argv[9:]
-        f_scale, w_scale, rows = traffic(fetch_csv, write_csv, calib, float(cbytes))
+        f_scale, w_scale, rows = traffic(fetch_csv, write_csv, calib, float(cbytes), largest)
         hit = [r for r in rows if kfilt in r[0]]
         if not hit:
             raise SystemExit(f"kernel '{kfilt}' not found")
@@ -111,6 +120,11 @@ def main():
         with open(out, "w") as f:
             json.dump(rec, f, indent=1, sort_keys=True)
         print(json.dumps(rec[f"{kind}|{workload}"], indent=1))
+    elif mode == "calls":
+        db = sqlite3.connect(sys.argv[2])
+        rows = db.execute("select name, duration from kernels order by start").fetchall()
+        durs = [d / 1e3 for n, d in rows if sys.argv[3] in n]
+        print(f"{len(durs)} calls of '{sys.argv[3]}' (us, launch order): " + " ".join(f"{d:.2f}" for d in durs))
     else:
         raise SystemExit(__doc__)
 
