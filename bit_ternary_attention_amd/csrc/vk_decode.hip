@@ -525,7 +525,7 @@ __device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], cons
 }
 
 template <int D, int G, int QDT, int PF, bool DYN>
-__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(4, 8))) void k_decode_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_decode_mfma(DecodeArgs a) {
   constexpr int NC = D / 64;   // 32-bit key code words per lane per unit
   constexpr int NV = D / 64;   // 32-bit value chunk words per lane per unit
   constexpr int NS = D / 32;   // 16x16x32 steps per unit of the score product
@@ -610,6 +610,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int32_t ent;
     float gk, gv;
     uint32_t plo, phi;
+    bool clean;     // every unit ternary, fully attended, with the chunk's one gamma pair
+    float gk0, gv0;  // that gamma pair (uniform)
   };
   auto load_chunk = [&](int c0) -> Chunk {
     const int lu = min(c0 + lane, u_last);
@@ -624,6 +626,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                              : reinterpret_cast<uint64_t>(P.dummy_page);
     c.plo = static_cast<uint32_t>(pg);
     c.phi = static_cast<uint32_t>(pg >> 32);
+    c.gk0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.gk)));
+    c.gv0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.gv)));
+    const int u = unit_of(lu);
+    const bool full = R.single ? u * 16 + 16 <= L : (u * 16 + 16 <= R.sinks || (u * 16 >= R.w0 && u * 16 + 16 <= L));
+    c.clean = __ballot(!(tern && full && c.gk == c.gk0 && c.gv == c.gv0)) == 0;
     return c;
   };
   auto lane_f = [](float x, int k) {
@@ -723,6 +730,63 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       for (int j = 0; j < NB; ++j) oacc[j] *= ratio;
       tsum *= ratio;
       vcur = vs;
+    }
+  };
+
+  // Two units of a clean chunk (both ternary, every token attended, one gamma pair): the
+  // same steps as process_group below without the per-unit checks.
+  auto process_group_clean = [&](const Chunk& cc, const UnitRaw<NC, NV>& r0, const UnitRaw<NC, NV>& r1) {
+    const float ks = cc.gk0 * a.scale_log2;
+    const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
+    float sc[UG][4];
+#pragma unroll
+    for (int g = 0; g < UG; ++g) {
+      h8_t ka[NS];
+      ka_ternary<NS, NC>(g == 0 ? r0.k : r1.k, ka, oc);
+      f4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[st], qb[st], s4, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    if (__ballot(mx > m + 1.0f) != 0) {  // lazy running max, as in process_group
+      mx = max_rows(mx);
+      const float mn = fmaxf(m, mx);
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) oacc[j] *= corr;
+      lsum *= corr;
+      tsum *= corr;
+      m = mn;
+    }
+    const float ms = m - 14.0f;
+    uint32_t pk[UG][2];
+#pragma unroll
+    for (int g = 0; g < UG; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const h2_t p2 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h] - ms)),
+                         static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h + 1] - ms))};
+        pk[g][h] = h2u(p2);
+        lsum = __builtin_amdgcn_fdot2(p2, ones, lsum, false);
+      }
+    if (cc.gv0 == 0.0f) return;  // every value of these pages is 0
+    set_value_scale(cc.gv0);
+#pragma unroll
+    for (int g = 0; g < UG; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][h]), ones, tsum, false);
+    const h8_t pb = __builtin_bit_cast(h8_t, u4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
+    h4_t v0[NB], v1[NB];
+    va_all<NV, NB>(vwords<NV>(r0.v), v0, oc);
+    va_all<NV, NB>(vwords<NV>(r1.v), v1, oc);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const u2_t x0 = __builtin_bit_cast(u2_t, v0[j]), x1 = __builtin_bit_cast(u2_t, v1[j]);
+      const h8_t av = __builtin_bit_cast(h8_t, u4_t{x0[0], x0[1], x1[0], x1[1]});
+      oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, oacc[j], 0, 0, 0);
     }
   };
 
@@ -1024,31 +1088,41 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     make_qb();
     for (int c0 = u_begin; c0 < u_end; c0 += CH) {
       const int c_end = min(c0 + CH, u_end);
+      // a clean chunk whose units all lie in the range runs a loop without per-unit checks
+      const bool clean = ch_cur.clean && ((c_end - c0) & 1) == 0;
+      auto run = [&](auto CLEAN) {
 #pragma unroll 1
-      for (int k = c0; k < c_end; k += NR) {
-        auto step = [&](auto GI) {
-          constexpr int gi = decltype(GI)::value;
-          // The copies into slots 2 gi and 2 gi + 1 have landed: at most NR - 2 ring copies
-          // were issued after them (vector memory returns in issue order; any other load
-          // in between only makes this wait stricter).  The compiler's own wait counting does
-          // not follow buffer-to-LDS copies into every ring array, so the wait is explicit.
-          __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
-          UnitRaw<NC, NV> r0, r1;
-          read_unit(ring_row(integral_constant<int, 2 * gi>{}), r0);
-          read_unit(ring_row(integral_constant<int, 2 * gi + 1>{}), r1);
-          process_group(k + 2 * gi, ch_cur, c0, r0, r1);
-          // the slot reads have returned before their rows are overwritten
-          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-          dma_unit(k + NR + 2 * gi, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi>{}));
-          dma_unit(k + NR + 2 * gi + 1, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi + 1>{}));
-        };
-        step(integral_constant<int, 0>{});
-        step(integral_constant<int, 1>{});
-        if constexpr (NR == 8) {
-          step(integral_constant<int, 2>{});
-          step(integral_constant<int, 3>{});
+        for (int k = c0; k < c_end; k += NR) {
+          auto step = [&](auto GI) {
+            constexpr int gi = decltype(GI)::value;
+            // The copies into slots 2 gi and 2 gi + 1 have landed: at most NR - 2 ring copies
+            // were issued after them (vector memory returns in issue order; any other load
+            // in between only makes this wait stricter).  The compiler's own wait counting
+            // does not follow buffer-to-LDS copies into every ring array, so the wait is explicit.
+            __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
+            UnitRaw<NC, NV> r0, r1;
+            read_unit(ring_row(integral_constant<int, 2 * gi>{}), r0);
+            read_unit(ring_row(integral_constant<int, 2 * gi + 1>{}), r1);
+            if constexpr (decltype(CLEAN)::value) {
+              if (k + 2 * gi < c_end) process_group_clean(ch_cur, r0, r1);
+            } else {
+              process_group(k + 2 * gi, ch_cur, c0, r0, r1);
+            }
+            // the slot reads have returned before their rows are overwritten
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            dma_unit(k + NR + 2 * gi, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi>{}));
+            dma_unit(k + NR + 2 * gi + 1, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi + 1>{}));
+          };
+          step(integral_constant<int, 0>{});
+          step(integral_constant<int, 1>{});
+          if constexpr (NR == 8) {
+            step(integral_constant<int, 2>{});
+            step(integral_constant<int, 3>{});
+          }
         }
-      }
+      };
+      if (clean) run(integral_constant<bool, true>{});
+      else run(integral_constant<bool, false>{});
       ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
       ch_nxt = load_chunk(c0 + 2 * CH);
     }
