@@ -533,7 +533,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int CH = 64;       // units per metadata chunk (one per lane)
   constexpr int UG = 2;        // units sharing one online-softmax update and one P*V product
   static_assert(G <= 16, "one query head per lane column");
-  static_assert(CH % PF == 0 && PF % UG == 0, "chunks hold whole prefetch rounds and groups");
+  // Column slots: the query heads are repeated over the 16 columns of the score product, in
+  // NSL slots of W columns.  A clean step puts one unit's scores in each slot, so its softmax
+  // steps cover NSL units at once; the other paths keep their sums in slot 0 only.
+  constexpr int W = G < 4 ? 4 : G;       // columns per slot
+  constexpr int NSL = 16 / W;            // 4 (G <= 4), 2 (G = 8) or 1 (G = 16)
+  constexpr int SU = NSL == 4 ? 4 : 2;   // units per clean step
+  static_assert(CH % PF == 0 && PF % UG == 0 && PF % SU == 0, "chunks hold whole prefetch rounds and groups");
   __shared__ float lds_m[kMfmaWaves][G], lds_l[kMfmaWaves][G];
   // LDS ring: NR slots per wave, each one unit's key tile then value tile (8 D bytes), filled
   // by buffer-to-LDS loads.  One array per slot, so the compiler's wait counting can tell
@@ -549,6 +555,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // wave-uniform indices live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63, grp = lane >> 4, c16 = lane & 15;
+  const int cslot = c16 / W;  // this lane's column slot
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int slot = a.slots[b], L = a.lens[b];
   const PoolsView& P = a.P;
@@ -637,12 +644,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), k));
   };
 
-  // Query head c16 (zero beyond the group) as the B operand of the score product: f16
-  // pairs (d, d+8) of each 16-dimension block.  For ternary codes in offset form the logit
+  // Query head c16 mod G as the B operand of the score product: f16 pairs (d, d+8) of each
+  // 16-dimension block.  For ternary codes in offset form the logit
   // is ks (2^14 acc - qoff), qoff = 2^14 sum_d off(d) q_d + sum_d q_d.
   h8_t qb[NS];
   float qsum = 0.0f, qoff = 0.0f;
-  const uint16_t* qhead = a.q + (qo0 + (c16 < G ? c16 : 0)) * D;
+  const uint16_t* qhead = a.q + (qo0 + (c16 & (G - 1))) * D;
   auto make_qb = [&]() {
     const uint16_t* qrow = qhead + dbase;
     uint32_t w[NS][4];
@@ -656,8 +663,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       for (int i = 0; i < 8; ++i) {
         const uint32_t e0 = (lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const uint32_t e1 = (hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t pr =
-            c16 < G ? (q_f16<QDT>(static_cast<uint16_t>(e0)) | (q_f16<QDT>(static_cast<uint16_t>(e1)) << 16)) : 0u;
+        const uint32_t pr = q_f16<QDT>(static_cast<uint16_t>(e0)) | (q_f16<QDT>(static_cast<uint16_t>(e1)) << 16);
         w[2 * c + (i >> 2)][i & 3] = pr;
         const h2_t hp = as_h2(pr);
         sum += static_cast<float>(hp[0]) + static_cast<float>(hp[1]);
@@ -733,26 +739,51 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  // Two units of a clean chunk (both ternary, every token attended, one gamma pair): the
-  // same steps as process_group below without the per-unit checks.
-  auto process_group_clean = [&](const Chunk& cc, const UnitRaw<NC, NV>& r0, const UnitRaw<NC, NV>& r1) {
+  // max over the slots of each head (lanes c16, c16 ^ W, ...; the rows are already merged)
+  auto max_slots = [&](float x) {
+#pragma unroll
+    for (int o = W; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+  };
+  // probabilities of the general paths count in slot 0 only (the other slots repeat its heads)
+  auto slot0 = [&](uint32_t p) { return NSL == 1 || cslot == 0 ? p : 0u; };
+
+  // One clean step: SU units of a clean chunk (every unit ternary, every token attended, one
+  // gamma pair), with the steps of process_group below and no per-unit checks.  With NSL > 1
+  // the score tiles of NSL units merge into one, unit i in slot i, so the softmax runs once
+  // for them; P*V then gives each unit's probabilities only to its own slot's columns (a
+  // block-diagonal B operand) and the slots are summed when the wave ends.
+  auto process_clean = [&](const Chunk& cc, const UnitRaw<NC, NV> (&r)[SU]) {
+    constexpr int UT = NSL == 1 ? 1 : NSL;  // units per score tile
+    constexpr int NT = SU / UT;             // score tiles
     const float ks = cc.gk0 * a.scale_log2;
     const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
-    float sc[UG][4];
+    float sc[NT][4];
 #pragma unroll
-    for (int g = 0; g < UG; ++g) {
-      h8_t ka[NS];
-      ka_ternary<NS, NC>(g == 0 ? r0.k : r1.k, ka, oc);
-      f4_t s4 = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) {
+      f4_t tile;
 #pragma unroll
-      for (int st = 0; st < NS; ++st) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[st], qb[st], s4, 0, 0, 0);
+      for (int i = 0; i < UT; ++i) {
+        h8_t ka[NS];
+        ka_ternary<NS, NC>(r[t * UT + i].k, ka, oc);
+        f4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
+        for (int st = 0; st < NS; ++st) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[st], qb[st], s4, 0, 0, 0);
+        if (i == 0) {
+          tile = s4;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) tile[q] = cslot == i ? s4[q] : tile[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sc[t][q] = fmaf(tile[q], a0, a1);
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mx = fmaxf(mx, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
     if (__ballot(mx > m + 1.0f) != 0) {  // lazy running max, as in process_group
-      mx = max_rows(mx);
+      mx = max_slots(max_rows(mx));
       const float mn = fmaxf(m, mx);
       const float corr = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
@@ -762,31 +793,41 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       m = mn;
     }
     const float ms = m - 14.0f;
-    uint32_t pk[UG][2];
+    uint32_t pk[NT][2];
 #pragma unroll
-    for (int g = 0; g < UG; ++g)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const h2_t p2 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h] - ms)),
-                         static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h + 1] - ms))};
-        pk[g][h] = h2u(p2);
+        const h2_t p2 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[t][2 * h] - ms)),
+                         static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[t][2 * h + 1] - ms))};
+        pk[t][h] = h2u(p2);
         lsum = __builtin_amdgcn_fdot2(p2, ones, lsum, false);
       }
     if (cc.gv0 == 0.0f) return;  // every value of these pages is 0
     set_value_scale(cc.gv0);
 #pragma unroll
-    for (int g = 0; g < UG; ++g)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][h]), ones, tsum, false);
-    const h8_t pb = __builtin_bit_cast(h8_t, u4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
-    h4_t v0[NB], v1[NB];
-    va_all<NV, NB>(vwords<NV>(r0.v), v0, oc);
-    va_all<NV, NB>(vwords<NV>(r1.v), v1, oc);
+      for (int h = 0; h < 2; ++h) tsum = __builtin_amdgcn_fdot2(as_h2(pk[t][h]), ones, tsum, false);
+    // P*V, two units per 16x16x32 product: unit u's probabilities sit in tile u / UT, and
+    // with slots only the lanes of slot u % UT pass them on
+    auto pvals = [&](int u, int h) {
+      const uint32_t x = pk[u / UT][h];
+      return UT == 1 || cslot == u % UT ? x : 0u;
+    };
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const u2_t x0 = __builtin_bit_cast(u2_t, v0[j]), x1 = __builtin_bit_cast(u2_t, v1[j]);
-      const h8_t av = __builtin_bit_cast(h8_t, u4_t{x0[0], x0[1], x1[0], x1[1]});
-      oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, oacc[j], 0, 0, 0);
+    for (int s2 = 0; s2 < SU / 2; ++s2) {
+      const h8_t pb = __builtin_bit_cast(
+          h8_t, u4_t{pvals(2 * s2, 0), pvals(2 * s2, 1), pvals(2 * s2 + 1, 0), pvals(2 * s2 + 1, 1)});
+      h4_t v0[NB], v1[NB];
+      va_all<NV, NB>(vwords<NV>(r[2 * s2].v), v0, oc);
+      va_all<NV, NB>(vwords<NV>(r[2 * s2 + 1].v), v1, oc);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const u2_t x0 = __builtin_bit_cast(u2_t, v0[j]), x1 = __builtin_bit_cast(u2_t, v1[j]);
+        const h8_t av = __builtin_bit_cast(h8_t, u4_t{x0[0], x0[1], x1[0], x1[1]});
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, oacc[j], 0, 0, 0);
+      }
     }
   };
 
@@ -862,8 +903,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       for (int h = 0; h < 2; ++h) {
         const h2_t p2 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h] - ms)),
                          static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[g][2 * h + 1] - ms))};
-        pk[g][h] = h2u(p2);
-        lsum = __builtin_amdgcn_fdot2(p2, ones, lsum, false);
+        pk[g][h] = slot0(h2u(p2));
+        lsum = __builtin_amdgcn_fdot2(as_h2(pk[g][h]), ones, lsum, false);
       }
     }
     if (tern[0] && tern[1] && vs[0] == vs[1]) {
@@ -1037,10 +1078,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                           static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[1] - ms))};
         const h2_t p23 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[2] - ms)),
                           static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[3] - ms))};
-        h2_t q01 = p01, q23 = p23;
+        h2_t q01 = as_h2(slot0(h2u(p01))), q23 = as_h2(slot0(h2u(p23)));
         if constexpr (!DYN) {
-          lsum = __builtin_amdgcn_fdot2(p01, ones, lsum, false);
-          lsum = __builtin_amdgcn_fdot2(p23, ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2(q01, ones, lsum, false);
+          lsum = __builtin_amdgcn_fdot2(q23, ones, lsum, false);
         } else {
           // each token's value scale relative to the unit's largest; the sum takes each weight
           // as P*V sees it (the f16 product divided back by the ratio) so both round alike
@@ -1051,10 +1092,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
           for (int r = 0; r < 4; ++r) {
             qh[r] = static_cast<_Float16>(pf[r] * prt[r]);
             const float qr = static_cast<float>(qh[r]);  // below the f16 normal range: unrounded
-            lsum += qr >= 0x1p-14f ? qr / prt[r] : pf[r];
+            if (NSL == 1 || cslot == 0) lsum += qr >= 0x1p-14f ? qr / prt[r] : pf[r];
           }
-          q01 = h2_t{qh[0], qh[1]};
-          q23 = h2_t{qh[2], qh[3]};
+          q01 = as_h2(slot0(h2u(h2_t{qh[0], qh[1]})));
+          q23 = as_h2(slot0(h2u(h2_t{qh[2], qh[3]})));
         }
         const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(q01), h2u(q23)});
         const float vs14 = vscale * (1.0f / 16384.0f);
@@ -1089,33 +1130,42 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     for (int c0 = u_begin; c0 < u_end; c0 += CH) {
       const int c_end = min(c0 + CH, u_end);
       // a clean chunk whose units all lie in the range runs a loop without per-unit checks
-      const bool clean = ch_cur.clean && ((c_end - c0) & 1) == 0;
+      const bool clean = ch_cur.clean && ((c_end - c0) % SU) == 0;
       auto run = [&](auto CLEAN) {
+        constexpr int S = decltype(CLEAN)::value ? SU : UG;  // units per step
 #pragma unroll 1
         for (int k = c0; k < c_end; k += NR) {
           auto step = [&](auto GI) {
             constexpr int gi = decltype(GI)::value;
-            // The copies into slots 2 gi and 2 gi + 1 have landed: at most NR - 2 ring copies
-            // were issued after them (vector memory returns in issue order; any other load
-            // in between only makes this wait stricter).  The compiler's own wait counting
-            // does not follow buffer-to-LDS copies into every ring array, so the wait is explicit.
-            __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
-            UnitRaw<NC, NV> r0, r1;
-            read_unit(ring_row(integral_constant<int, 2 * gi>{}), r0);
-            read_unit(ring_row(integral_constant<int, 2 * gi + 1>{}), r1);
+            UnitRaw<NC, NV> r[S];
+            // Slots are taken two at a time: wait until their copies have landed (at most
+            // NR - 2 ring copies were issued after them; vector memory returns in issue order
+            // and any other load in between only makes the wait stricter; the compiler's own
+            // wait counting does not follow buffer-to-LDS copies into every ring array), read
+            // them into registers, and refill them with the units NR ahead before any compute.
+            auto take2 = [&](auto H) {
+              constexpr int i = 2 * decltype(H)::value;  // first unit of the pair in this step
+              if constexpr (i < S) {
+                __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
+                read_unit(ring_row(integral_constant<int, S * gi + i>{}), r[i]);
+                read_unit(ring_row(integral_constant<int, S * gi + i + 1>{}), r[i + 1]);
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot reads have returned
+                dma_unit(k + NR + S * gi + i, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, S * gi + i>{}));
+                dma_unit(k + NR + S * gi + i + 1, ch_cur, ch_nxt, c0,
+                         ring_row(integral_constant<int, S * gi + i + 1>{}));
+              }
+            };
+            take2(integral_constant<int, 0>{});
+            take2(integral_constant<int, 1>{});
             if constexpr (decltype(CLEAN)::value) {
-              if (k + 2 * gi < c_end) process_group_clean(ch_cur, r0, r1);
+              if (k + S * gi < c_end) process_clean(ch_cur, r);
             } else {
-              process_group(k + 2 * gi, ch_cur, c0, r0, r1);
+              process_group(k + S * gi, ch_cur, c0, r[0], r[1]);
             }
-            // the slot reads have returned before their rows are overwritten
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            dma_unit(k + NR + 2 * gi, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi>{}));
-            dma_unit(k + NR + 2 * gi + 1, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, 2 * gi + 1>{}));
           };
           step(integral_constant<int, 0>{});
-          step(integral_constant<int, 1>{});
-          if constexpr (NR == 8) {
+          if constexpr (NR / S >= 2) step(integral_constant<int, 1>{});
+          if constexpr (NR / S >= 4) {
             step(integral_constant<int, 2>{});
             step(integral_constant<int, 3>{});
           }
@@ -1141,6 +1191,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   lsum += __shfl_xor(lsum, 32, 64);
   tsum += __shfl_xor(tsum, 16, 64);
   tsum += __shfl_xor(tsum, 32, 64);
+  // sum the slots: each head's columns hold the units of its own clean steps
+#pragma unroll
+  for (int o = W; o < 16; o <<= 1) {
+    lsum += __shfl_xor(lsum, o, 64);
+    tsum += __shfl_xor(tsum, o, 64);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) oacc[j][r] += __shfl_xor(oacc[j][r], o, 64);
+  }
   if (c16 < G) {
     constexpr float kInv = 1.0f / 16384.0f;
 #pragma unroll
