@@ -93,11 +93,14 @@ UnitRanges attended_units(int32_t length, int32_t sink_tokens, int32_t window) {
 }
 
 SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blocks, int32_t max_splits,
-                      int32_t min_units) {
+                      int32_t min_units, int32_t granule) {
   if (max_units <= 0) return {1, 1};
   const int64_t want = std::max<int64_t>(std::max(1, min_units), cdiv(total_units, std::max(1, target_blocks)));
   const int64_t n = std::min<int64_t>(std::max<int64_t>(1, cdiv(max_units, want)), std::max(1, max_splits));
-  return {static_cast<int32_t>(n), static_cast<int32_t>(cdiv(max_units, n))};
+  // split size rounded up to the granule (whole kernel steps per wave); fewer splits may then do
+  const int64_t g = std::max(1, granule);
+  const int64_t ups = cdiv(cdiv(max_units, n), g) * g;
+  return {static_cast<int32_t>(cdiv(max_units, ups)), static_cast<int32_t>(ups)};
 }
 
 HostState::HostState(const vk_cache_config& cfg) : cfg_(cfg) {

@@ -98,7 +98,7 @@ struct SplitPlan {
   int32_t units_per_split;
 };
 SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blocks, int32_t max_splits,
-                      int32_t min_units);
+                      int32_t min_units, int32_t granule = 1);
 
 class HostState {
  public:

@@ -39,6 +39,8 @@ constexpr int kDecodeTargetGroups = 4096;  // work groups a decode launch aims f
 constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMinUnits = 4;         // 16-token units per split, at least (vector-ALU kernel)
 constexpr int kDecodeMinUnitsPerWave = 8;  // matrix-core kernel: units per wave, at least
+constexpr int kDecodeUnitsPerStep = 4;     // matrix-core kernel: units per clean step, at most (a wave's
+                                           // range is a whole number of them when the split size is)
 constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
 constexpr int64_t kDecodeTargetBlocks = 1024;   // matrix-core decode blocks per launch (one round of 4 per CU)
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
@@ -534,7 +536,8 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     // ones (a block past a sequence's units writes an empty part).
     const int64_t all_units = (cu[0] + cu[1] + cu[2]) * cfg.n_kv_heads;
     const vk::SplitPlan sp = mfma ? vk::plan_splits(all_units, max_units, kDecodeTargetBlocks,
-                                                    std::max(1, max_splits), 4 * kDecodeMinUnitsPerWave)
+                                                    std::max(1, max_splits), 4 * kDecodeMinUnitsPerWave,
+                                                    4 * kDecodeUnitsPerStep)
                                   : vk::plan_splits(all_units, max_units, kDecodeTargetGroups,
                                                     std::max(1, max_splits), kDecodeMinUnits);
     a.n_splits = sp.n_splits;

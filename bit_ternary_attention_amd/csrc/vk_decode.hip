@@ -612,7 +612,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // Per-chunk unit metadata, one unit per lane (lanes past the end repeat the last unit):
   // block-table entry, the K and V gamma of ternary pages, and the address of the page the
   // codes are read from (the zeroed dummy page for other formats).  Page addresses are
-  // computed here, per lane, once per 64 units; a unit takes them with readlane.
+  // computed here, per lane, once per 64 units; a unit takes them with readlane.  The copies
+  // need only the addresses; the gamma values are first waited for by chunk_flags.
   struct Chunk {
     int32_t ent;
     float gk, gv;
@@ -633,12 +634,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
                              : reinterpret_cast<uint64_t>(P.dummy_page);
     c.plo = static_cast<uint32_t>(pg);
     c.phi = static_cast<uint32_t>(pg >> 32);
+    return c;
+  };
+  auto chunk_flags = [&](Chunk& c, int c0) {
+    const int lu = min(c0 + lane, u_last);
+    const bool tern = (static_cast<uint32_t>(c.ent) >> 30) == VK_FMT_TERNARY2;
     c.gk0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.gk)));
     c.gv0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.gv)));
     const int u = unit_of(lu);
     const bool full = R.single ? u * 16 + 16 <= L : (u * 16 + 16 <= R.sinks || (u * 16 >= R.w0 && u * 16 + 16 <= L));
     c.clean = __ballot(!(tern && full && c.gk == c.gk0 && c.gv == c.gv0)) == 0;
-    return c;
   };
   auto lane_f = [](float x, int k) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), k));
@@ -1110,12 +1115,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
 
   if (!mixed_part && u_begin < u_end) {
     // ring slot s holds unit k + s while the group of slots (2i, 2i + 1) is processed; a
-    // processed slot is refilled with the unit NR ahead.  The query set-up overlaps the
-    // first copies.
+    // processed slot is refilled with the unit NR ahead.  The first copies go out as soon as
+    // the first chunk's block-table entries are in (they lie in that chunk); the next chunk's
+    // metadata and the query set-up follow while they are in flight.
     using std::integral_constant;
     Chunk ch_cur = load_chunk(u_begin);
-    Chunk ch_nxt = load_chunk(u_begin + CH);
-    auto prologue = [&](auto I) { dma_unit(u_begin + decltype(I)::value, ch_cur, ch_nxt, u_begin, ring_row(I)); };
+    auto prologue = [&](auto I) { dma_unit(u_begin + decltype(I)::value, ch_cur, ch_cur, u_begin, ring_row(I)); };
     prologue(integral_constant<int, 0>{});
     prologue(integral_constant<int, 1>{});
     prologue(integral_constant<int, 2>{});
@@ -1126,9 +1131,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       prologue(integral_constant<int, 6>{});
       prologue(integral_constant<int, 7>{});
     }
+    // (no next chunk: the copies never select it, and it stays a copy of the current one)
+    Chunk ch_nxt = u_begin + CH < u_end ? load_chunk(u_begin + CH) : ch_cur;
     make_qb();
     for (int c0 = u_begin; c0 < u_end; c0 += CH) {
       const int c_end = min(c0 + CH, u_end);
+      chunk_flags(ch_cur, c0);
       // a clean chunk whose units all lie in the range runs a loop without per-unit checks
       const bool clean = ch_cur.clean && ((c_end - c0) % SU) == 0;
       auto run = [&](auto CLEAN) {
@@ -1174,7 +1182,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       if (clean) run(integral_constant<bool, true>{});
       else run(integral_constant<bool, false>{});
       ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
-      ch_nxt = load_chunk(c0 + 2 * CH);
+      if (c0 + 2 * CH < u_end) ch_nxt = load_chunk(c0 + 2 * CH);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy into the ring is left in flight
   }

@@ -102,9 +102,9 @@ void hs_attended_units(int length, int sinks, int window, int* out3) {
   out3[2] = r.b_end;
 }
 
-int hs_plan_splits(long long total_units, int max_units, int target, int max_splits, int min_units,
+int hs_plan_splits(long long total_units, int max_units, int target, int max_splits, int min_units, int granule,
                    int* units_per_split) {
-  const vk::SplitPlan p = vk::plan_splits(total_units, max_units, target, max_splits, min_units);
+  const vk::SplitPlan p = vk::plan_splits(total_units, max_units, target, max_splits, min_units, granule);
   *units_per_split = p.units_per_split;
   return p.n_splits;
 }

@@ -110,7 +110,7 @@ def hs():
     L.hs_evict.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), ctypes.c_int, P(ctypes.c_longlong)]
     L.hs_check_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), ctypes.c_int]
     L.hs_plan_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                 ctypes.POINTER(ctypes.c_int)]
+                                 ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     return L
 
 
@@ -279,9 +279,9 @@ def test_route_counters_match_page_formats(hs):
         assert list(out) == want, W
 
 
-def _plan(hs, total, max_units, target, max_splits, min_units):
+def _plan(hs, total, max_units, target, max_splits, min_units, granule=1):
     ups = ctypes.c_int(0)
-    n = hs.hs_plan_splits(total, max_units, target, max_splits, min_units, ctypes.byref(ups))
+    n = hs.hs_plan_splits(total, max_units, target, max_splits, min_units, granule, ctypes.byref(ups))
     return n, ups.value
 
 
@@ -296,8 +296,13 @@ def test_split_plan(hs):
     n, ups = _plan(hs, 8 * (1024 + 64), 1024, 64, 64, 8)
     assert (n, ups) == (8, 128)  # 136 wanted; 8 splits then cover 1024 units with 128 each
     for total, mx, tgt, cap, mn in [(1, 1, 2048, 64, 32), (10**7, 12345, 2048, 64, 32), (500, 7, 4096, 3, 4)]:
-        n, ups = _plan(hs, total, mx, tgt, cap, mn)
-        assert 1 <= n <= cap and n * ups >= mx and (n - 1) * ups < mx
+        for gr in (1, 16):
+            n, ups = _plan(hs, total, mx, tgt, cap, mn, gr)
+            assert 1 <= n <= cap and n * ups >= mx and (n - 1) * ups < mx and ups % gr == 0
+    # granule: 32 x 8 x 2048 units in 768 blocks wants 683-unit splits; rounded to 688 (3 splits)
+    assert _plan(hs, 32 * 8 * 2048, 2048, 768, 64, 32) == (3, 683)
+    assert _plan(hs, 32 * 8 * 2048, 2048, 768, 64, 32, 16) == (3, 688)
+    assert _plan(hs, 2 * 17, 17, 2048, 64, 32, 16) == (1, 32)  # 17 units round up to one 32-unit split
 
 
 @pytest.mark.parametrize("bs,S,sinkf,R", [(16, 4, 2, 256), (16, 4, 1, 16), (32, 40, 2, 33), (64, 0, 0, 100)])
