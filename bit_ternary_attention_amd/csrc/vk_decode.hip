@@ -1188,35 +1188,45 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   }
 
   // ---------------- this wave's partial state -> LDS ----------------
-  // (the G x D outputs of wave w go to ring array w, free once every wave has left its loop)
+  // (the G x D outputs of wave w go to ring array w, free once every wave has left its loop;
+  // dimension d of head h sits at h D + swz(h, d): the XOR spreads the heads' rows, written
+  // by lanes of one column each, over the LDS banks)
   static_assert(G * D * 4 <= kMfmaWaves * RB, "a wave's outputs fit one ring array");
   auto out_row = [&](int w) -> float* {
     uint8_t* r = w == 0 ? &ring0[0][0] : w == 1 ? &ring1[0][0] : w == 2 ? &ring2[0][0] : &ring3[0][0];
     return reinterpret_cast<float*>(r);
   };
+  auto swz = [](int h, int d) { return d ^ ((h & 7) << 2); };  // stays in d's 32-float block
   __syncthreads();
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   tsum += __shfl_xor(tsum, 16, 64);
   tsum += __shfl_xor(tsum, 32, 64);
-  // sum the slots: each head's columns hold the units of its own clean steps
+  // sum the slots (each head's columns hold the units of its own clean steps) with row
+  // rotations: after rotating by 8 a lane holds the sum over columns c16 and c16 ^ 8, and a
+  // rotation by 4 of that sum then covers all four slots
+  auto slot_sum = [](float x) {
+    if constexpr (NSL >= 2)
+      x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    if constexpr (NSL == 4)
+      x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+    return x;
+  };
+  lsum = slot_sum(lsum);
+  tsum = slot_sum(tsum);
 #pragma unroll
-  for (int o = W; o < 16; o <<= 1) {
-    lsum += __shfl_xor(lsum, o, 64);
-    tsum += __shfl_xor(tsum, o, 64);
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oacc[j][r] += __shfl_xor(oacc[j][r], o, 64);
-  }
+    for (int r = 0; r < 4; ++r) oacc[j][r] = slot_sum(oacc[j][r]);
   if (c16 < G) {
     constexpr float kInv = 1.0f / 16384.0f;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       // ternary tokens added p' (off_j + u 2^-14); their values are gamma (u - 1)
       const float sub = tsum * (va_off<NV>(j) + kInv);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) out_row(wave)[c16 * D + 16 * j + 4 * grp + r] = (oacc[j][r] - sub) * vcur;
+      *reinterpret_cast<float4*>(out_row(wave) + c16 * D + swz(c16, 16 * j + 4 * grp)) =
+          float4{(oacc[j][0] - sub) * vcur, (oacc[j][1] - sub) * vcur, (oacc[j][2] - sub) * vcur,
+                 (oacc[j][3] - sub) * vcur};
     }
     if (grp == 0) {
       lds_m[wave][c16] = m;
@@ -1226,31 +1236,42 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   __syncthreads();
 
   // ---------------- merge the four waves ----------------
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kMfmaWaves) {
-    const int hh = idx / D, dd = idx % D;
+  // four consecutive outputs of one head per thread: the waves' weights once, then one
+  // 16-byte LDS read per wave and one store (partials: (D + 2)-float records, 8-byte aligned)
+  static_assert(D % 4 == 0, "whole float4 groups per head");
+  for (int e = threadIdx.x; e < G * D / 4; e += 64 * kMfmaWaves) {
+    const int hh = (4 * e) / D, dd = (4 * e) % D;
+    float mw[kMfmaWaves], lw[kMfmaWaves];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kMfmaWaves; ++w) M = fmaxf(M, lds_m[w][hh]);
-    float num = 0.0f, den = 0.0f;
+    for (int w = 0; w < kMfmaWaves; ++w) {
+      mw[w] = lds_m[w][hh];
+      lw[w] = lds_l[w][hh];
+      M = fmaxf(M, mw[w]);
+    }
+    float4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+    float den = 0.0f;
 #pragma unroll
     for (int w = 0; w < kMfmaWaves; ++w) {
-      const float lw = lds_l[w][hh];
-      if (lw > 0.0f) {
-        const float wt = exp2f(lds_m[w][hh] - M);
-        num = fmaf(wt, out_row(w)[hh * D + dd], num);
-        den = fmaf(wt, lw, den);
+      const float4 o = *reinterpret_cast<const float4*>(out_row(w) + hh * D + swz(hh, dd));
+      if (lw[w] > 0.0f) {  // a wave with nothing attended adds nothing (its outputs are not set)
+        const float wt = exp2f(mw[w] - M);
+        num.x = fmaf(wt, o.x, num.x);
+        num.y = fmaf(wt, o.y, num.y);
+        num.z = fmaf(wt, o.z, num.z);
+        num.w = fmaf(wt, o.w, num.w);
+        den = fmaf(wt, lw[w], den);
       }
     }
     const int64_t qh = qh0 + hh;
     if (a.n_parts == 1) {
-      a.out[(qo0 + hh) * D + dd] = num / den;
+      *reinterpret_cast<float4*>(a.out + (qo0 + hh) * D + dd) =
+          float4{num.x / den, num.y / den, num.z / den, num.w / den};
     } else {
       float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
-      part[dd] = num;
-      if (dd == 0) {
-        part[D] = M;
-        part[D + 1] = den;
-      }
+      *reinterpret_cast<float2*>(part + dd) = float2{num.x, num.y};
+      *reinterpret_cast<float2*>(part + dd + 2) = float2{num.z, num.w};
+      if (dd == 0) *reinterpret_cast<float2*>(part + D) = float2{M, den};
     }
   }
 }
