@@ -618,8 +618,11 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int32_t ent;
     float gk, gv;
     uint32_t plo, phi;
-    bool clean;     // every unit ternary, fully attended, with the chunk's one gamma pair
-    float gk0, gv0;  // that gamma pair (uniform)
+    uint64_t cmask;  // bit i: unit c0 + i is ternary, fully attended, with the gamma pair below
+    float gk0, gv0;  // the gamma pair of the chunk's first ternary unit (uniform)
+  };
+  auto lane_f = [](float x, int k) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), k));
   };
   auto load_chunk = [&](int c0) -> Chunk {
     const int lu = min(c0 + lane, u_last);
@@ -639,14 +642,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   auto chunk_flags = [&](Chunk& c, int c0) {
     const int lu = min(c0 + lane, u_last);
     const bool tern = (static_cast<uint32_t>(c.ent) >> 30) == VK_FMT_TERNARY2;
-    c.gk0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.gk)));
-    c.gv0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c.gv)));
+    const uint64_t tm = __ballot(tern);
+    const int l0 = tm ? static_cast<int>(__builtin_ctzll(tm)) : 0;
+    c.gk0 = lane_f(c.gk, l0);
+    c.gv0 = lane_f(c.gv, l0);
     const int u = unit_of(lu);
     const bool full = R.single ? u * 16 + 16 <= L : (u * 16 + 16 <= R.sinks || (u * 16 >= R.w0 && u * 16 + 16 <= L));
-    c.clean = __ballot(!(tern && full && c.gk == c.gk0 && c.gv == c.gv0)) == 0;
-  };
-  auto lane_f = [](float x, int k) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), k));
+    c.cmask = __ballot(tern && full && c.gk == c.gk0 && c.gv == c.gv0);
   };
 
   // Query head c16 mod G as the B operand of the score product: f16 pairs (d, d+8) of each
@@ -753,8 +755,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // probabilities of the general paths count in slot 0 only (the other slots repeat its heads)
   auto slot0 = [&](uint32_t p) { return NSL == 1 || cslot == 0 ? p : 0u; };
 
-  // One clean step: SU units of a clean chunk (every unit ternary, every token attended, one
-  // gamma pair), with the steps of process_group below and no per-unit checks.  With NSL > 1
+  // One clean step: SU clean units (each ternary, every token attended, with the chunk's
+  // reference gamma pair gk0, gv0), with the steps of process_group below and no per-unit
+  // checks.  With NSL > 1
   // the score tiles of NSL units merge into one, unit i in slot i, so the softmax runs once
   // for them; P*V then gives each unit's probabilities only to its own slot's columns (a
   // block-diagonal B operand) and the slots are summed when the wave ends.
@@ -1137,50 +1140,49 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     for (int c0 = u_begin; c0 < u_end; c0 += CH) {
       const int c_end = min(c0 + CH, u_end);
       chunk_flags(ch_cur, c0);
-      // a clean chunk whose units all lie in the range runs a loop without per-unit checks
-      const bool clean = ch_cur.clean && ((c_end - c0) % SU) == 0;
-      auto run = [&](auto CLEAN) {
-        constexpr int S = decltype(CLEAN)::value ? SU : UG;  // units per step
+      constexpr int S = SU;  // units per step
 #pragma unroll 1
-        for (int k = c0; k < c_end; k += NR) {
-          auto step = [&](auto GI) {
-            constexpr int gi = decltype(GI)::value;
-            UnitRaw<NC, NV> r[S];
-            // Slots are taken two at a time: wait until their copies have landed (at most
-            // NR - 2 ring copies were issued after them; vector memory returns in issue order
-            // and any other load in between only makes the wait stricter; the compiler's own
-            // wait counting does not follow buffer-to-LDS copies into every ring array), read
-            // them into registers, and refill them with the units NR ahead before any compute.
-            auto take2 = [&](auto H) {
-              constexpr int i = 2 * decltype(H)::value;  // first unit of the pair in this step
-              if constexpr (i < S) {
-                __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
-                read_unit(ring_row(integral_constant<int, S * gi + i>{}), r[i]);
-                read_unit(ring_row(integral_constant<int, S * gi + i + 1>{}), r[i + 1]);
-                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot reads have returned
-                dma_unit(k + NR + S * gi + i, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, S * gi + i>{}));
-                dma_unit(k + NR + S * gi + i + 1, ch_cur, ch_nxt, c0,
-                         ring_row(integral_constant<int, S * gi + i + 1>{}));
-              }
-            };
-            take2(integral_constant<int, 0>{});
-            take2(integral_constant<int, 1>{});
-            if constexpr (decltype(CLEAN)::value) {
-              if (k + S * gi < c_end) process_clean(ch_cur, r);
-            } else {
-              process_group(k + S * gi, ch_cur, c0, r[0], r[1]);
+      for (int k = c0; k < c_end; k += NR) {
+        auto step = [&](auto GI) {
+          constexpr int gi = decltype(GI)::value;
+          UnitRaw<NC, NV> r[S];
+          // Slots are taken two at a time: wait until their copies have landed (at most
+          // NR - 2 ring copies were issued after them; vector memory returns in issue order
+          // and any other load in between only makes the wait stricter; the compiler's own
+          // wait counting does not follow buffer-to-LDS copies into every ring array), read
+          // them into registers, and refill them with the units NR ahead before any compute.
+          auto take2 = [&](auto H) {
+            constexpr int i = 2 * decltype(H)::value;  // first unit of the pair in this step
+            if constexpr (i < S) {
+              __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
+              read_unit(ring_row(integral_constant<int, S * gi + i>{}), r[i]);
+              read_unit(ring_row(integral_constant<int, S * gi + i + 1>{}), r[i + 1]);
+              __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot reads have returned
+              dma_unit(k + NR + S * gi + i, ch_cur, ch_nxt, c0, ring_row(integral_constant<int, S * gi + i>{}));
+              dma_unit(k + NR + S * gi + i + 1, ch_cur, ch_nxt, c0,
+                       ring_row(integral_constant<int, S * gi + i + 1>{}));
             }
           };
-          step(integral_constant<int, 0>{});
-          if constexpr (NR / S >= 2) step(integral_constant<int, 1>{});
-          if constexpr (NR / S >= 4) {
-            step(integral_constant<int, 2>{});
-            step(integral_constant<int, 3>{});
+          take2(integral_constant<int, 0>{});
+          take2(integral_constant<int, 1>{});
+          const int lu0 = k + S * gi;
+          if (lu0 >= c_end) return;
+          // a step of clean units runs without per-unit checks; any other takes the general path
+          constexpr uint64_t all = (uint64_t{1} << S) - 1;
+          if (lu0 + S <= c_end && ((ch_cur.cmask >> (lu0 - c0)) & all) == all) {
+            process_clean(ch_cur, r);
+          } else {
+            process_group(lu0, ch_cur, c0, r[0], r[1]);
+            if constexpr (S == 4) process_group(lu0 + 2, ch_cur, c0, r[2], r[3]);
           }
+        };
+        step(integral_constant<int, 0>{});
+        if constexpr (NR / S >= 2) step(integral_constant<int, 1>{});
+        if constexpr (NR / S >= 4) {
+          step(integral_constant<int, 2>{});
+          step(integral_constant<int, 3>{});
         }
-      };
-      if (clean) run(integral_constant<bool, true>{});
-      else run(integral_constant<bool, false>{});
+      }
       ch_cur = ch_nxt;  // the next chunk's metadata was fetched one chunk ahead
       if (c0 + 2 * CH < u_end) ch_nxt = load_chunk(c0 + 2 * CH);
     }
