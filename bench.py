@@ -31,8 +31,8 @@ METRIC = "decode-attn over packed KV: GB/s & % HBM peak; quantize+pack GB/s"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: Qwen2.5-3B-shaped)")
     ap.add_argument("--decode-kernel", type=int, default=0, help="0 default, 1 vector ALU, 2 matrix cores")
     ap.add_argument("--fp8-dynamic", action="store_true",

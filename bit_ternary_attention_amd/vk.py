@@ -101,16 +101,28 @@ def _check(status: int) -> None:
         raise VkError(status, lib().vk_last_error().decode())
 
 
+_id_arrays = {}  # recent sequence lists as int32 arrays (a decode loop passes the same list per layer)
+
+
 def _ids(seq_ids: Sequence[int]):
-    arr = (ctypes.c_int32 * len(seq_ids))(*[int(s) for s in seq_ids])
-    return arr, len(seq_ids)
+    key = tuple(int(s) for s in seq_ids)
+    arr = _id_arrays.get(key)
+    if arr is None:
+        if len(_id_arrays) >= 64:
+            _id_arrays.clear()
+        arr = _id_arrays[key] = (ctypes.c_int32 * len(key))(*key)
+    return arr, len(key)
 
 
-def _stream(stream):
+def _stream(stream, device_index=None):
+    """The raw HIP stream handle: the given stream, else the current stream of the device."""
     import torch
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None and device_index is not None:
+            return raw(device_index)
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _dtype_code(t) -> int:
@@ -150,6 +162,8 @@ class Cache:
         h = ctypes.c_void_p()
         _check(lib().vk_create_cache(ctypes.byref(self.cfg), ctypes.byref(h)))
         self._h = h
+        self._q_shape = (self.cfg.n_q_heads, self.cfg.head_dim)
+        self._decode_fn = lib().vk_decode_attn
 
     @property
     def handle(self):
@@ -166,9 +180,8 @@ class Cache:
         if k.shape[1] != len(seq_ids) or k.shape[3] != self.cfg.n_kv_heads or k.shape[4] != self.cfg.head_dim:
             raise ValueError(f"k shape {tuple(k.shape)} does not match the cache / seq_ids")
         ids, n = _ids(seq_ids)
-        _check(lib().vk_append(self.handle, layer_begin, k.shape[0], n, ids, k.shape[2],
-                               ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-                               _dtype_code(k), _stream(stream)))
+        _check(lib().vk_append(self.handle, layer_begin, k.shape[0], n, ids, k.shape[2], k.data_ptr(), v.data_ptr(),
+                               _dtype_code(k), _stream(stream, k.get_device())))
 
     def decode(self, q, seq_ids: Sequence[int], layer: int, window: int = -1, softmax_scale: float = 0.0,
                out=None, stream=None):
@@ -176,15 +189,15 @@ class Cache:
         import torch
         if not (q.is_cuda and q.is_contiguous()) or q.dim() != 3:
             raise ValueError("q must be a contiguous 3-d device tensor")
-        if q.shape != (len(seq_ids), self.cfg.n_q_heads, self.cfg.head_dim):
+        ids, n = _ids(seq_ids)
+        if q.shape[0] != n or q.shape[1:] != self._q_shape:
             raise ValueError(f"q shape {tuple(q.shape)} does not match the cache / seq_ids")
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         elif out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous():
             raise ValueError("out must be a contiguous float32 tensor shaped like q")
-        ids, n = _ids(seq_ids)
-        _check(lib().vk_decode_attn(self.handle, layer, n, ids, ctypes.c_void_p(q.data_ptr()), _dtype_code(q),
-                                    window, softmax_scale, ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+        _check(self._decode_fn(self.handle, layer, n, ids, q.data_ptr(), _dtype_code(q), window, softmax_scale,
+                               out.data_ptr(), _stream(stream, q.get_device())))
         return out
 
     def retier(self, seq_ids: Sequence[int], stream=None) -> int:
