@@ -119,6 +119,10 @@ EDGE_CASES = [
     ("mha-d64", dict(n_q_heads=3, n_kv_heads=3, head_dim=64, lengths=(200, 77)), [-1, 50]),
     ("gqa2-bs32", dict(n_q_heads=4, n_kv_heads=2, block_size=32, lengths=(333, 64, 1)), [-1, 100]),
     ("gqa8-d128-bf16", dict(n_q_heads=16, n_kv_heads=2, head_dim=128, dtype=1, lengths=(1000, 513)), [-1, 256]),
+    # the other group sizes at both head dims, long enough for whole 4-unit steps per wave
+    ("gqa8-d64", dict(n_q_heads=16, n_kv_heads=2, head_dim=64, lengths=(1100, 405)), [-1, 300]),
+    ("gqa2-d128", dict(n_q_heads=4, n_kv_heads=2, head_dim=128, dtype=1, lengths=(1300, 260)), [-1, 500]),
+    ("gqa1-d128", dict(n_q_heads=2, n_kv_heads=2, head_dim=128, lengths=(1030,)), [-1, 700]),
     ("bs64-chunks", dict(block_size=64, lengths=(640,), chunk_tokens=128), [-1, 200]),
     ("mixed-tiers-f16-fp8", dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
                                  recent_tokens=48, recent_format=oc.FP8E4M3, lengths=(700, 31, 250),
