@@ -539,6 +539,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int W = G < 4 ? 4 : G;       // columns per slot
   constexpr int NSL = 16 / W;            // 4 (G <= 4), 2 (G = 8) or 1 (G = 16)
   constexpr int SU = NSL == 4 ? 4 : 2;   // units per clean step
+  // clean steps may hold partly attended units (masked) where the registers allow it; at head
+  // dim 128 with g <= 4 the masking would spill, and such steps take the general path
+  constexpr bool PCLEAN = D == 64 || G == 8;
   static_assert(CH % PF == 0 && PF % UG == 0 && PF % SU == 0, "chunks hold whole prefetch rounds and groups");
   __shared__ float lds_m[kMfmaWaves][G], lds_l[kMfmaWaves][G];
   // LDS ring: NR slots per wave, each one unit's key tile then value tile (8 D bytes), filled
@@ -601,6 +604,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   };
 
   auto unit_of = [&](int lu) { return lu < n_a ? lu : R.b_begin + (lu - n_a); };
+  auto attended_tok = [&](int t) { return R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L)); };
   // every token of logical units [lu, lu + n) is attended
   auto fully_attended = [&](int lu, int n) {
     if (lu + n > u_end) return false;
@@ -618,7 +622,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     int32_t ent;
     float gk, gv;
     uint32_t plo, phi;
-    uint64_t cmask;  // bit i: unit c0 + i is ternary, fully attended, with the gamma pair below
+    uint64_t cmask;  // bit i: unit c0 + i is ternary with the gamma pair below
+    uint64_t fmask;  // bit i: every token of unit c0 + i is attended
     float gk0, gv0;  // the gamma pair of the chunk's first ternary unit (uniform)
   };
   auto lane_f = [](float x, int k) {
@@ -648,7 +653,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     c.gv0 = lane_f(c.gv, l0);
     const int u = unit_of(lu);
     const bool full = R.single ? u * 16 + 16 <= L : (u * 16 + 16 <= R.sinks || (u * 16 >= R.w0 && u * 16 + 16 <= L));
-    c.cmask = __ballot(tern && full && c.gk == c.gk0 && c.gv == c.gv0);
+    c.cmask = __ballot(tern && c.gk == c.gk0 && c.gv == c.gv0);
+    c.fmask = __ballot(full);
   };
 
   // Query head c16 mod G as the B operand of the score product: f16 pairs (d, d+8) of each
@@ -755,13 +761,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // probabilities of the general paths count in slot 0 only (the other slots repeat its heads)
   auto slot0 = [&](uint32_t p) { return NSL == 1 || cslot == 0 ? p : 0u; };
 
-  // One clean step: SU clean units (each ternary, every token attended, with the chunk's
-  // reference gamma pair gk0, gv0), with the steps of process_group below and no per-unit
-  // checks.  With NSL > 1
+  // One clean step: SU units that are ternary with the chunk's reference gamma pair gk0, gv0,
+  // with the steps of process_group below and no per-unit checks.  A partial step (a unit
+  // with tokens outside the attended set, or units past the end of the range, whose slots
+  // hold copies of nothing) masks those tokens' scores.  With NSL > 1
   // the score tiles of NSL units merge into one, unit i in slot i, so the softmax runs once
   // for them; P*V then gives each unit's probabilities only to its own slot's columns (a
   // block-diagonal B operand) and the slots are summed when the wave ends.
-  auto process_clean = [&](const Chunk& cc, const UnitRaw<NC, NV> (&r)[SU]) {
+  auto process_clean = [&](const Chunk& cc, const UnitRaw<NC, NV> (&r)[SU], bool partial, int lu0, int lu_end) {
     constexpr int UT = NSL == 1 ? 1 : NSL;  // units per score tile
     constexpr int NT = SU / UT;             // score tiles
     const float ks = cc.gk0 * a.scale_log2;
@@ -786,6 +793,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) sc[t][q] = fmaf(tile[q], a0, a1);
+    }
+    if (PCLEAN && partial) {  // this lane's rows of tile t are tokens 4 grp .. 4 grp + 3 of one unit
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int lu = lu0 + t * UT + (UT == 1 ? 0 : cslot);
+        const int t0 = unit_of(lu) * 16 + 4 * grp;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sc[t][q] = lu < lu_end && attended_tok(t0 + q) ? sc[t][q] : -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -955,7 +971,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // FP8 gives every token its own scales: ks = s_t, rt = s_t / s_max (at most 1: no f16
   // overflow) and vscale = s_max for the values.  Only attended tokens count towards s_max:
   // a slot past the sequence may hold a stale scale of a recycled page.
-  auto attended_tok = [&](int t) { return R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L)); };
   auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float (&ks)[4], float (&rt)[4],
                             float& vscale) {
     const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
@@ -1167,10 +1182,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
           take2(integral_constant<int, 1>{});
           const int lu0 = k + S * gi;
           if (lu0 >= c_end) return;
-          // a step of clean units runs without per-unit checks; any other takes the general path
-          constexpr uint64_t all = (uint64_t{1} << S) - 1;
-          if (lu0 + S <= c_end && ((ch_cur.cmask >> (lu0 - c0)) & all) == all) {
-            process_clean(ch_cur, r);
+          // a step whose units in the range are ternary with the chunk's gamma pair runs the
+          // clean path (masked when a unit is partly attended or the range ends inside the
+          // step); any other takes the general path
+          const int n_in = min(S, c_end - lu0);
+          const uint64_t in = (uint64_t{1} << n_in) - 1;
+          const bool partial = n_in < S || ((ch_cur.fmask >> (lu0 - c0)) & in) != in;
+          if (((ch_cur.cmask >> (lu0 - c0)) & in) == in && (PCLEAN || !partial)) {
+            process_clean(ch_cur, r, partial, lu0, c_end);
           } else {
             process_group(lu0, ch_cur, c0, r[0], r[1]);
             if constexpr (S == 4) process_group(lu0 + 2, ch_cur, c0, r[2], r[3]);
