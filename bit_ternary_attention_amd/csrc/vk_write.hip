@@ -80,20 +80,44 @@ __device__ double value16(uint32_t m) {
 }
 
 // Smallest magnitude pattern m with value(m) > d * (1/2 + 2^-25): codes are
-// nonzero exactly for |x| >= value(m).  Searches up to the infinity pattern.
+// nonzero exactly for |x| >= value(m).  The predicate is monotone in m and holds
+// from the infinity pattern on; one wave finds its first m in three rounds of 64
+// candidates (steps 512, 8, 1).  Every lane of the wave calls it; the result is uniform.
 template <int DT>
-__device__ uint32_t threshold16(float d) {
+__device__ uint32_t threshold16_wave(float d) {
   const double tau = static_cast<double>(d) * (0.5 + 0x1p-25);
-  uint32_t lo = 0, hi = DT == 1 ? 0x7F80u : 0x7C00u;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (value16<DT>(mid) > tau) hi = mid; else lo = mid + 1;
+  const uint32_t top = DT == 1 ? 0x7F80u : 0x7C00u;  // +infinity
+  const uint32_t lane = threadIdx.x & 63;
+  auto above = [&](uint32_t m) { return m >= top || value16<DT>(m) > tau; };
+  const uint64_t b1 = __ballot(above(lane * 512u));
+  if (b1 & 1u) return 0u;
+  // first holding candidate; none below 32256 puts it in the last step (above(32768) holds)
+  const uint32_t j1 = b1 ? static_cast<uint32_t>(__builtin_ctzll(b1)) : 64u;
+  const uint32_t lo1 = (j1 - 1u) * 512u;  // above(lo1) fails
+  const uint64_t b2 = __ballot(above(lo1 + lane * 8u));  // lo1 + 512 holds
+  const uint32_t j2 = b2 ? static_cast<uint32_t>(__builtin_ctzll(b2)) : 64u;
+  const uint32_t lo2 = lo1 + (j2 - 1u) * 8u;  // above(lo2) fails, above(lo2 + 8) holds
+  const uint64_t b3 = __ballot(lane >= 1u && lane <= 8u && above(lo2 + lane));
+  return lo2 + static_cast<uint32_t>(__builtin_ctzll(b3));
+}
+
+// Sum of n float64 partials by one wave: lane j adds partials j, j + 64, ... in
+// that order (eight loads in flight), then a fixed butterfly.  Uniform result.
+__device__ double sum_partials_wave(const double* p, int n) {
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  for (int j0 = lane; j0 < n; j0 += 8 * 64) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = j0 + u * 64 < n ? p[j0 + u * 64] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
   }
-  return lo;
+  return wave_sum(s);
 }
 
 template <int DT>
-__device__ __forceinline__ SegInfo finalize(double s, int64_t n, float eps) {
+__device__ __forceinline__ SegInfo finalize_wave(double s, int64_t n, float eps) {
   SegInfo info;
   if (n == 0) {
     info.gamma = 0.0f;
@@ -102,7 +126,7 @@ __device__ __forceinline__ SegInfo finalize(double s, int64_t n, float eps) {
   }
   info.gamma = static_cast<float>(s / static_cast<double>(n));
   const float d = info.gamma + eps;  // float32, as the encoding defines it
-  info.thresh = threshold16<DT>(d);
+  info.thresh = threshold16_wave<DT>(d);
   return info;
 }
 
@@ -177,10 +201,9 @@ __global__ __launch_bounds__(64) void k_gamma_finalize(AppendArgs a) {
   const int i = (seg >> 1) % a.n_seqs;
   const AppendSeqDesc d = a.descs[i];
   const int64_t n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * a.P.hkv * a.P.dim;
-  double s = 0.0;
-  for (int j = threadIdx.x; j < a.n_blk; j += 64) s += a.partials[static_cast<int64_t>(seg) * a.n_blk + j];
-  s = wave_sum(s);
-  if (threadIdx.x == 0) a.seg[seg] = finalize<DT>(s, n, a.eps);
+  const double s = sum_partials_wave(a.partials + static_cast<int64_t>(seg) * a.n_blk, a.n_blk);
+  const SegInfo info = finalize_wave<DT>(s, n, a.eps);
+  if (threadIdx.x == 0) a.seg[seg] = info;
 }
 
 // ------------------------------------------------------------- pass 2 ---
@@ -395,20 +418,17 @@ __global__ __launch_bounds__(kAbsThreads) void k_flat_absmean(QuantArgs a) {
 template <int DT>
 __global__ __launch_bounds__(64) void k_flat_finalize(QuantArgs a) {
   if (a.gamma_in) {
+    SegInfo info;
+    info.gamma = *a.gamma_in;
+    info.thresh = threshold16_wave<DT>(info.gamma + a.eps);
     if (threadIdx.x == 0) {
-      SegInfo info;
-      info.gamma = *a.gamma_in;
-      info.thresh = threshold16<DT>(info.gamma + a.eps);
       a.seg[0] = info;
       *a.gamma_out = info.gamma;
     }
     return;
   }
-  double s = 0.0;
-  for (int j = threadIdx.x; j < a.n_blk; j += 64) s += a.partials[j];
-  s = wave_sum(s);
+  const SegInfo info = finalize_wave<DT>(sum_partials_wave(a.partials, a.n_blk), a.n, a.eps);
   if (threadIdx.x == 0) {
-    const SegInfo info = finalize<DT>(s, a.n, a.eps);
     a.seg[0] = info;
     *a.gamma_out = info.gamma;
   }
