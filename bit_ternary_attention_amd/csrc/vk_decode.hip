@@ -559,7 +559,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63, grp = lane >> 4, c16 = lane & 15;
   const int cslot = c16 / W;  // this lane's column slot
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // grid (KV head, sequence, split): blocks dispatched together read the heads' slices of the
+  // same pages
+  const int split = blockIdx.z, kvh = blockIdx.x, b = blockIdx.y;
   const int slot = a.slots[b], L = a.lens[b];
   const PoolsView& P = a.P;
   const Units R = attended(L, a.sink_tokens, a.window);
@@ -1335,8 +1337,10 @@ __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
-  // matrix-core path: block x = n_splits (when present) takes the fp8 / fp16 pages
-  const dim3 grid(a.kernel == VK_DECODE_VALU ? a.n_splits : a.n_parts, a.P.hkv, a.n_seqs);
+  // matrix-core path: grid (hkv, n_seqs, n_parts), split n_splits (when present) takes the
+  // fp8 / fp16 pages; vector-ALU path: grid (n_splits, hkv, n_seqs)
+  const dim3 grid = a.kernel == VK_DECODE_VALU ? dim3(a.n_splits, a.P.hkv, a.n_seqs)
+                                               : dim3(a.P.hkv, a.n_seqs, a.n_parts);
   if (t) t->begin(VK_KERNEL_DECODE, s);
   if (a.kernel == VK_DECODE_VALU) {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
