@@ -365,6 +365,8 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
   a.n_blk = static_cast<int32_t>(n_blk);
   a.max_units = plan.max_units;
   a.eps = cfg.eps;
+  a.all_ternary = std::all_of(plan.entries.begin(), plan.entries.end(),
+                              [](int32_t e) { return vk::entry_fmt(e) == VK_FMT_TERNARY2; });
   if (c->timer.on) {
     // algorithmic bytes: pass 1 reads the ternary-routed input once; pass 2 reads
     // all input once and writes every stored byte once (+ one gamma per ternary page)

@@ -56,6 +56,7 @@ struct AppendArgs {
   int32_t n_tokens;
   int32_t n_blk;           // absmean blocks per segment
   int32_t max_units;       // most 16-token units touched by one sequence
+  int32_t all_ternary;     // every touched page is ternary (the pack kernel's lean instance)
   float eps;
 };
 

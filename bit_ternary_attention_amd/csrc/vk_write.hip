@@ -208,7 +208,9 @@ __global__ __launch_bounds__(64) void k_gamma_finalize(AppendArgs a) {
 
 // ------------------------------------------------------------- pass 2 ---
 
-template <int DT, int D>
+// MIXED = false: every page of the call is ternary (the fp8 / fp16 routes are left out, which
+// keeps the register count, and so the resident waves per SIMD, where the ternary route needs it)
+template <int DT, int D, bool MIXED>
 __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   constexpr int CPR = D / 8;     // 16-byte chunks per token row
   constexpr int RPI = 64 / CPR;  // rows per wave-wide load
@@ -300,6 +302,8 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
         else *reinterpret_cast<uint32_t*>(vdst) = w0;
         __syncthreads();
       }
+    } else if (!MIXED) {
+      // (not reached: the host launches this instance only when every page is ternary)
     } else if (fmt == VK_FMT_FP8E4M3) {
       const bool dyn = a.P.fp8_dynamic != 0;
 #pragma unroll
@@ -466,12 +470,18 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, Laun
   const int gx_max = gy < 16 ? 16384 / gy : 1024;
   const dim3 g2(n_tasks < gx_max ? n_tasks : gx_max, gy);
   if (t) t->begin(VK_KERNEL_PACK, s);
-  if (a.P.dim == 128) {
-    if (bf) k_pack<1, 128><<<g2, 64, 0, s>>>(a);
-    else k_pack<0, 128><<<g2, 64, 0, s>>>(a);
+  if (a.P.dim == 128 && a.all_ternary) {
+    if (bf) k_pack<1, 128, false><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 128, false><<<g2, 64, 0, s>>>(a);
+  } else if (a.P.dim == 128) {
+    if (bf) k_pack<1, 128, true><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 128, true><<<g2, 64, 0, s>>>(a);
+  } else if (a.all_ternary) {
+    if (bf) k_pack<1, 64, false><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 64, false><<<g2, 64, 0, s>>>(a);
   } else {
-    if (bf) k_pack<1, 64><<<g2, 64, 0, s>>>(a);
-    else k_pack<0, 64><<<g2, 64, 0, s>>>(a);
+    if (bf) k_pack<1, 64, true><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 64, true><<<g2, 64, 0, s>>>(a);
   }
   if (t) t->end(VK_KERNEL_PACK, s);
   return hipGetLastError();
