@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MIN_WARMUP_S = 0.3   # untimed warm-up lasts at least this long (and at least --warmup steps)
 METRIC = "decode-attn over packed KV: GB/s & % HBM peak; quantize+pack GB/s"
 
 
@@ -120,8 +121,15 @@ def main():
         for layer in range(w.n_layers):
             cache.decode(qs[layer], ids_all, layer, window=w.window, out=outs[layer])
 
-    for i in range(args.warmup):
-        step(i)
+    # W warm-up steps, then more untimed steps until the warm-up has lasted MIN_WARMUP_S: a
+    # GPU coming out of idle needs some time under load before its throughput is steady
+    tw = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or time.perf_counter() - tw < MIN_WARMUP_S:
+        step(warm)
+        warm += 1
+        if warm >= args.warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -170,6 +178,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
