@@ -210,6 +210,8 @@ def main():
                      "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": dk["avg_us"]},
     }
 
+    result["decode_step"] = decode_step_leg(cache, qs, outs, w, ids_all)
+
     if w.recent_tokens > 0 and w.recent_format == vk.FMT_FP8E4M3:
         cache.close()
         result["retier"] = retier_leg(w, args.steps, args.warmup, args.fp8_dynamic)
@@ -219,6 +221,46 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, calls, args.cpu_sample_layers)
     print(json.dumps(result), flush=True)
     cache.close()
+
+
+def attended_tokens(L, S, W):
+    """Tokens a decode attends: the first S and the last W (W = -1: all), counted once."""
+    if W < 0:
+        return L
+    a = min(S, L)
+    return a + (L - max(a, L - W))
+
+
+def decode_step_leg(cache, qs, outs, w, ids, reps=20):
+    """One decode step of every layer, timed with events on the launch stream (median of reps),
+    warm (right after the previous step) and cold: the 256 MB Infinity Cache and the L2s are
+    first refilled by reading 1 GiB of other data (a read, so that no dirty lines are left to be
+    written back during the timed step)."""
+    import torch
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    res = {}
+    for mode in ("warm", "cold"):
+        times = []
+        for r in range(reps):
+            if mode == "cold":
+                flush.sum()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for layer in range(w.n_layers):
+                cache.decode(qs[layer], ids, layer, window=w.window, out=outs[layer])
+            t1.record()
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1))
+        times.sort()
+        res[mode + "_us"] = round(1e3 * times[len(times) // 2], 2)
+    del flush
+    toks = sum(attended_tokens(L, w.sink_tokens, w.window) for L in w.lengths) * w.n_layers
+    res.update({"layers": w.n_layers, "attended_tokens": toks, "reps": reps,
+                "kv_tokens_per_s_warm": round(toks / (res["warm_us"] * 1e-6), 1),
+                "kv_tokens_per_s_cold": round(toks / (res["cold_us"] * 1e-6), 1),
+                "decode_steps_per_s_warm": round(w.n_seqs / (res["warm_us"] * 1e-6), 1),
+                "decode_steps_per_s_cold": round(w.n_seqs / (res["cold_us"] * 1e-6), 1)})
+    return res
 
 
 def retier_leg(w, steps, warmup, fp8_dynamic=False):
