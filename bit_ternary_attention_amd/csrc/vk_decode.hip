@@ -383,7 +383,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 // Lane l holds token/dimension row l%16 of the A operands and query head l%16
 // of the B operands; the score output (lane l: tokens 4(l/16)+r, head l%16) is
 // exactly the P operand layout of the second product, so probabilities never
-// leave registers.  Query heads beyond the group (g < 16) are zero columns.
+// leave registers.  With g < 16 the query heads repeat over the 16 columns (slots of
+// max(g, 4) columns); clean steps give each slot its own unit (see "Column slots" below).
 //
 // Codes enter the products as u = code + 1 in {0, 1, 2}, as f16 values off + u 2^-14
 // (offset form below: one v_and_or_b32 per pair of codes); the constant parts are
@@ -396,8 +397,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 // into the wave's LDS ring by one buffer-to-LDS load, NR units ahead; the page
 // addresses come from the block table, one entry per lane for 64 units at a time.
 // The four partial states are merged through LDS; global splits by k_merge.
-// Block x = n_splits (when the attended set has fp8 / fp16 pages) handles those
-// pages and writes one more partial state.
+// Split n_splits (when the attended set has fp8 / fp16 pages) handles those pages
+// and writes one more partial state.  The grid is (KV head, sequence, split).
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
