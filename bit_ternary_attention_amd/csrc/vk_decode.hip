@@ -77,6 +77,18 @@ __device__ __forceinline__ float max_rows(float x) {
   return fmaxf(__uint_as_float(b0), __uint_as_float(b1));
 }
 
+// sum over the four 16-lane rows of each lane column, with the same row-swap permutes
+__device__ __forceinline__ float sum_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = r16[0], a1 = r16[1];
+  x = __uint_as_float(a0) + __uint_as_float(a1);
+  const uint32_t v = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const uint32_t b0 = r32[0], b1 = r32[1];
+  return __uint_as_float(b0) + __uint_as_float(b1);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -1222,10 +1234,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   };
   auto swz = [](int h, int d) { return d ^ ((h & 7) << 2); };  // stays in d's 32-float block
   __syncthreads();
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
-  tsum += __shfl_xor(tsum, 16, 64);
-  tsum += __shfl_xor(tsum, 32, 64);
+  lsum = sum_rows(lsum);
+  tsum = sum_rows(tsum);
   // sum the slots (each head's columns hold the units of its own clean steps) with row
   // rotations: after rotating by 8 a lane holds the sum over columns c16 and c16 ^ 8, and a
   // rotation by 4 of that sum then covers all four slots
@@ -1279,7 +1289,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     for (int w = 0; w < kMfmaWaves; ++w) {
       const float4 o = *reinterpret_cast<const float4*>(out_row(w) + hh * D + swz(hh, dd));
       if (lw[w] > 0.0f) {  // a wave with nothing attended adds nothing (its outputs are not set)
-        const float wt = exp2f(mw[w] - M);
+        const float wt = __builtin_amdgcn_exp2f(mw[w] - M);
         num.x = fmaf(wt, o.x, num.x);
         num.y = fmaf(wt, o.y, num.y);
         num.z = fmaf(wt, o.z, num.z);
@@ -1289,8 +1299,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
     const int64_t qh = qh0 + hh;
     if (a.n_parts == 1) {
-      *reinterpret_cast<float4*>(a.out + (qo0 + hh) * D + dd) =
-          float4{num.x / den, num.y / den, num.z / den, num.w / den};
+      const float inv = 1.0f / den;
+      *reinterpret_cast<float4*>(a.out + (qo0 + hh) * D + dd) = float4{num.x * inv, num.y * inv, num.z * inv, num.w * inv};
     } else {
       float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
       *reinterpret_cast<float2*>(part + dd) = float2{num.x, num.y};
