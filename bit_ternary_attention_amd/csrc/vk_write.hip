@@ -231,7 +231,11 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   const int n_tasks = a.max_units * 2 * hkv;
   const int c = lane % CPR, rg = lane / CPR;
 
-  for (int task = blockIdx.x; task < n_tasks; task += gridDim.x) {
+  // each block takes a contiguous run of tasks: its consecutive tasks are the heads (then K or
+  // V) of the same 16 tokens, so a block walks whole input rows instead of one head's slice
+  const int per_blk = (n_tasks + gridDim.x - 1) / gridDim.x;
+  const int task_end = min(n_tasks, (static_cast<int>(blockIdx.x) + 1) * per_blk);
+  for (int task = blockIdx.x * per_blk; task < task_end; ++task) {
     const int h = task % hkv;
     const int kv = (task / hkv) & 1;
     const int uk = task / (2 * hkv);
