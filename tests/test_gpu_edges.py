@@ -46,7 +46,9 @@ def test_flat_pack_exhaustive_forced_gamma(dtype):
     vals = ot.values16(bits, dtype)
     gammas = [1.0, 0.828125, 2.0 ** -20, 0.7978846, 3.0, 0.5, 1.0 / 3.0, 1e-3]
     if dtype == 1:
-        gammas += [1e30, 7.5e-30]
+        # 1e38 and 3e38 put the bf16 threshold above pattern 32256, the last step of the
+        # first search round
+        gammas += [1e30, 7.5e-30, 1e38, 3e38]
     for g in gammas:
         for eps in (0.0, 1e-5):
             gt = torch.tensor([g], dtype=torch.float32, device="cuda")
