@@ -47,6 +47,12 @@ int decode_units_per_iter() {              // matrix-core prefetch depth in unit
   const char* e = std::getenv("VK_DECODE_UPI");
   return (e && e[0] == '4') ? 4 : 8;
 }
+constexpr int32_t kStealPiece = 16;            // units a stealing wave takes at a time
+constexpr int64_t kStealMinUnitsPerCu = 256;   // stealing launches: units per compute unit, at least
+int decode_steal_mode() {  // VK_DECODE_STEAL: 0 never, 1 whenever the launch's shape allows, else by size
+  const char* e = std::getenv("VK_DECODE_STEAL");
+  return (e && e[0] == '0') ? 0 : (e && e[0] == '1') ? 1 : 2;
+}
 
 // Per-kind launch timing with HIP event pairs recorded on the launch stream.
 class EventTimer : public vk::LaunchTimer {
@@ -117,6 +123,7 @@ struct vk_cache {
   vk_cache_config cfg;
   std::unique_ptr<vk::HostState> host;
   int device = 0;
+  int n_cu = 0;  // compute units of the device
   bool poisoned = false;
   vk::PoolsView pools{};
   double* partials = nullptr;
@@ -238,6 +245,8 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   c->cfg = *cfg;
   hipError_t e = hipGetDevice(&c->device);
   if (e != hipSuccess) return fail(VK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  e = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (e != hipSuccess) return fail(VK_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
   const std::vector<int64_t> sizes = buffer_sizes(*cfg);
   std::vector<void*> ptrs(sizes.size(), nullptr);
   for (size_t i = 0; i < sizes.size(); ++i) {
@@ -488,7 +497,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int64_t units[3] = {0, 0, 0};
-  int32_t splits_used = 1;
+  int32_t splits_used = 1, steal_used = 0;
   const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
   // sequences per launch: every (sequence, KV head) needs room for two partial slots
   const int32_t per_launch = static_cast<int32_t>(
@@ -544,8 +553,21 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
                                                     std::max(1, max_splits), kDecodeMinUnits);
     a.n_splits = sp.n_splits;
     a.units_per_split = sp.units_per_split;
+    // All-ternary launches with at most one (sequence, KV head) per compute unit and enough
+    // work take one 12-wave block per compute unit whose waves share the block's units piece
+    // by piece: the blocks' waves end together, and a block per pair writes its output itself.
+    const int steal_mode = decode_steal_mode();
+    if (mfma && !mixed && !cfg.fp8_dynamic && a.units_per_iter == 8 && c->n_cu > 0 && items <= c->n_cu &&
+        max_units > 0 && (steal_mode == 1 || (steal_mode == 2 && all_units >= kStealMinUnitsPerCu * c->n_cu))) {
+      const int32_t ns = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(c->n_cu / items, max_splits)));
+      const int32_t ups = (max_units + ns - 1) / ns;
+      a.units_per_split = (ups + kStealPiece - 1) / kStealPiece * kStealPiece;
+      a.n_splits = (max_units + a.units_per_split - 1) / a.units_per_split;
+      a.steal = 1;
+    }
     a.n_parts = a.n_splits + (mixed ? 1 : 0);
     splits_used = a.n_splits;
+    steal_used |= a.steal;
     if (c->timer.on) {
       const double row = cfg.head_dim;
       const double unit_kv = 2.0 * 16.0 * cfg.n_kv_heads;  // K and V, 16 tokens, every KV head
@@ -563,6 +585,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   }
   c->stats.decode_calls += 1;
   c->stats.last_decode_splits = splits_used;
+  c->stats.last_decode_steal = steal_used;
   for (int f = 0; f < 3; ++f) {
     c->stats.last_decode_units[f] = units[f];
     c->stats.total_decode_units[f] += units[f];

@@ -419,6 +419,8 @@ typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWaves = 4;
+constexpr int kStealWaves = 12;  // a whole CU at 3 waves per SIMD
+constexpr int kPiece = 16;       // units per piece a stealing wave takes
 // Fourth word of a raw buffer descriptor on gfx9-family parts (32-bit data format; byte
 // offsets checked against the record count, reads past it return 0).
 constexpr int kBufferWord3 = 0x00020000;
@@ -537,8 +539,12 @@ __device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], cons
   }
 }
 
-template <int D, int G, int QDT, int PF, bool DYN>
-__global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void k_decode_mfma(DecodeArgs a) {
+// STEAL: one 12-wave block per (sequence, KV head, split) whose waves take pieces of the
+// block's units from a shared counter (launches of all-ternary pages with a block per CU).
+template <int D, int G, int QDT, int PF, bool DYN, bool STEAL>
+__global__ __launch_bounds__(64 * (STEAL ? kStealWaves : kMfmaWaves)) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void k_decode_mfma(DecodeArgs a) {
+  constexpr int NW = STEAL ? kStealWaves : kMfmaWaves;  // waves per block
   constexpr int NC = D / 64;   // 32-bit key code words per lane per unit
   constexpr int NV = D / 64;   // 32-bit value chunk words per lane per unit
   constexpr int NS = D / 32;   // 16x16x32 steps per unit of the score product
@@ -556,7 +562,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // dim 128 with g <= 4 the masking would spill, and such steps take the general path
   constexpr bool PCLEAN = D == 64 || G == 8;
   static_assert(CH % PF == 0 && PF % UG == 0 && PF % SU == 0, "chunks hold whole prefetch rounds and groups");
-  __shared__ float lds_m[kMfmaWaves][G], lds_l[kMfmaWaves][G];
+  __shared__ float lds_m[NW][G], lds_l[NW][G];
+  __shared__ int lds_next;  // stealing blocks: the next piece to hand out
+  if constexpr (STEAL) {
+    if (threadIdx.x == 0) lds_next = 0;
+    __syncthreads();
+  }
   // LDS ring: NR slots per wave, each one unit's key tile then value tile (8 D bytes), filled
   // by buffer-to-LDS loads.  One array per slot, so the compiler's wait counting can tell
   // the slots apart and waits only for the load of the slot it reads.
@@ -564,9 +575,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int RB = 64 * 16;   // ring row: one 16-byte piece per lane (head dim 64 fills half)
   constexpr int NR = PF;
   static_assert(NR == 8 || NR == 4, "ring of 4 or 8 slots");
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[kMfmaWaves][RB], ring1[kMfmaWaves][RB],
-      ring2[kMfmaWaves][RB], ring3[kMfmaWaves][RB], ring4[NR == 8 ? kMfmaWaves : 1][RB],
-      ring5[NR == 8 ? kMfmaWaves : 1][RB], ring6[NR == 8 ? kMfmaWaves : 1][RB], ring7[NR == 8 ? kMfmaWaves : 1][RB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][RB], ring1[NW][RB],
+      ring2[NW][RB], ring3[NW][RB], ring4[NR == 8 ? NW : 1][RB],
+      ring5[NR == 8 ? NW : 1][RB], ring6[NR == 8 ? NW : 1][RB], ring7[NR == 8 ? NW : 1][RB];
 
   // wave-uniform indices live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -583,8 +594,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   const bool mixed_part = split >= a.n_splits;  // the extra block of the fp8 / fp16 pages
   const int s_begin = min(split * a.units_per_split, U);  // empty past the sequence's units
   const int s_end = min(s_begin + a.units_per_split, U);
-  const int u_begin = s_begin + ((s_end - s_begin) * wave) / kMfmaWaves;
-  const int u_end = s_begin + ((s_end - s_begin) * (wave + 1)) / kMfmaWaves;
+  // a wave's share of the split (stealing waves: the whole split, taken piece by piece)
+  const int u_begin = STEAL ? s_begin : s_begin + ((s_end - s_begin) * wave) / NW;
+  const int u_end = STEAL ? s_end : s_begin + ((s_end - s_begin) * (wave + 1)) / NW;
   const int u_last = max(u_end - 1, 0);
   const int dbase = grp * (D / 4);  // first head dimension of this lane group's key slice
   const int64_t layer = a.layer;
@@ -645,7 +657,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), k));
   };
   auto load_chunk = [&](int c0) -> Chunk {
-    const int lu = min(c0 + lane, u_last);
+    // (a piece needs kPiece lanes; the others repeat its first unit: no extra memory traffic)
+    const int lu = min(c0 + (STEAL && lane >= kPiece ? 0 : lane), u_last);
     Chunk c;
     c.ent = bt[(unit_of(lu) * 16) >> P.bs_shift];
     const bool tern = (static_cast<uint32_t>(c.ent) >> 30) == VK_FMT_TERNARY2;
@@ -1081,7 +1094,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
       while (todo) {
         const int k = __builtin_ctzll(todo);
         todo &= todo - 1;
-        if (rank++ % kMfmaWaves != wave) continue;
+        if (rank++ % NW != wave) continue;
         const int lu = c0 + k;
         const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
         h8_t ka[NS];
@@ -1146,7 +1159,71 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     }
   }
 
-  if (!mixed_part && u_begin < u_end) {
+  // One step of the ring loop: units k + S gi .. k + S gi + S - 1 of a range [c0, c_end) whose
+  // metadata is cc; refill(lu, row) starts the copy of unit lu into a ring row.  Slots are
+  // taken two at a time: wait until their copies have landed (at most NR - 2 ring copies were
+  // issued after them; vector memory returns in issue order and any other load in between only
+  // makes the wait stricter; the compiler's own wait counting does not follow buffer-to-LDS
+  // copies into every ring array), read them into registers, and refill them with the units
+  // NR ahead before any compute.
+  constexpr int S = SU;  // units per step
+  auto step = [&](auto GI, int k, int c0, int c_end, const Chunk& cc, auto&& refill) {
+    using std::integral_constant;
+    constexpr int gi = decltype(GI)::value;
+    UnitRaw<NC, NV> r[S];
+    auto take2 = [&](auto H) {
+      constexpr int i = 2 * decltype(H)::value;  // first unit of the pair in this step
+      if constexpr (i < S) {
+        __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
+        read_unit(ring_row(integral_constant<int, S * gi + i>{}), r[i]);
+        read_unit(ring_row(integral_constant<int, S * gi + i + 1>{}), r[i + 1]);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot reads have returned
+        refill(k + NR + S * gi + i, ring_row(integral_constant<int, S * gi + i>{}));
+        refill(k + NR + S * gi + i + 1, ring_row(integral_constant<int, S * gi + i + 1>{}));
+      }
+    };
+    take2(integral_constant<int, 0>{});
+    take2(integral_constant<int, 1>{});
+    const int lu0 = k + S * gi;
+    if (lu0 >= c_end) return;
+    // a step whose units in the range are ternary with the chunk's gamma pair runs the clean
+    // path (masked when a unit is partly attended or the range ends inside the step); any
+    // other takes the general path
+    const int n_in = min(S, c_end - lu0);
+    const uint64_t in = (uint64_t{1} << n_in) - 1;
+    const bool partial = n_in < S || ((cc.fmask >> (lu0 - c0)) & in) != in;
+    if (((cc.cmask >> (lu0 - c0)) & in) == in && (PCLEAN || !partial)) {
+      process_clean(cc, r, partial, lu0, c_end);
+    } else {
+      process_group(lu0, cc, c0, r[0], r[1]);
+      if constexpr (S == 4) process_group(lu0 + 2, cc, c0, r[2], r[3]);
+    }
+  };
+  auto ring_round = [&](int k, int c0, int c_end, const Chunk& cc, auto&& refill) {
+    using std::integral_constant;
+    step(integral_constant<int, 0>{}, k, c0, c_end, cc, refill);
+    if constexpr (NR / S >= 2) step(integral_constant<int, 1>{}, k, c0, c_end, cc, refill);
+    if constexpr (NR / S >= 4) {
+      step(integral_constant<int, 2>{}, k, c0, c_end, cc, refill);
+      step(integral_constant<int, 3>{}, k, c0, c_end, cc, refill);
+    }
+  };
+  auto prologue_copies = [&](int u0, auto&& refill) {
+    using std::integral_constant;
+    auto one = [&](auto I) { refill(u0 + decltype(I)::value, ring_row(I)); };
+    one(integral_constant<int, 0>{});
+    one(integral_constant<int, 1>{});
+    one(integral_constant<int, 2>{});
+    one(integral_constant<int, 3>{});
+    if constexpr (NR == 8) {
+      one(integral_constant<int, 4>{});
+      one(integral_constant<int, 5>{});
+      one(integral_constant<int, 6>{});
+      one(integral_constant<int, 7>{});
+    }
+  };
+
+  if (!STEAL && !mixed_part && u_begin < u_end) {
     // ring slot s holds unit k + s while the group of slots (2i, 2i + 1) is processed; a
     // processed slot is refilled with the unit NR ahead.  The first copies go out as soon as
     // the first chunk's block-table entries are in (they lie in that chunk); the next chunk's
@@ -1223,14 +1300,77 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy into the ring is left in flight
   }
 
+  if constexpr (STEAL) {
+    // Work stealing inside the block: its units go in pieces of kPiece to whichever wave asks
+    // next (an LDS counter), so every wave stays busy until the block's units run out.  A wave
+    // asks for its next piece when it starts one, so its ring copies run on into that piece; a
+    // piece holds two ring rounds, which gives the next piece's metadata a round to arrive.
+    // The counter only grows, so every wave leaves the loop.
+    static_assert(kPiece % NR == 0 && kPiece <= CH, "whole ring rounds per piece");
+    const int n_pieces = (s_end - s_begin + kPiece - 1) / kPiece;
+    auto grab = [&]() {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&lds_next, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    int p_cur = mixed_part ? n_pieces : grab();
+    if (p_cur < n_pieces) {
+      int p_nxt = grab();
+      int cs = s_begin + p_cur * kPiece, ce = min(cs + kPiece, s_end);
+      int ns = cs, ne = cs;  // next piece [ns, ne); empty when there is none
+      if (p_nxt < n_pieces) ns = s_begin + p_nxt * kPiece, ne = min(ns + kPiece, s_end);
+      Chunk ch_cur = load_chunk(cs);
+      Chunk ch_nxt = ch_cur;
+      // copy of unit lu: in the current piece, or position lu - cs - kPiece of the next one;
+      // a unit past either piece gets an empty record range (it reads no memory)
+      auto refill = [&](int lu, uint8_t* row) {
+        const bool in_cur = lu - cs < kPiece;
+        const int li = in_cur ? lu - cs : lu - cs - kPiece;
+        const int un = in_cur ? lu : ns + li;
+        const bool valid = in_cur ? un < ce : un < ne;
+        const uint32_t lo = __builtin_amdgcn_readlane(in_cur ? ch_cur.plo : ch_nxt.plo, li);
+        const uint32_t hi = __builtin_amdgcn_readlane(in_cur ? ch_cur.phi : ch_nxt.phi, li);
+        const uint8_t* pg = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+        const int upi = valid ? ((unit_of(un) * 16) & (P.bs - 1)) >> 4 : 0;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, valid ? page_bytes0 : 0, kBufferWord3);
+        const int soff = kvh * tile0 + upi * 4 * D;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)row, 16, dma_off, soff, 0, 0);
+      };
+      prologue_copies(cs, refill);
+      if (p_nxt < n_pieces) ch_nxt = load_chunk(ns);
+      make_qb();
+      while (true) {
+        chunk_flags(ch_cur, cs);
+#pragma unroll 1
+        for (int k = cs; k < cs + kPiece; k += NR) ring_round(k, cs, ce, ch_cur, refill);
+        if (p_nxt >= n_pieces) break;
+        p_cur = p_nxt;
+        cs = ns;
+        ce = ne;
+        ch_cur = ch_nxt;
+        p_nxt = grab();
+        ns = ne = cs;
+        if (p_nxt < n_pieces) {
+          ns = s_begin + p_nxt * kPiece;
+          ne = min(ns + kPiece, s_end);
+          ch_nxt = load_chunk(ns);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy into the ring is left in flight
+    }
+  }
+
   // ---------------- this wave's partial state -> LDS ----------------
   // (the G x D outputs of wave w go to ring array w, free once every wave has left its loop;
   // dimension d of head h sits at h D + swz(h, d): the XOR spreads the heads' rows, written
   // by lanes of one column each, over the LDS banks)
-  static_assert(G * D * 4 <= kMfmaWaves * RB, "a wave's outputs fit one ring array");
+  constexpr int PER = (NW * RB) / (G * D * 4) < NW ? (NW * RB) / (G * D * 4) : NW;  // waves per ring array
+  static_assert(PER >= 1 && (NW + PER - 1) / PER <= 4, "the waves' outputs fit ring arrays 0-3");
   auto out_row = [&](int w) -> float* {
-    uint8_t* r = w == 0 ? &ring0[0][0] : w == 1 ? &ring1[0][0] : w == 2 ? &ring2[0][0] : &ring3[0][0];
-    return reinterpret_cast<float*>(r);
+    const int q = w / PER;
+    uint8_t* r = q == 0 ? &ring0[0][0] : q == 1 ? &ring1[0][0] : q == 2 ? &ring2[0][0] : &ring3[0][0];
+    return reinterpret_cast<float*>(r) + (w % PER) * (G * D);
   };
   auto swz = [](int h, int d) { return d ^ ((h & 7) << 2); };  // stays in d's 32-float block
   __syncthreads();
@@ -1273,12 +1413,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
   // four consecutive outputs of one head per thread: the waves' weights once, then one
   // 16-byte LDS read per wave and one store (partials: (D + 2)-float records, 8-byte aligned)
   static_assert(D % 4 == 0, "whole float4 groups per head");
-  for (int e = threadIdx.x; e < G * D / 4; e += 64 * kMfmaWaves) {
+  for (int e = threadIdx.x; e < G * D / 4; e += 64 * NW) {
     const int hh = (4 * e) / D, dd = (4 * e) % D;
-    float mw[kMfmaWaves], lw[kMfmaWaves];
+    float mw[NW], lw[NW];
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kMfmaWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       mw[w] = lds_m[w][hh];
       lw[w] = lds_l[w][hh];
       M = fmaxf(M, mw[w]);
@@ -1286,7 +1426,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) __attribute__((amdgpu_waves_per_eu
     float4 num = {0.0f, 0.0f, 0.0f, 0.0f};
     float den = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMfmaWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float4 o = *reinterpret_cast<const float4*>(out_row(w) + hh * D + swz(hh, dd));
       if (lw[w] > 0.0f) {  // a wave with nothing attended adds nothing (its outputs are not set)
         const float wt = __builtin_amdgcn_exp2f(mw[w] - M);
@@ -1356,15 +1496,18 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   if (a.kernel == VK_DECODE_VALU) {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
     else k_decode<D, G, 0><<<grid, 64, 0, s>>>(a);
+  } else if (a.steal) {  // all-ternary launch with a block per CU: 12 waves share each block's units
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, false, true><<<grid, 64 * kStealWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 8, false, true><<<grid, 64 * kStealWaves, 0, s>>>(a);
   } else if (a.P.fp8_dynamic) {  // dynamic FP8 pages: their scale handling in its own instance
-    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, true><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
-    else k_decode_mfma<D, G, 0, 8, true><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, true, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 8, true, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   } else if (a.units_per_iter == 8) {
-    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
-    else k_decode_mfma<D, G, 0, 8, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 8, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   } else {
-    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 4, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
-    else k_decode_mfma<D, G, 0, 4, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 4, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    else k_decode_mfma<D, G, 0, 4, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
   }
   if (t) t->end(VK_KERNEL_DECODE, s);
   if (a.n_parts > 1) {

@@ -81,6 +81,8 @@ struct DecodeArgs {
                            // pages (matrix-core path); 1 = the decode kernel writes out directly
   int32_t kernel;          // VK_DECODE_VALU or VK_DECODE_MFMA
   int32_t units_per_iter;  // matrix-core kernel: prefetch depth in 16-token units (4 or 8)
+  int32_t steal;           // matrix-core kernel: 12-wave blocks whose waves take 16-unit pieces of
+                           // the block's units from a shared counter
   float scale_log2;        // softmax scale * log2(e)
   int32_t slots[kDecodeMaxSeqs];   // launch order: longest attended range first
   int32_t lens[kDecodeMaxSeqs];

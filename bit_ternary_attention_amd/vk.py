@@ -36,7 +36,7 @@ class Stats(ctypes.Structure):
     _fields_ = [("device_bytes", _c_i64), ("pool_pages", _c_i64 * 3), ("pages_used", _c_i64 * 3),
                 ("tokens_stored", _c_i64 * 3), ("append_calls", _c_i64), ("decode_calls", _c_i64),
                 ("last_decode_units", _c_i64 * 3), ("total_decode_units", _c_i64 * 3),
-                ("last_decode_splits", _c_i32), ("reserved", _c_i32), ("retier_calls", _c_i64),
+                ("last_decode_splits", _c_i32), ("last_decode_steal", _c_i32), ("retier_calls", _c_i64),
                 ("pages_retiered", _c_i64), ("pages_evicted", _c_i64)]
 
     def as_dict(self):

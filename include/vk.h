@@ -77,7 +77,11 @@ enum {
   VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores and P*V, pages staged in LDS by
                              buffer-to-LDS copies, codes unpacked to f16 in registers, query rows
                              resident as the B operand; fp8 / fp16 pages in one extra block per
-                             (sequence, KV head) that writes its own partial state             */
+                             (sequence, KV head) that writes its own partial state.  Large
+                             all-ternary launches with at most one (sequence, KV head) per
+                             compute unit run 12-wave blocks whose waves take 16-unit pieces
+                             from a shared counter (environment VK_DECODE_STEAL=0 never, =1
+                             whenever the launch's shape allows; vk_stats.last_decode_steal) */
 };
 
 typedef struct vk_cache vk_cache; /* opaque; owned by the library */
@@ -255,7 +259,7 @@ typedef struct vk_stats {
   int64_t last_decode_units[3];     /* 16-token units read by the last decode, by format  */
   int64_t total_decode_units[3];    /* route counters over the handle's life              */
   int32_t last_decode_splits;       /* split-K factor the last decode used                */
-  int32_t reserved;
+  int32_t last_decode_steal;        /* 1 if its matrix-core launches used stealing blocks */
   int64_t retier_calls;             /* vk_retier calls                                    */
   int64_t pages_retiered;           /* pages moved from FP8 to ternary (each in every layer) */
   int64_t pages_evicted;            /* pages freed by vk_evict                            */

@@ -156,6 +156,50 @@ def test_edge_workloads(name, kw, windows, kernel):
     cache.close()
 
 
+STEAL_CASES = [
+    # (name, workload kwargs, windows, sequences checked against the oracle (None: all))
+    # 128 (sequence, KV head) pairs: two splits of 16 pieces per pair, 12 waves sharing them
+    ("gqa4-d128-bf16-many-pieces", dict(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype=1, n_seqs=16,
+                                        lengths=tuple(8192 - 509 * i for i in range(16))), [-1, 3001], [0, 5, 15]),
+    ("gqa8-d128-bf16", dict(n_q_heads=16, n_kv_heads=2, head_dim=128, dtype=1, lengths=(5000, 1300, 17)),
+     [-1, 700], None),
+    ("gqa2-d128-f16", dict(n_q_heads=4, n_kv_heads=2, head_dim=128, lengths=(4100, 260)), [-1, 500], None),
+    ("gqa4-d128-f16", dict(n_q_heads=8, n_kv_heads=2, head_dim=128, lengths=(3333,)), [-1, 100], None),
+    ("gqa1-d64", dict(n_q_heads=2, n_kv_heads=2, head_dim=64, lengths=(2600, 999)), [-1, 40], None),
+    ("gqa8-d64-bf16", dict(n_q_heads=16, n_kv_heads=2, head_dim=64, dtype=1, lengths=(3000,)), [-1, 0], None),
+]
+
+
+@pytest.mark.parametrize("name,kw,windows,sample", STEAL_CASES, ids=[c[0] for c in STEAL_CASES])
+def test_stealing_blocks(name, kw, windows, sample, monkeypatch):
+    """All-ternary decodes through the 12-wave stealing blocks (forced on at these sizes): against
+    the oracle, and close to the 4-wave blocks' outputs on the same cache."""
+    w = wl.small_workload(**kw)
+    say(f"steal {name}: {w}")
+    cache = make_cache(w, decode_kernel=2)
+    fill(cache, w)
+    ids = list(range(w.n_seqs)) if sample is None else sample
+    encs = {}
+    for s in ids:
+        kb, vb = host_kv(w, 0, s)
+        encs[s] = oc.encode_sequence(spec_of(w), kb, vb, w.dtype, seq_calls(w, s))
+    q = wl.queries(w, 0, device="cuda")
+    for W in windows:
+        monkeypatch.setenv("VK_DECODE_STEAL", "1")
+        out = cache.decode(q, list(range(w.n_seqs)), 0, window=W)
+        torch.cuda.synchronize()
+        assert cache.stats()["last_decode_steal"] == 1
+        err = check_decode(out, q, w, encs, W)
+        monkeypatch.setenv("VK_DECODE_STEAL", "0")
+        plain = cache.decode(q, list(range(w.n_seqs)), 0, window=W)
+        torch.cuda.synchronize()
+        assert cache.stats()["last_decode_steal"] == 0
+        diff = float((out - plain).abs().max())
+        assert diff <= 2 * ATTN_ATOL
+        say(f"steal {name} window {W}: max err {err:.2e}, vs 4-wave blocks {diff:.2e}")
+    cache.close()
+
+
 @pytest.mark.parametrize("dyn", [0, 1], ids=["static-fp8", "dynamic-fp8"])
 @pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
 def test_incremental_decode_appends_into_recent_tier(kernel, dyn):
