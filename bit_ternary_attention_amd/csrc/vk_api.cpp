@@ -49,9 +49,12 @@ int decode_units_per_iter() {              // matrix-core prefetch depth in unit
 }
 constexpr int32_t kStealPiece = 16;            // units a stealing wave takes at a time
 constexpr int64_t kStealMinUnitsPerCu = 256;   // stealing launches: units per compute unit, at least
-int decode_steal_mode() {  // VK_DECODE_STEAL: 0 never, 1 whenever the launch's shape allows, else by size
+// Stealing blocks (opt-in: which wave sums which units changes from call to call, so outputs
+// repeat only within the decode tolerance).  VK_DECODE_STEAL=1: large launches (by size);
+// =2: whenever the launch's shape allows; unset or 0: never.
+int decode_steal_mode() {
   const char* e = std::getenv("VK_DECODE_STEAL");
-  return (e && e[0] == '0') ? 0 : (e && e[0] == '1') ? 1 : 2;
+  return (e && e[0] == '1') ? 1 : (e && e[0] == '2') ? 2 : 0;
 }
 
 // Per-kind launch timing with HIP event pairs recorded on the launch stream.
@@ -553,12 +556,12 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
                                                     std::max(1, max_splits), kDecodeMinUnits);
     a.n_splits = sp.n_splits;
     a.units_per_split = sp.units_per_split;
-    // All-ternary launches with at most one (sequence, KV head) per compute unit and enough
-    // work take one 12-wave block per compute unit whose waves share the block's units piece
-    // by piece: the blocks' waves end together, and a block per pair writes its output itself.
+    // Opted in: all-ternary launches with at most one (sequence, KV head) per compute unit and
+    // enough work take one 12-wave block per compute unit whose waves share the block's units
+    // piece by piece: the blocks' waves end together, and a block per pair writes its output.
     const int steal_mode = decode_steal_mode();
     if (mfma && !mixed && !cfg.fp8_dynamic && a.units_per_iter == 8 && c->n_cu > 0 && items <= c->n_cu &&
-        max_units > 0 && (steal_mode == 1 || (steal_mode == 2 && all_units >= kStealMinUnitsPerCu * c->n_cu))) {
+        max_units > 0 && (steal_mode == 2 || (steal_mode == 1 && all_units >= kStealMinUnitsPerCu * c->n_cu))) {
       const int32_t ns = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(c->n_cu / items, max_splits)));
       const int32_t ups = (max_units + ns - 1) / ns;
       a.units_per_split = (ups + kStealPiece - 1) / kStealPiece * kStealPiece;

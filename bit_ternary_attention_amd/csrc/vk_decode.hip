@@ -1223,7 +1223,61 @@ void k_decode_mfma(DecodeArgs a) {
     }
   };
 
-  if (!STEAL && !mixed_part && u_begin < u_end) {
+  // Short ranges (at most NR units per wave: launches too small to fill the GPU) send every
+  // copy at once and walk the slots in a run-time loop: one copy of the step's code instead
+  // of one per slot group, so a wave fetches far fewer instruction bytes (a launch this small
+  // is bound by latencies, cold instruction fetches among them).
+  const bool short_range = u_end - u_begin <= NR;
+  if (!STEAL && !mixed_part && u_begin < u_end && short_range) {
+    using std::integral_constant;
+    Chunk ch = load_chunk(u_begin);
+    auto prologue = [&](auto I) { dma_unit(u_begin + decltype(I)::value, ch, ch, u_begin, ring_row(I)); };
+    prologue(integral_constant<int, 0>{});
+    prologue(integral_constant<int, 1>{});
+    prologue(integral_constant<int, 2>{});
+    prologue(integral_constant<int, 3>{});
+    if constexpr (NR == 8) {
+      prologue(integral_constant<int, 4>{});
+      prologue(integral_constant<int, 5>{});
+      prologue(integral_constant<int, 6>{});
+      prologue(integral_constant<int, 7>{});
+    }
+    make_qb();
+    chunk_flags(ch, u_begin);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // every copy has landed
+    auto slot_row = [&](int i) -> const uint8_t* {  // ring row of slot i (wave-uniform)
+      const uint8_t* p = ring0[wave];
+      p = i == 1 ? ring1[wave] : p;
+      p = i == 2 ? ring2[wave] : p;
+      p = i == 3 ? ring3[wave] : p;
+      if constexpr (NR == 8) {
+        p = i == 4 ? ring4[wave] : p;
+        p = i == 5 ? ring5[wave] : p;
+        p = i == 6 ? ring6[wave] : p;
+        p = i == 7 ? ring7[wave] : p;
+      }
+      return p;
+    };
+    constexpr int S = SU;  // units per step; NR is a multiple of S, so every slot read is < NR
+#pragma unroll 1
+    for (int lu0 = u_begin; lu0 < u_end; lu0 += S) {
+      UnitRaw<NC, NV> r[S];
+#pragma unroll
+      for (int i = 0; i < S; ++i) read_unit(slot_row(lu0 - u_begin + i), r[i]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      const int n_in = min(S, u_end - lu0);
+      const uint64_t in = (uint64_t{1} << n_in) - 1;
+      const bool partial = n_in < S || ((ch.fmask >> (lu0 - u_begin)) & in) != in;
+      if (((ch.cmask >> (lu0 - u_begin)) & in) == in && (PCLEAN || !partial)) {
+        process_clean(ch, r, partial, lu0, u_end);
+      } else {
+        process_group(lu0, ch, u_begin, r[0], r[1]);
+        if constexpr (S == 4) process_group(lu0 + 2, ch, u_begin, r[2], r[3]);
+      }
+    }
+  }
+
+  if (!STEAL && !mixed_part && u_begin < u_end && !short_range) {
     // ring slot s holds unit k + s while the group of slots (2i, 2i + 1) is processed; a
     // processed slot is refilled with the unit NR ahead.  The first copies go out as soon as
     // the first chunk's block-table entries are in (they lie in that chunk); the next chunk's

@@ -77,11 +77,13 @@ enum {
   VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores and P*V, pages staged in LDS by
                              buffer-to-LDS copies, codes unpacked to f16 in registers, query rows
                              resident as the B operand; fp8 / fp16 pages in one extra block per
-                             (sequence, KV head) that writes its own partial state.  Large
-                             all-ternary launches with at most one (sequence, KV head) per
-                             compute unit run 12-wave blocks whose waves take 16-unit pieces
-                             from a shared counter (environment VK_DECODE_STEAL=0 never, =1
-                             whenever the launch's shape allows; vk_stats.last_decode_steal) */
+                             (sequence, KV head) that writes its own partial state.  Opt-in
+                             (environment VK_DECODE_STEAL=1: large launches, =2: whenever the
+                             shape allows): all-ternary launches with at most one (sequence,
+                             KV head) per compute unit run 12-wave blocks whose waves take
+                             16-unit pieces from a shared counter; the summation order then
+                             varies between calls, so outputs repeat only within the decode
+                             tolerance (vk_stats.last_decode_steal reports the choice)       */
 };
 
 typedef struct vk_cache vk_cache; /* opaque; owned by the library */

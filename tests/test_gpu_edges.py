@@ -173,7 +173,7 @@ STEAL_CASES = [
 @pytest.mark.parametrize("name,kw,windows,sample", STEAL_CASES, ids=[c[0] for c in STEAL_CASES])
 def test_stealing_blocks(name, kw, windows, sample, monkeypatch):
     """All-ternary decodes through the 12-wave stealing blocks (forced on at these sizes): against
-    the oracle, and close to the 4-wave blocks' outputs on the same cache."""
+    the oracle, and close to the 4-wave blocks' outputs (the default) on the same cache."""
     w = wl.small_workload(**kw)
     say(f"steal {name}: {w}")
     cache = make_cache(w, decode_kernel=2)
@@ -185,7 +185,7 @@ def test_stealing_blocks(name, kw, windows, sample, monkeypatch):
         encs[s] = oc.encode_sequence(spec_of(w), kb, vb, w.dtype, seq_calls(w, s))
     q = wl.queries(w, 0, device="cuda")
     for W in windows:
-        monkeypatch.setenv("VK_DECODE_STEAL", "1")
+        monkeypatch.setenv("VK_DECODE_STEAL", "2")
         out = cache.decode(q, list(range(w.n_seqs)), 0, window=W)
         torch.cuda.synchronize()
         assert cache.stats()["last_decode_steal"] == 1

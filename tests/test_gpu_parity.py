@@ -39,8 +39,7 @@ def test_workload2_qwen_shaped_36_layers(kernel):
 def test_workload3_full_retention_outliers(kernel):
     w = wl.workload(3)
     r = run_workload(w, sample_seqs=[0, 13, 31], page_layers=[0], decode_layers=[0], decode_kernel=kernel)
-    if torch.cuda.get_device_properties(0).multi_processor_count >= 256:  # a block per (sequence, KV head)
-        assert r["stats"]["last_decode_steal"] == int(kernel == 2)
+    assert r["stats"]["last_decode_steal"] == 0   # stealing blocks are opt-in
     say(f"workload 3: max err {r['max_err']:.3e}")
 
 
@@ -71,5 +70,5 @@ def test_workload5_prefill_128k_chunked(kernel):
     w = wl.workload(5)
     r = run_workload(w, sample_seqs=[2], page_layers=[0], decode_layers=[0], decode_kernel=kernel)
     assert r["stats"]["append_calls"] == 32
-    assert r["stats"]["last_decode_steal"] == int(kernel == 2)
+    assert r["stats"]["last_decode_steal"] == 0
     say(f"workload 5: max err {r['max_err']:.3e}")
