@@ -1416,18 +1416,23 @@ void k_decode_mfma(DecodeArgs a) {
   }
 
   // ---------------- this wave's partial state -> LDS ----------------
-  // (the G x D outputs of wave w go to ring array w, free once every wave has left its loop;
-  // dimension d of head h sits at h D + swz(h, d): the XOR spreads the heads' rows, written
-  // by lanes of one column each, over the LDS banks)
+  // (dimension d of head h of wave w sits at h D + swz(h, d) of the wave's staging rows: the
+  // XOR spreads the heads' rows, written by lanes of one column each, over the LDS banks)
+  // 4-wave blocks stage in LDS of their own (8-16 KB), so a wave that has finished stages its
+  // outputs while slower waves still compute; 12-wave blocks reuse the ring, once every wave
+  // has left its loop.
+  constexpr bool OWN_STAGE = !STEAL;
+  __shared__ __attribute__((aligned(16))) float stage[OWN_STAGE ? NW * G * D : 4];
   constexpr int PER = (NW * RB) / (G * D * 4) < NW ? (NW * RB) / (G * D * 4) : NW;  // waves per ring array
-  static_assert(PER >= 1 && (NW + PER - 1) / PER <= 4, "the waves' outputs fit ring arrays 0-3");
+  static_assert(OWN_STAGE || (PER >= 1 && (NW + PER - 1) / PER <= 4), "the waves' outputs fit ring arrays 0-3");
   auto out_row = [&](int w) -> float* {
+    if constexpr (OWN_STAGE) return stage + w * (G * D);
     const int q = w / PER;
     uint8_t* r = q == 0 ? &ring0[0][0] : q == 1 ? &ring1[0][0] : q == 2 ? &ring2[0][0] : &ring3[0][0];
     return reinterpret_cast<float*>(r) + (w % PER) * (G * D);
   };
   auto swz = [](int h, int d) { return d ^ ((h & 7) << 2); };  // stays in d's 32-float block
-  __syncthreads();
+  if constexpr (!OWN_STAGE) __syncthreads();
   lsum = sum_rows(lsum);
   tsum = sum_rows(tsum);
   // sum the slots (each head's columns hold the units of its own clean steps) with row
