@@ -100,26 +100,18 @@ struct Units {
   bool single;
 };
 
-// Same arithmetic as the host planner (attended_units in host_state.cpp).
+// Same arithmetic as the host planner (attended_units in host_state.cpp), written with
+// selects: no branch stands between a kernel's set-up loads.
 __device__ __forceinline__ Units attended(int L, int S, int W) {
   Units r;
   r.sinks = min(S, L);
   const int all = (L + 15) >> 4;
-  if (W < 0 || L - W <= r.sinks) {
-    r.single = true;
-    r.a_end = r.b_begin = r.b_end = all;
-    r.w0 = 0;
-    return r;
-  }
-  r.single = false;
-  r.w0 = L - W;
-  r.a_end = (r.sinks + 15) >> 4;
-  if (W == 0) {
-    r.b_begin = r.b_end = r.a_end;
-  } else {
-    r.b_begin = max(r.a_end, r.w0 >> 4);
-    r.b_end = all;
-  }
+  const int a_end = (r.sinks + 15) >> 4;
+  r.single = W < 0 || L - W <= r.sinks;  // one range: the whole context
+  r.w0 = r.single ? 0 : L - W;
+  r.a_end = r.single ? all : a_end;
+  r.b_begin = r.single ? all : (W == 0 ? a_end : max(a_end, (L - W) >> 4));
+  r.b_end = r.single ? all : (W == 0 ? a_end : all);
   return r;
 }
 
@@ -588,6 +580,16 @@ void k_decode_mfma(DecodeArgs a) {
   const int split = blockIdx.z, kvh = blockIdx.x, b = blockIdx.y;
   const int slot = a.slots[b], L = a.lens[b];
   const PoolsView& P = a.P;
+  // The kernel arguments the set-up reads, loaded in one batch: left to the compiler, the
+  // scalar loads go out in rounds, each waiting for the one before (a launch that moves a
+  // few tens of KB pays for every round).
+  {
+    const void* ptrs[5] = {P.block_table, P.gamma, P.pool[0], P.dummy_page, a.q};
+    asm volatile("" ::"s"(slot), "s"(L), "s"(a.sink_tokens), "s"(a.window), "s"(a.n_splits),
+                 "s"(a.units_per_split), "s"(a.rows[b]), "s"(a.hq), "s"(a.layer), "s"(P.max_pages),
+                 "s"(P.bs_shift), "s"(P.bs), "s"(P.hkv), "s"(P.cap[0]), "s"(P.page_bytes[0]),
+                 "s"(P.tile_bytes[0]), "s"(ptrs[0]), "s"(ptrs[1]), "s"(ptrs[2]), "s"(ptrs[3]), "s"(ptrs[4]));
+  }
   const Units R = attended(L, a.sink_tokens, a.window);
   const int n_a = R.a_end;
   const int U = R.a_end + (R.b_end - R.b_begin);
@@ -692,6 +694,9 @@ void k_decode_mfma(DecodeArgs a) {
   float qsum = 0.0f, qoff = 0.0f;
   const uint16_t* qhead = a.q + (qo0 + (c16 & (G - 1))) * D;
   auto make_qb = [&]() {
+    // (the memory clobber keeps the query's loads, and the wait for them, after the page
+    // copies issued before this call: the compiler would otherwise hoist them to the top)
+    asm volatile("" ::: "memory");
     const uint16_t* qrow = qhead + dbase;
     uint32_t w[NS][4];
     float sum = 0.0f;
