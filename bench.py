@@ -114,12 +114,16 @@ def main():
     outs = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for q in qs]
     torch.cuda.synchronize()
 
-    def step(i):
+    def step(i, seg=None):
         cache.reset(ids_all)
         for ids, k, v in sets[i % n_sets]:
             cache.append(k, v, ids)
+        if seg is not None:
+            seg[0].record()
         for layer in range(w.n_layers):
             cache.decode(qs[layer], ids_all, layer, window=w.window, out=outs[layer])
+        if seg is not None:
+            seg[1].record()
 
     # W warm-up steps, then more untimed steps until the warm-up has lasted MIN_WARMUP_S: a
     # GPU coming out of idle needs some time under load before its throughput is steady
@@ -137,6 +141,16 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # the same steps with one event pair per step around its decode launches (the launch stream
+    # is torch's current one): the decode segment's device time without a pair of events around
+    # every launch
+    segs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, segs[i])
+    torch.cuda.synchronize()
+    decode_seg_ms = sum(a.elapsed_time(b) for a, b in segs) / args.steps
 
     # same steps again with per-kernel HIP event timing (library hooks on the launch stream)
     cache.kernel_timing(True)
@@ -167,7 +181,15 @@ def main():
     read_bytes = sum(kt[k][2] for k in ("decode", "merge")) / args.steps
     read_ms = sum(kt[k][1] for k in ("decode", "merge")) / args.steps
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    dk = kernels[dominant]
+    dk = dict(kernels[dominant])
+    if dominant == "decode" and "merge" not in kernels:
+        # decode launches back to back with nothing between them: their average duration from
+        # the segment's events (an event pair around each launch adds a few microseconds to a
+        # launch this short)
+        dk["avg_us_per_launch_events"] = dk["avg_us"]
+        dk["avg_us"] = round(decode_seg_ms * 1e3 / dk["launches_per_step"], 3)
+        dk["GBps"] = round(dk["bytes_per_launch"] / (dk["avg_us"] * 1e-6) / 1e9, 1)
+        dk["hbm_frac"] = round(dk["GBps"] / HBM_PEAK_GBPS, 4)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     kv_tokens = sum(len(ids) * n for ids, _, n in calls)
 
@@ -201,13 +223,18 @@ def main():
                         "hbm_frac": round(read_bytes / (read_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                         "bytes_per_step": read_bytes, "device_ms_per_step": round(read_ms, 4),
                         "us_per_layer": round(read_ms * 1e3 / w.n_layers, 3),
+                        "segment_us_per_layer": round(decode_seg_ms * 1e3 / w.n_layers, 3),
                         "splits": stats["last_decode_splits"], "units_by_format": stats["last_decode_units"],
                         "kernel": {0: "default (matrix cores)", 1: "vector ALU", 2: "matrix cores"}[args.decode_kernel]},
         "kernels": kernels,
         "ms_per_step_with_kernel_timing": round(ms_step_timed, 4),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": measured_traffic(dominant, w.name),
-                     "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": dk["avg_us"]},
+                     "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": dk["avg_us"],
+                     "timing": ("decode segment events over the timed steps / launches"
+                                if "avg_us_per_launch_events" in dk else "event pair around each launch"),
+                     **({"avg_launch_us_event_pairs": dk["avg_us_per_launch_events"]}
+                        if "avg_us_per_launch_events" in dk else {})},
     }
 
     result["decode_step"] = decode_step_leg(cache, qs, outs, w, ids_all)
