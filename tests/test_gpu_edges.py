@@ -156,6 +156,34 @@ def test_edge_workloads(name, kw, windows, kernel):
     cache.close()
 
 
+UPI4_CASES = ["unit-plus-one", "many-sinks", "gqa8-d128-bf16", "gqa8-d64", "gqa1-d128", "mixed-tiers-f16-fp8"]
+
+
+@pytest.mark.parametrize("name", UPI4_CASES)
+def test_edge_workloads_ring_depth_4(name, monkeypatch):
+    """The matrix-core kernel with a 4-slot ring (VK_DECODE_UPI=4): waves with at most four
+    units take the short-range path at that depth, longer ones the ring."""
+    monkeypatch.setenv("VK_DECODE_UPI", "4")
+    _, kw, windows = next(c for c in EDGE_CASES if c[0] == name)
+    w = wl.small_workload(**kw)
+    say(f"edge {name} ring depth 4: {w}")
+    cache = make_cache(w, decode_kernel=2)
+    fill(cache, w)
+    encs = {}
+    for s in range(w.n_seqs):
+        kb, vb = host_kv(w, 0, s)
+        encs[s] = oc.encode_sequence(spec_of(w), kb, vb, w.dtype, seq_calls(w, s))
+    q = wl.queries(w, 0, device="cuda")
+    for W in windows:
+        if w.sink_tokens == 0 and W == 0:
+            continue
+        out = cache.decode(q, list(range(w.n_seqs)), 0, window=W)
+        torch.cuda.synchronize()
+        err = check_decode(out, q, w, encs, W)
+        say(f"edge {name} ring depth 4 window {W}: max err {err:.2e}")
+    cache.close()
+
+
 STEAL_CASES = [
     # (name, workload kwargs, windows, sequences checked against the oracle (None: all))
     # 128 (sequence, KV head) pairs: two splits of 16 pieces per pair, 12 waves sharing them
