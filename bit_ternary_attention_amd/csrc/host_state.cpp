@@ -364,6 +364,39 @@ void HostState::count_units(int32_t slot, int32_t window, int64_t out[kFormats])
   }
 }
 
+void HostState::mixed_ranges(int32_t slot, int32_t window, int32_t out[4]) const {
+  const SeqState& st = seqs_[slot];
+  const UnitRanges r = attended_units(st.length, cfg_.sink_tokens, window);
+  const int64_t upp = cfg_.block_size / kUnit;
+  const int64_t n_pages = static_cast<int64_t>(st.pages.size());
+  // logical intervals of the non-ternary runs, in order: the sink range first, then the window
+  std::vector<std::pair<int64_t, int64_t>> iv;
+  for (int part = 0; part < 2; ++part) {
+    const int64_t lo = part == 0 ? 0 : r.b_begin, hi = part == 0 ? r.a_end : r.b_end;
+    const int64_t base = part == 0 ? 0 : r.a_end - r.b_begin;  // unit -> logical unit
+    for (size_t k = 0; k < st.runs.size(); ++k) {
+      const int fmt = st.runs[k].second;
+      if (fmt == VK_FMT_TERNARY2 || fmt >= kFormats) continue;  // freed pages are never attended
+      const int64_t p0 = st.runs[k].first;
+      const int64_t p1 = k + 1 < st.runs.size() ? st.runs[k + 1].first : n_pages;
+      const int64_t u0 = std::max(p0 * upp, lo), u1 = std::min(p1 * upp, hi);
+      if (u0 < u1) iv.emplace_back(u0 + base, u1 + base);
+    }
+  }
+  out[0] = out[1] = out[2] = out[3] = 0;
+  if (iv.empty()) return;
+  size_t cut = iv.size() - 1;  // the two ranges are iv[0 .. cut] and iv[cut + 1 ..]
+  int64_t widest = -1;
+  for (size_t k = 0; k + 1 < iv.size(); ++k)
+    if (iv[k + 1].first - iv[k].second > widest) widest = iv[k + 1].first - iv[k].second, cut = k;
+  out[0] = static_cast<int32_t>(iv.front().first);
+  out[1] = static_cast<int32_t>(iv[cut].second);
+  if (cut + 1 < iv.size()) {
+    out[2] = static_cast<int32_t>(iv[cut + 1].first);
+    out[3] = static_cast<int32_t>(iv.back().second);
+  }
+}
+
 vk_status HostState::reset_seqs(int32_t n_seqs, const int32_t* seq_ids, std::string* err) {
   if (n_seqs < 0 || (n_seqs > 0 && !seq_ids)) { *err = "bad seq list"; return VK_ERR_ARG; }
   std::unordered_set<int32_t> seen;

@@ -133,6 +133,11 @@ class HostState {
   vk_status check_decode(int32_t n_seqs, const int32_t* seq_ids, int32_t window, std::string* err) const;
   // Attended units of `slot` by page format (route counters).
   void count_units(int32_t slot, int32_t window, int64_t out[kFormats]) const;
+  // Two ranges of logical attended units, [out[0], out[1]) and [out[2], out[3]), that hold
+  // every attended unit of `slot` whose page is not ternary (split at the widest gap between
+  // such units; empty ranges when there are none): the part of the sequence a decode's
+  // fp8 / fp16 block has to look at.
+  void mixed_ranges(int32_t slot, int32_t window, int32_t out[4]) const;
 
   vk_status reset_seqs(int32_t n_seqs, const int32_t* seq_ids, std::string* err);
 

@@ -43,6 +43,7 @@ constexpr int kDecodeUnitsPerStep = 4;     // matrix-core kernel: units per clea
                                            // range is a whole number of them when the split size is)
 constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
 constexpr int64_t kDecodeTargetBlocks = 1024;   // matrix-core decode blocks per launch (one round of 4 per CU)
+constexpr int kDecodeMixedParts = 1;  // matrix-core kernel: blocks per (sequence, KV head) for fp8 / fp16 pages
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
   const char* e = std::getenv("VK_DECODE_UPI");
   return (e && e[0] == '4') ? 4 : 8;
@@ -502,9 +503,10 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   int64_t units[3] = {0, 0, 0};
   int32_t splits_used = 1, steal_used = 0;
   const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
-  // sequences per launch: every (sequence, KV head) needs room for two partial slots
-  const int32_t per_launch = static_cast<int32_t>(
-      std::max<int64_t>(1, std::min<int64_t>(vk::kDecodeMaxSeqs, kDecodeScratchItems / (2 * cfg.n_kv_heads))));
+  // sequences per launch: every (sequence, KV head) needs room for a split's partial and the
+  // fp8 / fp16 blocks' partials
+  const int32_t per_launch = static_cast<int32_t>(std::max<int64_t>(
+      1, std::min<int64_t>(vk::kDecodeMaxSeqs, kDecodeScratchItems / ((1 + kDecodeMixedParts) * cfg.n_kv_heads))));
   for (int32_t base = 0; base < n_seqs; base += per_launch) {
     const int32_t nb = std::min<int32_t>(per_launch, n_seqs - base);
     vk::DecodeArgs a{};
@@ -538,14 +540,16 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       a.rows[i] = order[i];
       max_units = std::max(max_units, units_of[order[i]]);
       c->host->count_units(sid, window, cu);
+      c->host->mixed_ranges(sid, window, a.mix[i]);
     }
     for (int f = 0; f < 3; ++f) units[f] += cu[f];
     // matrix-core path: fp8 / fp16 pages go to one more block per (sequence, KV head), which
     // writes one more partial state
     const bool mixed = mfma && (cu[1] + cu[2]) > 0;
+    const int n_mix = mixed ? kDecodeMixedParts : 0;
     const int64_t items = static_cast<int64_t>(nb) * cfg.n_kv_heads;
     const int32_t max_splits = static_cast<int32_t>(
-        std::min<int64_t>(kDecodeMaxSplits - (mixed ? 1 : 0), kDecodeScratchItems / items - (mixed ? 1 : 0)));
+        std::min<int64_t>(kDecodeMaxSplits - n_mix, kDecodeScratchItems / items - n_mix));
     // Splits hold a fixed number of units, so long sequences get more of them than short
     // ones (a block past a sequence's units writes an empty part).
     const int64_t all_units = (cu[0] + cu[1] + cu[2]) * cfg.n_kv_heads;
@@ -568,7 +572,10 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       a.n_splits = (max_units + a.units_per_split - 1) / a.units_per_split;
       a.steal = 1;
     }
-    a.n_parts = a.n_splits + (mixed ? 1 : 0);
+    a.n_parts = a.n_splits + n_mix;
+    if (items * a.n_parts > kDecodeScratchItems)  // (only with thousands of KV heads)
+      return fail(VK_ERR_CAPACITY, "decode partial states: %lld needed, %lld held", static_cast<long long>(items * a.n_parts),
+                  static_cast<long long>(kDecodeScratchItems));
     splits_used = a.n_splits;
     steal_used |= a.steal;
     if (c->timer.on) {
@@ -580,7 +587,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       const double out_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 4.0;
       const double part1 = static_cast<double>(nb) * cfg.n_q_heads * (cfg.head_dim + 2) * 4.0;  // one part
       const double dec_out = a.n_parts > 1 ? part1 * a.n_splits : out_bytes;
-      c->timer.add_bytes(VK_KERNEL_DECODE, tern_bytes + other_bytes + q_bytes + dec_out + (mixed ? part1 : 0.0));
+      c->timer.add_bytes(VK_KERNEL_DECODE, tern_bytes + other_bytes + q_bytes + dec_out + n_mix * part1);
       if (a.n_parts > 1) c->timer.add_bytes(VK_KERNEL_MERGE, part1 * a.n_parts + out_bytes);
     }
     hipError_t e = vk::launch_decode(a, g, s, c->timer.on ? &c->timer : nullptr);

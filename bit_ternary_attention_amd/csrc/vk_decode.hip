@@ -593,7 +593,7 @@ void k_decode_mfma(DecodeArgs a) {
   const Units R = attended(L, a.sink_tokens, a.window);
   const int n_a = R.a_end;
   const int U = R.a_end + (R.b_end - R.b_begin);
-  const bool mixed_part = split >= a.n_splits;  // the extra block of the fp8 / fp16 pages
+  const bool mixed_part = split >= a.n_splits;  // one of the extra blocks of the fp8 / fp16 pages
   const int s_begin = min(split * a.units_per_split, U);  // empty past the sequence's units
   const int s_end = min(s_begin + a.units_per_split, U);
   // a wave's share of the split (stealing waves: the whole split, taken piece by piece)
@@ -1092,73 +1092,79 @@ void k_decode_mfma(DecodeArgs a) {
     make_qb();
     vcur = 1.0f;
     int rank = 0;  // non-ternary units seen so far (uniform)
-    for (int c0 = 0; c0 < U; c0 += 64) {
-      const int lu_l = c0 + lane;
-      const int32_t ent_l = lu_l < U ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
-      uint64_t todo = __ballot(lu_l < U && (static_cast<uint32_t>(ent_l) >> 30) != VK_FMT_TERNARY2);
-      while (todo) {
-        const int k = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        if (rank++ % NW != wave) continue;
-        const int lu = c0 + k;
-        const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
-        h8_t ka[NS];
-        h4_t va[NB];
-        float ksc[4], prt[4], vscale;
-        operands_other(lu, entry, ka, va, ksc, prt, vscale);
-        f4_t s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
-        const int u = unit_of(lu);
-        float sc[4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = u * 16 + 4 * grp + r;
-          const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
-          sc[r] = att ? s4[r] * (ksc[r] * a.scale_log2) : -INFINITY;
-          mx = fmaxf(mx, sc[r]);
-        }
-        mx = max_rows(mx);
-        if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) continue;
-        if (__ballot(mx > m) != 0) {
-          const float mn = fmaxf(m, mx);
-          const float corr = __builtin_amdgcn_exp2f(m - mn);
-#pragma unroll
-          for (int j = 0; j < NB; ++j) oacc[j] *= corr;
-          lsum *= corr;
-          m = mn;
-        }
-        const float ms = m - 14.0f;
-        const h2_t p01 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[0] - ms)),
-                          static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[1] - ms))};
-        const h2_t p23 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[2] - ms)),
-                          static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[3] - ms))};
-        h2_t q01 = as_h2(slot0(h2u(p01))), q23 = as_h2(slot0(h2u(p23)));
-        if constexpr (!DYN) {
-          lsum = __builtin_amdgcn_fdot2(q01, ones, lsum, false);
-          lsum = __builtin_amdgcn_fdot2(q23, ones, lsum, false);
-        } else {
-          // each token's value scale relative to the unit's largest; the sum takes each weight
-          // as P*V sees it (the f16 product divided back by the ratio) so both round alike
-          const float pf[4] = {__builtin_amdgcn_exp2f(sc[0] - ms), __builtin_amdgcn_exp2f(sc[1] - ms),
-                               __builtin_amdgcn_exp2f(sc[2] - ms), __builtin_amdgcn_exp2f(sc[3] - ms)};
-          _Float16 qh[4];
-#pragma unroll
+    // only the two ranges the host found to hold every fp8 / fp16 unit are scanned
+    const int m_lo[2] = {a.mix[b][0], a.mix[b][2]}, m_hi[2] = {min(a.mix[b][1], U), min(a.mix[b][3], U)};
+    for (int rg = 0; rg < 2; ++rg) {
+      for (int c0 = m_lo[rg]; c0 < m_hi[rg]; c0 += 64) {
+        const int lu_l = c0 + lane;
+        const bool in_rg = lu_l < m_hi[rg];
+        const int32_t ent_l = in_rg ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
+        uint64_t todo = __ballot(in_rg && (static_cast<uint32_t>(ent_l) >> 30) != VK_FMT_TERNARY2);
+        while (todo) {
+          const int k = __builtin_ctzll(todo);
+          todo &= todo - 1;
+          // the extra blocks' waves take the units in turn
+          if (rank++ % (NW * (a.n_parts - a.n_splits)) != (split - a.n_splits) * NW + wave) continue;
+          const int lu = c0 + k;
+          const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
+          h8_t ka[NS];
+          h4_t va[NB];
+          float ksc[4], prt[4], vscale;
+          operands_other(lu, entry, ka, va, ksc, prt, vscale);
+          f4_t s4 = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
+          const int u = unit_of(lu);
+          float sc[4];
+          float mx = -INFINITY;
+  #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            qh[r] = static_cast<_Float16>(pf[r] * prt[r]);
-            const float qr = static_cast<float>(qh[r]);  // below the f16 normal range: unrounded
-            if (NSL == 1 || cslot == 0) lsum += qr >= 0x1p-14f ? qr / prt[r] : pf[r];
+            const int t = u * 16 + 4 * grp + r;
+            const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
+            sc[r] = att ? s4[r] * (ksc[r] * a.scale_log2) : -INFINITY;
+            mx = fmaxf(mx, sc[r]);
           }
-          q01 = as_h2(slot0(h2u(h2_t{qh[0], qh[1]})));
-          q23 = as_h2(slot0(h2u(h2_t{qh[2], qh[3]})));
-        }
-        const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(q01), h2u(q23)});
-        const float vs14 = vscale * (1.0f / 16384.0f);
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const f4_t t4 = __builtin_amdgcn_mfma_f32_16x16x16f16(va[j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          oacc[j] += t4 * vs14;
+          mx = max_rows(mx);
+          if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) continue;
+          if (__ballot(mx > m) != 0) {
+            const float mn = fmaxf(m, mx);
+            const float corr = __builtin_amdgcn_exp2f(m - mn);
+  #pragma unroll
+            for (int j = 0; j < NB; ++j) oacc[j] *= corr;
+            lsum *= corr;
+            m = mn;
+          }
+          const float ms = m - 14.0f;
+          const h2_t p01 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[0] - ms)),
+                            static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[1] - ms))};
+          const h2_t p23 = {static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[2] - ms)),
+                            static_cast<_Float16>(__builtin_amdgcn_exp2f(sc[3] - ms))};
+          h2_t q01 = as_h2(slot0(h2u(p01))), q23 = as_h2(slot0(h2u(p23)));
+          if constexpr (!DYN) {
+            lsum = __builtin_amdgcn_fdot2(q01, ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2(q23, ones, lsum, false);
+          } else {
+            // each token's value scale relative to the unit's largest; the sum takes each weight
+            // as P*V sees it (the f16 product divided back by the ratio) so both round alike
+            const float pf[4] = {__builtin_amdgcn_exp2f(sc[0] - ms), __builtin_amdgcn_exp2f(sc[1] - ms),
+                                 __builtin_amdgcn_exp2f(sc[2] - ms), __builtin_amdgcn_exp2f(sc[3] - ms)};
+            _Float16 qh[4];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              qh[r] = static_cast<_Float16>(pf[r] * prt[r]);
+              const float qr = static_cast<float>(qh[r]);  // below the f16 normal range: unrounded
+              if (NSL == 1 || cslot == 0) lsum += qr >= 0x1p-14f ? qr / prt[r] : pf[r];
+            }
+            q01 = as_h2(slot0(h2u(h2_t{qh[0], qh[1]})));
+            q23 = as_h2(slot0(h2u(h2_t{qh[2], qh[3]})));
+          }
+          const h4_t pb = __builtin_bit_cast(h4_t, u2_t{h2u(q01), h2u(q23)});
+          const float vs14 = vscale * (1.0f / 16384.0f);
+  #pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const f4_t t4 = __builtin_amdgcn_mfma_f32_16x16x16f16(va[j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            oacc[j] += t4 * vs14;
+          }
         }
       }
     }

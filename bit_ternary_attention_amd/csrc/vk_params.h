@@ -87,6 +87,7 @@ struct DecodeArgs {
   int32_t slots[kDecodeMaxSeqs];   // launch order: longest attended range first
   int32_t lens[kDecodeMaxSeqs];
   int32_t rows[kDecodeMaxSeqs];    // query / output row (within the launch) of each
+  int32_t mix[kDecodeMaxSeqs][4];  // two logical-unit ranges holding every fp8 / fp16 unit
 };
 
 struct QuantArgs {

@@ -78,6 +78,9 @@ int hs_check_decode(void* h, int n_seqs, const int* ids, int window) {
   return static_cast<vk::HostState*>(h)->check_decode(n_seqs, ids, window, &e);
 }
 
+void hs_mixed_ranges(void* h, int seq, int window, int* out4) {
+  static_cast<vk::HostState*>(h)->mixed_ranges(seq, window, out4);
+}
 int hs_length(void* h, int seq) { return static_cast<vk::HostState*>(h)->seq(seq).length; }
 int hs_n_pages(void* h, int seq) { return static_cast<int>(static_cast<vk::HostState*>(h)->seq(seq).pages.size()); }
 int hs_page_entry(void* h, int seq, int page) { return static_cast<vk::HostState*>(h)->seq(seq).pages[page]; }

@@ -103,6 +103,7 @@ def hs():
     L.hs_tokens_stored.restype = ctypes.c_longlong
     L.hs_tokens_stored.argtypes = [ctypes.c_void_p, ctypes.c_int]
     L.hs_count_units.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(ctypes.c_longlong)]
+    L.hs_mixed_ranges.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(ctypes.c_int)]
     L.hs_reset.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int)]
     L.hs_attended_units.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P(ctypes.c_int)]
     L.hs_retier.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), P(ctypes.c_int), ctypes.c_int,
@@ -277,6 +278,48 @@ def test_route_counters_match_page_formats(hs):
         for u in units:
             want[enc.page_format[u]] += 1
         assert list(out) == want, W
+
+
+def _check_mixed_ranges(hs, h, seq, W):
+    """The two ranges cover every attended non-ternary unit (logical numbering) and are as short
+    as two intervals can be: the span minus the widest gap between runs of such units."""
+    L = hs.hs_length(h.h, seq)
+    out = (ctypes.c_int * 4)()
+    hs.hs_mixed_ranges(h.h, seq, W, out)
+    lo0, hi0, lo1, hi1 = list(out)
+    bs = h.cfg.block_size
+    fmts = [(e >> 30) & 3 for e in h.pages(seq)]
+    units = sorted({int(t) // 16 for t in oa.attended_tokens(L, h.cfg.sink_tokens, W)})
+    mixed = [i for i, u in enumerate(units) if fmts[u * 16 // bs] != 0]
+    assert 0 <= lo0 <= hi0 <= lo1 <= hi1 <= len(units) or (lo1 == hi1 == 0 and hi0 <= len(units)), list(out)
+    for i in mixed:
+        assert lo0 <= i < hi0 or lo1 <= i < hi1, (seq, W, i, list(out))
+    if not mixed:
+        assert (hi0 - lo0) + (hi1 - lo1) == 0
+        return
+    gaps = [b - a - 1 for a, b in zip(mixed, mixed[1:])]
+    assert (hi0 - lo0) + (hi1 - lo1) == (mixed[-1] - mixed[0] + 1) - max(gaps + [0]), (seq, W, list(out))
+
+
+def test_mixed_ranges_cover_every_non_ternary_unit(hs):
+    for bs, S, sinkf, R, recf in [(16, 4, 2, 256, 1), (16, 40, 1, 0, 1), (32, 4, 0, 100, 1), (64, 20, 2, 48, 2),
+                                  (16, 4, 0, 0, 1)]:
+        cfg = base_cfg(block_size=bs, sink_tokens=S, sink_format=sinkf, recent_tokens=R, recent_format=recf,
+                       max_tokens_per_seq=4096, pages_ternary=800, pages_fp8=200, pages_f16=50, max_seqs=3)
+        h = Host(hs, cfg)
+        for n in (1008, 48, 16, 304, 37):  # whole units, then a ragged tail
+            assert h.append([0, 2], n)[0] == 0
+            for W in (-1, 256, 100, 17, 0, 1):
+                if S == 0 and W == 0:
+                    continue
+                _check_mixed_ranges(hs, h, 0, W)
+        if R > 0 and recf == 1:
+            assert h.retier([0])[0] == 0    # fp8 pages past the window become ternary
+            for W in (-1, 256, 5):
+                _check_mixed_ranges(hs, h, 0, W)
+        if h.check_decode([2], 300) == 0:
+            assert h.evict([2], 300)[0] == 0
+            _check_mixed_ranges(hs, h, 2, 300)
 
 
 def _plan(hs, total, max_units, target, max_splits, min_units, granule=1):
