@@ -175,6 +175,12 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
  * 1/sqrt(head_dim).  Query head h reads KV head h / (n_q_heads/n_kv_heads).
  * Pages are read in their stored format through the block table; no dense
  * copy is made.  Every sequence must have L >= 1.
+ * The call only enqueues kernel launches on `stream` (no allocation, copy or
+ * synchronisation), so it may be captured into a HIP graph.  A replay repeats
+ * the launches as planned at capture (sequence lengths, window, split plan,
+ * the page-format ranges of each sequence) and reads the pages and block table
+ * current when it runs: it is valid while the captured sequences keep the
+ * lengths and tier layout they had at capture.
  */
 VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, const int32_t* seq_ids,
                                 const void* q, int32_t q_dtype, int32_t window, float softmax_scale,
