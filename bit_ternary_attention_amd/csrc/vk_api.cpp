@@ -487,6 +487,10 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   const vk_cache_config& cfg = c->cfg;
   if (layer < 0 || layer >= cfg.n_layers) return fail(VK_ERR_ARG, "layer %d out of range", layer);
   if (q_dtype != VK_DTYPE_F16 && q_dtype != VK_DTYPE_BF16) return fail(VK_ERR_ARG, "q_dtype must be F16 or BF16");
+  if (n_seqs == 0) {  // nothing to attend: no launch (q and out may be NULL)
+    g_error.clear();
+    return VK_OK;
+  }
   if (!q || !out) return fail(VK_ERR_ARG, "q or out is NULL");
   if ((reinterpret_cast<uintptr_t>(q) & 3) || (reinterpret_cast<uintptr_t>(out) & 15))
     return fail(VK_ERR_ARG, "q must be 4-byte and out 16-byte aligned");

@@ -174,7 +174,8 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
  * retention-preserving case of Minima-KV).  softmax_scale <= 0 means
  * 1/sqrt(head_dim).  Query head h reads KV head h / (n_q_heads/n_kv_heads).
  * Pages are read in their stored format through the block table; no dense
- * copy is made.  Every sequence must have L >= 1.
+ * copy is made.  Every sequence must have L >= 1.  n_seqs = 0 does nothing
+ * and returns VK_OK (q and out may then be NULL).
  * The call only enqueues kernel launches on `stream` (no allocation, copy or
  * synchronisation), so it may be captured into a HIP graph.  A replay repeats
  * the launches as planned at capture (sequence lengths, window, split plan,

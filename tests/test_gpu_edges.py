@@ -296,6 +296,26 @@ def test_many_sequences_subset_and_order(kernel):
     cache.close()
 
 
+def test_empty_and_zero_length_calls():
+    """A decode of no sequences is a no-op; appends of no tokens and empty tensors are refused;
+    the cache is unchanged and still decodes."""
+    w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(40,))
+    cache = make_cache(w, decode_kernel=2)
+    fill(cache, w)
+    q = wl.queries(w, 0, device="cuda")
+    before = cache.decode(q, [0], 0).cpu()
+    out = cache.decode(torch.empty((0, 4, 64), dtype=torch.float16, device="cuda"), [], 0)
+    assert out.shape == (0, 4, 64)
+    k0 = torch.zeros((1, 1, 0, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises((vk.VkError, ValueError)):
+        cache.append(k0, k0, [0])
+    with pytest.raises((vk.VkError, ValueError)):
+        vk.quantize_pack(torch.empty(0, dtype=torch.float16, device="cuda"))
+    assert cache.seq_length(0) == 40
+    assert torch.equal(cache.decode(q, [0], 0).cpu(), before)
+    cache.close()
+
+
 def test_errors_leave_cache_unchanged_and_usable():
     w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(64, 64), n_seqs=2)
     cache = make_cache(w, max_tokens=256)  # exactly the pages two 64-token sequences need (+2 slack)
