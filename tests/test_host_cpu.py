@@ -6,9 +6,11 @@
   g++-built test shim) against the oracle's format rule and attended set.
 """
 import ctypes
+import json
 import os
 import re
 import subprocess
+import sys
 import tempfile
 
 import numpy as np
@@ -459,3 +461,12 @@ def test_eviction_arguments(hs):
     assert h.evict([0], 100) == (0, 0)           # already freed
     assert h.check_decode([0], 108) == 0         # the window starts at 192
     assert h.check_decode([0], 109) == vk.ERR_ARG and h.check_decode([0], -1) == vk.ERR_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus above 1 prints why (one JSON line) and exits with 2."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
