@@ -7,7 +7,8 @@ oracle's float64 attention.
 """
 from __future__ import annotations
 
-import math
+import concurrent.futures
+import os
 import sys
 from typing import Dict, List, Sequence
 
@@ -19,6 +20,8 @@ from bit_ternary_attention_amd import workloads as wl
 from oracle import attention as oa
 from oracle import cache as oc
 from oracle import ternary as ot
+
+import page_codec as pc
 
 GAMMA_RTOL = 2.0 ** -22
 ATTN_ATOL = 2e-3
@@ -181,31 +184,128 @@ def check_decode(out: torch.Tensor, q: torch.Tensor, w: wl.Workload, encs: Dict[
     return worst
 
 
-def run_workload(w: wl.Workload, sample_seqs: Sequence[int], page_layers: Sequence[int],
-                 decode_layers: Sequence[int], shuffle=None, decode_kernel=0, fp8_dynamic=0) -> dict:
+def check_sequence(w: wl.Workload, spec: oc.CacheSpec, seq: int, kbits, vbits, pages, q_row, out_row,
+                   window: int, scale=None) -> dict:
+    """Every check of one (layer, sequence) against the oracle; runs on a worker thread.
+
+    pages: None, or (bytes, formats, gammas) of every page as read from the device: then
+    formats, every ternary page's gamma (2^-22 rel of the oracle's) and every stored code,
+    fp8 byte, fp16 value and dynamic scale are compared (codes re-encoded with the device's
+    gamma where the two gammas differ in the last bit).  out_row: None, or the device's decode
+    output for the sequence, compared with the oracle's float64 attention over its own encoding.
+    """
+    calls = seq_calls(w, seq)
+    enc = oc.encode_sequence(spec, kbits, vbits, w.dtype, calls)
+    rep = {"seq": seq, "pages": 0, "err": 0.0}
+    if pages is not None:
+        buf, fmts, gams = pages
+        n_pages = len(enc.page_format)
+        assert len(fmts) == n_pages, (seq, len(fmts), n_pages)
+        assert list(fmts) == enc.page_format, (seq, "page formats differ")
+        bs = w.block_size
+        dev_gamma = [(np.nan, np.nan)] * len(calls)
+        override = False
+        tern = np.nonzero(fmts == oc.TERNARY2)[0]
+        if tern.size:
+            call_of_page = enc.token_call[tern * bs]
+            want = np.array([enc.gamma[c] for c in call_of_page], dtype=np.float32)   # [n, 2]
+            got = gams[tern].astype(np.float32)
+            rel = np.abs(got.astype(np.float64) - want.astype(np.float64)) / want.astype(np.float64)
+            assert np.all(rel <= GAMMA_RTOL), (seq, "gamma", float(rel.max()))
+            for ci in range(len(calls)):
+                sel = np.nonzero(call_of_page == ci)[0]
+                if sel.size:
+                    g = got[sel]
+                    assert np.all(g == g[0]), (seq, ci, "pages of one call hold different gammas")
+                    dev_gamma[ci] = (float(g[0, 0]), float(g[0, 1]))
+                    override |= bool(np.any(g[0] != want[sel[0]]))
+        ref = enc if not override else oc.encode_sequence(spec, kbits, vbits, w.dtype, calls, gamma_override=dev_gamma)
+        got = pc.decode_pages(buf, fmts, enc.length, w.n_kv_heads, w.head_dim, bs, spec.fp8_dynamic)
+        for name in ("k_code", "v_code", "k_fp8", "v_fp8", "k_f16", "v_f16"):
+            if not np.array_equal(got[name], getattr(ref, name)):
+                bad = np.argwhere(got[name] != getattr(ref, name))
+                raise AssertionError(f"seq {seq}: {name} differs at {bad.shape[0]} places, first (token, head, dim) "
+                                     f"{tuple(bad[0])} page {bad[0][0] // bs}")
+        if spec.fp8_dynamic:
+            for name in ("k_fp8_scale", "v_fp8_scale"):
+                assert np.array_equal(got[name], getattr(ref, name)), (seq, name)
+        assert not got["k_pad"].any() and not got["v_pad"].any(), (seq, "padding codes")
+        rep["pages"] = n_pages
+    if out_row is not None:
+        refo = oa.decode_attention(q_row, enc.k_hat, enc.v_hat, enc.length, w.sink_tokens, window, scale)
+        err = float(np.max(np.abs(out_row - refo)))
+        assert err <= ATTN_ATOL, (seq, err)
+        rep["err"] = err
+    return rep
+
+
+def read_all_pages(cache: vk.Cache, layer: int, seq: int):
+    n = -(-cache.seq_length(seq) // cache.cfg.block_size)
+    return cache.read_pages(layer, seq, 0, n)
+
+
+def default_workers() -> int:
+    return max(1, min(8, (os.cpu_count() or 2) // 2))
+
+
+def check_layer(cache: vk.Cache, w: wl.Workload, layer: int, seqs: Sequence[int], pages: bool, decode: bool,
+                fp8_dynamic=0, window=None, workers: int = None, tag: str = "") -> dict:
+    """Checks (layer, s) for every s in seqs: all pages and/or the decode output of every sequence.
+
+    The device work (inputs regenerated on the device, page reads, one decode of every
+    sequence of the workload) runs on this thread; the oracle runs on a pool of worker
+    threads (numpy releases the GIL in its array loops), a few sequences at a time.
+    """
+    window = w.window if window is None else window
+    spec = spec_of(w, fp8_dynamic=fp8_dynamic)
+    out = q = None
+    if decode:
+        q = wl.queries(w, layer, device="cuda")
+        out = cache.decode(q, list(range(w.n_seqs)), layer, window=window)
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy()
+        assert np.all(np.isfinite(o))
+        qv = q_values(q, w.dtype)
+    workers = workers or default_workers()
+    worst, n_pages, done = 0.0, 0, 0
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        pending = []
+
+        def drain(limit):
+            nonlocal worst, n_pages, done
+            while len(pending) > limit:
+                r = pending.pop(0).result()
+                worst = max(worst, r["err"])
+                n_pages += r["pages"]
+                done += 1
+
+        for s in seqs:
+            kb, vb = host_kv(w, layer, s)
+            pg = read_all_pages(cache, layer, s) if pages else None
+            pending.append(ex.submit(check_sequence, w, spec, s, kb, vb, pg, qv[s] if decode else None,
+                                     o[s] if decode else None, window))
+            del kb, vb, pg
+            drain(workers)
+        drain(0)
+    say(f"[{w.name}]{tag} layer {layer}: {done} sequences, {n_pages} pages bit-exact, "
+        f"decode max abs err {worst:.3e}")
+    return {"max_err": worst, "pages": n_pages, "seqs": done}
+
+
+def run_workload(w: wl.Workload, page_layers: Sequence[int], decode_layers: Sequence[int], seqs=None,
+                 shuffle=None, decode_kernel=0, fp8_dynamic=0) -> dict:
+    """The workload at full size: every sequence's pages (in page_layers) and decode output
+    (in decode_layers) compared with the oracle."""
     say(f"[{w.name}] create+fill (decode kernel {decode_kernel}, dynamic fp8 {fp8_dynamic})")
     cache = make_cache(w, shuffle=shuffle, decode_kernel=decode_kernel, fp8_dynamic=fp8_dynamic)
     fill(cache, w)
-    report = {"gamma_checked": 0, "max_err": 0.0}
-    encs_by_layer = {}
+    seqs = list(range(w.n_seqs)) if seqs is None else list(seqs)
+    report = {"max_err": 0.0, "pages": 0, "seqs_decoded": 0}
     for layer in sorted(set(page_layers) | set(decode_layers)):
-        encs = {}
-        for s in sample_seqs:
-            kb, vb = host_kv(w, layer, s)
-            if layer in page_layers:
-                say(f"[{w.name}] pages layer {layer} seq {s}")
-                encs[s] = check_pages(cache, w, layer, s, kb, vb, fp8_dynamic=fp8_dynamic)
-            else:
-                encs[s] = oc.encode_sequence(spec_of(w, fp8_dynamic=fp8_dynamic), kb, vb, w.dtype, seq_calls(w, s))
-        encs_by_layer[layer] = encs
-        if layer in decode_layers:
-            q = wl.queries(w, layer, device="cuda")
-            out = cache.decode(q, list(range(w.n_seqs)), layer, window=w.window)
-            torch.cuda.synchronize()
-            err = check_decode(out, q, w, encs, w.window)
-            report["max_err"] = max(report["max_err"], err)
-            say(f"[{w.name}] decode kernel {decode_kernel} layer {layer}: max abs err {err:.3e}")
-        encs_by_layer.pop(layer, None)
+        r = check_layer(cache, w, layer, seqs, layer in page_layers, layer in decode_layers, fp8_dynamic=fp8_dynamic)
+        report["max_err"] = max(report["max_err"], r["max_err"])
+        report["pages"] += r["pages"] if layer in page_layers else 0
+        report["seqs_decoded"] += r["seqs"] if layer in decode_layers else 0
     report["stats"] = cache.stats()
     cache.close()
     return report
