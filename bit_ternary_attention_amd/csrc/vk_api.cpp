@@ -88,7 +88,7 @@ class EventTimer : public vk::LaunchTimer {
     pending_.push_back(open_);
     launches[kind] += 1;
     open_.kind = -1;
-    if (pending_.size() >= 4096) flush();
+    if (pending_.size() >= (1u << 16)) flush();  // (a flush waits for the device)
   }
   // Waits for every recorded pair and folds it into the totals.
   void flush() {
