@@ -731,31 +731,70 @@ VK_API int64_t vk_quantize_pack_workspace_bytes(int64_t n) {
   return 256 + ((n_blk * 8 + 255) & ~int64_t(255));
 }
 
-VK_API vk_status vk_quantize_pack(const void* x, int64_t n, int32_t dtype, float eps, const float* gamma_in,
-                                  uint8_t* packed, float* gamma_out, void* workspace, int64_t workspace_bytes,
-                                  void* stream) {
-  if (!x || !packed || !gamma_out || !workspace) return fail(VK_ERR_ARG, "NULL argument");
+namespace {
+
+// Checks shared by the flat entry points; "" when the arguments are usable.
+vk_status check_quantize_args(const void* x, int64_t n, int32_t dtype, float eps, const uint8_t* packed,
+                              const float* gamma_out) {
+  if (!x || !packed || !gamma_out) return fail(VK_ERR_ARG, "NULL argument");
   if (n < 8 || n % 8) return fail(VK_ERR_ARG, "n must be a positive multiple of 8");
   if (dtype != VK_DTYPE_F16 && dtype != VK_DTYPE_BF16) return fail(VK_ERR_ARG, "dtype must be F16 or BF16");
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(VK_ERR_ARG, "eps must be finite and >= 0");
-  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(packed) & 1) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 15))
-    return fail(VK_ERR_ARG, "x and workspace must be 16-byte aligned, packed 2-byte aligned");
-  if (workspace_bytes < vk_quantize_pack_workspace_bytes(n)) return fail(VK_ERR_ARG, "workspace too small");
-  const int64_t n_blk = (n + vk::kAbsElemsPerBlock - 1) / vk::kAbsElemsPerBlock;
-  if (n_blk > 0x7FFFFFFF) return fail(VK_ERR_ARG, "tensor too large");
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(packed) & 1))
+    return fail(VK_ERR_ARG, "x must be 16-byte aligned, packed 2-byte aligned");
+  return VK_OK;
+}
+
+vk::QuantArgs quantize_args(const void* x, int64_t n, int32_t dtype, float eps, const float* gamma_in,
+                            uint8_t* packed, float* gamma_out, uint8_t* scratch) {
   vk::QuantArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.packed = packed;
   a.gamma_in = gamma_in;
   a.gamma_out = gamma_out;
-  a.seg = static_cast<vk::SegInfo*>(workspace);
-  a.partials = reinterpret_cast<double*>(static_cast<uint8_t*>(workspace) + 256);
+  a.seg = reinterpret_cast<vk::SegInfo*>(scratch);
+  a.partials = reinterpret_cast<double*>(scratch + 256);
   a.n = n;
   a.dtype = dtype;
-  a.n_blk = static_cast<int32_t>(n_blk);
+  a.n_blk = static_cast<int32_t>((n + vk::kAbsElemsPerBlock - 1) / vk::kAbsElemsPerBlock);
   a.eps = eps;
+  return a;
+}
+
+}  // namespace
+
+VK_API vk_status vk_quantize_pack(const void* x, int64_t n, int32_t dtype, float eps, const float* gamma_in,
+                                  uint8_t* packed, float* gamma_out, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  vk_status st = check_quantize_args(x, n, dtype, eps, packed, gamma_out);
+  if (st) return st;
+  if (!workspace) return fail(VK_ERR_ARG, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return fail(VK_ERR_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < vk_quantize_pack_workspace_bytes(n)) return fail(VK_ERR_ARG, "workspace too small");
+  const int64_t n_blk = (n + vk::kAbsElemsPerBlock - 1) / vk::kAbsElemsPerBlock;
+  if (n_blk > 0x7FFFFFFF) return fail(VK_ERR_ARG, "tensor too large");
+  const vk::QuantArgs a = quantize_args(x, n, dtype, eps, gamma_in, packed, gamma_out, static_cast<uint8_t*>(workspace));
   hipError_t e = vk::launch_quantize(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(VK_ERR_HIP, "quantize kernels: %s", hipGetErrorString(e));
+  g_error.clear();
+  return VK_OK;
+}
+
+VK_API int64_t vk_quantize_pack_noalloc_max_elems(void) { return vk::kQuantNoAllocMaxElems; }
+
+VK_API vk_status vk_quantize_pack_noalloc(const void* x, int64_t n, int32_t dtype, float eps, const float* gamma_in,
+                                          uint8_t* packed, float* gamma_out, void* stream) {
+  vk_status st = check_quantize_args(x, n, dtype, eps, packed, gamma_out);
+  if (st) return st;
+  if (n > vk::kQuantNoAllocMaxElems)
+    return fail(VK_ERR_CAPACITY, "n = %lld exceeds the %lld elements the allocation-free scratch holds; "
+                "use vk_quantize_pack with a workspace", static_cast<long long>(n),
+                static_cast<long long>(vk::kQuantNoAllocMaxElems));
+  void* scratch = nullptr;
+  hipError_t e = vk::quantize_noalloc_scratch(&scratch);
+  if (e != hipSuccess) return fail(VK_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+  const vk::QuantArgs a = quantize_args(x, n, dtype, eps, gamma_in, packed, gamma_out, static_cast<uint8_t*>(scratch));
+  e = vk::launch_quantize(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(VK_ERR_HIP, "quantize kernels: %s", hipGetErrorString(e));
   g_error.clear();
   return VK_OK;

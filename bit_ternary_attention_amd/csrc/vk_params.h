@@ -103,6 +103,12 @@ struct QuantArgs {
   float eps;
 };
 
+// Allocation-free flat quantise+pack: its scratch is a device array of the library, sized for
+// tensors of up to 2^31 elements (one float64 partial per absmean block, after a 256-byte
+// finalize record).
+constexpr int64_t kQuantNoAllocMaxElems = int64_t(1) << 31;
+constexpr int64_t kQuantNoAllocScratchBytes = 256 + (kQuantNoAllocMaxElems / kAbsElemsPerBlock) * 8;
+
 struct RetierArgs {
   PoolsView P;
   const RetierTask* tasks;  // [n_tasks]
@@ -124,5 +130,8 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, Laun
 hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_retier(const RetierArgs& a, hipStream_t s, LaunchTimer* t);
+// Device address of the allocation-free scratch on the current device (looked up on the first
+// call per device, then cached).
+hipError_t quantize_noalloc_scratch(void** ptr);
 
 }  // namespace vk

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <mutex>
+
 #include "host_state.h"
 #include "vk_params.h"
 
@@ -489,6 +491,33 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, Laun
   }
   if (t) t->end(VK_KERNEL_PACK, s);
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free flat entry point: the finalize record (256 bytes) and the
+// absmean partials (8 bytes per 16384-element block) of one tensor of at most
+// kQuantNoAllocMaxElems elements.  Every device the library runs on holds one copy, and every
+// call on that device shares it.
+static __device__ __align__(256) uint8_t scratch[kQuantNoAllocScratchBytes];
+
+hipError_t quantize_noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // the array's name is a host-side stand-in: its device address is looked up once per
+    // device, with that device current, and only that address is handed to kernels
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {

@@ -68,6 +68,8 @@ EXPORTS = {
     "vk_release": (_c_i32, [_c_vp]),
     "vk_quantize_pack_workspace_bytes": (_c_i64, [_c_i64]),
     "vk_quantize_pack": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "vk_quantize_pack_noalloc_max_elems": (_c_i64, []),
+    "vk_quantize_pack_noalloc": (_c_i32, [_c_vp, _c_i64, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp, _c_vp]),
     "vk_last_error": (ctypes.c_char_p, []),
     "vk_status_string": (ctypes.c_char_p, [_c_i32]),
 }
@@ -293,4 +295,19 @@ def quantize_pack(x, eps: float = 1e-5, gamma=None, packed=None, gamma_out=None,
     _check(lib().vk_quantize_pack(ctypes.c_void_p(x.data_ptr()), n, _dtype_code(x), eps, gptr,
                                   ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(gamma_out.data_ptr()),
                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return packed, gamma_out
+
+
+def quantize_pack_noalloc(x, packed, gamma_out, eps: float = 1e-5, gamma=None, stream=None):
+    """vk_quantize_pack without a workspace (the library's own device scratch): the caller
+    passes the input and both outputs (packed uint8 [n/4], gamma float32 [1])."""
+    if not (x.is_cuda and x.is_contiguous()):
+        raise ValueError("x must be a contiguous device tensor")
+    n = x.numel()
+    if packed.numel() != n // 4 or gamma_out.numel() < 1:
+        raise ValueError("packed must hold n/4 bytes and gamma_out one float")
+    gptr = ctypes.c_void_p(gamma.data_ptr()) if gamma is not None else ctypes.c_void_p(0)
+    _check(lib().vk_quantize_pack_noalloc(ctypes.c_void_p(x.data_ptr()), n, _dtype_code(x), eps, gptr,
+                                          ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(gamma_out.data_ptr()),
+                                          _stream(stream)))
     return packed, gamma_out

@@ -317,6 +317,24 @@ VK_API vk_status vk_quantize_pack(const void* x, int64_t n, int32_t dtype, float
                                   uint8_t* packed, float* gamma_out, void* workspace, int64_t workspace_bytes,
                                   void* stream);
 
+/*
+ * Allocation-free flat quantise+pack, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments and results as
+ * vk_quantize_pack without the workspace: the absmean partials and the
+ * finalize record live in a device array of the library, 1 MiB + 256 bytes,
+ * held by every device the library runs on until the process ends; its device
+ * address is looked up on the first call on each device.  Nothing is
+ * allocated and nothing waits.  n <= vk_quantize_pack_noalloc_max_elems()
+ * (2^31), else VK_ERR_CAPACITY and nothing is enqueued.  Every call on one
+ * device uses the same scratch: calls whose device work may overlap (on
+ * different streams of one device, without ordering between them) race and
+ * give wrong results; calls ordered on one stream are safe.
+ */
+VK_API int64_t vk_quantize_pack_noalloc_max_elems(void);
+VK_API vk_status vk_quantize_pack_noalloc(const void* x, int64_t n, int32_t dtype, float eps, const float* gamma_in,
+                                          uint8_t* packed, float* gamma_out, void* stream);
+
 /* Thread-local text of the last error ("" if none). */
 VK_API const char* vk_last_error(void);
 
