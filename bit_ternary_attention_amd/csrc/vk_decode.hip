@@ -49,11 +49,30 @@ __device__ __forceinline__ h2_t fp8x2(uint32_t x) {
   return as_h2(f) * k256;
 }
 
+// Query elements enter the products as f16.  bf16 queries reach 2^128, beyond f16, so every
+// query of a (sequence, KV head) is first scaled by one power of two 2^sh that puts its
+// largest magnitude in [2^14, 2^15) (exact: a power-of-two product of a 16-bit value), and the
+// scores are multiplied back by 2^-sh.  Every element within 2^-28 of the largest stays exact
+// in f16 (a normal f16 value); smaller ones round to the f16 subnormal grid.
 template <int QDT>
-__device__ __forceinline__ uint32_t q_f16(uint16_t h) {
-  if (QDT == 0) return h;
-  return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(__uint_as_float(static_cast<uint32_t>(h) << 16))));
+__device__ __forceinline__ float q_value(uint16_t h) {
+  if (QDT == 0) return static_cast<float>(__builtin_bit_cast(_Float16, h));
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
+
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(x)));
+}
+
+// Exponent shift sh for a largest magnitude qmax (clamped to [-126, 126], where 2^sh and 2^-sh
+// are normal floats; 0 for qmax = 0).
+__device__ __forceinline__ int q_shift(float qmax) {
+  if (!(qmax > 0.0f)) return 0;
+  const int e = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFFu) - 127;  // floor(log2 qmax) for normals
+  const int sh = 14 - e;
+  return sh < -126 ? -126 : (sh > 126 ? 126 : sh);
+}
+__device__ __forceinline__ float pow2i(int k) { return __uint_as_float(static_cast<uint32_t>(k + 127) << 23); }
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -135,11 +154,17 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
   const int u_begin = min(split * a.units_per_split, U);
   const int u_end = min(u_begin + a.units_per_split, U);
 
-  // query rows of this KV head's group, as f16 pairs (d, d+8) within each 16-dim block
+  // query rows of this KV head's group, as f16 pairs (d, d+8) within each 16-dim block, scaled
+  // by 2^sh (q_shift); qsl = softmax scale * log2(e) * 2^-sh multiplies the scores
+  const uint16_t* qgrp = a.q + (static_cast<int64_t>(a.rows[b]) * a.hq + kvh * G) * D;
+  float qmax = 0.0f;
+  for (int j = lane; j < G * D; j += 64) qmax = fmaxf(qmax, fabsf(q_value<QDT>(qgrp[j])));
+  const int qsh = __builtin_amdgcn_readfirstlane(q_shift(wave_max(qmax)));
+  const float qmul = pow2i(qsh), qsl = a.scale_log2 * pow2i(-qsh);
   for (int j = lane; j < G * QP; j += 64) {
     const int hh = j / QP, jj = j % QP, w = jj >> 3, ii = jj & 7;
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(a.rows[b]) * a.hq + kvh * G + hh) * D;
-    q2[j] = q_f16<QDT>(qrow[16 * w + ii]) | (q_f16<QDT>(qrow[16 * w + 8 + ii]) << 16);
+    const uint16_t* qrow = qgrp + hh * D;
+    q2[j] = f16_bits(q_value<QDT>(qrow[16 * w + ii]) * qmul) | (f16_bits(q_value<QDT>(qrow[16 * w + 8 + ii]) * qmul) << 16);
   }
   __syncthreads();
 
@@ -237,7 +262,7 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
         kscale = 1.0f;
       }
       if (att) {
-        const float ks = kscale * a.scale_log2;
+        const float ks = kscale * qsl;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) logit[hh] = acc[hh] * ks;
       }
@@ -692,6 +717,7 @@ void k_decode_mfma(DecodeArgs a) {
   // is ks (2^14 acc - qoff), qoff = 2^14 sum_d off(d) q_d + sum_d q_d.
   h8_t qb[NS];
   float qsum = 0.0f, qoff = 0.0f;
+  float qsl = a.scale_log2;  // softmax scale * log2(e) * 2^-sh for the query scaled by 2^sh
   const uint16_t* qhead = a.q + (qo0 + (c16 & (G - 1))) * D;
   auto make_qb = [&]() {
     // (the memory clobber keeps the query's loads, and the wait for them, after the page
@@ -700,16 +726,30 @@ void k_decode_mfma(DecodeArgs a) {
     const uint16_t* qrow = qhead + dbase;
     uint32_t w[NS][4];
     float sum = 0.0f;
+    uint4 x[NC][2];
+    float qmax = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const uint4 x0 = reinterpret_cast<const uint4*>(qrow + 16 * c)[0];  // dims 16c .. 16c+7
-      const uint4 x1 = reinterpret_cast<const uint4*>(qrow + 16 * c)[1];  // dims 16c+8 .. 16c+15
-      const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+      x[c][0] = reinterpret_cast<const uint4*>(qrow + 16 * c)[0];  // dims 16c .. 16c+7
+      x[c][1] = reinterpret_cast<const uint4*>(qrow + 16 * c)[1];  // dims 16c+8 .. 16c+15
+      const uint32_t all[8] = {x[c][0].x, x[c][0].y, x[c][0].z, x[c][0].w, x[c][1].x, x[c][1].y, x[c][1].z, x[c][1].w};
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        qmax = fmaxf(qmax, fabsf(q_value<QDT>(static_cast<uint16_t>((all[i >> 1] >> (16 * (i & 1))) & 0xFFFFu))));
+    }
+    // one power of two for the whole group (every lane holds one of its query heads)
+    const int qsh = __builtin_amdgcn_readfirstlane(q_shift(wave_max(qmax)));
+    const float qmul = pow2i(qsh);
+    qsl = a.scale_log2 * pow2i(-qsh);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t lo[4] = {x[c][0].x, x[c][0].y, x[c][0].z, x[c][0].w}, hi[4] = {x[c][1].x, x[c][1].y, x[c][1].z, x[c][1].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t e0 = (lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const uint32_t e1 = (hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        const uint32_t pr = q_f16<QDT>(static_cast<uint16_t>(e0)) | (q_f16<QDT>(static_cast<uint16_t>(e1)) << 16);
+        const uint32_t pr = f16_bits(q_value<QDT>(static_cast<uint16_t>(e0)) * qmul) |
+                            (f16_bits(q_value<QDT>(static_cast<uint16_t>(e1)) * qmul) << 16);
         w[2 * c + (i >> 2)][i & 3] = pr;
         const h2_t hp = as_h2(pr);
         sum += static_cast<float>(hp[0]) + static_cast<float>(hp[1]);
@@ -804,7 +844,7 @@ void k_decode_mfma(DecodeArgs a) {
   auto process_clean = [&](const Chunk& cc, const UnitRaw<NC, NV> (&r)[SU], bool partial, int lu0, int lu_end) {
     constexpr int UT = NSL == 1 ? 1 : NSL;  // units per score tile
     constexpr int NT = SU / UT;             // score tiles
-    const float ks = cc.gk0 * a.scale_log2;
+    const float ks = cc.gk0 * qsl;
     const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
     float sc[NT][4];
 #pragma unroll
@@ -914,7 +954,7 @@ void k_decode_mfma(DecodeArgs a) {
         continue;
       }
       const UnitRaw<NC, NV>& raw = g == 0 ? r0 : r1;
-      const float ks = lane_f(cc.gk, k0 + g) * a.scale_log2;
+      const float ks = lane_f(cc.gk, k0 + g) * qsl;
       vs[g] = lane_f(cc.gv, k0 + g);
       h8_t ka[NS];
       ka_ternary<NS, NC>(raw.k, ka, oc);
@@ -1121,7 +1161,7 @@ void k_decode_mfma(DecodeArgs a) {
           for (int r = 0; r < 4; ++r) {
             const int t = u * 16 + 4 * grp + r;
             const bool att = R.single ? t < L : (t < R.sinks || (t >= R.w0 && t < L));
-            sc[r] = att ? s4[r] * (ksc[r] * a.scale_log2) : -INFINITY;
+            sc[r] = att ? s4[r] * (ksc[r] * qsl) : -INFINITY;
             mx = fmaxf(mx, sc[r]);
           }
           mx = max_rows(mx);

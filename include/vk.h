@@ -167,7 +167,10 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
 /*
  * One decode step of GQA attention for one layer (the read side).
  *
- * q: device [n_seqs][n_q_heads][head_dim] of q_dtype (|q| < 65504).
+ * q: device [n_seqs][n_q_heads][head_dim] of q_dtype, any finite values: the
+ *    queries of one (sequence, KV head) are scaled by one power of two before
+ *    the f16 products (largest magnitude in [2^14, 2^15)) and the scores by its
+ *    inverse, so bf16 queries beyond the f16 range are taken exactly.
  * out: device float32 [n_seqs][n_q_heads][head_dim].
  * Attended tokens of a sequence of length L: [0, min(sink_tokens, L)) and
  * [max(0, L - window), L); window = -1 attends the whole context (the

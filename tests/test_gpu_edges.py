@@ -255,6 +255,38 @@ def test_incremental_decode_appends_into_recent_tier(kernel, dyn):
     cache.close()
 
 
+QUERY_RANGES = [
+    # (query factor, softmax scale factor): bf16 queries far outside the f16 range, with a
+    # softmax scale that brings the scores back to order 1 (so every score matters)
+    (1e5, 1e-5), (3e37, 1e-37), (1e-30, 1e30), (1e-36, 1e36), (7.0, 1.0 / 7.0),
+]
+
+
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
+@pytest.mark.parametrize("qf,sf", QUERY_RANGES, ids=[f"q{c[0]:g}" for c in QUERY_RANGES])
+def test_query_outside_f16_range(kernel, qf, sf):
+    """bf16 queries of any magnitude: the decode scales them by a power of two before the f16
+    products and takes the scale back out of the scores."""
+    w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,
+                          recent_tokens=48, recent_format=oc.FP8E4M3, lengths=(700, 31, 250),
+                          batch_appends=False)
+    cache = make_cache(w, decode_kernel=kernel)
+    fill(cache, w)
+    encs = {}
+    for s in range(w.n_seqs):
+        kb, vb = host_kv(w, 0, s)
+        encs[s] = oc.encode_sequence(spec_of(w), kb, vb, w.dtype, seq_calls(w, s))
+    q = (wl.queries(w, 0, device="cuda").float() * qf).to(torch.bfloat16)
+    assert torch.isfinite(q.float()).all() and float(q.float().abs().max()) > 0
+    scale = sf / np.sqrt(w.head_dim)
+    for W in (-1, 60):
+        out = cache.decode(q, list(range(w.n_seqs)), 0, window=W, softmax_scale=scale)
+        torch.cuda.synchronize()
+        err = check_decode(out, q, w, encs, W, scale=scale)
+        say(f"query x {qf:g}, scale x {sf:g}, window {W}: max err {err:.2e}")
+    cache.close()
+
+
 @pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
 def test_page_placement_and_repeats_are_bit_identical(kernel):
     w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16,

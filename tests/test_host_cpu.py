@@ -83,12 +83,22 @@ def test_sizes():
 
 # ------------------------------------------------------------ host shim ---
 
+# With VK_HS_SANITIZE=1 the shim is built with AddressSanitizer and UndefinedBehaviorSanitizer
+# (the process must then have libasan preloaded; test_host_logic_under_sanitizers below runs
+# the shim tests that way in a child process).
+SANITIZE = os.environ.get("VK_HS_SANITIZE") == "1"
+SANITIZER_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+SHIM_TESTS = ("tier_router or capacity_align or allocator or attended_units or route_counters or mixed_ranges "
+              "or split_plan or retier_plan or retier_capacity or eviction")
+
+
 @pytest.fixture(scope="module")
 def hs():
     d = tempfile.mkdtemp(prefix="vk_hs_")
     so = os.path.join(d, "libhs.so")
-    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-shared", "-fPIC", "-I" + os.path.join(ROOT, "include"),
-                    "-I" + CSRC, os.path.join(ROOT, "tests", "native", "host_shim.cpp"),
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-shared", "-fPIC", *(SANITIZER_FLAGS if SANITIZE else []),
+                    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+                    os.path.join(ROOT, "tests", "native", "host_shim.cpp"),
                     os.path.join(CSRC, "host_state.cpp"), "-o", so], check=True)
     L = ctypes.CDLL(so)
     P = ctypes.POINTER
@@ -470,3 +480,22 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+@pytest.mark.skipif(SANITIZE, reason="this is the parent of the sanitized run")
+def test_host_logic_under_sanitizers():
+    """The allocator, router, planner, retier and eviction tests again, in a child process,
+    with the host logic built under AddressSanitizer and UndefinedBehaviorSanitizer."""
+    libasan = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    if not os.path.isabs(libasan) or not os.path.exists(libasan):
+        pytest.skip("libasan is not available")
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = libasan + ((":" + env["LD_PRELOAD"]) if env.get("LD_PRELOAD") else "")
+    env["ASAN_OPTIONS"] = "detect_leaks=0"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    env["VK_HS_SANITIZE"] = "1"
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", os.path.abspath(__file__),
+                        "-k", SHIM_TESTS], env=env, capture_output=True, text=True, cwd=ROOT, timeout=600)
+    tail = (r.stdout + r.stderr)[-3000:]
+    assert r.returncode == 0, tail
+    assert "passed" in r.stdout and "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, tail
