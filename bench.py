@@ -92,17 +92,23 @@ def main():
     cache = vk.Cache(cfg)
 
     # inputs resident in HBM: rotate enough sets to exceed the 256 MB Infinity Cache
-    in_bytes = sum(2 * w.n_layers * len(ids) * n * w.n_kv_heads * w.head_dim * 2 for ids, _, n in calls)
+    batches = w.append_batches()
+    in_bytes = sum(2 * w.n_layers * sum(ns) * w.n_kv_heads * w.head_dim * 2 for _, _, ns in batches)
     n_sets = max(1, min(3, -(-768 * 2 ** 20 // in_bytes)))
     sets = []
     for r in range(n_sets):
         per_call = []
-        for ci, (ids, t0, n) in enumerate(calls):
-            k, v = wl.append_inputs(w, ids, t0, n, device="cuda")
+        for ids, t0s, ns in batches:
+            if w.ragged_appends:
+                k, v = wl.append_inputs_ragged(w, ids, t0s, ns, device="cuda")
+                ax = 1
+            else:
+                k, v = wl.append_inputs(w, ids, t0s[0], ns[0], device="cuda")
+                ax = 2
             if r:  # other sets: same shapes, different draws
-                k = k[:, :, torch.randperm(n, device="cuda")].contiguous()
-                v = v[:, :, torch.randperm(n, device="cuda")].contiguous()
-            per_call.append((ids, k, v))
+                k = k.index_select(ax, torch.randperm(k.shape[ax], device="cuda")).contiguous()
+                v = v.index_select(ax, torch.randperm(v.shape[ax], device="cuda")).contiguous()
+            per_call.append((ids, ns, k, v))
         sets.append(per_call)
     qs = [wl.queries(w, layer, device="cuda") for layer in range(w.n_layers)]
     outs = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for q in qs]
@@ -110,8 +116,11 @@ def main():
 
     def step(i, seg=None):
         cache.reset(ids_all)
-        for ids, k, v in sets[i % n_sets]:
-            cache.append(k, v, ids)
+        for ids, ns, k, v in sets[i % n_sets]:
+            if w.ragged_appends:
+                cache.append_ragged(k, v, ids, ns)
+            else:
+                cache.append(k, v, ids)
         if seg is not None:
             seg[0].record()
         for layer in range(w.n_layers):
@@ -199,7 +208,7 @@ def main():
                    "tokens_per_seq": list(sorted(set(w.lengths))) if len(set(w.lengths)) > 1 else w.lengths[0],
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "sink_tokens": w.sink_tokens, "window": w.window,
-                   "append_calls": len(calls), "input_sets": n_sets,
+                   "append_calls": len(batches), "ragged_appends": w.ragged_appends, "input_sets": n_sets,
                    "fp8": "dynamic per (token, head)" if args.fp8_dynamic else "static scale"},
         "decode_attn": {"GBps": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                         "bytes_per_step": dec_bytes, "device_us_per_step": round(dec_ms * 1e3, 3),

@@ -130,14 +130,14 @@ int32_t HostState::new_page_format(int32_t page, int32_t new_len) const {
   return VK_FMT_TERNARY2;
 }
 
-vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, int32_t n_tokens, AppendPlan* plan,
+vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_tokens, AppendPlan* plan,
                                  std::string* err) const {
   if (n_seqs < 1 || n_seqs > cfg_.max_seqs) {
     *err = fmt_str("n_seqs %lld out of range [1, %lld]", n_seqs, cfg_.max_seqs);
     return VK_ERR_ARG;
   }
   if (!seq_ids) { *err = "seq_ids is NULL"; return VK_ERR_ARG; }
-  if (n_tokens < 1) { *err = "n_tokens must be >= 1"; return VK_ERR_ARG; }
+  if (!n_tokens) { *err = "n_tokens is NULL"; return VK_ERR_ARG; }
   std::unordered_set<int32_t> seen;
   const int32_t bs = cfg_.block_size;
   plan->seqs.clear();
@@ -145,14 +145,17 @@ vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, int32_t
   plan->new_fmt.clear();
   plan->max_units = 0;
   plan->max_tern_tokens = 0;
-  plan->n_tokens = n_tokens;
+  plan->total_tokens = 0;
+  plan->total_tasks = 0;
+  plan->total_blk = 0;
   for (int f = 0; f < kFormats; ++f) plan->new_pages[f] = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t s = seq_ids[i];
     if (s < 0 || s >= cfg_.max_seqs) { *err = fmt_str("seq id %lld out of range", s); return VK_ERR_ARG; }
     if (!seen.insert(s).second) { *err = fmt_str("seq id %lld repeated", s); return VK_ERR_ARG; }
+    if (n_tokens[i] < 1) { *err = fmt_str("n_tokens[%lld] must be >= 1", i); return VK_ERR_ARG; }
     const SeqState& st = seqs_[s];
-    const int64_t t0 = st.length, t1 = t0 + n_tokens;
+    const int64_t t0 = st.length, t1 = t0 + n_tokens[i];
     if (t1 > cfg_.max_tokens_per_seq) {
       *err = fmt_str("seq %lld would exceed max_tokens_per_seq (%lld)", s, cfg_.max_tokens_per_seq);
       return VK_ERR_ARG;
@@ -165,9 +168,16 @@ vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, int32_t
         return VK_ERR_ALIGN;
       }
     }
+    if (plan->total_tokens + n_tokens[i] > (int64_t{1} << 31) - 1) {
+      *err = "more than 2^31 - 1 tokens in one call";
+      return VK_ERR_ARG;
+    }
     AppendSeqDesc d{};
     d.slot = s;
     d.t0 = static_cast<int32_t>(t0);
+    d.n_tokens = n_tokens[i];
+    d.tok_off = static_cast<int32_t>(plan->total_tokens);
+    plan->total_tokens += n_tokens[i];
     d.page_first = static_cast<int32_t>(t0 / bs);
     d.page_off = static_cast<int32_t>(plan->entries.size());
     const int32_t page_end = static_cast<int32_t>(cdiv(t1, bs));
@@ -197,6 +207,16 @@ vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, int32_t
       d.tern_lo = d.tern_hi = 0;
     }
     plan->max_tern_tokens = std::max(plan->max_tern_tokens, d.tern_hi - d.tern_lo);
+    // pack tasks: (16-token unit, K|V, KV head); absmean blocks: kAbsBlockElems elements each
+    d.task_off = static_cast<int32_t>(plan->total_tasks);
+    d.blk_off = static_cast<int32_t>(plan->total_blk);
+    plan->total_tasks += static_cast<int64_t>(unit_end - d.unit_first) * 2 * cfg_.n_kv_heads;
+    plan->total_blk += cdiv(static_cast<int64_t>(d.tern_hi - d.tern_lo) * cfg_.n_kv_heads * cfg_.head_dim,
+                            kAbsBlockElems);
+    if (plan->total_tasks > (int64_t{1} << 30) || plan->total_blk > (int64_t{1} << 30)) {
+      *err = "append too large for one call; split it";
+      return VK_ERR_ARG;
+    }
     plan->seqs.push_back(d);
   }
   for (int f = 0; f < kFormats; ++f) {
@@ -227,7 +247,7 @@ void HostState::commit_append(AppendPlan* plan) {
       st.pages.push_back(e);
       if (st.runs.empty() || st.runs.back().second != f) st.runs.emplace_back(p, f);
     }
-    st.length += plan->n_tokens;
+    st.length += d.n_tokens;
   }
   (void)bs;
 }

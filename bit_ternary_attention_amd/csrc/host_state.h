@@ -19,6 +19,7 @@ namespace vk {
 
 constexpr int kFormats = 3;
 constexpr int kUnit = 16;          // tokens per unit: the decode and pack work granule
+constexpr int64_t kAbsBlockElems = 16384;  // elements per absmean block (the write side's pass 1)
 constexpr int32_t kNoPage = -1;
 
 inline int32_t make_entry(int fmt, int32_t idx) {
@@ -44,13 +45,19 @@ struct AppendSeqDesc {
   int32_t page_off;    // offset of that page's entry in the entry list
   int32_t n_pages;     // pages touched
   int32_t unit_first;  // first 16-token unit touched
+  int32_t n_tokens;    // tokens this call adds to the sequence
+  int32_t tok_off;     // row of its first token in each layer's input block
+  int32_t task_off;    // first pack task of the sequence within a layer (16-token unit, K|V, head)
+  int32_t blk_off;     // first absmean block of the sequence within a (layer, K|V)
 };
-static_assert(sizeof(AppendSeqDesc) == 32, "device layout");
+static_assert(sizeof(AppendSeqDesc) == 48, "device layout");
 
 struct AppendPlan {
   std::vector<AppendSeqDesc> seqs;
   std::vector<int32_t> entries;     // block-table entries of every touched page, per seq
-  int32_t n_tokens = 0;             // tokens added to every sequence
+  int64_t total_tokens = 0;         // rows of each layer's input block (sum over sequences)
+  int64_t total_tasks = 0;          // pack tasks per layer (sum over sequences)
+  int64_t total_blk = 0;            // absmean blocks per (layer, K|V) (sum over sequences)
   int32_t max_units = 0;            // most 16-token units touched by one sequence
   int32_t max_tern_tokens = 0;      // most ternary tokens in one sequence
   int64_t new_pages[kFormats] = {0, 0, 0};
@@ -111,8 +118,9 @@ class HostState {
   // Format of page `page` when first written by an append ending at new_len.
   int32_t new_page_format(int32_t page, int32_t new_len) const;
 
-  // Checks an append and computes what it needs.  Nothing changes.
-  vk_status plan_append(int32_t n_seqs, const int32_t* seq_ids, int32_t n_tokens, AppendPlan* plan,
+  // Checks an append of n_tokens[i] tokens to sequence seq_ids[i] and computes what it needs.
+  // Nothing changes.
+  vk_status plan_append(int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_tokens, AppendPlan* plan,
                         std::string* err) const;
   // Takes the pages from the free lists, fills plan->entries, advances lengths.
   void commit_append(AppendPlan* plan);

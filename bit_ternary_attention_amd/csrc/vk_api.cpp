@@ -31,7 +31,10 @@ vk_status fail(vk_status s, const char* fmt, ...) {
   return s;
 }
 
-constexpr int kRing = 4;                 // append plan staging slots
+constexpr int kRingMax = 64;             // append / retier plan staging slots, at most
+constexpr int kRingMin = 4;              // ... at least
+constexpr int64_t kRingBytes = 64 << 20; // pinned bytes the slots may take together (beyond kRingMin)
+constexpr int64_t kPackTargetBlocks = 32768;  // pack blocks per launch, at most
 constexpr int64_t kRetierTasksPerLaunch = 65536;  // pages one retier launch converts, at most
 constexpr int64_t kMaxPartials = 1 << 20;  // float64 absmean partials per append call
 constexpr int64_t kMaxSegs = 65535;        // (layer, seq, K|V) segments per append call (grid y)
@@ -134,10 +137,11 @@ struct vk_cache {
   vk::SegInfo* seg = nullptr;
   float* dec_partials = nullptr;
   int64_t plan_bytes = 0;
-  uint8_t* plan_host[kRing] = {};
-  uint8_t* plan_dev[kRing] = {};
-  hipEvent_t plan_ev[kRing] = {};
-  bool plan_ev_used[kRing] = {};
+  int n_ring = kRingMin;  // staging slots in use (ring_slots of the config)
+  uint8_t* plan_host[kRingMax] = {};
+  uint8_t* plan_dev[kRingMax] = {};
+  hipEvent_t plan_ev[kRingMax] = {};
+  bool plan_ev_used[kRingMax] = {};
   int ring_next = 0;
   int64_t device_bytes = 0;
   std::vector<void*> allocations;
@@ -167,6 +171,13 @@ int64_t plan_bytes_for(const vk_cache_config& cfg) {
   return (b + 255) & ~int64_t(255);
 }
 
+// Plan staging slots: as many as fit kRingBytes, between kRingMin and kRingMax.  A call waits on
+// the host only when every slot still holds a plan the device has not consumed.
+int ring_slots(const vk_cache_config& cfg) {
+  const int64_t fit = kRingBytes / plan_bytes_for(cfg);
+  return static_cast<int>(std::max<int64_t>(kRingMin, std::min<int64_t>(kRingMax, fit)));
+}
+
 // Device bytes of every buffer vk_create_cache allocates, in allocation order.
 std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
   std::vector<int64_t> s;
@@ -178,7 +189,8 @@ std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
   s.push_back(kMaxPartials * 8);                                      // absmean partials
   s.push_back(kMaxSegs * static_cast<int64_t>(sizeof(vk::SegInfo)));  // segment info
   s.push_back(partial_count(cfg) * 4);                                // decode split partials
-  for (int r = 0; r < kRing; ++r) s.push_back(plan_bytes_for(cfg));   // staged plans
+  const int rs = ring_slots(cfg);
+  for (int r = 0; r < kRingMax; ++r) s.push_back(r < rs ? plan_bytes_for(cfg) : 0);  // staged plans
   s.push_back(vk::page_bytes(cfg, VK_FMT_TERNARY2));                          // dummy page
   return s;
 }
@@ -186,7 +198,7 @@ std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
 void free_all(vk_cache* c) {
   for (void* p : c->allocations) (void)hipFree(p);
   c->allocations.clear();
-  for (int r = 0; r < kRing; ++r) {
+  for (int r = 0; r < kRingMax; ++r) {
     if (c->plan_host[r]) (void)hipHostFree(c->plan_host[r]);
     if (c->plan_ev[r]) (void)hipEventDestroy(c->plan_ev[r]);
     c->plan_host[r] = nullptr;
@@ -268,7 +280,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   c->allocations = ptrs;
   // pools and gamma start zeroed (finite bytes everywhere); the block table starts empty;
   // the dummy page (target of speculative decode loads) is zero too
-  for (size_t i : {size_t(0), size_t(1), size_t(2), size_t(3), size_t(8 + kRing)})
+  for (size_t i : {size_t(0), size_t(1), size_t(2), size_t(3), size_t(8 + kRingMax)})
     if (ptrs[i]) {
       e = hipMemset(ptrs[i], 0, static_cast<size_t>(sizes[i]));
       if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)); }
@@ -297,9 +309,10 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   c->partials = static_cast<double*>(ptrs[5]);
   c->seg = static_cast<vk::SegInfo*>(ptrs[6]);
   c->dec_partials = static_cast<float*>(ptrs[7]);
-  P.dummy_page = static_cast<const uint8_t*>(ptrs[8 + kRing]);
+  P.dummy_page = static_cast<const uint8_t*>(ptrs[8 + kRingMax]);
   c->plan_bytes = plan_bytes_for(*cfg);
-  for (int r = 0; r < kRing; ++r) {
+  c->n_ring = ring_slots(*cfg);
+  for (int r = 0; r < c->n_ring; ++r) {
     c->plan_dev[r] = static_cast<uint8_t*>(ptrs[8 + r]);
     e = hipHostMalloc(reinterpret_cast<void**>(&c->plan_host[r]), static_cast<size_t>(c->plan_bytes), 0);
     if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_OOM, "hipHostMalloc: %s", hipGetErrorString(e)); }
@@ -316,9 +329,12 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   return VK_OK;
 }
 
-VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
-                           const int32_t* seq_ids, int32_t n_tokens, const void* k, const void* v,
-                           int32_t dtype, void* stream) {
+namespace {
+
+// vk_append and vk_append_ragged: sequence i gets counts[i] tokens, its rows at tok_off_i of each
+// layer's input block (the sequences one after another).
+vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs, const int32_t* seq_ids,
+                      const int32_t* counts, const void* k, const void* v, int32_t dtype, void* stream) {
   vk_status st = check_handle(c);
   if (st) return st;
   const vk_cache_config& cfg = c->cfg;
@@ -330,17 +346,14 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
     return fail(VK_ERR_ARG, "k and v must be 16-byte aligned");
   vk::AppendPlan plan;
   std::string err;
-  st = c->host->plan_append(n_seqs, seq_ids, n_tokens, &plan, &err);
+  st = c->host->plan_append(n_seqs, seq_ids, counts, &plan, &err);
   if (st) return fail(st, "%s", err.c_str());
   const int64_t n_seg = static_cast<int64_t>(n_layers) * n_seqs * 2;
   const int64_t row = static_cast<int64_t>(cfg.n_kv_heads) * cfg.head_dim;
-  const int64_t n_blk = (static_cast<int64_t>(plan.max_tern_tokens) * row + vk::kAbsElemsPerBlock - 1) /
-                        vk::kAbsElemsPerBlock;
-  if (n_seg > kMaxSegs || n_seg * n_blk > kMaxPartials)
-    return fail(VK_ERR_ARG, "append too large for one call (%lld segments x %lld blocks); split it",
-                static_cast<long long>(n_seg), static_cast<long long>(n_blk));
-  if (n_blk > 65535) return fail(VK_ERR_ARG, "too many tokens in one call");
-  if (static_cast<int64_t>(n_layers) * n_seqs > 65535) return fail(VK_ERR_ARG, "n_layers * n_seqs must be <= 65535");
+  if (n_seg > kMaxSegs || 2 * static_cast<int64_t>(n_layers) * plan.total_blk > kMaxPartials)
+    return fail(VK_ERR_ARG, "append too large for one call (%lld segments, %lld absmean blocks per layer); split it",
+                static_cast<long long>(n_seg), static_cast<long long>(plan.total_blk));
+  const int64_t total = static_cast<int64_t>(n_layers) * plan.total_tasks;
   const int64_t need = static_cast<int64_t>(plan.seqs.size()) * sizeof(vk::AppendSeqDesc) +
                        static_cast<int64_t>(plan.entries.size()) * 4;
   if (need > c->plan_bytes) return fail(VK_ERR_ARG, "append plan too large");
@@ -348,9 +361,9 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int slot = c->ring_next;
-  c->ring_next = (c->ring_next + 1) % kRing;
+  c->ring_next = (c->ring_next + 1) % c->n_ring;
   hipError_t e = hipSuccess;
-  if (c->plan_ev_used[slot]) {
+  if (c->plan_ev_used[slot]) {  // every slot in flight: wait for the oldest plan's kernels
     e = hipEventSynchronize(c->plan_ev[slot]);
     if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
   }
@@ -374,9 +387,27 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
   a.layer_begin = layer_begin;
   a.n_layers = n_layers;
   a.n_seqs = n_seqs;
-  a.n_tokens = n_tokens;
-  a.n_blk = static_cast<int32_t>(n_blk);
-  a.max_units = plan.max_units;
+  a.total_tokens = static_cast<int32_t>(plan.total_tokens);
+  a.total_blk = static_cast<int32_t>(plan.total_blk);
+  a.total_tasks = static_cast<int32_t>(plan.total_tasks);
+  const int64_t blocks = std::min<int64_t>(total, kPackTargetBlocks);
+  a.tasks_per_blk = static_cast<int32_t>((total + blocks - 1) / blocks);
+  a.pack_blocks = static_cast<int32_t>((total + a.tasks_per_blk - 1) / a.tasks_per_blk);
+  // sequences with equal task (block) counts: the kernels find a task's sequence by division
+  a.seq_tasks = a.seq_blk = 0;
+  {
+    const int64_t nt0 = (plan.seqs.size() > 1 ? plan.seqs[1].task_off : plan.total_tasks);
+    const int64_t nb0 = (plan.seqs.size() > 1 ? plan.seqs[1].blk_off : plan.total_blk);
+    bool eq_t = true, eq_b = true;
+    for (size_t j = 0; j < plan.seqs.size(); ++j) {
+      eq_t &= plan.seqs[j].task_off == static_cast<int64_t>(j) * nt0;
+      eq_b &= plan.seqs[j].blk_off == static_cast<int64_t>(j) * nb0;
+    }
+    eq_t &= plan.total_tasks == static_cast<int64_t>(plan.seqs.size()) * nt0;
+    eq_b &= plan.total_blk == static_cast<int64_t>(plan.seqs.size()) * nb0;
+    if (eq_t && nt0 > 0) a.seq_tasks = static_cast<int32_t>(nt0);
+    if (eq_b && nb0 > 0) a.seq_blk = static_cast<int32_t>(nb0);
+  }
   a.eps = cfg.eps;
   a.all_ternary = std::all_of(plan.entries.begin(), plan.entries.end(),
                               [](int32_t e) { return vk::entry_fmt(e) == VK_FMT_TERNARY2; });
@@ -387,8 +418,8 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
     for (const vk::AppendSeqDesc& d : plan.seqs) tern_tokens += d.tern_hi - d.tern_lo;
     const double layers = n_layers;
     c->timer.add_bytes(VK_KERNEL_ABSMEAN, layers * 2.0 * tern_tokens * row * 2.0);
-    c->timer.add_bytes(VK_KERNEL_FINALIZE, static_cast<double>(n_seg) * n_blk * 8.0);
-    const double in_bytes = layers * n_seqs * 2.0 * n_tokens * row * 2.0;
+    c->timer.add_bytes(VK_KERNEL_FINALIZE, layers * 2.0 * static_cast<double>(plan.total_blk) * 8.0);
+    const double in_bytes = layers * 2.0 * static_cast<double>(plan.total_tokens) * row * 2.0;
     const double per_elem[3] = {0.25, 1.0 + (cfg.fp8_dynamic ? 4.0 / cfg.head_dim : 0.0), 2.0};  // + token scales
     double out_bytes = 0.0;
     for (const vk::AppendSeqDesc& d : plan.seqs) {
@@ -396,7 +427,7 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
         const int32_t p = d.page_first + j;
         const int f = vk::entry_fmt(plan.entries[d.page_off + j]);
         const int64_t lo = std::max<int64_t>(static_cast<int64_t>(p) * cfg.block_size, d.t0);
-        const int64_t hi = std::min<int64_t>(static_cast<int64_t>(p + 1) * cfg.block_size, d.t0 + n_tokens);
+        const int64_t hi = std::min<int64_t>(static_cast<int64_t>(p + 1) * cfg.block_size, d.t0 + d.n_tokens);
         out_bytes += 2.0 * (hi - lo) * row * per_elem[f] + (f == VK_FMT_TERNARY2 && lo % cfg.block_size == 0 ? 8.0 : 0.0);
       }
     }
@@ -410,6 +441,23 @@ VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, i
   c->stats.append_calls += 1;
   g_error.clear();
   return VK_OK;
+}
+
+}  // namespace
+
+VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                           const int32_t* seq_ids, int32_t n_tokens, const void* k, const void* v,
+                           int32_t dtype, void* stream) {
+  if (n_tokens < 1) return fail(VK_ERR_ARG, "n_tokens must be >= 1");
+  if (n_seqs < 1 || (c && n_seqs > c->cfg.max_seqs)) return fail(VK_ERR_ARG, "n_seqs %d out of range", n_seqs);
+  std::vector<int32_t> counts(static_cast<size_t>(n_seqs), n_tokens);
+  return append_impl(c, layer_begin, n_layers, n_seqs, seq_ids, counts.data(), k, v, dtype, stream);
+}
+
+VK_API vk_status vk_append_ragged(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                  const int32_t* seq_ids, const int32_t* n_tokens, const void* k, const void* v,
+                                  int32_t dtype, void* stream) {
+  return append_impl(c, layer_begin, n_layers, n_seqs, seq_ids, n_tokens, k, v, dtype, stream);
 }
 
 VK_API vk_status vk_retier(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, int64_t* n_pages, void* stream) {
@@ -431,7 +479,7 @@ VK_API vk_status vk_retier(vk_cache* c, int32_t n_seqs, const int32_t* seq_ids, 
   for (int64_t first = 0; first < n_tasks; first += per_launch) {
     const int64_t cnt = std::min(per_launch, n_tasks - first);
     const int slot = c->ring_next;
-    c->ring_next = (c->ring_next + 1) % kRing;
+    c->ring_next = (c->ring_next + 1) % c->n_ring;
     hipError_t e = hipSuccess;
     if (c->plan_ev_used[slot]) {
       e = hipEventSynchronize(c->plan_ev[slot]);

@@ -43,19 +43,23 @@ constexpr int kAbsElemsPerBlock = kAbsThreads * kAbsElemsPerThreadIter * kAbsIte
 
 struct AppendArgs {
   PoolsView P;
-  const uint16_t* k;       // [n_layers][n_seqs][n_tokens][hkv][dim]
+  const uint16_t* k;       // [n_layers][total_tokens][hkv][dim]: sequence i at rows descs[i].tok_off ..
   const uint16_t* v;
   const AppendSeqDesc* descs;
   const int32_t* entries;
-  double* partials;        // [n_seg][n_blk]
-  SegInfo* seg;            // [n_seg]
+  double* partials;        // [n_layers][K|V][total_blk]
+  SegInfo* seg;            // [n_layers][n_seqs][K|V]
   int32_t dtype;           // 0 f16, 1 bf16
   int32_t layer_begin;
   int32_t n_layers;
   int32_t n_seqs;
-  int32_t n_tokens;
-  int32_t n_blk;           // absmean blocks per segment
-  int32_t max_units;       // most 16-token units touched by one sequence
+  int32_t total_tokens;    // input rows per layer (sum of the sequences' token counts)
+  int32_t total_blk;       // absmean blocks per (layer, K|V) (sum over the sequences)
+  int32_t total_tasks;     // pack tasks per layer (sum over the sequences)
+  int32_t tasks_per_blk;   // pack tasks per block
+  int32_t pack_blocks;     // pack grid: ceil(n_layers * total_tasks / tasks_per_blk)
+  int32_t seq_tasks;       // pack tasks of every sequence when they all have the same count, else 0
+  int32_t seq_blk;         // absmean blocks of every sequence when they all have the same count, else 0
   int32_t all_ternary;     // every touched page is ternary (the pack kernel's lean instance)
   float eps;
 };

@@ -171,18 +171,39 @@ __device__ __forceinline__ uint32_t to_f16_bits(uint32_t h) {
   return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(to_f32<1>(h))));
 }
 
+// Index of the sequence whose range [off_i, off_{i+1}) holds x, for per-sequence offsets that
+// do not decrease with i (FIELD: a member of AppendSeqDesc): one load per lane and a ballot per
+// 64 sequences.  Every lane of the wave calls it; the result is uniform.
+template <int32_t AppendSeqDesc::*FIELD>
+__device__ __forceinline__ int find_seq(const AppendSeqDesc* descs, int n_seqs, int x) {
+  const int lane = threadIdx.x & 63;
+  int i = 0;
+  for (int j0 = 0; j0 < n_seqs; j0 += 64) {
+    const int j = j0 + lane;
+    const uint64_t le = __ballot(j < n_seqs && descs[j].*FIELD <= x);
+    i += __builtin_popcountll(le);
+    if (le != ~uint64_t{0}) break;
+  }
+  return i - 1;
+}
+
 // ------------------------------------------------------------- pass 1 ---
 
+// grid (absmean blocks of every sequence, layer x K|V): the sequences' blocks one after another,
+// so a ragged call (sequences of different token counts) launches no idle blocks
 template <int DT>
 __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(AppendArgs a) {
-  const int seg = blockIdx.y, blk = blockIdx.x;
-  const int kv = seg & 1, li = seg >> 1;
-  const int i = li % a.n_seqs, l_rel = li / a.n_seqs;
+  static_assert(kAbsElemsPerBlock == kAbsBlockElems, "block size shared with the host planner");
+  const int x = blockIdx.x;
+  const int kv = blockIdx.y & 1, l_rel = blockIdx.y >> 1;
+  // (a call whose sequences all have the same block count finds its sequence without a load)
+  const int i = a.seq_blk ? x / a.seq_blk : find_seq<&AppendSeqDesc::blk_off>(a.descs, a.n_seqs, x);
   const AppendSeqDesc d = a.descs[i];
+  const int blk = x - d.blk_off;
   const int64_t row = static_cast<int64_t>(a.P.hkv) * a.P.dim;
   const int64_t n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * row;
   const uint16_t* base =
-      (kv ? a.v : a.k) + ((static_cast<int64_t>(l_rel) * a.n_seqs + i) * a.n_tokens + d.tern_lo) * row;
+      (kv ? a.v : a.k) + (static_cast<int64_t>(l_rel) * a.total_tokens + d.tok_off + d.tern_lo) * row;
   const int64_t start = static_cast<int64_t>(blk) * kAbsElemsPerBlock;
   uint4 w[kAbsIters];
 #pragma unroll
@@ -194,22 +215,29 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(AppendArgs a) {
 #pragma unroll
   for (int it = 0; it < kAbsIters; ++it) acc += abs_sum8<DT>(w[it]);
   const double total = block_sum256(acc);
-  if (threadIdx.x == 0) a.partials[static_cast<int64_t>(seg) * a.n_blk + blk] = total;
+  if (threadIdx.x == 0) a.partials[static_cast<int64_t>(blockIdx.y) * a.total_blk + x] = total;
 }
 
+// one wave per segment (layer, sequence, K|V): its partials are blocks [blk_off, blk_off + n)
+// of its (layer, K|V) row
 template <int DT>
 __global__ __launch_bounds__(64) void k_gamma_finalize(AppendArgs a) {
   const int seg = blockIdx.x;
-  const int i = (seg >> 1) % a.n_seqs;
+  const int kv = seg & 1, i = (seg >> 1) % a.n_seqs, l_rel = (seg >> 1) / a.n_seqs;
   const AppendSeqDesc d = a.descs[i];
   const int64_t n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * a.P.hkv * a.P.dim;
-  const double s = sum_partials_wave(a.partials + static_cast<int64_t>(seg) * a.n_blk, a.n_blk);
+  const int n_blk = static_cast<int>((n + kAbsElemsPerBlock - 1) / kAbsElemsPerBlock);
+  const double s = sum_partials_wave(a.partials + static_cast<int64_t>(l_rel * 2 + kv) * a.total_blk + d.blk_off, n_blk);
   const SegInfo info = finalize_wave<DT>(s, n, a.eps);
   if (threadIdx.x == 0) a.seg[seg] = info;
 }
 
 // ------------------------------------------------------------- pass 2 ---
 
+// Tasks are (16-token unit, K|V, KV head) of every sequence of the call, the sequences' tasks
+// one after another within a layer, layer after layer; each block takes a contiguous run of
+// tasks_per_blk of them, so its consecutive tasks are the heads (then K or V) of the same 16
+// tokens and it walks whole input rows.
 // MIXED = false: every page of the call is ternary (the fp8 / fp16 routes are left out, which
 // keeps the register count, and so the resident waves per SIMD, where the ternary route needs it)
 template <int DT, int D, bool MIXED>
@@ -223,21 +251,27 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
 
   const int lane = threadIdx.x;
-  const int li = blockIdx.y;
-  const int i = li % a.n_seqs, l_rel = li / a.n_seqs;
-  const int layer = a.layer_begin + l_rel;
-  const AppendSeqDesc d = a.descs[i];
   const int hkv = a.P.hkv;
   const int64_t row = static_cast<int64_t>(hkv) * D;
-  const int t1 = d.t0 + a.n_tokens;
-  const int n_tasks = a.max_units * 2 * hkv;
   const int c = lane % CPR, rg = lane / CPR;
 
-  // each block takes a contiguous run of tasks: its consecutive tasks are the heads (then K or
-  // V) of the same 16 tokens, so a block walks whole input rows instead of one head's slice
-  const int per_blk = (n_tasks + gridDim.x - 1) / gridDim.x;
-  const int task_end = min(n_tasks, (static_cast<int>(blockIdx.x) + 1) * per_blk);
-  for (int task = blockIdx.x * per_blk; task < task_end; ++task) {
+  const int64_t g_end = static_cast<int64_t>(a.n_layers) * a.total_tasks;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * a.tasks_per_blk;
+  const int64_t g1 = g0 + a.tasks_per_blk < g_end ? g0 + a.tasks_per_blk : g_end;
+  int i = -1, l_rel = -1, task_end = 0;
+  AppendSeqDesc d{};
+  for (int64_t g = g0; g < g1; ++g) {
+    const int lr = static_cast<int>(g / a.total_tasks);
+    const int t = static_cast<int>(g - static_cast<int64_t>(lr) * a.total_tasks);
+    if (lr != l_rel || t >= task_end) {  // uniform: the block moves on to another sequence
+      l_rel = lr;
+      i = a.seq_tasks ? t / a.seq_tasks : find_seq<&AppendSeqDesc::task_off>(a.descs, a.n_seqs, t);
+      d = a.descs[i];
+      task_end = d.task_off + ((d.t0 + d.n_tokens + 15) / 16 - d.unit_first) * 2 * hkv;
+    }
+    const int layer = a.layer_begin + l_rel;
+    const int t1 = d.t0 + d.n_tokens;
+    const int task = t - d.task_off;
     const int h = task % hkv;
     const int kv = (task / hkv) & 1;
     const int uk = task / (2 * hkv);
@@ -252,7 +286,7 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
     uint8_t* tile = a.P.pool[fmt] + (static_cast<int64_t>(layer) * a.P.cap[fmt] + idx) * a.P.page_bytes[fmt] +
                     static_cast<int64_t>(kv * hkv + h) * a.P.tile_bytes[fmt];
     const uint16_t* src =
-        (kv ? a.v : a.k) + (static_cast<int64_t>(l_rel) * a.n_seqs + i) * a.n_tokens * row + h * D + c * 8;
+        (kv ? a.v : a.k) + (static_cast<int64_t>(l_rel) * a.total_tokens + d.tok_off) * row + h * D + c * 8;
 
     if (l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
       a.P.block_table[static_cast<int64_t>(d.slot) * a.P.max_pages + page] = entry;
@@ -263,7 +297,7 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
     for (int k = 0; k < NI; ++k) {
       const int r = rg * NI + k;
       const int j = pos0 + r - d.t0;  // call-relative token
-      ok[k] = j >= 0 && j < a.n_tokens;
+      ok[k] = j >= 0 && j < d.n_tokens;
       w[k] = ok[k] ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * row) : make_uint4(0, 0, 0, 0);
     }
 
@@ -459,8 +493,8 @@ __global__ __launch_bounds__(256) void k_flat_pack(QuantArgs a) {
 
 hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, LaunchTimer* t) {
   const bool bf = a.dtype == VK_DTYPE_BF16;
-  if (a.n_blk > 0) {
-    const dim3 g1(a.n_blk, n_seg);
+  if (a.total_blk > 0) {
+    const dim3 g1(a.total_blk, 2 * a.n_layers);
     if (t) t->begin(VK_KERNEL_ABSMEAN, s);
     if (bf) k_absmean_partial<1><<<g1, kAbsThreads, 0, s>>>(a);
     else k_absmean_partial<0><<<g1, kAbsThreads, 0, s>>>(a);
@@ -470,11 +504,7 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, Laun
     else k_gamma_finalize<0><<<n_seg, 64, 0, s>>>(a);
     if (t) t->end(VK_KERNEL_FINALIZE, s);
   }
-  // enough one-wave blocks to keep every SIMD busy (about 16 per CU), at most one per task
-  const int n_tasks = a.max_units * 2 * a.P.hkv;
-  const int gy = a.n_layers * a.n_seqs;
-  const int gx_max = gy < 16 ? 16384 / gy : 1024;
-  const dim3 g2(n_tasks < gx_max ? n_tasks : gx_max, gy);
+  const dim3 g2(a.pack_blocks);
   if (t) t->begin(VK_KERNEL_PACK, s);
   if (a.P.dim == 128 && a.all_ternary) {
     if (bf) k_pack<1, 128, false><<<g2, 64, 0, s>>>(a);

@@ -53,6 +53,8 @@ EXPORTS = {
     "vk_page_bytes": (_c_i64, [ctypes.POINTER(CacheConfig), _c_i32]),
     "vk_create_cache": (_c_i32, [ctypes.POINTER(CacheConfig), ctypes.POINTER(_c_vp)]),
     "vk_append": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_i32, _c_vp, _c_vp, _c_i32, _c_vp]),
+    "vk_append_ragged": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32), _c_vp,
+                                  _c_vp, _c_i32, _c_vp]),
     "vk_decode_attn": (_c_i32, [_c_vp, _c_i32, _c_i32, ctypes.POINTER(_c_i32), _c_vp, _c_i32, _c_i32, _c_f32,
                                 _c_vp, _c_vp]),
     "vk_retier": (_c_i32, [_c_vp, _c_i32, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64), _c_vp]),
@@ -184,6 +186,22 @@ class Cache:
         ids, n = _ids(seq_ids)
         _check(lib().vk_append(self.handle, layer_begin, k.shape[0], n, ids, k.shape[2], k.data_ptr(), v.data_ptr(),
                                _dtype_code(k), _stream(stream, k.get_device())))
+
+    def append_ragged(self, k, v, seq_ids: Sequence[int], n_tokens: Sequence[int], layer_begin: int = 0,
+                      stream=None) -> None:
+        """k, v: [n_layers][sum(n_tokens)][Hkv][D] float16/bfloat16 device tensors; sequence i's
+        tokens follow sequence i-1's within each layer."""
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+            raise ValueError("k and v must have the same 4-d shape and dtype")
+        if not (k.is_cuda and v.is_cuda and k.is_contiguous() and v.is_contiguous()):
+            raise ValueError("k and v must be contiguous device tensors")
+        if len(n_tokens) != len(seq_ids) or k.shape[1] != sum(n_tokens) or k.shape[2] != self.cfg.n_kv_heads \
+                or k.shape[3] != self.cfg.head_dim:
+            raise ValueError(f"k shape {tuple(k.shape)} does not match the cache / n_tokens")
+        ids, n = _ids(seq_ids)
+        counts = (_c_i32 * n)(*[int(x) for x in n_tokens])
+        _check(lib().vk_append_ragged(self.handle, layer_begin, k.shape[0], n, ids, counts, k.data_ptr(), v.data_ptr(),
+                                      _dtype_code(k), _stream(stream, k.get_device())))
 
     def decode(self, q, seq_ids: Sequence[int], layer: int, window: int = -1, softmax_scale: float = 0.0,
                out=None, stream=None):

@@ -58,6 +58,7 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_mult: float = 10.0
     batch_appends: bool = True  # one append call carries every sequence's chunk
+    ragged_appends: bool = False  # sequences of different lengths share one (ragged) append call
 
     @property
     def gqa(self) -> int:
@@ -87,6 +88,22 @@ class Workload:
         return calls
 
 
+    def append_batches(self) -> List[Tuple[List[int], List[int], List[int]]]:
+        """The append calls as issued: (sequence ids, first token of each, token count of each).
+
+        With ragged_appends the k-th append of every sequence goes into one call (vk_append_ragged);
+        otherwise each entry of appends() is one call with the same count for every sequence.
+        """
+        if not self.ragged_appends:
+            return [(ids, [t0] * len(ids), [n] * len(ids)) for ids, t0, n in self.appends()]
+        per_seq = [[(t0, n) for ids, t0, n in self.appends() if s in ids] for s in range(self.n_seqs)]
+        out = []
+        for k in range(max(len(c) for c in per_seq)):
+            ids = [s for s in range(self.n_seqs) if k < len(per_seq[s])]
+            out.append((ids, [per_seq[s][k][0] for s in ids], [per_seq[s][k][1] for s in ids]))
+        return out
+
+
 def _c4_lengths() -> Tuple[int, ...]:
     rng = np.random.Generator(np.random.PCG64(4004))
     return tuple(int(x) for x in rng.integers(1024, 16385, size=64))
@@ -105,7 +122,7 @@ def workload(number: int) -> Workload:
                         FMT_TERNARY2, 0, FMT_FP8E4M3, 0, (32768,) * 32, 0, outlier_frac=0.02)
     if number == 4:
         return Workload(4, "mixed-format-paged-64seq", 1, 64, 64, 8, 128, DTYPE_BF16, 16, 4, -1,
-                        FMT_F16, 256, FMT_FP8E4M3, 1004, _c4_lengths(), 0)
+                        FMT_F16, 256, FMT_FP8E4M3, 1004, _c4_lengths(), 0, ragged_appends=True)
     if number == 5:
         return Workload(5, "prefill-128k-b4-chunk4096", 1, 4, 32, 8, 128, DTYPE_BF16, 16, 4, -1,
                         FMT_TERNARY2, 0, FMT_FP8E4M3, 0, (131072,) * 4, 4096)
@@ -170,6 +187,16 @@ def append_inputs(w: Workload, seq_ids: Sequence[int], t0: int, n: int, device="
     return torch.stack(ks).contiguous(), torch.stack(vs).contiguous()
 
 
+def append_inputs_ragged(w: Workload, seq_ids: Sequence[int], t0s: Sequence[int], ns: Sequence[int], device="cpu"):
+    """(K, V) for one ragged append call: [n_layers][sum(ns)][Hkv][D] each, contiguous; within a
+    layer, sequence i's tokens [t0s[i], t0s[i] + ns[i]) follow sequence i-1's."""
+    ks, vs = [], []
+    for layer in range(w.n_layers):
+        ks.append(torch.cat([kv_block(w, "k", layer, s, t0, n, device) for s, t0, n in zip(seq_ids, t0s, ns)]))
+        vs.append(torch.cat([kv_block(w, "v", layer, s, t0, n, device) for s, t0, n in zip(seq_ids, t0s, ns)]))
+    return torch.stack(ks).contiguous(), torch.stack(vs).contiguous()
+
+
 def queries(w: Workload, layer: int, device="cpu") -> torch.Tensor:
     """One decode query per sequence for ``layer``: [n_seqs][Hq][D], input dtype."""
     x = _randn((w.n_seqs, w.n_q_heads, w.head_dim), _seed(3000 + w.number, layer), device)
@@ -185,11 +212,11 @@ def small_workload(n_layers=1, n_seqs=None, n_q_heads=8, n_kv_heads=2, head_dim=
                    dtype=DTYPE_F16, block_size=16, sink_tokens=4, window=-1,
                    sink_format=FMT_TERNARY2, recent_tokens=0, recent_format=FMT_FP8E4M3,
                    page_shuffle_seed=0, lengths=(64,), chunk_tokens=0, number=9,
-                   outlier_frac=0.0, batch_appends=True) -> Workload:
+                   outlier_frac=0.0, batch_appends=True, ragged_appends=False) -> Workload:
     """A custom small workload for edge-case tests (same generators)."""
     if n_seqs is None:
         n_seqs = len(lengths)
     return Workload(number, "custom", n_layers, n_seqs, n_q_heads, n_kv_heads, head_dim, dtype,
                     block_size, sink_tokens, window, sink_format, recent_tokens, recent_format,
                     page_shuffle_seed, tuple(lengths), chunk_tokens, outlier_frac=outlier_frac,
-                    batch_appends=batch_appends)
+                    batch_appends=batch_appends, ragged_appends=ragged_appends)

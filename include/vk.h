@@ -28,9 +28,14 @@
  *     any error the cache is left exactly as it was and a message is available
  *     from vk_last_error() (thread-local).  A HIP failure after enqueueing has
  *     begun poisons the handle: later calls return VK_ERR_STATE.
- *   - No call allocates device memory except vk_create_cache, and none blocks
- *     on the device except vk_read_pages, vk_get_kernel_times and vk_release
- *     (and vk_append, when all its plan staging slots are still in flight).
+ *   - No call allocates device memory except vk_create_cache.  Only
+ *     vk_read_pages, vk_get_kernel_times and vk_release wait for the device.
+ *     vk_append, vk_append_ragged and vk_retier stage their plans (descriptors
+ *     and block-table entries) in a ring of pinned slots (up to 64, as many as
+ *     fit 64 MiB); a call waits on the host only when every slot holds a plan
+ *     that the device has not reached yet (64 calls queued ahead of the
+ *     device at the workloads' sizes: back-pressure, as a full launch queue
+ *     gives).
  *   - A handle is not thread-safe; distinct handles are independent.
  */
 #ifndef VK_H_
@@ -163,6 +168,18 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out);
 VK_API vk_status vk_append(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
                            const int32_t* seq_ids, int32_t n_tokens, const void* k, const void* v,
                            int32_t dtype, void* stream);
+
+/*
+ * Ragged append: as vk_append, with its own token count per sequence, so that
+ * sequences of different lengths are written by one call (one launch of each
+ * write-side kernel).  n_tokens: host, n_seqs counts >= 1.  k, v: device,
+ * contiguous [n_layers][sum of n_tokens][n_kv_heads][head_dim]: within each
+ * layer, sequence i's tokens follow sequence i-1's.  Each sequence is its own
+ * gamma segment, exactly as in vk_append.  Errors as vk_append.
+ */
+VK_API vk_status vk_append_ragged(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_t n_seqs,
+                                  const int32_t* seq_ids, const int32_t* n_tokens, const void* k, const void* v,
+                                  int32_t dtype, void* stream);
 
 /*
  * One decode step of GQA attention for one layer (the read side).

@@ -70,9 +70,14 @@ def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_page
 
 
 def fill(cache: vk.Cache, w: wl.Workload) -> None:
-    for ids, t0, n in w.appends():
-        k, v = wl.append_inputs(w, ids, t0, n, device="cuda")
-        cache.append(k, v, ids)
+    """Issues the workload's append calls (ragged calls for workloads that use them)."""
+    for ids, t0s, ns in w.append_batches():
+        if w.ragged_appends:
+            k, v = wl.append_inputs_ragged(w, ids, t0s, ns, device="cuda")
+            cache.append_ragged(k, v, ids, ns)
+        else:
+            k, v = wl.append_inputs(w, ids, t0s[0], ns[0], device="cuda")
+            cache.append(k, v, ids)
         del k, v
     torch.cuda.synchronize()
 

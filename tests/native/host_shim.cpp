@@ -1,6 +1,7 @@
 // Test-only C shim over the HIP-free host state (page allocator, tier
 // router, planners), so the host logic can be checked on a machine without
 // a GPU.  Built by the tests with g++; not part of libvk.so.
+#include <vector>
 #include <cstring>
 #include <string>
 
@@ -27,7 +28,8 @@ int hs_append(void* h, int n_seqs, const int* ids, int n_tokens, int* tern_range
   auto* s = static_cast<vk::HostState*>(h);
   vk::AppendPlan plan;
   std::string e;
-  const vk_status st = s->plan_append(n_seqs, ids, n_tokens, &plan, &e);
+  std::vector<int> counts(n_seqs > 0 ? n_seqs : 0, n_tokens);
+  const vk_status st = s->plan_append(n_seqs, ids, counts.data(), &plan, &e);
   if (st) {
     std::strncpy(err, e.c_str(), errlen - 1);
     err[errlen - 1] = 0;

@@ -255,6 +255,64 @@ def test_incremental_decode_appends_into_recent_tier(kernel, dyn):
     cache.close()
 
 
+RAGGED_CASES = [
+    ("mixed-tiers", dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.F16, recent_tokens=48,
+                         recent_format=oc.FP8E4M3, lengths=(700, 31, 250, 1, 64, 17))),
+    ("chunked-d64", dict(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(200, 64, 130, 5), chunk_tokens=64)),
+    ("chunked-dynamic-fp8", dict(n_q_heads=16, n_kv_heads=2, head_dim=128, dtype=1, recent_tokens=40,
+                                 recent_format=oc.FP8E4M3, lengths=(333, 100, 48), chunk_tokens=48)),
+]
+
+
+@pytest.mark.parametrize("name,kw", RAGGED_CASES, ids=[c[0] for c in RAGGED_CASES])
+def test_ragged_append_matches_per_sequence_appends(name, kw):
+    """One vk_append_ragged call per round of chunks writes the same pages (bytes, formats,
+    gammas) and gives the same decode outputs, bit for bit, as one vk_append per sequence and
+    chunk; and its pages match the oracle."""
+    dyn = int("dynamic" in name)
+    w_r = wl.small_workload(**kw, batch_appends=False, ragged_appends=True)
+    w_s = wl.small_workload(**kw, batch_appends=False)
+    assert any(len(set(ns)) > 1 for _, _, ns in w_r.append_batches())
+    caches = []
+    for w in (w_r, w_s):
+        cache = make_cache(w, fp8_dynamic=dyn)
+        fill(cache, w)
+        caches.append(cache)
+    assert caches[0].stats()["append_calls"] == len(w_r.append_batches()) < caches[1].stats()["append_calls"]
+    q = wl.queries(w_r, 0, device="cuda")
+    for s in range(w_r.n_seqs):
+        n = -(-w_r.lengths[s] // w_r.block_size)
+        a, b = caches[0].read_pages(0, s, 0, n), caches[1].read_pages(0, s, 0, n)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y, equal_nan=True), (name, s)
+        kb, vb = host_kv(w_r, 0, s)
+        check_pages(caches[0], w_r, 0, s, kb, vb, pages=list(range(n)), fp8_dynamic=dyn)
+    for W in (-1, 40):
+        o = [c.decode(q, list(range(w_r.n_seqs)), 0, window=W) for c in caches]
+        torch.cuda.synchronize()
+        assert torch.equal(o[0], o[1]), (name, W)
+    for c in caches:
+        c.close()
+
+
+def test_ragged_append_arguments():
+    w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, lengths=(32, 16))
+    cache = make_cache(w)
+    k = torch.zeros((1, 48, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        cache.append_ragged(k, k, [0, 1], [32, 15])          # counts do not add up to the rows
+    with pytest.raises(vk.VkError) as e:
+        cache.append_ragged(k, k, [0, 1], [48, 0])           # a zero count
+    assert e.value.status == vk.ERR_ARG
+    with pytest.raises(vk.VkError) as e:
+        cache.append_ragged(k, k, [0, 0], [32, 16])          # a repeated id
+    assert e.value.status == vk.ERR_ARG
+    assert cache.seq_length(0) == 0 and cache.seq_length(1) == 0   # nothing changed
+    cache.append_ragged(k, k, [1, 0], [16, 32])
+    assert cache.seq_length(0) == 32 and cache.seq_length(1) == 16
+    cache.close()
+
+
 QUERY_RANGES = [
     # (query factor, softmax scale factor): bf16 queries far outside the f16 range, with a
     # softmax scale that brings the scores back to order 1 (so every score matters)
