@@ -12,6 +12,9 @@
       built from (a reader can tell whether the kernel has changed since)
   python -m bit_ternary_attention_amd.profsum calls <results.db> <name-filter>
       per-call durations of the matching kernels, in launch order
+  python -m bit_ternary_attention_amd.profsum counters <name-filter> <counter_collection.csv>...
+      per-dispatch averages of every counter in the given --pmc runs, over the dispatches of
+      the matching kernel with the largest grid (one launch shape out of a run that mixes several)
   --largest (traffic, record): average only each kernel's dispatches that fetch at least
       90% of its largest one (one launch size out of a run that mixes several)
 """
@@ -125,6 +128,23 @@ def main():
         rows = db.execute("select name, duration from kernels order by start").fetchall()
         durs = [d / 1e3 for n, d in rows if sys.argv[3] in n]
         print(f"{len(durs)} calls of '{sys.argv[3]}' (us, launch order): " + " ".join(f"{d:.2f}" for d in durs))
+    elif mode == "counters":
+        filt, paths = sys.argv[2], sys.argv[3:]
+        for path in paths:
+            rows = [r for r in csv.DictReader(open(path)) if filt in r["Kernel_Name"]]
+            if not rows:
+                continue
+            grid = max(int(r["Grid_Size"]) for r in rows)
+            per = {}
+            for r in rows:
+                if int(r["Grid_Size"]) == grid:
+                    per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            name = short(rows[0]["Kernel_Name"])
+            n = len(next(iter(per.values())))
+            print(f"{name} (grid {grid} threads, {n} dispatches averaged; {os.path.relpath(path)}):")
+            for k in sorted(per):
+                v = per[k]
+                print(f"  {k:28s} {sum(v) / len(v):18.2f}")
     else:
         raise SystemExit(__doc__)
 
