@@ -12,6 +12,8 @@ Readings where the pages are silent:
     ternary format.  A page keeps the format it was first written in.
   * A ternary page is written by one append only (its tokens share that
     append's gamma); appending into a partly filled ternary page is an error.
+    So is appending into a partly filled lossless page (its groups' exponent
+    centres cover all 16 tokens of a unit); lossless pages take bfloat16 input.
   * "Per tensor" gamma = one gamma per (layer, sequence, K or V, append call),
     over that call's ternary-routed tokens (all heads and dimensions).
   * Page bytes: [K tile of head 0..Hkv-1][V tile of head 0..Hkv-1]; ternary
@@ -44,11 +46,13 @@ from typing import Dict, List, Sequence, Tuple
 import numpy as np
 
 from . import fp8 as _fp8
+from . import lossless as _ll
 from . import ternary as _t
 
 TERNARY2 = 0
 FP8E4M3 = 1
 F16 = 2
+LOSSLESS = 3      # bfloat16 kept exactly, exponent / sign+mantissa split (lossless.py)
 
 
 class AlignError(ValueError):
@@ -96,6 +100,8 @@ class EncodedSequence:
     v_f16: np.ndarray
     k_hat: np.ndarray                     # [T, Hkv, D] float64 dequantised
     v_hat: np.ndarray
+    k_lossless: np.ndarray = None         # [T, Hkv, D] uint16 bfloat16 bits kept exactly (0 elsewhere)
+    v_lossless: np.ndarray = None
     k_fp8_scale: np.ndarray = None        # [T, Hkv] float32 dynamic FP8 scales (0 where not fp8)
     v_fp8_scale: np.ndarray = None
     # pages converted from FP8 by retier(): page -> (gamma_K, gamma_V) of that page
@@ -128,12 +134,14 @@ def encode_sequence(spec: CacheSpec, k_bits: np.ndarray, v_bits: np.ndarray, dty
             ("k_f16", np.uint16), ("v_f16", np.uint16), ("k_hat", np.float64), ("v_hat", np.float64))}
     out["k_fp8_scale"] = np.zeros(shape[:2], np.float32)
     out["v_fp8_scale"] = np.zeros(shape[:2], np.float32)
+    out["k_lossless"] = np.zeros(shape, np.uint16)
+    out["v_lossless"] = np.zeros(shape, np.uint16)
     for ci, (t0, n) in enumerate(calls):
         if t0 != length:
             raise ValueError("appends must be contiguous")
         new_len = t0 + n
-        if t0 % bs and page_format[t0 // bs] == TERNARY2:
-            raise AlignError("append into a partly filled ternary page")
+        if t0 % bs and page_format[t0 // bs] in (TERNARY2, LOSSLESS):
+            raise AlignError("append into a partly filled ternary or lossless page")
         for p in range(-(-t0 // bs), -(-new_len // bs)):
             page_format[p] = new_page_format(spec, p, new_len)
         for t in range(t0, new_len):
@@ -164,6 +172,13 @@ def encode_sequence(spec: CacheSpec, k_bits: np.ndarray, v_bits: np.ndarray, dty
                     c = _fp8.fp8_encode_input(src[f8], spec.fp8_scale)
                     out[code][f8] = c
                     out[hat][f8] = _fp8.fp8_dequantize(c, spec.fp8_scale)
+        ls = np.nonzero(tok_fmt[t0:new_len] == LOSSLESS)[0] + t0
+        if ls.size:
+            if dtype != _t.BF16:
+                raise ValueError("the lossless tier holds bfloat16 input")
+            for bits, code, hat, src in ((k_bits, "k_lossless", "k_hat", kx), (v_bits, "v_lossless", "v_hat", vx)):
+                out[code][ls] = bits[ls]
+                out[hat][ls] = src[ls]          # exact: the values themselves
         f16 = np.nonzero(tok_fmt[t0:new_len] == F16)[0] + t0
         if f16.size:
             for bits, code, hat in ((k_bits, "k_f16", "k_hat"), (v_bits, "v_f16", "v_hat")):
@@ -269,6 +284,10 @@ def page_tiles(spec: CacheSpec, enc: EncodedSequence, page: int) -> np.ndarray:
                     sc = np.zeros(bs, dtype="<f4")
                     sc[: hi - lo] = getattr(enc, which + "_fp8_scale")[lo:hi, h]
                     parts.append(sc.view(np.uint8))
+            elif fmt == LOSSLESS:   # token slots past the length hold the bits 0
+                c = np.zeros((bs, dim), dtype=np.uint16)
+                c[: hi - lo] = getattr(enc, which + "_lossless")[lo:hi, h]
+                parts.append(_ll.tile(c, which))
             else:
                 c = np.zeros((bs, dim), dtype=np.uint16)
                 c[: hi - lo] = getattr(enc, which + "_f16")[lo:hi, h]
@@ -278,6 +297,8 @@ def page_tiles(spec: CacheSpec, enc: EncodedSequence, page: int) -> np.ndarray:
 
 def page_bytes(spec: CacheSpec, fmt: int) -> int:
     """Bytes of one page of a format (K and V, every head)."""
+    if fmt == LOSSLESS:
+        return 2 * spec.n_kv_heads * (spec.block_size // 16) * _ll.slot_bytes(spec.head_dim)
     per_elem = {TERNARY2: 0.25, FP8E4M3: 1, F16: 2}[fmt]
     extra = 4 * spec.block_size if fmt == FP8E4M3 and spec.fp8_dynamic else 0   # scales per tile
     return int(2 * spec.n_kv_heads * (spec.block_size * spec.head_dim * per_elem + extra))
