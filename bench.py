@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MIN_WARMUP_S = 0.3   # untimed warm-up lasts at least this long (and at least --warmup steps)
 METRIC = "decode-attn over packed KV: GB/s & % HBM peak; quantize+pack GB/s"
+FORMATS = {"ternary": 0, "fp8": 1, "f16": 2, "lossless": 3}
 
 
 def parse():
@@ -42,6 +43,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3: full retention, 32 x 32K tokens)")
     ap.add_argument("--decode-kernel", type=int, default=0, help="0 default, 1 vector ALU, 2 matrix cores")
+    ap.add_argument("--sink-format", choices=sorted(FORMATS), default=None,
+                    help="page format of the sink pages instead of the workload's own (lossless: the exact "
+                         "bfloat16 tier)")
+    ap.add_argument("--recent-format", choices=sorted(FORMATS), default=None,
+                    help="page format of the recent tier instead of the workload's own")
     ap.add_argument("--fp8-dynamic", action="store_true",
                     help="FP8 pages with one scale per token and KV head instead of the static scale")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -75,6 +81,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = wl.workload(args.workload)
+    if args.sink_format or args.recent_format:
+        import dataclasses
+        w = dataclasses.replace(w, sink_format=FORMATS[args.sink_format] if args.sink_format else w.sink_format,
+                                recent_format=FORMATS[args.recent_format] if args.recent_format else w.recent_format)
     calls = w.appends()
     ids_all = list(range(w.n_seqs))
 
@@ -87,8 +97,8 @@ def main():
                          page_shuffle_seed=w.page_shuffle_seed, decode_kernel=args.decode_kernel,
                          fp8_dynamic=int(args.fp8_dynamic))
     formats = page_formats(w, calls)
-    need = [sum(f.count(x) for f in formats) for x in range(3)]
-    cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16 = need
+    need = [sum(f.count(x) for f in formats) for x in range(4)]
+    cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16, cfg.pages_lossless = need
     cache = vk.Cache(cfg)
 
     # inputs resident in HBM: rotate enough sets to exceed the 256 MB Infinity Cache
@@ -209,7 +219,10 @@ def main():
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "sink_tokens": w.sink_tokens, "window": w.window,
                    "append_calls": len(batches), "ragged_appends": w.ragged_appends, "input_sets": n_sets,
-                   "fp8": "dynamic per (token, head)" if args.fp8_dynamic else "static scale"},
+                   "fp8": "dynamic per (token, head)" if args.fp8_dynamic else "static scale",
+                   "sink_format": next(k for k, f in FORMATS.items() if f == w.sink_format),
+                   "recent_format": (next(k for k, f in FORMATS.items() if f == w.recent_format)
+                                     if w.recent_tokens > 0 else None)},
         "decode_attn": {"GBps": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                         "bytes_per_step": dec_bytes, "device_us_per_step": round(dec_ms * 1e3, 3),
                         "us_per_layer": round(dec_ms * 1e3 / w.n_layers, 3),
@@ -235,6 +248,8 @@ def main():
     }
 
     result["decode_step"] = decode_step_leg(cache, qs, outs, w, ids_all)
+    if stats["pages_used"][3] > 0:
+        result["lossless_tier"] = lossless_bytes(cache, w, ids_all)
 
     if w.recent_tokens > 0 and w.recent_format == vk.FMT_FP8E4M3:
         cache.close()
@@ -274,10 +289,11 @@ def page_formats(w, calls):
 def decode_step_bytes(w, formats, fp8_dynamic=False):
     """Algorithmic bytes of one decode step of every layer: per attended token and KV head the
     key and value in their stored format (ternary D/4 bytes each, fp8 D (+4 B of scale when
-    dynamic), fp16 2D), a gamma pair (8 B) per attended ternary page, the queries (16-bit) and
-    the float32 outputs."""
+    dynamic), fp16 2D, lossless 1.5 D + 1 (its two coded streams and a 16-byte header per 16
+    tokens; exceptions not counted)), a gamma pair (8 B) per attended ternary page, the queries
+    (16-bit) and the float32 outputs."""
     D, hkv, bs = w.head_dim, w.n_kv_heads, w.block_size
-    per_tok = {0: 2 * D / 4, 1: 2 * (D + (4 if fp8_dynamic else 0)), 2: 2 * 2 * D}
+    per_tok = {0: 2 * D / 4, 1: 2 * (D + (4 if fp8_dynamic else 0)), 2: 2 * 2 * D, 3: 2 * (1.5 * D + 1)}
     import numpy as np
     total = 0.0
     for s, L in enumerate(w.lengths):
@@ -295,6 +311,32 @@ def decode_step_bytes(w, formats, fp8_dynamic=False):
         total += 8 * int(np.count_nonzero((fm == 0) & (n_att > 0)))
     total += w.n_seqs * w.n_q_heads * D * (2 + 4)
     return total * w.n_layers
+
+
+def lossless_bytes(cache, w, ids):
+    """Bytes a decode reads from the lossless pages of layer 0 (each 16-token group's header, its
+    two coded streams and its exceptions, or its raw values) against their bfloat16 size, read
+    back from the device after the timed steps."""
+    import numpy as np
+    slot = 32 * w.head_dim + 16
+    read = raw = groups = raw_groups = 0
+    for s in ids:
+        n = -(-cache.seq_length(s) // w.block_size)
+        buf, fmt, _ = cache.read_pages(0, s, 0, n)
+        for p in np.nonzero(fmt == 3)[0]:
+            hdr = buf[p, :2 * w.n_kv_heads * (w.block_size // 16) * slot].reshape(-1, slot)[:, :8]
+            for h in hdr:
+                groups += 1
+                if h[1] == 1:
+                    raw_groups += 1
+                    read += 16 + 32 * w.head_dim
+                else:
+                    read += 16 + 24 * w.head_dim + int(h[4:8].view("<u4")[0])
+                raw += 32 * w.head_dim
+    return {"groups": groups, "raw_groups": raw_groups, "bytes_read": read, "bf16_bytes": raw,
+            "bf16_over_read": round(raw / read, 4) if read else None,
+            "note": "every 16-token group of every lossless page of layer 0, including units past a "
+                    "sequence's end inside its last page"}
 
 
 def attended_tokens(L, S, W):
@@ -357,6 +399,7 @@ def retier_leg(w, steps, warmup, fp8_dynamic=False):
     cfg.pages_ternary = per_seq * w.n_seqs
     cfg.pages_fp8 = per_seq * w.n_seqs
     cfg.pages_f16 = n_sink * w.n_seqs
+    cfg.pages_lossless = n_sink * w.n_seqs if w.sink_format == vk.FMT_LOSSLESS else 0
     cache = vk.Cache(cfg)
     g = torch.Generator(device="cuda")
     g.manual_seed(5000 + w.number)
@@ -420,6 +463,7 @@ def stream_leg(w, steps, warmup, prefill=1024, window=512, fp8_dynamic=False):
     cfg.pages_ternary = (per_seq + chunk // bs) * w.n_seqs
     cfg.pages_fp8 = ((w.recent_tokens + chunk) // bs + 3) * w.n_seqs
     cfg.pages_f16 = n_sink * w.n_seqs
+    cfg.pages_lossless = n_sink * w.n_seqs if w.sink_format == vk.FMT_LOSSLESS else 0
     cache = vk.Cache(cfg)
     g = torch.Generator(device="cuda")
     g.manual_seed(6000 + w.number)
@@ -535,7 +579,8 @@ def cpu_baseline(w, calls, sample_layers, fp8_dynamic=False):
                 enc_bytes += 2 * (kb.nbytes + vb.nbytes) + sum(p.size for p in pages)
                 idx = oa.attended_tokens(Ls, w.sink_tokens, w.window)
                 fmt = enc.token_format[idx]
-                per_tok = {0: 2 * w.head_dim / 4, 1: 2 * (w.head_dim + (4 if fp8_dynamic else 0)), 2: 4 * w.head_dim}
+                per_tok = {0: 2 * w.head_dim / 4, 1: 2 * (w.head_dim + (4 if fp8_dynamic else 0)), 2: 4 * w.head_dim,
+                           3: 2 * (1.5 * w.head_dim + 1)}
                 dec_bytes += sum(per_tok[f] * w.n_kv_heads * int(np.count_nonzero(fmt == f)) for f in per_tok)
                 dec_bytes += 8 * len(set(int(t) // w.block_size for t in idx[fmt == 0]))
                 dec_bytes += w.n_q_heads * w.head_dim * (2 + 4)

@@ -26,10 +26,13 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibili
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra",
              "-D__HIP_PLATFORM_AMD__", "-I" + INCLUDE, "-I" + CSRC, "-I" + os.path.join(ROCM, "include")]
 
-HIP_SOURCES = ["vk_write.hip", "vk_decode.hip", "vk_retier.hip"]
-# per-source flags: the decode kernels never produce or consume NaN (masked scores are -inf),
-# so float max needs no NaN quieting (otherwise each fmaxf operand is canonicalised first)
-HIP_SOURCE_FLAGS = {"vk_decode.hip": ["-fno-honor-nans"]}
+# (object name, source, extra flags).  The decode kernels never produce or consume NaN (masked
+# scores are -inf), so float max needs no NaN quieting (otherwise each fmaxf operand is
+# canonicalised first); their source is compiled once per head dim, in parallel.
+HIP_UNITS = [("vk_write", "vk_write.hip", []),
+             ("vk_decode_d128", "vk_decode.hip", ["-fno-honor-nans", "-DVK_DECODE_DIM=128"]),
+             ("vk_decode_d64", "vk_decode.hip", ["-fno-honor-nans", "-DVK_DECODE_DIM=64"]),
+             ("vk_retier", "vk_retier.hip", [])]
 CXX_SOURCES = ["host_state.cpp", "vk_api.cpp"]
 
 
@@ -48,15 +51,15 @@ def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = []
     objs = []
-    for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        jobs.append([hipcc, *HIP_FLAGS, *HIP_SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+    for name, src, extra in HIP_UNITS:
+        obj = os.path.join(BUILD, name + ".o")
+        jobs.append([hipcc, *HIP_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=6) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
             f.result()
     tmp = LIB + ".tmp"
@@ -66,11 +69,11 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
-def asm(source: str, out: str) -> None:
-    """Writes the gfx950 assembly of one kernel source (for inspection)."""
+def asm(unit: str, out: str) -> None:
+    """Writes the gfx950 assembly of one compile unit (a name of HIP_UNITS), for inspection."""
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
-    _run([hipcc, *HIP_FLAGS, *HIP_SOURCE_FLAGS.get(source, []), "--cuda-device-only", "-S", os.path.join(CSRC, source),
-          "-o", out], True)
+    name, src, extra = next(u for u in HIP_UNITS if u[0] == unit)
+    _run([hipcc, *HIP_FLAGS, *extra, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out], True)
 
 
 if __name__ == "__main__":

@@ -15,7 +15,7 @@ std::string fmt_str(const char* f, long long a, long long b = 0) {
   return buf;
 }
 
-bool valid_format(int32_t f) { return f == VK_FMT_TERNARY2 || f == VK_FMT_FP8E4M3 || f == VK_FMT_F16; }
+bool valid_format(int32_t f) { return f >= VK_FMT_TERNARY2 && f <= VK_FMT_LOSSLESS; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -48,10 +48,14 @@ std::string validate_config(const vk_cache_config& c) {
   if (c.recent_tokens < 0) return "recent_tokens must be >= 0";
   if (!valid_format(c.sink_format) || !valid_format(c.recent_format)) return "unknown page format";
   if (c.decode_kernel < 0 || c.decode_kernel > 2) return "decode_kernel must be 0, 1 or 2";
+  if (c.decode_kernel == VK_DECODE_VALU && (c.sink_format == VK_FMT_LOSSLESS || c.recent_format == VK_FMT_LOSSLESS))
+    return "lossless pages are read by the matrix-core decode kernel only";
   if (c.fp8_dynamic != 0 && c.fp8_dynamic != 1) return "fp8_dynamic must be 0 or 1";
   if (c.reserved0 != 0) return "reserved0 must be 0";
-  if (c.pages_ternary < 0 || c.pages_fp8 < 0 || c.pages_f16 < 0) return "pool capacities must be >= 0";
-  if (c.pages_ternary >= (1ll << 30) || c.pages_fp8 >= (1ll << 30) || c.pages_f16 >= (1ll << 30))
+  if (c.pages_ternary < 0 || c.pages_fp8 < 0 || c.pages_f16 < 0 || c.pages_lossless < 0)
+    return "pool capacities must be >= 0";
+  if (c.pages_ternary >= (1ll << 30) || c.pages_fp8 >= (1ll << 30) || c.pages_f16 >= (1ll << 30) ||
+      c.pages_lossless >= (1ll << 30))
     return "pool capacities must be < 2^30 pages";
   if (!(c.eps >= 0.0f) || !std::isfinite(c.eps)) return "eps must be finite and >= 0";
   if (!(c.fp8_scale > 0.0f) || !std::isfinite(c.fp8_scale)) return "fp8_scale must be finite and > 0";
@@ -66,6 +70,8 @@ int64_t tile_bytes(const vk_cache_config& c, int fmt) {
     case VK_FMT_TERNARY2: return elems / 4;
     case VK_FMT_FP8E4M3: return elems + (c.fp8_dynamic ? 4ll * c.block_size : 0);  // + token scales
     case VK_FMT_F16: return elems * 2;
+    // per 16-token unit: a 16-byte header and room for the raw bfloat16 values
+    case VK_FMT_LOSSLESS: return (c.block_size / kUnit) * (kUnit * 2ll * c.head_dim + 16);
   }
   return 0;
 }
@@ -106,7 +112,7 @@ SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blo
 HostState::HostState(const vk_cache_config& cfg) : cfg_(cfg) {
   max_pages_ = static_cast<int32_t>(cdiv(cfg.max_tokens_per_seq, cfg.block_size));
   seqs_.resize(cfg.max_seqs);
-  const int64_t caps[kFormats] = {cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16};
+  const int64_t caps[kFormats] = {cfg.pages_ternary, cfg.pages_fp8, cfg.pages_f16, cfg.pages_lossless};
   SplitMix64 rng{cfg.page_shuffle_seed};
   for (int f = 0; f < kFormats; ++f) {
     std::vector<int32_t> ids(caps[f]);
@@ -162,9 +168,9 @@ vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, const i
     }
     if (t0 % bs) {
       const int32_t e = st.pages[t0 / bs];
-      if (entry_fmt(e) == VK_FMT_TERNARY2) {
-        *err = fmt_str("seq %lld ends inside a ternary page (length %lld); ternary pages are written by one append",
-                       s, t0);
+      if (e != kNoPage && (entry_fmt(e) == VK_FMT_TERNARY2 || entry_fmt(e) == VK_FMT_LOSSLESS)) {
+        *err = fmt_str("seq %lld ends inside a ternary or lossless page (length %lld); such pages are written by "
+                       "one append", s, t0);
         return VK_ERR_ALIGN;
       }
     }
@@ -221,7 +227,7 @@ vk_status HostState::plan_append(int32_t n_seqs, const int32_t* seq_ids, const i
   }
   for (int f = 0; f < kFormats; ++f) {
     if (plan->new_pages[f] > static_cast<int64_t>(free_[f].size())) {
-      static const char* names[kFormats] = {"ternary", "fp8", "f16"};
+      static const char* names[kFormats] = {"ternary", "fp8", "f16", "lossless"};
       char buf[160];
       std::snprintf(buf, sizeof buf, "pool of %s pages exhausted: need %lld, %lld free", names[f],
                     static_cast<long long>(plan->new_pages[f]), static_cast<long long>(free_[f].size()));
@@ -434,7 +440,7 @@ vk_status HostState::reset_seqs(int32_t n_seqs, const int32_t* seq_ids, std::str
 }
 
 int64_t HostState::pages_used(int fmt) const {
-  const int64_t caps[kFormats] = {cfg_.pages_ternary, cfg_.pages_fp8, cfg_.pages_f16};
+  const int64_t caps[kFormats] = {cfg_.pages_ternary, cfg_.pages_fp8, cfg_.pages_f16, cfg_.pages_lossless};
   return caps[fmt] - static_cast<int64_t>(free_[fmt].size());
 }
 

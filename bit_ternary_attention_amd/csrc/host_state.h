@@ -17,7 +17,7 @@
 
 namespace vk {
 
-constexpr int kFormats = 3;
+constexpr int kFormats = 4;  // VK_FMT_TERNARY2, FP8E4M3, F16, LOSSLESS
 constexpr int kUnit = 16;          // tokens per unit: the decode and pack work granule
 constexpr int64_t kAbsBlockElems = 16384;  // elements per absmean block (the write side's pass 1)
 constexpr int32_t kNoPage = -1;
@@ -60,7 +60,7 @@ struct AppendPlan {
   int64_t total_blk = 0;            // absmean blocks per (layer, K|V) (sum over sequences)
   int32_t max_units = 0;            // most 16-token units touched by one sequence
   int32_t max_tern_tokens = 0;      // most ternary tokens in one sequence
-  int64_t new_pages[kFormats] = {0, 0, 0};
+  int64_t new_pages[kFormats] = {0, 0, 0, 0};
   std::vector<int32_t> new_fmt;     // per new page, in order (seq, page)
 };
 

@@ -163,7 +163,15 @@ int64_t partial_count(const vk_cache_config& cfg) {
 
 int64_t plan_bytes_for(const vk_cache_config& cfg) {
   const int64_t max_pages = (cfg.max_tokens_per_seq + cfg.block_size - 1) / cfg.block_size;
-  const int64_t append = static_cast<int64_t>(cfg.max_seqs) * (sizeof(vk::AppendSeqDesc) + 4 * (max_pages + 1));
+  // descriptors, block-table entries and (with a lossless tier) the call's lossless units: the
+  // sink pages and the pages the recent tier can hold, two int32 per 16-token unit
+  const int64_t upp = cfg.block_size / vk::kUnit;
+  const bool ll = cfg.sink_format == VK_FMT_LOSSLESS || cfg.recent_format == VK_FMT_LOSSLESS;
+  const int64_t ll_pages = ll ? (cfg.sink_tokens + cfg.block_size - 1) / cfg.block_size +
+                                    (cfg.recent_tokens + cfg.block_size - 1) / cfg.block_size + 2
+                              : 0;
+  const int64_t append = static_cast<int64_t>(cfg.max_seqs) *
+                         (sizeof(vk::AppendSeqDesc) + 4 * (max_pages + 1) + 8 * upp * std::min(ll_pages, max_pages));
   // a retier of every page of every sequence in one launch, up to kRetierTasksPerLaunch
   const int64_t retier = std::min<int64_t>(static_cast<int64_t>(cfg.max_seqs) * max_pages, kRetierTasksPerLaunch) *
                          static_cast<int64_t>(sizeof(vk::RetierTask));
@@ -192,8 +200,10 @@ std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
   const int rs = ring_slots(cfg);
   for (int r = 0; r < kRingMax; ++r) s.push_back(r < rs ? plan_bytes_for(cfg) : 0);  // staged plans
   s.push_back(vk::page_bytes(cfg, VK_FMT_TERNARY2));                          // dummy page
+  s.push_back(static_cast<int64_t>(cfg.n_layers) * cfg.pages_lossless * vk::page_bytes(cfg, VK_FMT_LOSSLESS));
   return s;
 }
+constexpr size_t kBufDummy = 8 + kRingMax, kBufLossless = 9 + kRingMax;  // indices in buffer_sizes
 
 void free_all(vk_cache* c) {
   for (void* p : c->allocations) (void)hipFree(p);
@@ -249,7 +259,7 @@ VK_API vk_status vk_cache_device_bytes(const vk_cache_config* cfg, int64_t* byte
 }
 
 VK_API int64_t vk_page_bytes(const vk_cache_config* cfg, int32_t fmt) {
-  if (!cfg || fmt < 0 || fmt > 2 || !vk::validate_config(*cfg).empty()) return 0;
+  if (!cfg || fmt < 0 || fmt > VK_FMT_LOSSLESS || !vk::validate_config(*cfg).empty()) return 0;
   return vk::page_bytes(*cfg, fmt);
 }
 
@@ -280,7 +290,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   c->allocations = ptrs;
   // pools and gamma start zeroed (finite bytes everywhere); the block table starts empty;
   // the dummy page (target of speculative decode loads) is zero too
-  for (size_t i : {size_t(0), size_t(1), size_t(2), size_t(3), size_t(8 + kRingMax)})
+  for (size_t i : {size_t(0), size_t(1), size_t(2), size_t(3), kBufDummy, kBufLossless})
     if (ptrs[i]) {
       e = hipMemset(ptrs[i], 0, static_cast<size_t>(sizes[i]));
       if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)); }
@@ -288,9 +298,9 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   e = hipMemset(ptrs[4], 0xFF, static_cast<size_t>(sizes[4]));
   if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)); }
   vk::PoolsView& P = c->pools;
-  const int64_t caps[3] = {cfg->pages_ternary, cfg->pages_fp8, cfg->pages_f16};
-  for (int f = 0; f < 3; ++f) {
-    P.pool[f] = static_cast<uint8_t*>(ptrs[f]);
+  const int64_t caps[4] = {cfg->pages_ternary, cfg->pages_fp8, cfg->pages_f16, cfg->pages_lossless};
+  for (int f = 0; f < 4; ++f) {
+    P.pool[f] = static_cast<uint8_t*>(ptrs[f < 3 ? f : kBufLossless]);
     P.cap[f] = caps[f];
     P.tile_bytes[f] = vk::tile_bytes(*cfg, f);
     P.page_bytes[f] = vk::page_bytes(*cfg, f);
@@ -309,7 +319,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   c->partials = static_cast<double*>(ptrs[5]);
   c->seg = static_cast<vk::SegInfo*>(ptrs[6]);
   c->dec_partials = static_cast<float*>(ptrs[7]);
-  P.dummy_page = static_cast<const uint8_t*>(ptrs[8 + kRingMax]);
+  P.dummy_page = static_cast<const uint8_t*>(ptrs[kBufDummy]);
   c->plan_bytes = plan_bytes_for(*cfg);
   c->n_ring = ring_slots(*cfg);
   for (int r = 0; r < c->n_ring; ++r) {
@@ -323,7 +333,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e)); }
   c->host.reset(new vk::HostState(*cfg));
   c->stats.device_bytes = c->device_bytes;
-  for (int f = 0; f < 3; ++f) c->stats.pool_pages[f] = caps[f];
+  for (int f = 0; f < 4; ++f) c->stats.pool_pages[f] = caps[f];
   *out = c.release();
   g_error.clear();
   return VK_OK;
@@ -348,14 +358,30 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   std::string err;
   st = c->host->plan_append(n_seqs, seq_ids, counts, &plan, &err);
   if (st) return fail(st, "%s", err.c_str());
+  if (plan.new_pages[VK_FMT_LOSSLESS] > 0 && dtype != VK_DTYPE_BF16)
+    return fail(VK_ERR_ARG, "lossless pages hold bfloat16 input");
   const int64_t n_seg = static_cast<int64_t>(n_layers) * n_seqs * 2;
   const int64_t row = static_cast<int64_t>(cfg.n_kv_heads) * cfg.head_dim;
   if (n_seg > kMaxSegs || 2 * static_cast<int64_t>(n_layers) * plan.total_blk > kMaxPartials)
     return fail(VK_ERR_ARG, "append too large for one call (%lld segments, %lld absmean blocks per layer); split it",
                 static_cast<long long>(n_seg), static_cast<long long>(plan.total_blk));
   const int64_t total = static_cast<int64_t>(n_layers) * plan.total_tasks;
+  // the 16-token units of lossless pages: (sequence index, unit) pairs for the pack kernel that
+  // writes them
+  std::vector<int32_t> ll_units;
+  for (size_t i = 0; i < plan.seqs.size(); ++i) {
+    const vk::AppendSeqDesc& d = plan.seqs[i];
+    const int32_t unit_end = (d.t0 + d.n_tokens + vk::kUnit - 1) / vk::kUnit;
+    for (int32_t u = d.unit_first; u < unit_end; ++u) {
+      const int32_t page = u * vk::kUnit / cfg.block_size;
+      if (vk::entry_fmt(plan.entries[d.page_off + page - d.page_first]) == VK_FMT_LOSSLESS) {
+        ll_units.push_back(static_cast<int32_t>(i));
+        ll_units.push_back(u);
+      }
+    }
+  }
   const int64_t need = static_cast<int64_t>(plan.seqs.size()) * sizeof(vk::AppendSeqDesc) +
-                       static_cast<int64_t>(plan.entries.size()) * 4;
+                       static_cast<int64_t>(plan.entries.size()) * 4 + static_cast<int64_t>(ll_units.size()) * 4;
   if (need > c->plan_bytes) return fail(VK_ERR_ARG, "append plan too large");
   st = set_device(c);
   if (st) return st;
@@ -373,6 +399,8 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   const size_t desc_bytes = plan.seqs.size() * sizeof(vk::AppendSeqDesc);
   std::memcpy(hp, plan.seqs.data(), desc_bytes);
   std::memcpy(hp + desc_bytes, plan.entries.data(), plan.entries.size() * 4);
+  const size_t ll_off = desc_bytes + plan.entries.size() * 4;
+  if (!ll_units.empty()) std::memcpy(hp + ll_off, ll_units.data(), ll_units.size() * 4);
   e = hipMemcpyAsync(c->plan_dev[slot], hp, static_cast<size_t>(need), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync");
   vk::AppendArgs a{};
@@ -409,8 +437,11 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
     if (eq_b && nb0 > 0) a.seq_blk = static_cast<int32_t>(nb0);
   }
   a.eps = cfg.eps;
-  a.all_ternary = std::all_of(plan.entries.begin(), plan.entries.end(),
-                              [](int32_t e) { return vk::entry_fmt(e) == VK_FMT_TERNARY2; });
+  a.ll_units = reinterpret_cast<const int32_t*>(c->plan_dev[slot] + ll_off);
+  a.n_ll_units = static_cast<int32_t>(ll_units.size() / 2);
+  a.all_ternary = std::all_of(plan.entries.begin(), plan.entries.end(), [](int32_t e) {
+    return vk::entry_fmt(e) == VK_FMT_TERNARY2 || vk::entry_fmt(e) == VK_FMT_LOSSLESS;
+  });
   if (c->timer.on) {
     // algorithmic bytes: pass 1 reads the ternary-routed input once; pass 2 reads
     // all input once and writes every stored byte once (+ one gamma per ternary page)
@@ -420,7 +451,10 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
     c->timer.add_bytes(VK_KERNEL_ABSMEAN, layers * 2.0 * tern_tokens * row * 2.0);
     c->timer.add_bytes(VK_KERNEL_FINALIZE, layers * 2.0 * static_cast<double>(plan.total_blk) * 8.0);
     const double in_bytes = layers * 2.0 * static_cast<double>(plan.total_tokens) * row * 2.0;
-    const double per_elem[3] = {0.25, 1.0 + (cfg.fp8_dynamic ? 4.0 / cfg.head_dim : 0.0), 2.0};  // + token scales
+    // + token scales; lossless: the coded streams (1.5 bytes per element) and a 16-byte header per
+    // 16 tokens (its exceptions, about 0.02% of the values on normal data, are not counted)
+    const double per_elem[4] = {0.25, 1.0 + (cfg.fp8_dynamic ? 4.0 / cfg.head_dim : 0.0), 2.0,
+                                1.5 + 1.0 / cfg.head_dim};
     double out_bytes = 0.0;
     for (const vk::AppendSeqDesc& d : plan.seqs) {
       for (int32_t j = 0; j < d.n_pages; ++j) {
@@ -552,13 +586,13 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   const int g = cfg.n_q_heads / cfg.n_kv_heads;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int64_t units[3] = {0, 0, 0};
+  int64_t units[4] = {0, 0, 0, 0};
   int32_t splits_used = 1, steal_used = 0;
   const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
   // sequences per launch: every (sequence, KV head) needs room for a split's partial and the
   // fp8 / fp16 blocks' partials
   const int32_t per_launch = static_cast<int32_t>(std::max<int64_t>(
-      1, std::min<int64_t>(vk::kDecodeMaxSeqs, kDecodeScratchItems / ((1 + kDecodeMixedParts) * cfg.n_kv_heads))));
+      1, std::min<int64_t>(vk::kDecodeMaxSeqs, kDecodeScratchItems / ((2 + kDecodeMixedParts) * cfg.n_kv_heads))));
   for (int32_t base = 0; base < n_seqs; base += per_launch) {
     const int32_t nb = std::min<int32_t>(per_launch, n_seqs - base);
     vk::DecodeArgs a{};
@@ -576,7 +610,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     a.units_per_iter = decode_units_per_iter();
     a.scale_log2 = scale * 1.4426950408889634f;
     int32_t max_units = 0;
-    int64_t cu[3] = {0, 0, 0};  // attended units per format in this launch
+    int64_t cu[4] = {0, 0, 0, 0};  // attended units per format in this launch
     // longest attended ranges first: their blocks are dispatched first, shorter ones fill in
     int32_t order[vk::kDecodeMaxSeqs], units_of[vk::kDecodeMaxSeqs];
     for (int32_t i = 0; i < nb; ++i) {
@@ -594,11 +628,18 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       c->host->count_units(sid, window, cu);
       c->host->mixed_ranges(sid, window, a.mix[i]);
     }
-    for (int f = 0; f < 3; ++f) units[f] += cu[f];
-    // matrix-core path: fp8 / fp16 pages go to one more block per (sequence, KV head), which
-    // writes one more partial state
-    const bool mixed = mfma && (cu[1] + cu[2]) > 0;
-    const int n_mix = mixed ? kDecodeMixedParts : 0;
+    for (int f = 0; f < 4; ++f) units[f] += cu[f];
+    // matrix-core path: fp8 / fp16 / lossless pages go to one more block per (sequence, KV head),
+    // which writes one more partial state
+    const bool mixed = mfma && (cu[1] + cu[2] + cu[3]) > 0;
+    // fp8 / fp16 pages: n_mix more blocks per (sequence, KV head); lossless pages: one more launch
+    // of a block per (sequence, KV head); each writes a partial state of its own
+    const int n_ll = mfma && cu[3] > 0 ? 1 : 0;
+    const int n_fp = mfma && (cu[1] + cu[2]) > 0 ? kDecodeMixedParts : 0;
+    const int n_mix = n_fp + n_ll;
+    a.lossless = n_ll;
+    a.n_mix_parts = n_fp;
+    a.part_base = 0;
     const int64_t items = static_cast<int64_t>(nb) * cfg.n_kv_heads;
     const int32_t max_splits = static_cast<int32_t>(
         std::min<int64_t>(kDecodeMaxSplits - n_mix, kDecodeScratchItems / items - n_mix));
@@ -634,7 +675,9 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       const double row = cfg.head_dim;
       const double unit_kv = 2.0 * 16.0 * cfg.n_kv_heads;  // K and V, 16 tokens, every KV head
       const double tern_bytes = unit_kv * cu[0] * row / 4.0;
-      const double other_bytes = unit_kv * (cu[1] * (row + (cfg.fp8_dynamic ? 4.0 : 0.0)) + cu[2] * row * 2.0);
+      // lossless units: header and the two coded streams (exceptions not counted)
+      const double other_bytes = unit_kv * (cu[1] * (row + (cfg.fp8_dynamic ? 4.0 : 0.0)) + cu[2] * row * 2.0 +
+                                            cu[3] * (row * 1.5 + 1.0));
       const double q_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 2.0;
       const double out_bytes = static_cast<double>(nb) * cfg.n_q_heads * cfg.head_dim * 4.0;
       const double part1 = static_cast<double>(nb) * cfg.n_q_heads * (cfg.head_dim + 2) * 4.0;  // one part
@@ -648,7 +691,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   c->stats.decode_calls += 1;
   c->stats.last_decode_splits = splits_used;
   c->stats.last_decode_steal = steal_used;
-  for (int f = 0; f < 3; ++f) {
+  for (int f = 0; f < 4; ++f) {
     c->stats.last_decode_units[f] = units[f];
     c->stats.total_decode_units[f] += units[f];
   }
@@ -693,7 +736,8 @@ VK_API vk_status vk_read_pages(vk_cache* c, int32_t layer, int32_t seq, int32_t 
   if (st) return st;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(c, e, "hipDeviceSynchronize");
-  const int64_t stride = vk::page_bytes(cfg, VK_FMT_F16);
+  int64_t stride = 0;  // the largest page of any format
+  for (int f = 0; f < 4; ++f) stride = std::max(stride, vk::page_bytes(cfg, f));
   for (int32_t j = 0; j < n_pages; ++j) {
     const int32_t ent = ss.pages[page0 + j];
     if (ent == vk::kNoPage) {  // freed by eviction
@@ -723,7 +767,7 @@ VK_API vk_status vk_read_pages(vk_cache* c, int32_t layer, int32_t seq, int32_t 
 VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out) {
   if (!c || !out) return fail(VK_ERR_ARG, "NULL argument");
   vk_stats s = c->stats;
-  for (int f = 0; f < 3; ++f) {
+  for (int f = 0; f < 4; ++f) {
     s.pages_used[f] = c->host->pages_used(f);
     s.tokens_stored[f] = c->host->tokens_stored(f);
   }

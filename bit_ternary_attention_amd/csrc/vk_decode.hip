@@ -558,7 +558,9 @@ __device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], cons
 
 // STEAL: one 12-wave block per (sequence, KV head, split) whose waves take pieces of the
 // block's units from a shared counter (launches of all-ternary pages with a block per CU).
-template <int D, int G, int QDT, int PF, bool DYN, bool STEAL>
+// LL: the fp8 / fp16 blocks also read lossless pages (an instance of its own, launched only when
+// a launch attends lossless units: their decode needs registers the other instances keep).
+template <int D, int G, int QDT, int PF, bool DYN, bool STEAL, bool LL = false>
 __global__ __launch_bounds__(64 * (STEAL ? kStealWaves : kMfmaWaves)) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void k_decode_mfma(DecodeArgs a) {
   constexpr int NW = STEAL ? kStealWaves : kMfmaWaves;  // waves per block
@@ -602,7 +604,7 @@ void k_decode_mfma(DecodeArgs a) {
   const int cslot = c16 / W;  // this lane's column slot
   // grid (KV head, sequence, split): blocks dispatched together read the heads' slices of the
   // same pages
-  const int split = blockIdx.z, kvh = blockIdx.x, b = blockIdx.y;
+  const int split = blockIdx.z + a.part_base, kvh = blockIdx.x, b = blockIdx.y;
   const int slot = a.slots[b], L = a.lens[b];
   const PoolsView& P = a.P;
   // The kernel arguments the set-up reads, loaded in one batch: left to the compiler, the
@@ -618,7 +620,8 @@ void k_decode_mfma(DecodeArgs a) {
   const Units R = attended(L, a.sink_tokens, a.window);
   const int n_a = R.a_end;
   const int U = R.a_end + (R.b_end - R.b_begin);
-  const bool mixed_part = split >= a.n_splits;  // one of the extra blocks of the fp8 / fp16 pages
+  // one of the extra blocks: fp8 / fp16 pages, or (LL) the lossless pages
+  const bool mixed_part = LL || split >= a.n_splits;
   const int s_begin = min(split * a.units_per_split, U);  // empty past the sequence's units
   const int s_end = min(s_begin + a.units_per_split, U);
   // a wave's share of the split (stealing waves: the whole split, taken piece by piece)
@@ -1098,6 +1101,126 @@ void k_decode_mfma(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) rt[r] = vv[r] * inv;
         vscale = vmax;
       }
+    } else if (LL && fmt == VK_FMT_LOSSLESS) {
+      // bfloat16 values of the unit's K and V groups, rebuilt from the exponent codes (escapes
+      // from the exception list, this lane's run of it) and the sign+mantissa bytes, or read
+      // raw; each group scaled by one power of two into f16 (largest magnitude below 2^15,
+      // exact for every value within 2^-28 of it) and the scale taken back out of the scores
+      // (ks) and of the P*V sum (vscale).  This lane's D/4 values of a group, in position order
+      // p: keys dims dbase + p; values dim 16 (p / 4) + c16, token 4 grp + p % 4 -- the very
+      // positions of its A operands, so each value goes straight into its operand word (as
+      // bfloat16 first, converted once the group's largest exponent is known).
+      const uint8_t* pg = P.pool[3] + (layer * P.cap[3] + idx) * P.page_bytes[3];
+      const int64_t slot_b = 32 * D + 16;
+      constexpr int NW = D / 32;     // 8-value chunks per lane (one code word each)
+      // out: the operand words as bfloat16 pairs.  Keys: row 2 (w/2) + q/4, word q % 4, half
+      // w % 2 (the pair (d, d + 8) of a 16-dim block); values: row j / 2, words 2 (j % 2) and
+      // 2 (j % 2) + 1 hold tokens (0, 1) and (2, 3) of dim 16 j + c16
+      auto lossless_group = [&](const uint8_t* slot, bool keys, uint32_t (&out)[NW][4]) -> float {
+        const uint4 hd = *reinterpret_cast<const uint4*>(slot);
+        const int cen = static_cast<int>(hd.x & 0xFFu);
+        const bool raw = (hd.x >> 8) & 1u;
+        const uint8_t* body = slot + 16;
+        const uint8_t* codes = body + 16 * D;
+        // element index (stored order) of the first value of chunk w; values: the chunk is
+        // dims 16 (2w) + c16 and 16 (2w + 1) + c16, four tokens each
+        auto e0 = [&](int w) { return keys ? c16 * D + dbase + 8 * w : (32 * w + c16) * 16 + 4 * grp; };
+        auto put = [&](int w, int q, uint32_t h) {   // q = position within the chunk
+          if (keys) out[2 * (w >> 1) + (q >> 2)][q & 3] |= h << (16 * (w & 1));
+          else out[w][2 * (q >> 2) + ((q >> 1) & 1)] |= h << (16 * (q & 1));
+        };
+#pragma unroll
+        for (int x = 0; x < NW; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) out[x][y] = 0u;
+        int emax = 0;
+        if (raw) {
+          const uint16_t* b16 = reinterpret_cast<const uint16_t*>(body);
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            uint32_t v[4];
+            if (keys) {
+              const uint4 x = *reinterpret_cast<const uint4*>(b16 + e0(w));
+              v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+            } else {
+              const uint2 x = *reinterpret_cast<const uint2*>(b16 + e0(w));
+              const uint2 y = *reinterpret_cast<const uint2*>(b16 + e0(w) + 256);
+              v[0] = x.x; v[1] = x.y; v[2] = y.x; v[3] = y.y;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t h = (v[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+              emax = max(emax, static_cast<int>((h >> 7) & 0xFFu));
+              put(w, q, h);
+            }
+          }
+        } else {
+          uint32_t cw[NW];
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            if (keys) {
+              cw[w] = *reinterpret_cast<const uint32_t*>(codes + (e0(w) >> 1));
+            } else {
+              cw[w] = static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(codes + (e0(w) >> 1))) |
+                      (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(codes + ((e0(w) + 256) >> 1))) << 16);
+            }
+          }
+          int cnt = 0;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const uint32_t x = cw[w];
+            cnt += __builtin_popcount(x & (x >> 1) & (x >> 2) & (x >> 3) & 0x11111111u);
+          }
+          int incl = cnt;  // exclusive prefix over the lanes: this lane's first exception
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+          }
+          const uint8_t* exc = codes + 8 * D + (incl - cnt);
+          int k = 0;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            uint32_t sm[2];
+            if (keys) {
+              const uint2 x = *reinterpret_cast<const uint2*>(body + e0(w));
+              sm[0] = x.x; sm[1] = x.y;
+            } else {
+              sm[0] = *reinterpret_cast<const uint32_t*>(body + e0(w));
+              sm[1] = *reinterpret_cast<const uint32_t*>(body + e0(w) + 256);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t cd = (cw[w] >> (4 * q)) & 0xFu;
+              const uint32_t e = cd == 15u ? exc[k++] : static_cast<uint32_t>(cen - 11) + cd;
+              const uint32_t b = (sm[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+              emax = max(emax, static_cast<int>(e & 0xFFu));
+              put(w, q, ((b & 0x80u) << 8) | ((e & 0xFFu) << 7) | (b & 0x7Fu));
+            }
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
+        const int sh = emax == 0 ? 0 : min(141 - emax, 126);
+        const float mul = pow2i(sh);
+#pragma unroll
+        for (int x = 0; x < NW; ++x)
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            const uint32_t u = out[x][y];
+            out[x][y] = f16_bits(__uint_as_float(u << 16) * mul) | (f16_bits(__uint_as_float(u & 0xFFFF0000u) * mul) << 16);
+          }
+        return pow2i(-sh);
+      };
+      uint32_t ow[NW][4];
+      const float kinv = lossless_group(pg + kvh * P.tile_bytes[3] + upi * slot_b, true, ow);
+#pragma unroll
+      for (int c = 0; c < 2 * NC; ++c) ka[c] = __builtin_bit_cast(h8_t, u4_t{ow[c][0], ow[c][1], ow[c][2], ow[c][3]});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ks[r] = kinv;
+      vscale = lossless_group(pg + (P.hkv + kvh) * P.tile_bytes[3] + upi * slot_b, false, ow);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) va[j] = __builtin_bit_cast(h4_t, u2_t{ow[j >> 1][2 * (j & 1)], ow[j >> 1][2 * (j & 1) + 1]});
     } else {
       const uint8_t* pg = P.pool[2] + (layer * P.cap[2] + idx) * P.page_bytes[2];
       const uint4* kp =
@@ -1139,12 +1262,15 @@ void k_decode_mfma(DecodeArgs a) {
         const int lu_l = c0 + lane;
         const bool in_rg = lu_l < m_hi[rg];
         const int32_t ent_l = in_rg ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
-        uint64_t todo = __ballot(in_rg && (static_cast<uint32_t>(ent_l) >> 30) != VK_FMT_TERNARY2);
+        const uint32_t fmt_l = static_cast<uint32_t>(ent_l) >> 30;
+        uint64_t todo = __ballot(in_rg && (LL ? fmt_l == VK_FMT_LOSSLESS
+                                              : fmt_l != VK_FMT_TERNARY2 && fmt_l != VK_FMT_LOSSLESS));
         while (todo) {
           const int k = __builtin_ctzll(todo);
           todo &= todo - 1;
           // the extra blocks' waves take the units in turn
-          if (rank++ % (NW * (a.n_parts - a.n_splits)) != (split - a.n_splits) * NW + wave) continue;
+          if (LL ? rank++ % NW != wave
+                 : rank++ % (NW * a.n_mix_parts) != (split - a.n_splits) * NW + wave) continue;
           const int lu = c0 + k;
           const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
           h8_t ka[NS];
@@ -1601,7 +1727,7 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   // matrix-core path: grid (hkv, n_seqs, n_parts), split n_splits (when present) takes the
   // fp8 / fp16 pages; vector-ALU path: grid (n_splits, hkv, n_seqs)
   const dim3 grid = a.kernel == VK_DECODE_VALU ? dim3(a.n_splits, a.P.hkv, a.n_seqs)
-                                               : dim3(a.P.hkv, a.n_seqs, a.n_parts);
+                                               : dim3(a.P.hkv, a.n_seqs, a.n_splits + a.n_mix_parts);
   if (t) t->begin(VK_KERNEL_DECODE, s);
   if (a.kernel == VK_DECODE_VALU) {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
@@ -1618,6 +1744,13 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   } else {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 4, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
     else k_decode_mfma<D, G, 0, 4, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+  }
+  if (a.lossless) {  // the lossless pages: one block per (KV head, sequence), part n_splits + n_mix_parts
+    DecodeArgs b = a;
+    b.part_base = a.n_splits + a.n_mix_parts;
+    const dim3 g1(a.P.hkv, a.n_seqs, 1);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, false, false, true><<<g1, 64 * kMfmaWaves, 0, s>>>(b);
+    else k_decode_mfma<D, G, 0, 8, false, false, true><<<g1, 64 * kMfmaWaves, 0, s>>>(b);
   }
   if (t) t->end(VK_KERNEL_DECODE, s);
   if (a.n_parts > 1) {
@@ -1641,10 +1774,22 @@ hipError_t launch_d(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTim
 
 }  // namespace
 
+// This file is compiled twice, once per head dim (VK_DECODE_DIM = 64 or 128), so that the two
+// halves of the kernel instances build in parallel.
+#if VK_DECODE_DIM == 64
+hipError_t launch_decode_d64(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t) {
+  return launch_d<64>(a, group, s, t);
+}
+#elif VK_DECODE_DIM == 128
+hipError_t launch_decode_d64(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t);
+
 hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t) {
   if (a.P.dim == 128) return launch_d<128>(a, group, s, t);
-  if (a.P.dim == 64) return launch_d<64>(a, group, s, t);
+  if (a.P.dim == 64) return launch_decode_d64(a, group, s, t);
   return hipErrorInvalidValue;
 }
+#else
+#error "compile with -DVK_DECODE_DIM=64 or -DVK_DECODE_DIM=128"
+#endif
 
 }  // namespace vk

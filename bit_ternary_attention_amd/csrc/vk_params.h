@@ -14,12 +14,12 @@ struct RetierTask;     // host_state.h
 //   pool[f] + (layer * cap[f] + idx) * page_bytes[f]
 // with the page laid out [K tile head 0..Hkv-1][V tile head 0..Hkv-1].
 struct PoolsView {
-  uint8_t* pool[3];
+  uint8_t* pool[4];        // by format (VK_FMT_*)
   float* gamma;            // [n_layers][cap[0]][2]: K and V gamma of ternary pages
   int32_t* block_table;    // [max_seqs][max_pages]: (format << 30) | pool index
-  int64_t cap[3];          // pages per layer
-  int64_t tile_bytes[3];   // one (K|V, head) tile
-  int64_t page_bytes[3];
+  int64_t cap[4];          // pages per layer
+  int64_t tile_bytes[4];   // one (K|V, head) tile
+  int64_t page_bytes[4];
   int32_t max_pages;
   int32_t n_layers;
   int32_t hkv;
@@ -60,7 +60,9 @@ struct AppendArgs {
   int32_t pack_blocks;     // pack grid: ceil(n_layers * total_tasks / tasks_per_blk)
   int32_t seq_tasks;       // pack tasks of every sequence when they all have the same count, else 0
   int32_t seq_blk;         // absmean blocks of every sequence when they all have the same count, else 0
-  int32_t all_ternary;     // every touched page is ternary (the pack kernel's lean instance)
+  int32_t all_ternary;     // every touched page is ternary or lossless (the pack kernel's lean instance)
+  const int32_t* ll_units; // [n_ll_units][2]: (sequence index, unit) of every lossless 16-token unit
+  int32_t n_ll_units;      // written by a pack launch of their own (the main one skips them)
   float eps;
 };
 
@@ -81,12 +83,16 @@ struct DecodeArgs {
   int32_t n_splits;        // splits of the attended units (parts 0 .. n_splits-1)
   int32_t units_per_split; // split x takes logical units [x u, (x + 1) u) of its sequence
                            // (none past the sequence's end: an empty part)
-  int32_t n_parts;         // n_splits, or n_splits + 1 when part n_splits holds the fp8 / fp16
-                           // pages (matrix-core path); 1 = the decode kernel writes out directly
+  int32_t n_parts;         // n_splits, + n_mix_parts, + 1 with lossless pages (matrix-core path);
+                           // 1 = the decode kernel writes out directly
   int32_t kernel;          // VK_DECODE_VALU or VK_DECODE_MFMA
   int32_t units_per_iter;  // matrix-core kernel: prefetch depth in 16-token units (4 or 8)
   int32_t steal;           // matrix-core kernel: 12-wave blocks whose waves take 16-unit pieces of
                            // the block's units from a shared counter
+  int32_t lossless;        // the launch attends lossless pages: after the main launch, one more launch
+                           // (an instance that reads them) writes part n_splits + n_mix_parts
+  int32_t n_mix_parts;     // parts n_splits .. n_splits + n_mix_parts - 1 hold the fp8 / fp16 pages
+  int32_t part_base;       // part index of blockIdx.z == 0
   float scale_log2;        // softmax scale * log2(e)
   int32_t slots[kDecodeMaxSeqs];   // launch order: longest attended range first
   int32_t lens[kDecodeMaxSeqs];

@@ -238,15 +238,17 @@ __global__ __launch_bounds__(64) void k_gamma_finalize(AppendArgs a) {
 // one after another within a layer, layer after layer; each block takes a contiguous run of
 // tasks_per_blk of them, so its consecutive tasks are the heads (then K or V) of the same 16
 // tokens and it walks whole input rows.
-// MIXED = false: every page of the call is ternary (the fp8 / fp16 routes are left out, which
-// keeps the register count, and so the resident waves per SIMD, where the ternary route needs it)
-template <int DT, int D, bool MIXED>
+// MODE 0: every page of the call is ternary (the other routes are left out, which keeps the
+// register count, and so the resident waves per SIMD, where the ternary route needs it);
+// MODE 1: ternary, fp8 and fp16 pages; MODE 2: lossless pages as well.
+template <int DT, int D, int MODE>
 __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   constexpr int CPR = D / 8;     // 16-byte chunks per token row
   constexpr int RPI = 64 / CPR;  // rows per wave-wide load
   constexpr int NI = 16 / RPI;   // loads per lane per unit
   constexpr int DPL = D / 64;    // head dims per lane in the transposed fp8 / fp16 value stores
   __shared__ uint32_t lds[D * 16 * 2 / 4 + 4];
+  __shared__ uint32_t lds_bm[MODE == 2 ? 64 : 1], lds_off[MODE == 2 ? 64 : 1];  // lossless exceptions
   uint16_t* lds16 = reinterpret_cast<uint16_t*>(lds);
   uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
 
@@ -255,26 +257,40 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   const int64_t row = static_cast<int64_t>(hkv) * D;
   const int c = lane % CPR, rg = lane / CPR;
 
-  const int64_t g_end = static_cast<int64_t>(a.n_layers) * a.total_tasks;
-  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * a.tasks_per_blk;
-  const int64_t g1 = g0 + a.tasks_per_blk < g_end ? g0 + a.tasks_per_blk : g_end;
+  // MODE 2 runs over the lossless units only (a list of (sequence index, unit)), one task per block
+  const int64_t g_end = static_cast<int64_t>(a.n_layers) * (MODE == 2 ? 2LL * hkv * a.n_ll_units : a.total_tasks);
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (MODE == 2 ? 1 : a.tasks_per_blk);
+  const int64_t g1 = MODE == 2 ? g0 + 1 : (g0 + a.tasks_per_blk < g_end ? g0 + a.tasks_per_blk : g_end);
   int i = -1, l_rel = -1, task_end = 0;
   AppendSeqDesc d{};
   for (int64_t g = g0; g < g1; ++g) {
-    const int lr = static_cast<int>(g / a.total_tasks);
-    const int t = static_cast<int>(g - static_cast<int64_t>(lr) * a.total_tasks);
-    if (lr != l_rel || t >= task_end) {  // uniform: the block moves on to another sequence
-      l_rel = lr;
-      i = a.seq_tasks ? t / a.seq_tasks : find_seq<&AppendSeqDesc::task_off>(a.descs, a.n_seqs, t);
+    int h, kv, uk;
+    if constexpr (MODE == 2) {
+      const int64_t per_layer = 2LL * hkv * a.n_ll_units;
+      l_rel = static_cast<int>(g / per_layer);
+      const int r = static_cast<int>(g - static_cast<int64_t>(l_rel) * per_layer);
+      const int lu = r / (2 * hkv);
+      h = r % hkv;
+      kv = (r / hkv) & 1;
+      i = a.ll_units[2 * lu];
       d = a.descs[i];
-      task_end = d.task_off + ((d.t0 + d.n_tokens + 15) / 16 - d.unit_first) * 2 * hkv;
+      uk = a.ll_units[2 * lu + 1] - d.unit_first;
+    } else {
+      const int lr = static_cast<int>(g / a.total_tasks);
+      const int t = static_cast<int>(g - static_cast<int64_t>(lr) * a.total_tasks);
+      if (lr != l_rel || t >= task_end) {  // uniform: the block moves on to another sequence
+        l_rel = lr;
+        i = a.seq_tasks ? t / a.seq_tasks : find_seq<&AppendSeqDesc::task_off>(a.descs, a.n_seqs, t);
+        d = a.descs[i];
+        task_end = d.task_off + ((d.t0 + d.n_tokens + 15) / 16 - d.unit_first) * 2 * hkv;
+      }
+      const int task = t - d.task_off;
+      h = task % hkv;
+      kv = (task / hkv) & 1;
+      uk = task / (2 * hkv);
     }
     const int layer = a.layer_begin + l_rel;
     const int t1 = d.t0 + d.n_tokens;
-    const int task = t - d.task_off;
-    const int h = task % hkv;
-    const int kv = (task / hkv) & 1;
-    const int uk = task / (2 * hkv);
     const int unit = d.unit_first + uk;
     if (unit * 16 >= t1) continue;  // uniform over the block
     const int pos0 = unit * 16;
@@ -288,8 +304,9 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
     const uint16_t* src =
         (kv ? a.v : a.k) + (static_cast<int64_t>(l_rel) * a.total_tokens + d.tok_off) * row + h * D + c * 8;
 
-    if (l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
+    if (MODE != 2 && l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
       a.P.block_table[static_cast<int64_t>(d.slot) * a.P.max_pages + page] = entry;
+    if (MODE != 2 && fmt == VK_FMT_LOSSLESS) continue;  // written by the launch over the lossless units
 
     uint4 w[NI];
     bool ok[NI];
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
       w[k] = ok[k] ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * row) : make_uint4(0, 0, 0, 0);
     }
 
-    if (fmt == VK_FMT_TERNARY2) {
+    if (MODE != 2 && fmt == VK_FMT_TERNARY2) {
       const SegInfo si = a.seg[(l_rel * a.n_seqs + i) * 2 + kv];
       if (upi == 0 && h == 0 && lane == 0)
         a.P.gamma[(static_cast<int64_t>(layer) * a.P.cap[0] + idx) * 2 + kv] = si.gamma;
@@ -342,9 +359,9 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
         else *reinterpret_cast<uint32_t*>(vdst) = w0;
         __syncthreads();
       }
-    } else if (!MIXED) {
-      // (not reached: the host launches this instance only when every page is ternary)
-    } else if (fmt == VK_FMT_FP8E4M3) {
+    } else if (MODE == 0) {
+      // (not reached: the host launches this instance only when every page is ternary or lossless)
+    } else if (MODE == 1 && fmt == VK_FMT_FP8E4M3) {
       const bool dyn = a.P.fp8_dynamic != 0;
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
@@ -396,7 +413,161 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
         }
         __syncthreads();
       }
-    } else {  // VK_FMT_F16
+    } else if (MODE == 2) {  // the list holds lossless units only
+      // One group: the 16 tokens of this unit, head h, K or V (bfloat16 input).  Exponent
+      // fields around the group's centre c = floor(mean of the nonzero fields) as 4-bit codes
+      // (15 = escape), a sign+mantissa byte per value, and the escaped fields in decode-lane
+      // order; raw values when more than 8 D fields escape.  Slot: [16-byte header][...].
+      // Fields are taken from the input words w[] whenever they are needed (no copies held).
+      uint8_t* slot = tile + static_cast<int64_t>(upi) * (32 * D + 16);
+      auto half = [&](int q) -> uint32_t {  // value q of this lane: row rg * NI + q / 8, dim 8 c + q % 8
+        const uint4 x = w[q >> 3];
+        const int e = q & 7;
+        const uint32_t wd = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+        return (wd >> (16 * (e & 1))) & 0xFFFFu;
+      };
+      auto field = [&](int q) { return (half(q) >> 7) & 0xFFu; };
+      // the fields are recomputed from w[] in every phase below: an empty asm that "changes" w[]
+      // keeps the compiler from holding each phase's per-value results (3 x 8 NI registers)
+      auto launder = [&]() {
+#pragma unroll
+        for (int k = 0; k < NI; ++k) asm volatile("" : "+v"(w[k].x), "+v"(w[k].y), "+v"(w[k].z), "+v"(w[k].w));
+      };
+      uint32_t esum = 0, ecnt = 0;
+#pragma unroll
+      for (int q = 0; q < 8 * NI; ++q) {
+        const uint32_t f = field(q);
+        esum += f;
+        ecnt += f != 0u;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        esum += __shfl_xor(esum, off, 64);
+        ecnt += __shfl_xor(ecnt, off, 64);
+      }
+      const int cen = __builtin_amdgcn_readfirstlane(ecnt ? static_cast<int>(esum / ecnt) : 0);
+      auto code = [&](int q) -> uint32_t {
+        const int ee = static_cast<int>(field(q));
+        return (ee >= cen - 11 && ee <= cen + 3) ? static_cast<uint32_t>(ee - cen + 11) : 15u;
+      };
+      auto smb = [&](int q) { const uint32_t hx = half(q); return ((hx >> 8) & 0x80u) | (hx & 0x7Fu); };
+      launder();
+      int n_exc = 0;
+#pragma unroll
+      for (int q = 0; q < 8 * NI; ++q) n_exc += code(q) == 15u;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) n_exc += __shfl_xor(n_exc, off, 64);
+      n_exc = __builtin_amdgcn_readfirstlane(n_exc);
+      const bool raw = n_exc > 8 * D;
+      if (lane == 0) {
+        *reinterpret_cast<uint4*>(slot) = make_uint4(static_cast<uint32_t>(cen) | (raw ? 0x100u : 0u),
+                                                     raw ? 0u : static_cast<uint32_t>(n_exc), 0u, 0u);
+      }
+      uint8_t* body = slot + 16;
+      launder();
+      if (raw) {
+        if (kv == 0) {
+#pragma unroll
+          for (int k = 0; k < NI; ++k)
+            *reinterpret_cast<uint4*>(body + ((rg * NI + k) * D + 8 * c) * 2) = w[k];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8 * NI; ++q) lds16[(8 * c + q % 8) * 16 + rg * NI + q / 8] = static_cast<uint16_t>(half(q));
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) {
+            const int dd = lane * DPL + j;
+            const uint4* s4 = reinterpret_cast<const uint4*>(lds16 + dd * 16);
+            reinterpret_cast<uint4*>(body + dd * 32)[0] = s4[0];
+            reinterpret_cast<uint4*>(body + dd * 32)[1] = s4[1];
+          }
+          __syncthreads();
+        }
+      } else {
+        // sign+mantissa bytes and codes in the stored order (keys token-major, values
+        // dimension-major, codes two per byte, element 2i in the low nibble of byte i)
+        uint8_t* codes = body + 16 * D;
+        if (kv == 0) {
+#pragma unroll
+          for (int k = 0; k < NI; ++k) {
+            const int r = rg * NI + k;
+            uint32_t lo = 0, hi = 0, nib = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lo |= smb(8 * k + e) << (8 * e);
+              hi |= smb(8 * k + 4 + e) << (8 * e);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nib |= code(8 * k + e) << (4 * e);
+            *reinterpret_cast<uint2*>(body + r * D + 8 * c) = make_uint2(lo, hi);
+            *reinterpret_cast<uint32_t*>(codes + (r * D + 8 * c) / 2) = nib;
+          }
+        } else {
+          uint8_t* lsm = lds8;            // [D][16] sign+mantissa bytes
+          uint8_t* lcd = lds8 + 16 * D;   // [D][16] codes, one per byte
+#pragma unroll
+          for (int q = 0; q < 8 * NI; ++q) {
+            const int at = (8 * c + q % 8) * 16 + rg * NI + q / 8;
+            lsm[at] = static_cast<uint8_t>(smb(q));
+            lcd[at] = static_cast<uint8_t>(code(q));
+          }
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) {
+            const int dd = lane * DPL + j;
+            *reinterpret_cast<uint4*>(body + dd * 16) = *reinterpret_cast<const uint4*>(lsm + dd * 16);
+            const uint4 q4 = *reinterpret_cast<const uint4*>(lcd + dd * 16);   // codes of tokens 0..15
+            const uint32_t qs[4] = {q4.x, q4.y, q4.z, q4.w};
+            uint32_t pk[2] = {0u, 0u};
+#pragma unroll
+            for (int t = 0; t < 16; ++t) pk[t >> 3] |= ((qs[t >> 2] >> (8 * (t & 3))) & 0xFu) << (4 * (t & 7));
+            *reinterpret_cast<uint2*>(codes + dd * 8) = make_uint2(pk[0], pk[1]);
+          }
+          __syncthreads();
+        }
+        if (n_exc > 0) {
+          // exceptions in decode-lane order: keys lane = (d / (D/4)) * 16 + t, position d % (D/4);
+          // values lane = (t / 4) * 16 + d % 16, position (d / 16) * 4 + t % 4
+          auto lane_pos = [&](int q, int& L, int& pos) {
+            const int t = rg * NI + q / 8, d = 8 * c + q % 8;
+            L = kv == 0 ? (d / (D / 4)) * 16 + t : (t / 4) * 16 + (d % 16);
+            pos = kv == 0 ? d % (D / 4) : (d / 16) * 4 + (t % 4);
+          };
+          lds_bm[lane] = 0u;
+          __syncthreads();
+          launder();
+#pragma unroll
+          for (int q = 0; q < 8 * NI; ++q) {
+            if (code(q) != 15u) continue;
+            int L, pos;
+            lane_pos(q, L, pos);
+            atomicOr(&lds_bm[L], 1u << pos);
+          }
+          __syncthreads();
+          // exclusive prefix of the lanes' escape counts
+          const int cnt = __builtin_popcount(lds_bm[lane]);
+          int incl = cnt;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+          }
+          lds_off[lane] = static_cast<uint32_t>(incl - cnt);
+          __syncthreads();
+          launder();
+          uint8_t* exc = codes + 8 * D;
+#pragma unroll
+          for (int q = 0; q < 8 * NI; ++q) {
+            if (code(q) != 15u) continue;
+            int L, pos;
+            lane_pos(q, L, pos);
+            const uint32_t rank = lds_off[L] + __builtin_popcount(lds_bm[L] & ((1u << pos) - 1u));
+            exc[rank] = static_cast<uint8_t>(field(q));
+          }
+          __syncthreads();
+        }
+      }
+    } else if (MODE == 1) {  // VK_FMT_F16
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
         const int r = rg * NI + k;
@@ -507,17 +678,24 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, Laun
   const dim3 g2(a.pack_blocks);
   if (t) t->begin(VK_KERNEL_PACK, s);
   if (a.P.dim == 128 && a.all_ternary) {
-    if (bf) k_pack<1, 128, false><<<g2, 64, 0, s>>>(a);
-    else k_pack<0, 128, false><<<g2, 64, 0, s>>>(a);
+    if (bf) k_pack<1, 128, 0><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 128, 0><<<g2, 64, 0, s>>>(a);
   } else if (a.P.dim == 128) {
-    if (bf) k_pack<1, 128, true><<<g2, 64, 0, s>>>(a);
-    else k_pack<0, 128, true><<<g2, 64, 0, s>>>(a);
+    if (bf) k_pack<1, 128, 1><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 128, 1><<<g2, 64, 0, s>>>(a);
   } else if (a.all_ternary) {
-    if (bf) k_pack<1, 64, false><<<g2, 64, 0, s>>>(a);
-    else k_pack<0, 64, false><<<g2, 64, 0, s>>>(a);
+    if (bf) k_pack<1, 64, 0><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 64, 0><<<g2, 64, 0, s>>>(a);
   } else {
-    if (bf) k_pack<1, 64, true><<<g2, 64, 0, s>>>(a);
-    else k_pack<0, 64, true><<<g2, 64, 0, s>>>(a);
+    if (bf) k_pack<1, 64, 1><<<g2, 64, 0, s>>>(a);
+    else k_pack<0, 64, 1><<<g2, 64, 0, s>>>(a);
+  }
+  // the lossless units: one block per (layer, unit, K|V, head); bfloat16 input only (checked on
+  // the host)
+  if (a.n_ll_units > 0) {
+    const dim3 g3(static_cast<unsigned>(2LL * a.P.hkv * a.n_ll_units * a.n_layers));
+    if (a.P.dim == 128) k_pack<1, 128, 2><<<g3, 64, 0, s>>>(a);
+    else k_pack<1, 64, 2><<<g3, 64, 0, s>>>(a);
   }
   if (t) t->end(VK_KERNEL_PACK, s);
   return hipGetLastError();

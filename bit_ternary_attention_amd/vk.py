@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libvk.so")
 
 OK, ERR_ARG, ERR_OOM, ERR_CAPACITY, ERR_ALIGN, ERR_STATE, ERR_HIP = range(7)
 DTYPE_F16, DTYPE_BF16 = 0, 1
-FMT_TERNARY2, FMT_FP8E4M3, FMT_F16 = 0, 1, 2
+FMT_TERNARY2, FMT_FP8E4M3, FMT_F16, FMT_LOSSLESS = 0, 1, 2, 3
+N_FORMATS = 4
 KERNELS = ("absmean", "finalize", "pack", "decode", "merge", "retier")
 DECODE_DEFAULT, DECODE_VALU, DECODE_MFMA = 0, 1, 2
 
@@ -29,13 +30,14 @@ class CacheConfig(ctypes.Structure):
                 ("sink_tokens", _c_i32), ("sink_format", _c_i32), ("recent_tokens", _c_i32),
                 ("recent_format", _c_i32), ("decode_kernel", _c_i32), ("fp8_dynamic", _c_i32), ("reserved0", _c_i32),
                 ("pages_ternary", _c_i64), ("pages_fp8", _c_i64), ("pages_f16", _c_i64),
-                ("eps", _c_f32), ("fp8_scale", _c_f32), ("page_shuffle_seed", _c_u64)]
+                ("eps", _c_f32), ("fp8_scale", _c_f32), ("page_shuffle_seed", _c_u64),
+                ("pages_lossless", _c_i64)]
 
 
 class Stats(ctypes.Structure):
-    _fields_ = [("device_bytes", _c_i64), ("pool_pages", _c_i64 * 3), ("pages_used", _c_i64 * 3),
-                ("tokens_stored", _c_i64 * 3), ("append_calls", _c_i64), ("decode_calls", _c_i64),
-                ("last_decode_units", _c_i64 * 3), ("total_decode_units", _c_i64 * 3),
+    _fields_ = [("device_bytes", _c_i64), ("pool_pages", _c_i64 * 4), ("pages_used", _c_i64 * 4),
+                ("tokens_stored", _c_i64 * 4), ("append_calls", _c_i64), ("decode_calls", _c_i64),
+                ("last_decode_units", _c_i64 * 4), ("total_decode_units", _c_i64 * 4),
                 ("last_decode_splits", _c_i32), ("last_decode_steal", _c_i32), ("retier_calls", _c_i64),
                 ("pages_retiered", _c_i64), ("pages_evicted", _c_i64)]
 
@@ -245,7 +247,10 @@ class Cache:
 
     def read_pages(self, layer: int, seq: int, page0: int, n_pages: int):
         """(bytes [n_pages, max page bytes] uint8, formats [n_pages], gamma [n_pages, 2])."""
-        stride = page_bytes(self.cfg, FMT_F16)
+        sizes = [page_bytes(self.cfg, f) for f in range(N_FORMATS)]
+        if min(sizes) <= 0:
+            raise RuntimeError("library reports no page size for some format")
+        stride = max(sizes)   # the library lays pages out at the largest page size
         buf = np.zeros((n_pages, stride), dtype=np.uint8)
         fmt = np.zeros(n_pages, dtype=np.int32)
         gam = np.zeros((n_pages, 2), dtype=np.float32)

@@ -29,6 +29,7 @@ import torch
 FMT_TERNARY2 = 0
 FMT_FP8E4M3 = 1
 FMT_F16 = 2
+FMT_LOSSLESS = 3
 
 DTYPE_F16 = 0
 DTYPE_BF16 = 1

@@ -72,13 +72,23 @@ enum {
                            KV head) vector (0 and codes 0 for a zero vector), stored after each
                            tile as block_size float32 values ("dynamic FP8 streaming mode" of
                            Show HN: Vantage-V-AI)                                              */
-  VK_FMT_F16 = 2        /* IEEE float16, round to nearest even from the input                    */
+  VK_FMT_F16 = 2,       /* IEEE float16, round to nearest even from the input                    */
+  VK_FMT_LOSSLESS = 3   /* bfloat16 kept exactly (bfloat16 input only): per 16-token unit and KV
+                           head, K and V apart, the exponent fields coded in 4 bits around the
+                           group's exponent centre (escapes to an exception list) beside one
+                           sign+mantissa byte per value, or the raw values when the exceptions
+                           overflow ("ExANS", ainews.dk: exponent / sign+mantissa streams with a
+                           per-group exponent centre); a slot of 32 head_dim + 16 bytes per
+                           group, of which the decode reads the header, the two streams and the
+                           exceptions.  Like ternary pages, a lossless page is written by one
+                           append                                                           */
 };
 
 /* decode kernels (same results within the decode tolerance; see vk_decode_attn) */
 enum {
   VK_DECODE_DEFAULT = 0,  /* the library's choice (currently VK_DECODE_MFMA)                      */
-  VK_DECODE_VALU = 1,     /* vector ALU: v_dot2_f32_f16 over unpacked codes, query rows in LDS     */
+  VK_DECODE_VALU = 1,     /* vector ALU: v_dot2_f32_f16 over unpacked codes, query rows in LDS (no
+                             lossless pages: a config with them and this kernel is refused) */
   VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores and P*V, pages staged in LDS by
                              buffer-to-LDS copies, codes unpacked to f16 in registers, query rows
                              resident as the B operand; fp8 / fp16 pages in one extra block per
@@ -126,6 +136,7 @@ typedef struct vk_cache_config {
   float fp8_scale;            /* static FP8 scale s > 0 (default 1.0)                  */
   uint64_t page_shuffle_seed; /* 0: pages are handed out in index order; else a seeded
                                  permutation of each free list (splitmix64 Fisher-Yates) */
+  int64_t pages_lossless;     /* pool capacity per layer of VK_FMT_LOSSLESS pages (>= 0) */
 } vk_cache_config;
 
 /* Fills defaults: sink_tokens 4, sink/recent formats ternary/fp8, recent_tokens 0,
@@ -271,7 +282,7 @@ VK_API vk_status vk_seq_length(vk_cache* c, int32_t seq, int32_t* length);
  * Introspection, synchronous (waits for the device): copies pages
  * [page0, page0+n_pages) of (layer, seq) to host (a page freed by vk_evict
  * reads as zeros with format -1).  Page j lands at
- * host_bytes + j * vk_page_bytes(cfg, VK_FMT_F16) (the largest page), laid out
+ * host_bytes + j * vk_page_bytes(cfg, VK_FMT_LOSSLESS) (the largest page), laid out
  * [K tile head 0..Hkv-1][V tile head 0..Hkv-1] in its own format.
  * host_fmt[j] receives the format; host_gamma[2j], [2j+1] the K and V gamma
  * of ternary pages (NaN otherwise).  Pages must be allocated.
@@ -281,12 +292,12 @@ VK_API vk_status vk_read_pages(vk_cache* c, int32_t layer, int32_t seq, int32_t 
 
 typedef struct vk_stats {
   int64_t device_bytes;             /* all device memory owned by the handle              */
-  int64_t pool_pages[3];            /* capacity per layer, by format                      */
-  int64_t pages_used[3];            /* allocated pages per layer, by format               */
-  int64_t tokens_stored[3];         /* tokens held, by format (per layer)                 */
+  int64_t pool_pages[4];            /* capacity per layer, by format (VK_FMT_*)           */
+  int64_t pages_used[4];            /* allocated pages per layer, by format               */
+  int64_t tokens_stored[4];         /* tokens held, by format (per layer)                 */
   int64_t append_calls, decode_calls;
-  int64_t last_decode_units[3];     /* 16-token units read by the last decode, by format  */
-  int64_t total_decode_units[3];    /* route counters over the handle's life              */
+  int64_t last_decode_units[4];     /* 16-token units read by the last decode, by format  */
+  int64_t total_decode_units[4];    /* route counters over the handle's life              */
   int32_t last_decode_splits;       /* split-K factor the last decode used                */
   int32_t last_decode_steal;        /* 1 if its matrix-core launches used stealing blocks */
   int64_t retier_calls;             /* vk_retier calls                                    */

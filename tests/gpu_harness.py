@@ -45,7 +45,7 @@ def seq_calls(w: wl.Workload, seq: int):
 def pages_needed(w: wl.Workload) -> List[int]:
     """Pages per format per layer that the append schedule takes (plus slack)."""
     spec = spec_of(w)
-    need = [0, 0, 0]
+    need = [0, 0, 0, 0]
     for s in range(w.n_seqs):
         length = 0
         for t0, n in seq_calls(w, s):
@@ -63,7 +63,7 @@ def make_cache(w: wl.Workload, shuffle=None, eps=1e-5, fp8_scale=1.0, slack_page
                          max_tokens_per_seq=max_tokens or w.max_len, sink_tokens=w.sink_tokens, sink_format=w.sink_format,
                          recent_tokens=w.recent_tokens, recent_format=w.recent_format,
                          pages_ternary=need[0] + slack_pages[0], pages_fp8=need[1] + slack_pages[1],
-                         pages_f16=need[2] + slack_pages[2], eps=eps, fp8_scale=fp8_scale,
+                         pages_f16=need[2] + slack_pages[2], pages_lossless=need[3], eps=eps, fp8_scale=fp8_scale,
                          page_shuffle_seed=w.page_shuffle_seed if shuffle is None else shuffle,
                          decode_kernel=decode_kernel, fp8_dynamic=int(fp8_dynamic))
     return vk.Cache(cfg)
@@ -129,7 +129,9 @@ def check_pages(cache: vk.Cache, w: wl.Workload, layer: int, seq: int, kbits, vb
         nb = oc.page_bytes(spec, fmt)
         got = buf[:nb]
         lo, hi = p * bs, min((p + 1) * bs, enc.length)
-        if fmt == oc.TERNARY2 and (hi - lo == bs or bs == 16):
+        if fmt == oc.LOSSLESS:
+            compare_lossless_page(got, oc.page_tiles(spec, enc_dev, p), spec, hi - lo, (layer, seq, p))
+        elif fmt == oc.TERNARY2 and (hi - lo == bs or bs == 16):
             want = oc.page_tiles(spec, enc_dev, p)
             if not np.array_equal(got, want):
                 bad = np.nonzero(got != want)[0]
@@ -140,9 +142,33 @@ def check_pages(cache: vk.Cache, w: wl.Workload, layer: int, seq: int, kbits, vb
     return enc
 
 
+def compare_lossless_page(got, want, spec, n_tok, where):
+    """Bytes of a lossless page against the oracle's, group by group: the header and the bytes the
+    group uses (coded: the two streams and its exceptions; raw: the values).  Groups of units past
+    the sequence's end are never written, and neither is the unused end of a slot."""
+    slot = 32 * spec.head_dim + 16
+    units = spec.block_size // 16
+    for g in range(2 * spec.n_kv_heads * units):
+        if (g % units) * 16 >= n_tok:
+            continue
+        w = want[g * slot:(g + 1) * slot]
+        used = 16 + (32 * spec.head_dim if w[1] == 1 else 24 * spec.head_dim + int(w[4:8].view("<u4")[0]))
+        a = got[g * slot:g * slot + used]
+        if not np.array_equal(a, w[:used]):
+            bad = np.nonzero(a != w[:used])[0]
+            raise AssertionError(f"lossless page bytes differ at {where}, group {g}: first bad byte {bad[0]} "
+                                 f"of {used} ({bad.size} bad)")
+
+
 def check_partial_page(spec, enc, p, got, fmt, n_tok):
     """Per-token comparison for a page whose tail was never written."""
     bs, hkv, dim = spec.block_size, spec.n_kv_heads, spec.head_dim
+    if fmt == oc.LOSSLESS:
+        got_all = pc.decode_pages(got[None], np.array([fmt]), n_tok, hkv, dim, bs)
+        for which in ("k", "v"):
+            want = getattr(enc, which + "_lossless")[p * bs:p * bs + n_tok]
+            assert np.array_equal(got_all[which + "_lossless"], want), (p, which, fmt)
+        return
     tb = {oc.TERNARY2: bs * dim // 4, oc.FP8E4M3: bs * dim, oc.F16: bs * dim * 2}[fmt]
     stride = tb + (4 * bs if fmt == oc.FP8E4M3 and spec.fp8_dynamic else 0)   # + token scales
     lo = p * bs
@@ -226,7 +252,7 @@ def check_sequence(w: wl.Workload, spec: oc.CacheSpec, seq: int, kbits, vbits, p
                     override |= bool(np.any(g[0] != want[sel[0]]))
         ref = enc if not override else oc.encode_sequence(spec, kbits, vbits, w.dtype, calls, gamma_override=dev_gamma)
         got = pc.decode_pages(buf, fmts, enc.length, w.n_kv_heads, w.head_dim, bs, spec.fp8_dynamic)
-        for name in ("k_code", "v_code", "k_fp8", "v_fp8", "k_f16", "v_f16"):
+        for name in ("k_code", "v_code", "k_fp8", "v_fp8", "k_f16", "v_f16", "k_lossless", "v_lossless"):
             if not np.array_equal(got[name], getattr(ref, name)):
                 bad = np.argwhere(got[name] != getattr(ref, name))
                 raise AssertionError(f"seq {seq}: {name} differs at {bad.shape[0]} places, first (token, head, dim) "

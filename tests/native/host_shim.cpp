@@ -40,7 +40,7 @@ int hs_append(void* h, int n_seqs, const int* ids, int n_tokens, int* tern_range
     tern_ranges[2 * i] = plan.seqs[i].tern_lo;
     tern_ranges[2 * i + 1] = plan.seqs[i].tern_hi;
   }
-  for (int f = 0; f < 3; ++f) new_pages[f] = plan.new_pages[f];
+  for (int f = 0; f < 3; ++f) new_pages[f] = plan.new_pages[f];   // (the tests use three formats)
   return 0;
 }
 
@@ -90,7 +90,7 @@ long long hs_free_pages(void* h, int fmt) { return static_cast<vk::HostState*>(h
 long long hs_tokens_stored(void* h, int fmt) { return static_cast<vk::HostState*>(h)->tokens_stored(fmt); }
 
 void hs_count_units(void* h, int seq, int window, long long* out3) {
-  int64_t o[3] = {0, 0, 0};
+  int64_t o[vk::kFormats] = {};
   static_cast<vk::HostState*>(h)->count_units(seq, window, o);
   for (int f = 0; f < 3; ++f) out3[f] = o[f];
 }

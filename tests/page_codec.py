@@ -22,6 +22,16 @@ Layouts (one page: [K tile of head 0..Hkv-1][V tile of head 0..Hkv-1]):
     dimension at 2j inside the byte;
   * fp8 / fp16 tiles: keys [Bs][D], values [D][Bs]; dynamic FP8 tiles end
     with Bs float32 token scales.
+  * lossless tiles: per 16-token unit a slot of 32 D + 16 bytes: a 16-byte
+    header (byte 0 the exponent centre c, byte 1 the mode, bytes 4..7 the
+    exception count), then either (mode 1) the raw bfloat16 values or
+    (mode 0) one sign+mantissa byte per value, 4-bit exponent codes two per
+    byte (value e - c + 11, 15 = look the exponent up in the exception list)
+    and the exception list, values in the stored order (keys [16][D], values
+    [D][16]); the exception list runs over decode lanes in order and, within
+    a lane, over its positions: keys of dim d, token t sit in lane
+    (d // (D/4)) * 16 + t at position d % (D/4); values in lane
+    (t // 4) * 16 + d % 16 at position (d // 16) * 4 + t % 4.
 """
 from __future__ import annotations
 
@@ -29,7 +39,7 @@ from typing import Dict
 
 import numpy as np
 
-TERNARY2, FP8E4M3, F16 = 0, 1, 2
+TERNARY2, FP8E4M3, F16, LOSSLESS = 0, 1, 2, 3
 
 
 def value_bit(r: int, j: int, dim: int) -> int:
@@ -74,6 +84,41 @@ def value_codes(tiles: np.ndarray, bs: int, dim: int) -> np.ndarray:
     return _fields_to_codes(u)
 
 
+def lossless_group_bits(slot: np.ndarray, dim: int, keys: bool) -> np.ndarray:
+    """One lossless slot -> its bfloat16 bits [16][D] (token, dimension)."""
+    slot = np.asarray(slot, dtype=np.uint8)
+    c, mode = int(slot[0]), int(slot[1])
+    body = slot[16:]
+    if mode == 1:
+        v = body[:32 * dim].view("<u2").astype(np.uint16)
+        return v.reshape(16, dim) if keys else v.reshape(dim, 16).T
+    if mode != 0:
+        raise ValueError("unknown lossless mode")
+    n_exc = int(slot[4:8].view("<u4")[0])
+    sm = body[:16 * dim]
+    nib = body[16 * dim:24 * dim]
+    cd = np.empty(16 * dim, dtype=np.int64)
+    cd[0::2] = nib & 0xF
+    cd[1::2] = nib >> 4
+    to_td = (lambda a: a.reshape(16, dim)) if keys else (lambda a: a.reshape(dim, 16).T)
+    sm, cd = to_td(sm), to_td(cd)
+    exp = cd + c - 11
+    t, d = np.meshgrid(np.arange(16), np.arange(dim), indexing="ij")
+    if keys:
+        lane, pos = (d // (dim // 4)) * 16 + t, d % (dim // 4)
+    else:
+        lane, pos = (t // 4) * 16 + d % 16, (d // 16) * 4 + t % 4
+    esc = cd == 15
+    if int(esc.sum()) != n_exc:
+        raise ValueError("exception count does not match the escape codes")
+    order = np.lexsort((pos[esc], lane[esc]))
+    e_idx = np.argwhere(esc)[order]
+    exp[e_idx[:, 0], e_idx[:, 1]] = body[24 * dim:24 * dim + n_exc]
+    if np.any((exp < 0) | (exp > 255)):
+        raise ValueError("exponent out of range")
+    return (((sm.astype(np.uint32) & 0x80) << 8) | (exp.astype(np.uint32) << 7) | (sm.astype(np.uint32) & 0x7F)).astype(np.uint16)
+
+
 def decode_pages(buf: np.ndarray, fmts: np.ndarray, length: int, n_kv_heads: int, head_dim: int,
                  block_size: int, fp8_dynamic: bool = False, chunk: int = 512) -> Dict[str, np.ndarray]:
     """Per-token contents of every page of one (layer, sequence).
@@ -92,9 +137,19 @@ def decode_pages(buf: np.ndarray, fmts: np.ndarray, length: int, n_kv_heads: int
         "k_fp8": np.zeros((T, hkv, dim), np.uint8), "v_fp8": np.zeros((T, hkv, dim), np.uint8),
         "k_f16": np.zeros((T, hkv, dim), np.uint16), "v_f16": np.zeros((T, hkv, dim), np.uint16),
         "k_fp8_scale": np.zeros((T, hkv), np.float32), "v_fp8_scale": np.zeros((T, hkv), np.float32),
+        "k_lossless": np.zeros((T, hkv, dim), np.uint16), "v_lossless": np.zeros((T, hkv, dim), np.uint16),
     }
     by_page = {k: a.reshape((n_pages, bs) + a.shape[1:]) for k, a in out.items()}
     fmts = np.asarray(fmts)
+    slot = 32 * dim + 16
+    for p in np.nonzero(fmts == LOSSLESS)[0]:
+        tb = (bs // 16) * slot
+        for w, which in ((0, "k"), (1, "v")):
+            for h in range(hkv):
+                base = (w * hkv + h) * tb
+                for u in range(bs // 16):
+                    g = lossless_group_bits(buf[p, base + u * slot:base + (u + 1) * slot], dim, which == "k")
+                    by_page[which + "_lossless"][p, 16 * u:16 * u + 16, h] = g
     for f in (TERNARY2, FP8E4M3, F16):
         idx_all = np.nonzero(fmts == f)[0]
         for c0 in range(0, idx_all.size, chunk):

@@ -470,3 +470,92 @@ def test_dynamic_fp8_mixed_tiers_with_extreme_rows(kernel):
         err = check_decode(out, q, w, encs, W)
         say(f"dynamic fp8 window {W}: max err {err:.2e}")
     cache.close()
+
+
+# ------------------------------------------------------ lossless tier ---
+
+@pytest.mark.parametrize("dim", [128, 64])
+@pytest.mark.parametrize("arrangement", ["sorted", "strided", "shuffled"])
+def test_lossless_route_every_bf16_pattern(dim, arrangement):
+    """Every bfloat16 pattern (infinities and NaNs included) through the lossless page route, keys and
+    values: page bytes equal the oracle's (centre, codes, exception order; coded and raw groups)
+    and read back to the input bits."""
+    n_tok = 65536 // dim
+    w = wl.small_workload(n_kv_heads=1, n_q_heads=1, head_dim=dim, dtype=1, block_size=16, sink_tokens=n_tok,
+                          sink_format=oc.LOSSLESS, lengths=(n_tok,))
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    if arrangement == "strided":
+        bits = bits.reshape(16 * dim, -1).T.ravel().copy()
+    elif arrangement == "shuffled":
+        bits = np.random.default_rng(9).permutation(bits)
+    kb = bits.reshape(n_tok, 1, dim)
+    vb = np.ascontiguousarray(bits[::-1]).reshape(n_tok, 1, dim)
+    cache = make_cache(w)
+    k = to_dev(kb.ravel(), 1).view(1, 1, n_tok, 1, dim)
+    v = to_dev(vb.ravel(), 1).view(1, 1, n_tok, 1, dim)
+    cache.append(k, v, [0])
+    enc = check_pages(cache, w, 0, 0, kb, vb, pages=list(range(n_tok // 16)))
+    assert set(enc.page_format) == {oc.LOSSLESS}
+    buf, fmt, _ = cache.read_pages(0, 0, 0, n_tok // 16)
+    modes = {int(buf[p, 1]) for p in range(n_tok // 16)}
+    assert modes == ({0} if arrangement == "sorted" else ({1} if arrangement == "strided" else modes))
+    cache.close()
+
+
+LOSSLESS_CASES = [
+    ("anchor-d128-g4", dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.LOSSLESS,
+                            lengths=(700, 31, 250, 1), batch_appends=False), [-1, 60, 0]),
+    ("anchor-recent-d64-g8", dict(n_q_heads=16, n_kv_heads=2, head_dim=64, dtype=1, sink_tokens=40,
+                                  sink_format=oc.LOSSLESS, recent_tokens=48, recent_format=oc.LOSSLESS,
+                                  block_size=32, lengths=(400, 90), batch_appends=False), [-1, 100]),
+    ("anchor-lossless-recent-fp8-g2", dict(n_q_heads=4, n_kv_heads=2, head_dim=128, dtype=1, sink_format=oc.LOSSLESS,
+                                           recent_tokens=64, recent_format=oc.FP8E4M3, lengths=(1000, 300),
+                                           batch_appends=False), [-1, 200]),
+    ("outliers-and-zeros", dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=1, sink_tokens=64,
+                                sink_format=oc.LOSSLESS, lengths=(500,), outlier_frac=0.2), [-1, 30]),
+]
+
+
+@pytest.mark.parametrize("dyn", [0, 1], ids=["static-fp8", "dynamic-fp8"])
+@pytest.mark.parametrize("name,kw,windows", LOSSLESS_CASES, ids=[c[0] for c in LOSSLESS_CASES])
+def test_lossless_tier_pages_and_decode(name, kw, windows, dyn):
+    """Lossless anchor (and recent) pages beside ternary and fp8 pages: every page against the
+    oracle, decode against the oracle's float64 attention over the exact bfloat16 values."""
+    w = wl.small_workload(**kw)
+    cache = make_cache(w, fp8_dynamic=dyn)
+    fill(cache, w)
+    encs = {}
+    for s in range(w.n_seqs):
+        kb, vb = host_kv(w, 0, s)
+        encs[s] = check_pages(cache, w, 0, s, kb, vb, pages=list(range(-(-w.lengths[s] // w.block_size))),
+                              fp8_dynamic=dyn)
+    assert cache.stats()["pages_used"][oc.LOSSLESS] > 0
+    q = wl.queries(w, 0, device="cuda")
+    for W in windows:
+        out = cache.decode(q, list(range(w.n_seqs)), 0, window=W)
+        torch.cuda.synchronize()
+        err = check_decode(out, q, w, encs, W)
+        assert cache.stats()["last_decode_units"][oc.LOSSLESS] > 0
+        say(f"lossless {name} window {W}: max err {err:.2e}")
+    cache.close()
+
+
+def test_lossless_tier_errors():
+    """float16 input into lossless pages, the vector-ALU kernel with lossless pages and an append
+    into a partly filled lossless page are refused; the cache stays usable."""
+    w = wl.small_workload(n_q_heads=4, n_kv_heads=2, head_dim=64, dtype=1, block_size=32, sink_tokens=32,
+                          sink_format=oc.LOSSLESS, lengths=(64,))
+    with pytest.raises(vk.VkError) as e:
+        make_cache(w, decode_kernel=1)
+    assert e.value.status == vk.ERR_ARG
+    cache = make_cache(w)
+    k16 = torch.zeros((1, 1, 20, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(vk.VkError) as e:
+        cache.append(k16, k16, [0])
+    assert e.value.status == vk.ERR_ARG and cache.seq_length(0) == 0
+    kb = torch.randn((1, 1, 20, 2, 64), device="cuda").to(torch.bfloat16)
+    cache.append(kb, kb, [0])
+    with pytest.raises(vk.VkError) as e:
+        cache.append(kb, kb, [0])
+    assert e.value.status == vk.ERR_ALIGN and cache.seq_length(0) == 20
+    cache.close()

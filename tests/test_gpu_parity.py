@@ -6,6 +6,8 @@ oracle: every page's stored codes, fp8 bytes and fp16 values bit-exactly (and
 every ternary page's gamma within 2^-22), and every sequence's decode output
 within max-abs 2e-3 of the float64 oracle.
 """
+import dataclasses
+
 import pytest
 import torch
 
@@ -34,7 +36,7 @@ def test_workload1_tiny(kernel):
     w = wl.workload(1)
     r = run_workload(w, page_layers=[0], decode_layers=[0], decode_kernel=kernel)
     check_all(w, r, [0], [0])
-    assert r["stats"]["last_decode_units"] == [17, 0, 0]   # units holding tokens 0..3 and 256..511
+    assert r["stats"]["last_decode_units"] == [17, 0, 0, 0]   # units holding tokens 0..3 and 256..511
     say(f"workload 1: {r}")
 
 
@@ -44,7 +46,7 @@ def test_workload2_qwen_shaped_36_layers(kernel):
     layers = list(range(36))
     r = run_workload(w, page_layers=layers, decode_layers=layers, decode_kernel=kernel)
     check_all(w, r, layers, layers)
-    assert r["stats"]["pages_used"] == [256, 0, 0]
+    assert r["stats"]["pages_used"] == [256, 0, 0, 0]
     say(f"workload 2: max err {r['max_err']:.3e}")
 
 
@@ -75,6 +77,17 @@ def test_workload4_dynamic_fp8(kernel):
     check_all(w, r, [0], [0])
     assert r["stats"]["last_decode_units"][1] > 0
     say(f"workload 4 dynamic fp8: max err {r['max_err']:.3e}")
+
+
+def test_workload4_lossless_anchor_tier():
+    """Workload 4 with its sink pages in the lossless bfloat16 tier instead of fp16 (matrix-core
+    decode: the vector-ALU kernel does not read lossless pages)."""
+    w = dataclasses.replace(wl.workload(4), sink_format=wl.FMT_LOSSLESS)
+    r = run_workload(w, page_layers=[0], decode_layers=[0], decode_kernel=2)
+    check_all(w, r, [0], [0])
+    units = r["stats"]["last_decode_units"]
+    assert units[wl.FMT_LOSSLESS] == 64 and units[wl.FMT_F16] == 0 and units[wl.FMT_FP8E4M3] > 0
+    say(f"workload 4 lossless anchors: max err {r['max_err']:.3e} units {units}")
 
 
 @KERNELS

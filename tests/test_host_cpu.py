@@ -59,7 +59,8 @@ def test_config_defaults():
 @pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_q_heads=12), dict(n_q_heads=2, n_kv_heads=4),
                                  dict(n_q_heads=48, n_kv_heads=2), dict(head_dim=96), dict(block_size=24),
                                  dict(block_size=8), dict(max_seqs=0), dict(sink_tokens=-1),
-                                 dict(sink_format=3), dict(pages_fp8=-1), dict(eps=-1.0),
+                                 dict(sink_format=4), dict(pages_fp8=-1), dict(pages_lossless=-1),
+                                 dict(decode_kernel=1, sink_format=3), dict(eps=-1.0),
                                  dict(fp8_scale=0.0), dict(decode_kernel=3), dict(eps=float("nan"))])
 def test_config_rejected(bad):
     with pytest.raises(vk.VkError) as e:
@@ -72,6 +73,9 @@ def test_sizes():
     assert vk.page_bytes(c, vk.FMT_TERNARY2) == 2 * 2 * 16 * 128 // 4
     assert vk.page_bytes(c, vk.FMT_FP8E4M3) == 2 * 2 * 16 * 128
     assert vk.page_bytes(c, vk.FMT_F16) == 2 * 2 * 16 * 128 * 2
+    assert vk.page_bytes(c, vk.FMT_LOSSLESS) == 2 * 2 * (32 * 128 + 16)      # one 16-token group per tile
+    assert vk.page_bytes(base_cfg(block_size=64, head_dim=64), vk.FMT_LOSSLESS) == 2 * 2 * 4 * (32 * 64 + 16)
+    assert vk.page_bytes(c, 4) == 0
     total = vk.device_bytes(c)
     pools = 2 * (100 * 2048 + 10 * 8192 + 5 * 16384)
     assert total >= pools + 2 * 100 * 8 + 4 * 64 * 4

@@ -46,6 +46,36 @@ def test_reserved_field_is_rejected():
         pc.value_codes(np.full(16 * 16, 0xC0, np.uint8), 16, 64)
 
 
+@pytest.mark.parametrize("dim,bs", [(64, 32), (128, 16)])
+def test_lossless_pages_decode_to_the_oracle_bits(dim, bs):
+    """Lossless sink and recent pages (coded groups, a raw group, zero padding past the end)
+    read back to the input bits, as the oracle encoded them."""
+    spec = oc.CacheSpec(n_kv_heads=2, head_dim=dim, block_size=bs, sink_tokens=20, sink_format=oc.LOSSLESS,
+                        recent_tokens=24, recent_format=oc.LOSSLESS)
+    rng = np.random.default_rng(dim + bs)
+    T = 16 * 7 + 3
+    x = rng.standard_normal((2, T, 2, dim)).astype(np.float32)
+    x[0, 0:16, 1] *= np.where(rng.random((16, dim)) < 0.6, 1e30, 1e-30)   # a group of escapes: raw
+    x[1, 3, 0, 5] = 0.0
+    bits = ((x.view(np.uint32) + 0x7FFF + ((x.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    kb, vb = bits[0], bits[1]
+    enc = oc.encode_sequence(spec, kb, vb, ot.BF16, [(0, T)])
+    assert oc.LOSSLESS in enc.page_format and oc.TERNARY2 in enc.page_format
+    n_pages = len(enc.page_format)
+    stride = oc.page_bytes(spec, oc.LOSSLESS)
+    buf = np.zeros((n_pages, stride), np.uint8)
+    for p in range(n_pages):
+        t = oc.page_tiles(spec, enc, p)
+        buf[p, :t.size] = t
+    got = pc.decode_pages(buf, np.array(enc.page_format), T, 2, dim, bs)
+    for name in ("k_lossless", "v_lossless", "k_code", "v_code"):
+        assert np.array_equal(got[name], getattr(enc, name)), name
+    ls = enc.token_format == oc.LOSSLESS
+    assert np.array_equal(got["k_lossless"][ls], kb[ls]) and np.array_equal(got["v_lossless"][ls], vb[ls])
+    # the group of head 1's keys in unit 0 holds escapes beyond its exception room: raw
+    assert buf[0, (32 * dim + 16) * (bs // 16) + 1] == 1
+
+
 @pytest.mark.parametrize("dynamic", [False, True])
 def test_decode_pages_matches_oracle_encoding(dynamic):
     """A mixed-format sequence encoded by the oracle, laid out as the device reads it back,
