@@ -45,7 +45,15 @@ constexpr int kDecodeMinUnitsPerWave = 8;  // matrix-core kernel: units per wave
 constexpr int kDecodeUnitsPerStep = 4;     // matrix-core kernel: units per clean step, at most (a wave's
                                            // range is a whole number of them when the split size is)
 constexpr int64_t kDecodeScratchItems = 16384;  // (seq, q-head group, split) partial slots
-constexpr int64_t kDecodeTargetBlocks = 1024;   // matrix-core decode blocks per launch (one round of 4 per CU)
+// matrix-core decode blocks per compute unit a launch aims for (3 four-wave blocks fit one at
+// the kernel's 3 waves per SIMD; 2 larger ones measured faster than 3 or 4 on 128K-token
+// contexts, where each wave's set-up is a larger share of its work, and no slower on 32K ones).
+// VK_DECODE_BLOCKS_PER_CU=1..8 overrides.
+int decode_blocks_per_cu() {
+  const char* e = std::getenv("VK_DECODE_BLOCKS_PER_CU");
+  const int v = e ? std::atoi(e) : 0;
+  return v >= 1 && v <= 8 ? v : 2;
+}
 constexpr int kDecodeMixedParts = 1;  // matrix-core kernel: blocks per (sequence, KV head) for fp8 / fp16 pages
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
   const char* e = std::getenv("VK_DECODE_UPI");
@@ -646,7 +654,8 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     // Splits hold a fixed number of units, so long sequences get more of them than short
     // ones (a block past a sequence's units writes an empty part).
     const int64_t all_units = (cu[0] + cu[1] + cu[2]) * cfg.n_kv_heads;
-    const vk::SplitPlan sp = mfma ? vk::plan_splits(all_units, max_units, kDecodeTargetBlocks,
+    const int32_t target_blocks = static_cast<int32_t>(std::max(1, c->n_cu) * decode_blocks_per_cu());
+    const vk::SplitPlan sp = mfma ? vk::plan_splits(all_units, max_units, target_blocks,
                                                     std::max(1, max_splits), 4 * kDecodeMinUnitsPerWave,
                                                     4 * kDecodeUnitsPerStep)
                                   : vk::plan_splits(all_units, max_units, kDecodeTargetGroups,

@@ -66,10 +66,12 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
 
 // Exponent shift sh for a largest magnitude qmax (clamped to [-126, 126], where 2^sh and 2^-sh
 // are normal floats; 0 for qmax = 0).
+// TOP: the exponent the largest magnitude is brought to (14 for f16 operands).
+template <int TOP = 14>
 __device__ __forceinline__ int q_shift(float qmax) {
   if (!(qmax > 0.0f)) return 0;
   const int e = static_cast<int>((__float_as_uint(qmax) >> 23) & 0xFFu) - 127;  // floor(log2 qmax) for normals
-  const int sh = 14 - e;
+  const int sh = TOP - e;
   return sh < -126 ? -126 : (sh > 126 ? 126 : sh);
 }
 __device__ __forceinline__ float pow2i(int k) { return __uint_as_float(static_cast<uint32_t>(k + 127) << 23); }
@@ -421,6 +423,15 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 // sum_d (off_d + 2^-14) q_d, and sum_t p_t (u_t - 1) from the P*V product and
 // sum_t p_t (off_j + 2^-14) per 16-dimension block j.
 //
+// Head dim 128 scores ternary keys with one fp4 x fp8 product per unit and query term
+// (v_mfma_scale_f32_16x16x128_f8f6f4): a 2-bit field u with two zero bits above it is the
+// e2m1 value u / 2, so a key code word becomes two fp4 operand words with an AND and a
+// shift-AND.  A bfloat16 query, scaled so its largest magnitude lies in [2^6, 2^7), is held
+// as the sum of two e4m3 terms, the second stored at 2^4 its value and weighted 2^-4 by the
+// product's scale operand: each term takes four significant bits, so the two hold every
+// element exactly down to 2^-10 of the largest (smaller ones to within 2^-13 of it).  Then
+// sum_d q_d (u_d - 1) = 2 acc - sum_d q_d, with q the sum of the terms.
+//
 // Four waves share one (sequence, KV head, split): each walks a quarter of the
 // split's units.  A unit's key and value tiles of the head (8 D bytes) are copied
 // into the wave's LDS ring by one buffer-to-LDS load, NR units ahead; the page
@@ -434,6 +445,7 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMfmaWaves = 4;
 constexpr int kStealWaves = 12;  // a whole CU at 3 waves per SIMD
@@ -570,6 +582,11 @@ void k_decode_mfma(DecodeArgs a) {
   constexpr int NB = D / 16;   // 16-dimension output blocks
   constexpr int CH = 64;       // units per metadata chunk (one per lane)
   constexpr int UG = 2;        // units sharing one online-softmax update and one P*V product
+  // ternary scores on the fp4 x fp8 product: head dim 128, bfloat16 queries (two e4m3 terms
+  // hold one exactly; f16 queries would need a third term's registers and keep the f16 product)
+  constexpr bool F4 = D == 128 && QDT == 1;
+  constexpr int NQ = 2;  // e4m3 terms of the query
+  constexpr float KMUL = F4 ? 2.0f : 16384.0f;  // ternary logit = ks (KMUL acc - qoff)
   static_assert(G <= 16, "one query head per lane column");
   // Column slots: the query heads are repeated over the 16 columns of the score product, in
   // NSL slots of W columns.  A clean step puts one unit's scores in each slot, so its softmax
@@ -775,6 +792,65 @@ void k_decode_mfma(DecodeArgs a) {
     qsum = sum;
     qoff = 16384.0f * koff + sum;  // logit = ks (2^14 acc - qoff) for offset-form codes
   };
+  // The query as NQ e4m3 terms, the B operands of the fp4 x fp8 score product (head dim 128,
+  // ternary blocks).  The product pairs nibble n of word v of an A lane of group g (key
+  // dimension 32 g + 16 (v / 2) + 2 n + v % 2, from tern_score) with byte 16 (g / 2) + 8 (v % 2)
+  // + n of a B lane of group 2 (g % 2) + v / 2; so B lane group g holds, in bytes jb and
+  // 16 + jb (jb < 16), dimensions 16 g + e(jb) and 64 + 16 g + e(jb), e(jb) = 2 (jb % 8) + jb / 8.
+  v8i_t qf[NQ];
+  auto make_qf = [&]() {
+    asm volatile("" ::: "memory");  // (as in make_qb)
+    uint32_t x[2][8];
+    float qmax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint16_t* qrow = qhead + 64 * c + 16 * grp;
+      const uint4 lo = reinterpret_cast<const uint4*>(qrow)[0];  // dims +0 .. +7
+      const uint4 hi = reinterpret_cast<const uint4*>(qrow)[1];  // dims +8 .. +15
+      const uint32_t all[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[c][i] = all[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        qmax = fmaxf(qmax, fabsf(q_value<QDT>(static_cast<uint16_t>((all[i >> 1] >> (16 * (i & 1))) & 0xFFFFu))));
+    }
+    const int qsh = __builtin_amdgcn_readfirstlane(q_shift<6>(wave_max(qmax)));
+    const float qmul = pow2i(qsh);
+    qsl = a.scale_log2 * pow2i(-qsh);
+    uint32_t w[NQ][8];
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[t][i] = 0u;
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int c = j >> 4, i = 2 * (j & 7) + ((j >> 3) & 1);  // dimension 64 c + 16 grp + i
+      float r = q_value<QDT>(static_cast<uint16_t>((x[c][i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) * qmul;
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        const int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(r * pow2i(4 * t), 0.0f, 0, false) & 0xFF;
+        const float back = __builtin_amdgcn_cvt_f32_fp8(e8, 0) * pow2i(-4 * t);  // the term's value
+        r -= back;
+        sum += back;
+        w[t][j >> 2] |= static_cast<uint32_t>(e8) << (8 * (j & 3));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+      qf[t] = v8i_t{static_cast<int>(w[t][0]), static_cast<int>(w[t][1]), static_cast<int>(w[t][2]),
+                    static_cast<int>(w[t][3]), static_cast<int>(w[t][4]), static_cast<int>(w[t][5]),
+                    static_cast<int>(w[t][6]), static_cast<int>(w[t][7])};
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    qsum = sum;
+    qoff = sum;  // logit = ks (2 acc - qoff)
+  };
+  // query operands of the ternary blocks
+  auto make_qt = [&]() {
+    if constexpr (F4) make_qf();
+    else make_qb();
+  };
 
   f4_t oacc[NB];
 #pragma unroll
@@ -784,6 +860,24 @@ void k_decode_mfma(DecodeArgs a) {
   float m = -INFINITY, lsum = 0.0f, tsum = 0.0f, vcur = 0.0f;
   const h2_t ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
   const OConst oc = oconst();
+  // raw score accumulator of one ternary unit (logit = ks (KMUL acc - qoff))
+  auto tern_score = [&](const uint32_t (&k)[NC]) -> f4_t {
+    f4_t s4 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (F4) {
+      constexpr uint32_t M = 0x33333333u;  // the even 2-bit fields, one per nibble
+      const v8i_t ak = {static_cast<int>(k[0] & M), static_cast<int>((k[0] >> 2) & M),
+                        static_cast<int>(k[NC - 1] & M), static_cast<int>((k[NC - 1] >> 2) & M), 0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+        s4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ak, qf[t], s4, 4, 0, 0, 127, 0, 127 - 4 * t);
+    } else {
+      h8_t ka[NS];
+      ka_ternary<NS, NC>(k, ka, oc);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[st], qb[st], s4, 0, 0, 0);
+    }
+    return s4;
+  };
 
   // Starts the copy of logical unit lu's key and value tiles of this head into a ring row.
   // Always issued (a fixed number of loads per unit keeps the waits exact): other formats
@@ -848,18 +942,14 @@ void k_decode_mfma(DecodeArgs a) {
     constexpr int UT = NSL == 1 ? 1 : NSL;  // units per score tile
     constexpr int NT = SU / UT;             // score tiles
     const float ks = cc.gk0 * qsl;
-    const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
+    const float a0 = ks * KMUL, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
     float sc[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       f4_t tile;
 #pragma unroll
       for (int i = 0; i < UT; ++i) {
-        h8_t ka[NS];
-        ka_ternary<NS, NC>(r[t * UT + i].k, ka, oc);
-        f4_t s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < NS; ++st) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[st], qb[st], s4, 0, 0, 0);
+        const f4_t s4 = tern_score(r[t * UT + i].k);
         if (i == 0) {
           tile = s4;
         } else {
@@ -959,12 +1049,8 @@ void k_decode_mfma(DecodeArgs a) {
       const UnitRaw<NC, NV>& raw = g == 0 ? r0 : r1;
       const float ks = lane_f(cc.gk, k0 + g) * qsl;
       vs[g] = lane_f(cc.gv, k0 + g);
-      h8_t ka[NS];
-      ka_ternary<NS, NC>(raw.k, ka, oc);
-      f4_t s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < NS; ++st) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[st], qb[st], s4, 0, 0, 0);
-      const float a0 = ks * 16384.0f, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
+      const f4_t s4 = tern_score(raw.k);
+      const float a0 = ks * KMUL, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
       if (full) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
@@ -1419,7 +1505,7 @@ void k_decode_mfma(DecodeArgs a) {
       prologue(integral_constant<int, 6>{});
       prologue(integral_constant<int, 7>{});
     }
-    make_qb();
+    make_qt();
     chunk_flags(ch, u_begin);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // every copy has landed
     auto slot_row = [&](int i) -> const uint8_t* {  // ring row of slot i (wave-uniform)
@@ -1474,7 +1560,7 @@ void k_decode_mfma(DecodeArgs a) {
     }
     // (no next chunk: the copies never select it, and it stays a copy of the current one)
     Chunk ch_nxt = u_begin + CH < u_end ? load_chunk(u_begin + CH) : ch_cur;
-    make_qb();
+    make_qt();
     for (int c0 = u_begin; c0 < u_end; c0 += CH) {
       const int c_end = min(c0 + CH, u_end);
       chunk_flags(ch_cur, c0);
@@ -1570,7 +1656,7 @@ void k_decode_mfma(DecodeArgs a) {
       };
       prologue_copies(cs, refill);
       if (p_nxt < n_pieces) ch_nxt = load_chunk(ns);
-      make_qb();
+      make_qt();
       while (true) {
         chunk_flags(ch_cur, cs);
 #pragma unroll 1
