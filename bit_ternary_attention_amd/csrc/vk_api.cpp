@@ -37,7 +37,6 @@ constexpr int64_t kRingBytes = 64 << 20; // pinned bytes the slots may take toge
 constexpr int64_t kPackTargetBlocks = 32768;  // pack blocks per launch, at most
 constexpr int64_t kRetierTasksPerLaunch = 65536;  // pages one retier launch converts, at most
 constexpr int64_t kMaxPartials = 1 << 20;  // float64 absmean partials per append call
-constexpr int64_t kMaxSegs = 65535;        // (layer, seq, K|V) segments per append call (grid y)
 constexpr int kDecodeTargetGroups = 4096;  // work groups a decode launch aims for
 constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMinUnits = 4;         // 16-token units per split, at least (vector-ALU kernel)
@@ -142,7 +141,6 @@ struct vk_cache {
   bool poisoned = false;
   vk::PoolsView pools{};
   double* partials = nullptr;
-  vk::SegInfo* seg = nullptr;
   float* dec_partials = nullptr;
   int64_t plan_bytes = 0;
   int n_ring = kRingMin;  // staging slots in use (ring_slots of the config)
@@ -203,7 +201,6 @@ std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
   const int64_t max_pages = (cfg.max_tokens_per_seq + cfg.block_size - 1) / cfg.block_size;
   s.push_back(static_cast<int64_t>(cfg.max_seqs) * max_pages * 4);    // block table
   s.push_back(kMaxPartials * 8);                                      // absmean partials
-  s.push_back(kMaxSegs * static_cast<int64_t>(sizeof(vk::SegInfo)));  // segment info
   s.push_back(partial_count(cfg) * 4);                                // decode split partials
   const int rs = ring_slots(cfg);
   for (int r = 0; r < kRingMax; ++r) s.push_back(r < rs ? plan_bytes_for(cfg) : 0);  // staged plans
@@ -211,7 +208,7 @@ std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
   s.push_back(static_cast<int64_t>(cfg.n_layers) * cfg.pages_lossless * vk::page_bytes(cfg, VK_FMT_LOSSLESS));
   return s;
 }
-constexpr size_t kBufDummy = 8 + kRingMax, kBufLossless = 9 + kRingMax;  // indices in buffer_sizes
+constexpr size_t kBufDummy = 7 + kRingMax, kBufLossless = 8 + kRingMax;  // indices in buffer_sizes
 
 void free_all(vk_cache* c) {
   for (void* p : c->allocations) (void)hipFree(p);
@@ -325,13 +322,12 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   P.fp8_scale = cfg->fp8_scale;
   P.fp8_dynamic = cfg->fp8_dynamic;
   c->partials = static_cast<double*>(ptrs[5]);
-  c->seg = static_cast<vk::SegInfo*>(ptrs[6]);
-  c->dec_partials = static_cast<float*>(ptrs[7]);
+  c->dec_partials = static_cast<float*>(ptrs[6]);
   P.dummy_page = static_cast<const uint8_t*>(ptrs[kBufDummy]);
   c->plan_bytes = plan_bytes_for(*cfg);
   c->n_ring = ring_slots(*cfg);
   for (int r = 0; r < c->n_ring; ++r) {
-    c->plan_dev[r] = static_cast<uint8_t*>(ptrs[8 + r]);
+    c->plan_dev[r] = static_cast<uint8_t*>(ptrs[7 + r]);
     e = hipHostMalloc(reinterpret_cast<void**>(&c->plan_host[r]), static_cast<size_t>(c->plan_bytes), 0);
     if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_OOM, "hipHostMalloc: %s", hipGetErrorString(e)); }
     e = hipEventCreateWithFlags(&c->plan_ev[r], hipEventDisableTiming);
@@ -368,11 +364,10 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   if (st) return fail(st, "%s", err.c_str());
   if (plan.new_pages[VK_FMT_LOSSLESS] > 0 && dtype != VK_DTYPE_BF16)
     return fail(VK_ERR_ARG, "lossless pages hold bfloat16 input");
-  const int64_t n_seg = static_cast<int64_t>(n_layers) * n_seqs * 2;
   const int64_t row = static_cast<int64_t>(cfg.n_kv_heads) * cfg.head_dim;
-  if (n_seg > kMaxSegs || 2 * static_cast<int64_t>(n_layers) * plan.total_blk > kMaxPartials)
-    return fail(VK_ERR_ARG, "append too large for one call (%lld segments, %lld absmean blocks per layer); split it",
-                static_cast<long long>(n_seg), static_cast<long long>(plan.total_blk));
+  if (2 * static_cast<int64_t>(n_layers) * plan.total_blk > kMaxPartials)
+    return fail(VK_ERR_ARG, "append too large for one call (%lld absmean blocks per layer); split it",
+                static_cast<long long>(plan.total_blk));
   const int64_t total = static_cast<int64_t>(n_layers) * plan.total_tasks;
   // the 16-token units of lossless pages: (sequence index, unit) pairs for the pack kernel that
   // writes them
@@ -418,7 +413,6 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   a.descs = reinterpret_cast<const vk::AppendSeqDesc*>(c->plan_dev[slot]);
   a.entries = reinterpret_cast<const int32_t*>(c->plan_dev[slot] + desc_bytes);
   a.partials = c->partials;
-  a.seg = c->seg;
   a.dtype = dtype;
   a.layer_begin = layer_begin;
   a.n_layers = n_layers;
@@ -475,7 +469,7 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
     }
     c->timer.add_bytes(VK_KERNEL_PACK, in_bytes + layers * out_bytes);
   }
-  e = vk::launch_append(a, static_cast<int32_t>(n_seg), s, c->timer.on ? &c->timer : nullptr);
+  e = vk::launch_append(a, s, c->timer.on ? &c->timer : nullptr);
   if (e != hipSuccess) return hip_fail(c, e, "append kernels");
   e = hipEventRecord(c->plan_ev[slot], s);
   if (e != hipSuccess) return hip_fail(c, e, "hipEventRecord");

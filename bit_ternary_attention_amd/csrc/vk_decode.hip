@@ -429,7 +429,8 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 // shift-AND.  A bfloat16 query, scaled so its largest magnitude lies in [2^6, 2^7), is held
 // as the sum of two e4m3 terms, the second stored at 2^4 its value and weighted 2^-4 by the
 // product's scale operand: each term takes four significant bits, so the two hold every
-// element exactly down to 2^-10 of the largest (smaller ones to within 2^-13 of it).  Then
+// element of at least 2^-12 times the largest exactly (e4m3 steps reach 2^-9) and the smaller
+// ones to within 2^-20 times the largest.  Then
 // sum_d q_d (u_d - 1) = 2 acc - sum_d q_d, with q the sum of the terms.
 //
 // Four waves share one (sequence, KV head, split): each walks a quarter of the

@@ -48,7 +48,6 @@ struct AppendArgs {
   const AppendSeqDesc* descs;
   const int32_t* entries;
   double* partials;        // [n_layers][K|V][total_blk]
-  SegInfo* seg;            // [n_layers][n_seqs][K|V]
   int32_t dtype;           // 0 f16, 1 bf16
   int32_t layer_begin;
   int32_t n_layers;
@@ -136,7 +135,7 @@ class LaunchTimer {
 };
 
 // Launchers (vk_write.hip, vk_decode.hip, vk_retier.hip).  Return the first HIP error.
-hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, LaunchTimer* t);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s, LaunchTimer* t);
 hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_retier(const RetierArgs& a, hipStream_t s, LaunchTimer* t);

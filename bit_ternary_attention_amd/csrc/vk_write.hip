@@ -6,12 +6,13 @@
 // FP8 recent pages and FP16 anchor (sink) pages follow "Minima-KV"
 // (twodots.gr), section "Recent, Anchor and Stale".
 //
-// Three kernels per append call:
+// Two kernels per append call:
 //   k_absmean_partial  pass 1: fixed-partition float64 sums of |x|, one per
 //                      (segment, 32 KiB block), no atomics -> deterministic
-//   k_gamma_finalize   one wave per segment: fixed-order sum, gamma = fp32(S/N),
-//                      and the exact 16-bit magnitude threshold of a nonzero code
 //   k_pack             pass 2: one wave per (16-token unit, K|V, head) tile;
+//                      the segment's gamma = fp32(S/N) from a fixed-order sum of
+//                      its partials and the exact 16-bit magnitude threshold of a
+//                      nonzero code, derived by every wave that needs them;
 //                      codes from an integer compare against the threshold,
 //                      keys stored token-major, values rearranged through LDS
 //                      into per-unit chunks (one chunk per decode lane)
@@ -218,18 +219,16 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(AppendArgs a) {
   if (threadIdx.x == 0) a.partials[static_cast<int64_t>(blockIdx.y) * a.total_blk + x] = total;
 }
 
-// one wave per segment (layer, sequence, K|V): its partials are blocks [blk_off, blk_off + n)
-// of its (layer, K|V) row
+// gamma and threshold of a segment (layer, sequence, K|V), by one wave: its partials are blocks
+// [blk_off, blk_off + n) of its (layer, K|V) row.  Every pack wave that codes a tile of the
+// segment derives them itself, with the same fixed-order sum, so all agree bit for bit (the
+// partials of a call are a few KB, read from L2): no finalize launch between the two passes.
 template <int DT>
-__global__ __launch_bounds__(64) void k_gamma_finalize(AppendArgs a) {
-  const int seg = blockIdx.x;
-  const int kv = seg & 1, i = (seg >> 1) % a.n_seqs, l_rel = (seg >> 1) / a.n_seqs;
-  const AppendSeqDesc d = a.descs[i];
+__device__ __forceinline__ SegInfo segment_info(const AppendArgs& a, const AppendSeqDesc& d, int l_rel, int kv) {
   const int64_t n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * a.P.hkv * a.P.dim;
   const int n_blk = static_cast<int>((n + kAbsElemsPerBlock - 1) / kAbsElemsPerBlock);
   const double s = sum_partials_wave(a.partials + static_cast<int64_t>(l_rel * 2 + kv) * a.total_blk + d.blk_off, n_blk);
-  const SegInfo info = finalize_wave<DT>(s, n, a.eps);
-  if (threadIdx.x == 0) a.seg[seg] = info;
+  return finalize_wave<DT>(s, n, a.eps);
 }
 
 // ------------------------------------------------------------- pass 2 ---
@@ -263,6 +262,8 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   const int64_t g1 = MODE == 2 ? g0 + 1 : (g0 + a.tasks_per_blk < g_end ? g0 + a.tasks_per_blk : g_end);
   int i = -1, l_rel = -1, task_end = 0;
   AppendSeqDesc d{};
+  SegInfo seg_k{}, seg_v{};  // the current (layer, sequence)'s records, derived when first needed
+  bool have_k = false, have_v = false;
   for (int64_t g = g0; g < g1; ++g) {
     int h, kv, uk;
     if constexpr (MODE == 2) {
@@ -283,6 +284,7 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
         i = a.seq_tasks ? t / a.seq_tasks : find_seq<&AppendSeqDesc::task_off>(a.descs, a.n_seqs, t);
         d = a.descs[i];
         task_end = d.task_off + ((d.t0 + d.n_tokens + 15) / 16 - d.unit_first) * 2 * hkv;
+        have_k = have_v = false;
       }
       const int task = t - d.task_off;
       h = task % hkv;
@@ -319,7 +321,15 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
     }
 
     if (MODE != 2 && fmt == VK_FMT_TERNARY2) {
-      const SegInfo si = a.seg[(l_rel * a.n_seqs + i) * 2 + kv];
+      if (kv == 0 && !have_k) {
+        seg_k = segment_info<DT>(a, d, l_rel, 0);
+        have_k = true;
+      }
+      if (kv == 1 && !have_v) {
+        seg_v = segment_info<DT>(a, d, l_rel, 1);
+        have_v = true;
+      }
+      const SegInfo si = kv == 0 ? seg_k : seg_v;
       if (upi == 0 && h == 0 && lane == 0)
         a.P.gamma[(static_cast<int64_t>(layer) * a.P.cap[0] + idx) * 2 + kv] = si.gamma;
       if (kv == 0) {
@@ -662,7 +672,7 @@ __global__ __launch_bounds__(256) void k_flat_pack(QuantArgs a) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, LaunchTimer* t) {
+hipError_t launch_append(const AppendArgs& a, hipStream_t s, LaunchTimer* t) {
   const bool bf = a.dtype == VK_DTYPE_BF16;
   if (a.total_blk > 0) {
     const dim3 g1(a.total_blk, 2 * a.n_layers);
@@ -670,10 +680,6 @@ hipError_t launch_append(const AppendArgs& a, int32_t n_seg, hipStream_t s, Laun
     if (bf) k_absmean_partial<1><<<g1, kAbsThreads, 0, s>>>(a);
     else k_absmean_partial<0><<<g1, kAbsThreads, 0, s>>>(a);
     if (t) t->end(VK_KERNEL_ABSMEAN, s);
-    if (t) t->begin(VK_KERNEL_FINALIZE, s);
-    if (bf) k_gamma_finalize<1><<<n_seg, 64, 0, s>>>(a);
-    else k_gamma_finalize<0><<<n_seg, 64, 0, s>>>(a);
-    if (t) t->end(VK_KERNEL_FINALIZE, s);
   }
   const dim3 g2(a.pack_blocks);
   if (t) t->begin(VK_KERNEL_PACK, s);

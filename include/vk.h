@@ -197,8 +197,13 @@ VK_API vk_status vk_append_ragged(vk_cache* c, int32_t layer_begin, int32_t n_la
  *
  * q: device [n_seqs][n_q_heads][head_dim] of q_dtype, any finite values: the
  *    queries of one (sequence, KV head) are scaled by one power of two before
- *    the f16 products (largest magnitude in [2^14, 2^15)) and the scores by its
- *    inverse, so bf16 queries beyond the f16 range are taken exactly.
+ *    the products and the scores by its inverse, so bf16 queries beyond the f16
+ *    range are taken exactly.  f16 operands (the largest magnitude brought to
+ *    [2^14, 2^15)) for f16 queries, head_dim 64 and pages other than ternary;
+ *    ternary keys at head_dim 128 with bf16 queries meet the query as the sum of
+ *    two e4m3 terms (largest magnitude in [2^6, 2^7)), which hold every element
+ *    of at least 2^-12 times the largest exactly and the smaller ones to within
+ *    2^-20 times the largest.
  * out: device float32 [n_seqs][n_q_heads][head_dim].
  * Attended tokens of a sequence of length L: [0, min(sink_tokens, L)) and
  * [max(0, L - window), L); window = -1 attends the whole context (the
@@ -316,7 +321,8 @@ VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out);
  */
 enum {
   VK_KERNEL_ABSMEAN = 0,   /* write side pass 1: mean |x| partial sums        */
-  VK_KERNEL_FINALIZE = 1,  /* gamma and code threshold per segment            */
+  VK_KERNEL_FINALIZE = 1,  /* (unused: the pack kernel derives gamma and the   */
+                           /*  code threshold of each segment itself)         */
   VK_KERNEL_PACK = 2,      /* write side pass 2: quantise, pack, scatter      */
   VK_KERNEL_DECODE = 3,    /* paged decode attention (per split)              */
   VK_KERNEL_MERGE = 4,     /* split-K online-softmax merge                    */

@@ -503,3 +503,23 @@ def test_host_logic_under_sanitizers():
     tail = (r.stdout + r.stderr)[-3000:]
     assert r.returncode == 0, tail
     assert "passed" in r.stdout and "ERROR: AddressSanitizer" not in r.stderr and "runtime error" not in r.stderr, tail
+
+
+def test_two_e4m3_terms_hold_scaled_bfloat16_queries():
+    """The decode's fp4 x fp8 score product takes a bfloat16 query, scaled so its largest
+    magnitude lies in [2^6, 2^7), as t1 + t2 / 16 with t1 = e4m3(x) and t2 = e4m3(16 (x - t1))
+    (round to nearest even).  Every bfloat16 value of magnitude 2^-6 .. 2^7 is then held exactly
+    (so every element within 2^-12 of the largest), and smaller ones to within 2^-14."""
+    from oracle.fp8 import e4m3fn_decode, e4m3fn_encode
+    bits = np.arange(0x10000, dtype=np.uint32)
+    x32 = (bits << 16).view(np.float32)
+    x32 = x32[np.isfinite(x32)]
+    x = x32.astype(np.float64)
+    x = x[np.abs(x) < 2.0 ** 7]
+    t1 = e4m3fn_decode(e4m3fn_encode(x))
+    t2 = e4m3fn_decode(e4m3fn_encode(16.0 * (x - t1))) / 16.0
+    err = np.abs(x - t1 - t2)
+    big = np.abs(x) >= 2.0 ** -6
+    assert big.sum() > 3000
+    assert np.all(err[big] == 0.0)
+    assert np.all(err[~big] <= 2.0 ** -14)
