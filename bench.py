@@ -1,8 +1,9 @@
 """Benchmark: quantize+pack into the packed ternary KV cache, then decode attention over it.
 
 One step is one pass of the whole hot path over one batch of synthetic input:
-every append call of the workload (absmean pass, gamma finalize, quantise +
-pack + page scatter) followed by one decode step of every layer.  The default
+every append call of the workload (absmean pass, then quantise + pack + page
+scatter, whose waves derive each segment's gamma) followed by one decode step of
+every layer.  The default
 workload is the full-retention long-context batch (32 sequences of 32768 bf16
 tokens, 32 query / 8 KV heads, head_dim 128, 2% outlier channels, every token
 attended): the largest workload that is bandwidth-bound on one GPU.  Other
@@ -13,7 +14,7 @@ bytes of one decode step (the attended pages in their stored formats, their
 gammas, the queries and the outputs) divided by the device time of the step's
 decode launches (decode + split merge), from HIP event pairs around each
 launch on the launch stream, over the timed steps.  The quantize+pack
-rate (algorithmic bytes of the write side over the device time of its three
+rate (algorithmic bytes of the write side over the device time of its two
 kernels) stands beside it, with a roofline for the decode kernel, the pack
 kernel and the absmean kernel.  Inputs are resident in HBM before the timed
 region; several input sets rotate when one set would fit in the 256 MB
@@ -209,10 +210,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in; 2-bit codes (4 per u8); f16-operand MFMA, f32 accumulate and softmax",
+        "dtype": ("bf16 in; 2-bit codes (4 per u8); scores fp4 codes x two e4m3 query terms (head dim 128, "
+                  "bf16 queries; f16 operands otherwise), P*V f16-operand MFMA; f32 accumulate and softmax"),
         "dtype_detail": ("write side: 16-bit inputs, float64 absmean sums, codes by integer thresholds equal to "
-                         "float32 RoundClip(x / (gamma + eps)); decode: codes and the query as f16 MFMA operands, "
-                         "probabilities as f16 (scaled by 2^14), f32 scores, softmax state and accumulation"),
+                         "float32 RoundClip(x / (gamma + eps)); decode: ternary key codes as e2m1 operands against "
+                         "the bf16 query held exactly as two e4m3 terms (scaled MFMA, head dim 128), other keys, "
+                         "the values and f16 queries as f16 operands, probabilities as f16 (scaled by 2^14), "
+                         "f32 scores, softmax state and accumulation"),
         "data": "synthetic (seeded torch.randn, see bit_ternary_attention_amd/workloads.py)",
         "config": {"workload": w.name, "layers": w.n_layers, "seqs": w.n_seqs,
                    "tokens_per_seq": list(sorted(set(w.lengths))) if len(set(w.lengths)) > 1 else w.lengths[0],
@@ -239,7 +243,7 @@ def main():
                           "hbm_frac": round(write_bytes / (write_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "bytes_per_step": write_bytes, "device_us_per_step": round(write_ms * 1e3, 3),
                           "kv_tokens_per_s": round(kv_tokens * w.n_layers / (write_ms * 1e-3), 1),
-                          "timing": "sum of the absmean, finalize and pack launches' event pairs"},
+                          "timing": "sum of the absmean and pack launches' event pairs"},
         "step_GBps": round((dec_bytes + write_bytes) / (ms_step * 1e-3) / 1e9, 1),
         "kernels": kernels,
         "roofline": roofline("decode"),

@@ -53,7 +53,14 @@ int decode_blocks_per_cu() {
   const int v = e ? std::atoi(e) : 0;
   return v >= 1 && v <= 8 ? v : 2;
 }
-constexpr int kDecodeMixedParts = 1;  // matrix-core kernel: blocks per (sequence, KV head) for fp8 / fp16 pages
+// matrix-core kernel: blocks per (sequence, KV head) for fp8 / fp16 pages (at most kDecodeMixedPartsMax;
+// VK_DECODE_MIX_PARTS=1..4 overrides)
+constexpr int kDecodeMixedPartsMax = 4;
+int decode_mixed_parts() {
+  const char* e = std::getenv("VK_DECODE_MIX_PARTS");
+  const int v = e ? std::atoi(e) : 0;
+  return v >= 1 && v <= kDecodeMixedPartsMax ? v : 1;
+}
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
   const char* e = std::getenv("VK_DECODE_UPI");
   return (e && e[0] == '4') ? 4 : 8;
@@ -594,7 +601,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   // sequences per launch: every (sequence, KV head) needs room for a split's partial and the
   // fp8 / fp16 blocks' partials
   const int32_t per_launch = static_cast<int32_t>(std::max<int64_t>(
-      1, std::min<int64_t>(vk::kDecodeMaxSeqs, kDecodeScratchItems / ((2 + kDecodeMixedParts) * cfg.n_kv_heads))));
+      1, std::min<int64_t>(vk::kDecodeMaxSeqs, kDecodeScratchItems / ((2 + kDecodeMixedPartsMax) * cfg.n_kv_heads))));
   for (int32_t base = 0; base < n_seqs; base += per_launch) {
     const int32_t nb = std::min<int32_t>(per_launch, n_seqs - base);
     vk::DecodeArgs a{};
@@ -637,7 +644,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     // fp8 / fp16 pages: n_mix more blocks per (sequence, KV head); lossless pages: one more launch
     // of a block per (sequence, KV head); each writes a partial state of its own
     const int n_ll = mfma && cu[3] > 0 ? 1 : 0;
-    const int n_fp = mfma && (cu[1] + cu[2]) > 0 ? kDecodeMixedParts : 0;
+    const int n_fp = mfma && (cu[1] + cu[2]) > 0 ? decode_mixed_parts() : 0;
     const int n_mix = n_fp + n_ll;
     a.lossless = n_ll;
     a.n_mix_parts = n_fp;

@@ -587,7 +587,10 @@ void k_decode_mfma(DecodeArgs a) {
   // hold one exactly; f16 queries would need a third term's registers and keep the f16 product)
   constexpr bool F4 = D == 128 && QDT == 1;
   constexpr int NQ = 2;  // e4m3 terms of the query
-  constexpr float KMUL = F4 ? 2.0f : 16384.0f;  // ternary logit = ks (KMUL acc - qoff)
+  // ternary logit = ks (kmul acc - qoff): kmul 2 for the fp4 product, 2^14 for the f16 one
+  using ProdF4 = std::integral_constant<bool, F4>;  // long ranges: the fp4 product where built
+  using ProdF16 = std::false_type;                  // short ranges: the f16 product, whose
+                                                    // query set-up is shorter (latency-bound)
   static_assert(G <= 16, "one query head per lane column");
   // Column slots: the query heads are repeated over the 16 columns of the score product, in
   // NSL slots of W columns.  A clean step puts one unit's scores in each slot, so its softmax
@@ -819,22 +822,28 @@ void k_decode_mfma(DecodeArgs a) {
     const float qmul = pow2i(qsh);
     qsl = a.scale_log2 * pow2i(-qsh);
     uint32_t w[NQ][8];
-#pragma unroll
-    for (int t = 0; t < NQ; ++t)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[t][i] = 0u;
     float sum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int c = j >> 4, i = 2 * (j & 7) + ((j >> 3) & 1);  // dimension 64 c + 16 grp + i
-      float r = q_value<QDT>(static_cast<uint16_t>((x[c][i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) * qmul;
+    for (int t8 = 0; t8 < 8; ++t8) {  // operand word t8: bytes (slots) 4 t8 .. 4 t8 + 3
+      float r[4];
 #pragma unroll
-      for (int t = 0; t < NQ; ++t) {
-        const int e8 = __builtin_amdgcn_cvt_pk_fp8_f32(r * pow2i(4 * t), 0.0f, 0, false) & 0xFF;
-        const float back = __builtin_amdgcn_cvt_f32_fp8(e8, 0) * pow2i(-4 * t);  // the term's value
-        r -= back;
-        sum += back;
-        w[t][j >> 2] |= static_cast<uint32_t>(e8) << (8 * (j & 3));
+      for (int k = 0; k < 4; ++k) {
+        const int j = 4 * t8 + k, c = j >> 4, i = 2 * (j & 7) + ((j >> 3) & 1);  // dimension 64 c + 16 grp + i
+        r[k] = q_value<QDT>(static_cast<uint16_t>((x[c][i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) * qmul;
+      }
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {  // term t, stored at 2^(4 t): four bytes by two packed converts
+        const float up = pow2i(4 * t), down = pow2i(-4 * t);
+        int e = __builtin_amdgcn_cvt_pk_fp8_f32(r[0] * up, r[1] * up, 0, false);
+        e = __builtin_amdgcn_cvt_pk_fp8_f32(r[2] * up, r[3] * up, e, true);
+        const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(e, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(e, true);
+        const float back[4] = {lo[0] * down, lo[1] * down, hi[0] * down, hi[1] * down};  // the term's values
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          r[k] -= back[k];
+          sum += back[k];
+        }
+        w[t][t8] = static_cast<uint32_t>(e);
       }
     }
 #pragma unroll
@@ -861,10 +870,11 @@ void k_decode_mfma(DecodeArgs a) {
   float m = -INFINITY, lsum = 0.0f, tsum = 0.0f, vcur = 0.0f;
   const h2_t ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
   const OConst oc = oconst();
-  // raw score accumulator of one ternary unit (logit = ks (KMUL acc - qoff))
-  auto tern_score = [&](const uint32_t (&k)[NC]) -> f4_t {
+  // raw score accumulator of one ternary unit (logit = ks (kmul acc - qoff)); PRD: ProdF4 or
+  // ProdF16, the product the wave's query operands were built for (make_qt or make_qb)
+  auto tern_score = [&](const uint32_t (&k)[NC], auto PRD) -> f4_t {
     f4_t s4 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (F4) {
+    if constexpr (decltype(PRD)::value) {
       constexpr uint32_t M = 0x33333333u;  // the even 2-bit fields, one per nibble
       const v8i_t ak = {static_cast<int>(k[0] & M), static_cast<int>((k[0] >> 2) & M),
                         static_cast<int>(k[NC - 1] & M), static_cast<int>((k[NC - 1] >> 2) & M), 0, 0, 0, 0};
@@ -939,18 +949,20 @@ void k_decode_mfma(DecodeArgs a) {
   // the score tiles of NSL units merge into one, unit i in slot i, so the softmax runs once
   // for them; P*V then gives each unit's probabilities only to its own slot's columns (a
   // block-diagonal B operand) and the slots are summed when the wave ends.
-  auto process_clean = [&](const Chunk& cc, const UnitRaw<NC, NV> (&r)[SU], bool partial, int lu0, int lu_end) {
+  auto process_clean = [&](const Chunk& cc, const UnitRaw<NC, NV> (&r)[SU], bool partial, int lu0, int lu_end,
+                           auto PRD) {
+    constexpr float kmul = decltype(PRD)::value ? 2.0f : 16384.0f;
     constexpr int UT = NSL == 1 ? 1 : NSL;  // units per score tile
     constexpr int NT = SU / UT;             // score tiles
     const float ks = cc.gk0 * qsl;
-    const float a0 = ks * KMUL, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
+    const float a0 = ks * kmul, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
     float sc[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       f4_t tile;
 #pragma unroll
       for (int i = 0; i < UT; ++i) {
-        const f4_t s4 = tern_score(r[t * UT + i].k);
+        const f4_t s4 = tern_score(r[t * UT + i].k, PRD);
         if (i == 0) {
           tile = s4;
         } else {
@@ -1025,7 +1037,8 @@ void k_decode_mfma(DecodeArgs a) {
   // Two consecutive units: scores, one online-softmax update, then P*V (one 16x16x32
   // product per 16-dimension block when both units are ternary with one gamma_V).
   auto process_group = [&](int lu0, const Chunk& cc, int c0, const UnitRaw<NC, NV>& r0,
-                           const UnitRaw<NC, NV>& r1) {
+                           const UnitRaw<NC, NV>& r1, auto PRD) {
+    constexpr float kmul = decltype(PRD)::value ? 2.0f : 16384.0f;
     if (lu0 >= u_end) return;
     const bool have1 = lu0 + 1 < u_end;
     const int k0 = lu0 - c0;
@@ -1050,8 +1063,8 @@ void k_decode_mfma(DecodeArgs a) {
       const UnitRaw<NC, NV>& raw = g == 0 ? r0 : r1;
       const float ks = lane_f(cc.gk, k0 + g) * qsl;
       vs[g] = lane_f(cc.gv, k0 + g);
-      const f4_t s4 = tern_score(raw.k);
-      const float a0 = ks * KMUL, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
+      const f4_t s4 = tern_score(raw.k, PRD);
+      const float a0 = ks * kmul, a1 = -qoff * ks;  // logit (log2 units) = a0 * acc + a1
       if (full) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[g][r] = fmaf(s4[r], a0, a1);
@@ -1457,10 +1470,10 @@ void k_decode_mfma(DecodeArgs a) {
     const uint64_t in = (uint64_t{1} << n_in) - 1;
     const bool partial = n_in < S || ((cc.fmask >> (lu0 - c0)) & in) != in;
     if (((cc.cmask >> (lu0 - c0)) & in) == in && (PCLEAN || !partial)) {
-      process_clean(cc, r, partial, lu0, c_end);
+      process_clean(cc, r, partial, lu0, c_end, ProdF4{});
     } else {
-      process_group(lu0, cc, c0, r[0], r[1]);
-      if constexpr (S == 4) process_group(lu0 + 2, cc, c0, r[2], r[3]);
+      process_group(lu0, cc, c0, r[0], r[1], ProdF4{});
+      if constexpr (S == 4) process_group(lu0 + 2, cc, c0, r[2], r[3], ProdF4{});
     }
   };
   auto ring_round = [&](int k, int c0, int c_end, const Chunk& cc, auto&& refill) {
@@ -1506,7 +1519,7 @@ void k_decode_mfma(DecodeArgs a) {
       prologue(integral_constant<int, 6>{});
       prologue(integral_constant<int, 7>{});
     }
-    make_qt();
+    make_qb();  // (the f16 product: see ProdF16)
     chunk_flags(ch, u_begin);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // every copy has landed
     auto slot_row = [&](int i) -> const uint8_t* {  // ring row of slot i (wave-uniform)
@@ -1533,10 +1546,10 @@ void k_decode_mfma(DecodeArgs a) {
       const uint64_t in = (uint64_t{1} << n_in) - 1;
       const bool partial = n_in < S || ((ch.fmask >> (lu0 - u_begin)) & in) != in;
       if (((ch.cmask >> (lu0 - u_begin)) & in) == in && (PCLEAN || !partial)) {
-        process_clean(ch, r, partial, lu0, u_end);
+        process_clean(ch, r, partial, lu0, u_end, ProdF16{});
       } else {
-        process_group(lu0, ch, u_begin, r[0], r[1]);
-        if constexpr (S == 4) process_group(lu0 + 2, ch, u_begin, r[2], r[3]);
+        process_group(lu0, ch, u_begin, r[0], r[1], ProdF16{});
+        if constexpr (S == 4) process_group(lu0 + 2, ch, u_begin, r[2], r[3], ProdF16{});
       }
     }
   }
@@ -1599,10 +1612,10 @@ void k_decode_mfma(DecodeArgs a) {
           const uint64_t in = (uint64_t{1} << n_in) - 1;
           const bool partial = n_in < S || ((ch_cur.fmask >> (lu0 - c0)) & in) != in;
           if (((ch_cur.cmask >> (lu0 - c0)) & in) == in && (PCLEAN || !partial)) {
-            process_clean(ch_cur, r, partial, lu0, c_end);
+            process_clean(ch_cur, r, partial, lu0, c_end, ProdF4{});
           } else {
-            process_group(lu0, ch_cur, c0, r[0], r[1]);
-            if constexpr (S == 4) process_group(lu0 + 2, ch_cur, c0, r[2], r[3]);
+            process_group(lu0, ch_cur, c0, r[0], r[1], ProdF4{});
+            if constexpr (S == 4) process_group(lu0 + 2, ch_cur, c0, r[2], r[3], ProdF4{});
           }
         };
         step(integral_constant<int, 0>{});
@@ -1811,8 +1824,8 @@ __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
-  // matrix-core path: grid (hkv, n_seqs, n_parts), split n_splits (when present) takes the
-  // fp8 / fp16 pages; vector-ALU path: grid (n_splits, hkv, n_seqs)
+  // matrix-core path: grid (hkv, n_seqs, n_parts), parts n_splits .. take the fp8 / fp16 pages;
+  // vector-ALU path: grid (n_splits, hkv, n_seqs)
   const dim3 grid = a.kernel == VK_DECODE_VALU ? dim3(a.n_splits, a.P.hkv, a.n_seqs)
                                                : dim3(a.P.hkv, a.n_seqs, a.n_splits + a.n_mix_parts);
   if (t) t->begin(VK_KERNEL_DECODE, s);

@@ -57,7 +57,7 @@ def test_config_defaults():
 
 
 @pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_q_heads=12), dict(n_q_heads=2, n_kv_heads=4),
-                                 dict(n_q_heads=48, n_kv_heads=2), dict(head_dim=96), dict(block_size=24),
+                                 dict(n_q_heads=48, n_kv_heads=2), dict(head_dim=96), dict(head_dim=256), dict(block_size=24),
                                  dict(block_size=8), dict(max_seqs=0), dict(sink_tokens=-1),
                                  dict(sink_format=4), dict(pages_fp8=-1), dict(pages_lossless=-1),
                                  dict(decode_kernel=1, sink_format=3), dict(eps=-1.0),
