@@ -246,7 +246,7 @@ def main():
                           "timing": "sum of the absmean and pack launches' event pairs"},
         "step_GBps": round((dec_bytes + write_bytes) / (ms_step * 1e-3) / 1e9, 1),
         "kernels": kernels,
-        "roofline": roofline("decode"),
+        "roofline": {**roofline("decode"), "counters": measured_counters("decode", w.name)},
         "roofline_pack": roofline("pack"),
         "roofline_absmean": roofline("absmean"),
     }
@@ -515,6 +515,31 @@ def stream_leg(w, steps, warmup, prefill=1024, window=512, fp8_dynamic=False):
             "host_us_per_call": {"retier": round(host_s[0] * 1e6 / steps, 2), "evict": round(host_s[1] * 1e6 / steps, 2)},
             "pages_in_use": st["pages_used"], "page_bound": (per_seq - 1) * w.n_seqs,
             "pages_retiered": st["pages_retiered"], "pages_evicted": st["pages_evicted"]}
+
+
+def measured_counters(kind, workload_name):
+    """Hardware counters of this kernel on this workload (VALU busy, matrix-core busy, LDS bank
+    conflicts, L2 hits and misses, instructions per attended 16-token unit), from the record kept
+    with the profiles, or None when there is none or the kernel's sources have changed since."""
+    from bit_ternary_attention_amd import profsum
+
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kind}|{workload_name}")
+    if rec is None:
+        return None
+    srcs = [os.path.join(ROOT, p) for p in rec["sources"]]
+    if not all(os.path.exists(p) for p in srcs) or profsum.sources_sha256(srcs) != rec["source_sha256"]:
+        return None
+    c = rec["counters"]
+    keep = ("VALUBusy", "VALUUtilization", "MfmaUtil", "LDSBankConflict")
+    out = {k: c[k] for k in keep if k in c}
+    if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+        out["L2_hit_rate"] = round(c["TCC_HIT_sum"] / max(1.0, c["TCC_HIT_sum"] + c["TCC_MISS_sum"]), 4)
+    out["per_unit"] = rec["per_unit"]
+    out["source"] = "profiles/counters.json (rocprofv3 --pmc, one run per counter set)"
+    return out
 
 
 def measured_traffic(kind, workload_name):

@@ -15,6 +15,11 @@
   python -m bit_ternary_attention_amd.profsum counters <name-filter> <counter_collection.csv>...
       per-dispatch averages of every counter in the given --pmc runs, over the dispatches of
       the matching kernel with the largest grid (one launch shape out of a run that mixes several)
+  python -m bit_ternary_attention_amd.profsum record-counters <name-filter> <workload> <units> <out.json>
+      <counter_collection.csv>... -- <source>...
+      the counters mode's averages of one kernel as a JSON record (with the instruction counts
+      divided by the attended 16-token units of one launch), keyed by kernel kind and workload,
+      with the SHA-256 of its sources
   --largest (traffic, record): average only each kernel's dispatches that fetch at least
       90% of its largest one (one launch size out of a run that mixes several)
 """
@@ -89,6 +94,21 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
+def counter_averages(path: str, filt: str):
+    """(kernel, grid, dispatches, {counter: average}) over the dispatches of the matching kernel
+    with the largest grid in one --pmc csv, or None."""
+    rows = [r for r in csv.DictReader(open(path)) if filt in r["Kernel_Name"]]
+    if not rows:
+        return None
+    grid = max(int(r["Grid_Size"]) for r in rows)
+    per = {}
+    for r in rows:
+        if int(r["Grid_Size"]) == grid:
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    n = len(next(iter(per.values())))
+    return short(rows[0]["Kernel_Name"]), grid, n, {k: sum(v) / len(v) for k, v in per.items()}
+
+
 def main():
     largest = "--largest" in sys.argv
     sys.argv = [a for a in sys.argv if a != "--largest"]
@@ -131,20 +151,37 @@ def main():
     elif mode == "counters":
         filt, paths = sys.argv[2], sys.argv[3:]
         for path in paths:
-            rows = [r for r in csv.DictReader(open(path)) if filt in r["Kernel_Name"]]
-            if not rows:
+            got = counter_averages(path, filt)
+            if got is None:
                 continue
-            grid = max(int(r["Grid_Size"]) for r in rows)
-            per = {}
-            for r in rows:
-                if int(r["Grid_Size"]) == grid:
-                    per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-            name = short(rows[0]["Kernel_Name"])
-            n = len(next(iter(per.values())))
+            name, grid, n, per = got
             print(f"{name} (grid {grid} threads, {n} dispatches averaged; {os.path.relpath(path)}):")
             for k in sorted(per):
-                v = per[k]
-                print(f"  {k:28s} {sum(v) / len(v):18.2f}")
+                print(f"  {k:28s} {per[k]:18.2f}")
+    elif mode == "record-counters":
+        filt, workload, units, out = sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5]
+        rest = sys.argv[6:]
+        cut = rest.index("--")
+        paths, srcs = rest[:cut], rest[cut + 1:]
+        vals, name = {}, None
+        for path in paths:
+            got = counter_averages(path, filt)
+            if got is not None:
+                name = got[0]
+                vals.update(got[3])
+        if not vals:
+            raise SystemExit(f"kernel '{filt}' not found")
+        per_unit = {k[len("SQ_INSTS_"):].lower() + "_per_unit": round(v / units, 2)
+                    for k, v in vals.items() if k.startswith("SQ_INSTS_")}
+        rec = json.load(open(out)) if os.path.exists(out) else {}
+        kind = next((v for key, v in KINDS.items() if key in name), "other")
+        rec[f"{kind}|{workload}"] = {
+            "kind": kind, "kernel": name, "workload": workload, "units_per_launch": units,
+            "counters": {k: round(v, 2) for k, v in sorted(vals.items())}, "per_unit": per_unit,
+            "sources": [os.path.relpath(p) for p in srcs], "source_sha256": sources_sha256(srcs)}
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+        print(json.dumps(rec[f"{kind}|{workload}"], indent=1))
     else:
         raise SystemExit(__doc__)
 
