@@ -39,7 +39,7 @@ std::string validate_config(const vk_cache_config& c) {
   if (c.n_q_heads < 1 || c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a positive multiple of n_kv_heads";
   int g = c.n_q_heads / c.n_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return "n_q_heads / n_kv_heads must be 1, 2, 4 or 8";
-  if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256) return "head_dim must be 64, 128 or 256";
   if (c.block_size < kUnit || c.block_size > 65536 || (c.block_size & (c.block_size - 1)))
     return "block_size must be a power of two in [16, 65536]";
   if (c.max_seqs < 1) return "max_seqs must be >= 1";
@@ -50,6 +50,10 @@ std::string validate_config(const vk_cache_config& c) {
   if (c.decode_kernel < 0 || c.decode_kernel > 2) return "decode_kernel must be 0, 1 or 2";
   if (c.decode_kernel == VK_DECODE_VALU && (c.sink_format == VK_FMT_LOSSLESS || c.recent_format == VK_FMT_LOSSLESS))
     return "lossless pages are read by the matrix-core decode kernel only";
+  if (c.head_dim == 256 && c.decode_kernel == VK_DECODE_MFMA)
+    return "head_dim 256 is read by the vector-ALU decode kernel (decode_kernel 0 or 1)";
+  if (c.head_dim == 256 && (c.sink_format == VK_FMT_LOSSLESS || c.recent_format == VK_FMT_LOSSLESS))
+    return "lossless pages take head_dim 64 or 128";
   if (c.fp8_dynamic != 0 && c.fp8_dynamic != 1) return "fp8_dynamic must be 0 or 1";
   if (c.reserved0 != 0) return "reserved0 must be 0";
   if (c.pages_ternary < 0 || c.pages_fp8 < 0 || c.pages_f16 < 0 || c.pages_lossless < 0)

@@ -597,7 +597,8 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   int64_t units[4] = {0, 0, 0, 0};
   int32_t splits_used = 1, steal_used = 0;
-  const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
+  // head dim 256 has vector-ALU instances only (the config check refuses the other choice)
+  const bool mfma = cfg.decode_kernel != VK_DECODE_VALU && cfg.head_dim != 256;
   // sequences per launch: every (sequence, KV head) needs room for a split's partial and the
   // fp8 / fp16 blocks' partials
   const int32_t per_launch = static_cast<int32_t>(std::max<int64_t>(

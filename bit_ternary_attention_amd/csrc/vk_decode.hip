@@ -142,6 +142,9 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
   constexpr int QP = D / 2;    // f16 pairs per query row
   constexpr int DPL = D / 64;  // value dimensions per lane
   constexpr int UPI = kDecodeUnitsPerIter;
+  // key words per pass of the score loop: head dim 256 takes its row in four passes that stay
+  // a loop (their query reads from LDS are not hoisted into registers), the others in one
+  constexpr int KW = D == 256 ? 4 : DW;
   __shared__ uint32_t q2[G * QP];
   __shared__ uint32_t pbuf[UPI * G * 8];
   __shared__ float vmax_s[UPI];  // dynamic FP8: largest value scale of each unit's 16 tokens
@@ -208,35 +211,41 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
       float kscale;
       if (fmt == VK_FMT_TERNARY2) {
         const uint4* krow = reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[0] + (upi * 16 + r) * (D / 4));
-        uint32_t kw[DW];
+#pragma unroll 1
+        for (int p0 = 0; p0 < DW; p0 += KW) {
+          uint32_t kw[KW];
 #pragma unroll
-        for (int q4 = 0; q4 < DW / 4; ++q4) {
-          const uint4 x = krow[q4];
-          kw[4 * q4] = x.x; kw[4 * q4 + 1] = x.y; kw[4 * q4 + 2] = x.z; kw[4 * q4 + 3] = x.w;
-        }
+          for (int q4 = 0; q4 < KW / 4; ++q4) {
+            const uint4 x = krow[p0 / 4 + q4];
+            kw[4 * q4] = x.x; kw[4 * q4 + 1] = x.y; kw[4 * q4 + 2] = x.z; kw[4 * q4 + 3] = x.w;
+          }
 #pragma unroll
-        for (int w = 0; w < DW; ++w) {
+          for (int w = 0; w < KW; ++w) {
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const h2_t c2 = tern2(kw[w], ii);
+            for (int ii = 0; ii < 8; ++ii) {
+              const h2_t c2 = tern2(kw[w], ii);
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) acc[hh] = dot2(q2[hh * QP + w * 8 + ii], c2, acc[hh]);
+              for (int hh = 0; hh < G; ++hh) acc[hh] = dot2(q2[hh * QP + (p0 + w) * 8 + ii], c2, acc[hh]);
+            }
           }
         }
         kscale = P.gamma[(layer * P.cap[0] + idx) * 2];
       } else if (fmt == VK_FMT_FP8E4M3) {
         const uint4* krow = reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[1] + (upi * 16 + r) * D);
+#pragma unroll 1
+        for (int p0 = 0; p0 < DW; p0 += KW) {
 #pragma unroll
-        for (int w = 0; w < DW; ++w) {
-          const uint4 x = krow[w];  // bytes 16w .. 16w+15
-          const uint32_t lo[2] = {x.x, x.y}, hi[2] = {x.z, x.w};
+          for (int w = p0; w < p0 + KW; ++w) {
+            const uint4 x = krow[w];  // bytes 16w .. 16w+15
+            const uint32_t lo[2] = {x.x, x.y}, hi[2] = {x.z, x.w};
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const uint32_t bl = (lo[ii >> 2] >> (8 * (ii & 3))) & 0xFFu;
-            const uint32_t bh = (hi[ii >> 2] >> (8 * (ii & 3))) & 0xFFu;
-            const h2_t c2 = fp8x2(bl | (bh << 16));
+            for (int ii = 0; ii < 8; ++ii) {
+              const uint32_t bl = (lo[ii >> 2] >> (8 * (ii & 3))) & 0xFFu;
+              const uint32_t bh = (hi[ii >> 2] >> (8 * (ii & 3))) & 0xFFu;
+              const h2_t c2 = fp8x2(bl | (bh << 16));
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) acc[hh] = dot2(q2[hh * QP + w * 8 + ii], c2, acc[hh]);
+              for (int hh = 0; hh < G; ++hh) acc[hh] = dot2(q2[hh * QP + w * 8 + ii], c2, acc[hh]);
+            }
           }
         }
         kscale = P.fp8_scale;
@@ -248,17 +257,20 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
         }
       } else {
         const uint4* krow = reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[2] + (upi * 16 + r) * D * 2);
+#pragma unroll 1
+        for (int p0 = 0; p0 < DW; p0 += KW) {
 #pragma unroll
-        for (int w = 0; w < DW; ++w) {
-          const uint4 x0 = krow[2 * w], x1 = krow[2 * w + 1];  // elements 16w..+7, 16w+8..+15
-          const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+          for (int w = p0; w < p0 + KW; ++w) {
+            const uint4 x0 = krow[2 * w], x1 = krow[2 * w + 1];  // elements 16w..+7, 16w+8..+15
+            const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const uint32_t a16 = (lo[ii >> 1] >> (16 * (ii & 1))) & 0xFFFFu;
-            const uint32_t b16 = (hi[ii >> 1] >> (16 * (ii & 1))) & 0xFFFFu;
-            const h2_t c2 = as_h2(a16 | (b16 << 16));
+            for (int ii = 0; ii < 8; ++ii) {
+              const uint32_t a16 = (lo[ii >> 1] >> (16 * (ii & 1))) & 0xFFFFu;
+              const uint32_t b16 = (hi[ii >> 1] >> (16 * (ii & 1))) & 0xFFFFu;
+              const h2_t c2 = as_h2(a16 | (b16 << 16));
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) acc[hh] = dot2(q2[hh * QP + w * 8 + ii], c2, acc[hh]);
+              for (int hh = 0; hh < G; ++hh) acc[hh] = dot2(q2[hh * QP + w * 8 + ii], c2, acc[hh]);
+            }
           }
         }
         kscale = 1.0f;
@@ -329,7 +341,11 @@ __global__ __launch_bounds__(64) void k_decode(DecodeArgs a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             h2_t c01, c23;  // tokens (4g, 4g+1) and (4g+2, 4g+3)
-            if (D == 128) {
+            if (D == 256) {  // two head-dim-128 chunks: dimensions with jj < 8, then jj >= 8
+              const uint4 x = *reinterpret_cast<const uint4*>(vu + (cq * 4 + g) * (D / 16));
+              c01 = tern2(jj < 8 ? x.x : x.z, jj & 7);
+              c23 = tern2(jj < 8 ? x.y : x.w, jj & 7);
+            } else if (D == 128) {
               const uint2 x = *reinterpret_cast<const uint2*>(vu + (cq * 4 + g) * (D / 16));
               c01 = tern2(x.x, jj);
               c23 = tern2(x.y, jj);
@@ -1872,12 +1888,39 @@ hipError_t launch_d(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTim
   return hipErrorInvalidValue;
 }
 
+// Head dim 256: the vector-ALU kernel only (the host refuses the matrix-core kernel there),
+// grid (n_splits, hkv, n_seqs), then the merge when there are several splits.
+template <int G>
+hipError_t launch_valu_d256(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
+  if (a.kernel != VK_DECODE_VALU || a.lossless || a.n_mix_parts) return hipErrorInvalidValue;
+  if (t) t->begin(VK_KERNEL_DECODE, s);
+  const dim3 grid(a.n_splits, a.P.hkv, a.n_seqs);
+  if (a.q_dtype == VK_DTYPE_BF16) k_decode<256, G, 1><<<grid, 64, 0, s>>>(a);
+  else k_decode<256, G, 0><<<grid, 64, 0, s>>>(a);
+  if (t) t->end(VK_KERNEL_DECODE, s);
+  if (a.n_parts > 1) {
+    if (t) t->begin(VK_KERNEL_MERGE, s);
+    k_merge<256><<<dim3(a.hq, a.n_seqs), 256, 0, s>>>(a);
+    if (t) t->end(VK_KERNEL_MERGE, s);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// This file is compiled twice, once per head dim (VK_DECODE_DIM = 64 or 128), so that the two
-// halves of the kernel instances build in parallel.
+// This file is compiled twice (VK_DECODE_DIM = 64 or 128), so that the kernel instances build
+// in two halves in parallel; the head-dim-64 half also holds the head-dim-256 instances.
 #if VK_DECODE_DIM == 64
 hipError_t launch_decode_d64(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t) {
+  if (a.P.dim == 256) {
+    switch (group) {
+      case 1: return launch_valu_d256<1>(a, s, t);
+      case 2: return launch_valu_d256<2>(a, s, t);
+      case 4: return launch_valu_d256<4>(a, s, t);
+      case 8: return launch_valu_d256<8>(a, s, t);
+    }
+    return hipErrorInvalidValue;
+  }
   return launch_d<64>(a, group, s, t);
 }
 #elif VK_DECODE_DIM == 128
@@ -1885,7 +1928,7 @@ hipError_t launch_decode_d64(const DecodeArgs& a, int32_t group, hipStream_t s, 
 
 hipError_t launch_decode(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t) {
   if (a.P.dim == 128) return launch_d<128>(a, group, s, t);
-  if (a.P.dim == 64) return launch_decode_d64(a, group, s, t);
+  if (a.P.dim == 64 || a.P.dim == 256) return launch_decode_d64(a, group, s, t);
   return hipErrorInvalidValue;
 }
 #else

@@ -120,7 +120,7 @@ template <int D>
 __device__ __forceinline__ void store_chunk(const uint32_t* x, uint32_t add, uint8_t* out) {
   const uint32_t add01 = __builtin_amdgcn_perm(add, add, 0x01010000u);  // tokens 0, 0, 1, 1
   const uint32_t add23 = __builtin_amdgcn_perm(add, add, 0x03030202u);  // tokens 2, 2, 3, 3
-  uint32_t w0 = 0, w1 = 0;
+  uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
 #pragma unroll
   for (int j = 0; j < D / 16; j += 2) {
     // [x_j.b0, x_j+1.b0, x_j.b1, x_j+1.b1] and the same of bytes 2, 3
@@ -128,16 +128,21 @@ __device__ __forceinline__ void store_chunk(const uint32_t* x, uint32_t add, uin
     const uint32_t f23 = fields4(__builtin_amdgcn_perm(x[j + 1], x[j], 0x07030602u), add23);
     const uint32_t t01 = (f01 & 0x00030003u) | ((f01 >> 6) & 0x000C000Cu);  // bits 0-3, 16-19
     const uint32_t t23 = (f23 & 0x00030003u) | ((f23 >> 6) & 0x000C000Cu);
-    if (D == 128) {
+    if (D == 64) {
+      // one word: token 4g at bits 2j, 4g+2 at 8+2j, 4g+1 at 16+2j, 4g+3 at 24+2j
+      w0 |= (t01 << (2 * j)) | (t23 << (8 + 2 * j));
+    } else if (j < 8) {
       // word 0: token 4g at bits 2j, 4g+1 at bits 16+2j; word 1: tokens 4g+2, 4g+3
       w0 |= t01 << (2 * j);
       w1 |= t23 << (2 * j);
     } else {
-      // one word: token 4g at bits 2j, 4g+2 at 8+2j, 4g+1 at 16+2j, 4g+3 at 24+2j
-      w0 |= (t01 << (2 * j)) | (t23 << (8 + 2 * j));
+      // head dim 256: words 2 and 3 the same for dimensions 16j + c with j >= 8
+      w2 |= t01 << (2 * (j - 8));
+      w3 |= t23 << (2 * (j - 8));
     }
   }
-  if (D == 128) *reinterpret_cast<uint2*>(out) = make_uint2(w0, w1);
+  if (D == 256) *reinterpret_cast<uint4*>(out) = make_uint4(w0, w1, w2, w3);
+  else if (D == 128) *reinterpret_cast<uint2*>(out) = make_uint2(w0, w1);
   else *reinterpret_cast<uint32_t*>(out) = w0;
 }
 
@@ -348,10 +353,12 @@ hipError_t launch_retier(const RetierArgs& a, hipStream_t s, LaunchTimer* t) {
   const dim3 grid(a.n_tasks, a.P.n_layers, 2);
   if (t) t->begin(VK_KERNEL_RETIER, s);
   if (a.P.fp8_dynamic) {
-    if (a.P.dim == 128) k_retier_dyn<128><<<grid, kRetierThreads, 0, s>>>(a);
+    if (a.P.dim == 256) k_retier_dyn<256><<<grid, kRetierThreads, 0, s>>>(a);
+    else if (a.P.dim == 128) k_retier_dyn<128><<<grid, kRetierThreads, 0, s>>>(a);
     else k_retier_dyn<64><<<grid, kRetierThreads, 0, s>>>(a);
   } else {
-    if (a.P.dim == 128) k_retier<128><<<grid, kRetierThreads, 0, s>>>(a);
+    if (a.P.dim == 256) k_retier<256><<<grid, kRetierThreads, 0, s>>>(a);
+    else if (a.P.dim == 128) k_retier<128><<<grid, kRetierThreads, 0, s>>>(a);
     else k_retier<64><<<grid, kRetierThreads, 0, s>>>(a);
   }
   if (t) t->end(VK_KERNEL_RETIER, s);

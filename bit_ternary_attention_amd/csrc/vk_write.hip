@@ -347,25 +347,30 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
         }
         __syncthreads();
         // value tile, chunked per 16-token unit: lane = chunk 4*cq + g = tokens 4g..4g+3 of
-        // dimensions 16j + cq; LDS rows (4g, 4g+1) and (4g+2, 4g+3) arrive as one dword each
+        // dimensions 16j + cq; LDS rows (4g, 4g+1) and (4g+2, 4g+3) arrive as one dword each.
+        // Head dim 256 keeps two head-dim-128 chunks side by side (j < 8, then j >= 8).
         const int cq = lane >> 2, g = lane & 3;
         const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds16);
-        uint32_t w0 = 0, w1 = 0;
+        uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
           const int dd = 16 * j + cq;
           const int cc = dd >> 3, e = dd & 7;
           const uint32_t f01 = (l32[cc * 8 + 2 * g] >> (2 * e)) & 0x00030003u;
           const uint32_t f23 = (l32[cc * 8 + 2 * g + 1] >> (2 * e)) & 0x00030003u;
-          if (D == 128) {
+          if (D == 64) {
+            w0 |= (f01 << (2 * j)) | (f23 << (8 + 2 * j));
+          } else if (j < 8) {
             w0 |= f01 << (2 * j);
             w1 |= f23 << (2 * j);
           } else {
-            w0 |= (f01 << (2 * j)) | (f23 << (8 + 2 * j));
+            w2 |= f01 << (2 * (j - 8));
+            w3 |= f23 << (2 * (j - 8));
           }
         }
         uint8_t* vdst = tile + upi * 4 * D + lane * (D / 16);
-        if (D == 128) *reinterpret_cast<uint2*>(vdst) = make_uint2(w0, w1);
+        if (D == 256) *reinterpret_cast<uint4*>(vdst) = make_uint4(w0, w1, w2, w3);
+        else if (D == 128) *reinterpret_cast<uint2*>(vdst) = make_uint2(w0, w1);
         else *reinterpret_cast<uint32_t*>(vdst) = w0;
         __syncthreads();
       }
@@ -683,7 +688,15 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s, LaunchTimer* t) {
   }
   const dim3 g2(a.pack_blocks);
   if (t) t->begin(VK_KERNEL_PACK, s);
-  if (a.P.dim == 128 && a.all_ternary) {
+  if (a.P.dim == 256) {  // (no lossless pages at head dim 256: refused on the host)
+    if (a.all_ternary) {
+      if (bf) k_pack<1, 256, 0><<<g2, 64, 0, s>>>(a);
+      else k_pack<0, 256, 0><<<g2, 64, 0, s>>>(a);
+    } else {
+      if (bf) k_pack<1, 256, 1><<<g2, 64, 0, s>>>(a);
+      else k_pack<0, 256, 1><<<g2, 64, 0, s>>>(a);
+    }
+  } else if (a.P.dim == 128 && a.all_ternary) {
     if (bf) k_pack<1, 128, 0><<<g2, 64, 0, s>>>(a);
     else k_pack<0, 128, 0><<<g2, 64, 0, s>>>(a);
   } else if (a.P.dim == 128) {
@@ -698,7 +711,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s, LaunchTimer* t) {
   }
   // the lossless units: one block per (layer, unit, K|V, head); bfloat16 input only (checked on
   // the host)
-  if (a.n_ll_units > 0) {
+  if (a.n_ll_units > 0 && a.P.dim != 256) {
     const dim3 g3(static_cast<unsigned>(2LL * a.P.hkv * a.n_ll_units * a.n_layers));
     if (a.P.dim == 128) k_pack<1, 128, 2><<<g3, 64, 0, s>>>(a);
     else k_pack<1, 64, 2><<<g3, 64, 0, s>>>(a);

@@ -86,10 +86,12 @@ enum {
 
 /* decode kernels (same results within the decode tolerance; see vk_decode_attn) */
 enum {
-  VK_DECODE_DEFAULT = 0,  /* the library's choice (currently VK_DECODE_MFMA)                      */
+  VK_DECODE_DEFAULT = 0,  /* the library's choice (VK_DECODE_MFMA; VK_DECODE_VALU at head_dim 256)  */
   VK_DECODE_VALU = 1,     /* vector ALU: v_dot2_f32_f16 over unpacked codes, query rows in LDS (no
                              lossless pages: a config with them and this kernel is refused) */
-  VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores and P*V, pages staged in LDS by
+  VK_DECODE_MFMA = 2      /* matrix cores (head_dim 64 and 128; a head_dim 256 config with this
+                             kernel is refused, and the default takes the vector-ALU kernel
+                             there): 16x16x32 f16 scores and P*V, pages staged in LDS by
                              buffer-to-LDS copies, codes unpacked to f16 in registers, query rows
                              resident as the B operand; fp8 / fp16 pages in one extra block per
                              (sequence, KV head) that writes its own partial state.  Opt-in
@@ -117,7 +119,8 @@ typedef struct vk_cache_config {
   int32_t n_layers;           /* >= 1                                                  */
   int32_t n_kv_heads;         /* >= 1                                                  */
   int32_t n_q_heads;          /* multiple of n_kv_heads; n_q_heads/n_kv_heads in {1,2,4,8} */
-  int32_t head_dim;           /* 64 or 128                                             */
+  int32_t head_dim;           /* 64, 128 or 256 (256: vector-ALU decode kernel and no
+                                 lossless pages)                                      */
   int32_t block_size;         /* tokens per page: power of two in [16, 65536]          */
   int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1                      */
   int32_t max_tokens_per_seq; /* >= 1                                                  */
@@ -170,7 +173,8 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out);
  * 16j+c (head_dim 128: two little-endian words, word h with token 4g+2h in its
  * low and 4g+2h+1 in its high 16 bits, dimension 16j+c at bits 2j; head_dim 64:
  * one word, tokens 4g, 4g+2, 4g+1, 4g+3 in bytes 0..3, dimension 16j+c at bits
- * 2j of each byte).
+ * 2j of each byte; head_dim 256: four words, words 0 and 1 as head_dim 128
+ * for j < 8, words 2 and 3 the same for j >= 8 at bits 2(j-8)).
  * gamma never returns to the host.
  *
  * Errors: VK_ERR_ARG (ids, sizes, pointers, dtype), VK_ERR_CAPACITY (pool
@@ -199,7 +203,8 @@ VK_API vk_status vk_append_ragged(vk_cache* c, int32_t layer_begin, int32_t n_la
  *    queries of one (sequence, KV head) are scaled by one power of two before
  *    the products and the scores by its inverse, so bf16 queries beyond the f16
  *    range are taken exactly.  f16 operands (the largest magnitude brought to
- *    [2^14, 2^15)) for f16 queries, head_dim 64 and pages other than ternary;
+ *    [2^14, 2^15)) for f16 queries, head_dim 64 and 256 and pages other than
+ *    ternary;
  *    ternary keys at head_dim 128 with bf16 queries meet the query as the sum of
  *    two e4m3 terms (largest magnitude in [2^6, 2^7)), which hold every element
  *    of at least 2^-12 times the largest exactly and the smaller ones to within

@@ -23,7 +23,10 @@ Readings where that page is silent:
                token 4g+2h+1 in its high 16 bits, dimension 16j+c at bits 2j;
       D = 64:  one word; its low 16 bits hold token 4g (bits 0-7) and 4g+2
                (bits 8-15), its high 16 bits token 4g+1 and 4g+3; dimension
-               16j+c at bits 2j of each byte.
+               16j+c at bits 2j of each byte;
+      D = 256: four words, two D = 128 chunks one after the other: words 0
+               and 1 hold the dimensions with j < 8 as D = 128 does, words 2
+               and 3 those with j >= 8 at bits 2(j - 8).
     Still four codes per byte.
 
 All inputs are the raw 16-bit patterns of float16 or bfloat16 tensors.
@@ -116,7 +119,9 @@ def _v_bit(r: int, j: int, dim: int) -> int:
         return 32 * (r // 2) + 16 * (r % 2) + 2 * j
     if dim == 64:
         return 16 * (r % 2) + 8 * (r // 2) + 2 * j
-    raise ValueError("head_dim must be 64 or 128")
+    if dim == 256:
+        return 64 * (j // 8) + 32 * (r // 2) + 16 * (r % 2) + 2 * (j % 8)
+    raise ValueError("head_dim must be 64, 128 or 256")
 
 
 def v_tile(codes: np.ndarray) -> np.ndarray:
@@ -125,19 +130,18 @@ def v_tile(codes: np.ndarray) -> np.ndarray:
     bs, dim = q.shape
     if bs % 16:
         raise ValueError("block size must be a multiple of 16")
-    u = (q + 1).astype(np.uint64)
+    u = q + 1
     nb = dim // 16                                  # dimensions per chunk; chunk = nb bytes
-    out = np.zeros((bs // 16, 64), dtype=np.uint64)  # one chunk per (c, g), as an integer
+    out = np.zeros((bs // 16, 64, nb), dtype=np.uint8)
     for k in range(bs // 16):
         for c in range(16):
             for g in range(4):
-                val = 0
+                val = 0                             # the chunk as one little-endian integer
                 for r in range(4):
                     for j in range(nb):
                         val |= int(u[16 * k + 4 * g + r, 16 * j + c]) << _v_bit(r, j, dim)
-                out[k, 4 * c + g] = val
-    chunk_bytes = out.astype("<u8").view(np.uint8).reshape(bs // 16, 64, 8)[:, :, :nb]
-    return np.ascontiguousarray(chunk_bytes).reshape(-1)
+                out[k, 4 * c + g] = np.frombuffer(val.to_bytes(nb, "little"), dtype=np.uint8)
+    return out.reshape(-1)
 
 
 def v_tile_codes(tile: np.ndarray, bs: int, dim: int) -> np.ndarray:

@@ -19,7 +19,9 @@ Layouts (one page: [K tile of head 0..Hkv-1][V tile of head 0..Hkv-1]):
     at bit value_bit(r, j): head_dim 128 -> two 32-bit words, word r//2 with
     token r even in its low and odd in its high half, dimension at 2j inside
     the half; head_dim 64 -> one word, token r at byte (r%2)*2 + r//2,
-    dimension at 2j inside the byte;
+    dimension at 2j inside the byte; head_dim 256 -> four 32-bit words, the
+    dimensions with j < 8 in words 0 and 1 as head_dim 128 places them, those
+    with j >= 8 in words 2 and 3 at 2(j - 8);
   * fp8 / fp16 tiles: keys [Bs][D], values [D][Bs]; dynamic FP8 tiles end
     with Bs float32 token scales.
   * lossless tiles: per 16-token unit a slot of 32 D + 16 bytes: a 16-byte
@@ -50,7 +52,10 @@ def value_bit(r: int, j: int, dim: int) -> int:
     if dim == 64:
         byte = 2 * (r % 2) + r // 2
         return 8 * byte + 2 * j
-    raise ValueError("head_dim must be 64 or 128")
+    if dim == 256:
+        word, half = 2 * (j // 8) + r // 2, r % 2
+        return 32 * word + 16 * half + 2 * (j % 8)
+    raise ValueError("head_dim must be 64, 128 or 256")
 
 
 def _fields_to_codes(u: np.ndarray) -> np.ndarray:
@@ -73,11 +78,9 @@ def value_codes(tiles: np.ndarray, bs: int, dim: int) -> np.ndarray:
     nb = dim // 16                       # bytes per chunk
     units = bs // 16
     chunks = b.reshape(lead + (units, 16, 4, nb))           # [..., unit, c, g, byte]
-    word = np.zeros(chunks.shape[:-1], dtype=np.uint64)
-    for i in range(nb):                                      # little-endian integer of the chunk
-        word |= chunks[..., i].astype(np.uint64) << np.uint64(8 * i)
-    shifts = np.array([[value_bit(r, j, dim) for j in range(nb)] for r in range(4)], dtype=np.uint64)
-    u = (word[..., None, None] >> shifts) & np.uint64(3)     # [..., unit, c, g, r, j]
+    bits = np.array([[value_bit(r, j, dim) for j in range(nb)] for r in range(4)])
+    # field of (r, j): byte bits // 8 of the chunk, shifted down by bits % 8
+    u = (chunks[..., bits // 8] >> (bits % 8).astype(np.uint8)) & np.uint8(3)   # [..., unit, c, g, r, j]
     nd = len(lead)
     perm = tuple(range(nd)) + (nd, nd + 2, nd + 3, nd + 4, nd + 1)   # -> [..., unit, g, r, j, c]
     u = np.transpose(u, perm).reshape(lead + (bs, dim))      # token 16*unit + 4g + r, dim 16j + c

@@ -139,7 +139,10 @@ def check_decode(cache, stream, encs, layer, window, S):
                                                          (64, 16, 20, wl.FMT_FP8E4M3, 16, 0.25, 0),
                                                          (128, 16, 4, wl.FMT_F16, 48, 1.0, 1),
                                                          (64, 32, 4, wl.FMT_TERNARY2, 40, 1.0, 1),
-                                                         (128, 64, 20, wl.FMT_FP8E4M3, 100, 1.0, 1)])
+                                                         (128, 64, 20, wl.FMT_FP8E4M3, 100, 1.0, 1),
+                                                         (256, 16, 4, wl.FMT_F16, 48, 1.0, 0),
+                                                         (256, 64, 4, wl.FMT_TERNARY2, 100, 0.5, 0),
+                                                         (256, 32, 20, wl.FMT_FP8E4M3, 40, 1.0, 1)])
 def test_retier_ragged_appends(dim, bs, S, sinkf, R, scale, dyn):
     """Ragged appends per sequence, retiering after every call; every page checked."""
     say(f"retier ragged: dim {dim} bs {bs} S {S} sink fmt {sinkf} R {R} scale {scale} dynamic {dyn}")

@@ -153,7 +153,7 @@ def test_v_tile_hand_example_and_inverse():
             want[int(k)] = v
         assert tile.tolist() == want.tolist(), dim
     rng = np.random.default_rng(5)
-    for dim in (64, 128):
+    for dim in (64, 128, 256):
         q = rng.integers(-1, 2, size=(64, dim)).astype(np.int8)
         assert np.array_equal(ot.v_tile_codes(ot.v_tile(q), 64, dim), q)
         # each unit's chunk bytes depend only on that unit's tokens

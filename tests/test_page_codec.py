@@ -10,7 +10,7 @@ from oracle import ternary as ot
 import page_codec as pc
 
 
-@pytest.mark.parametrize("dim", [64, 128])
+@pytest.mark.parametrize("dim", [64, 128, 256])
 @pytest.mark.parametrize("bs", [16, 32])
 def test_value_codes_invert_oracle_v_tile(dim, bs):
     rng = np.random.default_rng(dim * 100 + bs)
@@ -21,7 +21,7 @@ def test_value_codes_invert_oracle_v_tile(dim, bs):
         assert np.array_equal(pc.value_codes(tile, bs, dim), ot.v_tile_codes(tile, bs, dim))
 
 
-@pytest.mark.parametrize("dim", [64, 128])
+@pytest.mark.parametrize("dim", [64, 128, 256])
 def test_value_codes_single_field_positions(dim):
     """One nonzero code at a time lands where the oracle puts it (catches a swapped token or dimension)."""
     bs = 16
