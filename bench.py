@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3: full retention, 32 x 32K tokens)")
+    ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3: full retention, 32 x 32K tokens); 6: head dim 256, 32 x 16K tokens")
     ap.add_argument("--decode-kernel", type=int, default=0, help="0 default, 1 vector ALU, 2 matrix cores")
     ap.add_argument("--sink-format", choices=sorted(FORMATS), default=None,
                     help="page format of the sink pages instead of the workload's own (lossless: the exact "

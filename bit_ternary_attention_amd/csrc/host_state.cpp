@@ -50,8 +50,6 @@ std::string validate_config(const vk_cache_config& c) {
   if (c.decode_kernel < 0 || c.decode_kernel > 2) return "decode_kernel must be 0, 1 or 2";
   if (c.decode_kernel == VK_DECODE_VALU && (c.sink_format == VK_FMT_LOSSLESS || c.recent_format == VK_FMT_LOSSLESS))
     return "lossless pages are read by the matrix-core decode kernel only";
-  if (c.head_dim == 256 && c.decode_kernel == VK_DECODE_MFMA)
-    return "head_dim 256 is read by the vector-ALU decode kernel (decode_kernel 0 or 1)";
   if (c.head_dim == 256 && (c.sink_format == VK_FMT_LOSSLESS || c.recent_format == VK_FMT_LOSSLESS))
     return "lossless pages take head_dim 64 or 128";
   if (c.fp8_dynamic != 0 && c.fp8_dynamic != 1) return "fp8_dynamic must be 0 or 1";

@@ -597,8 +597,8 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   int64_t units[4] = {0, 0, 0, 0};
   int32_t splits_used = 1, steal_used = 0;
-  // head dim 256 has vector-ALU instances only (the config check refuses the other choice)
-  const bool mfma = cfg.decode_kernel != VK_DECODE_VALU && cfg.head_dim != 256;
+  const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
+  const bool d256 = cfg.head_dim == 256;  // matrix-core instances: 4-slot ring, no stealing blocks
   // sequences per launch: every (sequence, KV head) needs room for a split's partial and the
   // fp8 / fp16 blocks' partials
   const int32_t per_launch = static_cast<int32_t>(std::max<int64_t>(
@@ -617,7 +617,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     a.sink_tokens = cfg.sink_tokens;
     a.window = window;
     a.kernel = mfma ? VK_DECODE_MFMA : VK_DECODE_VALU;
-    a.units_per_iter = decode_units_per_iter();
+    a.units_per_iter = d256 ? 4 : decode_units_per_iter();
     a.scale_log2 = scale * 1.4426950408889634f;
     int32_t max_units = 0;
     int64_t cu[4] = {0, 0, 0, 0};  // attended units per format in this launch
@@ -668,7 +668,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     // enough work take one 12-wave block per compute unit whose waves share the block's units
     // piece by piece: the blocks' waves end together, and a block per pair writes its output.
     const int steal_mode = decode_steal_mode();
-    if (mfma && !mixed && !cfg.fp8_dynamic && a.units_per_iter == 8 && c->n_cu > 0 && items <= c->n_cu &&
+    if (mfma && !d256 && !mixed && !cfg.fp8_dynamic && a.units_per_iter == 8 && c->n_cu > 0 && items <= c->n_cu &&
         max_units > 0 && (steal_mode == 2 || (steal_mode == 1 && all_units >= kStealMinUnitsPerCu * c->n_cu))) {
       const int32_t ns = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(c->n_cu / items, max_splits)));
       const int32_t ups = (max_units + ns - 1) / ns;

@@ -564,17 +564,24 @@ __device__ __forceinline__ VWords<NV> vwords(const uint32_t (&v)[NV]) {
 // A operand of block j of the value product: tokens (4g, 4g+1), (4g+2, 4g+3) of dim 16j + l%16.
 // Head dim 128 (two words, block j at bits 2j of each): offset form, constant OPos<2j>::off.
 // Head dim 64 (one word, bits 2j and 8 + 2j): plain form u * 2^-14 (bit pattern u << 10).
+// Head dim 256 (four words): blocks j < 8 as head dim 128 in words 0 and 1, blocks j >= 8 the
+// same in words 2 and 3 (at bits 2 (j - 8)), constant OPos<2 (j % 8)>::off.
 template <int NV, int J>
 __device__ __forceinline__ h4_t va_ternary(const VWords<NV>& v, const OConst& o) {
-  if constexpr (NV == 2)
+  if constexpr (NV == 4) {
+    constexpr int w = 2 * (J / 8), p = 2 * (J % 8);
+    return __builtin_bit_cast(h4_t, u2_t{ocode2<p>(v.w[w], v.l4[w], v.r6[w], o),
+                                         ocode2<p>(v.w[w + 1], v.l4[w + 1], v.r6[w + 1], o)});
+  } else if constexpr (NV == 2) {
     return __builtin_bit_cast(h4_t, u2_t{ocode2<2 * J>(v.w[0], v.l4[0], v.r6[0], o),
                                          ocode2<2 * J>(v.w[NV - 1], v.l4[NV - 1], v.r6[NV - 1], o)});
-  else
+  } else {
     return __builtin_bit_cast(h4_t, u2_t{ucode2<2 * J>(v.w[0]), ucode2<2 * J + 8>(v.w[0])});
+  }
 }
 template <int NV>
 __device__ __forceinline__ float va_off(int j) {
-  return NV == 2 ? ocode_off(2 * j) : 0.0f;
+  return NV == 4 ? ocode_off(2 * (j & 7)) : NV == 2 ? ocode_off(2 * j) : 0.0f;
 }
 
 template <int NV, int NB, int J = 0>
@@ -590,7 +597,8 @@ __device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], cons
 // LL: the fp8 / fp16 blocks also read lossless pages (an instance of its own, launched only when
 // a launch attends lossless units: their decode needs registers the other instances keep).
 template <int D, int G, int QDT, int PF, bool DYN, bool STEAL, bool LL = false>
-__global__ __launch_bounds__(64 * (STEAL ? kStealWaves : kMfmaWaves)) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ __launch_bounds__(64 * (STEAL ? kStealWaves : kMfmaWaves))
+__attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : 3, 8)))  // head dim 256: twice the state per lane
 void k_decode_mfma(DecodeArgs a) {
   constexpr int NW = STEAL ? kStealWaves : kMfmaWaves;  // waves per block
   constexpr int NC = D / 64;   // 32-bit key code words per lane per unit
@@ -608,6 +616,7 @@ void k_decode_mfma(DecodeArgs a) {
   using ProdF16 = std::false_type;                  // short ranges: the f16 product, whose
                                                     // query set-up is shorter (latency-bound)
   static_assert(G <= 16, "one query head per lane column");
+  static_assert(D != 256 || (!STEAL && !LL), "head dim 256: no stealing blocks and no lossless pages");
   // Column slots: the query heads are repeated over the 16 columns of the score product, in
   // NSL slots of W columns.  A clean step puts one unit's scores in each slot, so its softmax
   // steps cover NSL units at once; the other paths keep their sums in slot 0 only.
@@ -616,7 +625,7 @@ void k_decode_mfma(DecodeArgs a) {
   constexpr int SU = NSL == 4 ? 4 : 2;   // units per clean step
   // clean steps may hold partly attended units (masked) where the registers allow it; at head
   // dim 128 with g <= 4 the masking would spill, and such steps take the general path
-  constexpr bool PCLEAN = D == 64 || G == 8;
+  constexpr bool PCLEAN = D == 64 || (D == 128 && G == 8);
   static_assert(CH % PF == 0 && PF % UG == 0 && PF % SU == 0, "chunks hold whole prefetch rounds and groups");
   __shared__ float lds_m[NW][G], lds_l[NW][G];
   __shared__ int lds_next;  // stealing blocks: the next piece to hand out
@@ -628,7 +637,10 @@ void k_decode_mfma(DecodeArgs a) {
   // by buffer-to-LDS loads.  One array per slot, so the compiler's wait counting can tell
   // the slots apart and waits only for the load of the slot it reads.
   constexpr int UB = 8 * D;     // bytes of one unit's tiles of one head
-  constexpr int RB = 64 * 16;   // ring row: one 16-byte piece per lane (head dim 64 fills half)
+  // ring row: one 16-byte piece per lane (head dim 64 fills half); head dim 256: two pieces per
+  // lane, the key tile and then the value tile, by two copies
+  constexpr int NCP = D == 256 ? 2 : 1;  // copies per unit
+  constexpr int RB = 64 * 16 * NCP;
   constexpr int NR = PF;
   static_assert(NR == 8 || NR == 4, "ring of 4 or 8 slots");
   __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][RB], ring1[NW][RB],
@@ -677,6 +689,8 @@ void k_decode_mfma(DecodeArgs a) {
   // at 16 c16 + 4 grp.  The copy moves 16-byte pieces, lane i to ring offset 16 i.  Head dim
   // 128 places piece (row r, half h) at 16 (16 h + r): then the 8-byte reads of lanes
   // 0..31 (and of 32..63) cover 256 contiguous bytes, free of bank conflicts.
+  // Head dim 256: 16 bytes at 64 c16 + 16 grp of each tile, whose copies place every piece
+  // in order.
   // lane_k = this lane's read offset in the key half of a ring row (+ UB / 2: value half).
   const uint32_t lane_k = D == 128 ? 256 * (grp >> 1) + 16 * c16 + 8 * (grp & 1) : c16 * (D / 4) + grp * (D / 16);
   // piece fetched by this lane: lanes [0, D/4) the key tile, [D/4, D/2) the value tile; with
@@ -923,9 +937,17 @@ void k_decode_mfma(DecodeArgs a) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pg), 0, lu < u_end ? page_bytes0 : 0, kBufferWord3);
     const int soff = kvh * tile0 + upi * 4 * D;  // unit offset within the key (and value) tile
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)row, 16, dma_off, soff, 0, 0);
+    if constexpr (NCP == 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(row + UB / 2), 16,
+                                               dma_off + hkv_tile, soff, 0, 0);
   };
   auto read_unit = [&](const uint8_t* row, UnitRaw<NC, NV>& r) {
-    if (NC == 2) {
+    if constexpr (NC == 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(row + lane_k);
+      const uint4 y = *reinterpret_cast<const uint4*>(row + UB / 2 + lane_k);
+      r.k[0] = x.x; r.k[1] = x.y; r.k[2] = x.z; r.k[3] = x.w;
+      r.v[0] = y.x; r.v[1] = y.y; r.v[2] = y.z; r.v[3] = y.w;
+    } else if (NC == 2) {
       const uint2 x = *reinterpret_cast<const uint2*>(row + lane_k);
       const uint2 y = *reinterpret_cast<const uint2*>(row + UB / 2 + lane_k);
       r.k[0] = x.x;
@@ -1454,8 +1476,8 @@ void k_decode_mfma(DecodeArgs a) {
 
   // One step of the ring loop: units k + S gi .. k + S gi + S - 1 of a range [c0, c_end) whose
   // metadata is cc; refill(lu, row) starts the copy of unit lu into a ring row.  Slots are
-  // taken two at a time: wait until their copies have landed (at most NR - 2 ring copies were
-  // issued after them; vector memory returns in issue order and any other load in between only
+  // taken two at a time: wait until their copies have landed (at most NR - 2 units' ring copies,
+  // NCP each, were issued after them; vector memory returns in issue order and any other load in between only
   // makes the wait stricter; the compiler's own wait counting does not follow buffer-to-LDS
   // copies into every ring array), read them into registers, and refill them with the units
   // NR ahead before any compute.
@@ -1467,7 +1489,7 @@ void k_decode_mfma(DecodeArgs a) {
     auto take2 = [&](auto H) {
       constexpr int i = 2 * decltype(H)::value;  // first unit of the pair in this step
       if constexpr (i < S) {
-        __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
+        __builtin_amdgcn_s_waitcnt(wait_vm(NCP * (NR - 2)));
         read_unit(ring_row(integral_constant<int, S * gi + i>{}), r[i]);
         read_unit(ring_row(integral_constant<int, S * gi + i + 1>{}), r[i + 1]);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot reads have returned
@@ -1601,14 +1623,14 @@ void k_decode_mfma(DecodeArgs a) {
           constexpr int gi = decltype(GI)::value;
           UnitRaw<NC, NV> r[S];
           // Slots are taken two at a time: wait until their copies have landed (at most
-          // NR - 2 ring copies were issued after them; vector memory returns in issue order
+          // NR - 2 units' ring copies (NCP each) were issued after them; vector memory returns in issue order
           // and any other load in between only makes the wait stricter; the compiler's own
           // wait counting does not follow buffer-to-LDS copies into every ring array), read
           // them into registers, and refill them with the units NR ahead before any compute.
           auto take2 = [&](auto H) {
             constexpr int i = 2 * decltype(H)::value;  // first unit of the pair in this step
             if constexpr (i < S) {
-              __builtin_amdgcn_s_waitcnt(wait_vm(NR - 2));
+              __builtin_amdgcn_s_waitcnt(wait_vm(NCP * (NR - 2)));
               read_unit(ring_row(integral_constant<int, S * gi + i>{}), r[i]);
               read_unit(ring_row(integral_constant<int, S * gi + i + 1>{}), r[i + 1]);
               __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the slot reads have returned
@@ -1888,15 +1910,28 @@ hipError_t launch_d(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTim
   return hipErrorInvalidValue;
 }
 
-// Head dim 256: the vector-ALU kernel only (the host refuses the matrix-core kernel there),
-// grid (n_splits, hkv, n_seqs), then the merge when there are several splits.
+// Head dim 256: the vector-ALU kernel, or the matrix-core kernel with a 4-slot ring of 2 KB
+// rows (no stealing blocks, no lossless pages: the host sends neither), then the merge when
+// there are several parts.
 template <int G>
-hipError_t launch_valu_d256(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
-  if (a.kernel != VK_DECODE_VALU || a.lossless || a.n_mix_parts) return hipErrorInvalidValue;
+hipError_t launch_d256(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
+  if (a.lossless || a.steal) return hipErrorInvalidValue;
   if (t) t->begin(VK_KERNEL_DECODE, s);
-  const dim3 grid(a.n_splits, a.P.hkv, a.n_seqs);
-  if (a.q_dtype == VK_DTYPE_BF16) k_decode<256, G, 1><<<grid, 64, 0, s>>>(a);
-  else k_decode<256, G, 0><<<grid, 64, 0, s>>>(a);
+  if (a.kernel == VK_DECODE_VALU) {
+    if (a.n_mix_parts) return hipErrorInvalidValue;
+    const dim3 grid(a.n_splits, a.P.hkv, a.n_seqs);
+    if (a.q_dtype == VK_DTYPE_BF16) k_decode<256, G, 1><<<grid, 64, 0, s>>>(a);
+    else k_decode<256, G, 0><<<grid, 64, 0, s>>>(a);
+  } else {
+    const dim3 grid(a.P.hkv, a.n_seqs, a.n_splits + a.n_mix_parts);
+    if (a.P.fp8_dynamic) {
+      if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<256, G, 1, 4, true, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+      else k_decode_mfma<256, G, 0, 4, true, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    } else {
+      if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<256, G, 1, 4, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+      else k_decode_mfma<256, G, 0, 4, false, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
+    }
+  }
   if (t) t->end(VK_KERNEL_DECODE, s);
   if (a.n_parts > 1) {
     if (t) t->begin(VK_KERNEL_MERGE, s);
@@ -1914,10 +1949,10 @@ hipError_t launch_valu_d256(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) 
 hipError_t launch_decode_d64(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTimer* t) {
   if (a.P.dim == 256) {
     switch (group) {
-      case 1: return launch_valu_d256<1>(a, s, t);
-      case 2: return launch_valu_d256<2>(a, s, t);
-      case 4: return launch_valu_d256<4>(a, s, t);
-      case 8: return launch_valu_d256<8>(a, s, t);
+      case 1: return launch_d256<1>(a, s, t);
+      case 2: return launch_d256<2>(a, s, t);
+      case 4: return launch_d256<4>(a, s, t);
+      case 8: return launch_d256<8>(a, s, t);
     }
     return hipErrorInvalidValue;
   }

@@ -111,7 +111,8 @@ def _c4_lengths() -> Tuple[int, ...]:
 
 
 def workload(number: int) -> Workload:
-    """The five seeded workloads, numbered 1..5."""
+    """The five seeded workloads, numbered 1..5, and number 6: head dim 256 at workload 3's page
+    bytes (32 sequences of 16384 bfloat16 tokens, 32 query / 8 KV heads, full retention)."""
     if number == 1:
         return Workload(1, "tiny-gqa4-d64-512tok", 1, 1, 8, 2, 64, DTYPE_F16, 512, 4, 256,
                         FMT_TERNARY2, 0, FMT_FP8E4M3, 0, (512,), 0)
@@ -127,6 +128,9 @@ def workload(number: int) -> Workload:
     if number == 5:
         return Workload(5, "prefill-128k-b4-chunk4096", 1, 4, 32, 8, 128, DTYPE_BF16, 16, 4, -1,
                         FMT_TERNARY2, 0, FMT_FP8E4M3, 0, (131072,) * 4, 4096)
+    if number == 6:
+        return Workload(6, "head-dim-256-b32-16k", 1, 32, 32, 8, 256, DTYPE_BF16, 16, 4, -1,
+                        FMT_TERNARY2, 0, FMT_FP8E4M3, 0, (16384,) * 32, 0)
     raise ValueError(f"no workload {number}")
 
 

@@ -86,12 +86,10 @@ enum {
 
 /* decode kernels (same results within the decode tolerance; see vk_decode_attn) */
 enum {
-  VK_DECODE_DEFAULT = 0,  /* the library's choice (VK_DECODE_MFMA; VK_DECODE_VALU at head_dim 256)  */
+  VK_DECODE_DEFAULT = 0,  /* the library's choice (currently VK_DECODE_MFMA)                      */
   VK_DECODE_VALU = 1,     /* vector ALU: v_dot2_f32_f16 over unpacked codes, query rows in LDS (no
                              lossless pages: a config with them and this kernel is refused) */
-  VK_DECODE_MFMA = 2      /* matrix cores (head_dim 64 and 128; a head_dim 256 config with this
-                             kernel is refused, and the default takes the vector-ALU kernel
-                             there): 16x16x32 f16 scores and P*V, pages staged in LDS by
+  VK_DECODE_MFMA = 2      /* matrix cores: 16x16x32 f16 scores and P*V, pages staged in LDS by
                              buffer-to-LDS copies, codes unpacked to f16 in registers, query rows
                              resident as the B operand; fp8 / fp16 pages in one extra block per
                              (sequence, KV head) that writes its own partial state.  Opt-in
@@ -100,7 +98,8 @@ enum {
                              KV head) per compute unit run 12-wave blocks whose waves take
                              16-unit pieces from a shared counter; the summation order then
                              varies between calls, so outputs repeat only within the decode
-                             tolerance (vk_stats.last_decode_steal reports the choice)       */
+                             tolerance (vk_stats.last_decode_steal reports the choice; never
+                             at head_dim 256)                                                 */
 };
 
 typedef struct vk_cache vk_cache; /* opaque; owned by the library */
@@ -119,8 +118,7 @@ typedef struct vk_cache_config {
   int32_t n_layers;           /* >= 1                                                  */
   int32_t n_kv_heads;         /* >= 1                                                  */
   int32_t n_q_heads;          /* multiple of n_kv_heads; n_q_heads/n_kv_heads in {1,2,4,8} */
-  int32_t head_dim;           /* 64, 128 or 256 (256: vector-ALU decode kernel and no
-                                 lossless pages)                                      */
+  int32_t head_dim;           /* 64, 128 or 256 (256: no lossless pages)               */
   int32_t block_size;         /* tokens per page: power of two in [16, 65536]          */
   int32_t max_seqs;           /* sequence ids are 0 .. max_seqs-1                      */
   int32_t max_tokens_per_seq; /* >= 1                                                  */

@@ -1,8 +1,9 @@
 """Head dim 256 on the GPU against the CPU oracle.
 
 At head dim 256 the cache is written by the same pack kernel (value chunks of 16
-bytes: two head-dim-128 chunks side by side) and read by the vector-ALU decode
-kernel, which the default decode choice takes there.  Every page is compared
+bytes: two head-dim-128 chunks side by side) and read by either decode kernel
+(the matrix-core one, the default, with a 4-slot ring of 2 KB rows and no
+stealing blocks; or the vector-ALU one).  Every page is compared
 bit for bit with the oracle's encoding and every decode output within the
 attention tolerance, over group sizes 1-8, ragged lengths, windows, fp16 and
 fp8 tiers (static and dynamic scales), block sizes and both input dtypes, plus
@@ -41,7 +42,7 @@ D256_CASES = [
 
 
 @pytest.mark.parametrize("dyn", [0, 1], ids=["static-fp8", "dynamic-fp8"])
-@pytest.mark.parametrize("kernel", [0, 1], ids=["default", "valu"])
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
 @pytest.mark.parametrize("name,kw,windows", D256_CASES, ids=[c[0] for c in D256_CASES])
 def test_head_dim_256(name, kw, windows, kernel, dyn):
     if dyn and "fp8" not in name.lower() and "tiers" not in name and "ragged" not in name:
@@ -66,22 +67,41 @@ def test_head_dim_256(name, kw, windows, kernel, dyn):
     cache.close()
 
 
-def test_head_dim_256_long_launch():
+@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
+def test_head_dim_256_long_launch(kernel):
     """Eight sequences of 6k-16k bfloat16 tokens, 16 query / 8 KV heads (group 2), shuffled
-    pages, full retention: several splits per (sequence, KV head), merged."""
+    pages, full retention: several splits per (sequence, KV head), merged; the matrix-core
+    waves walk their ring many times over."""
     lengths = (16384, 12000, 9001, 16000, 6000, 15999, 8192, 11111)
     w = wl.small_workload(n_q_heads=16, n_kv_heads=8, head_dim=256, dtype=wl.DTYPE_BF16, lengths=lengths,
                           page_shuffle_seed=21, number=11)
-    r = run_workload(w, page_layers=[0], decode_layers=[0])
+    r = run_workload(w, page_layers=[0], decode_layers=[0], decode_kernel=kernel)
     assert r["seqs_decoded"] == w.n_seqs
     assert r["pages"] == sum(-(-L // w.block_size) for L in lengths)
     assert r["stats"]["last_decode_splits"] > 1
-    say(f"d256 long launch: {r['stats']['last_decode_splits']} splits, max err {r['max_err']:.3e}")
+    say(f"d256 long launch ({kernel}): {r['stats']['last_decode_splits']} splits, max err {r['max_err']:.3e}")
 
 
-def test_head_dim_256_refuses_matrix_core_and_lossless():
+def test_head_dim_256_stealing_blocks_not_taken(monkeypatch):
+    """VK_DECODE_STEAL=2 asks for stealing blocks wherever the shape allows; head dim 256 has
+    no such instance, so the 4-wave blocks run and the outputs stay on the oracle."""
+    monkeypatch.setenv("VK_DECODE_STEAL", "2")
+    w = wl.small_workload(n_q_heads=8, n_kv_heads=2, head_dim=256, dtype=1, lengths=(3000,))
+    cache = make_cache(w, decode_kernel=2)
+    fill(cache, w)
+    kb, vb = host_kv(w, 0, 0)
+    enc = check_pages(cache, w, 0, 0, kb, vb, pages=[0, 1, 100, 187])
+    q = wl.queries(w, 0, device="cuda")
+    out = cache.decode(q, [0], 0, window=-1)
+    torch.cuda.synchronize()
+    assert cache.stats()["last_decode_steal"] == 0
+    say(f"d256 steal refused: max err {check_decode(out, q, w, {0: enc}, -1):.2e}")
+    cache.close()
+
+
+def test_head_dim_256_refuses_lossless():
     base = dict(n_layers=1, n_kv_heads=2, n_q_heads=4, head_dim=256, block_size=16, max_seqs=1,
-                max_tokens_per_seq=64, pages_ternary=8)
-    for bad in (dict(decode_kernel=2), dict(sink_format=wl.FMT_LOSSLESS, pages_lossless=2)):
+                max_tokens_per_seq=64, pages_ternary=8, pages_lossless=2)
+    for bad in (dict(sink_format=wl.FMT_LOSSLESS), dict(recent_tokens=16, recent_format=wl.FMT_LOSSLESS)):
         with pytest.raises(vk.VkError):
             vk.Cache(vk.make_config(**base, **bad))

@@ -61,7 +61,7 @@ def test_config_defaults():
                                  dict(block_size=8), dict(max_seqs=0), dict(sink_tokens=-1),
                                  dict(sink_format=4), dict(pages_fp8=-1), dict(pages_lossless=-1),
                                  dict(decode_kernel=1, sink_format=3), dict(eps=-1.0),
-                                 dict(head_dim=256, decode_kernel=2), dict(head_dim=256, sink_format=3),
+                                 dict(head_dim=256, sink_format=3),
                                  dict(head_dim=256, recent_tokens=16, recent_format=3),
                                  dict(fp8_scale=0.0), dict(decode_kernel=3), dict(eps=float("nan"))])
 def test_config_rejected(bad):
@@ -71,8 +71,8 @@ def test_config_rejected(bad):
 
 
 def test_head_dim_256_config():
-    """Head dim 256 is taken with the default or vector-ALU decode kernel; its pages scale with D."""
-    for kern in (0, 1):
+    """Head dim 256 is taken with every decode kernel; its pages scale with D."""
+    for kern in (0, 1, 2):
         c = base_cfg(head_dim=256, decode_kernel=kern, recent_tokens=16)
         assert vk.device_bytes(c) > vk.device_bytes(base_cfg(decode_kernel=kern, recent_tokens=16))
         assert vk.page_bytes(c, vk.FMT_TERNARY2) == 2 * 2 * 16 * 256 // 4
