@@ -592,6 +592,30 @@ __device__ __forceinline__ void va_all(const VWords<NV>& v, h4_t (&va)[NB], cons
   }
 }
 
+// Head dim 256: the value product of two units (16x16x32) or of one (16x16x16), one word pair
+// (8 blocks) at a time, each operand built just before its product: the shifted copies and the
+// operands of all 16 blocks would not fit beside the other state.
+template <int H, int J = 8 * H>
+__device__ __forceinline__ void pv2_half(const uint32_t (&a)[4], const uint32_t (&b)[4], h8_t pb, f4_t (&oacc)[16],
+                                         const OConst& o) {
+  if constexpr (J < 8 * H + 8) {
+    constexpr int p = 2 * (J % 8), w = 2 * H;
+    const uint32_t x0 = ocode2<p>(a[w], a[w] << 4, a[w] >> 6, o), x1 = ocode2<p>(a[w + 1], a[w + 1] << 4, a[w + 1] >> 6, o);
+    const uint32_t y0 = ocode2<p>(b[w], b[w] << 4, b[w] >> 6, o), y1 = ocode2<p>(b[w + 1], b[w + 1] << 4, b[w + 1] >> 6, o);
+    oacc[J] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, u4_t{x0, x1, y0, y1}), pb, oacc[J], 0, 0, 0);
+    pv2_half<H, J + 1>(a, b, pb, oacc, o);
+  }
+}
+template <int H, int J = 8 * H>
+__device__ __forceinline__ void pv1_half(const uint32_t (&a)[4], h4_t pb, f4_t (&oacc)[16], const OConst& o) {
+  if constexpr (J < 8 * H + 8) {
+    constexpr int p = 2 * (J % 8), w = 2 * H;
+    const uint32_t x0 = ocode2<p>(a[w], a[w] << 4, a[w] >> 6, o), x1 = ocode2<p>(a[w + 1], a[w + 1] << 4, a[w + 1] >> 6, o);
+    oacc[J] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, u2_t{x0, x1}), pb, oacc[J], 0, 0, 0);
+    pv1_half<H, J + 1>(a, pb, oacc, o);
+  }
+}
+
 // STEAL: one 12-wave block per (sequence, KV head, split) whose waves take pieces of the
 // block's units from a shared counter (launches of all-ternary pages with a block per CU).
 // LL: the fp8 / fp16 blocks also read lossless pages (an instance of its own, launched only when
@@ -1060,6 +1084,11 @@ void k_decode_mfma(DecodeArgs a) {
     for (int s2 = 0; s2 < SU / 2; ++s2) {
       const h8_t pb = __builtin_bit_cast(
           h8_t, u4_t{pvals(2 * s2, 0), pvals(2 * s2, 1), pvals(2 * s2 + 1, 0), pvals(2 * s2 + 1, 1)});
+      if constexpr (NV == 4) {
+        pv2_half<0>(r[2 * s2].v, r[2 * s2 + 1].v, pb, oacc, oc);
+        pv2_half<1>(r[2 * s2].v, r[2 * s2 + 1].v, pb, oacc, oc);
+        continue;
+      }
       h4_t v0[NB], v1[NB];
       va_all<NV, NB>(vwords<NV>(r[2 * s2].v), v0, oc);
       va_all<NV, NB>(vwords<NV>(r[2 * s2 + 1].v), v1, oc);
@@ -1153,6 +1182,11 @@ void k_decode_mfma(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][h]), ones, tsum, false);
       const h8_t pb = __builtin_bit_cast(h8_t, u4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]});
+      if constexpr (NV == 4) {
+        pv2_half<0>(r0.v, r1.v, pb, oacc, oc);
+        pv2_half<1>(r0.v, r1.v, pb, oacc, oc);
+        return;
+      }
       h4_t v0[NB], v1[NB];
       va_all<NV, NB>(vwords<NV>(r0.v), v0, oc);
       va_all<NV, NB>(vwords<NV>(r1.v), v1, oc);
@@ -1172,6 +1206,11 @@ void k_decode_mfma(DecodeArgs a) {
       const h4_t pb = __builtin_bit_cast(h4_t, u2_t{pk[g][0], pk[g][1]});
       tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][0]), ones, tsum, false);
       tsum = __builtin_amdgcn_fdot2(as_h2(pk[g][1]), ones, tsum, false);
+      if constexpr (NV == 4) {
+        pv1_half<0>(g == 0 ? r0.v : r1.v, pb, oacc, oc);
+        pv1_half<1>(g == 0 ? r0.v : r1.v, pb, oacc, oc);
+        continue;
+      }
       h4_t vt[NB];
       va_all<NV, NB>(vwords<NV>(g == 0 ? r0.v : r1.v), vt, oc);
 #pragma unroll
