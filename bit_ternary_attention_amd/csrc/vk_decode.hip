@@ -631,10 +631,12 @@ void k_decode_mfma(DecodeArgs a) {
   constexpr int NB = D / 16;   // 16-dimension output blocks
   constexpr int CH = 64;       // units per metadata chunk (one per lane)
   constexpr int UG = 2;        // units sharing one online-softmax update and one P*V product
-  // ternary scores on the fp4 x fp8 product: head dim 128, bfloat16 queries (two e4m3 terms
-  // hold one exactly; f16 queries would need a third term's registers and keep the f16 product)
-  constexpr bool F4 = D == 128 && QDT == 1;
-  constexpr int NQ = 2;  // e4m3 terms of the query
+  // ternary scores on the fp4 x fp8 product: head dims 128 and 256, bfloat16 queries (two e4m3
+  // terms hold one exactly; f16 queries would need a third term's registers and keep the f16
+  // product)
+  constexpr bool F4 = (D == 128 || D == 256) && QDT == 1;
+  constexpr int NQ = 2;       // e4m3 terms of the query
+  constexpr int NH = D >= 128 ? D / 128 : 1;  // fp4 products per term (128 dimensions each)
   // ternary logit = ks (kmul acc - qoff): kmul 2 for the fp4 product, 2^14 for the f16 one
   using ProdF4 = std::integral_constant<bool, F4>;  // long ranges: the fp4 product where built
   using ProdF16 = std::false_type;                  // short ranges: the f16 product, whose
@@ -850,61 +852,71 @@ void k_decode_mfma(DecodeArgs a) {
     qsum = sum;
     qoff = 16384.0f * koff + sum;  // logit = ks (2^14 acc - qoff) for offset-form codes
   };
-  // The query as NQ e4m3 terms, the B operands of the fp4 x fp8 score product (head dim 128,
-  // ternary blocks).  The product pairs nibble n of word v of an A lane of group g (key
-  // dimension 32 g + 16 (v / 2) + 2 n + v % 2, from tern_score) with byte 16 (g / 2) + 8 (v % 2)
-  // + n of a B lane of group 2 (g % 2) + v / 2; so B lane group g holds, in bytes jb and
-  // 16 + jb (jb < 16), dimensions 16 g + e(jb) and 64 + 16 g + e(jb), e(jb) = 2 (jb % 8) + jb / 8.
-  v8i_t qf[NQ];
+  // The query as NQ e4m3 terms, the B operands of the fp4 x fp8 score product (ternary
+  // blocks).  The product pairs nibble n of word v of an A lane of group g (product dimension
+  // 32 g + 16 (v / 2) + 2 n + v % 2, from tern_score) with byte 16 (g / 2) + 8 (v % 2) + n of a
+  // B lane of group 2 (g % 2) + v / 2; so B lane group g holds, in bytes jb and 16 + jb
+  // (jb < 16), product dimensions 16 g + e(jb) and 64 + 16 g + e(jb), e(jb) = 2 (jb % 8) +
+  // jb / 8.  Head dim 128: product dimension = head dimension.  Head dim 256 takes two
+  // products; product h pairs each A lane's words 2h, 2h + 1, so its dimension p is head
+  // dimension 64 (p / 32) + 32 h + p % 32, and the 16 dimensions 64 c + 16 g + [0, 16) of B
+  // lane group g are head dimensions 128 c + 64 (g / 2) + 32 h + 16 (g % 2) + [0, 16).
+  v8i_t qf[NH][NQ];
   auto make_qf = [&]() {
     asm volatile("" ::: "memory");  // (as in make_qb)
-    uint32_t x[2][8];
+    uint32_t x[NH][2][8];
     float qmax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint16_t* qrow = qhead + 64 * c + 16 * grp;
-      const uint4 lo = reinterpret_cast<const uint4*>(qrow)[0];  // dims +0 .. +7
-      const uint4 hi = reinterpret_cast<const uint4*>(qrow)[1];  // dims +8 .. +15
-      const uint32_t all[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[c][i] = all[i];
+      for (int c = 0; c < 2; ++c) {
+        const uint16_t* qrow =
+            qhead + (NH == 1 ? 64 * c + 16 * grp : 128 * c + 64 * (grp >> 1) + 32 * h + 16 * (grp & 1));
+        const uint4 lo = reinterpret_cast<const uint4*>(qrow)[0];  // dims +0 .. +7
+        const uint4 hi = reinterpret_cast<const uint4*>(qrow)[1];  // dims +8 .. +15
+        const uint32_t all[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        qmax = fmaxf(qmax, fabsf(q_value<QDT>(static_cast<uint16_t>((all[i >> 1] >> (16 * (i & 1))) & 0xFFFFu))));
-    }
+        for (int i = 0; i < 8; ++i) x[h][c][i] = all[i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          qmax = fmaxf(qmax, fabsf(q_value<QDT>(static_cast<uint16_t>((all[i >> 1] >> (16 * (i & 1))) & 0xFFFFu))));
+      }
     const int qsh = __builtin_amdgcn_readfirstlane(q_shift<6>(wave_max(qmax)));
     const float qmul = pow2i(qsh);
     qsl = a.scale_log2 * pow2i(-qsh);
-    uint32_t w[NQ][8];
     float sum = 0.0f;
 #pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) {  // operand word t8: bytes (slots) 4 t8 .. 4 t8 + 3
-      float r[4];
+    for (int h = 0; h < NH; ++h) {
+      uint32_t w[NQ][8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = 4 * t8 + k, c = j >> 4, i = 2 * (j & 7) + ((j >> 3) & 1);  // dimension 64 c + 16 grp + i
-        r[k] = q_value<QDT>(static_cast<uint16_t>((x[c][i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) * qmul;
-      }
-#pragma unroll
-      for (int t = 0; t < NQ; ++t) {  // term t, stored at 2^(4 t): four bytes by two packed converts
-        const float up = pow2i(4 * t), down = pow2i(-4 * t);
-        int e = __builtin_amdgcn_cvt_pk_fp8_f32(r[0] * up, r[1] * up, 0, false);
-        e = __builtin_amdgcn_cvt_pk_fp8_f32(r[2] * up, r[3] * up, e, true);
-        const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(e, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(e, true);
-        const float back[4] = {lo[0] * down, lo[1] * down, hi[0] * down, hi[1] * down};  // the term's values
+      for (int t8 = 0; t8 < 8; ++t8) {  // operand word t8: bytes (slots) 4 t8 .. 4 t8 + 3
+        float r[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          r[k] -= back[k];
-          sum += back[k];
+          const int j = 4 * t8 + k, c = j >> 4, i = 2 * (j & 7) + ((j >> 3) & 1);  // product dimension 64 c + 16 grp + i
+          r[k] = q_value<QDT>(static_cast<uint16_t>((x[h][c][i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) * qmul;
         }
-        w[t][t8] = static_cast<uint32_t>(e);
-      }
-    }
 #pragma unroll
-    for (int t = 0; t < NQ; ++t)
-      qf[t] = v8i_t{static_cast<int>(w[t][0]), static_cast<int>(w[t][1]), static_cast<int>(w[t][2]),
-                    static_cast<int>(w[t][3]), static_cast<int>(w[t][4]), static_cast<int>(w[t][5]),
-                    static_cast<int>(w[t][6]), static_cast<int>(w[t][7])};
+        for (int t = 0; t < NQ; ++t) {  // term t, stored at 2^(4 t): four bytes by two packed converts
+          const float up = pow2i(4 * t), down = pow2i(-4 * t);
+          int e = __builtin_amdgcn_cvt_pk_fp8_f32(r[0] * up, r[1] * up, 0, false);
+          e = __builtin_amdgcn_cvt_pk_fp8_f32(r[2] * up, r[3] * up, e, true);
+          const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(e, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(e, true);
+          const float back[4] = {lo[0] * down, lo[1] * down, hi[0] * down, hi[1] * down};  // the term's values
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            r[k] -= back[k];
+            sum += back[k];
+          }
+          w[t][t8] = static_cast<uint32_t>(e);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+        qf[h][t] = v8i_t{static_cast<int>(w[t][0]), static_cast<int>(w[t][1]), static_cast<int>(w[t][2]),
+                         static_cast<int>(w[t][3]), static_cast<int>(w[t][4]), static_cast<int>(w[t][5]),
+                         static_cast<int>(w[t][6]), static_cast<int>(w[t][7])};
+    }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
     qsum = sum;
@@ -930,11 +942,15 @@ void k_decode_mfma(DecodeArgs a) {
     f4_t s4 = {0.f, 0.f, 0.f, 0.f};
     if constexpr (decltype(PRD)::value) {
       constexpr uint32_t M = 0x33333333u;  // the even 2-bit fields, one per nibble
-      const v8i_t ak = {static_cast<int>(k[0] & M), static_cast<int>((k[0] >> 2) & M),
-                        static_cast<int>(k[NC - 1] & M), static_cast<int>((k[NC - 1] >> 2) & M), 0, 0, 0, 0};
 #pragma unroll
-      for (int t = 0; t < NQ; ++t)
-        s4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ak, qf[t], s4, 4, 0, 0, 127, 0, 127 - 4 * t);
+      for (int h = 0; h < NH; ++h) {  // product h: words 2h, 2h + 1 of the lane's key slice
+        const uint32_t k0 = k[2 * h], k1 = k[2 * h + 1];
+        const v8i_t ak = {static_cast<int>(k0 & M), static_cast<int>((k0 >> 2) & M),
+                          static_cast<int>(k1 & M), static_cast<int>((k1 >> 2) & M), 0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < NQ; ++t)
+          s4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ak, qf[h][t], s4, 4, 0, 0, 127, 0, 127 - 4 * t);
+      }
     } else {
       h8_t ka[NS];
       ka_ternary<NS, NC>(k, ka, oc);

@@ -1,7 +1,8 @@
 """Repeatability of the matrix-core decode, whose pages are staged through an LDS ring
 filled by buffer-to-LDS copies: the same call gives bit-identical outputs every time, at
-both ring depths, and agrees with the vector-ALU kernel on every sequence (2e-4, far
-below the 2e-3 parity bar: the two kernels only round differently).  A read of a ring slot
+both ring depths (head dim 256 has one, its 4-slot ring), and agrees with the vector-ALU
+kernel on every sequence (2e-4, far below the 2e-3 parity bar: the two kernels only round
+differently).  A read of a ring slot
 before its copy has landed shows up here as run-to-run differences.
 """
 import os
@@ -18,7 +19,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-@pytest.mark.parametrize("number", [4, 5])
+@pytest.mark.parametrize("number", [4, 5, 6])
 def test_mfma_decode_repeats_bit_identically(number):
     w = wl.workload(number)
     q = wl.queries(w, 0, device="cuda")
