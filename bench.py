@@ -210,11 +210,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16 in; 2-bit codes (4 per u8); scores fp4 codes x two e4m3 query terms (head dim 128, "
-                  "bf16 queries; f16 operands otherwise), P*V f16-operand MFMA; f32 accumulate and softmax"),
+        "dtype": ("bf16 in; 2-bit codes (4 per u8); scores fp4 codes x two e4m3 query terms (head dims 128 "
+                  "and 256, bf16 queries; f16 operands otherwise), P*V f16-operand MFMA; f32 accumulate and softmax"),
         "dtype_detail": ("write side: 16-bit inputs, float64 absmean sums, codes by integer thresholds equal to "
                          "float32 RoundClip(x / (gamma + eps)); decode: ternary key codes as e2m1 operands against "
-                         "the bf16 query held exactly as two e4m3 terms (scaled MFMA, head dim 128), other keys, "
+                         "the bf16 query held exactly as two e4m3 terms (scaled MFMA, head dims 128 and 256), other keys, "
                          "the values and f16 queries as f16 operands, probabilities as f16 (scaled by 2^14), "
                          "f32 scores, softmax state and accumulation"),
         "data": "synthetic (seeded torch.randn, see bit_ternary_attention_amd/workloads.py)",

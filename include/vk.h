@@ -201,9 +201,8 @@ VK_API vk_status vk_append_ragged(vk_cache* c, int32_t layer_begin, int32_t n_la
  *    queries of one (sequence, KV head) are scaled by one power of two before
  *    the products and the scores by its inverse, so bf16 queries beyond the f16
  *    range are taken exactly.  f16 operands (the largest magnitude brought to
- *    [2^14, 2^15)) for f16 queries, head_dim 64 and 256 and pages other than
- *    ternary;
- *    ternary keys at head_dim 128 with bf16 queries meet the query as the sum of
+ *    [2^14, 2^15)) for f16 queries, head_dim 64 and pages other than ternary;
+ *    ternary keys at head_dim 128 and 256 with bf16 queries meet the query as the sum of
  *    two e4m3 terms (largest magnitude in [2^6, 2^7)), which hold every element
  *    of at least 2^-12 times the largest exactly and the smaller ones to within
  *    2^-20 times the largest.
