@@ -111,6 +111,34 @@ SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blo
   return {static_cast<int32_t>(cdiv(max_units, ups)), static_cast<int32_t>(ups)};
 }
 
+bool plan_decode_order(const int32_t* units, const int64_t* mix_weight, int32_t n_seqs, int32_t n_splits,
+                       int32_t units_per_split, int32_t n_mix, int32_t max_entries, std::vector<uint16_t>* order) {
+  order->clear();
+  const int32_t n_parts = n_splits + n_mix;
+  const int64_t n = static_cast<int64_t>(n_seqs) * n_parts;
+  if (n_seqs < 1 || n_seqs > 256 || n_parts < 1 || n_parts > 255 || n > max_entries) return false;
+  std::vector<std::pair<int64_t, uint16_t>> items;  // (weight, entry) in the default order
+  items.reserve(static_cast<size_t>(n));
+  for (int32_t z = 0; z < n_parts; ++z) {
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      const int64_t w = z < n_splits ? std::clamp<int64_t>(static_cast<int64_t>(units[i]) -
+                                                               static_cast<int64_t>(z) * units_per_split,
+                                                           0, units_per_split)
+                                     : mix_weight[i];
+      items.emplace_back(w, static_cast<uint16_t>((z << 8) | i));
+    }
+  }
+  std::stable_sort(items.begin(), items.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+  bool same = true;
+  for (int64_t k = 0; k < n; ++k) {
+    const int32_t z = static_cast<int32_t>(k / n_seqs), i = static_cast<int32_t>(k % n_seqs);
+    same &= items[k].second == static_cast<uint16_t>((z << 8) | i);
+  }
+  if (same) return false;
+  for (const auto& it : items) order->push_back(it.second);
+  return true;
+}
+
 HostState::HostState(const vk_cache_config& cfg) : cfg_(cfg) {
   max_pages_ = static_cast<int32_t>(cdiv(cfg.max_tokens_per_seq, cfg.block_size));
   seqs_.resize(cfg.max_seqs);

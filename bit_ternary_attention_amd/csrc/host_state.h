@@ -107,6 +107,18 @@ struct SplitPlan {
 SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blocks, int32_t max_splits,
                       int32_t min_units, int32_t granule = 1);
 
+// Dispatch order of a matrix-core decode launch over sequences of different lengths: every
+// (sequence i, part z) block of the launch once, heaviest first (the longest-processing-time
+// rule: the hardware hands the next block to whichever compute-unit slot frees up, so the large
+// blocks start first and the small ones fill the tail).  Split z of sequence i weighs the units
+// it takes, clamp(units[i] - z * units_per_split, 0, units_per_split); each of the n_mix fp8 /
+// fp16 parts weighs mix_weight[i] (0 when the sequence has no such pages).  Equal weights keep
+// the default order (part-major, then sequence).  Entries are (part << 8) | i.  Returns false
+// (and leaves `order` empty) when the result is the default order or has more than max_entries
+// entries: the launch then keeps its plain grid.
+bool plan_decode_order(const int32_t* units, const int64_t* mix_weight, int32_t n_seqs, int32_t n_splits,
+                       int32_t units_per_split, int32_t n_mix, int32_t max_entries, std::vector<uint16_t>* order);
+
 class HostState {
  public:
   explicit HostState(const vk_cache_config& cfg);

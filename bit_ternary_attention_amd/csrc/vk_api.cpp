@@ -61,6 +61,24 @@ int decode_mixed_parts() {
   const int v = e ? std::atoi(e) : 0;
   return v >= 1 && v <= kDecodeMixedPartsMax ? v : 1;
 }
+// Launches over sequences of different lengths (or with fp8 / fp16 parts) dispatch their blocks
+// heaviest first from an order table.  VK_DECODE_ORDER=0 keeps the plain grid;
+// VK_DECODE_BLOCKS_PER_CU_RAGGED=1..8 sets such launches' split target (default: as the others);
+// VK_DECODE_MIX_FIXED=n: an fp8 / fp16 part weighs n units beyond its pages' bytes in 1 KB units.
+bool decode_order_on() {
+  const char* e = std::getenv("VK_DECODE_ORDER");
+  return !(e && e[0] == '0');
+}
+int decode_blocks_per_cu_ragged() {
+  const char* e = std::getenv("VK_DECODE_BLOCKS_PER_CU_RAGGED");
+  const int v = e ? std::atoi(e) : 0;
+  return v >= 1 && v <= 8 ? v : decode_blocks_per_cu();
+}
+int64_t decode_mix_fixed() {
+  const char* e = std::getenv("VK_DECODE_MIX_FIXED");
+  const long long v = e ? std::atoll(e) : -1;
+  return v >= 0 ? v : 0;
+}
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
   const char* e = std::getenv("VK_DECODE_UPI");
   return (e && e[0] == '4') ? 4 : 8;
@@ -619,8 +637,9 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     a.kernel = mfma ? VK_DECODE_MFMA : VK_DECODE_VALU;
     a.units_per_iter = d256 ? 4 : decode_units_per_iter();
     a.scale_log2 = scale * 1.4426950408889634f;
-    int32_t max_units = 0;
+    int32_t max_units = 0, min_units = 0;
     int64_t cu[4] = {0, 0, 0, 0};  // attended units per format in this launch
+    int64_t other_kb[vk::kDecodeMaxSeqs];  // fp8 / fp16 units' bytes per head, in ternary units'
     // longest attended ranges first: their blocks are dispatched first, shorter ones fill in
     int32_t order[vk::kDecodeMaxSeqs], units_of[vk::kDecodeMaxSeqs];
     for (int32_t i = 0; i < nb; ++i) {
@@ -629,13 +648,17 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       order[i] = i;
     }
     std::stable_sort(order, order + nb, [&](int32_t x, int32_t y) { return units_of[x] > units_of[y]; });
+    min_units = nb > 0 ? units_of[order[nb - 1]] : 0;
     for (int32_t i = 0; i < nb; ++i) {
       const int32_t sid = seq_ids[base + order[i]];
       a.slots[i] = sid;
       a.lens[i] = c->host->seq(sid).length;
       a.rows[i] = order[i];
       max_units = std::max(max_units, units_of[order[i]]);
-      c->host->count_units(sid, window, cu);
+      int64_t cs[4] = {0, 0, 0, 0};
+      c->host->count_units(sid, window, cs);
+      for (int f = 0; f < 4; ++f) cu[f] += cs[f];
+      other_kb[i] = cs[1] * 4 + cs[2] * 8;
       c->host->mixed_ranges(sid, window, a.mix[i]);
     }
     for (int f = 0; f < 4; ++f) units[f] += cu[f];
@@ -656,7 +679,9 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     // Splits hold a fixed number of units, so long sequences get more of them than short
     // ones (a block past a sequence's units writes an empty part).
     const int64_t all_units = (cu[0] + cu[1] + cu[2]) * cfg.n_kv_heads;
-    const int32_t target_blocks = static_cast<int32_t>(std::max(1, c->n_cu) * decode_blocks_per_cu());
+    const bool ragged = mfma && (max_units != min_units || n_fp > 0);
+    const int32_t target_blocks =
+        static_cast<int32_t>(std::max(1, c->n_cu) * (ragged ? decode_blocks_per_cu_ragged() : decode_blocks_per_cu()));
     const vk::SplitPlan sp = mfma ? vk::plan_splits(all_units, max_units, target_blocks,
                                                     std::max(1, max_splits), 4 * kDecodeMinUnitsPerWave,
                                                     4 * kDecodeUnitsPerStep)
@@ -677,6 +702,21 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       a.steal = 1;
     }
     a.n_parts = a.n_splits + n_mix;
+    a.n_order = 0;
+    if (ragged && !a.steal && decode_order_on()) {
+      int32_t u_launch[vk::kDecodeMaxSeqs];
+      int64_t w_mix[vk::kDecodeMaxSeqs];
+      const int64_t fixed = decode_mix_fixed();
+      for (int32_t i = 0; i < nb; ++i) {
+        u_launch[i] = units_of[order[i]];
+        w_mix[i] = other_kb[i] > 0 ? fixed + (other_kb[i] + n_fp - 1) / std::max(1, n_fp) : 0;
+      }
+      std::vector<uint16_t> ord;
+      if (vk::plan_decode_order(u_launch, w_mix, nb, a.n_splits, a.units_per_split, n_fp, vk::kDecodeMaxOrder, &ord)) {
+        a.n_order = static_cast<int32_t>(ord.size());
+        std::copy(ord.begin(), ord.end(), a.order);
+      }
+    }
     if (items * a.n_parts > kDecodeScratchItems)  // (only with thousands of KV heads)
       return fail(VK_ERR_CAPACITY, "decode partial states: %lld needed, %lld held", static_cast<long long>(items * a.n_parts),
                   static_cast<long long>(kDecodeScratchItems));

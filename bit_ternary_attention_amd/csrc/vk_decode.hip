@@ -678,8 +678,12 @@ void k_decode_mfma(DecodeArgs a) {
   const int lane = threadIdx.x & 63, grp = lane >> 4, c16 = lane & 15;
   const int cslot = c16 / W;  // this lane's column slot
   // grid (KV head, sequence, split): blocks dispatched together read the heads' slices of the
-  // same pages
-  const int split = blockIdx.z + a.part_base, kvh = blockIdx.x, b = blockIdx.y;
+  // same pages.  With a dispatch order (launches of sequences of different lengths) the grid is
+  // (KV head, order index) and entry y of the order names the sequence and the part.
+  const uint32_t ord = a.n_order > 0 ? static_cast<uint32_t>(a.order[blockIdx.y]) : 0u;
+  const int kvh = blockIdx.x;
+  const int b = a.n_order > 0 ? static_cast<int>(ord & 0xFFu) : static_cast<int>(blockIdx.y);
+  const int split = (a.n_order > 0 ? static_cast<int>(ord >> 8) : static_cast<int>(blockIdx.z)) + a.part_base;
   const int slot = a.slots[b], L = a.lens[b];
   const PoolsView& P = a.P;
   // The kernel arguments the set-up reads, loaded in one batch: left to the compiler, the
@@ -1920,7 +1924,11 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   // matrix-core path: grid (hkv, n_seqs, n_parts), parts n_splits .. take the fp8 / fp16 pages;
   // vector-ALU path: grid (n_splits, hkv, n_seqs)
   const dim3 grid = a.kernel == VK_DECODE_VALU ? dim3(a.n_splits, a.P.hkv, a.n_seqs)
-                                               : dim3(a.P.hkv, a.n_seqs, a.n_splits + a.n_mix_parts);
+                   : a.n_order > 0               ? dim3(a.P.hkv, a.n_order, 1)
+                                                 : dim3(a.P.hkv, a.n_seqs, a.n_splits + a.n_mix_parts);
+  if (a.n_order > 0 && (a.kernel == VK_DECODE_VALU || a.steal ||
+                        a.n_order != a.n_seqs * (a.n_splits + a.n_mix_parts)))
+    return hipErrorInvalidValue;
   if (t) t->begin(VK_KERNEL_DECODE, s);
   if (a.kernel == VK_DECODE_VALU) {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode<D, G, 1><<<grid, 64, 0, s>>>(a);
@@ -1941,6 +1949,7 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   if (a.lossless) {  // the lossless pages: one block per (KV head, sequence), part n_splits + n_mix_parts
     DecodeArgs b = a;
     b.part_base = a.n_splits + a.n_mix_parts;
+    b.n_order = 0;
     const dim3 g1(a.P.hkv, a.n_seqs, 1);
     if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<D, G, 1, 8, false, false, true><<<g1, 64 * kMfmaWaves, 0, s>>>(b);
     else k_decode_mfma<D, G, 0, 8, false, false, true><<<g1, 64 * kMfmaWaves, 0, s>>>(b);
@@ -1971,6 +1980,8 @@ hipError_t launch_d(const DecodeArgs& a, int32_t group, hipStream_t s, LaunchTim
 template <int G>
 hipError_t launch_d256(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
   if (a.lossless || a.steal) return hipErrorInvalidValue;
+  if (a.n_order > 0 && (a.kernel == VK_DECODE_VALU || a.n_order != a.n_seqs * (a.n_splits + a.n_mix_parts)))
+    return hipErrorInvalidValue;
   if (t) t->begin(VK_KERNEL_DECODE, s);
   if (a.kernel == VK_DECODE_VALU) {
     if (a.n_mix_parts) return hipErrorInvalidValue;
@@ -1978,7 +1989,7 @@ hipError_t launch_d256(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
     if (a.q_dtype == VK_DTYPE_BF16) k_decode<256, G, 1><<<grid, 64, 0, s>>>(a);
     else k_decode<256, G, 0><<<grid, 64, 0, s>>>(a);
   } else {
-    const dim3 grid(a.P.hkv, a.n_seqs, a.n_splits + a.n_mix_parts);
+    const dim3 grid = a.n_order > 0 ? dim3(a.P.hkv, a.n_order, 1) : dim3(a.P.hkv, a.n_seqs, a.n_splits + a.n_mix_parts);
     if (a.P.fp8_dynamic) {
       if (a.q_dtype == VK_DTYPE_BF16) k_decode_mfma<256, G, 1, 4, true, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);
       else k_decode_mfma<256, G, 0, 4, true, false><<<grid, 64 * kMfmaWaves, 0, s>>>(a);

@@ -66,6 +66,7 @@ struct AppendArgs {
 };
 
 constexpr int kDecodeMaxSeqs = 64;    // sequences per decode launch (kernel-argument table)
+constexpr int kDecodeMaxOrder = 768;  // entries of a decode launch's dispatch order (kernel arguments)
 constexpr int kDecodeUnitsPerIter = 4;
 
 struct DecodeArgs {
@@ -97,7 +98,13 @@ struct DecodeArgs {
   int32_t lens[kDecodeMaxSeqs];
   int32_t rows[kDecodeMaxSeqs];    // query / output row (within the launch) of each
   int32_t mix[kDecodeMaxSeqs][4];  // two logical-unit ranges holding every fp8 / fp16 unit
+  // Matrix-core path, optional: the launch's blocks in dispatch order, (part << 8) | sequence
+  // index per entry, every (sequence, part) once; the grid is then (hkv, n_order).  0 = the
+  // grid (hkv, n_seqs, n_parts) in that order.
+  int32_t n_order;
+  uint16_t order[kDecodeMaxOrder];
 };
+static_assert(sizeof(DecodeArgs) <= 4096, "decode kernel arguments within 4 KB");
 
 struct QuantArgs {
   const uint16_t* x;

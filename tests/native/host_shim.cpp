@@ -113,4 +113,15 @@ int hs_plan_splits(long long total_units, int max_units, int target, int max_spl
   *units_per_split = p.units_per_split;
   return p.n_splits;
 }
+
+// dispatch order of a decode launch: returns the entry count (0 = the plain grid's order)
+int hs_plan_decode_order(const int* units, const long long* mix_weight, int n_seqs, int n_splits,
+                         int units_per_split, int n_mix, int max_entries, unsigned short* out) {
+  std::vector<int64_t> w(mix_weight, mix_weight + n_seqs);
+  std::vector<uint16_t> order;
+  if (!vk::plan_decode_order(units, w.data(), n_seqs, n_splits, units_per_split, n_mix, max_entries, &order))
+    return 0;
+  for (size_t k = 0; k < order.size(); ++k) out[k] = order[k];
+  return static_cast<int>(order.size());
+}
 }

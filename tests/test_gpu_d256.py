@@ -41,12 +41,20 @@ D256_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dyn", [0, 1], ids=["static-fp8", "dynamic-fp8"])
-@pytest.mark.parametrize("kernel", [2, 1], ids=["mfma", "valu"])
-@pytest.mark.parametrize("name,kw,windows", D256_CASES, ids=[c[0] for c in D256_CASES])
+def _has_fp8(kw):
+    return oc.FP8E4M3 in (kw.get("sink_format"), kw.get("recent_format"))
+
+
+# dynamic FP8 scales only where the case holds fp8 pages
+D256_PARAMS = [pytest.param(name, kw, windows, kernel, dyn,
+                            id=f"{name}-{kid}-{'dynamic' if dyn else 'static'}-fp8")
+               for name, kw, windows in D256_CASES
+               for kernel, kid in ((2, "mfma"), (1, "valu"))
+               for dyn in ((0, 1) if _has_fp8(kw) else (0,))]
+
+
+@pytest.mark.parametrize("name,kw,windows,kernel,dyn", D256_PARAMS)
 def test_head_dim_256(name, kw, windows, kernel, dyn):
-    if dyn and "fp8" not in name.lower() and "tiers" not in name and "ragged" not in name:
-        pytest.skip("no fp8 pages in this case")
     w = wl.small_workload(head_dim=256, **kw)
     say(f"d256 {name} kernel {kernel} dynamic fp8 {dyn}: {w}")
     cache = make_cache(w, decode_kernel=kernel, fp8_dynamic=dyn)

@@ -140,6 +140,8 @@ def hs():
     L.hs_check_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), ctypes.c_int]
     L.hs_plan_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.hs_plan_decode_order.argtypes = [P(ctypes.c_int), P(ctypes.c_longlong), ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, P(ctypes.c_ushort)]
     return L
 
 
@@ -535,3 +537,38 @@ def test_two_e4m3_terms_hold_scaled_bfloat16_queries():
     assert big.sum() > 3000
     assert np.all(err[big] == 0.0)
     assert np.all(err[~big] <= 2.0 ** -14)
+
+
+def _order(hs, units, mix_w, n_splits, ups, n_mix, max_entries=768):
+    n = len(units)
+    out = (ctypes.c_ushort * max(1, n * (n_splits + n_mix)))()
+    k = hs.hs_plan_decode_order((ctypes.c_int * n)(*units), (ctypes.c_longlong * n)(*mix_w), n, n_splits, ups,
+                                n_mix, max_entries, out)
+    return [(out[j] >> 8, out[j] & 0xFF) for j in range(k)]
+
+
+def test_decode_dispatch_order(hs):
+    # equal lengths, no fp8 / fp16 parts: the plain grid order already is heaviest first
+    assert _order(hs, [512] * 4, [0] * 4, 2, 256, 0) == []
+    # brute force over small launches: every (part, sequence) once, weights never increase along
+    # the order, equal weights in the plain order (part-major, then sequence)
+    rng = __import__("random").Random(5)
+    for _ in range(300):
+        n = rng.randint(1, 9)
+        ups = rng.choice([16, 32, 48])
+        units = sorted((rng.randint(0, 200) for _ in range(n)), reverse=True)
+        n_splits = max(1, -(-max(units) // ups))
+        n_mix = rng.choice([0, 1, 2])
+        mix_w = [rng.choice([0, 5, 40, 300]) for _ in range(n)]
+        got = _order(hs, units, mix_w, n_splits, ups, n_mix)
+        plain = [(z, i) for z in range(n_splits + n_mix) for i in range(n)]
+        w = {(z, i): (min(max(units[i] - z * ups, 0), ups) if z < n_splits else mix_w[i]) for z, i in plain}
+        want = sorted(plain, key=lambda zi: -w[zi])  # (sorted is stable)
+        assert got == ([] if want == plain else want)
+        if got:
+            assert sorted(got) == plain
+    # a hand-worked launch: lengths 100 and 30 units in 64-unit splits, one fp8 part of weight 50
+    # on the second sequence: (0,0)=64, (0,1)=30, (1,0)=36, (1,1)=0, mix (2,0)=0, (2,1)=50
+    assert _order(hs, [100, 30], [0, 50], 2, 64, 1) == [(0, 0), (2, 1), (1, 0), (0, 1), (1, 1), (2, 0)]
+    # too many entries for the kernel-argument table: the plain grid
+    assert _order(hs, [100, 30], [0, 50], 2, 64, 1, max_entries=5) == []
