@@ -1238,26 +1238,61 @@ void k_decode_mfma(DecodeArgs a) {
     }
   };
 
-  // A operands and scales of a non-ternary unit, loaded here (f16 values, not u * 2^-14).
-  // ks[r]: factor of the score of token 4 grp + r (applied to the float32 product); rt[r]:
-  // factor of that token's probability in P*V; vscale: factor of the unit's P*V sum.  Dynamic
-  // FP8 gives every token its own scales: ks = s_t, rt = s_t / s_max (at most 1: no f16
-  // overflow) and vscale = s_max for the values.  Only attended tokens count towards s_max:
-  // a slot past the sequence may hold a stale scale of a recycled page.
-  auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float (&ks)[4], float (&rt)[4],
-                            float& vscale) {
+  // Raw words of one fp8 / fp16 unit as loaded, before any conversion, so that a wave can have
+  // the next unit's loads in flight while it computes one (fp8: k[0, NC) and v[j].x).
+  struct OtherRaw {
+    uint4 k[2 * NC];
+    uint2 v[NB];
+    float4 ks4, vs4;  // dynamic FP8: the token scales of this lane's score and value rows
+  };
+  auto load_other = [&](int lu, int32_t entry, OtherRaw& r) {
     const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
     const int64_t idx = entry & 0x3FFFFFFF;
     const int upi = ((unit_of(lu) * 16) & (P.bs - 1)) >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ks[r] = 1.0f, rt[r] = 1.0f;
-    vscale = 1.0f;
-    if (fmt == VK_FMT_FP8E4M3) {
+    if (fmt != VK_FMT_F16) {  // fp8 (the words fp8 units use of OtherRaw: 16 registers, + 8 dynamic)
       const uint8_t* pg = P.pool[1] + (layer * P.cap[1] + idx) * P.page_bytes[1];
       const uint4* kp = reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[1] + (upi * 16 + c16) * D + dbase);
 #pragma unroll
+      for (int c = 0; c < NC; ++c) r.k[c] = kp[c];
+      const uint8_t* vt = pg + (P.hkv + kvh) * P.tile_bytes[1];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        r.v[j].x = *reinterpret_cast<const uint32_t*>(vt + static_cast<int64_t>(16 * j + c16) * P.bs + upi * 16 + 4 * grp);
+      if constexpr (DYN) {
+        // token scales after each tile's codes; this lane's score and value rows are tokens
+        // 4 grp .. 4 grp + 3
+        const int64_t so = static_cast<int64_t>(P.bs) * D + 4 * (upi * 16 + 4 * grp);
+        r.ks4 = *reinterpret_cast<const float4*>(pg + kvh * P.tile_bytes[1] + so);
+        r.vs4 = *reinterpret_cast<const float4*>(vt + so);
+      }
+    } else {
+      const uint8_t* pg = P.pool[2] + (layer * P.cap[2] + idx) * P.page_bytes[2];
+      const uint4* kp =
+          reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[2] + ((upi * 16 + c16) * D + dbase) * 2);
+#pragma unroll
+      for (int c = 0; c < 2 * NC; ++c) r.k[c] = kp[c];
+      const uint8_t* vt = pg + (P.hkv + kvh) * P.tile_bytes[2];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        r.v[j] = *reinterpret_cast<const uint2*>(vt + (static_cast<int64_t>(16 * j + c16) * P.bs + upi * 16 + 4 * grp) * 2);
+    }
+  };
+  // The A operands and scales of an fp8 / fp16 unit from its raw words (f16 values, not
+  // u * 2^-14).  ks[r]: factor of the score of token 4 grp + r (applied to the float32 product);
+  // rt[r]: factor of that token's probability in P*V; vscale: factor of the unit's P*V sum.
+  // Dynamic FP8 gives every token its own scales: ks = s_t, rt = s_t / s_max (at most 1: no f16
+  // overflow) and vscale = s_max for the values.  Only attended tokens count towards s_max: a
+  // slot past the sequence may hold a stale scale of a recycled page.
+  auto convert_other = [&](int lu, int32_t entry, const OtherRaw& r, h8_t (&ka)[NS], h4_t (&va)[NB],
+                           float (&ks)[4], float (&rt)[4], float& vscale) {
+    const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ks[i] = 1.0f, rt[i] = 1.0f;
+    vscale = 1.0f;
+    if (fmt == VK_FMT_FP8E4M3) {
+#pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint4 x = kp[c];
+        const uint4 x = r.k[c];
         const uint32_t lo[2] = {x.x, x.y}, hi[2] = {x.z, x.w};
         uint32_t t[8];
 #pragma unroll
@@ -1269,36 +1304,63 @@ void k_decode_mfma(DecodeArgs a) {
         ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{t[0], t[1], t[2], t[3]});
         ka[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{t[4], t[5], t[6], t[7]});
       }
-      const uint8_t* vt = pg + (P.hkv + kvh) * P.tile_bytes[1];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const uint32_t x =
-            *reinterpret_cast<const uint32_t*>(vt + static_cast<int64_t>(16 * j + c16) * P.bs + upi * 16 + 4 * grp);
+        const uint32_t x = r.v[j].x;
         va[j] = __builtin_bit_cast(h4_t, u2_t{h2u(fp8x2((x & 0xFFu) | ((x & 0xFF00u) << 8))),
                                               h2u(fp8x2(((x >> 16) & 0xFFu) | ((x >> 8) & 0x00FF0000u)))});
       }
       if constexpr (!DYN) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ks[r] = P.fp8_scale;
+        for (int i = 0; i < 4; ++i) ks[i] = P.fp8_scale;
         vscale = P.fp8_scale;
       } else {
-        // token scales after each tile's codes; this lane's score and value rows are tokens
-        // 4 grp .. 4 grp + 3
         const int t0 = unit_of(lu) * 16;
-        const int64_t so = static_cast<int64_t>(P.bs) * D + 4 * (upi * 16 + 4 * grp);
-        const float4 k4 = *reinterpret_cast<const float4*>(pg + kvh * P.tile_bytes[1] + so);
-        ks[0] = k4.x; ks[1] = k4.y; ks[2] = k4.z; ks[3] = k4.w;
-        const float4 v4 = *reinterpret_cast<const float4*>(vt + so);
-        float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        ks[0] = r.ks4.x; ks[1] = r.ks4.y; ks[2] = r.ks4.z; ks[3] = r.ks4.w;
+        float vv[4] = {r.vs4.x, r.vs4.y, r.vs4.z, r.vs4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vv[r] = attended_tok(t0 + 4 * grp + r) ? vv[r] : 0.0f;
+        for (int i = 0; i < 4; ++i) vv[i] = attended_tok(t0 + 4 * grp + i) ? vv[i] : 0.0f;
         const float vmax = max_rows(fmaxf(fmaxf(vv[0], vv[1]), fmaxf(vv[2], vv[3])));
         const float inv = vmax > 0.0f ? 1.0f / vmax : 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) rt[r] = vv[r] * inv;
+        for (int i = 0; i < 4; ++i) rt[i] = vv[i] * inv;
         vscale = vmax;
       }
-    } else if (LL && fmt == VK_FMT_LOSSLESS) {
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 x0 = r.k[2 * c], x1 = r.k[2 * c + 1];
+        const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+        uint32_t t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          t[i] = ((lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) | (((hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
+        ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{t[0], t[1], t[2], t[3]});
+        ka[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{t[4], t[5], t[6], t[7]});
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) va[j] = __builtin_bit_cast(h4_t, u2_t{r.v[j].x, r.v[j].y});
+    }
+  };
+
+  // A operands and scales of a non-ternary unit, loaded here: fp8 / fp16 through the two steps
+  // above; lossless pages (LL instances) rebuilt from their streams.
+  auto operands_other = [&](int lu, int32_t entry, h8_t (&ka)[NS], h4_t (&va)[NB], float (&ks)[4], float (&rt)[4],
+                            float& vscale) {
+    const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
+    if (!(LL && fmt == VK_FMT_LOSSLESS)) {
+      OtherRaw r;
+      load_other(lu, entry, r);
+      convert_other(lu, entry, r, ka, va, ks, rt, vscale);
+      return;
+    }
+    const int64_t idx = entry & 0x3FFFFFFF;
+    const int upi = ((unit_of(lu) * 16) & (P.bs - 1)) >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ks[r] = 1.0f, rt[r] = 1.0f;
+    vscale = 1.0f;
+    {
+
       // bfloat16 values of the unit's K and V groups, rebuilt from the exponent codes (escapes
       // from the exception list, this lane's run of it) and the sign+mantissa bytes, or read
       // raw; each group scaled by one power of two into f16 (largest magnitude below 2^15,
@@ -1418,28 +1480,6 @@ void k_decode_mfma(DecodeArgs a) {
       vscale = lossless_group(pg + (P.hkv + kvh) * P.tile_bytes[3] + upi * slot_b, false, ow);
 #pragma unroll
       for (int j = 0; j < NB; ++j) va[j] = __builtin_bit_cast(h4_t, u2_t{ow[j >> 1][2 * (j & 1)], ow[j >> 1][2 * (j & 1) + 1]});
-    } else {
-      const uint8_t* pg = P.pool[2] + (layer * P.cap[2] + idx) * P.page_bytes[2];
-      const uint4* kp =
-          reinterpret_cast<const uint4*>(pg + kvh * P.tile_bytes[2] + ((upi * 16 + c16) * D + dbase) * 2);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const uint4 x0 = kp[2 * c], x1 = kp[2 * c + 1];
-        const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
-        uint32_t t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          t[i] = ((lo[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) | (((hi[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16);
-        ka[2 * c] = __builtin_bit_cast(h8_t, u4_t{t[0], t[1], t[2], t[3]});
-        ka[2 * c + 1] = __builtin_bit_cast(h8_t, u4_t{t[4], t[5], t[6], t[7]});
-      }
-      const uint8_t* vt = pg + (P.hkv + kvh) * P.tile_bytes[2];
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const uint2 x =
-            *reinterpret_cast<const uint2*>(vt + (static_cast<int64_t>(16 * j + c16) * P.bs + upi * 16 + 4 * grp) * 2);
-        va[j] = __builtin_bit_cast(h4_t, u2_t{x.x, x.y});
-      }
     }
   };
 
@@ -1451,29 +1491,14 @@ void k_decode_mfma(DecodeArgs a) {
   if (mixed_part) {
     make_qb();
     vcur = 1.0f;
-    int rank = 0;  // non-ternary units seen so far (uniform)
     // only the two ranges the host found to hold every fp8 / fp16 unit are scanned
     const int m_lo[2] = {a.mix[b][0], a.mix[b][2]}, m_hi[2] = {min(a.mix[b][1], U), min(a.mix[b][3], U)};
-    for (int rg = 0; rg < 2; ++rg) {
-      for (int c0 = m_lo[rg]; c0 < m_hi[rg]; c0 += 64) {
-        const int lu_l = c0 + lane;
-        const bool in_rg = lu_l < m_hi[rg];
-        const int32_t ent_l = in_rg ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
-        const uint32_t fmt_l = static_cast<uint32_t>(ent_l) >> 30;
-        uint64_t todo = __ballot(in_rg && (LL ? fmt_l == VK_FMT_LOSSLESS
-                                              : fmt_l != VK_FMT_TERNARY2 && fmt_l != VK_FMT_LOSSLESS));
-        while (todo) {
-          const int k = __builtin_ctzll(todo);
-          todo &= todo - 1;
-          // the extra blocks' waves take the units in turn
-          if (LL ? rank++ % NW != wave
-                 : rank++ % (NW * a.n_mix_parts) != (split - a.n_splits) * NW + wave) continue;
-          const int lu = c0 + k;
-          const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
-          h8_t ka[NS];
-          h4_t va[NB];
-          float ksc[4], prt[4], vscale;
-          operands_other(lu, entry, ka, va, ksc, prt, vscale);
+    // the extra blocks' waves take the units in turn
+    const int n_take = LL ? NW : NW * a.n_mix_parts;
+    const int my_turn = LL ? wave : (split - a.n_splits) * NW + wave;
+    // one fp8 / fp16 (LL: lossless) unit: scores, online softmax, P*V
+    auto mix_unit = [&](const int lu, const h8_t (&ka)[NS], const h4_t (&va)[NB], const float (&ksc)[4],
+                        const float (&prt)[4], const float vscale) {
           f4_t s4 = {0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int s = 0; s < NS; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[s], qb[s], s4, 0, 0, 0);
@@ -1488,7 +1513,7 @@ void k_decode_mfma(DecodeArgs a) {
             mx = fmaxf(mx, sc[r]);
           }
           mx = max_rows(mx);
-          if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) continue;
+          if (__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)) == __builtin_bit_cast(int, -INFINITY)) return;
           if (__ballot(mx > m) != 0) {
             const float mn = fmaxf(m, mx);
             const float corr = __builtin_amdgcn_exp2f(m - mn);
@@ -1528,7 +1553,84 @@ void k_decode_mfma(DecodeArgs a) {
             const f4_t t4 = __builtin_amdgcn_mfma_f32_16x16x16f16(va[j], pb, f4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             oacc[j] += t4 * vs14;
           }
+    };
+    if constexpr (LL || D > 128) {
+      int rank = 0;  // non-ternary units seen so far (uniform)
+      for (int rg = 0; rg < 2; ++rg) {
+        for (int c0 = m_lo[rg]; c0 < m_hi[rg]; c0 += 64) {
+          const int lu_l = c0 + lane;
+          const bool in_rg = lu_l < m_hi[rg];
+          const int32_t ent_l = in_rg ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
+          const uint32_t fmt_l = static_cast<uint32_t>(ent_l) >> 30;
+          uint64_t todo = __ballot(in_rg && (LL ? fmt_l == VK_FMT_LOSSLESS
+                                                : fmt_l != VK_FMT_TERNARY2 && fmt_l != VK_FMT_LOSSLESS));
+          while (todo) {
+            const int k = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            if (rank++ % n_take != my_turn) continue;
+            const int lu = c0 + k;
+            const int32_t entry = __builtin_amdgcn_readlane(ent_l, k);
+            h8_t ka[NS];
+            h4_t va[NB];
+            float ksc[4], prt[4], vscale;
+            operands_other(lu, entry, ka, va, ksc, prt, vscale);
+            mix_unit(lu, ka, va, ksc, prt, vscale);
+          }
         }
+      }
+    } else {
+      // The wave first lists its units, up to 64 at a time (lane j holds the j-th), then runs
+      // them with the next unit's loads in flight while it computes one.  These blocks run
+      // while the ternary blocks keep the memory system full, where every load waits a long
+      // queue: one load round trip per unit, one after another, would set their time.
+      for (int first = 0;; first += 64) {
+        int rank = 0, mine = 0, n = 0;  // (uniform)
+        int my_lu = 0;
+        int32_t my_ent = 0;
+        for (int rg = 0; rg < 2; ++rg) {
+          for (int c0 = m_lo[rg]; c0 < m_hi[rg]; c0 += 64) {
+            const int lu_l = c0 + lane;
+            const bool in_rg = lu_l < m_hi[rg];
+            const int32_t ent_l = in_rg ? bt[(unit_of(lu_l) * 16) >> P.bs_shift] : 0;
+            const uint32_t fmt_l = static_cast<uint32_t>(ent_l) >> 30;
+            uint64_t todo = __ballot(in_rg && fmt_l != VK_FMT_TERNARY2 && fmt_l != VK_FMT_LOSSLESS);
+            while (todo) {
+              const int k = __builtin_ctzll(todo);
+              todo &= todo - 1;
+              if (rank++ % n_take != my_turn) continue;
+              const int j = mine++ - first;
+              if (j < 0 || j >= 64) continue;
+              const int32_t e = __builtin_amdgcn_readlane(ent_l, k);
+              my_lu = lane == j ? c0 + k : my_lu;
+              my_ent = lane == j ? e : my_ent;
+              ++n;
+            }
+          }
+        }
+        if (n == 0) break;
+        // Unit i's words are converted to operands, the next fp8 unit's loads go out into the
+        // same registers (a clamped index repeats the last unit), and unit i is computed while
+        // they land.  fp16 units (the sinks: rare, and twice the registers) load when their turn
+        // comes.
+        auto fetch8 = [&](int i, OtherRaw& r) {
+          const int ii = min(i, n - 1);
+          const int32_t e = __builtin_amdgcn_readlane(my_ent, ii);
+          if ((static_cast<uint32_t>(e) >> 30) == VK_FMT_FP8E4M3) load_other(__builtin_amdgcn_readlane(my_lu, ii), e, r);
+        };
+        OtherRaw raw;
+        fetch8(0, raw);
+        for (int i = 0; i < n; ++i) {
+          const int lu = __builtin_amdgcn_readlane(my_lu, i);
+          const int32_t entry = __builtin_amdgcn_readlane(my_ent, i);
+          h8_t ka[NS];
+          h4_t va[NB];
+          float ksc[4], prt[4], vscale;
+          if ((static_cast<uint32_t>(entry) >> 30) == VK_FMT_FP8E4M3) convert_other(lu, entry, raw, ka, va, ksc, prt, vscale);
+          else operands_other(lu, entry, ka, va, ksc, prt, vscale);
+          fetch8(i + 1, raw);
+          mix_unit(lu, ka, va, ksc, prt, vscale);
+        }
+        if (n < 64) break;
       }
     }
   }

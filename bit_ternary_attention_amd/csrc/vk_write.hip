@@ -298,18 +298,12 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
     const int pos0 = unit * 16;
     const int page = pos0 >> a.P.bs_shift;
     const int upi = (pos0 & (a.P.bs - 1)) >> 4;
+    // The block-table entry, the input tile and (MODE 0: every page ternary or lossless) the
+    // segment's absmean partials are loaded before anything waits for one of them: each needs
+    // only the sequence's descriptor.
     const int32_t entry = a.entries[d.page_off + page - d.page_first];
-    const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
-    const int64_t idx = entry & 0x3FFFFFFF;
-    uint8_t* tile = a.P.pool[fmt] + (static_cast<int64_t>(layer) * a.P.cap[fmt] + idx) * a.P.page_bytes[fmt] +
-                    static_cast<int64_t>(kv * hkv + h) * a.P.tile_bytes[fmt];
     const uint16_t* src =
         (kv ? a.v : a.k) + (static_cast<int64_t>(l_rel) * a.total_tokens + d.tok_off) * row + h * D + c * 8;
-
-    if (MODE != 2 && l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
-      a.P.block_table[static_cast<int64_t>(d.slot) * a.P.max_pages + page] = entry;
-    if (MODE != 2 && fmt == VK_FMT_LOSSLESS) continue;  // written by the launch over the lossless units
-
     uint4 w[NI];
     bool ok[NI];
 #pragma unroll
@@ -319,6 +313,24 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
       ok[k] = j >= 0 && j < d.n_tokens;
       w[k] = ok[k] ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * row) : make_uint4(0, 0, 0, 0);
     }
+    if constexpr (MODE == 0) {  // (a lossless unit derives the record too; it is not used)
+      if (kv == 0 && !have_k) {
+        seg_k = segment_info<DT>(a, d, l_rel, 0);
+        have_k = true;
+      }
+      if (kv == 1 && !have_v) {
+        seg_v = segment_info<DT>(a, d, l_rel, 1);
+        have_v = true;
+      }
+    }
+    const int fmt = static_cast<int>(static_cast<uint32_t>(entry) >> 30);
+    const int64_t idx = entry & 0x3FFFFFFF;
+    uint8_t* tile = a.P.pool[fmt] + (static_cast<int64_t>(layer) * a.P.cap[fmt] + idx) * a.P.page_bytes[fmt] +
+                    static_cast<int64_t>(kv * hkv + h) * a.P.tile_bytes[fmt];
+
+    if (MODE != 2 && l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
+      a.P.block_table[static_cast<int64_t>(d.slot) * a.P.max_pages + page] = entry;
+    if (MODE != 2 && fmt == VK_FMT_LOSSLESS) continue;  // written by the launch over the lossless units
 
     if (MODE != 2 && fmt == VK_FMT_TERNARY2) {
       if (kv == 0 && !have_k) {
