@@ -51,6 +51,9 @@ def parse():
                     help="page format of the recent tier instead of the workload's own")
     ap.add_argument("--fp8-dynamic", action="store_true",
                     help="FP8 pages with one scale per token and KV head instead of the static scale")
+    ap.add_argument("--page-order", choices=["workload", "sequential", "shuffled"], default="workload",
+                    help="page placement in the pools: the workload's own, in allocation order, or a seeded "
+                         "random permutation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-layers", type=int, default=0, help="0 = workload's own sample rule")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -86,6 +89,9 @@ def main():
         import dataclasses
         w = dataclasses.replace(w, sink_format=FORMATS[args.sink_format] if args.sink_format else w.sink_format,
                                 recent_format=FORMATS[args.recent_format] if args.recent_format else w.recent_format)
+    if args.page_order != "workload":
+        import dataclasses
+        w = dataclasses.replace(w, page_shuffle_seed=0 if args.page_order == "sequential" else 12345)
     calls = w.appends()
     ids_all = list(range(w.n_seqs))
 
@@ -222,6 +228,7 @@ def main():
                    "tokens_per_seq": list(sorted(set(w.lengths))) if len(set(w.lengths)) > 1 else w.lengths[0],
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "sink_tokens": w.sink_tokens, "window": w.window,
+                   "page_order": "shuffled" if w.page_shuffle_seed else "sequential",
                    "append_calls": len(batches), "ragged_appends": w.ragged_appends, "input_sets": n_sets,
                    "fp8": "dynamic per (token, head)" if args.fp8_dynamic else "static scale",
                    "sink_format": next(k for k, f in FORMATS.items() if f == w.sink_format),
@@ -235,6 +242,7 @@ def main():
                         "segment_us_per_step": round(decode_seg_ms * 1e3, 3),
                         "segment_GBps": round(dec_bytes / (decode_seg_ms * 1e-3) / 1e9, 1),
                         "splits": stats["last_decode_splits"], "units_by_format": stats["last_decode_units"],
+                        "ordered_dispatch": bool(stats["last_decode_ordered"]),
                         "timing": ("decode + merge launches, HIP event pair around each on the launch stream, "
                                    "over the timed steps; segment_*: one event pair per step around the step's "
                                    "decode launches"),

@@ -614,7 +614,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(cfg.head_dim));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int64_t units[4] = {0, 0, 0, 0};
-  int32_t splits_used = 1, steal_used = 0;
+  int32_t splits_used = 1, steal_used = 0, ordered_used = 0;
   const bool mfma = cfg.decode_kernel != VK_DECODE_VALU;
   const bool d256 = cfg.head_dim == 256;  // matrix-core instances: 4-slot ring, no stealing blocks
   // sequences per launch: every (sequence, KV head) needs room for a split's partial and the
@@ -722,6 +722,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
                   static_cast<long long>(kDecodeScratchItems));
     splits_used = a.n_splits;
     steal_used |= a.steal;
+    ordered_used |= a.n_order > 0 ? 1 : 0;
     if (c->timer.on) {
       const double row = cfg.head_dim;
       const double unit_kv = 2.0 * 16.0 * cfg.n_kv_heads;  // K and V, 16 tokens, every KV head
@@ -742,6 +743,7 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
   c->stats.decode_calls += 1;
   c->stats.last_decode_splits = splits_used;
   c->stats.last_decode_steal = steal_used;
+  c->stats.last_decode_ordered = ordered_used;
   for (int f = 0; f < 4; ++f) {
     c->stats.last_decode_units[f] = units[f];
     c->stats.total_decode_units[f] += units[f];

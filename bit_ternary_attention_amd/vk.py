@@ -39,7 +39,8 @@ class Stats(ctypes.Structure):
                 ("tokens_stored", _c_i64 * 4), ("append_calls", _c_i64), ("decode_calls", _c_i64),
                 ("last_decode_units", _c_i64 * 4), ("total_decode_units", _c_i64 * 4),
                 ("last_decode_splits", _c_i32), ("last_decode_steal", _c_i32), ("retier_calls", _c_i64),
-                ("pages_retiered", _c_i64), ("pages_evicted", _c_i64)]
+                ("pages_retiered", _c_i64), ("pages_evicted", _c_i64), ("last_decode_ordered", _c_i32),
+                ("reserved", _c_i32)]
 
     def as_dict(self):
         out = {}

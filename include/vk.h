@@ -310,6 +310,10 @@ typedef struct vk_stats {
   int64_t retier_calls;             /* vk_retier calls                                    */
   int64_t pages_retiered;           /* pages moved from FP8 to ternary (each in every layer) */
   int64_t pages_evicted;            /* pages freed by vk_evict                            */
+  int32_t last_decode_ordered;      /* 1 if its matrix-core launches dispatched their blocks
+                                       heaviest first from a host-planned order (sequences of
+                                       different lengths, or fp8 / fp16 parts)              */
+  int32_t reserved;                 /* 0                                                   */
 } vk_stats;
 
 VK_API vk_status vk_get_stats(vk_cache* c, vk_stats* out);

@@ -56,6 +56,7 @@ def test_workload3_full_retention_outliers(kernel):
     r = run_workload(w, page_layers=[0], decode_layers=[0], decode_kernel=kernel)
     check_all(w, r, [0], [0])
     assert r["stats"]["last_decode_steal"] == 0   # stealing blocks are opt-in
+    assert r["stats"]["last_decode_ordered"] == 0  # equal lengths: the plain grid
     say(f"workload 3: max err {r['max_err']:.3e}")
 
 
@@ -66,6 +67,8 @@ def test_workload4_mixed_format_paged(kernel):
     check_all(w, r, [0], [0])
     units = r["stats"]["last_decode_units"]
     assert units[0] > 0 and units[1] > 0 and units[2] == 64   # every route ran
+    # ragged lengths and fp8 / fp16 parts: the matrix-core launch dispatches from its order table
+    assert r["stats"]["last_decode_ordered"] == (0 if kernel == 1 else 1)
     say(f"workload 4: max err {r['max_err']:.3e} units {units}")
 
 
