@@ -35,6 +35,7 @@ constexpr int kRingMax = 64;             // append / retier plan staging slots, 
 constexpr int kRingMin = 4;              // ... at least
 constexpr int64_t kRingBytes = 64 << 20; // pinned bytes the slots may take together (beyond kRingMin)
 constexpr int64_t kPackTargetBlocks = 32768;  // pack blocks per launch, at most
+constexpr int64_t kPackPipeMaxTasks = 16;      // pipelined pack: tasks per block, at most
 constexpr int64_t kRetierTasksPerLaunch = 65536;  // pages one retier launch converts, at most
 constexpr int64_t kMaxPartials = 1 << 20;  // float64 absmean partials per append call
 constexpr int kDecodeTargetGroups = 4096;  // work groups a decode launch aims for
@@ -60,6 +61,18 @@ int decode_mixed_parts() {
   const char* e = std::getenv("VK_DECODE_MIX_PARTS");
   const int v = e ? std::atoi(e) : 0;
   return v >= 1 && v <= kDecodeMixedPartsMax ? v : 1;
+}
+// Short all-ternary appends at head dims 64 and 128 run the pipelined pack kernel (VK_PACK_PIPE=0:
+// k_pack's one-task blocks) with VK_PACK_BLOCKS_PER_CU blocks per compute unit at most (default 16:
+// the kernel's 120 registers leave room for 4 waves per SIMD, 16 one-wave blocks per CU).
+bool pack_pipelined_on() {
+  const char* e = std::getenv("VK_PACK_PIPE");
+  return !(e && e[0] == '0');
+}
+int pack_blocks_per_cu() {
+  const char* e = std::getenv("VK_PACK_BLOCKS_PER_CU");
+  const int v = e ? std::atoi(e) : 0;
+  return v >= 1 && v <= 64 ? v : 16;
 }
 // Launches over sequences of different lengths (or with fp8 / fp16 parts) dispatch their blocks
 // heaviest first from an order table.  VK_DECODE_ORDER=0 keeps the plain grid;
@@ -445,7 +458,18 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   a.total_tokens = static_cast<int32_t>(plan.total_tokens);
   a.total_blk = static_cast<int32_t>(plan.total_blk);
   a.total_tasks = static_cast<int32_t>(plan.total_tasks);
-  const int64_t blocks = std::min<int64_t>(total, kPackTargetBlocks);
+  // Every touched page ternary, head dim 64 or 128, and a call of at most kPackPipeMaxTasks
+  // tasks per block at pack_blocks_per_cu() blocks per compute unit (4096 tokens x 4 sequences
+  // x 8 heads, or 36 layers x 4096 tokens x 2 heads): the pipelined pack kernel, with about as
+  // many blocks as the GPU holds at once.  Larger calls stream better through the one-task
+  // blocks of k_pack (more waves resident: 67 registers against 120).
+  const bool only_ternary = std::all_of(plan.entries.begin(), plan.entries.end(),
+                                        [](int32_t e) { return vk::entry_fmt(e) == VK_FMT_TERNARY2; });
+  const int64_t pipe_blocks = static_cast<int64_t>(std::max(1, c->n_cu)) * pack_blocks_per_cu();
+  a.pack_pipelined =
+      only_ternary && cfg.head_dim != 256 && total <= pipe_blocks * kPackPipeMaxTasks && pack_pipelined_on() ? 1 : 0;
+  const int64_t target = a.pack_pipelined ? pipe_blocks : kPackTargetBlocks;
+  const int64_t blocks = std::min<int64_t>(total, target);
   a.tasks_per_blk = static_cast<int32_t>((total + blocks - 1) / blocks);
   a.pack_blocks = static_cast<int32_t>((total + a.tasks_per_blk - 1) / a.tasks_per_blk);
   // sequences with equal task (block) counts: the kernels find a task's sequence by division

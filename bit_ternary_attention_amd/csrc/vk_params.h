@@ -60,6 +60,8 @@ struct AppendArgs {
   int32_t seq_tasks;       // pack tasks of every sequence when they all have the same count, else 0
   int32_t seq_blk;         // absmean blocks of every sequence when they all have the same count, else 0
   int32_t all_ternary;     // every touched page is ternary or lossless (the pack kernel's lean instance)
+  int32_t pack_pipelined;  // every touched page is ternary, head dim 64 or 128: k_pack_tern, whose
+                           // blocks keep the next task's loads in flight (tasks_per_blk sized for it)
   const int32_t* ll_units; // [n_ll_units][2]: (sequence index, unit) of every lossless 16-token unit
   int32_t n_ll_units;      // written by a pack launch of their own (the main one skips them)
   float eps;

@@ -224,11 +224,70 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(AppendArgs a) {
 // segment derives them itself, with the same fixed-order sum, so all agree bit for bit (the
 // partials of a call are a few KB, read from L2): no finalize launch between the two passes.
 template <int DT>
+__device__ __forceinline__ SegInfo segment_info_n(const AppendArgs& a, int64_t n, int blk_off, int l_rel, int kv) {
+  const int n_blk = static_cast<int>((n + kAbsElemsPerBlock - 1) / kAbsElemsPerBlock);
+  const double s = sum_partials_wave(a.partials + static_cast<int64_t>(l_rel * 2 + kv) * a.total_blk + blk_off, n_blk);
+  return finalize_wave<DT>(s, n, a.eps);
+}
+
+template <int DT>
 __device__ __forceinline__ SegInfo segment_info(const AppendArgs& a, const AppendSeqDesc& d, int l_rel, int kv) {
   const int64_t n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * a.P.hkv * a.P.dim;
   const int n_blk = static_cast<int>((n + kAbsElemsPerBlock - 1) / kAbsElemsPerBlock);
   const double s = sum_partials_wave(a.partials + static_cast<int64_t>(l_rel * 2 + kv) * a.total_blk + d.blk_off, n_blk);
   return finalize_wave<DT>(s, n, a.eps);
+}
+
+// Codes of one (16-token unit, K|V, head) tile from this lane's input words w (rows rg * NI + k,
+// 16-byte chunk c of the row), stored in the page layout: keys token-major (16-bit stores of
+// eight codes), values through an LDS transpose into the decode's chunks (lane = chunk
+// 4 cq + g = tokens 4g..4g+3 of dimensions 16j + cq; LDS rows (4g, 4g+1) and (4g+2, 4g+3)
+// arrive as one dword each; head dim 256 keeps two head-dim-128 chunks side by side).  One
+// wave; the value path holds two barriers, so every lane of the block calls it.
+template <int D>
+__device__ __forceinline__ void store_ternary_tile(const uint4 (&w)[16 / (64 / (D / 8))], uint32_t thresh, uint8_t* tile,
+                                                   int upi, int kv, uint16_t* lds16) {
+  constexpr int CPR = D / 8, NI = 16 / (64 / CPR);
+  const int lane = threadIdx.x, c = lane % CPR, rg = lane / CPR;
+  if (kv == 0) {
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int r = rg * NI + k;
+      const uint32_t cw = code_word8(w[k], thresh);
+      *reinterpret_cast<uint16_t*>(tile + (upi * 16 + r) * (D / 4) + 2 * c) = static_cast<uint16_t>(cw);
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < NI; ++k) {
+    const int r = rg * NI + k;
+    lds16[c * 16 + r] = static_cast<uint16_t>(code_word8(w[k], thresh));
+  }
+  __syncthreads();
+  const int cq = lane >> 2, g = lane & 3;
+  const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds16);
+  uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const int dd = 16 * j + cq;
+    const int cc = dd >> 3, e = dd & 7;
+    const uint32_t f01 = (l32[cc * 8 + 2 * g] >> (2 * e)) & 0x00030003u;
+    const uint32_t f23 = (l32[cc * 8 + 2 * g + 1] >> (2 * e)) & 0x00030003u;
+    if (D == 64) {
+      w0 |= (f01 << (2 * j)) | (f23 << (8 + 2 * j));
+    } else if (j < 8) {
+      w0 |= f01 << (2 * j);
+      w1 |= f23 << (2 * j);
+    } else {
+      w2 |= f01 << (2 * (j - 8));
+      w3 |= f23 << (2 * (j - 8));
+    }
+  }
+  uint8_t* vdst = tile + upi * 4 * D + lane * (D / 16);
+  if (D == 256) *reinterpret_cast<uint4*>(vdst) = make_uint4(w0, w1, w2, w3);
+  else if (D == 128) *reinterpret_cast<uint2*>(vdst) = make_uint2(w0, w1);
+  else *reinterpret_cast<uint32_t*>(vdst) = w0;
+  __syncthreads();
 }
 
 // ------------------------------------------------------------- pass 2 ---
@@ -344,48 +403,7 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
       const SegInfo si = kv == 0 ? seg_k : seg_v;
       if (upi == 0 && h == 0 && lane == 0)
         a.P.gamma[(static_cast<int64_t>(layer) * a.P.cap[0] + idx) * 2 + kv] = si.gamma;
-      if (kv == 0) {
-#pragma unroll
-        for (int k = 0; k < NI; ++k) {
-          const int r = rg * NI + k;
-          const uint32_t cw = code_word8(w[k], si.thresh);
-          *reinterpret_cast<uint16_t*>(tile + (upi * 16 + r) * (D / 4) + 2 * c) = static_cast<uint16_t>(cw);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < NI; ++k) {
-          const int r = rg * NI + k;
-          lds16[c * 16 + r] = static_cast<uint16_t>(code_word8(w[k], si.thresh));
-        }
-        __syncthreads();
-        // value tile, chunked per 16-token unit: lane = chunk 4*cq + g = tokens 4g..4g+3 of
-        // dimensions 16j + cq; LDS rows (4g, 4g+1) and (4g+2, 4g+3) arrive as one dword each.
-        // Head dim 256 keeps two head-dim-128 chunks side by side (j < 8, then j >= 8).
-        const int cq = lane >> 2, g = lane & 3;
-        const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds16);
-        uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) {
-          const int dd = 16 * j + cq;
-          const int cc = dd >> 3, e = dd & 7;
-          const uint32_t f01 = (l32[cc * 8 + 2 * g] >> (2 * e)) & 0x00030003u;
-          const uint32_t f23 = (l32[cc * 8 + 2 * g + 1] >> (2 * e)) & 0x00030003u;
-          if (D == 64) {
-            w0 |= (f01 << (2 * j)) | (f23 << (8 + 2 * j));
-          } else if (j < 8) {
-            w0 |= f01 << (2 * j);
-            w1 |= f23 << (2 * j);
-          } else {
-            w2 |= f01 << (2 * (j - 8));
-            w3 |= f23 << (2 * (j - 8));
-          }
-        }
-        uint8_t* vdst = tile + upi * 4 * D + lane * (D / 16);
-        if (D == 256) *reinterpret_cast<uint4*>(vdst) = make_uint4(w0, w1, w2, w3);
-        else if (D == 128) *reinterpret_cast<uint2*>(vdst) = make_uint2(w0, w1);
-        else *reinterpret_cast<uint32_t*>(vdst) = w0;
-        __syncthreads();
-      }
+      store_ternary_tile<D>(w, si.thresh, tile, upi, kv, lds16);
     } else if (MODE == 0) {
       // (not reached: the host launches this instance only when every page is ternary or lossless)
     } else if (MODE == 1 && fmt == VK_FMT_FP8E4M3) {
@@ -640,6 +658,122 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
 
 // ------------------------------------------------------- flat tensor ---
 
+// All-ternary appends at head dims 64 and 128 (every touched page ternary): the tasks of
+// k_pack, but a block's run of tasks is pipelined: the next task's block-table entry and input
+// tile are loaded before the current one is coded and stored, so a block streams its run
+// instead of paying a loaded-memory round trip per task.  Launched with about as many blocks
+// as fit the GPU at once (short appends then run in one round).  Appends into partly filled
+// ternary pages are refused on the host, so a task's unit starts at or after the call's first
+// token.
+template <int DT, int D>
+__global__ __launch_bounds__(64) void k_pack_tern(AppendArgs a) {
+  constexpr int CPR = D / 8;     // 16-byte chunks per token row
+  constexpr int RPI = 64 / CPR;  // rows per wave-wide load
+  constexpr int NI = 16 / RPI;   // loads per lane per unit
+  static_assert(D == 64 || D == 128, "head dims 64 and 128");
+  __shared__ uint32_t lds[D * 16 * 2 / 4 + 4];
+  uint16_t* lds16 = reinterpret_cast<uint16_t*>(lds);
+  const int lane = threadIdx.x;
+  const int hkv = a.P.hkv;
+  const int64_t row = static_cast<int64_t>(hkv) * D;
+  const int c = lane % CPR, rg = lane / CPR;
+  const int64_t g_end = static_cast<int64_t>(a.n_layers) * a.total_tasks;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * a.tasks_per_blk;
+  const int64_t g1 = g0 + a.tasks_per_blk < g_end ? g0 + a.tasks_per_blk : g_end;
+  if (g0 >= g1) return;  // (uniform)
+
+  // What one task needs once its loads are out (uniform except src).
+  struct Task {
+    int l_rel, seq, h, kv, uk, upi, page, slot, rows, blk_off;
+    int64_t seg_n;          // elements of the task's segment (its sequence's ternary tokens x heads x D)
+    const int32_t* ent_p;   // its block-table entry in the call's entry list
+    const uint16_t* src;    // this lane's chunk of the unit's first row
+  };
+  // the sequence the block's decoding has reached (tasks are decoded in increasing order)
+  int cur_l = -1, cur_i = 0, task_end = 0;
+  AppendSeqDesc d{};
+  auto decode_task = [&](int64_t g) -> Task {
+    const int lr = static_cast<int>(g / a.total_tasks);
+    const int tt = static_cast<int>(g - static_cast<int64_t>(lr) * a.total_tasks);
+    if (lr != cur_l || tt >= task_end) {
+      cur_l = lr;
+      cur_i = a.seq_tasks ? tt / a.seq_tasks : find_seq<&AppendSeqDesc::task_off>(a.descs, a.n_seqs, tt);
+      d = a.descs[cur_i];
+      task_end = d.task_off + ((d.t0 + d.n_tokens + 15) / 16 - d.unit_first) * 2 * hkv;
+    }
+    Task t;
+    const int task = tt - d.task_off;
+    t.l_rel = lr;
+    t.seq = cur_i;
+    t.h = task % hkv;
+    t.kv = (task / hkv) & 1;
+    t.uk = task / (2 * hkv);
+    const int pos0 = (d.unit_first + t.uk) * 16;
+    t.page = pos0 >> a.P.bs_shift;
+    t.upi = (pos0 & (a.P.bs - 1)) >> 4;
+    t.slot = d.slot;
+    t.rows = d.t0 + d.n_tokens - pos0;  // (>= 1: every task's unit holds tokens of the call)
+    t.blk_off = d.blk_off;
+    t.seg_n = static_cast<int64_t>(d.tern_hi - d.tern_lo) * hkv * D;
+    t.ent_p = a.entries + (d.page_off + t.page - d.page_first);
+    t.src = (t.kv ? a.v : a.k) + (static_cast<int64_t>(lr) * a.total_tokens + d.tok_off + (pos0 - d.t0)) * row +
+            t.h * D + c * 8;
+    return t;
+  };
+  auto load = [&](const Task& t, uint4 (&w)[NI], int32_t& ent) {
+    ent = *t.ent_p;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int r = rg * NI + k;
+      w[k] = r < t.rows ? *reinterpret_cast<const uint4*>(t.src + static_cast<int64_t>(r) * row) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // the segment records (gamma, code threshold) of the (layer, sequence) last coded
+  int seg_l = -1, seg_i = -1;
+  SegInfo seg_k{}, seg_v{};
+  bool have_k = false, have_v = false;
+  auto process = [&](const Task& t, const uint4 (&w)[NI], int32_t ent) {
+    const int64_t layer = a.layer_begin + t.l_rel;
+    const int64_t idx = ent & 0x3FFFFFFF;
+    uint8_t* tile = a.P.pool[0] + (layer * a.P.cap[0] + idx) * a.P.page_bytes[0] +
+                    static_cast<int64_t>(t.kv * hkv + t.h) * a.P.tile_bytes[0];
+    if (t.l_rel == 0 && t.kv == 0 && t.h == 0 && lane == 0 && (t.uk == 0 || t.upi == 0))
+      a.P.block_table[static_cast<int64_t>(t.slot) * a.P.max_pages + t.page] = ent;
+    if (t.l_rel != seg_l || t.seq != seg_i) {
+      seg_l = t.l_rel;
+      seg_i = t.seq;
+      have_k = have_v = false;
+    }
+    if (t.kv == 0 && !have_k) {
+      seg_k = segment_info_n<DT>(a, t.seg_n, t.blk_off, t.l_rel, 0);
+      have_k = true;
+    }
+    if (t.kv == 1 && !have_v) {
+      seg_v = segment_info_n<DT>(a, t.seg_n, t.blk_off, t.l_rel, 1);
+      have_v = true;
+    }
+    const SegInfo si = t.kv == 0 ? seg_k : seg_v;
+    if (t.upi == 0 && t.h == 0 && lane == 0) a.P.gamma[(layer * a.P.cap[0] + idx) * 2 + t.kv] = si.gamma;
+    store_ternary_tile<D>(w, si.thresh, tile, t.upi, t.kv, lds16);
+  };
+
+  // Two tasks in flight: while one buffer's task is coded, the other buffer's loads land.  An
+  // index past the run repeats its last task (loaded, never processed), so every iteration
+  // issues the same loads.
+  Task ta = decode_task(g0);
+  uint4 wa[NI], wb[NI];
+  int32_t ea, eb;
+  load(ta, wa, ea);
+  for (int64_t g = g0; g < g1; g += 2) {
+    const Task tb = decode_task(g + 1 < g1 ? g + 1 : g1 - 1);
+    load(tb, wb, eb);
+    process(ta, wa, ea);
+    ta = decode_task(g + 2 < g1 ? g + 2 : g1 - 1);
+    load(ta, wa, ea);
+    if (g + 1 < g1) process(tb, wb, eb);
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kAbsThreads) void k_flat_absmean(QuantArgs a) {
   const int blk = blockIdx.x;
@@ -700,7 +834,15 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s, LaunchTimer* t) {
   }
   const dim3 g2(a.pack_blocks);
   if (t) t->begin(VK_KERNEL_PACK, s);
-  if (a.P.dim == 256) {  // (no lossless pages at head dim 256: refused on the host)
+  if (a.pack_pipelined && (a.P.dim == 128 || a.P.dim == 64)) {  // every page ternary (set on the host)
+    if (a.P.dim == 128) {
+      if (bf) k_pack_tern<1, 128><<<g2, 64, 0, s>>>(a);
+      else k_pack_tern<0, 128><<<g2, 64, 0, s>>>(a);
+    } else {
+      if (bf) k_pack_tern<1, 64><<<g2, 64, 0, s>>>(a);
+      else k_pack_tern<0, 64><<<g2, 64, 0, s>>>(a);
+    }
+  } else if (a.P.dim == 256) {  // (no lossless pages at head dim 256: refused on the host)
     if (a.all_ternary) {
       if (bf) k_pack<1, 256, 0><<<g2, 64, 0, s>>>(a);
       else k_pack<0, 256, 0><<<g2, 64, 0, s>>>(a);
