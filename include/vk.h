@@ -36,7 +36,11 @@
  *     that the device has not reached yet (64 calls queued ahead of the
  *     device at the workloads' sizes: back-pressure, as a full launch queue
  *     gives).
- *   - A handle is not thread-safe; distinct handles are independent.
+ *   - A handle is not thread-safe; distinct handles are independent.  Its calls
+ *     share device scratch (the absmean partials of an append, the split partial
+ *     states of a decode): calls on one handle that are enqueued on different
+ *     streams must be ordered by the caller (an event between them), or they
+ *     race on that scratch.
  */
 #ifndef VK_H_
 #define VK_H_
