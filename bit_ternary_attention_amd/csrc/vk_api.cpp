@@ -74,6 +74,13 @@ int pack_blocks_per_cu() {
   const int v = e ? std::atoi(e) : 0;
   return v >= 1 && v <= 64 ? v : 16;
 }
+// Matrix-core launches with several parts (and no lossless pages) merge them in the kernel: the
+// last block to finish a (sequence, KV head) combines its parts, and no k_merge launch follows.
+// VK_DECODE_FUSED_MERGE=0 keeps the merge launch.
+bool decode_fused_merge_on() {
+  const char* e = std::getenv("VK_DECODE_FUSED_MERGE");
+  return !(e && e[0] == '0');
+}
 // Launches over sequences of different lengths (or with fp8 / fp16 parts) dispatch their blocks
 // heaviest first from an order table.  VK_DECODE_ORDER=0 keeps the plain grid;
 // VK_DECODE_BLOCKS_PER_CU_RAGGED=1..8 sets such launches' split target (default: as the others);
@@ -180,6 +187,7 @@ struct vk_cache {
   vk::PoolsView pools{};
   double* partials = nullptr;
   float* dec_partials = nullptr;
+  uint32_t* part_count = nullptr;  // decode: parts finished per (sequence, KV head); 0 between launches
   int64_t plan_bytes = 0;
   int n_ring = kRingMin;  // staging slots in use (ring_slots of the config)
   uint8_t* plan_host[kRingMax] = {};
@@ -244,9 +252,10 @@ std::vector<int64_t> buffer_sizes(const vk_cache_config& cfg) {
   for (int r = 0; r < kRingMax; ++r) s.push_back(r < rs ? plan_bytes_for(cfg) : 0);  // staged plans
   s.push_back(vk::page_bytes(cfg, VK_FMT_TERNARY2));                          // dummy page
   s.push_back(static_cast<int64_t>(cfg.n_layers) * cfg.pages_lossless * vk::page_bytes(cfg, VK_FMT_LOSSLESS));
+  s.push_back(kDecodeScratchItems * 4);  // decode part counters, one per (sequence, KV head) of a launch
   return s;
 }
-constexpr size_t kBufDummy = 7 + kRingMax, kBufLossless = 8 + kRingMax;  // indices in buffer_sizes
+constexpr size_t kBufDummy = 7 + kRingMax, kBufLossless = 8 + kRingMax, kBufCount = 9 + kRingMax;  // indices in buffer_sizes
 
 void free_all(vk_cache* c) {
   for (void* p : c->allocations) (void)hipFree(p);
@@ -333,7 +342,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   c->allocations = ptrs;
   // pools and gamma start zeroed (finite bytes everywhere); the block table starts empty;
   // the dummy page (target of speculative decode loads) is zero too
-  for (size_t i : {size_t(0), size_t(1), size_t(2), size_t(3), kBufDummy, kBufLossless})
+  for (size_t i : {size_t(0), size_t(1), size_t(2), size_t(3), kBufDummy, kBufLossless, kBufCount})
     if (ptrs[i]) {
       e = hipMemset(ptrs[i], 0, static_cast<size_t>(sizes[i]));
       if (e != hipSuccess) { free_all(c.get()); return fail(VK_ERR_HIP, "hipMemset: %s", hipGetErrorString(e)); }
@@ -361,6 +370,7 @@ VK_API vk_status vk_create_cache(const vk_cache_config* cfg, vk_cache** out) {
   P.fp8_dynamic = cfg->fp8_dynamic;
   c->partials = static_cast<double*>(ptrs[5]);
   c->dec_partials = static_cast<float*>(ptrs[6]);
+  c->part_count = static_cast<uint32_t*>(ptrs[kBufCount]);
   P.dummy_page = static_cast<const uint8_t*>(ptrs[kBufDummy]);
   c->plan_bytes = plan_bytes_for(*cfg);
   c->n_ring = ring_slots(*cfg);
@@ -726,6 +736,8 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       a.steal = 1;
     }
     a.n_parts = a.n_splits + n_mix;
+    a.part_count = c->part_count;
+    a.fused_merge = mfma && a.n_parts > 1 && !n_ll && !a.steal && decode_fused_merge_on() ? 1 : 0;
     a.n_order = 0;
     if (ragged && !a.steal && decode_order_on()) {
       int32_t u_launch[vk::kDecodeMaxSeqs];
@@ -759,7 +771,10 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
       const double part1 = static_cast<double>(nb) * cfg.n_q_heads * (cfg.head_dim + 2) * 4.0;  // one part
       const double dec_out = a.n_parts > 1 ? part1 * a.n_splits : out_bytes;
       c->timer.add_bytes(VK_KERNEL_DECODE, tern_bytes + other_bytes + q_bytes + dec_out + n_mix * part1);
-      if (a.n_parts > 1) c->timer.add_bytes(VK_KERNEL_MERGE, part1 * a.n_parts + out_bytes);
+      // the parts' combination: read every part, write the output (inside the decode kernel
+      // when it merges them itself)
+      if (a.n_parts > 1)
+        c->timer.add_bytes(a.fused_merge ? VK_KERNEL_DECODE : VK_KERNEL_MERGE, part1 * a.n_parts + out_bytes);
     }
     hipError_t e = vk::launch_decode(a, g, s, c->timer.on ? &c->timer : nullptr);
     if (e != hipSuccess) return hip_fail(c, e, "decode kernels");

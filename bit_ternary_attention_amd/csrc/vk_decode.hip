@@ -620,6 +620,58 @@ __device__ __forceinline__ void pv1_half(const uint32_t (&a)[4], h4_t pb, f4_t (
 // block's units from a shared counter (launches of all-ternary pages with a block per CU).
 // LL: the fp8 / fp16 blocks also read lossless pages (an instance of its own, launched only when
 // a launch attends lossless units: their decode needs registers the other instances keep).
+// Fused split merge (matrix-core launches with several parts and no lossless launch): every
+// block of a (sequence, KV head) has stored its part with device-coherent stores; once they have
+// completed, one thread adds 1 to the pair's part counter (a device-scope atomic).  The block that
+// brings it to n_parts is the last, so every other part is stored: it resets the counter for the
+// next launch and combines the parts as k_merge does, in the same order with the same arithmetic
+// (one wave per query head: lane s holds part s's (max, sum) for the butterflies, then every lane
+// sums its dimensions over the parts in part order), so outputs equal the two-launch path bit for
+// bit.  No block waits for another: the ones that finish earlier just leave.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_parts_last_block(const DecodeArgs& a, int b, int kvh, int64_t qh0, int64_t qo0) {
+  __shared__ int last_s;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's part stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = a.part_count + static_cast<int64_t>(b) * a.P.hkv + kvh;
+    const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    last_s = done == static_cast<uint32_t>(a.n_parts);
+    if (done == static_cast<uint32_t>(a.n_parts)) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last_s) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ns = a.n_parts;  // <= 64
+  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  for (int hh = wave; hh < G; hh += NW) {
+    const float* base = a.partials + (qh0 + hh) * ns * (D + 2);
+    const float ms = lane < ns ? ld(base + lane * (D + 2) + D) : -INFINITY;
+    const float ls = lane < ns ? ld(base + lane * (D + 2) + D + 1) : 0.0f;
+    float M = ms;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float wgt = ls > 0.0f ? exp2f(ms - M) : 0.0f;
+    float den = wgt * ls;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+    for (int dd = lane; dd < D; dd += 64) {
+      float num = 0.0f;
+      for (int s0 = 0; s0 < ns; s0 += 8) {
+        float o8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o8[k] = s0 + k < ns ? ld(base + (s0 + k) * (D + 2) + dd) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float w = __shfl(wgt, (s0 + k) & 63, 64);
+          num = s0 + k < ns ? fmaf(w, o8[k], num) : num;
+        }
+      }
+      a.out[(qo0 + hh) * D + dd] = num / den;
+    }
+  }
+}
+
 template <int D, int G, int QDT, int PF, bool DYN, bool STEAL, bool LL = false>
 __global__ __launch_bounds__(64 * (STEAL ? kStealWaves : kMfmaWaves))
 __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : 3, 8)))  // head dim 256: twice the state per lane
@@ -1976,13 +2028,25 @@ void k_decode_mfma(DecodeArgs a) {
     if (a.n_parts == 1) {
       const float inv = 1.0f / den;
       *reinterpret_cast<float4*>(a.out + (qo0 + hh) * D + dd) = float4{num.x * inv, num.y * inv, num.z * inv, num.w * inv};
-    } else {
+    } else if (!a.fused_merge) {
       float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
       *reinterpret_cast<float2*>(part + dd) = float2{num.x, num.y};
       *reinterpret_cast<float2*>(part + dd + 2) = float2{num.z, num.w};
       if (dd == 0) *reinterpret_cast<float2*>(part + D) = float2{M, den};
+    } else {
+      // device-coherent stores (they reach the memory every XCD reads, not only this XCD's L2),
+      // so the block that merges, on any XCD, reads them with device-coherent loads
+      float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
+      const float v[4] = {num.x, num.y, num.z, num.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) __hip_atomic_store(part + dd + k, v[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (dd == 0) {
+        __hip_atomic_store(part + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(part + D + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
+  if (a.n_parts > 1 && a.fused_merge) merge_parts_last_block<D, G, NW>(a, b, kvh, qh0, qo0);
 }
 
 // Combines split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
@@ -2057,7 +2121,7 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
     else k_decode_mfma<D, G, 0, 8, false, false, true><<<g1, 64 * kMfmaWaves, 0, s>>>(b);
   }
   if (t) t->end(VK_KERNEL_DECODE, s);
-  if (a.n_parts > 1) {
+  if (a.n_parts > 1 && !a.fused_merge) {
     if (t) t->begin(VK_KERNEL_MERGE, s);
     k_merge<D><<<dim3(a.hq, a.n_seqs), D, 0, s>>>(a);
     if (t) t->end(VK_KERNEL_MERGE, s);
@@ -2101,7 +2165,7 @@ hipError_t launch_d256(const DecodeArgs& a, hipStream_t s, LaunchTimer* t) {
     }
   }
   if (t) t->end(VK_KERNEL_DECODE, s);
-  if (a.n_parts > 1) {
+  if (a.n_parts > 1 && !a.fused_merge) {
     if (t) t->begin(VK_KERNEL_MERGE, s);
     k_merge<256><<<dim3(a.hq, a.n_seqs), 256, 0, s>>>(a);
     if (t) t->end(VK_KERNEL_MERGE, s);

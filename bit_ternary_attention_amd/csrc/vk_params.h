@@ -103,6 +103,9 @@ struct DecodeArgs {
   // Matrix-core path, optional: the launch's blocks in dispatch order, (part << 8) | sequence
   // index per entry, every (sequence, part) once; the grid is then (hkv, n_order).  0 = the
   // grid (hkv, n_seqs, n_parts) in that order.
+  uint32_t* part_count;    // [n_seqs][hkv]: parts finished in this launch (0 before and after it)
+  int32_t fused_merge;     // matrix-core path with n_parts > 1 and no lossless launch: the last block
+                           // of each (sequence, KV head) merges its parts (no k_merge launch)
   int32_t n_order;
   uint16_t order[kDecodeMaxOrder];
 };
