@@ -2036,14 +2036,15 @@ void k_decode_mfma(DecodeArgs a) {
     } else {
       // device-coherent stores (they reach the memory every XCD reads, not only this XCD's L2),
       // so the block that merges, on any XCD, reads them with device-coherent loads
+      // (8-byte stores: the (D + 2)-float records are 8-byte aligned)
       float* part = a.partials + (qh * a.n_parts + split) * (D + 2);
-      const float v[4] = {num.x, num.y, num.z, num.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) __hip_atomic_store(part + dd + k, v[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (dd == 0) {
-        __hip_atomic_store(part + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(part + D + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      auto st2 = [](float* p, float x, float y) {
+        const uint64_t v = (static_cast<uint64_t>(__float_as_uint(y)) << 32) | __float_as_uint(x);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      st2(part + dd, num.x, num.y);
+      st2(part + dd + 2, num.z, num.w);
+      if (dd == 0) st2(part + D, M, den);
     }
   }
   if (a.n_parts > 1 && a.fused_merge) merge_parts_last_block<D, G, NW>(a, b, kvh, qh0, qo0);
