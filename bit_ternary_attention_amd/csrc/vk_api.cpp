@@ -218,7 +218,9 @@ int64_t plan_bytes_for(const vk_cache_config& cfg) {
   // descriptors, block-table entries and (with a lossless tier) the call's lossless units: the
   // sink pages and the pages the recent tier can hold, two int32 per 16-token unit
   const int64_t upp = cfg.block_size / vk::kUnit;
-  const bool ll = cfg.sink_format == VK_FMT_LOSSLESS || cfg.recent_format == VK_FMT_LOSSLESS;
+  // (and, with an fp8 / fp16 tier, the call's units of those pages: a page is of one format, so
+  // both lists together stay within the same bound)
+  const bool ll = cfg.sink_format != VK_FMT_TERNARY2 || (cfg.recent_tokens > 0 && cfg.recent_format != VK_FMT_TERNARY2);
   const int64_t ll_pages = ll ? (cfg.sink_tokens + cfg.block_size - 1) / cfg.block_size +
                                     (cfg.recent_tokens + cfg.block_size - 1) / cfg.block_size + 2
                               : 0;
@@ -419,21 +421,34 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   const int64_t total = static_cast<int64_t>(n_layers) * plan.total_tasks;
   // the 16-token units of lossless pages: (sequence index, unit) pairs for the pack kernel that
   // writes them
-  std::vector<int32_t> ll_units;
+  std::vector<int32_t> ll_units, ot_units;  // (and the fp8 / fp16 units, likewise)
+  int64_t n_units = 0;
   for (size_t i = 0; i < plan.seqs.size(); ++i) {
     const vk::AppendSeqDesc& d = plan.seqs[i];
     const int32_t unit_end = (d.t0 + d.n_tokens + vk::kUnit - 1) / vk::kUnit;
     for (int32_t u = d.unit_first; u < unit_end; ++u) {
       const int32_t page = u * vk::kUnit / cfg.block_size;
-      if (vk::entry_fmt(plan.entries[d.page_off + page - d.page_first]) == VK_FMT_LOSSLESS) {
+      const int f = vk::entry_fmt(plan.entries[d.page_off + page - d.page_first]);
+      if (f == VK_FMT_LOSSLESS) {
         ll_units.push_back(static_cast<int32_t>(i));
         ll_units.push_back(u);
+      } else if (f != VK_FMT_TERNARY2) {
+        ot_units.push_back(static_cast<int32_t>(i));
+        ot_units.push_back(u);
       }
+      ++n_units;
     }
   }
-  const int64_t need = static_cast<int64_t>(plan.seqs.size()) * sizeof(vk::AppendSeqDesc) +
-                       static_cast<int64_t>(plan.entries.size()) * 4 + static_cast<int64_t>(ll_units.size()) * 4;
+  int64_t need = static_cast<int64_t>(plan.seqs.size()) * sizeof(vk::AppendSeqDesc) +
+                 static_cast<int64_t>(plan.entries.size()) * 4 + static_cast<int64_t>(ll_units.size()) * 4;
   if (need > c->plan_bytes) return fail(VK_ERR_ARG, "append plan too large");
+  // A call that is mostly ternary writes its fp8 / fp16 units in a launch of their own, so that
+  // the main launch runs the pack kernel's lean ternary instance (fewer registers, more waves);
+  // calls made of such units (decode-time appends into the recent tier) keep one launch.
+  if (ot_units.empty() || 8 * static_cast<int64_t>(ot_units.size() / 2) > n_units ||
+      need + static_cast<int64_t>(ot_units.size()) * 4 > c->plan_bytes)
+    ot_units.clear();
+  need += static_cast<int64_t>(ot_units.size()) * 4;
   st = set_device(c);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -452,6 +467,8 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   std::memcpy(hp + desc_bytes, plan.entries.data(), plan.entries.size() * 4);
   const size_t ll_off = desc_bytes + plan.entries.size() * 4;
   if (!ll_units.empty()) std::memcpy(hp + ll_off, ll_units.data(), ll_units.size() * 4);
+  const size_t ot_off = ll_off + ll_units.size() * 4;
+  if (!ot_units.empty()) std::memcpy(hp + ot_off, ot_units.data(), ot_units.size() * 4);
   e = hipMemcpyAsync(c->plan_dev[slot], hp, static_cast<size_t>(need), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync");
   vk::AppendArgs a{};
@@ -500,6 +517,8 @@ vk_status append_impl(vk_cache* c, int32_t layer_begin, int32_t n_layers, int32_
   a.eps = cfg.eps;
   a.ll_units = reinterpret_cast<const int32_t*>(c->plan_dev[slot] + ll_off);
   a.n_ll_units = static_cast<int32_t>(ll_units.size() / 2);
+  a.ot_units = reinterpret_cast<const int32_t*>(c->plan_dev[slot] + ot_off);
+  a.n_ot_units = static_cast<int32_t>(ot_units.size() / 2);
   a.all_ternary = std::all_of(plan.entries.begin(), plan.entries.end(), [](int32_t e) {
     return vk::entry_fmt(e) == VK_FMT_TERNARY2 || vk::entry_fmt(e) == VK_FMT_LOSSLESS;
   });

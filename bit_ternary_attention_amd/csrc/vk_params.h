@@ -64,6 +64,9 @@ struct AppendArgs {
                            // blocks keep the next task's loads in flight (tasks_per_blk sized for it)
   const int32_t* ll_units; // [n_ll_units][2]: (sequence index, unit) of every lossless 16-token unit
   int32_t n_ll_units;      // written by a pack launch of their own (the main one skips them)
+  const int32_t* ot_units; // [n_ot_units][2]: (sequence index, unit) of every fp8 / fp16 16-token
+  int32_t n_ot_units;      // unit, when they get a pack launch of their own (0: the main launch
+                           // writes them)
   float eps;
 };
 

@@ -298,7 +298,9 @@ __device__ __forceinline__ void store_ternary_tile(const uint4 (&w)[16 / (64 / (
 // tokens and it walks whole input rows.
 // MODE 0: every page of the call is ternary (the other routes are left out, which keeps the
 // register count, and so the resident waves per SIMD, where the ternary route needs it);
-// MODE 1: ternary, fp8 and fp16 pages; MODE 2: lossless pages as well.
+// MODE 1: ternary, fp8 and fp16 pages; MODE 2: a list of lossless units; MODE 3: a list of fp8 /
+// fp16 units (a call that holds some runs MODE 0 over every task, which skips them and keeps the
+// ternary route's register count, then MODE 3 over them).
 template <int DT, int D, int MODE>
 __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   constexpr int CPR = D / 8;     // 16-byte chunks per token row
@@ -315,26 +317,29 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
   const int64_t row = static_cast<int64_t>(hkv) * D;
   const int c = lane % CPR, rg = lane / CPR;
 
-  // MODE 2 runs over the lossless units only (a list of (sequence index, unit)), one task per block
-  const int64_t g_end = static_cast<int64_t>(a.n_layers) * (MODE == 2 ? 2LL * hkv * a.n_ll_units : a.total_tasks);
-  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (MODE == 2 ? 1 : a.tasks_per_blk);
-  const int64_t g1 = MODE == 2 ? g0 + 1 : (g0 + a.tasks_per_blk < g_end ? g0 + a.tasks_per_blk : g_end);
+  // MODES 2 and 3 run over a list of (sequence index, unit) pairs, one task per block
+  constexpr bool LIST = MODE >= 2;
+  const int32_t* list = MODE == 2 ? a.ll_units : a.ot_units;
+  const int n_list = MODE == 2 ? a.n_ll_units : a.n_ot_units;
+  const int64_t g_end = static_cast<int64_t>(a.n_layers) * (LIST ? 2LL * hkv * n_list : a.total_tasks);
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (LIST ? 1 : a.tasks_per_blk);
+  const int64_t g1 = LIST ? g0 + 1 : (g0 + a.tasks_per_blk < g_end ? g0 + a.tasks_per_blk : g_end);
   int i = -1, l_rel = -1, task_end = 0;
   AppendSeqDesc d{};
   SegInfo seg_k{}, seg_v{};  // the current (layer, sequence)'s records, derived when first needed
   bool have_k = false, have_v = false;
   for (int64_t g = g0; g < g1; ++g) {
     int h, kv, uk;
-    if constexpr (MODE == 2) {
-      const int64_t per_layer = 2LL * hkv * a.n_ll_units;
+    if constexpr (LIST) {
+      const int64_t per_layer = 2LL * hkv * n_list;
       l_rel = static_cast<int>(g / per_layer);
       const int r = static_cast<int>(g - static_cast<int64_t>(l_rel) * per_layer);
       const int lu = r / (2 * hkv);
       h = r % hkv;
       kv = (r / hkv) & 1;
-      i = a.ll_units[2 * lu];
+      i = list[2 * lu];
       d = a.descs[i];
-      uk = a.ll_units[2 * lu + 1] - d.unit_first;
+      uk = list[2 * lu + 1] - d.unit_first;
     } else {
       const int lr = static_cast<int>(g / a.total_tasks);
       const int t = static_cast<int>(g - static_cast<int64_t>(lr) * a.total_tasks);
@@ -387,11 +392,11 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
     uint8_t* tile = a.P.pool[fmt] + (static_cast<int64_t>(layer) * a.P.cap[fmt] + idx) * a.P.page_bytes[fmt] +
                     static_cast<int64_t>(kv * hkv + h) * a.P.tile_bytes[fmt];
 
-    if (MODE != 2 && l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
+    if (!LIST && l_rel == 0 && kv == 0 && h == 0 && lane == 0 && (uk == 0 || upi == 0))
       a.P.block_table[static_cast<int64_t>(d.slot) * a.P.max_pages + page] = entry;
-    if (MODE != 2 && fmt == VK_FMT_LOSSLESS) continue;  // written by the launch over the lossless units
+    if (!LIST && fmt == VK_FMT_LOSSLESS) continue;  // written by the launch over the lossless units
 
-    if (MODE != 2 && fmt == VK_FMT_TERNARY2) {
+    if (!LIST && fmt == VK_FMT_TERNARY2) {
       if (kv == 0 && !have_k) {
         seg_k = segment_info<DT>(a, d, l_rel, 0);
         have_k = true;
@@ -405,8 +410,8 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
         a.P.gamma[(static_cast<int64_t>(layer) * a.P.cap[0] + idx) * 2 + kv] = si.gamma;
       store_ternary_tile<D>(w, si.thresh, tile, upi, kv, lds16);
     } else if (MODE == 0) {
-      // (not reached: the host launches this instance only when every page is ternary or lossless)
-    } else if (MODE == 1 && fmt == VK_FMT_FP8E4M3) {
+      // fp8 / fp16 units: written by the MODE 3 launch over their list
+    } else if ((MODE == 1 || MODE == 3) && fmt == VK_FMT_FP8E4M3) {
       const bool dyn = a.P.fp8_dynamic != 0;
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
           __syncthreads();
         }
       }
-    } else if (MODE == 1) {  // VK_FMT_F16
+    } else if (MODE == 1 || MODE == 3) {  // VK_FMT_F16
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
         const int r = rg * NI + k;
@@ -834,6 +839,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s, LaunchTimer* t) {
   }
   const dim3 g2(a.pack_blocks);
   if (t) t->begin(VK_KERNEL_PACK, s);
+  // the lean instance (MODE 0) when every page is ternary or lossless, or when the fp8 / fp16
+  // units go to a launch of their own over their list
+  const bool lean = a.all_ternary || a.n_ot_units > 0;
   if (a.pack_pipelined && (a.P.dim == 128 || a.P.dim == 64)) {  // every page ternary (set on the host)
     if (a.P.dim == 128) {
       if (bf) k_pack_tern<1, 128><<<g2, 64, 0, s>>>(a);
@@ -843,25 +851,40 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s, LaunchTimer* t) {
       else k_pack_tern<0, 64><<<g2, 64, 0, s>>>(a);
     }
   } else if (a.P.dim == 256) {  // (no lossless pages at head dim 256: refused on the host)
-    if (a.all_ternary) {
+    if (lean) {
       if (bf) k_pack<1, 256, 0><<<g2, 64, 0, s>>>(a);
       else k_pack<0, 256, 0><<<g2, 64, 0, s>>>(a);
     } else {
       if (bf) k_pack<1, 256, 1><<<g2, 64, 0, s>>>(a);
       else k_pack<0, 256, 1><<<g2, 64, 0, s>>>(a);
     }
-  } else if (a.P.dim == 128 && a.all_ternary) {
+  } else if (a.P.dim == 128 && lean) {
     if (bf) k_pack<1, 128, 0><<<g2, 64, 0, s>>>(a);
     else k_pack<0, 128, 0><<<g2, 64, 0, s>>>(a);
   } else if (a.P.dim == 128) {
     if (bf) k_pack<1, 128, 1><<<g2, 64, 0, s>>>(a);
     else k_pack<0, 128, 1><<<g2, 64, 0, s>>>(a);
-  } else if (a.all_ternary) {
+  } else if (lean) {
     if (bf) k_pack<1, 64, 0><<<g2, 64, 0, s>>>(a);
     else k_pack<0, 64, 0><<<g2, 64, 0, s>>>(a);
   } else {
     if (bf) k_pack<1, 64, 1><<<g2, 64, 0, s>>>(a);
     else k_pack<0, 64, 1><<<g2, 64, 0, s>>>(a);
+  }
+  // the fp8 / fp16 units: one block per (layer, unit, K|V, head), after the main launch, which
+  // writes their block-table entries
+  if (a.n_ot_units > 0) {
+    const dim3 g4(static_cast<unsigned>(2LL * a.P.hkv * a.n_ot_units * a.n_layers));
+    if (a.P.dim == 256) {
+      if (bf) k_pack<1, 256, 3><<<g4, 64, 0, s>>>(a);
+      else k_pack<0, 256, 3><<<g4, 64, 0, s>>>(a);
+    } else if (a.P.dim == 128) {
+      if (bf) k_pack<1, 128, 3><<<g4, 64, 0, s>>>(a);
+      else k_pack<0, 128, 3><<<g4, 64, 0, s>>>(a);
+    } else {
+      if (bf) k_pack<1, 64, 3><<<g4, 64, 0, s>>>(a);
+      else k_pack<0, 64, 3><<<g4, 64, 0, s>>>(a);
+    }
   }
   // the lossless units: one block per (layer, unit, K|V, head); bfloat16 input only (checked on
   // the host)
