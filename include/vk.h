@@ -216,7 +216,12 @@ VK_API vk_status vk_append_ragged(vk_cache* c, int32_t layer_begin, int32_t n_la
  * retention-preserving case of Minima-KV).  softmax_scale <= 0 means
  * 1/sqrt(head_dim).  Query head h reads KV head h / (n_q_heads/n_kv_heads).
  * Pages are read in their stored format through the block table; no dense
- * copy is made.  Every sequence must have L >= 1.  n_seqs = 0 does nothing
+ * copy is made.  With several parts per (sequence, KV head) (split ranges,
+ * fp8 / fp16 blocks) the matrix-core kernel's last block of each pair to finish
+ * combines the partial softmax states (device-scope part counters that the
+ * merging block sets back to zero); the vector-ALU kernel and launches with
+ * lossless pages run a merge launch instead.  Both give the same bits.
+ * Every sequence must have L >= 1.  n_seqs = 0 does nothing
  * and returns VK_OK (q and out may then be NULL).
  * The call only enqueues kernel launches on `stream` (no allocation, copy or
  * synchronisation), so it may be captured into a HIP graph.  A replay repeats
@@ -334,8 +339,9 @@ enum {
   VK_KERNEL_FINALIZE = 1,  /* (unused: the pack kernel derives gamma and the   */
                            /*  code threshold of each segment itself)         */
   VK_KERNEL_PACK = 2,      /* write side pass 2: quantise, pack, scatter      */
-  VK_KERNEL_DECODE = 3,    /* paged decode attention (per split)              */
-  VK_KERNEL_MERGE = 4,     /* split-K online-softmax merge                    */
+  VK_KERNEL_DECODE = 3,    /* paged decode attention (with the split merge     */
+                           /*  when the kernel combines the parts itself)     */
+  VK_KERNEL_MERGE = 4,     /* split-K online-softmax merge launch             */
   VK_KERNEL_RETIER = 5,    /* FP8 -> ternary page conversion (vk_retier)      */
   VK_KERNEL_COUNT = 6
 };
