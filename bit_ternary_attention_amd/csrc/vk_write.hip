@@ -450,9 +450,10 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
       if (kv == 1) {
         __syncthreads();
         const bool full = pos0 >= d.t0 && pos0 + 16 <= t1;
+        // dimension j * 64 + lane: each store instruction writes 64 consecutive 16-byte rows
 #pragma unroll
         for (int j = 0; j < DPL; ++j) {
-          const int dd = lane * DPL + j;
+          const int dd = j * 64 + lane;
           uint8_t* dst = tile + static_cast<int64_t>(dd) * a.P.bs + upi * 16;
           if (full) {
             *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(lds8 + dd * 16);
@@ -642,17 +643,18 @@ __global__ __launch_bounds__(64) void k_pack(AppendArgs a) {
       if (kv == 1) {
         __syncthreads();
         const bool full = pos0 >= d.t0 && pos0 + 16 <= t1;
+        // 16-byte piece k * 64 + lane (dimension p / 2, tokens 8 (p % 2) .. + 7): each store
+        // instruction writes 64 consecutive pieces
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) {
-          const int dd = lane * DPL + j;
-          uint16_t* dst = reinterpret_cast<uint16_t*>(tile) + static_cast<int64_t>(dd) * a.P.bs + upi * 16;
+        for (int k = 0; k < 2 * DPL; ++k) {
+          const int p = k * 64 + lane;
+          const int dd = p >> 1, th = (p & 1) * 8;
+          uint16_t* dst = reinterpret_cast<uint16_t*>(tile) + static_cast<int64_t>(dd) * a.P.bs + upi * 16 + th;
           if (full) {
-            const uint4* s4 = reinterpret_cast<const uint4*>(lds16 + dd * 16);
-            reinterpret_cast<uint4*>(dst)[0] = s4[0];
-            reinterpret_cast<uint4*>(dst)[1] = s4[1];
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(lds16 + dd * 16 + th);
           } else {
-            for (int t = 0; t < 16; ++t)
-              if (pos0 + t >= d.t0 && pos0 + t < t1) dst[t] = lds16[dd * 16 + t];
+            for (int t = 0; t < 8; ++t)
+              if (pos0 + th + t >= d.t0 && pos0 + th + t < t1) dst[t] = lds16[dd * 16 + th + t];
           }
         }
         __syncthreads();
