@@ -111,6 +111,37 @@ SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blo
   return {static_cast<int32_t>(cdiv(max_units, ups)), static_cast<int32_t>(ups)};
 }
 
+SplitPlan balance_splits(SplitPlan base, int64_t items, int32_t max_units, int32_t n_cu, int32_t max_per_cu,
+                         int32_t max_splits, int32_t min_units, int32_t granule) {
+  static constexpr int64_t kWeight[4] = {0, 118, 100, 104};  // per resident blocks per CU (1..3)
+  const int64_t cap = std::min<int64_t>(3, max_per_cu);
+  if (items <= 0 || n_cu <= 0 || max_units <= 0 || base.n_splits < 1 || cap < 1) return base;
+  // cost of a plan on its busiest compute unit, or -1 outside the weighed range
+  auto cost = [&](int64_t n_splits, int64_t ups) -> int64_t {
+    const int64_t blocks = items * n_splits;
+    if (blocks < n_cu) return -1;
+    const int64_t k = cdiv(blocks, n_cu);
+    return k <= cap ? k * ups * kWeight[k] : -1;
+  };
+  const int64_t base_cost = cost(base.n_splits, base.units_per_split);
+  if (base_cost < 0) return base;
+  SplitPlan best = base;
+  int64_t best_cost = base_cost;
+  const int64_t g = std::max(1, granule);
+  for (int32_t s = 1; s <= max_splits; ++s) {
+    const int64_t ups = cdiv(cdiv(max_units, s), g) * g;
+    if (ups < min_units) break;  // ups only shrinks as s grows
+    const int64_t n = cdiv(max_units, ups);
+    if (n > max_splits) continue;
+    const int64_t c = cost(n, ups);
+    if (c >= 0 && 100 * c < 95 * base_cost && c < best_cost) {
+      best = {static_cast<int32_t>(n), static_cast<int32_t>(ups)};
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
 bool plan_decode_order(const int32_t* units, const int64_t* mix_weight, int32_t n_seqs, int32_t n_splits,
                        int32_t units_per_split, int32_t n_mix, int32_t max_entries, std::vector<uint16_t>* order) {
   order->clear();

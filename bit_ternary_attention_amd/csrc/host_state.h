@@ -107,6 +107,17 @@ struct SplitPlan {
 SplitPlan plan_splits(int64_t total_units, int32_t max_units, int32_t target_blocks, int32_t max_splits,
                       int32_t min_units, int32_t granule = 1);
 
+// A launch whose `items` (sequence, KV head) pairs all attend max_units units runs in
+// ceil(items x n_splits / n_cu) blocks on its busiest compute unit, and takes about as long as
+// that unit's units (blocks x units_per_split) weighted by how well that many resident blocks
+// stream (measured on 32 x 32K tokens at 1, 2 and 3 blocks per CU: 1.18, 1.00, 1.04).  Returns
+// the split count (same granule and minimum split size) with the smallest such cost when it
+// beats `base` by more than 5%, else `base`.  Only plans that fill every compute unit and keep
+// at most max_per_cu (<= 3) blocks per CU, all resident at once, are weighed; `base` outside
+// that range is returned as it is.
+SplitPlan balance_splits(SplitPlan base, int64_t items, int32_t max_units, int32_t n_cu, int32_t max_per_cu,
+                         int32_t max_splits, int32_t min_units, int32_t granule);
+
 // Dispatch order of a matrix-core decode launch over sequences of different lengths: every
 // (sequence i, part z) block of the launch once, heaviest first (the longest-processing-time
 // rule: the hardware hands the next block to whichever compute-unit slot frees up, so the large

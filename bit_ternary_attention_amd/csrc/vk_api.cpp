@@ -41,6 +41,7 @@ constexpr int64_t kMaxPartials = 1 << 20;  // float64 absmean partials per appen
 constexpr int kDecodeTargetGroups = 4096;  // work groups a decode launch aims for
 constexpr int kDecodeMaxSplits = 64;
 constexpr int kDecodeMinUnits = 4;         // 16-token units per split, at least (vector-ALU kernel)
+constexpr int kDecodeMaxResidentBlocks = 3;  // matrix-core kernel, head dims 64 / 128: blocks per CU at once
 constexpr int kDecodeMinUnitsPerWave = 8;  // matrix-core kernel: units per wave, at least
 constexpr int kDecodeUnitsPerStep = 4;     // matrix-core kernel: units per clean step, at most (a wave's
                                            // range is a whole number of them when the split size is)
@@ -98,6 +99,13 @@ int64_t decode_mix_fixed() {
   const char* e = std::getenv("VK_DECODE_MIX_FIXED");
   const long long v = e ? std::atoll(e) : -1;
   return v >= 0 ? v : 0;
+}
+// Equal-length all-ternary matrix-core launches re-weigh their split count so that the busiest
+// compute unit holds as few units as the blocks' residency allows (balance_splits).
+// VK_DECODE_BALANCE=0, or a VK_DECODE_BLOCKS_PER_CU override, keeps the plain plan.
+bool decode_balance_on() {
+  const char* e = std::getenv("VK_DECODE_BALANCE");
+  return !(e && e[0] == '0') && !std::getenv("VK_DECODE_BLOCKS_PER_CU");
 }
 int decode_units_per_iter() {              // matrix-core prefetch depth in units; VK_DECODE_UPI=4|8 overrides
   const char* e = std::getenv("VK_DECODE_UPI");
@@ -735,11 +743,17 @@ VK_API vk_status vk_decode_attn(vk_cache* c, int32_t layer, int32_t n_seqs, cons
     const bool ragged = mfma && (max_units != min_units || n_fp > 0);
     const int32_t target_blocks =
         static_cast<int32_t>(std::max(1, c->n_cu) * (ragged ? decode_blocks_per_cu_ragged() : decode_blocks_per_cu()));
-    const vk::SplitPlan sp = mfma ? vk::plan_splits(all_units, max_units, target_blocks,
-                                                    std::max(1, max_splits), 4 * kDecodeMinUnitsPerWave,
-                                                    4 * kDecodeUnitsPerStep)
-                                  : vk::plan_splits(all_units, max_units, kDecodeTargetGroups,
-                                                    std::max(1, max_splits), kDecodeMinUnits);
+    vk::SplitPlan sp = mfma ? vk::plan_splits(all_units, max_units, target_blocks,
+                                              std::max(1, max_splits), 4 * kDecodeMinUnitsPerWave,
+                                              4 * kDecodeUnitsPerStep)
+                            : vk::plan_splits(all_units, max_units, kDecodeTargetGroups,
+                                              std::max(1, max_splits), kDecodeMinUnits);
+    // every pair attends the same units: a split count whose blocks spread evenly over the
+    // compute units (e.g. 24 sequences x 8 KV heads: 4 splits, 3 blocks on every CU, rather
+    // than 3 splits, 3 blocks on some CUs and 2 on others)
+    if (mfma && !ragged && !d256 && n_mix == 0 && c->n_cu > 0 && decode_balance_on())
+      sp = vk::balance_splits(sp, items, max_units, c->n_cu, kDecodeMaxResidentBlocks, std::max(1, max_splits),
+                              4 * kDecodeMinUnitsPerWave, 4 * kDecodeUnitsPerStep);
     a.n_splits = sp.n_splits;
     a.units_per_split = sp.units_per_split;
     // Opted in: all-ternary launches with at most one (sequence, KV head) per compute unit and

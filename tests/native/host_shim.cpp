@@ -114,6 +114,14 @@ int hs_plan_splits(long long total_units, int max_units, int target, int max_spl
   return p.n_splits;
 }
 
+int hs_balance_splits(int base_splits, int base_ups, long long items, int max_units, int n_cu, int max_per_cu,
+                      int max_splits, int min_units, int granule, int* units_per_split) {
+  const vk::SplitPlan p = vk::balance_splits({base_splits, base_ups}, items, max_units, n_cu, max_per_cu, max_splits,
+                                             min_units, granule);
+  *units_per_split = p.units_per_split;
+  return p.n_splits;
+}
+
 // dispatch order of a decode launch: returns the entry count (0 = the plain grid's order)
 int hs_plan_decode_order(const int* units, const long long* mix_weight, int n_seqs, int n_splits,
                          int units_per_split, int n_mix, int max_entries, unsigned short* out) {

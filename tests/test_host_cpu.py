@@ -140,6 +140,8 @@ def hs():
     L.hs_check_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, P(ctypes.c_int), ctypes.c_int]
     L.hs_plan_splits.argtypes = [ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.hs_balance_splits.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_longlong] + [ctypes.c_int] * 6 + \
+        [ctypes.POINTER(ctypes.c_int)]
     L.hs_plan_decode_order.argtypes = [P(ctypes.c_int), P(ctypes.c_longlong), ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, P(ctypes.c_ushort)]
     return L
@@ -356,6 +358,45 @@ def _plan(hs, total, max_units, target, max_splits, min_units, granule=1):
     ups = ctypes.c_int(0)
     n = hs.hs_plan_splits(total, max_units, target, max_splits, min_units, granule, ctypes.byref(ups))
     return n, ups.value
+
+
+def _balance(hs, n_seqs, max_units, n_cu=256, heads=8, cap=64, mn=32, gr=16):
+    """The launch's plan as the library makes it: two blocks per CU wanted, then balanced."""
+    items = n_seqs * heads
+    base = _plan(hs, items * max_units, max_units, 2 * n_cu, cap, mn, gr)
+    ups = ctypes.c_int(0)
+    n = hs.hs_balance_splits(base[0], base[1], items, max_units, n_cu, 3, cap, mn, gr, ctypes.byref(ups))
+    return base, (n, ups.value)
+
+
+def test_split_balance(hs):
+    # 32 x 32K tokens (2048 units) x 8 KV heads: two blocks on every CU already, kept
+    assert _balance(hs, 32, 2048) == ((2, 1024), (2, 1024))
+    # 24 sequences: 3 splits put 3 blocks on some CUs and 2 on others; 4 splits, 3 on every CU
+    assert _balance(hs, 24, 2048) == ((3, 688), (4, 512))
+    # 12 sequences: 6 splits (576 blocks) -> 8 splits (768 blocks, 3 per CU)
+    assert _balance(hs, 12, 2048) == ((6, 352), (8, 256))
+    # 20 sequences: 4 splits (640 blocks, up to 3 per CU) -> 3 splits (480, at most 2 per CU)
+    assert _balance(hs, 20, 2048) == ((4, 512), (3, 688))
+    # 4 x 128K tokens and 16 / 8 / 4 sequences of 32K: already even, kept
+    for n_seqs, mx in ((4, 8192), (16, 2048), (8, 2048), (4, 2048)):
+        base, bal = _balance(hs, n_seqs, mx)
+        assert bal == base, (n_seqs, mx, base, bal)
+    # launches that do not fill every CU are left alone (small batches, latency-bound)
+    for n_seqs, mx in ((1, 17), (1, 300), (2, 64)):
+        base, bal = _balance(hs, n_seqs, mx)
+        assert bal == base
+    # invariants over many shapes: whole granules, the minimum size, the cap, every unit covered,
+    # and the busiest CU never holds more units than with the plain plan
+    for n_seqs in range(1, 65):
+        for mx in (33, 517, 2048, 3001, 8192):
+            base, (n, ups) = _balance(hs, n_seqs, mx)
+            assert ups % 16 == 0 and (ups >= 32 or (n, ups) == base) and 1 <= n <= 64
+            assert n * ups >= mx and (n - 1) * ups < mx
+            blocks = lambda s: n_seqs * 8 * s
+            if (n, ups) != base:
+                k_b, k_n = -(-blocks(base[0]) // 256), -(-blocks(n) // 256)
+                assert blocks(n) >= 256 and k_n <= 3 and k_n * ups < k_b * base[1] or k_b == 1
 
 
 def test_split_plan(hs):
